@@ -1,0 +1,224 @@
+"""CPU oracle for D = A x B (+ C) on fp16/bf16 inputs.
+
+TEST INFRASTRUCTURE ONLY: imported by tests/, by the smoke check and by the
+benchmark's CPU-baseline leg, never by the product path.  It shares no code
+with the HIP library and does not import it.
+
+The arithmetic lives in oracle.c (plain C, binary64).  This module only
+marshals numpy arrays into it:
+
+  gemm_f64(A, B, C, dtype)         -> (ref, S)  full M x N reference and
+                                      S = sum_k |a_ik b_kj|
+  gemm_f64_at(A, B, C, ii, jj, dt) -> (ref, S)  the same at chosen positions
+  decode / encode_rne / ulp_out    exact fp16/bf16 <-> binary64 conversions
+  tol_check(got, ref, S, dtype)    acceptance rule |g-ref| <= ulp_out(ref) + 2^-20 S
+  grouped_order                    the grouped tile visiting order, enumerated
+                                   plainly (FlagGems "Hygon optimization",
+                                   section "Grouped scheduling")
+
+Inputs are numpy uint16 arrays holding the raw fp16/bf16 bit patterns (any
+element strides); dtype is "f16" or "bf16".
+
+Every function here is pinned by tests/test_oracle.py against exhaustive
+library conversions, exact rational arithmetic, BLAS in float64 and closed
+forms (identity, permutation, rank-1, integer-valued inputs).
+"""
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+_DT = {"f16": 0, "bf16": 1}
+_i64 = ctypes.c_int64
+_p = ctypes.c_void_p
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        from . import build as _b
+        _b.build()
+    lib = ctypes.CDLL(_LIB_PATH)
+    lib.oracle_decode_f16.restype = ctypes.c_double
+    lib.oracle_decode_f16.argtypes = [ctypes.c_uint16]
+    lib.oracle_decode_bf16.restype = ctypes.c_double
+    lib.oracle_decode_bf16.argtypes = [ctypes.c_uint16]
+    lib.oracle_ulp_out.restype = ctypes.c_double
+    lib.oracle_ulp_out.argtypes = [ctypes.c_double, ctypes.c_int]
+    lib.oracle_encode_rne.restype = ctypes.c_uint16
+    lib.oracle_encode_rne.argtypes = [ctypes.c_double, ctypes.c_int]
+    lib.oracle_decode_array.restype = None
+    lib.oracle_decode_array.argtypes = [_p, _p, _i64, ctypes.c_int]
+    lib.oracle_encode_array.restype = None
+    lib.oracle_encode_array.argtypes = [_p, _p, _i64, ctypes.c_int]
+    lib.oracle_ulp_array.restype = ctypes.c_double
+    lib.oracle_ulp_array.argtypes = [_p, _p, _i64, ctypes.c_int]
+    lib.oracle_gemm_f64.restype = ctypes.c_int
+    lib.oracle_gemm_f64.argtypes = [_i64, _i64, _i64, ctypes.c_int,
+                                    _p, _i64, _i64, _p, _i64, _i64, _p, _i64, _i64, _p, _p]
+    lib.oracle_gemm_f64_at.restype = ctypes.c_int
+    lib.oracle_gemm_f64_at.argtypes = [_i64, ctypes.c_int,
+                                       _p, _i64, _i64, _p, _i64, _i64, _p, _i64, _i64,
+                                       _i64, _p, _p, _p, _p]
+    lib.oracle_tol_check.restype = _i64
+    lib.oracle_tol_check.argtypes = [_i64, _p, _p, _p, ctypes.c_int,
+                                     ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_i64)]
+    lib.oracle_num_threads.restype = ctypes.c_int
+    lib.oracle_num_threads.argtypes = []
+    _lib = lib
+    return lib
+
+
+def _dt(dtype):
+    try:
+        return _DT[dtype]
+    except KeyError:
+        raise ValueError("dtype must be 'f16' or 'bf16', got %r" % (dtype,))
+
+
+def _bits(x, name):
+    if not isinstance(x, np.ndarray) or x.dtype != np.uint16:
+        raise TypeError("%s must be a numpy uint16 array of raw fp16/bf16 bits" % name)
+    if x.ndim != 2:
+        raise ValueError("%s must be 2-D" % name)
+    return x
+
+
+def _estrides(x):
+    """Element strides of a uint16 array (numpy reports bytes)."""
+    return x.strides[0] // 2, x.strides[1] // 2
+
+
+def num_threads() -> int:
+    return _load().oracle_num_threads()
+
+
+def decode(bits, dtype):
+    """Exact binary64 value of each fp16/bf16 bit pattern."""
+    b = np.ascontiguousarray(bits, dtype=np.uint16)
+    out = np.empty(b.shape, dtype=np.float64)
+    _load().oracle_decode_array(b.ctypes.data, out.ctypes.data, b.size, _dt(dtype))
+    return out
+
+
+def encode_rne(x, dtype):
+    """Bit patterns of x rounded to fp16/bf16, nearest with ties to even."""
+    v = np.ascontiguousarray(x, dtype=np.float64)
+    out = np.empty(v.shape, dtype=np.uint16)
+    _load().oracle_encode_array(v.ctypes.data, out.ctypes.data, v.size, _dt(dtype))
+    return out
+
+
+def ulp_out(x, dtype):
+    """One ulp of the output format in the binade of |x| (subnormal quantum at least)."""
+    v = np.ascontiguousarray(x, dtype=np.float64)
+    out = np.empty(v.shape, dtype=np.float64)
+    _load().oracle_ulp_array(v.ctypes.data, out.ctypes.data, v.size, _dt(dtype))
+    return out
+
+
+def gemm_f64(A, B, C=None, dtype="f16"):
+    """ref = A x B (+ C) and S = sum_k |a_ik b_kj|, in binary64, from exact inputs."""
+    A = _bits(A, "A")
+    B = _bits(B, "B")
+    M, K = A.shape
+    K2, N = B.shape
+    if K2 != K:
+        raise ValueError("inner dimensions differ: A is %dx%d, B is %dx%d" % (M, K, K2, N))
+    sam, sak = _estrides(A)
+    sbk, sbn = _estrides(B)
+    if C is not None:
+        C = _bits(C, "C")
+        if C.shape != (M, N):
+            raise ValueError("C must be %dx%d" % (M, N))
+        scm, scn = _estrides(C)
+        cptr = C.ctypes.data
+    else:
+        scm = scn = 0
+        cptr = None
+    ref = np.empty((M, N), dtype=np.float64)
+    S = np.empty((M, N), dtype=np.float64)
+    rc = _load().oracle_gemm_f64(M, N, K, _dt(dtype), A.ctypes.data, sam, sak,
+                                 B.ctypes.data, sbk, sbn, cptr, scm, scn,
+                                 ref.ctypes.data, S.ctypes.data)
+    if rc != 0:
+        raise RuntimeError("oracle_gemm_f64 failed (%d)" % rc)
+    return ref, S
+
+
+def gemm_f64_at(A, B, C, ii, jj, dtype="f16"):
+    """ref and S at output positions (ii[t], jj[t])."""
+    A = _bits(A, "A")
+    B = _bits(B, "B")
+    M, K = A.shape
+    K2, N = B.shape
+    if K2 != K:
+        raise ValueError("inner dimensions differ")
+    ii = np.ascontiguousarray(ii, dtype=np.int64)
+    jj = np.ascontiguousarray(jj, dtype=np.int64)
+    if ii.shape != jj.shape or ii.ndim != 1:
+        raise ValueError("ii and jj must be 1-D and of equal length")
+    if ii.size and (ii.min() < 0 or ii.max() >= M or jj.min() < 0 or jj.max() >= N):
+        raise IndexError("sample position outside the output")
+    sam, sak = _estrides(A)
+    sbk, sbn = _estrides(B)
+    if C is not None:
+        C = _bits(C, "C")
+        scm, scn = _estrides(C)
+        cptr = C.ctypes.data
+    else:
+        scm = scn = 0
+        cptr = None
+    ref = np.empty(ii.shape, dtype=np.float64)
+    S = np.empty(ii.shape, dtype=np.float64)
+    rc = _load().oracle_gemm_f64_at(K, _dt(dtype), A.ctypes.data, sam, sak,
+                                    B.ctypes.data, sbk, sbn, cptr, scm, scn,
+                                    ii.size, ii.ctypes.data, jj.ctypes.data,
+                                    ref.ctypes.data, S.ctypes.data)
+    if rc != 0:
+        raise RuntimeError("oracle_gemm_f64_at failed (%d)" % rc)
+    return ref, S
+
+
+def tol_check(got, ref, S, dtype):
+    """Apply the acceptance rule to computed output bits.
+
+    Returns (n_fail, worst, first_bad): worst is max |g-ref|/(ulp_out(ref)+2^-20 S)
+    (inf when some g is not finite); first_bad the flat index of the first
+    failure or -1.
+    """
+    g = np.ascontiguousarray(got, dtype=np.uint16).ravel()
+    r = np.ascontiguousarray(ref, dtype=np.float64).ravel()
+    s = np.ascontiguousarray(S, dtype=np.float64).ravel()
+    if not (g.size == r.size == s.size):
+        raise ValueError("got, ref and S differ in size")
+    worst = ctypes.c_double(0.0)
+    first = ctypes.c_int64(-1)
+    n = _load().oracle_tol_check(g.size, g.ctypes.data, r.ctypes.data, s.ctypes.data,
+                                 _dt(dtype), ctypes.byref(worst), ctypes.byref(first))
+    return int(n), float(worst.value), int(first.value)
+
+
+def grouped_order(num_pid_m, num_pid_n, group_m):
+    """Order in which a grouped launch visits the output tiles (FlagGems
+    "Hygon optimization", section "Grouped scheduling: improve L2 data reuse").
+
+    The M tiles are cut into bands of group_m consecutive tiles (the last band
+    keeps only the tiles that remain).  Bands are visited one after another;
+    inside a band the walk goes down the band's M tiles for one N tile, then
+    moves to the next N tile, so consecutive programs share a K x N panel of B.
+    Returns the list of (pid_m, pid_n); program id p computes entry p.
+    """
+    order = []
+    for first in range(0, num_pid_m, group_m):
+        band = range(first, min(first + group_m, num_pid_m))
+        for n in range(num_pid_n):
+            for m in band:
+                order.append((m, n))
+    return order
