@@ -1,0 +1,290 @@
+#!/usr/bin/env python3
+"""Benchmark of the gfx950 tiled GEMM on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--sweep] [--no-cpu] [--config k=v,...]
+
+A step is one launch of the whole hot path, D = A x B (+C), on the workload's
+synthetic inputs, which are resident in HBM before timing starts.  The timed
+region is K launches on one stream between two HIP events, preceded and
+followed by a device synchronization; ms_per_step is elapsed / K.
+
+One JSON line is printed (rank 0, N = 1):
+  value     TFLOP/s of the headline workload (bf16 4096^3 by default)
+  roofline  the kernel's achieved flop rate against the dense bf16 MFMA peak
+            (256 CUs x 2.4 GHz x 4096 flop/clk/CU = 2516.6 TFLOP/s), plus the
+            HBM roofline figures of the skinny workload (bf16 16 x 8192 x 8192,
+            B rotated over 4 copies so every launch reads it from HBM)
+  cpu_baseline  the CPU oracle timed on this host on a bounded sample of rows
+            of the same workload, scaled to TFLOP/s
+
+--sweep times interleaved variants (GROUP_M, instruction shape, tile sizes):
+every round visits the variants in a fresh seeded-random order and times a
+batch of launches per visit; the median and spread = (max - min) / median
+over the rounds are reported ("Tuning Triton", section 2: compare a delta with
+the spread, not with zero).
+"""
+import argparse
+import json
+import os
+import random
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 256 * 2.4e9 * 4096 / 1e12        # 2516.6
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="square_bf16_4096")
+    ap.add_argument("--sweep", action="store_true")
+    ap.add_argument("--rounds", type=int, default=30)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-skinny", action="store_true")
+    ap.add_argument("--config", default="", help="forced config fields, e.g. bm=128,bn=128,mfma=32")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--out", default="")
+    return ap.parse_args()
+
+
+def _cfg(s):
+    if not s:
+        return None
+    d = {}
+    for kv in s.split(","):
+        k, v = kv.split("=")
+        d[k.strip()] = int(v)
+    return d
+
+
+class Case:
+    """Device-resident inputs of one workload plus rotation copies of B."""
+
+    def __init__(self, w, rotate=1):
+        import torch
+        import gemm_inputs
+        self.w = w
+        A, B, C = gemm_inputs.make(w)
+        self.A = A.cuda()
+        self.Bs = [B.cuda()]
+        for r in range(1, rotate):
+            self.Bs.append(gemm_inputs.draw((w.K, w.N), w.seeds[1] + 1000 * r, w.dtype, w.dist,
+                                            w.scale).cuda())
+        self.C = C.cuda() if C is not None else None
+        self.D = torch.empty((w.M, w.N), dtype=self.A.dtype, device="cuda")
+        self.host = (A, B, C)
+
+    def launcher(self, config=None):
+        import torch
+        import dense_tiled_gemm_02_amd as g
+        pl = g.plan_for(self.A, self.Bs[0], self.C, self.D, config)
+        stream = torch.cuda.current_stream().cuda_stream
+        lib = g.lib()
+        h = pl.handle
+        a = self.A.data_ptr()
+        bs = [b.data_ptr() for b in self.Bs]
+        c = self.C.data_ptr() if self.C is not None else None
+        d = self.D.data_ptr()
+        run = lib.gemm_run
+        nb = len(bs)
+        state = {"i": 0}
+
+        def launch(n):
+            i = state["i"]
+            for _ in range(n):
+                st = run(h, a, bs[i % nb], c, d, None, 0, stream)
+                if st != 0:
+                    raise g.GemmError(st, g.gemm_last_error())
+                i += 1
+            state["i"] = i
+        return launch, pl
+
+
+def time_region(launch, steps, warmup):
+    """(ms per launch) over `steps` launches between two events on the launch stream."""
+    import torch
+    launch(warmup)
+    torch.cuda.synchronize()
+    s = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    s.record()
+    launch(steps)
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / steps
+
+
+def batch_times(launch, batch, rounds):
+    """Per-launch ms of `rounds` batches of `batch` launches (for median/spread)."""
+    import torch
+    out = []
+    for _ in range(rounds):
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        s.record()
+        launch(batch)
+        e.record()
+        e.synchronize()
+        out.append(s.elapsed_time(e) / batch)
+    return out
+
+
+def stats(ts):
+    med = statistics.median(ts)
+    q = statistics.quantiles(ts, n=4) if len(ts) >= 4 else [med, med, med]
+    return {"median_ms": med, "spread": (max(ts) - min(ts)) / med, "p25_ms": q[0], "p75_ms": q[2],
+            "min_ms": min(ts), "max_ms": max(ts), "n": len(ts)}
+
+
+def cpu_baseline(w, seconds):
+    """Time the CPU oracle on the first rows of the workload (bounded sample)."""
+    import oracle
+    import gemm_inputs
+    A, B, C = gemm_inputs.make(w)
+    Ab, Bb = gemm_inputs.bits(A), gemm_inputs.bits(B)
+    Cb = gemm_inputs.bits(C) if C is not None else None
+    rows = 4
+    t0 = time.perf_counter()
+    oracle.gemm_f64(Ab[:rows], Bb, Cb[:rows] if Cb is not None else None, w.dtype)
+    t1 = time.perf_counter() - t0
+    rows = int(max(4, min(w.M, rows * seconds / max(t1, 1e-3))))
+    t0 = time.perf_counter()
+    oracle.gemm_f64(Ab[:rows], Bb, Cb[:rows] if Cb is not None else None, w.dtype)
+    t = time.perf_counter() - t0
+    flops = 2.0 * rows * w.N * w.K
+    return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": "first %d of %d rows of %s (%dx%dx%d), full K and N; %.2f s" % (
+                rows, w.M, w.name, rows, w.N, w.K, t)}
+
+
+def host_cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def sweep(args):
+    import gemm_inputs
+    variants = {
+        "square_bf16_4096": [dict(bm=256, bn=256, mfma=16, group_m=gm) for gm in (1, 4, 8)] +
+                            [dict(bm=256, bn=256, mfma=32, group_m=gm) for gm in (1, 4, 8)] +
+                            [dict(bm=256, bn=128, mfma=16, group_m=8), dict(bm=128, bn=128, bk=64, mfma=16, group_m=8)],
+        "square_f16_1024": [dict(bm=32, bn=32, bk=32), dict(bm=64, bn=64, bk=32), dict(bm=128, bn=128, bk=64),
+                            dict(bm=64, bn=64, bk=64)],
+        "square_f16_256": [dict(bm=32, bn=32, bk=32), dict(bm=64, bn=64, bk=32), dict(bm=64, bn=64, bk=64),
+                           dict(bm=16, bn=64, bk=64)],
+        "skinny_bf16_16x8192": [dict(bm=16, bn=64, bk=64)],
+        "tail_f16_4000x3000x1000_c": [dict(bm=256, bn=128), dict(bm=128, bn=128, bk=64), dict(bm=256, bn=256),
+                                      dict(bm=128, bn=256)],
+    }[args.workload]
+    w = gemm_inputs.WORKLOADS[args.workload]
+    rot = 4 if w.name.startswith("skinny") else 1
+    case = Case(w, rotate=rot)
+    ls = []
+    for v in variants:
+        launch, pl = case.launcher(v)
+        launch(3)
+        ls.append((v, launch, pl))
+    import torch
+    torch.cuda.synchronize()
+    # batch so that one visit is >= ~1 ms
+    probe = time_region(ls[0][1], 5, 2)
+    batch = max(4, int(1.0 / max(probe, 1e-3)))
+    times = {i: [] for i in range(len(ls))}
+    rng = random.Random(1234)
+    for _ in range(args.rounds):
+        order = list(range(len(ls)))
+        rng.shuffle(order)
+        for i in order:
+            times[i].extend(batch_times(ls[i][1], batch, 1))
+    rows = []
+    for i, (v, _, pl) in enumerate(ls):
+        st = stats(times[i])
+        ms = st["median_ms"]
+        rec = {"workload": w.name, "variant": v, "plan": pl.describe(), **st,
+               "tflops": w.flops() / ms / 1e9, "pct_mfma": 100 * w.flops() / ms / 1e9 / PEAK_BF16_TFLOPS,
+               "gbs": w.bytes() / ms / 1e6, "pct_hbm": 100 * w.bytes() / ms / 1e6 / PEAK_HBM_GBS}
+        rows.append(rec)
+        print(json.dumps(rec), flush=True)
+    return rows
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: the GEMM of this library is a single-GPU kernel "
+              "(multi-GPU sharding is described, not built); got --gpus %d" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import gemm_inputs
+    import dense_tiled_gemm_02_amd as g
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    if args.sweep:
+        sweep(args)
+        return
+    w = gemm_inputs.WORKLOADS[args.workload]
+    case = Case(w, rotate=4 if w.name.startswith("skinny") else 1)
+    launch, pl = case.launcher(_cfg(args.config))
+    torch.cuda.synchronize()
+    ms = time_region(launch, args.steps, args.warmup)
+    spread = stats(batch_times(launch, max(1, args.steps // 10), 10))
+    flops = w.flops()
+    tflops = flops / ms / 1e9
+    rec = {
+        "metric": "GEMM TFLOPS + % of MFMA peak at 4096^3 bf16; % HBM BW on skinny",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f16",
+        "data": "synthetic",
+        "config": {**w.describe(), "plan": pl.describe(), "parallelism": "single-gpu"},
+        "spread": spread,
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": round(PEAK_BF16_TFLOPS, 1),
+                     "unit": "TFLOP/s", "frac": tflops / PEAK_BF16_TFLOPS, "traffic": None},
+    }
+    if not args.no_skinny and args.workload != "skinny_bf16_16x8192":
+        sw = gemm_inputs.WORKLOADS["skinny_bf16_16x8192"]
+        sc = Case(sw, rotate=4)
+        sl, spl = sc.launcher()
+        sms = time_region(sl, max(40, args.steps), 8)
+        gbs = sw.bytes() / sms / 1e6
+        rec["skinny"] = {"workload": sw.name, "plan": spl.describe(), "ms_per_step": sms,
+                         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                                      "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS, "traffic": None},
+                         "tflops": sw.flops() / sms / 1e9}
+        del sc
+    if not args.no_cpu:
+        cb = cpu_baseline(w, args.cpu_seconds)
+        cb["host_cpu"] = host_cpu_model()
+        rec["cpu_baseline"] = cb
+    line = json.dumps(rec)
+    print(line, flush=True)
+    if args.out:
+        with open(args.out, "a") as f:
+            f.write(line + "\n")
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,78 @@
+"""Build the HIP library libgemm.so (gfx950) in-tree.
+
+    python -m dense_tiled_gemm_02_amd.build [-j N]
+
+Each HIP/C++ source is compiled with hipcc for gfx950 into an object under
+_build/, then linked into dense_tiled_gemm_02_amd/libgemm.so.  Packed fp32
+vector instructions are disabled for device code.  The gfx950 assembly of
+every kernel source is also written to _build/*.s, so the compiler's resource
+report (VGPRs, AGPRs, scratch, LDS, occupancy) can be checked.
+"""
+import concurrent.futures as cf
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+BUILD = os.path.join(ROOT, "_build")
+LIB = os.path.join(PKG, "libgemm.so")
+PROBE_LIB = os.path.join(PKG, "libgemm_probe.so")
+ARCH = "gfx950"
+
+SOURCES = ["api.cpp", "gemm_tile.hip", "gemm_skinny.hip"]
+PROBE_SOURCES = ["probe.hip"]
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+COMMON = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH,
+          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-I" + CSRC, "-I" + os.path.join(ROOT, "include"), "-Wall"]
+
+
+def _run(cmd, verbose):
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    out = "\n".join(l for l in r.stdout.splitlines()
+                    if "packed-fp32-ops' is not a recognized feature" not in l
+                    and "argument unused during compilation: '--hip-link'" not in l)
+    if r.returncode != 0:
+        raise RuntimeError("command failed (%d): %s\n%s" % (r.returncode, " ".join(cmd), out))
+    if out.strip() and verbose:
+        print(out, flush=True)
+
+
+def _compile(src, verbose):
+    path = os.path.join(CSRC, src)
+    obj = os.path.join(BUILD, src + ".o")
+    lang = ["-x", "hip"] if src.endswith(".hip") else []
+    _run([HIPCC] + COMMON + lang + ["-c", path, "-o", obj], verbose)
+    if src.endswith(".hip"):
+        asm = os.path.join(BUILD, src + ".s")
+        _run([HIPCC] + COMMON + ["-x", "hip", "--cuda-device-only", "-S", path, "-o", asm], verbose)
+    return obj
+
+
+def _link(objs, out, verbose):
+    tmp = out + ".tmp%d" % os.getpid()
+    _run([HIPCC, "-shared", "-fPIC", "--offload-arch=" + ARCH, "-o", tmp] + objs, verbose)
+    os.replace(tmp, out)
+
+
+def build(verbose=False, jobs=None):
+    os.makedirs(BUILD, exist_ok=True)
+    jobs = jobs or min(8, os.cpu_count() or 1)
+    srcs = SOURCES + PROBE_SOURCES
+    with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
+        objs = dict(zip(srcs, ex.map(lambda s: _compile(s, verbose), srcs)))
+    _link([objs[s] for s in SOURCES], LIB, verbose)
+    _link([objs[s] for s in PROBE_SOURCES], PROBE_LIB, verbose)
+    return LIB
+
+
+if __name__ == "__main__":
+    j = None
+    if "-j" in sys.argv:
+        j = int(sys.argv[sys.argv.index("-j") + 1])
+    print(build(verbose="-v" in sys.argv, jobs=j))

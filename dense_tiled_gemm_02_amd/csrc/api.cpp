@@ -1,0 +1,499 @@
+// C ABI of the tiled GEMM library: validation, planner (tile-configuration
+// choice), plan cache and launch.  Declarations and the contract of every
+// entry point are in include/gemm.h.
+//
+// The planner keys its choice on every dimension the kernels tile on
+// (M, N, K), the storage type, the layout and the presence of C ("Tuning
+// Triton", section 3: a cache key that omits a tiled dimension silently serves
+// a wrong tile), and separates regimes (section 4: a skinny M wants a
+// different tile family from a square problem).  It prunes by the LDS budget
+// of the device (FlagGems "Hygon optimization", section "Software
+// pipelining": stages x (BLOCK_M + BLOCK_N) x BLOCK_K x 2 bytes).
+
+#include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <map>
+#include <memory>
+#include <mutex>
+#include <string>
+#include <tuple>
+#include <vector>
+
+#include "../../include/gemm.h"
+#include "kernels.h"
+#include "tile_order.h"
+
+struct gemm_plan {
+    gemm_problem prob;
+    gemm_device_info dev;
+    gemm_config cfg;
+    const dtg::KernelEntry* entry;      // the chosen variant
+    const dtg::KernelEntry* fallback;   // element-wise variant, for unaligned bases
+    int64_t num_pid_m, num_pid_n, grid;
+};
+
+namespace {
+
+thread_local std::string g_err;
+
+gemm_status fail(gemm_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+gemm_status fail(gemm_status st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return st;
+}
+
+gemm_status ok() { return GEMM_OK; }
+
+bool log_enabled() {
+    static const bool on = [] {
+        const char* v = getenv("GEMM_LOG");
+        return v && *v && strcmp(v, "0") != 0;
+    }();
+    return on;
+}
+
+constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
+
+gemm_status validate(const gemm_problem* p) {
+    if (!p) return fail(GEMM_ERR_INVALID_ARG, "problem is NULL");
+    if (p->M < 0 || p->N < 0 || p->K < 0)
+        return fail(GEMM_ERR_INVALID_ARG, "negative size M=%lld N=%lld K=%lld", (long long)p->M,
+                    (long long)p->N, (long long)p->K);
+    if (p->dtype != GEMM_F16 && p->dtype != GEMM_BF16)
+        return fail(GEMM_ERR_INVALID_ARG, "dtype %d is neither GEMM_F16 nor GEMM_BF16", (int)p->dtype);
+    if (p->has_c != 0 && p->has_c != 1)
+        return fail(GEMM_ERR_INVALID_ARG, "has_c must be 0 or 1, got %d", (int)p->has_c);
+    if (p->M > kMaxDim || p->N > kMaxDim || p->K > kMaxDim)
+        return fail(GEMM_ERR_UNSUPPORTED, "dimensions above 2^31-1 are not supported");
+    const int64_t rs[4] = {p->sa_m, p->sb_k, p->sc_m, p->sd_m};
+    const int64_t cs[4] = {p->sa_k, p->sb_n, p->sc_n, p->sd_n};
+    const char* nm[4] = {"A", "B", "C", "D"};
+    for (int i = 0; i < 4; ++i) {
+        if (i == 2 && !p->has_c) continue;
+        if (rs[i] < 0 || cs[i] < 0)
+            return fail(GEMM_ERR_UNSUPPORTED, "negative stride of %s", nm[i]);
+        const int64_t rows = (i == 0) ? p->M : (i == 1) ? p->K : p->M;
+        const int64_t cols = (i == 0) ? p->K : p->N;
+        if (rows == 0 || cols == 0) continue;
+        if (cs[i] != 1 && cols > 1)
+            return fail(GEMM_ERR_UNSUPPORTED,
+                        "%s column stride %lld: only row-major operands (column stride 1) are supported",
+                        nm[i], (long long)cs[i]);
+        if (i == 3 && rows > 1 && rs[i] < cols)
+            return fail(GEMM_ERR_INVALID_ARG, "D row stride %lld < N=%lld makes output rows overlap",
+                        (long long)rs[i], (long long)cols);
+    }
+    const int64_t pm = (p->M + 15) / 16, pn = (p->N + 15) / 16;
+    if (pm * pn > kMaxDim) return fail(GEMM_ERR_UNSUPPORTED, "output too large for one launch");
+    return ok();
+}
+
+bool vec_shape_ok(const gemm_problem* p) {
+    return p->K % 8 == 0 && p->N % 8 == 0 && p->sa_m % 8 == 0 && p->sb_k % 8 == 0;
+}
+
+std::vector<const dtg::KernelEntry*> all_entries() {
+    std::vector<const dtg::KernelEntry*> v;
+    int n = 0;
+    const dtg::KernelEntry* t = dtg::tile_kernel_table(&n);
+    for (int i = 0; i < n; ++i) v.push_back(&t[i]);
+    t = dtg::skinny_kernel_table(&n);
+    for (int i = 0; i < n; ++i) v.push_back(&t[i]);
+    return v;
+}
+
+bool matches(const dtg::KernelEntry* e, const gemm_config& f) {
+    return (f.kernel == 0 || f.kernel == e->family) && (f.bm == 0 || f.bm == e->bm) &&
+           (f.bn == 0 || f.bn == e->bn) && (f.bk == 0 || f.bk == e->bk) &&
+           (f.stages == 0 || f.stages == e->stages) && (f.mfma == 0 || f.mfma == e->mfma) &&
+           (f.waves_m == 0 || f.waves_m == e->waves_m) && (f.waves_n == 0 || f.waves_n == e->waves_n) &&
+           (f.splitk == 0 || f.splitk == e->splitk);
+}
+
+// The first compiled variant that fits the device and matches `want`.
+const dtg::KernelEntry* find_entry(const gemm_config& want, int dtype, int vec,
+                                   const gemm_device_info& dev) {
+    for (const dtg::KernelEntry* e : all_entries()) {
+        if (e->dtype != dtype || e->vec != vec) continue;
+        if (e->lds_bytes > dev.lds_per_wg) continue;
+        if (matches(e, want)) return e;
+    }
+    return nullptr;
+}
+
+gemm_config cfg_of(int fam, int bm, int bn, int bk, int st, int mf, int wm, int wn) {
+    gemm_config c;
+    memset(&c, 0, sizeof c);
+    c.kernel = fam; c.bm = bm; c.bn = bn; c.bk = bk; c.stages = st; c.mfma = mf;
+    c.waves_m = wm; c.waves_n = wn; c.splitk = 1;
+    return c;
+}
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Measured choices for exact problem keys (M, N, K, dtype, has_c).  Anything
+// not listed falls back to the regime heuristic below.
+struct TunedKey {
+    int64_t M, N, K;
+    int dtype, has_c;
+    gemm_config cfg;
+    int group_m, xcd;
+};
+const std::vector<TunedKey>& tuned_table() {
+    static const std::vector<TunedKey> t = {};
+    return t;
+}
+
+// Regime heuristic.  Square / tail problems take the largest tile that still
+// gives every CU at least one workgroup; skinny M takes a short-M tile.
+gemm_config heuristic(const gemm_problem* p, const gemm_device_info& dev, int* group_m) {
+    const int64_t M = p->M, N = p->N;
+    *group_m = 8;
+    if (M <= 16) return cfg_of(dtg::KF_TILE, 16, 64, 64, 2, 16, 1, 4);
+    if (M <= 32) return cfg_of(dtg::KF_TILE, 32, 32, 32, 2, 16, 2, 2);
+    struct C { int bm, bn, bk, st, mf, wm, wn; };
+    static const C ladder[] = {
+        {256, 256, 64, 2, 16, 2, 4}, {256, 128, 64, 2, 16, 2, 2}, {128, 128, 64, 2, 16, 2, 2},
+        {64, 64, 64, 2, 16, 2, 2},   {32, 32, 32, 2, 16, 2, 2},
+    };
+    const C* best = nullptr;
+    int64_t best_tiles = -1;
+    for (const C& c : ladder) {
+        const int64_t tiles = cdiv(M, c.bm) * cdiv(N, c.bn);
+        if (tiles >= dev.cu_count) { best = &c; break; }
+        if (tiles > best_tiles) { best_tiles = tiles; best = &c; }
+    }
+    return cfg_of(dtg::KF_TILE, best->bm, best->bn, best->bk, best->st, best->mf, best->wm, best->wn);
+}
+
+gemm_status plan_impl(const gemm_problem* prob, const gemm_device_info* dev, const gemm_config* force,
+                      gemm_plan** out) {
+    if (!out) return fail(GEMM_ERR_INVALID_ARG, "out is NULL");
+    *out = nullptr;
+    gemm_status st = validate(prob);
+    if (st != GEMM_OK) return st;
+    if (!dev) return fail(GEMM_ERR_INVALID_ARG, "device info is NULL");
+    if (dev->cu_count <= 0 || dev->lds_per_wg <= 0)
+        return fail(GEMM_ERR_INVALID_ARG, "device info has no CUs or no LDS");
+
+    const bool vec = vec_shape_ok(prob);
+    int group_m = 8, xcd = 1;
+    gemm_config want;
+    bool tuned = false;
+    for (const TunedKey& t : tuned_table()) {
+        if (t.M == prob->M && t.N == prob->N && t.K == prob->K && t.dtype == prob->dtype &&
+            t.has_c == prob->has_c) {
+            want = t.cfg;
+            group_m = t.group_m;
+            xcd = t.xcd;
+            tuned = true;
+            break;
+        }
+    }
+    if (!tuned) want = heuristic(prob, *dev, &group_m);
+    if (force) {
+        // Any forced tile field replaces the planner's tile; the tile fields
+        // left at 0 are then free (the first compiled variant that matches).
+        const gemm_config& f = *force;
+        if (f.group_m < 0 || f.xcd_remap < 0 || f.xcd_remap > 2)
+            return fail(GEMM_ERR_INVALID_ARG, "group_m must be >= 0 and xcd_remap one of 0, 1, 2");
+        if (f.bm || f.bn || f.bk || f.mfma || f.waves_m || f.waves_n || f.stages || f.kernel || f.splitk)
+            want = f;
+        if (f.group_m) group_m = f.group_m;
+        if (f.xcd_remap) xcd = (f.xcd_remap == GEMM_XCD_ON);
+    }
+    const dtg::KernelEntry* e = nullptr;
+    if (vec) e = find_entry(want, prob->dtype, 1, *dev);
+    const dtg::KernelEntry* fb = find_entry(cfg_of(dtg::KF_TILE, 0, 0, 0, 0, 16, 0, 0), prob->dtype, 0, *dev);
+    if (!e) {
+        if (!vec && (!force || want.kernel == 0 || want.kernel == dtg::KF_TILE)) {
+            // element-wise path: any shape, any alignment (16x16x32 instruction)
+            if (force && (want.bm || want.bn || want.bk || want.mfma == 32))
+                e = find_entry(want, prob->dtype, 0, *dev);
+            else
+                e = fb;
+        }
+        if (!e)
+            return fail(GEMM_ERR_UNSUPPORTED,
+                        "no compiled kernel for bm=%d bn=%d bk=%d stages=%d mfma=%d waves=%dx%d kernel=%d "
+                        "(dtype %d, vector path %d) within %lld bytes of LDS",
+                        want.bm, want.bn, want.bk, want.stages, want.mfma, want.waves_m, want.waves_n,
+                        want.kernel, (int)prob->dtype, (int)vec, (long long)dev->lds_per_wg);
+    }
+    gemm_plan* pl = new (std::nothrow) gemm_plan;
+    if (!pl) return fail(GEMM_ERR_INVALID_ARG, "out of host memory");
+    pl->prob = *prob;
+    pl->dev = *dev;
+    pl->entry = e;
+    pl->fallback = fb;
+    pl->num_pid_m = cdiv(prob->M, e->bm);
+    pl->num_pid_n = cdiv(prob->N, e->bn);
+    pl->grid = pl->num_pid_m * pl->num_pid_n;
+    if (group_m < 1) group_m = 1;
+    gemm_config& c = pl->cfg;
+    c = cfg_of(e->family, e->bm, e->bn, e->bk, e->stages, e->mfma, e->waves_m, e->waves_n);
+    c.splitk = e->splitk;
+    c.group_m = group_m;
+    c.xcd_remap = (xcd && dev->xcd_count > 1) ? GEMM_XCD_ON : GEMM_XCD_OFF;
+    if (log_enabled()) {
+        char buf[512];
+        gemm_plan_describe(pl, buf, sizeof buf);
+        fprintf(stderr, "[gemm] M=%lld N=%lld K=%lld dtype=%d has_c=%d: %s%s\n", (long long)prob->M,
+                (long long)prob->N, (long long)prob->K, (int)prob->dtype, (int)prob->has_c, buf,
+                tuned ? " (tuned)" : "");
+    }
+    *out = pl;
+    return ok();
+}
+
+std::mutex g_dev_mu;
+std::map<int, gemm_device_info> g_dev_cache;
+
+gemm_status device_info_cached(int device, gemm_device_info* info) {
+    std::lock_guard<std::mutex> lk(g_dev_mu);
+    auto it = g_dev_cache.find(device);
+    if (it != g_dev_cache.end()) {
+        *info = it->second;
+        return ok();
+    }
+    gemm_status st = gemm_device_query(device, info);
+    if (st == GEMM_OK) g_dev_cache[device] = *info;
+    return st;
+}
+
+// byte range [lo, hi) a row-major rows x cols matrix occupies
+void span(const void* p, int64_t rows, int64_t cols, int64_t ld, uintptr_t* lo, uintptr_t* hi) {
+    *lo = reinterpret_cast<uintptr_t>(p);
+    *hi = *lo + static_cast<uintptr_t>(((rows - 1) * ld + cols) * 2);
+}
+
+bool overlaps(uintptr_t a0, uintptr_t a1, uintptr_t b0, uintptr_t b1) { return a0 < b1 && b0 < a1; }
+
+struct CacheKey {
+    int device;
+    int64_t f[12];
+    bool operator<(const CacheKey& o) const {
+        if (device != o.device) return device < o.device;
+        return memcmp(f, o.f, sizeof f) < 0;
+    }
+};
+std::mutex g_cache_mu;
+std::map<CacheKey, std::unique_ptr<gemm_plan>> g_cache;
+
+}  // namespace
+
+extern "C" {
+
+const char* gemm_status_string(gemm_status s) {
+    switch (s) {
+        case GEMM_OK: return "GEMM_OK";
+        case GEMM_ERR_INVALID_ARG: return "GEMM_ERR_INVALID_ARG";
+        case GEMM_ERR_UNSUPPORTED: return "GEMM_ERR_UNSUPPORTED";
+        case GEMM_ERR_HIP: return "GEMM_ERR_HIP";
+        case GEMM_ERR_WORKSPACE: return "GEMM_ERR_WORKSPACE";
+    }
+    return "GEMM_ERR_UNKNOWN";
+}
+
+const char* gemm_last_error(void) { return g_err.c_str(); }
+
+gemm_status gemm_device_query(int device, gemm_device_info* info) {
+    if (!info) return fail(GEMM_ERR_INVALID_ARG, "info is NULL");
+    hipDeviceProp_t prop;
+    hipError_t e = hipGetDeviceProperties(&prop, device);
+    if (e != hipSuccess)
+        return fail(GEMM_ERR_HIP, "hipGetDeviceProperties(%d): %s", device, hipGetErrorString(e));
+    memset(info, 0, sizeof *info);
+    int arch = 0;
+    if (sscanf(prop.gcnArchName, "gfx%d", &arch) != 1) arch = 0;
+    info->arch = arch;
+    info->cu_count = prop.multiProcessorCount;
+    info->clock_khz = prop.clockRate;
+    info->lds_per_cu = static_cast<int64_t>(prop.maxSharedMemoryPerMultiProcessor);
+    info->lds_per_wg = static_cast<int64_t>(prop.sharedMemPerBlock);
+    if (prop.sharedMemPerBlockOptin > prop.sharedMemPerBlock)
+        info->lds_per_wg = static_cast<int64_t>(prop.sharedMemPerBlockOptin);
+    if (info->lds_per_cu > 0 && info->lds_per_wg > info->lds_per_cu) info->lds_per_wg = info->lds_per_cu;
+    info->wave_size = prop.warpSize;
+    int xccs = 1;
+    if (hipDeviceGetAttribute(&xccs, hipDeviceAttributeNumberOfXccs, device) != hipSuccess || xccs < 1)
+        xccs = 1;
+    info->xcd_count = xccs;
+    if (arch != 950)
+        return fail(GEMM_ERR_UNSUPPORTED, "device %d is %s; the kernels are built for gfx950", device,
+                    prop.gcnArchName);
+    if (prop.warpSize != 64) return fail(GEMM_ERR_UNSUPPORTED, "wave size %d, expected 64", prop.warpSize);
+    return ok();
+}
+
+gemm_status gemm_plan_create_for(const gemm_problem* prob, const gemm_device_info* info,
+                                 const gemm_config* force, gemm_plan** out) {
+    return plan_impl(prob, info, force, out);
+}
+
+gemm_status gemm_plan_create(const gemm_problem* prob, int device, const gemm_config* force,
+                             gemm_plan** out) {
+    if (out) *out = nullptr;
+    gemm_status st = validate(prob);
+    if (st != GEMM_OK) return st;
+    gemm_device_info info;
+    st = device_info_cached(device, &info);
+    if (st != GEMM_OK) return st;
+    return plan_impl(prob, &info, force, out);
+}
+
+void gemm_plan_destroy(gemm_plan* plan) { delete plan; }
+
+gemm_status gemm_plan_config(const gemm_plan* plan, gemm_config* out) {
+    if (!plan || !out) return fail(GEMM_ERR_INVALID_ARG, "plan or out is NULL");
+    *out = plan->cfg;
+    return ok();
+}
+
+gemm_status gemm_plan_launch(const gemm_plan* plan, int64_t* grid, int32_t* threads, int64_t* lds) {
+    if (!plan) return fail(GEMM_ERR_INVALID_ARG, "plan is NULL");
+    if (grid) *grid = plan->grid;
+    if (threads) *threads = plan->entry->threads;
+    if (lds) *lds = plan->entry->lds_bytes;
+    return ok();
+}
+
+gemm_status gemm_plan_describe(const gemm_plan* plan, char* buf, size_t len) {
+    if (!plan || !buf || len == 0) return fail(GEMM_ERR_INVALID_ARG, "plan or buf is NULL");
+    const gemm_config& c = plan->cfg;
+    snprintf(buf, len,
+             "kernel=%s bm=%d bn=%d bk=%d stages=%d mfma=%d waves=%dx%d group_m=%d splitk=%d xcd_remap=%d "
+             "grid=%lld threads=%d lds=%lld vec=%d",
+             plan->entry->name, c.bm, c.bn, c.bk, c.stages, c.mfma, c.waves_m, c.waves_n, c.group_m,
+             c.splitk, c.xcd_remap, (long long)plan->grid, plan->entry->threads,
+             (long long)plan->entry->lds_bytes, plan->entry->vec);
+    return ok();
+}
+
+gemm_status gemm_workspace_size(const gemm_plan* plan, size_t* bytes) {
+    if (!plan || !bytes) return fail(GEMM_ERR_INVALID_ARG, "plan or bytes is NULL");
+    *bytes = 0;
+    return ok();
+}
+
+gemm_status gemm_run(const gemm_plan* plan, const void* A, const void* B, const void* C, void* D,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+    (void)workspace;
+    (void)workspace_bytes;
+    if (!plan) return fail(GEMM_ERR_INVALID_ARG, "plan is NULL");
+    const gemm_problem& p = plan->prob;
+    if (p.has_c && !C) return fail(GEMM_ERR_INVALID_ARG, "problem has C but C is NULL");
+    if (!p.has_c && C) return fail(GEMM_ERR_INVALID_ARG, "C given but the problem has has_c = 0");
+    if (p.M == 0 || p.N == 0) return ok();
+    if (!D) return fail(GEMM_ERR_INVALID_ARG, "D is NULL");
+    if (p.K > 0 && (!A || !B)) return fail(GEMM_ERR_INVALID_ARG, "A or B is NULL");
+    uintptr_t d0, d1;
+    span(D, p.M, p.N, p.sd_m, &d0, &d1);
+    if (p.K > 0) {
+        uintptr_t a0, a1, b0, b1;
+        span(A, p.M, p.K, p.sa_m, &a0, &a1);
+        span(B, p.K, p.N, p.sb_k, &b0, &b1);
+        if (overlaps(d0, d1, a0, a1)) return fail(GEMM_ERR_INVALID_ARG, "D overlaps A");
+        if (overlaps(d0, d1, b0, b1)) return fail(GEMM_ERR_INVALID_ARG, "D overlaps B");
+    }
+    if (p.has_c) {
+        uintptr_t c0, c1;
+        span(C, p.M, p.N, p.sc_m, &c0, &c1);
+        const bool same = (C == D) && (p.sc_m == p.sd_m || p.M == 1);
+        if (!same && overlaps(d0, d1, c0, c1))
+            return fail(GEMM_ERR_INVALID_ARG, "D overlaps C (only D == C with equal strides is allowed)");
+    }
+    const dtg::KernelEntry* e = plan->entry;
+    if (e->vec && p.K > 0 &&
+        ((reinterpret_cast<uintptr_t>(A) & 15) || (reinterpret_cast<uintptr_t>(B) & 15)))
+        e = plan->fallback;   // element-wise loads; bitwise identical for 16x16x32 plans
+    dtg::KArgs a;
+    a.A = static_cast<const uint16_t*>(A);
+    a.B = static_cast<const uint16_t*>(B);
+    a.C = static_cast<const uint16_t*>(C);
+    a.D = static_cast<uint16_t*>(D);
+    a.M = static_cast<int32_t>(p.M);
+    a.N = static_cast<int32_t>(p.N);
+    a.K = static_cast<int32_t>(p.K);
+    a.num_pid_m = static_cast<int32_t>((p.M + e->bm - 1) / e->bm);
+    a.num_pid_n = static_cast<int32_t>((p.N + e->bn - 1) / e->bn);
+    a.group_m = plan->cfg.group_m;
+    a.xcds = (plan->cfg.xcd_remap == GEMM_XCD_ON) ? plan->dev.xcd_count : 1;
+    a.has_c = p.has_c;
+    a.lda = p.sa_m;
+    a.ldb = p.sb_k;
+    a.ldc = p.has_c ? p.sc_m : 0;
+    a.ldd = p.sd_m;
+    const int64_t grid = static_cast<int64_t>(a.num_pid_m) * a.num_pid_n;
+    hipError_t err = e->launch(a, grid, static_cast<hipStream_t>(stream));
+    if (err != hipSuccess) return fail(GEMM_ERR_HIP, "launch of %s: %s", e->name, hipGetErrorString(err));
+    return ok();
+}
+
+gemm_status gemm(const void* A, const void* B, const void* C, void* D, int64_t M, int64_t N, int64_t K,
+                 const int64_t strides[8], gemm_dtype dtype, int32_t has_c, void* stream) {
+    if (!strides) return fail(GEMM_ERR_INVALID_ARG, "strides is NULL");
+    gemm_problem p;
+    p.M = M; p.N = N; p.K = K;
+    p.sa_m = strides[0]; p.sa_k = strides[1]; p.sb_k = strides[2]; p.sb_n = strides[3];
+    p.sc_m = strides[4]; p.sc_n = strides[5]; p.sd_m = strides[6]; p.sd_n = strides[7];
+    p.dtype = dtype;
+    p.has_c = has_c;
+    int device = 0;
+    hipError_t e = hipGetDevice(&device);
+    if (e != hipSuccess) return fail(GEMM_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    CacheKey key;
+    key.device = device;
+    const int64_t f[12] = {M, N, K, p.sa_m, p.sa_k, p.sb_k, p.sb_n,
+                           has_c ? p.sc_m : 0, has_c ? p.sc_n : 0, p.sd_m, p.sd_n,
+                           (int64_t)dtype * 2 + has_c};
+    memcpy(key.f, f, sizeof f);
+    const gemm_plan* plan = nullptr;
+    {
+        std::lock_guard<std::mutex> lk(g_cache_mu);
+        auto it = g_cache.find(key);
+        if (it != g_cache.end()) {
+            plan = it->second.get();
+        } else {
+            gemm_plan* np = nullptr;
+            gemm_status st = gemm_plan_create(&p, device, nullptr, &np);
+            if (st != GEMM_OK) return st;
+            g_cache[key].reset(np);
+            plan = np;
+        }
+    }
+    return gemm_run(plan, A, B, C, D, nullptr, 0, stream);
+}
+
+void gemm_cache_clear(void) {
+    std::lock_guard<std::mutex> lk(g_cache_mu);
+    g_cache.clear();
+}
+
+int64_t gemm_lds_bytes(int32_t bm, int32_t bn, int32_t bk, int32_t stages, gemm_dtype dtype) {
+    if (bm <= 0 || bn <= 0 || bk <= 0 || stages <= 0) return -1;
+    if (dtype != GEMM_F16 && dtype != GEMM_BF16) return -1;
+    return static_cast<int64_t>(stages) * (bm + bn) * bk * 2;
+}
+
+gemm_status gemm_tile_of_workgroup(int64_t wg, int64_t num_pid_m, int64_t num_pid_n, int32_t group_m,
+                                   int32_t xcd_count, int64_t* pid_m, int64_t* pid_n) {
+    if (!pid_m || !pid_n) return fail(GEMM_ERR_INVALID_ARG, "output pointer is NULL");
+    if (num_pid_m <= 0 || num_pid_n <= 0 || group_m <= 0 || xcd_count <= 0)
+        return fail(GEMM_ERR_INVALID_ARG, "grid sizes, group_m and xcd_count must be positive");
+    if (wg < 0 || wg >= num_pid_m * num_pid_n) return fail(GEMM_ERR_INVALID_ARG, "workgroup outside the grid");
+    dtg::tile_of_workgroup<int64_t>(wg, num_pid_m, num_pid_n, group_m, xcd_count, pid_m, pid_n);
+    return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,46 @@
+// Internal interface between the planner / C ABI and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dtg {
+
+// Arguments of every GEMM kernel.  Row-major operands; leading strides in
+// elements.  M, N, K < 2^31 (the planner rejects larger).
+struct KArgs {
+    const uint16_t* A;
+    const uint16_t* B;
+    const uint16_t* C;   // nullptr unless has_c
+    uint16_t* D;
+    int32_t M, N, K;
+    int32_t num_pid_m, num_pid_n;
+    int32_t group_m;
+    int32_t xcds;        // 1: no XCD pre-permutation
+    int32_t has_c;
+    int64_t lda, ldb, ldc, ldd;
+};
+
+typedef hipError_t (*launch_fn)(const KArgs& args, int64_t grid, hipStream_t stream);
+
+enum KernelFamily { KF_TILE = 1, KF_SKINNY = 2 };
+
+// One compiled kernel variant.  vec = 1: 16-byte vector loads (requires
+// K % 8 == 0, N % 8 == 0, lda % 8 == 0, ldb % 8 == 0 and 16-byte aligned A, B);
+// vec = 0: element loads, any shape.
+struct KernelEntry {
+    int32_t family;
+    int32_t bm, bn, bk, stages, mfma, waves_m, waves_n, splitk;
+    int32_t dtype;       // 0 fp16, 1 bf16
+    int32_t vec;
+    int32_t threads;
+    int64_t lds_bytes;
+    launch_fn launch;
+    const char* name;
+};
+
+// All compiled variants (tile kernels followed by skinny kernels).
+const KernelEntry* tile_kernel_table(int* count);
+const KernelEntry* skinny_kernel_table(int* count);
+
+}  // namespace dtg

@@ -1,0 +1,95 @@
+// Single-instruction probe kernels (test support, built into libgemm_probe.so).
+//
+// probe_mfma runs ONE matrix instruction in one wavefront with the operand and
+// result lane layouts the tile kernel assumes, on a small A (rows x k) and
+// B (k x cols) given in row-major order, and writes the rows x cols result in
+// row-major order.  A test with exact integer inputs then pins those layouts
+// (the single-instruction kernel of "DCU K100 节点初探", section 5.4, used as a
+// layout check).
+//
+// probe_lds_read_tr fills 1024 bytes of LDS from `in` and has every lane run one
+// transposing 64-bit LDS read at byte address 8 * lane; the 4 halfwords each
+// lane receives are written to out[4 * lane + 0..3].  It reports the lane
+// mapping of that instruction; every address is inside the 1024 bytes.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+template <int MF, bool BF16>
+__global__ __launch_bounds__(64) void probe_mfma_kernel(const uint16_t* A, const uint16_t* B, float* D) {
+    constexpr int KI = (MF == 16) ? 32 : 16;
+    const int l = threadIdx.x;
+    const int rc = l % MF, g = l / MF;
+    uint16_t a[8], b[8];
+    for (int t = 0; t < 8; ++t) {
+        a[t] = A[rc * KI + 8 * g + t];       // A row rc, k = 8g + t
+        b[t] = B[(8 * g + t) * MF + rc];     // B column rc, k = 8g + t
+    }
+    u32x4 av, bv;
+    for (int d = 0; d < 4; ++d) {
+        av[d] = a[2 * d] | (static_cast<uint32_t>(a[2 * d + 1]) << 16);
+        bv[d] = b[2 * d] | (static_cast<uint32_t>(b[2 * d + 1]) << 16);
+    }
+    if constexpr (MF == 16) {
+        f32x4 c = {0, 0, 0, 0};
+        if constexpr (BF16)
+            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av),
+                                                        __builtin_bit_cast(bf16x8, bv), c, 0, 0, 0);
+        else
+            c = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, av),
+                                                       __builtin_bit_cast(f16x8, bv), c, 0, 0, 0);
+        for (int r = 0; r < 4; ++r) D[(4 * g + r) * 16 + rc] = c[r];
+    } else {
+        f32x16 c = {};
+        if constexpr (BF16)
+            c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av),
+                                                        __builtin_bit_cast(bf16x8, bv), c, 0, 0, 0);
+        else
+            c = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, av),
+                                                       __builtin_bit_cast(f16x8, bv), c, 0, 0, 0);
+        for (int r = 0; r < 16; ++r) D[(8 * (r / 4) + 4 * g + (r % 4)) * 32 + rc] = c[r];
+    }
+}
+
+__global__ __launch_bounds__(64) void probe_lds_read_tr_kernel(const uint16_t* in, uint16_t* out) {
+    __shared__ __attribute__((aligned(16))) uint16_t lds[512];
+    const int l = threadIdx.x;
+    for (int i = l; i < 512; i += 64) lds[i] = in[i];
+    __syncthreads();
+    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+    i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(lds + 4 * l));
+    for (int i = 0; i < 4; ++i) out[4 * l + i] = static_cast<uint16_t>(v[i]);
+}
+
+}  // namespace
+
+extern "C" {
+
+// mf: 16 (A 16x32, B 32x16, D 16x16) or 32 (A 32x16, B 16x32, D 32x32).
+// dtype: 0 fp16, 1 bf16.  All pointers are device pointers.  Returns a
+// hipError_t value (0 = success); the kernel runs on `stream`.
+int probe_mfma(int mf, int dtype, const uint16_t* A, const uint16_t* B, float* D, void* stream) {
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (mf == 16 && dtype == 1) hipLaunchKernelGGL((probe_mfma_kernel<16, true>), dim3(1), dim3(64), 0, s, A, B, D);
+    else if (mf == 16 && dtype == 0) hipLaunchKernelGGL((probe_mfma_kernel<16, false>), dim3(1), dim3(64), 0, s, A, B, D);
+    else if (mf == 32 && dtype == 1) hipLaunchKernelGGL((probe_mfma_kernel<32, true>), dim3(1), dim3(64), 0, s, A, B, D);
+    else if (mf == 32 && dtype == 0) hipLaunchKernelGGL((probe_mfma_kernel<32, false>), dim3(1), dim3(64), 0, s, A, B, D);
+    else return static_cast<int>(hipErrorInvalidValue);
+    return static_cast<int>(hipGetLastError());
+}
+
+// in: 512 halfwords, out: 256 halfwords (device pointers).
+int probe_lds_read_tr(const uint16_t* in, uint16_t* out, void* stream) {
+    hipLaunchKernelGGL(probe_lds_read_tr_kernel, dim3(1), dim3(64), 0, static_cast<hipStream_t>(stream), in, out);
+    return static_cast<int>(hipGetLastError());
+}
+
+}  // extern "C"

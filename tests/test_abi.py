@@ -1,0 +1,192 @@
+"""Host-side tests of the C ABI and planner (CPU only: no kernel is launched).
+
+The planner is a pure function of (problem, device facts), so it is tested
+with a hand-made gfx950 device description: 256 CUs, 8 XCDs, 2.4 GHz,
+160 KiB of LDS per CU.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import dense_tiled_gemm_02_amd as g
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def fake_gfx950():
+    d = g.gemm_device_info()
+    d.arch, d.cu_count, d.xcd_count, d.clock_khz = 950, 256, 8, 2400000
+    d.lds_per_cu = d.lds_per_wg = 160 * 1024
+    d.wave_size = 64
+    return d
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "gemm.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(gemm\w*)\s*\(", src, flags=re.M)))
+
+
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert len(names) >= 14
+    L = g.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert sorted(n for n, _, _ in g.SIGNATURES) == names
+
+
+def test_status_strings():
+    assert g.gemm_status_string(g.GEMM_OK) == "GEMM_OK"
+    assert g.gemm_status_string(g.GEMM_ERR_UNSUPPORTED) == "GEMM_ERR_UNSUPPORTED"
+    assert g.gemm_status_string(99) == "GEMM_ERR_UNKNOWN"
+
+
+def test_lds_formula_worked_value():
+    # FlagGems "Hygon optimization", section "Software pipelining": one A/B tile
+    # pair of 64 x 64 x 32 fp16 is 8 KiB.
+    assert g.gemm_lds_bytes(64, 64, 32, 1, g.GEMM_F16) == 8 * 1024
+    assert g.gemm_lds_bytes(64, 64, 32, 2, g.GEMM_F16) == 16 * 1024
+    assert g.gemm_lds_bytes(256, 256, 64, 2, g.GEMM_BF16) == 128 * 1024
+    assert g.gemm_lds_bytes(0, 64, 32, 1, g.GEMM_F16) == -1
+
+
+@pytest.mark.parametrize("npm,npn,gm", [(5, 3, 2), (16, 16, 8), (7, 11, 4), (1, 9, 8), (9, 1, 1),
+                                        (32, 24, 8), (13, 13, 3)])
+def test_tile_order_matches_enumerated_grouped_order(npm, npn, gm):
+    want = oracle.grouped_order(npm, npn, gm)
+    got = [g.gemm_tile_of_workgroup(w, npm, npn, gm, 1) for w in range(npm * npn)]
+    assert got == want
+
+
+@pytest.mark.parametrize("npm,npn,gm,x", [(16, 16, 8, 8), (32, 24, 8, 8), (5, 3, 2, 8), (7, 11, 4, 8),
+                                          (3, 3, 1, 8), (10, 13, 4, 3)])
+def test_xcd_permutation_is_a_bijection_with_contiguous_ranges(npm, npn, gm, x):
+    grid = npm * npn
+    order = oracle.grouped_order(npm, npn, gm)
+    pos_of = {t: i for i, t in enumerate(order)}
+    tiles = [g.gemm_tile_of_workgroup(w, npm, npn, gm, x) for w in range(grid)]
+    assert sorted(tiles) == sorted(order)            # every tile exactly once
+    # workgroups of one die (w % x) cover one contiguous run of the tile order
+    for die in range(x):
+        ps = sorted(pos_of[tiles[w]] for w in range(die, grid, x))
+        assert ps == list(range(ps[0], ps[0] + len(ps))) if ps else True
+        # and in dispatch order
+        assert [pos_of[tiles[w]] for w in range(die, grid, x)] == ps
+
+
+def test_tile_order_rejects_bad_arguments():
+    with pytest.raises(g.GemmError) as e:
+        g.gemm_tile_of_workgroup(9, 3, 3, 1, 1)
+    assert e.value.status == g.GEMM_ERR_INVALID_ARG
+    with pytest.raises(g.GemmError):
+        g.gemm_tile_of_workgroup(0, 3, 3, 0, 1)
+
+
+def plan(M, N, K, dt=g.GEMM_BF16, has_c=False, force=None, **ld):
+    return g.gemm_plan_create_for(g.problem(M, N, K, dt, has_c, **ld), fake_gfx950(), force)
+
+
+def test_plans_for_the_five_workloads_fit_the_device():
+    cases = [(256, 256, 256, g.GEMM_F16, False), (1024, 1024, 1024, g.GEMM_F16, False),
+             (4096, 4096, 4096, g.GEMM_BF16, False), (16, 8192, 8192, g.GEMM_BF16, False),
+             (4000, 3000, 1000, g.GEMM_F16, True)]
+    for M, N, K, dt, c in cases:
+        p = plan(M, N, K, dt, c)
+        cfg = p.config
+        grid, threads, lds = g.gemm_plan_launch(p)
+        assert lds <= 160 * 1024
+        assert threads % 64 == 0 and threads <= 1024
+        assert grid == -(-M // cfg.bm) * -(-N // cfg.bn) * (cfg.splitk if cfg.kernel == 2 else 1) or cfg.kernel == 2
+        assert lds == g.gemm_lds_bytes(cfg.bm, cfg.bn, cfg.bk, cfg.stages, dt) or cfg.kernel == 2
+        assert "kernel=" in p.describe()
+
+
+def test_key_includes_m():
+    # "Tuning Triton", section 3: M=1 and M=4096 with equal N, K must not share a tile.
+    big = plan(4096, 4096, 4096).config
+    small = plan(1, 4096, 4096).config
+    assert (big.bm, big.bn, big.kernel) != (small.bm, small.bn, small.kernel)
+    assert small.bm <= 16
+
+
+def test_forced_config_is_honoured_or_rejected():
+    p = plan(1024, 1024, 1024, g.GEMM_F16, force={"bm": 128, "bn": 128, "bk": 64, "mfma": 32})
+    c = p.config
+    assert (c.bm, c.bn, c.bk, c.mfma) == (128, 128, 64, 32)
+    p = plan(1024, 1024, 1024, force={"group_m": 4, "xcd_remap": g.GEMM_XCD_OFF})
+    assert p.config.group_m == 4 and p.config.xcd_remap == g.GEMM_XCD_OFF
+    with pytest.raises(g.GemmError) as e:
+        plan(1024, 1024, 1024, force={"bm": 48})
+    assert e.value.status == g.GEMM_ERR_UNSUPPORTED
+    small = fake_gfx950()
+    small.lds_per_wg = 64 * 1024
+    with pytest.raises(g.GemmError) as e:
+        g.gemm_plan_create_for(g.problem(4096, 4096, 4096, g.GEMM_BF16), small, {"bm": 256, "bn": 256})
+    assert e.value.status == g.GEMM_ERR_UNSUPPORTED
+
+
+def test_unaligned_shapes_take_the_element_path():
+    p = plan(100, 30, 17, g.GEMM_F16)
+    assert "VEC" not in p.describe()
+    assert p.describe().endswith("vec=0")
+    p = plan(128, 64, 64, g.GEMM_F16)
+    assert p.describe().endswith("vec=1")
+
+
+def test_validation_errors():
+    info = fake_gfx950()
+
+    def status(prob, force=None):
+        h = ctypes.c_void_p()
+        s = g.lib().gemm_plan_create_for(ctypes.byref(prob), ctypes.byref(info), None, ctypes.byref(h))
+        if h.value:
+            g.lib().gemm_plan_destroy(h)
+        return s
+
+    assert status(g.problem(-1, 4, 4, g.GEMM_F16)) == g.GEMM_ERR_INVALID_ARG
+    p = g.problem(4, 4, 4, g.GEMM_F16)
+    p.dtype = 7
+    assert status(p) == g.GEMM_ERR_INVALID_ARG
+    p = g.problem(4, 4, 4, g.GEMM_F16)
+    p.has_c = 2
+    assert status(p) == g.GEMM_ERR_INVALID_ARG
+    p = g.problem(4, 4, 4, g.GEMM_F16)
+    p.sa_k = 2                                   # column-strided A: not this version
+    assert status(p) == g.GEMM_ERR_UNSUPPORTED
+    assert "column stride" in g.gemm_last_error()
+    p = g.problem(4, 8, 4, g.GEMM_F16, ldd=4)    # output rows would overlap
+    assert status(p) == g.GEMM_ERR_INVALID_ARG
+    p = g.problem(1 << 31, 4, 4, g.GEMM_F16)
+    assert status(p) == g.GEMM_ERR_UNSUPPORTED
+    assert status(g.problem(0, 4, 4, g.GEMM_F16)) == g.GEMM_OK
+    assert status(g.problem(4, 4, 0, g.GEMM_BF16, True)) == g.GEMM_OK
+    assert g.lib().gemm_plan_create_for(None, ctypes.byref(info), None,
+                                        ctypes.byref(ctypes.c_void_p())) == g.GEMM_ERR_INVALID_ARG
+
+
+def test_run_rejects_bad_pointers_without_launching():
+    p = plan(64, 64, 64, g.GEMM_F16, True)
+    with pytest.raises(g.GemmError) as e:
+        g.gemm_run(p, 4096, 8192, None, 1 << 20)         # C missing
+    assert e.value.status == g.GEMM_ERR_INVALID_ARG
+    p = plan(64, 64, 64, g.GEMM_F16)
+    with pytest.raises(g.GemmError):
+        g.gemm_run(p, 4096, 8192, 1 << 24, 1 << 20)      # C given, problem has none
+    with pytest.raises(g.GemmError) as e:
+        g.gemm_run(p, 1 << 20, 1 << 24, None, (1 << 20) + 64)   # D overlaps A
+    assert "overlaps A" in e.value.detail
+    with pytest.raises(g.GemmError):
+        g.gemm_run(p, 1 << 20, 1 << 24, None, None)      # D missing
+    # M = 0: nothing to do, nothing launched, even with no pointers
+    g.gemm_run(plan(0, 64, 64, g.GEMM_F16), None, None, None, None)
+
+
+def test_in_place_addend_allowed_only_with_equal_strides():
+    p = plan(64, 64, 64, g.GEMM_F16, True)
+    with pytest.raises(g.GemmError) as e:
+        g.gemm_run(p, 1 << 20, 1 << 24, (1 << 28) + 2, 1 << 28)   # shifted alias
+    assert "overlaps C" in e.value.detail

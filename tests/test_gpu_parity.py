@@ -1,0 +1,234 @@
+"""Parity of the HIP path with the CPU oracle (GPU).
+
+Every output must satisfy |d - ref| <= ulp_out(ref) + 2^-20 * sum_k |a_ik b_kj|
+against the binary64 oracle on the same stored inputs; exact cases (identity,
+integer inputs, dyadic rank-1) must match the correctly rounded exact result
+bit for bit.  Sizes span several tiles and ragged tails; the large workloads
+are checked in full where the oracle is fast and on sampled outputs otherwise,
+in the launch configuration the benchmark times.
+"""
+import itertools
+
+import numpy as np
+import pytest
+import torch
+
+import dense_tiled_gemm_02_amd as g
+import gemm_inputs
+import oracle
+from helpers import DT_CODE, check, gpu_run, sample_positions
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    assert torch.cuda.is_available(), "GPU test run without a GPU"
+    torch.cuda.init()
+
+
+def _inputs(M, N, K, dt, has_c, seed, dist="uniform", scale=1.0):
+    A = gemm_inputs.draw((M, K), seed, dt, dist, scale)
+    B = gemm_inputs.draw((K, N), seed + 1, dt, dist, scale)
+    C = gemm_inputs.draw((M, N), seed + 2, dt, dist, scale) if has_c else None
+    return A, B, C
+
+
+# ---------------------------------------------------------------- workloads
+
+
+@pytest.mark.parametrize("name", ["square_f16_256", "square_f16_1024", "skinny_bf16_16x8192",
+                                  "tail_f16_4000x3000x1000_c"])
+def test_workload_full_parity(name):
+    w = gemm_inputs.WORKLOADS[name]
+    A, B, C = gemm_inputs.make(w)
+    print("case", name, flush=True)
+    D = gpu_run(A, B, C)
+    check(A, B, C, D, w.dtype, label=name)
+
+
+def test_workload_4096_sampled_parity():
+    w = gemm_inputs.WORKLOADS["square_bf16_4096"]
+    A, B, C = gemm_inputs.make(w)
+    D = gpu_run(A, B, C)
+    check(A, B, C, D, w.dtype, sample=sample_positions(w.M, w.N, 20000, 7), label=w.name)
+    # every output finite and of the expected scale (property at any size)
+    Df = D.float()
+    assert torch.isfinite(Df).all()
+    assert 0.5 < Df.std().item() < 2.0        # N(0,1)/sqrt(K) entries: std of D ~ 1
+
+
+# ---------------------------------------------------------------- ragged shapes
+
+ODD = [1, 2, 7, 15, 16, 17, 31, 33, 63, 65, 127, 129]
+
+
+def _odd_cases():
+    rng = np.random.default_rng(3)
+    all_ = list(itertools.product(ODD, ODD, ODD))
+    pick = rng.choice(len(all_), 40, replace=False)
+    return [all_[i] for i in sorted(pick)] + [(1, 1, 1), (129, 129, 129), (1, 129, 1), (129, 1, 129)]
+
+
+@pytest.mark.parametrize("mnk", _odd_cases())
+def test_odd_shapes(mnk):
+    M, N, K = mnk
+    for dt, has_c in (("f16", True), ("bf16", False)):
+        A, B, C = _inputs(M, N, K, dt, has_c, seed=M * 10007 + N * 101 + K)
+        D = gpu_run(A, B, C)
+        check(A, B, C, D, dt, label="%s %dx%dx%d c=%d" % (dt, M, N, K, has_c))
+
+
+@pytest.mark.parametrize("shape", [(300, 200, 136), (520, 264, 1000), (96, 1000, 72)])
+def test_every_compiled_variant(shape):
+    """Each compiled tile variant, forced, passes on a ragged shape; variants with
+    the same instruction shape agree bit for bit (same k-block summation order)."""
+    M, N, K = shape
+    for dt in ("f16", "bf16"):
+        A, B, C = _inputs(M, N, K, dt, True, seed=M + N + K)
+        by_mf = {}
+        for cfg in _variants(dt):
+            D = gpu_run(A, B, C, config=cfg)
+            check(A, B, C, D, dt, label="%s %s %s" % (dt, shape, cfg))
+            key = cfg["mfma"]
+            if key in by_mf:
+                assert torch.equal(by_mf[key][1].view(torch.int16), D.view(torch.int16)), (cfg, by_mf[key][0])
+            else:
+                by_mf[key] = (cfg, D)
+
+
+def _variants(dt):
+    import ctypes
+    seen = []
+    for bm, bn, bk, st, mf, wm, wn in [(256, 256, 64, 2, 16, 2, 4), (256, 256, 64, 2, 32, 2, 4),
+                                       (256, 128, 64, 2, 16, 2, 2), (256, 128, 64, 2, 32, 2, 2),
+                                       (128, 256, 64, 2, 16, 2, 2), (128, 128, 64, 2, 16, 2, 2),
+                                       (128, 128, 64, 2, 32, 2, 2), (128, 128, 64, 1, 16, 2, 2),
+                                       (128, 128, 32, 2, 16, 2, 2), (64, 64, 64, 2, 16, 2, 2),
+                                       (64, 64, 32, 2, 16, 2, 2), (64, 64, 32, 1, 16, 2, 2),
+                                       (32, 32, 32, 2, 16, 2, 2), (16, 64, 64, 2, 16, 1, 4)]:
+        seen.append(dict(bm=bm, bn=bn, bk=bk, stages=st, mfma=mf, waves_m=wm, waves_n=wn, kernel=1))
+    return seen
+
+
+@pytest.mark.parametrize("gm,xcd", [(1, 2), (4, 2), (8, 2), (8, 1), (3, 1)])
+def test_group_and_xcd_orders_are_bitwise_identical(gm, xcd):
+    A, B, C = _inputs(1000, 700, 256, "bf16", False, seed=77)
+    base = gpu_run(A, B, C, config={"bm": 128, "bn": 128, "group_m": 1, "xcd_remap": 2})
+    D = gpu_run(A, B, C, config={"bm": 128, "bn": 128, "group_m": gm, "xcd_remap": xcd})
+    assert torch.equal(base.view(torch.int16), D.view(torch.int16))
+
+
+# ---------------------------------------------------------------- exact cases
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+def test_identity_with_subnormals_is_exact(dt):
+    M, N = 200, 136
+    rng = np.random.default_rng(5)
+    x = rng.uniform(-1, 1, (M, N))
+    tiny = 2.0 ** -20 if dt == "f16" else 2.0 ** -130
+    x[rng.random((M, N)) < 0.2] *= tiny
+    B = gemm_inputs.from_bits(oracle.encode_rne(x, dt), dt)
+    I = torch.eye(M).to(gemm_inputs.TORCH_DTYPES[dt])
+    D = gpu_run(I, B)
+    assert torch.equal(D.view(torch.int16), B.view(torch.int16))
+    # with an addend: D = round(B + C), B + C exact in binary64
+    C = gemm_inputs.draw((M, N), 9, dt)
+    D = gpu_run(I, B, C)
+    want = oracle.encode_rne(oracle.decode(gemm_inputs.bits(B), dt) + oracle.decode(gemm_inputs.bits(C), dt), dt)
+    assert np.array_equal(gemm_inputs.bits(D), want)
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+def test_integer_inputs_are_exact(dt):
+    M, N, K = 333, 250, 28          # |D| <= 9*28 + 3 = 255: exact in both types
+    rng = np.random.default_rng(6)
+    Ai, Bi, Ci = rng.integers(-3, 4, (M, K)), rng.integers(-3, 4, (K, N)), rng.integers(-3, 4, (M, N))
+    T = gemm_inputs.TORCH_DTYPES[dt]
+    A, B, C = (torch.from_numpy(x.astype(np.float32)).to(T) for x in (Ai, Bi, Ci))
+    D = gpu_run(A, B, C)
+    assert np.array_equal(D.float().numpy(), (Ai @ Bi + Ci).astype(np.float32))
+
+
+def test_rank_one_dyadic_is_exact():
+    M, N, K = 130, 90, 512
+    rng = np.random.default_rng(8)
+    u = 2.0 ** rng.integers(-4, 2, M) * rng.choice([-1, 1], M)
+    v = 2.0 ** rng.integers(-4, 2, N)
+    A = torch.from_numpy(np.repeat(u[:, None], K, 1)).to(torch.bfloat16)
+    B = torch.from_numpy(np.repeat(v[None, :], K, 0)).to(torch.bfloat16)
+    D = gpu_run(A, B)
+    assert np.array_equal(D.double().numpy(), K * np.outer(u, v))
+
+
+# ---------------------------------------------------------------- edges and invariants
+
+
+def test_k_zero_gives_c_and_m_zero_is_a_no_op():
+    C = gemm_inputs.draw((40, 24), 1, "f16")
+    A = torch.empty((40, 0), dtype=torch.float16)
+    B = torch.empty((0, 24), dtype=torch.float16)
+    D = gpu_run(A, B, C)
+    assert torch.equal(D.view(torch.int16), C.view(torch.int16))
+    D = gpu_run(A, B)
+    assert torch.equal(D, torch.zeros_like(D))
+    out = torch.full((0, 24), 1.0, dtype=torch.float16, device="cuda")
+    g.matmul(torch.empty((0, 8), dtype=torch.float16, device="cuda"),
+             torch.ones((8, 24), dtype=torch.float16, device="cuda"), out=out)
+    torch.cuda.synchronize()
+
+
+def test_guard_band_untouched():
+    M, N, K = 257, 129, 96
+    A, B, C = _inputs(M, N, K, "f16", True, seed=11)
+    big = torch.full((M + 64, N + 64), 7.0, dtype=torch.float16, device="cuda")
+    D = big[32:32 + M, 16:16 + N]
+    g.matmul(A.cuda(), B.cuda(), C.cuda(), out=D)
+    torch.cuda.synchronize()
+    host = big.cpu()
+    mask = torch.ones_like(host, dtype=torch.bool)
+    mask[32:32 + M, 16:16 + N] = False
+    assert torch.all(host[mask] == 7.0)
+    check(A, B, C, host[32:32 + M, 16:16 + N].contiguous(), "f16", label="strided D")
+
+
+def test_in_place_addend():
+    M, N, K = 300, 200, 64
+    A, B, C = _inputs(M, N, K, "bf16", True, seed=12)
+    dC = C.cuda()
+    g.matmul(A.cuda(), B.cuda(), dC, out=dC)
+    torch.cuda.synchronize()
+    check(A, B, C, dC.cpu(), "bf16", label="in place")
+
+
+def test_unaligned_base_uses_element_path():
+    M, N, K = 190, 130, 200
+    A0 = gemm_inputs.draw((M * K + 1,), 13, "f16")
+    A = A0[1:].view(M, K)                 # base address 2 bytes past a 16-byte boundary
+    B = gemm_inputs.draw((K, N), 15, "f16")
+    dA = A0.cuda()[1:].view(M, K)
+    D = g.matmul(dA, B.cuda())
+    torch.cuda.synchronize()
+    check(A, B, None, D.cpu(), "f16", label="unaligned")
+
+
+def test_run_to_run_bitwise_identical():
+    w = gemm_inputs.WORKLOADS["tail_f16_4000x3000x1000_c"]
+    A, B, C = gemm_inputs.make(w)
+    dA, dB, dC = A.cuda(), B.cuda(), C.cuda()
+    D1 = g.matmul(dA, dB, dC)
+    D2 = g.matmul(dA, dB, dC)
+    torch.cuda.synchronize()
+    assert torch.equal(D1.view(torch.int16), D2.view(torch.int16))
+
+
+def test_one_shot_entry_point():
+    M, N, K = 100, 72, 40
+    A, B, C = _inputs(M, N, K, "bf16", True, seed=16)
+    dA, dB, dC = A.cuda(), B.cuda(), C.cuda()
+    D = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    g.gemm(dA.data_ptr(), dB.data_ptr(), dC.data_ptr(), D.data_ptr(), M, N, K,
+           [K, 1, N, 1, N, 1, N, 1], g.GEMM_BF16, 1, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    check(A, B, C, D.cpu(), "bf16", label="one-shot")
