@@ -152,14 +152,17 @@ def cpu_baseline(w, seconds):
     A, B, C = gemm_inputs.make(w)
     Ab, Bb = gemm_inputs.bits(A), gemm_inputs.bits(B)
     Cb = gemm_inputs.bits(C) if C is not None else None
-    rows = 4
-    t0 = time.perf_counter()
-    oracle.gemm_f64(Ab[:rows], Bb, Cb[:rows] if Cb is not None else None, w.dtype)
-    t1 = time.perf_counter() - t0
-    rows = int(max(4, min(w.M, rows * seconds / max(t1, 1e-3))))
-    t0 = time.perf_counter()
-    oracle.gemm_f64(Ab[:rows], Bb, Cb[:rows] if Cb is not None else None, w.dtype)
-    t = time.perf_counter() - t0
+    # calibrate: the oracle decodes all of B once per call, then costs per row
+    def timed(r):
+        t0 = time.perf_counter()
+        oracle.gemm_f64(Ab[:r], Bb, Cb[:r] if Cb is not None else None, w.dtype)
+        return time.perf_counter() - t0
+    r1 = min(w.M, 8)
+    r2 = min(w.M, 40)
+    t1, t2 = timed(r1), timed(r2)
+    per_row = max((t2 - t1) / max(r2 - r1, 1), 1e-6)
+    rows = int(max(r2, min(w.M, (seconds - t1) / per_row)))
+    t = timed(rows)
     flops = 2.0 * rows * w.N * w.K
     return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
             "kind": "oracle",

@@ -7,6 +7,10 @@
 // (the single-instruction kernel of "DCU K100 节点初探", section 5.4, used as a
 // layout check).
 //
+// probe_lds_dma records where the direct global -> LDS loads put each lane's
+// 16 bytes, and that the buffer form writes zeros for offsets past the
+// descriptor's range.
+//
 // probe_lds_read_tr fills 1024 bytes of LDS from `in` and has every lane run one
 // transposing 64-bit LDS read at byte address 8 * lane; the 4 halfwords each
 // lane receives are written to out[4 * lane + 0..3].  It reports the lane
@@ -69,9 +73,43 @@ __global__ __launch_bounds__(64) void probe_lds_read_tr_kernel(const uint16_t* i
     for (int i = 0; i < 4; ++i) out[4 * l + i] = static_cast<uint16_t>(v[i]);
 }
 
+// 64 lanes, one 16-byte load each, straight into LDS.  LDS halfwords
+// [0, 512): buffer loads through a descriptor covering the first num_records
+// bytes of `in`; lane l < 48 fetches 16-byte chunk (7 l) mod 64, lanes 48..55
+// use offset 0x80000000 and lanes 56..63 offsets num_records + 16 (l - 56),
+// both past num_records (the descriptor's range check must return zeros).
+// LDS halfwords [512, 1024): plain global loads, lane l fetches chunk (5 l)
+// mod 64.  LDS starts filled with 0xFFFF; all of it is copied to out.
+// `in` must hold at least num_records + 128 bytes and num_records >= 1024.
+__global__ __launch_bounds__(64) void probe_lds_dma_kernel(const uint16_t* in, uint16_t* out,
+                                                           int num_records) {
+    __shared__ __attribute__((aligned(16))) uint16_t lds[1024];
+    const int l = threadIdx.x;
+    for (int i = l; i < 1024; i += 64) lds[i] = 0xFFFF;
+    __syncthreads();
+    __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)in, 0, num_records, 0x00020000);
+    const unsigned voff = (l < 48) ? ((l * 7) % 64) * 16
+                        : (l < 56) ? 0x80000000u : static_cast<unsigned>(num_records + 16 * (l - 56));
+    typedef __attribute__((address_space(3))) void lds_void;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voff, 0, 0, 0);
+    __builtin_amdgcn_global_load_lds((const void*)(in + 8 * ((l * 5) % 64)), (lds_void*)(lds + 512), 16, 0, 0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    for (int i = l; i < 1024; i += 64) out[i] = lds[i];
+}
+
 }  // namespace
 
 extern "C" {
+
+// in: >= num_records + 128 bytes, out: 1024 halfwords (device pointers).
+int probe_lds_dma(const uint16_t* in, uint16_t* out, int num_records, void* stream) {
+    if (num_records < 1024) return static_cast<int>(hipErrorInvalidValue);
+    hipLaunchKernelGGL(probe_lds_dma_kernel, dim3(1), dim3(64), 0, static_cast<hipStream_t>(stream), in, out,
+                       num_records);
+    return static_cast<int>(hipGetLastError());
+}
+
 
 // mf: 16 (A 16x32, B 32x16, D 16x16) or 32 (A 32x16, B 16x32, D 32x32).
 // dtype: 0 fp16, 1 bf16.  All pointers are device pointers.  Returns a

@@ -55,7 +55,8 @@ def test_workload_4096_sampled_parity():
     # every output finite and of the expected scale (property at any size)
     Df = D.float()
     assert torch.isfinite(Df).all()
-    assert 0.5 < Df.std().item() < 2.0        # N(0,1)/sqrt(K) entries: std of D ~ 1
+    # A, B entries N(0,1)/64: each output has variance K * (1/64)^4, std 1/64
+    assert 0.9 / 64 < Df.std().item() < 1.1 / 64
 
 
 # ---------------------------------------------------------------- ragged shapes
@@ -113,7 +114,7 @@ def _variants(dt):
 
 @pytest.mark.parametrize("gm,xcd", [(1, 2), (4, 2), (8, 2), (8, 1), (3, 1)])
 def test_group_and_xcd_orders_are_bitwise_identical(gm, xcd):
-    A, B, C = _inputs(1000, 700, 256, "bf16", False, seed=77)
+    A, B, C = _inputs(1000, 704, 256, "bf16", False, seed=77)
     base = gpu_run(A, B, C, config={"bm": 128, "bn": 128, "group_m": 1, "xcd_remap": 2})
     D = gpu_run(A, B, C, config={"bm": 128, "bn": 128, "group_m": gm, "xcd_remap": xcd})
     assert torch.equal(base.view(torch.int16), D.view(torch.int16))
@@ -132,7 +133,11 @@ def test_identity_with_subnormals_is_exact(dt):
     B = gemm_inputs.from_bits(oracle.encode_rne(x, dt), dt)
     I = torch.eye(M).to(gemm_inputs.TORCH_DTYPES[dt])
     D = gpu_run(I, B)
-    assert torch.equal(D.view(torch.int16), B.view(torch.int16))
+    # the exact result is B itself, except that 0 + (-0) = +0
+    want = oracle.encode_rne(oracle.decode(gemm_inputs.bits(B), dt) + 0.0, dt)
+    assert np.array_equal(gemm_inputs.bits(D), want)
+    bv = np.abs(oracle.decode(gemm_inputs.bits(B), dt))
+    assert np.count_nonzero((bv > 0) & (bv < (2.0 ** -14 if dt == "f16" else 2.0 ** -126))) > 100
     # with an addend: D = round(B + C), B + C exact in binary64
     C = gemm_inputs.draw((M, N), 9, dt)
     D = gpu_run(I, B, C)
