@@ -21,7 +21,7 @@ LIB = os.path.join(PKG, "libgemm.so")
 PROBE_LIB = os.path.join(PKG, "libgemm_probe.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "gemm_tile.hip", "gemm_skinny.hip"]
+SOURCES = ["api.cpp", "gemm_tile.hip", "gemm_dma.hip", "gemm_skinny.hip"]
 PROBE_SOURCES = ["probe.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

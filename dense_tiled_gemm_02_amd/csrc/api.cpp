@@ -102,10 +102,20 @@ bool vec_shape_ok(const gemm_problem* p) {
     return p->K % 8 == 0 && p->N % 8 == 0 && p->sa_m % 8 == 0 && p->sb_k % 8 == 0;
 }
 
+// The direct-to-LDS kernels address one BM-row panel of A and one BK-row slab
+// of B with 32-bit byte offsets from descriptors rebased every K step.
+bool dma_offsets_ok(const gemm_problem* p, const dtg::KernelEntry* e) {
+    const int64_t lim = (int64_t(1) << 31) - 4096;
+    return static_cast<int64_t>(e->bm) * p->sa_m * 2 + e->bk * 2 < lim &&
+           static_cast<int64_t>(e->bk) * p->sb_k * 2 + e->bn * 2 < lim;
+}
+
 std::vector<const dtg::KernelEntry*> all_entries() {
     std::vector<const dtg::KernelEntry*> v;
     int n = 0;
     const dtg::KernelEntry* t = dtg::tile_kernel_table(&n);
+    for (int i = 0; i < n; ++i) v.push_back(&t[i]);
+    t = dtg::dma_kernel_table(&n);
     for (int i = 0; i < n; ++i) v.push_back(&t[i]);
     t = dtg::skinny_kernel_table(&n);
     for (int i = 0; i < n; ++i) v.push_back(&t[i]);
@@ -122,10 +132,11 @@ bool matches(const dtg::KernelEntry* e, const gemm_config& f) {
 
 // The first compiled variant that fits the device and matches `want`.
 const dtg::KernelEntry* find_entry(const gemm_config& want, int dtype, int vec,
-                                   const gemm_device_info& dev) {
+                                   const gemm_device_info& dev, const gemm_problem* p) {
     for (const dtg::KernelEntry* e : all_entries()) {
         if (e->dtype != dtype || e->vec != vec) continue;
         if (e->lds_bytes > dev.lds_per_wg) continue;
+        if (e->family == dtg::KF_DMA && !dma_offsets_ok(p, e)) continue;
         if (matches(e, want)) return e;
     }
     return nullptr;
@@ -161,10 +172,11 @@ gemm_config heuristic(const gemm_problem* p, const gemm_device_info& dev, int* g
     *group_m = 8;
     if (M <= 16) return cfg_of(dtg::KF_TILE, 16, 64, 64, 2, 16, 1, 4);
     if (M <= 32) return cfg_of(dtg::KF_TILE, 32, 32, 32, 2, 16, 2, 2);
-    struct C { int bm, bn, bk, st, mf, wm, wn; };
+    struct C { int fam, bm, bn, bk, st, mf, wm, wn; };
     static const C ladder[] = {
-        {256, 256, 64, 2, 16, 2, 4}, {256, 128, 64, 2, 16, 2, 2}, {128, 128, 64, 2, 16, 2, 2},
-        {64, 64, 64, 2, 16, 2, 2},   {32, 32, 32, 2, 16, 2, 2},
+        {dtg::KF_DMA, 256, 256, 64, 2, 16, 2, 4}, {dtg::KF_DMA, 256, 128, 64, 2, 16, 2, 2},
+        {dtg::KF_DMA, 128, 128, 64, 2, 16, 2, 2}, {dtg::KF_TILE, 64, 64, 64, 2, 16, 2, 2},
+        {dtg::KF_TILE, 32, 32, 32, 2, 16, 2, 2},
     };
     const C* best = nullptr;
     int64_t best_tiles = -1;
@@ -173,7 +185,7 @@ gemm_config heuristic(const gemm_problem* p, const gemm_device_info& dev, int* g
         if (tiles >= dev.cu_count) { best = &c; break; }
         if (tiles > best_tiles) { best_tiles = tiles; best = &c; }
     }
-    return cfg_of(dtg::KF_TILE, best->bm, best->bn, best->bk, best->st, best->mf, best->wm, best->wn);
+    return cfg_of(best->fam, best->bm, best->bn, best->bk, best->st, best->mf, best->wm, best->wn);
 }
 
 gemm_status plan_impl(const gemm_problem* prob, const gemm_device_info* dev, const gemm_config* force,
@@ -213,13 +225,20 @@ gemm_status plan_impl(const gemm_problem* prob, const gemm_device_info* dev, con
         if (f.xcd_remap) xcd = (f.xcd_remap == GEMM_XCD_ON);
     }
     const dtg::KernelEntry* e = nullptr;
-    if (vec) e = find_entry(want, prob->dtype, 1, *dev);
-    const dtg::KernelEntry* fb = find_entry(cfg_of(dtg::KF_TILE, 0, 0, 0, 0, 16, 0, 0), prob->dtype, 0, *dev);
+    if (vec) e = find_entry(want, prob->dtype, 1, *dev, prob);
+    if (!e && vec && !tuned && (!force || force->kernel == 0) && want.kernel == dtg::KF_DMA) {
+        // no direct-to-LDS variant fits (offset range): same tile, register-staged kernel
+        gemm_config w2 = want;
+        w2.kernel = dtg::KF_TILE;
+        e = find_entry(w2, prob->dtype, 1, *dev, prob);
+    }
+    const dtg::KernelEntry* fb =
+        find_entry(cfg_of(dtg::KF_TILE, 0, 0, 0, 0, 16, 0, 0), prob->dtype, 0, *dev, prob);
     if (!e) {
         if (!vec && (!force || want.kernel == 0 || want.kernel == dtg::KF_TILE)) {
             // element-wise path: any shape, any alignment (16x16x32 instruction)
             if (force && (want.bm || want.bn || want.bk || want.mfma == 32))
-                e = find_entry(want, prob->dtype, 0, *dev);
+                e = find_entry(want, prob->dtype, 0, *dev, prob);
             else
                 e = fb;
         }

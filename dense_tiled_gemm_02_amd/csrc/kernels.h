@@ -23,7 +23,7 @@ struct KArgs {
 
 typedef hipError_t (*launch_fn)(const KArgs& args, int64_t grid, hipStream_t stream);
 
-enum KernelFamily { KF_TILE = 1, KF_SKINNY = 2 };
+enum KernelFamily { KF_TILE = 1, KF_SKINNY = 2, KF_DMA = 3 };
 
 // One compiled kernel variant.  vec = 1: 16-byte vector loads (requires
 // K % 8 == 0, N % 8 == 0, lda % 8 == 0, ldb % 8 == 0 and 16-byte aligned A, B);
@@ -42,5 +42,6 @@ struct KernelEntry {
 // All compiled variants (tile kernels followed by skinny kernels).
 const KernelEntry* tile_kernel_table(int* count);
 const KernelEntry* skinny_kernel_table(int* count);
+const KernelEntry* dma_kernel_table(int* count);
 
 }  // namespace dtg

@@ -94,8 +94,8 @@ typedef struct gemm_problem {
  *   xcd_remap     GEMM_XCD_ON: pre-permute workgroup ids so each XCD gets a
  *                 contiguous band of the tile order; GEMM_XCD_OFF: plain ids
  *                 (0 in a forced configuration: the planner's choice)
- *   kernel        kernel family: 1 = square/tail tile kernel,
- *                 2 = skinny split-K kernel */
+ *   kernel        kernel family: 1 = register-staged tile kernel (any shape),
+ *                 2 = skinny split-K kernel, 3 = direct-to-LDS tile kernel */
 #define GEMM_XCD_ON 1
 #define GEMM_XCD_OFF 2
 

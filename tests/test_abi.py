@@ -103,6 +103,7 @@ def test_plans_for_the_five_workloads_fit_the_device():
         assert grid == -(-M // cfg.bm) * -(-N // cfg.bn) * (cfg.splitk if cfg.kernel == 2 else 1) or cfg.kernel == 2
         assert lds == g.gemm_lds_bytes(cfg.bm, cfg.bn, cfg.bk, cfg.stages, dt) or cfg.kernel == 2
         assert "kernel=" in p.describe()
+    assert plan(4096, 4096, 4096).config.kernel == 3          # direct-to-LDS family when aligned
 
 
 def test_key_includes_m():

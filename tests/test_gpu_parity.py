@@ -82,8 +82,9 @@ def test_odd_shapes(mnk):
 
 @pytest.mark.parametrize("shape", [(300, 200, 136), (520, 264, 1000), (96, 1000, 72)])
 def test_every_compiled_variant(shape):
-    """Each compiled tile variant, forced, passes on a ragged shape; variants with
-    the same instruction shape agree bit for bit (same k-block summation order)."""
+    """Each compiled tile variant (both kernel families), forced, passes on a
+    ragged shape; variants with the same instruction shape agree bit for bit
+    (same k-block summation order)."""
     M, N, K = shape
     for dt in ("f16", "bf16"):
         A, B, C = _inputs(M, N, K, dt, True, seed=M + N + K)
@@ -109,6 +110,12 @@ def _variants(dt):
                                        (64, 64, 32, 2, 16, 2, 2), (64, 64, 32, 1, 16, 2, 2),
                                        (32, 32, 32, 2, 16, 2, 2), (16, 64, 64, 2, 16, 1, 4)]:
         seen.append(dict(bm=bm, bn=bn, bk=bk, stages=st, mfma=mf, waves_m=wm, waves_n=wn, kernel=1))
+    for bm, bn, bk, st, mf, wm, wn in [(256, 256, 64, 2, 16, 2, 4), (256, 256, 32, 3, 16, 2, 4),
+                                       (256, 256, 32, 4, 16, 2, 4), (256, 256, 64, 2, 32, 2, 4),
+                                       (256, 128, 64, 2, 16, 2, 2), (256, 128, 64, 3, 16, 2, 2),
+                                       (128, 128, 64, 2, 16, 2, 2), (128, 128, 64, 3, 16, 2, 2),
+                                       (128, 128, 64, 2, 32, 2, 2)]:
+        seen.append(dict(bm=bm, bn=bn, bk=bk, stages=st, mfma=mf, waves_m=wm, waves_n=wn, kernel=3))
     return seen
 
 
