@@ -53,6 +53,8 @@ def parse():
     ap.add_argument("--config", default="", help="forced config fields, e.g. bm=128,bn=128,mfma=32")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--out", default="")
+    ap.add_argument("--copy-mb", type=int, default=0,
+                    help="after timing, run one device copy of this many MiB (counter calibration)")
     return ap.parse_args()
 
 
@@ -184,15 +186,14 @@ def sweep(args):
     import gemm_inputs
     variants = {
         "square_bf16_4096": [dict(kernel=1, bm=256, bn=256, mfma=16, group_m=8)] +
-                            [dict(kernel=3, bm=256, bn=256, bk=64, stages=2, mfma=16, group_m=gm) for gm in (1, 4, 8)] +
-                            [dict(kernel=3, bm=256, bn=256, bk=64, stages=2, mfma=16, group_m=8, xcd_remap=2),
-                             dict(kernel=3, bm=256, bn=256, bk=64, stages=2, mfma=32, group_m=8),
-                             dict(kernel=3, bm=256, bn=256, bk=32, stages=3, mfma=16, group_m=8),
-                             dict(kernel=3, bm=256, bn=256, bk=32, stages=4, mfma=16, group_m=8),
-                             dict(kernel=3, bm=256, bn=128, bk=64, stages=2, mfma=16, group_m=8),
-                             dict(kernel=3, bm=256, bn=128, bk=64, stages=3, mfma=16, group_m=8),
-                             dict(kernel=3, bm=128, bn=128, bk=64, stages=2, mfma=16, group_m=8),
-                             dict(kernel=3, bm=128, bn=128, bk=64, stages=3, mfma=16, group_m=8)],
+                            [dict(kernel=3, bm=256, bn=256, bk=64, mfma=16, group_m=gm) for gm in (1, 4, 8)] +
+                            [dict(kernel=3, bm=256, bn=256, bk=64, mfma=16, group_m=8, xcd_remap=2),
+                             dict(kernel=3, bm=256, bn=256, bk=64, mfma=32, group_m=8),
+                             dict(kernel=3, bm=256, bn=256, bk=32, mfma=32, group_m=8),
+                             dict(kernel=3, bm=256, bn=128, bk=64, mfma=16, group_m=8),
+                             dict(kernel=3, bm=128, bn=256, bk=64, mfma=16, group_m=8),
+                             dict(kernel=3, bm=128, bn=128, bk=64, mfma=16, group_m=8),
+                             dict(kernel=3, bm=128, bn=128, bk=64, mfma=32, group_m=8)],
         "square_f16_1024": [dict(bm=32, bn=32, bk=32), dict(bm=64, bn=64, bk=32), dict(bm=128, bn=128, bk=64),
                             dict(bm=64, bn=64, bk=64)],
         "square_f16_256": [dict(bm=32, bn=32, bk=32), dict(bm=64, bn=64, bk=32), dict(bm=64, bn=64, bk=64),
@@ -285,6 +286,14 @@ def main():
                                       "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS, "traffic": None},
                          "tflops": sw.flops() / sms / 1e9}
         del sc
+    if args.copy_mb:
+        n = args.copy_mb * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        rec["copy_calibration_bytes"] = 4 * n
+        del src, dst
     if not args.no_cpu:
         cb = cpu_baseline(w, args.cpu_seconds)
         cb["host_cpu"] = host_cpu_model()

@@ -61,39 +61,48 @@ __device__ __forceinline__ int bsw(int r) {
 }
 
 // wait until at most N vector-memory operations of this wave are outstanding
+template <int N, typename Fn>
+__device__ __forceinline__ void static_for(Fn&& fn) {
+    if constexpr (N > 0) {
+        static_for<N - 1>(fn);
+        fn(std::integral_constant<int, N - 1>{});
+    }
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vm() {
     static_assert(N >= 0 && N < 64, "vmcnt");
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// Transposing 64-bit LDS read (ds_read_b64_tr_b16) at LDS byte address
-// `addr`: within each 16-lane group the 16 addressed 8-byte pieces, in lane
-// order, form a 4 x 16 matrix of halfwords (lanes 4i..4i+3 give row i); lane t
-// receives column t.  Issued as inline asm so the compiler does not guard it
-// with a wait for every outstanding global -> LDS load; the caller waits with
-// lds_wait() before using the result.
-__device__ __forceinline__ i16x4 lds_read_tr(uint32_t addr) {
-    i16x4 v;
-    asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(v) : "v"(addr));
+// LDS operand reads are issued as inline asm: the compiler then neither
+// guards them with waits for every outstanding global -> LDS load (it cannot
+// tell which stage a read touches) nor moves them; the kernel waits for them
+// explicitly with lds_wait_all() + tie() before the MFMAs that use them.
+//
+// 16-byte read at LDS byte address addr + OFF.
+template <int OFF>
+__device__ __forceinline__ u32x4 lds_read16(uint32_t addr) {
+    u32x4 v;
+    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
     return v;
 }
 
-// Wait for every LDS read of this wave, and make the values in `regs` depend
-// on that wait so no use of them is scheduled before it.
-template <int NR>
-__device__ __forceinline__ void lds_wait(u32x4 (&regs)[NR]) {
-    static_assert(NR >= 1 && NR <= 8, "lds_wait");
-    if constexpr (NR == 1) asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(regs[0]));
-    else if constexpr (NR == 2) asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(regs[0]), "+v"(regs[1]));
-    else if constexpr (NR == 4)
-        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(regs[0]), "+v"(regs[1]), "+v"(regs[2]), "+v"(regs[3]));
-    else if constexpr (NR == 8)
-        asm volatile("s_waitcnt lgkmcnt(0)"
-                     : "+v"(regs[0]), "+v"(regs[1]), "+v"(regs[2]), "+v"(regs[3]), "+v"(regs[4]),
-                       "+v"(regs[5]), "+v"(regs[6]), "+v"(regs[7]));
-    else static_assert(NR == 1 || NR == 2 || NR == 4 || NR == 8, "lds_wait");
+// Transposing 64-bit read (ds_read_b64_tr_b16) at addr + OFF: within each
+// 16-lane group the 16 addressed 8-byte pieces, in lane order, form a 4 x 16
+// matrix of halfwords (lanes 4i..4i+3 give row i); lane t receives column t.
+template <int OFF>
+__device__ __forceinline__ i16x4 lds_read_tr(uint32_t addr) {
+    i16x4 v;
+    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
+    return v;
 }
+
+__device__ __forceinline__ void lds_wait_all() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// Make `v` depend on the preceding lds_wait_all() (volatile asm keeps its
+// order), so no use of v is scheduled before the wait.
+__device__ __forceinline__ void tie(u32x4& v) { asm volatile("" : "+v"(v)); }
 
 __device__ __forceinline__ uint32_t lds_addr(const uint16_t* p) {
     return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) uint16_t*)p));
@@ -117,11 +126,13 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(KArgs p) {
     constexpr int IB_W = BK / RB / NW;
     constexpr int SA = BM * BK, SB = BK * BN;   // elements per stage
     constexpr int L = IA_W + IB_W;              // loads per wave per stage
+    constexpr int NKS = BK / KI;                // instruction k sub-steps per K step
+    static_assert(NKS % 2 == 0, "fragment double buffering needs an even number of k sub-steps");
     static_assert(BM % (WM * MF) == 0 && BN % (WN * MF) == 0, "tile vs wave grid");
     static_assert(BK % KI == 0 && (CHA == 4 || CHA == 8 || CHA == 16), "BK");
     static_assert(CHB >= 8 && CHB <= 64 && 64 % CHB == 0, "BN");
     static_assert((BM / RA) % NW == 0 && (BK / RB) % NW == 0 && IA_W > 0 && IB_W > 0, "load split");
-    static_assert(ST >= 2 && (ST - 2) * L < 64, "stages");
+    static_assert(ST == 2, "this kernel runs a two-stage LDS ring");
     typedef typename AccT<MF>::type acc_t;
 
     __shared__ __attribute__((aligned(1024))) uint16_t smem[ST * (SA + SB)];
@@ -198,80 +209,121 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(KArgs p) {
 #pragma unroll
             for (int r = 0; r < AccT<MF>::regs; ++r) acc[i][j][r] = 0.0f;
 
-    // per-lane operand read geometry
-    const int a_row = lane % MF;
-    const int a_kc0 = lane / MF;
-    const int a_sw = swz<CHA>(a_row);
-    int b_jq, b_g, b_col;                       // see the two cases below
-    if constexpr (MF == 16) {
-        b_jq = lane & 15;                       // column within the fragment
-        b_g = lane >> 4;                        // k group: k = 8 g + 0..7
-        b_col = 0;
-    } else {
-        b_jq = lane & 15;                       // column within a 16-column half
-        b_g = lane >> 5;                        // k group: k = 8 g + 0..7
-        b_col = 16 * ((lane >> 4) & 1);         // which 16-column half
-    }
-    const int b_sw = (CHB >= 16) ? 2 * ((b_jq >> 2) | ((b_g & 1) << 2)) : 2 * (b_jq >> 2);
-
-    auto compute = [&](int s) {
-        const uint16_t* As = smem + s * (SA + SB);
-        const uint16_t* Bs = As + SA;
+    // ---- per-lane operand read addresses (LDS bytes), for both stages
+    //  A fragment (i, ks): row wm*TM + i*MF + lane % MF, chunk ks*KI/8 + lane / MF
+    //  (XOR-swizzled); the i*MF*BK*2 part is an immediate offset.
+    //  B fragment (j, ks), half hh: the transposing read of k rows
+    //  ks*KI + 8 g + 4 hh + (jq >> 2) and 4 columns starting at
+    //  nb + 4 (jq & 3); the (ks*KI + 4 hh) * BN * 2 part is an immediate offset.
+    const uint32_t smem0 = lds_addr(smem);
+    uint32_t a_addr[2][NKS], b_addr[2][FN];
+    {
+        const int a_row = wm * TM + lane % MF;
+        const int a_kc0 = lane / MF;
+        const int a_sw = swz<CHA>(lane % MF);
+        int jq, g, col;
+        if constexpr (MF == 16) { jq = lane & 15; g = lane >> 4; col = 0; }
+        else { jq = lane & 15; g = lane >> 5; col = 16 * ((lane >> 4) & 1); }
+        const int b_sw = (CHB >= 16) ? 2 * ((jq >> 2) | ((g & 1) << 2)) : 2 * (jq >> 2);
+        const int b_row = 8 * g + (jq >> 2);
 #pragma unroll
-        for (int ks = 0; ks < BK / KI; ++ks) {
-            u32x4 af[FM], bv[FN];
-            const int coff = (((ks * (KI / 8) + a_kc0) ^ a_sw) * 8);
+        for (int st = 0; st < 2; ++st) {
+            const uint32_t sa = smem0 + st * (SA + SB) * 2;
+            const uint32_t sb = sa + SA * 2;
 #pragma unroll
-            for (int i = 0; i < FM; ++i)
-                af[i] = *reinterpret_cast<const u32x4*>(As + (wm * TM + i * MF + a_row) * BK + coff);
+            for (int ks = 0; ks < NKS; ++ks)
+                a_addr[st][ks] = sa + (a_row * BK + (((ks * (KI / 8) + a_kc0) ^ a_sw) * 8)) * 2;
 #pragma unroll
             for (int j = 0; j < FN; ++j) {
-                const int nb = wn * TN + j * MF + b_col;
-                i16x4 h[2];
-#pragma unroll
-                for (int hh = 0; hh < 2; ++hh) {
-                    const int r = ks * KI + 8 * b_g + 4 * hh + (b_jq >> 2);
-                    const uint16_t* src = Bs + r * BN + (((nb >> 3) ^ b_sw) << 3) + 4 * (b_jq & 3);
-                    h[hh] = lds_read_tr(lds_addr(src));
-                }
-                bv[j] = __builtin_bit_cast(u32x4, __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3, 4, 5, 6, 7));
+                const int nb = wn * TN + j * MF + col;
+                b_addr[st][j] = sb + (b_row * BN + (((nb >> 3) ^ b_sw) << 3) + 4 * (jq & 3)) * 2;
             }
-            lds_wait(bv);
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-#pragma unroll
-                for (int j = 0; j < FN; ++j) acc[i][j] = mfma<MF, BF16>(af[i], bv[j], acc[i][j]);
         }
+    }
+
+    u32x4 fa[2][FM], fb[2][FN];       // fragments, double-buffered across k sub-steps
+
+    auto read_frags = [&](auto stage_tag, auto ks_tag, auto slot_tag) {
+        constexpr int S = decltype(stage_tag)::value;
+        constexpr int KS = decltype(ks_tag)::value;
+        constexpr int SL = decltype(slot_tag)::value;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            i16x4 h0 = lds_read_tr<(KS * KI + 0) * BN * 2>(b_addr[S][j]);
+            i16x4 h1 = lds_read_tr<(KS * KI + 4) * BN * 2>(b_addr[S][j]);
+            fb[SL][j] = __builtin_bit_cast(u32x4, __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+        static_for<FM>([&](auto i_tag) {
+            constexpr int I = decltype(i_tag)::value;
+            fa[SL][I] = lds_read16<I * MF * BK * 2>(a_addr[S][KS]);
+        });
+    };
+    auto wait_frags = [&](auto slot_tag) {
+        constexpr int SL = decltype(slot_tag)::value;
+        lds_wait_all();
+#pragma unroll
+        for (int j = 0; j < FN; ++j) tie(fb[SL][j]);
+#pragma unroll
+        for (int i = 0; i < FM; ++i) tie(fa[SL][i]);
+    };
+    auto mfmas = [&](auto slot_tag) {
+        constexpr int SL = decltype(slot_tag)::value;
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) acc[i][j] = mfma<MF, BF16>(fa[SL][i], fb[SL][j], acc[i][j]);
     };
 
     const int nkt = (K + BK - 1) / BK;
     const int nfull = K / BK;
-#pragma unroll
-    for (int s = 0; s < ST - 1; ++s) {
-        if (s < nkt) {
-            if (!edge && s < nfull) issue(F{}, s, s);
-            else issue(T{}, s, s);
-        }
-    }
-    for (int kt = 0; kt < nkt; ++kt) {
-        // tile kt is complete once at most min(ST - 2, tiles issued after it)
-        // stages of loads are still in flight
-        const int after = (nkt - 1 - kt < ST - 2) ? (nkt - 1 - kt) : (ST - 2);
-        if constexpr (ST == 2) {
-            wait_vm<0>();
-        } else if constexpr (ST == 3) {
-            if (after >= 1) wait_vm<L>(); else wait_vm<0>();
-        } else {
-            static_assert(ST <= 4, "stages");
-            if (after >= 2) wait_vm<2 * L>(); else if (after == 1) wait_vm<L>(); else wait_vm<0>();
-        }
+    auto issue_tile = [&](int kt, int st) {
+        if (!edge && kt < nfull) issue(F{}, kt, st);
+        else issue(T{}, kt, st);
+    };
+
+    // One K step on LDS stage S.  On entry the fragments of sub-step 0 are in
+    // slot 0.  Sub-step ks issues the reads of sub-step ks + 1 (or, at the
+    // last sub-step, waits for the next tile, passes the barrier, starts the
+    // loads of the tile after it into this stage and reads the next tile's
+    // first fragments), then runs its MFMAs, then waits for those reads.
+    auto step = [&](auto stage_tag, int kt) {
+        constexpr int S = decltype(stage_tag)::value;
+        static_for<NKS>([&](auto ks_tag) {
+            constexpr int KS = decltype(ks_tag)::value;
+            constexpr int CUR = KS & 1, NXT = CUR ^ 1;
+            bool pending = true;
+            if constexpr (KS + 1 < NKS) {
+                read_frags(std::integral_constant<int, S>{}, std::integral_constant<int, KS + 1>{},
+                           std::integral_constant<int, NXT>{});
+            } else {
+                pending = kt + 1 < nkt;
+                if (pending) {
+                    wait_vm<0>();
+                    __builtin_amdgcn_s_barrier();
+                    if (kt + 2 < nkt) issue_tile(kt + 2, S);
+                    read_frags(std::integral_constant<int, S ^ 1>{}, std::integral_constant<int, 0>{},
+                               std::integral_constant<int, NXT>{});
+                }
+            }
+            mfmas(std::integral_constant<int, CUR>{});
+            // keep every MFMA of this sub-step ahead of the wait
+            __builtin_amdgcn_sched_barrier(0);
+            if (pending) wait_frags(std::integral_constant<int, NXT>{});
+        });
+    };
+
+    if (nkt > 0) {
+        issue_tile(0, 0);
+        wait_vm<0>();
         __builtin_amdgcn_s_barrier();
-        const int nt = kt + ST - 1;
-        if (nt < nkt) {
-            if (!edge && nt < nfull) issue(F{}, nt, nt % ST);
-            else issue(T{}, nt, nt % ST);
+        if (nkt > 1) issue_tile(1, 1);
+        read_frags(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{},
+                   std::integral_constant<int, 0>{});
+        wait_frags(std::integral_constant<int, 0>{});
+        for (int kt = 0; kt < nkt; kt += 2) {
+            step(std::integral_constant<int, 0>{}, kt);
+            if (kt + 1 < nkt) step(std::integral_constant<int, 1>{}, kt + 1);
         }
-        compute(kt % ST);
     }
 
     // ---- epilogue: + C in fp32, round, masked store
@@ -316,14 +368,12 @@ hipError_t launch_dma(const KArgs& a, int64_t grid, hipStream_t stream) {
 
 const KernelEntry kDmaTable[] = {
     DMA_BOTH(256, 256, 64, 2, 4, 16, 2),
-    DMA_BOTH(256, 256, 32, 2, 4, 16, 3),
-    DMA_BOTH(256, 256, 32, 2, 4, 16, 4),
     DMA_BOTH(256, 256, 64, 2, 4, 32, 2),
     DMA_BOTH(256, 128, 64, 2, 2, 16, 2),
-    DMA_BOTH(256, 128, 64, 2, 2, 16, 3),
+    DMA_BOTH(128, 256, 64, 2, 2, 16, 2),
     DMA_BOTH(128, 128, 64, 2, 2, 16, 2),
-    DMA_BOTH(128, 128, 64, 2, 2, 16, 3),
     DMA_BOTH(128, 128, 64, 2, 2, 32, 2),
+    DMA_BOTH(256, 256, 32, 2, 4, 32, 2),
 };
 
 }  // namespace

@@ -124,7 +124,7 @@ def test_forced_config_is_honoured_or_rejected():
         plan(1024, 1024, 1024, force={"bm": 48})
     assert e.value.status == g.GEMM_ERR_UNSUPPORTED
     small = fake_gfx950()
-    small.lds_per_wg = 64 * 1024
+    small.lds_per_wg = 48 * 1024
     with pytest.raises(g.GemmError) as e:
         g.gemm_plan_create_for(g.problem(4096, 4096, 4096, g.GEMM_BF16), small, {"bm": 256, "bn": 256})
     assert e.value.status == g.GEMM_ERR_UNSUPPORTED
