@@ -96,6 +96,7 @@ class Case:
         bs = [b.data_ptr() for b in self.Bs]
         c = self.C.data_ptr() if self.C is not None else None
         d = self.D.data_ptr()
+        ws, ws_bytes = g.workspace_for(pl, torch.cuda.current_device(), stream)
         run = lib.gemm_run
         nb = len(bs)
         state = {"i": 0}
@@ -103,7 +104,7 @@ class Case:
         def launch(n):
             i = state["i"]
             for _ in range(n):
-                st = run(h, a, bs[i % nb], c, d, None, 0, stream)
+                st = run(h, a, bs[i % nb], c, d, ws, ws_bytes, stream)
                 if st != 0:
                     raise g.GemmError(st, g.gemm_last_error())
                 i += 1
@@ -198,7 +199,12 @@ def sweep(args):
                             dict(bm=64, bn=64, bk=64)],
         "square_f16_256": [dict(bm=32, bn=32, bk=32), dict(bm=64, bn=64, bk=32), dict(bm=64, bn=64, bk=64),
                            dict(bm=16, bn=64, bk=64)],
-        "skinny_bf16_16x8192": [dict(bm=16, bn=64, bk=64)],
+        "skinny_bf16_16x8192": [dict(kernel=2, bn=32, waves_n=8, bk=64, stages=3, splitk=1)] +
+                               [dict(kernel=2, bn=128, waves_n=8, bk=32, stages=2, splitk=s) for s in (4, 6)] +
+                               [dict(kernel=2, bn=128, waves_n=4, bk=32, stages=st, splitk=s)
+                                for st in (3, 4) for s in (4, 6, 8)] +
+                               [dict(kernel=2, bn=128, waves_n=2, bk=32, stages=st, splitk=s)
+                                for st in (6, 8) for s in (4, 8)],
         "tail_f16_4000x3000x1000_c": [dict(bm=256, bn=128), dict(bm=128, bn=128, bk=64), dict(bm=256, bn=256),
                                       dict(bm=128, bn=256)],
     }[args.workload]

@@ -76,6 +76,7 @@ SIGNATURES = [
     ("gemm_plan_launch", ctypes.c_int, [_p, ctypes.POINTER(_i64), ctypes.POINTER(_i32), ctypes.POINTER(_i64)]),
     ("gemm_plan_describe", ctypes.c_int, [_p, ctypes.c_char_p, ctypes.c_size_t]),
     ("gemm_workspace_size", ctypes.c_int, [_p, ctypes.POINTER(ctypes.c_size_t)]),
+    ("gemm_workspace_init", ctypes.c_int, [_p, _p, ctypes.c_size_t, _p]),
     ("gemm_run", ctypes.c_int, [_p, _p, _p, _p, _p, _p, ctypes.c_size_t, _p]),
     ("gemm", ctypes.c_int, [_p, _p, _p, _p, _i64, _i64, _i64, ctypes.POINTER(_i64), ctypes.c_int, _i32, _p]),
     ("gemm_cache_clear", None, []),
@@ -206,6 +207,10 @@ def gemm_workspace_size(plan):
     return n.value
 
 
+def gemm_workspace_init(plan, workspace, workspace_bytes, stream=None):
+    _check(lib().gemm_workspace_init(plan.handle, workspace, workspace_bytes, stream))
+
+
 def gemm_run(plan, A, B, C, D, workspace=None, workspace_bytes=0, stream=None):
     """A, B, C, D, workspace, stream: integer device addresses / hipStream_t (or None)."""
     _check(lib().gemm_run(plan.handle, A, B, C, D, workspace, workspace_bytes, stream))
@@ -284,6 +289,25 @@ def problem_for(A, B, C=None, D=None):
 
 _plan_cache = {}
 _plan_lock = threading.Lock()
+_ws_cache = {}
+
+
+def workspace_for(plan, device, stream):
+    """A zero-filled workspace of at least the plan's size, one per (device,
+    stream), grown on demand and reused (launches leave it ready for reuse).
+    Returns (address, bytes) or (None, 0)."""
+    import torch
+    need = gemm_workspace_size(plan)
+    if need == 0:
+        return None, 0
+    key = (device, stream)
+    with _plan_lock:
+        buf = _ws_cache.get(key)
+        if buf is None or buf.numel() < need:
+            # 256-byte aligned by the caching allocator; zero-filled on creation
+            buf = torch.zeros(max(need, 1 << 20), dtype=torch.uint8, device="cuda:%d" % device)
+            _ws_cache[key] = buf
+    return buf.data_ptr(), buf.numel()
 
 
 def plan_for(A, B, C=None, D=None, config=None):
@@ -317,6 +341,8 @@ def matmul(A, B, C=None, out=None, config=None, stream=None):
         stream = torch.cuda.current_stream(A.device).cuda_stream
     elif hasattr(stream, "cuda_stream"):
         stream = stream.cuda_stream
+    dev = A.device.index if A.device.index is not None else 0
+    ws, ws_bytes = workspace_for(pl, dev, stream)
     gemm_run(pl, A.data_ptr(), B.data_ptr(), C.data_ptr() if C is not None else None,
-             out.data_ptr(), None, 0, stream)
+             out.data_ptr(), ws, ws_bytes, stream)
     return out

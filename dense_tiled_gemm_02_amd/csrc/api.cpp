@@ -35,6 +35,7 @@ struct gemm_plan {
     const dtg::KernelEntry* entry;      // the chosen variant
     const dtg::KernelEntry* fallback;   // element-wise variant, for unaligned bases
     int64_t num_pid_m, num_pid_n, grid;
+    int64_t ws_bytes;                   // workspace the chosen kernel needs
 };
 
 namespace {
@@ -127,7 +128,7 @@ bool matches(const dtg::KernelEntry* e, const gemm_config& f) {
            (f.bn == 0 || f.bn == e->bn) && (f.bk == 0 || f.bk == e->bk) &&
            (f.stages == 0 || f.stages == e->stages) && (f.mfma == 0 || f.mfma == e->mfma) &&
            (f.waves_m == 0 || f.waves_m == e->waves_m) && (f.waves_n == 0 || f.waves_n == e->waves_n) &&
-           (f.splitk == 0 || f.splitk == e->splitk);
+           (f.splitk == 0 || e->splitk == 0 || f.splitk == e->splitk);
 }
 
 // The first compiled variant that fits the device and matches `want`.
@@ -167,10 +168,30 @@ const std::vector<TunedKey>& tuned_table() {
 
 // Regime heuristic.  Square / tail problems take the largest tile that still
 // gives every CU at least one workgroup; skinny M takes a short-M tile.
-gemm_config heuristic(const gemm_problem* p, const gemm_device_info& dev, int* group_m) {
-    const int64_t M = p->M, N = p->N;
+gemm_config heuristic(const gemm_problem* p, const gemm_device_info& dev, int* group_m, bool allow_ws) {
+    const int64_t M = p->M, N = p->N, K = p->K;
     *group_m = 8;
-    if (M <= 16) return cfg_of(dtg::KF_TILE, 16, 64, 64, 2, 16, 1, 4);
+    if (M <= 16) {
+        // Stream B.  Each workgroup reads a 256-byte band of every row of its
+        // K slice (HBM needs >= 128-byte runs), and the K slices supply the
+        // workgroups: S = CUs / slabs (one workgroup per CU: these kernels
+        // hold most of the LDS), at most 8, each slice >= 512 k.
+        if (allow_ws && cdiv(N, 128) <= 4096) {
+            const int64_t slabs = cdiv(N, 128);
+            int64_t s = dev.cu_count / (slabs > 0 ? slabs : 1);
+            if (s > 8) s = 8;
+            while (s > 1 && K / s < 512) --s;
+            if (s < 1) s = 1;
+            gemm_config c = cfg_of(dtg::KF_SKINNY, 16, 128, 32, 2, 16, 1, 8);
+            c.splitk = static_cast<int32_t>(s);
+            return c;
+        }
+        // no workspace: one workgroup per 32-column slab, K split over its 8 waves
+        const int bn = (cdiv(N, 32) >= dev.cu_count) ? 32 : 16;
+        gemm_config c = cfg_of(dtg::KF_SKINNY, 16, bn, 64, 3, 16, 1, 8);
+        c.splitk = 1;
+        return c;
+    }
     if (M <= 32) return cfg_of(dtg::KF_TILE, 32, 32, 32, 2, 16, 2, 2);
     struct C { int fam, bm, bn, bk, st, mf, wm, wn; };
     static const C ladder[] = {
@@ -189,7 +210,7 @@ gemm_config heuristic(const gemm_problem* p, const gemm_device_info& dev, int* g
 }
 
 gemm_status plan_impl(const gemm_problem* prob, const gemm_device_info* dev, const gemm_config* force,
-                      gemm_plan** out) {
+                      gemm_plan** out, bool allow_ws = true) {
     if (!out) return fail(GEMM_ERR_INVALID_ARG, "out is NULL");
     *out = nullptr;
     gemm_status st = validate(prob);
@@ -212,7 +233,7 @@ gemm_status plan_impl(const gemm_problem* prob, const gemm_device_info* dev, con
             break;
         }
     }
-    if (!tuned) want = heuristic(prob, *dev, &group_m);
+    if (!tuned) want = heuristic(prob, *dev, &group_m, allow_ws);
     if (force) {
         // Any forced tile field replaces the planner's tile; the tile fields
         // left at 0 are then free (the first compiled variant that matches).
@@ -249,6 +270,16 @@ gemm_status plan_impl(const gemm_problem* prob, const gemm_device_info* dev, con
                         want.bm, want.bn, want.bk, want.stages, want.mfma, want.waves_m, want.waves_n,
                         want.kernel, (int)prob->dtype, (int)vec, (long long)dev->lds_per_wg);
     }
+    if (e->family == dtg::KF_SKINNY && prob->M > 16)
+        return fail(GEMM_ERR_UNSUPPORTED, "the skinny kernel family runs M <= 16 only (M=%lld)",
+                    (long long)prob->M);
+    int splits = 1;
+    if (e->family == dtg::KF_SKINNY) {
+        splits = want.splitk > 0 ? want.splitk : 1;
+        if (splits > 64) return fail(GEMM_ERR_UNSUPPORTED, "at most 64 K slices (splitk=%d)", splits);
+        if (splits > 1 && !allow_ws)
+            return fail(GEMM_ERR_UNSUPPORTED, "K slices across workgroups need a workspace");
+    }
     gemm_plan* pl = new (std::nothrow) gemm_plan;
     if (!pl) return fail(GEMM_ERR_INVALID_ARG, "out of host memory");
     pl->prob = *prob;
@@ -257,11 +288,16 @@ gemm_status plan_impl(const gemm_problem* prob, const gemm_device_info* dev, con
     pl->fallback = fb;
     pl->num_pid_m = cdiv(prob->M, e->bm);
     pl->num_pid_n = cdiv(prob->N, e->bn);
-    pl->grid = pl->num_pid_m * pl->num_pid_n;
+    pl->grid = pl->num_pid_m * pl->num_pid_n * splits;
+    pl->ws_bytes = e->family == dtg::KF_SKINNY ? dtg::skinny_workspace_bytes(pl->num_pid_n, e->bn, splits) : 0;
+    if (pl->ws_bytes < 0) {
+        delete pl;
+        return fail(GEMM_ERR_UNSUPPORTED, "K slices across workgroups support at most 4096 column slabs");
+    }
     if (group_m < 1) group_m = 1;
     gemm_config& c = pl->cfg;
     c = cfg_of(e->family, e->bm, e->bn, e->bk, e->stages, e->mfma, e->waves_m, e->waves_n);
-    c.splitk = e->splitk;
+    c.splitk = e->family == dtg::KF_SKINNY ? splits : e->splitk;
     c.group_m = group_m;
     c.xcd_remap = (xcd && dev->xcd_count > 1) ? GEMM_XCD_ON : GEMM_XCD_OFF;
     if (log_enabled()) {
@@ -401,14 +437,23 @@ gemm_status gemm_plan_describe(const gemm_plan* plan, char* buf, size_t len) {
 
 gemm_status gemm_workspace_size(const gemm_plan* plan, size_t* bytes) {
     if (!plan || !bytes) return fail(GEMM_ERR_INVALID_ARG, "plan or bytes is NULL");
-    *bytes = 0;
+    *bytes = static_cast<size_t>(plan->ws_bytes);
+    return ok();
+}
+
+gemm_status gemm_workspace_init(const gemm_plan* plan, void* workspace, size_t workspace_bytes, void* stream) {
+    if (!plan) return fail(GEMM_ERR_INVALID_ARG, "plan is NULL");
+    if (plan->ws_bytes == 0) return ok();
+    if (!workspace || workspace_bytes < static_cast<size_t>(plan->ws_bytes))
+        return fail(GEMM_ERR_WORKSPACE, "workspace of %zu bytes given, %lld needed", workspace_bytes,
+                    (long long)plan->ws_bytes);
+    hipError_t e = dtg::zero_words(workspace, plan->ws_bytes / 4, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(GEMM_ERR_HIP, "workspace zero fill: %s", hipGetErrorString(e));
     return ok();
 }
 
 gemm_status gemm_run(const gemm_plan* plan, const void* A, const void* B, const void* C, void* D,
                      void* workspace, size_t workspace_bytes, void* stream) {
-    (void)workspace;
-    (void)workspace_bytes;
     if (!plan) return fail(GEMM_ERR_INVALID_ARG, "plan is NULL");
     const gemm_problem& p = plan->prob;
     if (p.has_c && !C) return fail(GEMM_ERR_INVALID_ARG, "problem has C but C is NULL");
@@ -433,6 +478,12 @@ gemm_status gemm_run(const gemm_plan* plan, const void* A, const void* B, const 
             return fail(GEMM_ERR_INVALID_ARG, "D overlaps C (only D == C with equal strides is allowed)");
     }
     const dtg::KernelEntry* e = plan->entry;
+    const bool needs_ws = plan->ws_bytes > 0;
+    if (needs_ws && (!workspace || workspace_bytes < static_cast<size_t>(plan->ws_bytes)))
+        return fail(GEMM_ERR_WORKSPACE, "plan needs a workspace of %lld bytes (%zu given)",
+                    (long long)plan->ws_bytes, workspace ? workspace_bytes : static_cast<size_t>(0));
+    if (needs_ws && (reinterpret_cast<uintptr_t>(workspace) & 255))
+        return fail(GEMM_ERR_WORKSPACE, "workspace must be 256-byte aligned");
     if (e->vec && p.K > 0 &&
         ((reinterpret_cast<uintptr_t>(A) & 15) || (reinterpret_cast<uintptr_t>(B) & 15)))
         e = plan->fallback;   // element-wise loads; bitwise identical for 16x16x32 plans
@@ -453,7 +504,9 @@ gemm_status gemm_run(const gemm_plan* plan, const void* A, const void* B, const 
     a.ldb = p.sb_k;
     a.ldc = p.has_c ? p.sc_m : 0;
     a.ldd = p.sd_m;
-    const int64_t grid = static_cast<int64_t>(a.num_pid_m) * a.num_pid_n;
+    a.splits = (e == plan->entry && e->family == dtg::KF_SKINNY) ? plan->cfg.splitk : 1;
+    a.ws = workspace;
+    const int64_t grid = static_cast<int64_t>(a.num_pid_m) * a.num_pid_n * a.splits;
     hipError_t err = e->launch(a, grid, static_cast<hipStream_t>(stream));
     if (err != hipSuccess) return fail(GEMM_ERR_HIP, "launch of %s: %s", e->name, hipGetErrorString(err));
     return ok();
@@ -485,7 +538,10 @@ gemm_status gemm(const void* A, const void* B, const void* C, void* D, int64_t M
             plan = it->second.get();
         } else {
             gemm_plan* np = nullptr;
-            gemm_status st = gemm_plan_create(&p, device, nullptr, &np);
+            gemm_device_info info;
+            gemm_status st = device_info_cached(device, &info);
+            if (st != GEMM_OK) return st;
+            st = plan_impl(&p, &info, nullptr, &np, /*allow_ws=*/false);
             if (st != GEMM_OK) return st;
             g_cache[key].reset(np);
             plan = np;

@@ -38,18 +38,6 @@ namespace {
 
 using namespace dev;
 
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef short i16x8 __attribute__((ext_vector_type(8)));
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
-
-typedef std::integral_constant<bool, true> T;    // checked loads (edges, K tail)
-typedef std::integral_constant<bool, false> F;   // interior loads
-
-constexpr uint32_t kRsrcWord3 = 0x00020000u;   // raw buffer of dwords
-constexpr uint32_t kOOB = 0x80000000u;         // offset past any descriptor range
-constexpr int64_t kMaxRecords = 0x7ffffff0;
-
 // Swizzle of the B tile (rows of BN contiguous n, CHB 16-byte chunks per row):
 // physical chunk = logical chunk ^ bsw(r).  Even values keep the two chunks a
 // 16-lane group reads from one row adjacent; the 4 (or 8) rows one transposing
@@ -61,57 +49,6 @@ __device__ __forceinline__ int bsw(int r) {
 }
 
 // wait until at most N vector-memory operations of this wave are outstanding
-template <int N, typename Fn>
-__device__ __forceinline__ void static_for(Fn&& fn) {
-    if constexpr (N > 0) {
-        static_for<N - 1>(fn);
-        fn(std::integral_constant<int, N - 1>{});
-    }
-}
-
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-    static_assert(N >= 0 && N < 64, "vmcnt");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-// LDS operand reads are issued as inline asm: the compiler then neither
-// guards them with waits for every outstanding global -> LDS load (it cannot
-// tell which stage a read touches) nor moves them; the kernel waits for them
-// explicitly with lds_wait_all() + tie() before the MFMAs that use them.
-//
-// 16-byte read at LDS byte address addr + OFF.
-template <int OFF>
-__device__ __forceinline__ u32x4 lds_read16(uint32_t addr) {
-    u32x4 v;
-    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
-    return v;
-}
-
-// Transposing 64-bit read (ds_read_b64_tr_b16) at addr + OFF: within each
-// 16-lane group the 16 addressed 8-byte pieces, in lane order, form a 4 x 16
-// matrix of halfwords (lanes 4i..4i+3 give row i); lane t receives column t.
-template <int OFF>
-__device__ __forceinline__ i16x4 lds_read_tr(uint32_t addr) {
-    i16x4 v;
-    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
-    return v;
-}
-
-__device__ __forceinline__ void lds_wait_all() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
-
-// Make `v` depend on the preceding lds_wait_all() (volatile asm keeps its
-// order), so no use of v is scheduled before the wait.
-__device__ __forceinline__ void tie(u32x4& v) { asm volatile("" : "+v"(v)); }
-
-__device__ __forceinline__ uint32_t lds_addr(const uint16_t* p) {
-    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) uint16_t*)p));
-}
-
-__device__ __forceinline__ uint32_t clamp_records(int64_t bytes) {
-    return static_cast<uint32_t>(bytes < kMaxRecords ? bytes : kMaxRecords);
-}
-
 template <int BM, int BN, int BK, int WM, int WN, int MF, int ST, bool BF16>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(KArgs p) {
     constexpr int NW = WM * WN;
@@ -277,8 +214,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(KArgs p) {
     const int nkt = (K + BK - 1) / BK;
     const int nfull = K / BK;
     auto issue_tile = [&](int kt, int st) {
-        if (!edge && kt < nfull) issue(F{}, kt, st);
-        else issue(T{}, kt, st);
+        if (!edge && kt < nfull) issue(Unchecked{}, kt, st);
+        else issue(Checked{}, kt, st);
     };
 
     // One K step on LDS stage S.  On entry the fragments of sub-step 0 are in

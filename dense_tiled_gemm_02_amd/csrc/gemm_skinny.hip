@@ -1,14 +1,360 @@
-// Skinny-M kernels (M of a few rows, large N and K): bandwidth-bound regime.
+// Skinny-M GEMM kernel for gfx950:  D = A x B (+ C) with M <= 16.
+//
+// With a handful of rows the product is bound by streaming B from HBM (the
+// decode regime of "Tuning Triton", section 4: a skinny M wants its own tile
+// family, BM = 16 with a deep K).  K is split twice ("Tuning Triton", section
+// 6: a K split is the axis that matters at M = 16; "Hopper Support in
+// Triton", slides 15-16: SPLIT_K): across S workgroups per BN-column slab of D
+// (S is a launch parameter) and, inside a workgroup, across its NWV waves.
+// HBM streams well only when each workgroup reads at least a 128-byte band of
+// every row of B, so slabs are 64 or 128 columns wide and S supplies the
+// parallelism (N = 8192, BN = 128, S = 4: 256 workgroups).
+// Each wave streams its K range in CK-deep chunks through a private ST-stage
+// LDS ring with direct global -> LDS loads (B rows of BN columns, A rows of
+// CK k), so no workgroup barrier is needed until the end; the A operand is
+// read with 16-byte LDS reads and the B operand with the transposing 64-bit
+// LDS read, and one v_mfma_f32_16x16x32 per 16 columns per 32 k accumulates
+// in fp32.  The NWV partial 16 x BN tiles are then summed through LDS in a
+// fixed wave order.  With S = 1 the workgroup then adds C in fp32, rounds and
+// stores rows < M, columns < N.  With S > 1 it writes its fp32 partial tile to
+// the workspace and counts itself in on the slab's counter; the workgroup that
+// arrives last sums the S partials in slice order (so the result does not
+// depend on arrival order), adds C, rounds, stores, and resets the counter to
+// zero for the next launch.  The counters sit in a fixed region at the head of
+// the workspace, so one zero-filled workspace serves every plan in turn.
+//
+// Out-of-range rows of A (>= M), columns of B (>= N) and k (>= K) are loaded
+// as zeros through buffer offsets past the descriptor range.
+
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "device_common.h"
 #include "kernels.h"
+#include "tile_order.h"
 
 namespace dtg {
+namespace {
+
+using namespace dev;
+
+// B stage layout: CK rows of BN contiguous columns.  One transposing read
+// touches rows 8 g + 4 h + 0..3 for lane groups g; these layouts keep the
+// rows of groups g and g + 1 in different banks:
+//  BN = 32 (64-byte rows): the two 32-byte halves of a row swap when bit 3
+//          of the row index is set;
+//  BN = 16 (32-byte rows): rows 8..15 of every 16 are stored in the order
+//          12..15, 8..11 (row r sits at position r ^ (4 * bit 3 of r));
+//  BN = 64 (128-byte rows): chunk pairs XOR 2 * (bit 1 of r | bit 3 of r << 1),
+//          so the 8 rows two neighbouring lane groups read tile one 256-byte
+//          bank window;
+//  BN = 128, 256 (256-, 512-byte rows): chunk pairs XOR 2 * ((r & 3) | bit 3
+//          of r << 2).
+// All these maps are involutions.
+// The workspace starts with a fixed region of kMaxSlabs arrival counters, the
+// same for every plan, so plans of any slab count can share one workspace;
+// fp32 partial tiles follow.
+constexpr int kMaxSlabs = 4096;
+constexpr int64_t kCounterBytes = kMaxSlabs * 4;
+
+template <int BN>
+__device__ __forceinline__ int b_pos(int r) {
+    if constexpr (BN == 16) return r ^ (((r >> 3) & 1) << 2);
+    else return r;
+}
+template <int BN>
+__device__ __forceinline__ int b_chunk(int r, int q) {
+    if constexpr (BN == 32) return q ^ (((r >> 3) & 1) << 1);
+    else if constexpr (BN == 64) return q ^ (2 * (((r >> 1) & 1) | (((r >> 3) & 1) << 1)));
+    else if constexpr (BN >= 128) return q ^ (2 * ((r & 3) | (((r >> 3) & 1) << 2)));
+    else return q;
+}
+
+template <int BN, int NWV, int CK, int ST, bool BF16>
+__global__ __launch_bounds__(64 * NWV) void gemm_skinny_kernel(KArgs p) {
+    constexpr int NT = 64 * NWV;
+    constexpr int CHB = BN / 8;            // 16-byte chunks per B row
+    constexpr int RB = 64 / CHB;           // B rows per wave instruction
+    constexpr int IB = CK / RB;            // B instructions per chunk
+    constexpr int CHA = CK / 8;            // 16-byte chunks per A row
+    constexpr int RA = 64 / CHA;           // A rows per wave instruction
+    constexpr int IA = 16 / RA;            // A instructions per chunk
+    constexpr int FN = BN / 16;
+    constexpr int KSN = CK / 32;
+    constexpr int SB = CK * BN, SAE = 16 * CK, STG = SB + SAE;   // elements
+    constexpr int OPS = IB + IA;           // vector-memory ops per chunk
+    static_assert(BN == 16 || BN == 32 || BN == 64 || BN == 128 || BN == 256, "BN");
+    static_assert(CK == 32 || CK == 64, "CK");
+    static_assert(IA >= 1 && IB >= 1, "load split");
+    static_assert(ST >= 2 && ST <= 8 && (ST - 2) * OPS < 64, "stages");
+    static_assert(NWV * ST * STG * 2 >= NWV * 16 * BN * 4 + 4, "reduction buffer and flag");
+    static_assert(OPS < 64, "vmcnt");
+
+    __shared__ __attribute__((aligned(1024))) uint16_t smem[NWV * ST * STG];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    // Workgroup -> (slab, slice): consecutive positions are consecutive slabs of
+    // one slice, and the XCD permutation gives each die one contiguous run of
+    // positions, so a die's L2 sees whole rows of a band of columns.
+    const int nslabs = p.num_pid_n;
+    const int S = p.splits;
+    const int pos = xcd_permute<int>(blockIdx.x, gridDim.x, p.xcds);
+    const int slab = pos % nslabs, slice = pos / nslabs;
+    const int n0 = slab * BN;
+    const int M = p.M, N = p.N, K = p.K;
+
+    // chunks of this slice, then of this wave
+    const int nck = (K + CK - 1) / CK;
+    const int per_slice = (nck + S - 1) / S;
+    const int s_first = slice * per_slice;
+    const int s_end = (s_first + per_slice < nck) ? s_first + per_slice : nck;
+    const int s_n = s_end > s_first ? s_end - s_first : 0;
+    const int per = (s_n + NWV - 1) / NWV;
+    const int c_first = s_first + wave * per;
+    const int c_last = (wave * per + per < s_n) ? c_first + per : s_first + s_n;
+    const int nc = c_last > c_first ? c_last - c_first : 0;
+
+    // ---- per-lane load offsets (bytes from the per-chunk descriptors)
+    uint32_t b_voff[IB];
+    int b_row[IB];
+    bool b_ok[IB];
+#pragma unroll
+    for (int i = 0; i < IB; ++i) {
+        const int pos = i * RB + lane / CHB;
+        const int r = b_pos<BN>(pos);
+        const int q = b_chunk<BN>(r, lane % CHB);
+        b_row[i] = r;
+        b_ok[i] = n0 + 8 * q < N;
+        b_voff[i] = static_cast<uint32_t>(static_cast<int64_t>(r) * p.ldb * 2 + q * 16);
+    }
+    uint32_t a_voff[IA];
+    int a_kc[IA];
+    bool a_ok[IA];
+#pragma unroll
+    for (int i = 0; i < IA; ++i) {
+        const int row = i * RA + lane / CHA;
+        const int q = (lane % CHA) ^ swz<CHA>(row);
+        a_ok[i] = row < M;
+        a_kc[i] = 8 * q;
+        a_voff[i] = static_cast<uint32_t>(static_cast<int64_t>(row) * p.lda * 2 + q * 16);
+    }
+
+    auto issue = [&](int c, int slot) {
+        const int k0 = (c_first + c) * CK;
+        const uint16_t* bbase = p.B + static_cast<int64_t>(k0) * p.ldb + n0;
+        const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t*>(bbase), 0,
+            clamp_records((static_cast<int64_t>(K - 1 - k0) * p.ldb + (N - n0)) * 2), kRsrcWord3);
+        const uint16_t* abase = p.A + k0;
+        const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t*>(abase), 0,
+            clamp_records((static_cast<int64_t>(M - 1) * p.lda + (K - k0)) * 2), kRsrcWord3);
+        uint16_t* sb = smem + (wave * ST + slot) * STG;
+        uint16_t* sa = sb + SB;
+#pragma unroll
+        for (int i = 0; i < IB; ++i) {
+            const uint32_t v = (b_ok[i] && k0 + b_row[i] < K) ? b_voff[i] : kOOB;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void_t*)(sb + i * 512), 16, v, 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < IA; ++i) {
+            const uint32_t v = (a_ok[i] && k0 + a_kc[i] < K) ? a_voff[i] : kOOB;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t*)(sa + i * 512), 16, v, 0, 0, 0);
+        }
+    };
+
+    // ---- per-lane operand read offsets (LDS bytes within a stage)
+    uint32_t a_off[KSN], b_off[FN][KSN][2];
+    {
+        const int i = lane & 15, g = lane >> 4;
+#pragma unroll
+        for (int ks = 0; ks < KSN; ++ks)
+            a_off[ks] = (SB + i * CK + (((ks * 4 + g) ^ swz<CHA>(i)) * 8)) * 2;   // chunk ks*4 + g of row i
+        const int jq = lane & 15;
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+            for (int ks = 0; ks < KSN; ++ks)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int r = ks * 32 + 8 * g + 4 * h + (jq >> 2);
+                    const int col = fn * 16 + 4 * (jq & 3);
+                    const int ph = b_chunk<BN>(r, col >> 3);
+                    b_off[fn][ks][h] = (b_pos<BN>(r) * BN + ph * 8 + (col & 7)) * 2;
+                }
+    }
+
+    f32x4 acc[FN];
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) acc[fn] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    const uint32_t ring = lds_addr(smem) + wave * ST * STG * 2;
+#pragma unroll
+    for (int s = 0; s < ST - 1; ++s)
+        if (s < nc) issue(s, s);
+    for (int c = 0; c < nc; ++c) {
+        // chunk c is complete once at most the chunks issued after it remain
+        // in flight: min(ST - 2, nc - 1 - c) chunks of OPS loads each
+        const int after = (nc - 1 - c < ST - 2) ? (nc - 1 - c) : (ST - 2);
+        static_for<ST - 1>([&](auto i_tag) {
+            constexpr int I = decltype(i_tag)::value;
+            if (after == I) wait_vm<I * OPS>();
+        });
+        const int slot = c % ST;
+        if (c + ST - 1 < nc) issue(c + ST - 1, (c + ST - 1) % ST);
+        const uint32_t base = ring + slot * STG * 2;
+        u32x4 af[KSN], bf[FN][KSN];
+#pragma unroll
+        for (int ks = 0; ks < KSN; ++ks) af[ks] = lds_read16<0>(base + a_off[ks]);
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+            for (int ks = 0; ks < KSN; ++ks) {
+                const i16x4 h0 = lds_read_tr<0>(base + b_off[fn][ks][0]);
+                const i16x4 h1 = lds_read_tr<0>(base + b_off[fn][ks][1]);
+                bf[fn][ks] = __builtin_bit_cast(u32x4, __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7));
+            }
+        lds_wait_all();
+#pragma unroll
+        for (int ks = 0; ks < KSN; ++ks) tie(af[ks]);
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+            for (int ks = 0; ks < KSN; ++ks) tie(bf[fn][ks]);
+#pragma unroll
+        for (int ks = 0; ks < KSN; ++ks)
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn) acc[fn] = mfma<16, BF16>(af[ks], bf[fn][ks], acc[fn]);
+    }
+
+    // ---- sum the wave partials in a fixed order, + C, round, store
+    __syncthreads();                                   // every ring is drained
+    float* red = reinterpret_cast<float*>(smem);       // [NWV][16][BN]
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            red[(wave * 16 + 4 * (lane >> 4) + r) * BN + fn * 16 + (lane & 15)] = acc[fn][r];
+    __syncthreads();
+    const bool has_c = p.has_c != 0;
+    if (S == 1) {
+        for (int t = tid; t < 16 * BN; t += NT) {
+            const int row = t / BN, col = t % BN;
+            float v = 0.0f;
+#pragma unroll
+            for (int w = 0; w < NWV; ++w) v += red[(w * 16 + row) * BN + col];
+            if (row < M && n0 + col < N) {
+                if (has_c) v += widen<BF16>(p.C[static_cast<int64_t>(row) * p.ldc + n0 + col]);
+                p.D[static_cast<int64_t>(row) * p.ldd + n0 + col] = narrow<BF16>(v);
+            }
+        }
+        return;
+    }
+    // ---- S > 1: partial tile -> workspace; the last workgroup of the slab sums.
+    // The partials are written and read with system-scope accesses, which go
+    // past the (per-XCD, mutually non-coherent) L2 caches to memory; each wave
+    // waits until its writes have completed before the barrier that precedes
+    // the arrival count, so a workgroup that counts itself in has its partial
+    // in memory, and the last arriver reads every partial from memory.  This
+    // avoids writing back or invalidating whole L2 caches.
+    int* counters = static_cast<int*>(p.ws);
+    float* part = reinterpret_cast<float*>(static_cast<char*>(p.ws) + kCounterBytes) +
+                  static_cast<int64_t>(slab) * S * 16 * BN;
+    for (int t = tid; t < 16 * BN; t += NT) {
+        float v = 0.0f;
+#pragma unroll
+        for (int w = 0; w < NWV; ++w) v += red[(w * 16 + t / BN) * BN + t % BN];
+        __hip_atomic_store(&part[slice * 16 * BN + t], v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    }
+    wait_vm<0>();
+    __syncthreads();
+    int* last = reinterpret_cast<int*>(red + NWV * 16 * BN);   // just past the partial sums
+    if (tid == 0)
+        *last = __hip_atomic_fetch_add(&counters[slab], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) == S - 1;
+    __syncthreads();
+    if (!*last) return;
+    for (int t = tid; t < 16 * BN; t += NT) {
+        const int row = t / BN, col = t % BN;
+        float v = 0.0f;
+        // up to 8 slices' loads in flight at once, summed in slice order
+        for (int s0 = 0; s0 < S; s0 += 8) {
+            float x[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                x[u] = s0 + u < S ? __hip_atomic_load(&part[(s0 + u) * 16 * BN + t], __ATOMIC_RELAXED,
+                                                      __HIP_MEMORY_SCOPE_SYSTEM)
+                                  : 0.0f;
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                if (s0 + u < S) v += x[u];
+        }
+        if (row < M && n0 + col < N) {
+            if (has_c) v += widen<BF16>(p.C[static_cast<int64_t>(row) * p.ldc + n0 + col]);
+            p.D[static_cast<int64_t>(row) * p.ldd + n0 + col] = narrow<BF16>(v);
+        }
+    }
+    if (tid == 0) __hip_atomic_store(&counters[slab], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
+template <int BN, int NWV, int CK, int ST, bool BF16>
+hipError_t launch_skinny(const KArgs& a, int64_t grid, hipStream_t stream) {
+    hipLaunchKernelGGL((gemm_skinny_kernel<BN, NWV, CK, ST, BF16>), dim3(static_cast<unsigned>(grid)),
+                       dim3(64 * NWV), 0, stream, a);
+    return hipGetLastError();
+}
+
+#define DTG_STR2(x) #x
+#define DTG_STR(x) DTG_STR2(x)
+#define SKINNY_ENTRY(BN, NWV, CK, ST, BF)                                                    \
+    {KF_SKINNY, 16, BN, CK, ST, 16, 1, NWV, 0, BF, 1, 64 * NWV,                             \
+     static_cast<int64_t>(NWV) * ST * (CK * BN + 16 * CK) * 2,                              \
+     &launch_skinny<BN, NWV, CK, ST, (BF != 0)>,                                            \
+     "gemm_skinny_kernel<" DTG_STR(BN) "," DTG_STR(NWV) "," DTG_STR(CK) "," DTG_STR(ST) ","  \
+     DTG_STR(BF) ">"}
+#define SKINNY_BOTH(BN, NWV, CK, ST) SKINNY_ENTRY(BN, NWV, CK, ST, 0), SKINNY_ENTRY(BN, NWV, CK, ST, 1)
+
+const KernelEntry kSkinnyTable[] = {
+    SKINNY_BOTH(256, 4, 32, 2),
+    SKINNY_BOTH(128, 4, 32, 3),
+    SKINNY_BOTH(128, 4, 32, 4),
+    SKINNY_BOTH(128, 2, 32, 8),
+    SKINNY_BOTH(128, 2, 32, 6),
+    SKINNY_BOTH(128, 8, 32, 2),
+    SKINNY_BOTH(64, 4, 64, 3),
+    SKINNY_BOTH(64, 8, 64, 2),
+    SKINNY_BOTH(32, 8, 64, 3),
+    SKINNY_BOTH(16, 8, 64, 3),
+};
+
+}  // namespace
+
+namespace {
+__global__ __launch_bounds__(256) void zero_words_kernel(uint32_t* p, int64_t n) {
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n;
+         i += static_cast<int64_t>(gridDim.x) * 256)
+        p[i] = 0u;
+}
+}  // namespace
+
+hipError_t zero_words(void* p, int64_t nwords, hipStream_t stream) {
+    if (nwords <= 0) return hipSuccess;
+    const int64_t blocks = (nwords + 255) / 256;
+    const unsigned grid = static_cast<unsigned>(blocks < 1024 ? blocks : 1024);
+    hipLaunchKernelGGL(zero_words_kernel, dim3(grid), dim3(256), 0, stream, static_cast<uint32_t*>(p), nwords);
+    return hipGetLastError();
+}
+
+int64_t skinny_workspace_bytes(int64_t nslabs, int bn, int splits) {
+    if (splits <= 1) return 0;
+    if (nslabs > kMaxSlabs) return -1;
+    return kCounterBytes + nslabs * splits * 16 * bn * 4;
+}
 
 const KernelEntry* skinny_kernel_table(int* count) {
-    *count = 0;
-    return nullptr;
+    *count = static_cast<int>(sizeof(kSkinnyTable) / sizeof(kSkinnyTable[0]));
+    return kSkinnyTable;
 }
 
 }  // namespace dtg

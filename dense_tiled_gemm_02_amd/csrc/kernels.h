@@ -18,7 +18,9 @@ struct KArgs {
     int32_t group_m;
     int32_t xcds;        // 1: no XCD pre-permutation
     int32_t has_c;
+    int32_t splits;      // K slices across workgroups (skinny kernels; 1 = none)
     int64_t lda, ldb, ldc, ldd;
+    void* ws;            // workspace: per-slab counters, then fp32 partial tiles
 };
 
 typedef hipError_t (*launch_fn)(const KArgs& args, int64_t grid, hipStream_t stream);
@@ -43,5 +45,13 @@ struct KernelEntry {
 const KernelEntry* tile_kernel_table(int* count);
 const KernelEntry* skinny_kernel_table(int* count);
 const KernelEntry* dma_kernel_table(int* count);
+
+// Workspace bytes of a skinny launch over nslabs slabs of bn columns split
+// into `splits` K slices (0 when splits == 1, -1 when nslabs is above the
+// fixed counter region).
+int64_t skinny_workspace_bytes(int64_t nslabs, int bn, int splits);
+
+// Enqueue a kernel that writes zeros to nwords 32-bit words at p.
+hipError_t zero_words(void* p, int64_t nwords, hipStream_t stream);
 
 }  // namespace dtg

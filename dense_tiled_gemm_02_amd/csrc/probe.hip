@@ -98,9 +98,141 @@ __global__ __launch_bounds__(64) void probe_lds_dma_kernel(const uint16_t* in, u
     for (int i = l; i < 1024; i += 64) out[i] = lds[i];
 }
 
+// Streaming reads of `bytes` bytes (a multiple of 16) for a read-bandwidth
+// reference: every thread walks the buffer in a grid-stride loop of 16-byte
+// loads, U loads in flight per thread; the XOR of all loaded words goes to
+// out[blockIdx.x] so the loads are not dead.  Every address is < bytes.
+template <int U>
+__global__ __launch_bounds__(256) void probe_stream_read_kernel(const u32x4* in, uint64_t n16, uint32_t* out) {
+    const uint64_t stride = static_cast<uint64_t>(gridDim.x) * 256;
+    uint64_t i = static_cast<uint64_t>(blockIdx.x) * 256 + threadIdx.x;
+    u32x4 acc = {0, 0, 0, 0};
+    for (; i + (U - 1) * stride < n16; i += U * stride) {
+        u32x4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) v[u] = __builtin_nontemporal_load(in + i + u * stride);
+#pragma unroll
+        for (int u = 0; u < U; ++u) acc ^= v[u];
+    }
+    for (; i < n16; i += stride) acc ^= in[i];
+    uint32_t x = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+    for (int o = 32; o > 0; o >>= 1) x ^= __shfl_xor(x, o);
+    __shared__ uint32_t red[4];
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
+    __syncthreads();
+    if (threadIdx.x == 0) out[blockIdx.x] = red[0] ^ red[1] ^ red[2] ^ red[3];
+}
+
+// Band reads: the buffer is `rows` rows of `row_bytes`; workgroup w reads the
+// column band [band * (w % nbands), band * (w % nbands + 1)) of rows
+// [rows_per * (w / nbands), rows_per * (w / nbands + 1)), 16 bytes per lane,
+// each wave instruction covering 1024 / band consecutive rows.  Reports the
+// bandwidth of a column-slab access pattern.  Every address is inside
+// rows * row_bytes (band divides row_bytes, rows_per divides rows).
+__global__ __launch_bounds__(256) void probe_band_read_kernel(const uint8_t* in, int rows, int row_bytes,
+                                                              int band, int rows_per, uint32_t* out) {
+    const int nbands = row_bytes / band;
+    const int b = blockIdx.x % nbands, slice = blockIdx.x / nbands;
+    const int lanes_per_row = band / 16;
+    const int rows_per_iter = 256 / lanes_per_row;
+    const int t = threadIdx.x;
+    const int r_in = t / lanes_per_row, c = (t % lanes_per_row) * 16;
+    u32x4 acc = {0, 0, 0, 0};
+    const int r0 = slice * rows_per;
+    for (int r = r0 + r_in; r < r0 + rows_per; r += 4 * rows_per_iter) {
+        u32x4 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int rr = r + u * rows_per_iter;
+            v[u] = rr < r0 + rows_per
+                       ? *reinterpret_cast<const u32x4*>(in + static_cast<int64_t>(rr) * row_bytes + b * band + c)
+                       : u32x4{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) acc ^= v[u];
+    }
+    uint32_t x = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+    for (int o = 32; o > 0; o >>= 1) x ^= __shfl_xor(x, o);
+    __shared__ uint32_t red[4];
+    if ((t & 63) == 0) red[t >> 6] = x;
+    __syncthreads();
+    if (t == 0) out[blockIdx.x] = red[0] ^ red[1] ^ red[2] ^ red[3];
+}
+
+// Band reads straight into LDS: same geometry as probe_band_read_kernel, but
+// each wave issues 16-byte buffer loads into an 8-slot LDS ring of its own
+// (1 KB per slot), keeping at most 7 loads in flight before reusing a slot.
+// Nothing reads the LDS; out gets one word per workgroup.  Every global offset
+// is < rows * row_bytes; LDS use is 4 waves x 8 KB.
+__global__ __launch_bounds__(256) void probe_band_read_lds_kernel(const uint8_t* in, int rows, int row_bytes,
+                                                                  int band, int rows_per, uint32_t* out) {
+    __shared__ __attribute__((aligned(1024))) uint8_t ring[4 * 8 * 1024];
+    const int nbands = row_bytes / band;
+    const int b = blockIdx.x % nbands, slice = blockIdx.x / nbands;
+    const int lanes_per_row = band / 16;
+    const int rows_per_inst = 64 / lanes_per_row;             // rows one wave instruction covers
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int r_in = lane / lanes_per_row, c = (lane % lanes_per_row) * 16;
+    const int r0 = slice * rows_per;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(in), 0, 0x7ffffff0, 0x00020000);
+    typedef __attribute__((address_space(3))) void lds_void;
+    int it = 0;
+    for (int r = r0 + wave * rows_per_inst; r < r0 + rows_per; r += 4 * rows_per_inst, ++it) {
+        const int rr = r + r_in;
+        const int64_t off = static_cast<int64_t>(rr) * row_bytes + b * band + c;
+        // offsets within the 2 GiB descriptor range (the probe uses < 2 GiB)
+        const uint32_t v = rr < r0 + rows_per ? static_cast<uint32_t>(off) : 0x80000000u;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(ring + (wave * 8 + (it & 7)) * 1024), 16, v,
+                                                 0, 0, 0);
+        __builtin_amdgcn_s_waitcnt((7 & 15) | (7 << 4) | (15 << 8));        // vmcnt(7)
+    }
+    __builtin_amdgcn_s_waitcnt((0 & 15) | (7 << 4) | (15 << 8));            // vmcnt(0)
+    __syncthreads();
+    if (threadIdx.x == 0) out[blockIdx.x] = ring[blockIdx.x & 1023];
+}
+
 }  // namespace
 
 extern "C" {
+
+// Band-read-into-LDS probe; same arguments and limits as probe_band_read,
+// plus rows * row_bytes < 2 GiB.
+int probe_band_read_lds(const void* in, int rows, int row_bytes, int band, int rows_per, uint32_t* out,
+                        void* stream) {
+    if (band < 16 || band > 1024 || band % 16 || row_bytes % band || rows_per <= 0 || rows % rows_per ||
+        64 % (band / 16) || static_cast<int64_t>(rows) * row_bytes >= (int64_t(1) << 31))
+        return static_cast<int>(hipErrorInvalidValue);
+    const int grid = (row_bytes / band) * (rows / rows_per);
+    hipLaunchKernelGGL(probe_band_read_lds_kernel, dim3(grid), dim3(256), 0, static_cast<hipStream_t>(stream),
+                       static_cast<const uint8_t*>(in), rows, row_bytes, band, rows_per, out);
+    return static_cast<int>(hipGetLastError());
+}
+
+// Band-read probe (see the kernel); grid = (row_bytes / band) * (rows / rows_per).
+int probe_band_read(const void* in, int rows, int row_bytes, int band, int rows_per, uint32_t* out,
+                    void* stream) {
+    if (band < 16 || band > 4096 || band % 16 || row_bytes % band || rows_per <= 0 || rows % rows_per ||
+        256 % (band / 16))
+        return static_cast<int>(hipErrorInvalidValue);
+    const int grid = (row_bytes / band) * (rows / rows_per);
+    hipLaunchKernelGGL(probe_band_read_kernel, dim3(grid), dim3(256), 0, static_cast<hipStream_t>(stream),
+                       static_cast<const uint8_t*>(in), rows, row_bytes, band, rows_per, out);
+    return static_cast<int>(hipGetLastError());
+}
+
+// Streaming-read probe: reads `bytes` (multiple of 16) bytes of `in` with
+// `grid` workgroups of 256 threads; out needs `grid` words.  unroll: 4 or 8.
+int probe_stream_read(const void* in, uint64_t bytes, uint32_t* out, int grid, int unroll, void* stream) {
+    if (bytes % 16 || grid <= 0) return static_cast<int>(hipErrorInvalidValue);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const u32x4* p = static_cast<const u32x4*>(in);
+    if (unroll == 8) hipLaunchKernelGGL(probe_stream_read_kernel<8>, dim3(grid), dim3(256), 0, s, p, bytes / 16, out);
+    else if (unroll == 4) hipLaunchKernelGGL(probe_stream_read_kernel<4>, dim3(grid), dim3(256), 0, s, p, bytes / 16, out);
+    else return static_cast<int>(hipErrorInvalidValue);
+    return static_cast<int>(hipGetLastError());
+}
 
 // in: >= num_records + 128 bytes, out: 1024 halfwords (device pointers).
 int probe_lds_dma(const uint16_t* in, uint16_t* out, int num_records, void* stream) {

@@ -90,7 +90,9 @@ typedef struct gemm_problem {
  *   mfma          matrix instruction: 16 (16x16x32) or 32 (32x32x16)
  *   waves_m/_n    wavefront grid inside one workgroup (64 lanes per wave)
  *   group_m       GROUP_M of the grouped tile order (1 = row-major order)
- *   splitk        K slices reduced in-workgroup (1 = no split)
+ *   splitk        K slices across workgroups, summed in slice order by the
+ *                 last workgroup of each output slab (skinny family; needs a
+ *                 workspace when > 1); 1 for the tile families
  *   xcd_remap     GEMM_XCD_ON: pre-permute workgroup ids so each XCD gets a
  *                 contiguous band of the tile order; GEMM_XCD_OFF: plain ids
  *                 (0 in a forced configuration: the planner's choice)
@@ -155,15 +157,30 @@ gemm_status gemm_plan_launch(const gemm_plan* plan, int64_t* grid, int32_t* thre
  * LDS, kernel name) written into buf[0..len).  Truncates to fit. */
 gemm_status gemm_plan_describe(const gemm_plan* plan, char* buf, size_t len);
 
-/* Device workspace the plan needs in bytes (0 for every current kernel). */
+/* Device workspace the plan needs in bytes (0 unless the plan splits K across
+ * workgroups).  Layout: a fixed 16 KiB region of per-slab arrival counters,
+ * then the fp32 partial tiles. */
 gemm_status gemm_workspace_size(const gemm_plan* plan, size_t* bytes);
+
+/* Prepare a workspace for a plan: enqueue on `stream` a kernel that zero-fills
+ * it.  Required once before the first gemm_run with that workspace (a
+ * zero-filled allocation needs nothing more); every launch leaves its counters
+ * zero again, so the workspace can be reused for any number of runs of plans
+ * whose workspace size fits (the counters sit in a fixed region shared by all
+ * plans).  One workspace serves one launch at a time: runs
+ * that overlap in time (other streams) need separate workspaces.
+ * GEMM_ERR_WORKSPACE if it is NULL or smaller than gemm_workspace_size. */
+gemm_status gemm_workspace_init(const gemm_plan* plan, void* workspace, size_t workspace_bytes,
+                                void* stream);
 
 /* Enqueue D = A x B (+ C) on `stream`.  A, B, D are device pointers; C is a
  * device pointer when the plan's problem has has_c = 1 and must be NULL
  * otherwise.  D may equal C when their strides are equal (in place D += AxB);
  * any other overlap of D with A, B or C is GEMM_ERR_INVALID_ARG.  workspace
- * may be NULL when gemm_workspace_size reports 0.  M = 0 or N = 0 launches
- * nothing; K = 0 writes D = C (or zeros). */
+ * may be NULL when gemm_workspace_size reports 0; otherwise it must be at
+ * least that many bytes, 256-byte aligned and prepared by gemm_workspace_init
+ * (else GEMM_ERR_WORKSPACE).  M = 0 or N = 0 launches nothing; K = 0 writes
+ * D = C (or zeros). */
 gemm_status gemm_run(const gemm_plan* plan, const void* A, const void* B, const void* C,
                      void* D, void* workspace, size_t workspace_bytes, void* stream);
 

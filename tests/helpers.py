@@ -13,6 +13,9 @@ def gpu_run(A, B, C=None, config=None, out=None):
     """D = A x B (+C) through libgemm.so; A, B, C are CPU tensors; returns CPU D."""
     dA, dB = A.cuda(), B.cuda()
     dC = C.cuda() if C is not None else None
+    if out is None:
+        # NaN-filled: an output the kernels fail to write cannot pass a check
+        out = torch.full((A.shape[0], B.shape[1]), float("nan"), dtype=A.dtype, device="cuda")
     D = g.matmul(dA, dB, dC, out=out, config=config)
     torch.cuda.synchronize()
     return D.cpu()

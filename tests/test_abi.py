@@ -191,3 +191,24 @@ def test_in_place_addend_allowed_only_with_equal_strides():
     with pytest.raises(g.GemmError) as e:
         g.gemm_run(p, 1 << 20, 1 << 24, (1 << 28) + 2, 1 << 28)   # shifted alias
     assert "overlaps C" in e.value.detail
+
+
+def test_split_k_plans_need_and_check_a_workspace():
+    p = plan(16, 8192, 8192)
+    c = p.config
+    assert c.kernel == 2 and c.bn >= 64 and c.splitk > 1          # 128-byte bands, K slices
+    grid, _, _ = g.gemm_plan_launch(p)
+    assert grid == -(-8192 // c.bn) * c.splitk
+    need = g.gemm_workspace_size(p)
+    assert need >= c.splitk * 8192 * 16 * 4
+    with pytest.raises(g.GemmError) as e:
+        g.gemm_run(p, 1 << 20, 1 << 30, None, 1 << 24)              # no workspace
+    assert e.value.status == g.GEMM_ERR_WORKSPACE
+    with pytest.raises(g.GemmError) as e:
+        g.gemm_run(p, 1 << 20, 1 << 30, None, 1 << 24, 1 << 34, need - 4)
+    assert e.value.status == g.GEMM_ERR_WORKSPACE
+    with pytest.raises(g.GemmError) as e:
+        g.gemm_workspace_init(p, None, 0)
+    assert e.value.status == g.GEMM_ERR_WORKSPACE
+    p1 = plan(16, 8192, 8192, force={"kernel": 2, "bn": 32, "splitk": 1})
+    assert g.gemm_workspace_size(p1) == 0

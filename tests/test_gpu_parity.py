@@ -118,6 +118,66 @@ def _variants(dt):
     return seen
 
 
+SKINNY = [(256, 4, 32, 2), (128, 4, 32, 3), (128, 4, 32, 4), (128, 2, 32, 8), (128, 2, 32, 6), (128, 8, 32, 2), (64, 4, 64, 3), (64, 8, 64, 2), (32, 8, 64, 3), (16, 8, 64, 3)]
+
+
+@pytest.mark.parametrize("mnk", [(16, 1000, 1000), (1, 520, 264), (5, 4096, 512), (16, 64, 64),
+                                 (9, 136, 8), (16, 8192, 1032), (16, 1024, 4096)])
+def test_skinny_variants(mnk):
+    """The skinny-M kernels on ragged shapes (N and K tails, M < 16, K split over
+    waves and over 1-8 workgroup slices, some slices and waves left without
+    work); kernels with the same K partition (waves, chunk depth, slices) agree
+    bit for bit whatever their slab width."""
+    M, N, K = mnk
+    for dt, has_c in (("bf16", True), ("f16", False)):
+        A, B, C = _inputs(M, N, K, dt, has_c, seed=M + 7 * N + 13 * K)
+        by_part = {}
+        for bn, nw, ck, st in SKINNY:
+            for sk in (1, 2, 3, 8):
+                cfg = dict(kernel=2, bn=bn, waves_n=nw, bk=ck, stages=st, splitk=sk)
+                D = gpu_run(A, B, C, config=cfg)
+                check(A, B, C, D, dt, label="%s %s %s" % (dt, mnk, cfg))
+                key = (nw, ck, sk)
+                if key in by_part:
+                    assert torch.equal(by_part[key].view(torch.int16), D.view(torch.int16)), cfg
+                else:
+                    by_part[key] = D
+
+
+def test_skinny_workspace_reuse():
+    """Slab counters reset themselves: many launches (and two plans) on one
+    workspace all give the same, correct result."""
+    M, N, K = 16, 2048, 2048
+    A, B, C = _inputs(M, N, K, "bf16", True, seed=99)
+    dA, dB, dC = A.cuda(), B.cuda(), C.cuda()
+    pl4 = g.plan_for(dA, dB, dC, None, dict(kernel=2, bn=128, splitk=4))
+    pl8 = g.plan_for(dA, dB, dC, None, dict(kernel=2, bn=64, splitk=8))
+    need = max(g.gemm_workspace_size(pl4), g.gemm_workspace_size(pl8))
+    assert need > 0
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    st = torch.cuda.current_stream().cuda_stream
+    g.gemm_workspace_init(pl4, ws.data_ptr(), need, st)
+    outs = []
+    for i in range(6):
+        pl = pl4 if i % 2 == 0 else pl8
+        D = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        g.gemm_run(pl, dA.data_ptr(), dB.data_ptr(), dC.data_ptr(), D.data_ptr(), ws.data_ptr(), need, st)
+        outs.append(D)
+    torch.cuda.synchronize()
+    for i, D in enumerate(outs):
+        check(A, B, C, D.cpu(), "bf16", label="reuse %d" % i)
+        assert torch.equal(outs[i % 2].view(torch.int16), D.view(torch.int16))
+    with pytest.raises(g.GemmError) as e:
+        g.gemm_run(pl4, dA.data_ptr(), dB.data_ptr(), dC.data_ptr(), outs[0].data_ptr(), None, 0, st)
+    assert e.value.status == g.GEMM_ERR_WORKSPACE
+
+
+def test_skinny_rejects_tall_problems():
+    with pytest.raises(g.GemmError) as e:
+        g.gemm_plan_create(g.problem(32, 64, 64, g.GEMM_BF16), 0, dict(kernel=2))
+    assert e.value.status == g.GEMM_ERR_UNSUPPORTED
+
+
 @pytest.mark.parametrize("gm,xcd", [(1, 2), (4, 2), (8, 2), (8, 1), (3, 1)])
 def test_group_and_xcd_orders_are_bitwise_identical(gm, xcd):
     A, B, C = _inputs(1000, 704, 256, "bf16", False, seed=77)
