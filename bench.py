@@ -38,6 +38,29 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 256 * 2.4e9 * 4096 / 1e12        # 2516.6
 PEAK_HBM_GBS = 8000.0
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def measured_traffic(kernel_name):
+    """HBM bytes per launch of this kernel from the committed counter runs, or
+    None if there are none or the kernel sources changed since."""
+    try:
+        import json as _json
+        from dense_tiled_gemm_02_amd import rocprof_summary
+        t = _json.load(open(TRAFFIC_JSON))
+        if t.get("source_sha256") != rocprof_summary.source_hash():
+            return None
+        for k, v in t["kernels"].items():
+            if kernel_name in k.replace(" ", ""):
+                return v["bytes"]
+    except (OSError, ValueError, KeyError):
+        return None
+    return None
+
+
+def kernel_of(plan_desc):
+    """'gemm_dma_kernel<256,256,...>' from a plan description."""
+    return plan_desc.split("kernel=")[1].split(" ")[0]
 
 
 def parse():
@@ -279,7 +302,8 @@ def main():
         "config": {**w.describe(), "plan": pl.describe(), "parallelism": "single-gpu"},
         "spread": spread,
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": round(PEAK_BF16_TFLOPS, 1),
-                     "unit": "TFLOP/s", "frac": tflops / PEAK_BF16_TFLOPS, "traffic": None},
+                     "unit": "TFLOP/s", "frac": tflops / PEAK_BF16_TFLOPS,
+                     "traffic": measured_traffic(kernel_of(pl.describe()))},
     }
     if not args.no_skinny and args.workload != "skinny_bf16_16x8192":
         sw = gemm_inputs.WORKLOADS["skinny_bf16_16x8192"]
@@ -289,7 +313,8 @@ def main():
         gbs = sw.bytes() / sms / 1e6
         rec["skinny"] = {"workload": sw.name, "plan": spl.describe(), "ms_per_step": sms,
                          "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
-                                      "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS, "traffic": None},
+                                      "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
+                                      "traffic": measured_traffic(kernel_of(spl.describe()))},
                          "tflops": sw.flops() / sms / 1e9}
         del sc
     if args.copy_mb:

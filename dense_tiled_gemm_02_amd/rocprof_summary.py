@@ -1,6 +1,7 @@
 """Summarise rocprofv3 CSV output per kernel.
 
     python -m dense_tiled_gemm_02_amd.rocprof_summary DIR [--match SUBSTR]
+    python -m dense_tiled_gemm_02_amd.rocprof_summary --traffic FETCH_DIR WRITE_DIR COPY_BYTES OUT.json
 
 DIR holds the CSV files of one or more rocprofv3 runs (kernel_stats,
 kernel_trace, counter_collection).  Prints, per kernel name: dispatch count
@@ -11,9 +12,55 @@ calibration factor of those counters.
 """
 import csv
 import glob
+import hashlib
+import json
 import os
 import sys
 from collections import defaultdict
+
+CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
+
+
+def source_hash():
+    """sha256 over the kernel sources; measured counters are valid only for it."""
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(CSRC, "*"))):
+        if f.endswith((".hip", ".h", ".cpp")):
+            h.update(os.path.basename(f).encode())
+            h.update(open(f, "rb").read())
+    return h.hexdigest()
+
+
+def counter_means(d, name):
+    """{kernel name: mean per dispatch of counter `name`} from a --pmc run."""
+    per = defaultdict(lambda: defaultdict(float))
+    for c in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(c)):
+            if r["Counter_Name"] == name:
+                per[r["Kernel_Name"]][r.get("Dispatch_Id")] += float(r["Counter_Value"])
+    return {k: sum(v.values()) / len(v) for k, v in per.items()}
+
+
+def traffic(fetch_dir, write_dir, copy_bytes):
+    """HBM bytes per launch of every kernel: FETCH_SIZE and WRITE_SIZE (KiB per
+    dispatch), each scaled so that the copy kernel of copy_bytes reads and
+    writes exactly copy_bytes."""
+    fetch = counter_means(fetch_dir, "FETCH_SIZE")
+    write = counter_means(write_dir, "WRITE_SIZE")
+    copy_f = [v for k, v in fetch.items() if "copy" in k.lower()]
+    copy_w = [v for k, v in write.items() if "copy" in k.lower()]
+    if not copy_f or not copy_w:
+        raise SystemExit("no copy kernel in the counter runs")
+    ff = copy_bytes / (copy_f[0] * 1024.0)
+    fw = copy_bytes / (copy_w[0] * 1024.0)
+    out = {"source_sha256": source_hash(), "copy_bytes": copy_bytes,
+           "fetch_scale": ff, "write_scale": fw, "kernels": {}}
+    for k in fetch:
+        if "copy" in k.lower() or k not in write:
+            continue
+        out["kernels"][k] = {"fetch_kib": fetch[k], "write_kib": write[k],
+                             "bytes": fetch[k] * 1024.0 * ff + write[k] * 1024.0 * fw}
+    return out
 
 
 def _short(name, n=110):
@@ -57,6 +104,16 @@ def summarise(d, match=None):
 
 if __name__ == "__main__":
     args = sys.argv[1:]
+    if args and args[0] == "--traffic":
+        t = traffic(args[1], args[2], int(args[3]))
+        with open(args[4], "w") as f:
+            json.dump(t, f, indent=1)
+        for k, v in t["kernels"].items():
+            print("%-100s fetch %10.1f KiB  write %10.1f KiB  -> %.1f MB per launch" % (
+                _short(k, 100), v["fetch_kib"], v["write_kib"], v["bytes"] / 1e6))
+        print("scales: fetch %.4f  write %.4f  (copy of %d bytes)" % (t["fetch_scale"], t["write_scale"],
+                                                                     t["copy_bytes"]))
+        sys.exit(0)
     m = None
     if "--match" in args:
         i = args.index("--match")
