@@ -209,15 +209,13 @@ def host_cpu_model():
 def sweep(args):
     import gemm_inputs
     variants = {
-        "square_bf16_4096": [dict(kernel=1, bm=256, bn=256, mfma=16, group_m=8)] +
-                            [dict(kernel=3, bm=256, bn=256, bk=64, mfma=16, group_m=gm) for gm in (1, 4, 8)] +
-                            [dict(kernel=3, bm=256, bn=256, bk=64, mfma=16, group_m=8, xcd_remap=2),
-                             dict(kernel=3, bm=256, bn=256, bk=64, mfma=32, group_m=8),
-                             dict(kernel=3, bm=256, bn=256, bk=32, mfma=32, group_m=8),
-                             dict(kernel=3, bm=256, bn=128, bk=64, mfma=16, group_m=8),
-                             dict(kernel=3, bm=128, bn=256, bk=64, mfma=16, group_m=8),
-                             dict(kernel=3, bm=128, bn=128, bk=64, mfma=16, group_m=8),
-                             dict(kernel=3, bm=128, bn=128, bk=64, mfma=32, group_m=8)],
+        "square_bf16_4096": [dict(kernel=3, bm=256, bn=256, bk=64, stages=2, mfma=16, group_m=gm) for gm in (1, 8)] +
+                            [dict(kernel=3, bm=256, bn=256, bk=32, stages=4, mfma=16, group_m=gm) for gm in (1, 8)] +
+                            [dict(kernel=3, bm=256, bn=256, bk=64, stages=2, mfma=32, group_m=8),
+                             dict(kernel=3, bm=256, bn=256, bk=32, stages=4, mfma=32, group_m=8),
+                             dict(kernel=3, bm=256, bn=128, bk=64, stages=3, mfma=16, group_m=8),
+                             dict(kernel=3, bm=128, bn=128, bk=64, stages=4, mfma=16, group_m=8),
+                             dict(kernel=3, bm=128, bn=128, bk=64, stages=2, mfma=32, group_m=8)],
         "square_f16_1024": [dict(bm=32, bn=32, bk=32), dict(bm=64, bn=64, bk=32), dict(bm=128, bn=128, bk=64),
                             dict(bm=64, bn=64, bk=64)],
         "square_f16_256": [dict(bm=32, bn=32, bk=32), dict(bm=64, bn=64, bk=32), dict(bm=64, bn=64, bk=64),

@@ -61,12 +61,16 @@ __device__ __forceinline__ uint16_t narrow(float v) {
 
 // Physical 16-byte chunk of logical chunk c in LDS row r is c ^ swz(r).  The
 // XOR pattern depends only on r % 16, so it is a per-lane constant for the
-// MFMA operand reads (fragment rows start at multiples of 16).  Chosen so that
-// the 16 rows read by one 16-lane group fall on distinct banks.
+// MFMA operand reads (fragment rows start at multiples of 16).  For 128-byte
+// rows (CH = 8) the pattern was chosen by measurement: of the 4096 linear XOR
+// maps of the row bits, this one reads both instruction shapes' operand
+// layouts (16 rows x one chunk per 16 lanes, 32 rows x one chunk per 32 lanes)
+// without a single bank-conflict cycle, whereas e.g. r & 7 or
+// (r & 7) ^ (r >> 3 & 1) each conflict on one of the two.
 template <int CH>
 __device__ __forceinline__ int swz(int r) {
     if constexpr (CH == 4) return ((r >> 2) ^ (r >> 1)) & 3;
-    else if constexpr (CH == 8) return (r & 7) ^ ((r >> 3) & 1);
+    else if constexpr (CH == 8) return ((r >> 1) & 7) ^ (r & 1);
     else return r & 15;
 }
 

@@ -64,12 +64,11 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(KArgs p) {
     constexpr int SA = BM * BK, SB = BK * BN;   // elements per stage
     constexpr int L = IA_W + IB_W;              // loads per wave per stage
     constexpr int NKS = BK / KI;                // instruction k sub-steps per K step
-    static_assert(NKS % 2 == 0, "fragment double buffering needs an even number of k sub-steps");
     static_assert(BM % (WM * MF) == 0 && BN % (WN * MF) == 0, "tile vs wave grid");
     static_assert(BK % KI == 0 && (CHA == 4 || CHA == 8 || CHA == 16), "BK");
     static_assert(CHB >= 8 && CHB <= 64 && 64 % CHB == 0, "BN");
     static_assert((BM / RA) % NW == 0 && (BK / RB) % NW == 0 && IA_W > 0 && IB_W > 0, "load split");
-    static_assert(ST == 2, "this kernel runs a two-stage LDS ring");
+    static_assert(ST >= 2 && ST <= 5 && (ST - 1) * L < 64, "stages");
     typedef typename AccT<MF>::type acc_t;
 
     __shared__ __attribute__((aligned(1024))) uint16_t smem[ST * (SA + SB)];
@@ -153,7 +152,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(KArgs p) {
     //  ks*KI + 8 g + 4 hh + (jq >> 2) and 4 columns starting at
     //  nb + 4 (jq & 3); the (ks*KI + 4 hh) * BN * 2 part is an immediate offset.
     const uint32_t smem0 = lds_addr(smem);
-    uint32_t a_addr[2][NKS], b_addr[2][FN];
+    uint32_t a_addr[ST][NKS], b_addr[ST][FN];
     {
         const int a_row = wm * TM + lane % MF;
         const int a_kc0 = lane / MF;
@@ -164,7 +163,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(KArgs p) {
         const int b_sw = (CHB >= 16) ? 2 * ((jq >> 2) | ((g & 1) << 2)) : 2 * (jq >> 2);
         const int b_row = 8 * g + (jq >> 2);
 #pragma unroll
-        for (int st = 0; st < 2; ++st) {
+        for (int st = 0; st < ST; ++st) {
             const uint32_t sa = smem0 + st * (SA + SB) * 2;
             const uint32_t sb = sa + SA * 2;
 #pragma unroll
@@ -218,16 +217,30 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(KArgs p) {
         else issue(Checked{}, kt, st);
     };
 
-    // One K step on LDS stage S.  On entry the fragments of sub-step 0 are in
-    // slot 0.  Sub-step ks issues the reads of sub-step ks + 1 (or, at the
-    // last sub-step, waits for the next tile, passes the barrier, starts the
-    // loads of the tile after it into this stage and reads the next tile's
-    // first fragments), then runs its MFMAs, then waits for those reads.
-    auto step = [&](auto stage_tag, int kt) {
-        constexpr int S = decltype(stage_tag)::value;
+    // Wait until tile `need` has landed: at most the tiles issued after it
+    // (up to `last_issued`) may still be in flight, L loads each.
+    auto wait_tile = [&](int need, int last_issued) {
+        const int after = last_issued - need;
+        static_for<ST>([&](auto i_tag) {
+            constexpr int I = decltype(i_tag)::value;
+            if (after == I) wait_vm<I * L>();
+        });
+    };
+
+    // One K step (tile kt) on LDS stage S = kt % ST; U is kt's position in the
+    // unrolled loop, which fixes which fragment slot holds which sub-step.  On
+    // entry the fragments of sub-step 0 are in slot (U * NKS) % 2.  Sub-step ks
+    // issues the reads of sub-step ks + 1 (or, at the last sub-step, waits for
+    // tile kt + 1, passes the barrier, refills this stage with tile kt + ST and
+    // reads tile kt + 1's first fragments), then runs its MFMAs, then waits for
+    // those reads.  Tile kt + ST goes into the stage of tile kt: every wave has
+    // read all of tile kt's fragments before the barrier.
+    auto step = [&](auto u_tag, int kt) {
+        constexpr int U = decltype(u_tag)::value;
+        constexpr int S = U % ST;
         static_for<NKS>([&](auto ks_tag) {
             constexpr int KS = decltype(ks_tag)::value;
-            constexpr int CUR = KS & 1, NXT = CUR ^ 1;
+            constexpr int CUR = (U * NKS + KS) & 1, NXT = CUR ^ 1;
             bool pending = true;
             if constexpr (KS + 1 < NKS) {
                 read_frags(std::integral_constant<int, S>{}, std::integral_constant<int, KS + 1>{},
@@ -235,10 +248,11 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(KArgs p) {
             } else {
                 pending = kt + 1 < nkt;
                 if (pending) {
-                    wait_vm<0>();
+                    const int last_issued = (kt + ST - 1 < nkt - 1) ? kt + ST - 1 : nkt - 1;
+                    wait_tile(kt + 1, last_issued);
                     __builtin_amdgcn_s_barrier();
-                    if (kt + 2 < nkt) issue_tile(kt + 2, S);
-                    read_frags(std::integral_constant<int, S ^ 1>{}, std::integral_constant<int, 0>{},
+                    if (kt + ST < nkt) issue_tile(kt + ST, S);
+                    read_frags(std::integral_constant<int, (S + 1) % ST>{}, std::integral_constant<int, 0>{},
                                std::integral_constant<int, NXT>{});
                 }
             }
@@ -249,17 +263,21 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(KArgs p) {
         });
     };
 
+    // unroll so that both the stage and the fragment-slot parity repeat
+    constexpr int UNROLL = ((ST * NKS) % 2 == 0) ? ST : 2 * ST;
     if (nkt > 0) {
-        issue_tile(0, 0);
-        wait_vm<0>();
+        const int first = (ST < nkt) ? ST : nkt;
+        for (int t = 0; t < first; ++t) issue_tile(t, t);
+        wait_tile(0, first - 1);
         __builtin_amdgcn_s_barrier();
-        if (nkt > 1) issue_tile(1, 1);
         read_frags(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{},
                    std::integral_constant<int, 0>{});
         wait_frags(std::integral_constant<int, 0>{});
-        for (int kt = 0; kt < nkt; kt += 2) {
-            step(std::integral_constant<int, 0>{}, kt);
-            if (kt + 1 < nkt) step(std::integral_constant<int, 1>{}, kt + 1);
+        for (int kt = 0; kt < nkt; kt += UNROLL) {
+            static_for<UNROLL>([&](auto u_tag) {
+                constexpr int UU = decltype(u_tag)::value;
+                if (kt + UU < nkt) step(u_tag, kt + UU);
+            });
         }
     }
 
@@ -305,12 +323,15 @@ hipError_t launch_dma(const KArgs& a, int64_t grid, hipStream_t stream) {
 
 const KernelEntry kDmaTable[] = {
     DMA_BOTH(256, 256, 64, 2, 4, 16, 2),
+    DMA_BOTH(256, 256, 32, 2, 4, 16, 4),
     DMA_BOTH(256, 256, 64, 2, 4, 32, 2),
+    DMA_BOTH(256, 256, 32, 2, 4, 32, 4),
+    DMA_BOTH(256, 128, 64, 2, 2, 16, 3),
     DMA_BOTH(256, 128, 64, 2, 2, 16, 2),
     DMA_BOTH(128, 256, 64, 2, 2, 16, 2),
     DMA_BOTH(128, 128, 64, 2, 2, 16, 2),
+    DMA_BOTH(128, 128, 64, 2, 2, 16, 4),
     DMA_BOTH(128, 128, 64, 2, 2, 32, 2),
-    DMA_BOTH(256, 256, 32, 2, 4, 32, 2),
 };
 
 }  // namespace

@@ -193,9 +193,150 @@ __global__ __launch_bounds__(256) void probe_band_read_lds_kernel(const uint8_t*
     if (threadIdx.x == 0) out[blockIdx.x] = ring[blockIdx.x & 1023];
 }
 
+// LDS read patterns, one kernel per pattern so counters separate them.  Four
+// waves, 64 KiB of LDS; wave w works in its own 8 KiB window at 8192 w + the
+// offsets below (all < 8192).  Each wave runs `iters` reads and XORs the data
+// into out[threadIdx.x + 256 blockIdx.x].
+//  0: 16-byte reads, lane l at 16 l (+ 1 KiB per iteration mod 4 KiB)
+//  1: 16-byte reads, operand layout of A (rows of 128 bytes, lane l: row
+//     l % 16 + 16 (it % 4), logical chunk l / 16 + 4 (it % 2), XOR swizzle)
+//  2: as 1 without the swizzle
+//  3: transposing 8-byte reads, operand layout of B (rows of 512 bytes, lane
+//     group g = l / 16, j = l % 16: row 8 g + 4 (it % 2) + j / 4, columns
+//     16 (it / 2 % 16) + 4 (j % 4), chunk-pair XOR swizzle)
+//  4: as 3 without the swizzle
+//  5: transposing 8-byte reads, lane l at 8 l
+//  6: 8-byte reads, lane l at 8 l
+template <int P>
+__global__ __launch_bounds__(256) void probe_lds_pattern_kernel(uint32_t* out, int iters) {
+    __shared__ __attribute__((aligned(1024))) uint32_t lds[16384];
+    for (int i = threadIdx.x; i < 16384; i += 256) lds[i] = i * 2654435761u;
+    __syncthreads();
+    const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const uint32_t base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+                              (const __attribute__((address_space(3))) uint32_t*)lds)) + w * 8192;
+    u32x4 acc = {0, 0, 0, 0};
+    for (int it = 0; it < iters; ++it) {
+        uint32_t a;
+        if constexpr (P == 0) {
+            a = 16 * l + 1024 * (it & 3);
+        } else if constexpr (P == 1 || P == 2) {
+            const int row = (l & 15) + 16 * (it & 3), chunk = (l >> 4) + 4 * ((it >> 2) & 1);
+            const int sw = (P == 1) ? ((row & 7) ^ ((row >> 3) & 1)) : 0;
+            a = row * 128 + ((chunk ^ sw) * 16);
+        } else if constexpr (P == 3 || P == 4) {
+            const int g = l >> 4, j = l & 15, h = it & 1;
+            const int r = 8 * g + 4 * h + (j >> 2);
+            const int nb = 16 * ((it >> 1) & 15);
+            const int f = (P == 3) ? 2 * ((r & 3) | (((r >> 3) & 1) << 2)) : 0;
+            a = r * 512 + ((((nb >> 3) ^ f)) << 4) + 8 * (j & 3);
+        } else {
+            a = 8 * l + 512 * (it & 7);
+        }
+        if constexpr (P <= 2) {
+            u32x4 v;
+            asm volatile("ds_read_b128 %0, %1\n s_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(base + a));
+            acc ^= v;
+        } else if constexpr (P <= 5) {
+            i16x4 v;
+            asm volatile("ds_read_b64_tr_b16 %0, %1\n s_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(base + a));
+            acc[0] ^= __builtin_bit_cast(uint64_t, v) & 0xffffffffu;
+        } else {
+            i16x4 v;
+            asm volatile("ds_read_b64 %0, %1\n s_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(base + a));
+            acc[0] ^= __builtin_bit_cast(uint64_t, v) & 0xffffffffu;
+        }
+    }
+    out[threadIdx.x + 256 * blockIdx.x] = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+}
+
+// Lane-pair LDS probe: every lane reads 16 bytes at 16 l (no conflicts),
+// except lane j, which reads at 16 i + 4096 (same banks as lane i under any
+// bank period dividing 4096).  The bank-conflict counter of a dispatch then
+// tells whether lanes i and j are served in the same LDS cycle.  One wave per
+// workgroup, 8 KiB of LDS; all addresses < 8192.
+__global__ __launch_bounds__(64) void probe_lds_pair_kernel(uint32_t* out, int i, int j, int iters) {
+    __shared__ __attribute__((aligned(1024))) uint32_t lds[2048];
+    for (int k = threadIdx.x; k < 2048; k += 64) lds[k] = k;
+    __syncthreads();
+    const int l = threadIdx.x;
+    const uint32_t base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+        (const __attribute__((address_space(3))) uint32_t*)lds));
+    const uint32_t a = base + ((l == j) ? 16 * i + 4096 : 16 * l);
+    u32x4 acc = {0, 0, 0, 0};
+    for (int it = 0; it < iters; ++it) {
+        u32x4 v;
+        asm volatile("ds_read_b128 %0, %1\n s_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(a));
+        acc ^= v;
+    }
+    out[threadIdx.x + 64 * blockIdx.x] = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+}
+
+// Swizzle-candidate probe: the 16-byte operand reads of an A tile with
+// 128-byte rows, physical chunk = logical chunk ^ table[row % 16].
+// mf = 16: lane l reads row l % 16 + 16 (it % 4), logical chunk l / 16 + 4 (it / 4 % 2);
+// mf = 32: lane l reads row l % 32 + 32 (it % 2), logical chunk l / 32 + 2 (it / 2 % 4).
+// table (16 ints, each 0..7) is passed by value.  One wave per workgroup,
+// 8 KiB of LDS; all addresses < 8192.
+struct SwzTable { int v[16]; };
+__global__ __launch_bounds__(64) void probe_lds_swizzle_kernel(uint32_t* out, SwzTable t, int mf, int iters) {
+    __shared__ __attribute__((aligned(1024))) uint32_t lds[2048];
+    for (int k = threadIdx.x; k < 2048; k += 64) lds[k] = k;
+    __syncthreads();
+    const int l = threadIdx.x;
+    const uint32_t base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+        (const __attribute__((address_space(3))) uint32_t*)lds));
+    u32x4 acc = {0, 0, 0, 0};
+    for (int it = 0; it < iters; ++it) {
+        int row, chunk;
+        if (mf == 16) { row = (l & 15) + 16 * (it & 3); chunk = (l >> 4) + 4 * ((it >> 2) & 1); }
+        else { row = (l & 31) + 32 * (it & 1); chunk = (l >> 5) + 2 * ((it >> 1) & 3); }
+        const uint32_t a = base + row * 128 + ((chunk ^ (t.v[row & 15] & 7)) * 16);
+        u32x4 v;
+        asm volatile("ds_read_b128 %0, %1\n s_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(a));
+        acc ^= v;
+    }
+    out[threadIdx.x + 64 * blockIdx.x] = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+}
+
 }  // namespace
 
 extern "C" {
+
+// Swizzle probe: table = 16 ints in host memory (each masked to 0..7).
+int probe_lds_swizzle(const int* table, int mf, uint32_t* out, int grid, int iters, void* stream) {
+    if (mf != 16 && mf != 32) return static_cast<int>(hipErrorInvalidValue);
+    SwzTable t;
+    for (int k = 0; k < 16; ++k) t.v[k] = table[k] & 7;
+    hipLaunchKernelGGL(probe_lds_swizzle_kernel, dim3(grid), dim3(64), 0, static_cast<hipStream_t>(stream), out, t,
+                       mf, iters);
+    return static_cast<int>(hipGetLastError());
+}
+
+// Lane-pair probe: `grid` one-wave workgroups; out needs 64 * grid words;
+// 0 <= i, j < 64.
+int probe_lds_pair(int i, int j, uint32_t* out, int grid, int iters, void* stream) {
+    if (i < 0 || i > 63 || j < 0 || j > 63) return static_cast<int>(hipErrorInvalidValue);
+    hipLaunchKernelGGL(probe_lds_pair_kernel, dim3(grid), dim3(64), 0, static_cast<hipStream_t>(stream), out, i,
+                       j, iters);
+    return static_cast<int>(hipGetLastError());
+}
+
+// LDS pattern probe: `grid` workgroups of 256 threads; out needs 256 * grid words.
+int probe_lds_pattern(int pattern, uint32_t* out, int grid, int iters, void* stream) {
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    switch (pattern) {
+        case 0: hipLaunchKernelGGL(probe_lds_pattern_kernel<0>, dim3(grid), dim3(256), 0, s, out, iters); break;
+        case 1: hipLaunchKernelGGL(probe_lds_pattern_kernel<1>, dim3(grid), dim3(256), 0, s, out, iters); break;
+        case 2: hipLaunchKernelGGL(probe_lds_pattern_kernel<2>, dim3(grid), dim3(256), 0, s, out, iters); break;
+        case 3: hipLaunchKernelGGL(probe_lds_pattern_kernel<3>, dim3(grid), dim3(256), 0, s, out, iters); break;
+        case 4: hipLaunchKernelGGL(probe_lds_pattern_kernel<4>, dim3(grid), dim3(256), 0, s, out, iters); break;
+        case 5: hipLaunchKernelGGL(probe_lds_pattern_kernel<5>, dim3(grid), dim3(256), 0, s, out, iters); break;
+        case 6: hipLaunchKernelGGL(probe_lds_pattern_kernel<6>, dim3(grid), dim3(256), 0, s, out, iters); break;
+        default: return static_cast<int>(hipErrorInvalidValue);
+    }
+    return static_cast<int>(hipGetLastError());
+}
 
 // Band-read-into-LDS probe; same arguments and limits as probe_band_read,
 // plus rows * row_bytes < 2 GiB.

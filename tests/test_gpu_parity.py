@@ -110,10 +110,11 @@ def _variants(dt):
                                        (64, 64, 32, 2, 16, 2, 2), (64, 64, 32, 1, 16, 2, 2),
                                        (32, 32, 32, 2, 16, 2, 2), (16, 64, 64, 2, 16, 1, 4)]:
         seen.append(dict(bm=bm, bn=bn, bk=bk, stages=st, mfma=mf, waves_m=wm, waves_n=wn, kernel=1))
-    for bm, bn, bk, st, mf, wm, wn in [(256, 256, 64, 2, 16, 2, 4), (256, 256, 64, 2, 32, 2, 4),
-                                       (256, 128, 64, 2, 16, 2, 2), (128, 256, 64, 2, 16, 2, 2),
-                                       (128, 128, 64, 2, 16, 2, 2), (128, 128, 64, 2, 32, 2, 2),
-                                       (256, 256, 32, 2, 32, 2, 4)]:
+    for bm, bn, bk, st, mf, wm, wn in [(256, 256, 64, 2, 16, 2, 4), (256, 256, 32, 4, 16, 2, 4),
+                                       (256, 256, 64, 2, 32, 2, 4), (256, 256, 32, 4, 32, 2, 4),
+                                       (256, 128, 64, 3, 16, 2, 2), (256, 128, 64, 2, 16, 2, 2),
+                                       (128, 256, 64, 2, 16, 2, 2), (128, 128, 64, 2, 16, 2, 2),
+                                       (128, 128, 64, 4, 16, 2, 2), (128, 128, 64, 2, 32, 2, 2)]:
         seen.append(dict(bm=bm, bn=bn, bk=bk, stages=st, mfma=mf, waves_m=wm, waves_n=wn, kernel=3))
     return seen
 
