@@ -56,7 +56,9 @@ def _compile(src, verbose):
 
 def _link(objs, out, verbose):
     tmp = out + ".tmp%d" % os.getpid()
-    _run([HIPCC, "-shared", "-fPIC", "--offload-arch=" + ARCH, "-o", tmp] + objs, verbose)
+    # -z defs: a symbol left undefined (e.g. a kernel stub the host pass did
+    # not emit) fails the build instead of the first load of the library
+    _run([HIPCC, "-shared", "-fPIC", "--offload-arch=" + ARCH, "-Wl,-z,defs", "-o", tmp] + objs, verbose)
     os.replace(tmp, out)
 
 

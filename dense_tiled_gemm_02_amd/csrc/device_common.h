@@ -128,6 +128,7 @@ __device__ __forceinline__ void lds_wait_all() { asm volatile("s_waitcnt lgkmcnt
 // Make `v` depend on the preceding lds_wait_all() (volatile asm keeps its
 // order), so no use of v is scheduled before the wait.
 __device__ __forceinline__ void tie(u32x4& v) { asm volatile("" : "+v"(v)); }
+__device__ __forceinline__ void tie(i16x4& v) { asm volatile("" : "+v"(v)); }
 
 __device__ __forceinline__ uint32_t lds_addr(const uint16_t* p) {
     return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) uint16_t*)p));

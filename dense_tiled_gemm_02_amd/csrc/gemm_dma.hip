@@ -48,7 +48,6 @@ __device__ __forceinline__ int bsw(int r) {
     else return 2 * (r & 3);
 }
 
-// wait until at most N vector-memory operations of this wave are outstanding
 template <int BM, int BN, int BK, int WM, int WN, int MF, int ST, bool BF16>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(KArgs p) {
     constexpr int NW = WM * WN;
@@ -84,57 +83,90 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(KArgs p) {
     const int M = p.M, N = p.N, K = p.K;
     const bool edge = (m0 + BM > M) || (n0 + BN > N);
 
-    // ---- per-lane load offsets (bytes, relative to the rebased descriptors)
-    uint32_t a_voff[IA_W];
-    int a_kc[IA_W];
-    bool a_ok[IA_W];
+    // ---- per-lane load offsets (bytes, relative to the rebased descriptors).
+    // Load X of the A tile fills rows X*NW*RA + wave*RA + lane/CHA, load Y of
+    // the B tile k rows Y*NW*RB + wave*RB + lane/CHB.  When NW*RA (NW*RB) is a
+    // multiple of the swizzle's period, every load of a wave has the same
+    // chunk permutation: one voffset serves them all and the row step goes
+    // into the scalar offset.  Otherwise each load keeps its own voffset.
+    constexpr bool PA = (NW * RA) % 16 == 0;
+    constexpr bool PB = (NW * RB) % ((CHB >= 16) ? 16 : 4) == 0;
+    constexpr int NVA = PA ? 1 : IA_W, NVB = PB ? 1 : IB_W;
+    const int a_row0 = wave * RA + lane / CHA;
+    const int b_row0 = wave * RB + lane / CHB;
+    uint32_t a_voff[NVA], b_voff[NVB];
+    int a_kc[NVA], b_c8[NVB];
 #pragma unroll
-    for (int i = 0; i < IA_W; ++i) {
-        const int inst = i * NW + wave;
-        const int row = inst * RA + lane / CHA;
+    for (int i = 0; i < NVA; ++i) {
+        const int row = a_row0 + i * NW * RA;
         const int c = (lane % CHA) ^ swz<CHA>(row);
-        a_ok[i] = m0 + row < M;
         a_voff[i] = static_cast<uint32_t>(static_cast<int64_t>(row) * p.lda * 2 + c * 16);
         a_kc[i] = 8 * c;
     }
-    uint32_t b_voff[IB_W];
-    int b_kr[IB_W];
-    bool b_ok[IB_W];
 #pragma unroll
-    for (int i = 0; i < IB_W; ++i) {
-        const int inst = i * NW + wave;
-        const int row = inst * RB + lane / CHB;
+    for (int i = 0; i < NVB; ++i) {
+        const int row = b_row0 + i * NW * RB;
         const int c = (lane % CHB) ^ bsw<CHB>(row);
-        b_ok[i] = n0 + 8 * c < N;
         b_voff[i] = static_cast<uint32_t>(static_cast<int64_t>(row) * p.ldb * 2 + c * 16);
-        b_kr[i] = row;
+        b_c8[i] = 8 * c;
     }
+    const uint32_t a_step = static_cast<uint32_t>(NW * RA) * static_cast<uint32_t>(p.lda) * 2u;
+    const uint32_t b_step = static_cast<uint32_t>(NW * RB) * static_cast<uint32_t>(p.ldb) * 2u;
 
-    auto issue = [&](auto check_tag, int kt, int s) {
-        constexpr bool CHECK = decltype(check_tag)::value;
-        const int k0 = kt * BK;
-        const uint16_t* abase = p.A + static_cast<int64_t>(m0) * p.lda + k0;
-        const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+    // LDS layout: the ST stages of A, then the ST stages of B.
+    const uint32_t smem0 = lds_addr(smem);
+
+    // Buffer descriptors of K step kt: A rows m0.. and B rows k0.. from column
+    // k0 (A) / n0 (B); the ranges end at the matrices' last element, so any
+    // offset past them reads zeros.
+    struct Desc {
+        __amdgpu_buffer_rsrc_t ra, rb;
+        int k0;
+        bool chk;    // edge tile or K tail: lanes test their own bounds
+    };
+    const int nfull = K / BK;
+    auto make_desc = [&](int kt) {
+        Desc d;
+        d.k0 = kt * BK;
+        const bool live = d.k0 < K;   // tiles past K (issued only to keep the ring uniform) read nothing
+        const uint16_t* abase = p.A + static_cast<int64_t>(m0) * p.lda + (live ? d.k0 : 0);
+        d.ra = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<uint16_t*>(abase), 0,
-            clamp_records((static_cast<int64_t>(M - 1 - m0) * p.lda + (K - k0)) * 2), kRsrcWord3);
-        const uint16_t* bbase = p.B + static_cast<int64_t>(k0) * p.ldb + n0;
-        const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+            live ? clamp_records((static_cast<int64_t>(M - 1 - m0) * p.lda + (K - d.k0)) * 2) : 0u, kRsrcWord3);
+        const uint16_t* bbase = p.B + (live ? static_cast<int64_t>(d.k0) * p.ldb : 0) + n0;
+        d.rb = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<uint16_t*>(bbase), 0,
-            clamp_records((static_cast<int64_t>(K - 1 - k0) * p.ldb + (N - n0)) * 2), kRsrcWord3);
-        uint16_t* sa = smem + s * (SA + SB);
-        uint16_t* sb = sa + SA;
-#pragma unroll
-        for (int i = 0; i < IA_W; ++i) {
-            uint32_t v = a_voff[i];
-            if constexpr (CHECK) v = (a_ok[i] && k0 + a_kc[i] < K) ? v : kOOB;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t*)(sa + (i * NW + wave) * 512), 16, v, 0, 0, 0);
+            live ? clamp_records((static_cast<int64_t>(K - 1 - d.k0) * p.ldb + (N - n0)) * 2) : 0u, kRsrcWord3);
+        d.chk = edge || kt >= nfull;
+        return d;
+    };
+    // Load number X (A loads first, then B) of a K step into LDS stage s.
+    auto load_op = [&](auto x_tag, const Desc& d, int s) {
+        constexpr int X = decltype(x_tag)::value;
+        if constexpr (X < IA_W) {
+            constexpr int V = PA ? 0 : X;
+            uint32_t v = a_voff[V];
+            const uint32_t so = PA ? X * a_step : 0u;
+            if (d.chk) v = (m0 + a_row0 + X * NW * RA < M && d.k0 + a_kc[V] < K) ? v : kOOB;
+            // (a non-const local: clang's host pass drops the kernel when the
+            // builtin is handed a member of a const reference)
+            __amdgpu_buffer_rsrc_t r = d.ra;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(smem + s * SA + (X * NW + wave) * 512), 16, v,
+                                                    so, 0, 0);
+        } else {
+            constexpr int Y = X - IA_W;
+            constexpr int V = PB ? 0 : Y;
+            uint32_t v = b_voff[V];
+            const uint32_t so = PB ? Y * b_step : 0u;
+            if (d.chk) v = (n0 + b_c8[V] < N && d.k0 + b_row0 + Y * NW * RB < K) ? v : kOOB;
+            __amdgpu_buffer_rsrc_t r = d.rb;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                r, (lds_void_t*)(smem + ST * SA + s * SB + (Y * NW + wave) * 512), 16, v, so, 0, 0);
         }
-#pragma unroll
-        for (int i = 0; i < IB_W; ++i) {
-            uint32_t v = b_voff[i];
-            if constexpr (CHECK) v = (b_ok[i] && k0 + b_kr[i] < K) ? v : kOOB;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void_t*)(sb + (i * NW + wave) * 512), 16, v, 0, 0, 0);
-        }
+    };
+    auto issue_tile = [&](int kt, int s) {
+        const Desc d = make_desc(kt);
+        static_for<L>([&](auto x_tag) { load_op(x_tag, d, s); });
     };
 
     acc_t acc[FM][FN];
@@ -145,14 +177,18 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(KArgs p) {
 #pragma unroll
             for (int r = 0; r < AccT<MF>::regs; ++r) acc[i][j][r] = 0.0f;
 
-    // ---- per-lane operand read addresses (LDS bytes), for both stages
+    // ---- per-lane operand read addresses (LDS bytes)
     //  A fragment (i, ks): row wm*TM + i*MF + lane % MF, chunk ks*KI/8 + lane / MF
-    //  (XOR-swizzled); the i*MF*BK*2 part is an immediate offset.
+    //  (XOR-swizzled); i*MF*BK*2 goes into the instruction's offset field.
     //  B fragment (j, ks), half hh: the transposing read of k rows
     //  ks*KI + 8 g + 4 hh + (jq >> 2) and 4 columns starting at
-    //  nb + 4 (jq & 3); the (ks*KI + 4 hh) * BN * 2 part is an immediate offset.
-    const uint32_t smem0 = lds_addr(smem);
-    uint32_t a_addr[ST][NKS], b_addr[ST][FN];
+    //  nb + 4 (jq & 3); (ks*KI + 4 hh) * BN * 2 goes into the offset field.
+    //  The stage offset goes there too when the 16-bit field can hold it
+    //  (AI / BI), else each stage keeps its own addresses.
+    constexpr bool AI = (ST - 1) * SA * 2 + (FM - 1) * MF * BK * 2 < 65536;
+    constexpr bool BI = (ST - 1) * SB * 2 + (BK - 4) * BN * 2 < 65536;
+    constexpr int NAS = AI ? 1 : ST, NBS = BI ? 1 : ST;
+    uint32_t a_addr[NAS][NKS], b_addr[NBS][FN];
     {
         const int a_row = wm * TM + lane % MF;
         const int a_kc0 = lane / MF;
@@ -163,12 +199,15 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(KArgs p) {
         const int b_sw = (CHB >= 16) ? 2 * ((jq >> 2) | ((g & 1) << 2)) : 2 * (jq >> 2);
         const int b_row = 8 * g + (jq >> 2);
 #pragma unroll
-        for (int st = 0; st < ST; ++st) {
-            const uint32_t sa = smem0 + st * (SA + SB) * 2;
-            const uint32_t sb = sa + SA * 2;
+        for (int st = 0; st < NAS; ++st) {
+            const uint32_t sa = smem0 + st * SA * 2;
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks)
                 a_addr[st][ks] = sa + (a_row * BK + (((ks * (KI / 8) + a_kc0) ^ a_sw) * 8)) * 2;
+        }
+#pragma unroll
+        for (int st = 0; st < NBS; ++st) {
+            const uint32_t sb = smem0 + (ST * SA + st * SB) * 2;
 #pragma unroll
             for (int j = 0; j < FN; ++j) {
                 const int nb = wn * TN + j * MF + col;
@@ -177,22 +216,29 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(KArgs p) {
         }
     }
 
-    u32x4 fa[2][FM], fb[2][FN];       // fragments, double-buffered across k sub-steps
+    // Fragments, double-buffered across k sub-steps: A as one 16-byte read per
+    // fragment, B as two transposing reads (k 0..3 and 4..7 of the operand).
+    u32x4 fa[2][FM], fb[2][FN];
+    i16x4 hb[2][FN][2];               // B halves until their wait
+    constexpr int NR = 2 * FN + FM;   // LDS reads per sub-step
 
-    auto read_frags = [&](auto stage_tag, auto ks_tag, auto slot_tag) {
+    // LDS read number R of sub-step KS of stage S into slot SL: the B halves
+    // first, then the A fragments.
+    auto read_op = [&](auto stage_tag, auto ks_tag, auto slot_tag, auto r_tag) {
         constexpr int S = decltype(stage_tag)::value;
         constexpr int KS = decltype(ks_tag)::value;
         constexpr int SL = decltype(slot_tag)::value;
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-            i16x4 h0 = lds_read_tr<(KS * KI + 0) * BN * 2>(b_addr[S][j]);
-            i16x4 h1 = lds_read_tr<(KS * KI + 4) * BN * 2>(b_addr[S][j]);
-            fb[SL][j] = __builtin_bit_cast(u32x4, __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7));
+        constexpr int R = decltype(r_tag)::value;
+        if constexpr (R < 2 * FN) {
+            constexpr int J = R / 2, H = R % 2;
+            hb[SL][J][H] = lds_read_tr<(BI ? S * SB * 2 : 0) + (KS * KI + 4 * H) * BN * 2>(b_addr[BI ? 0 : S][J]);
+            if constexpr (H == 1)
+                fb[SL][J] = __builtin_bit_cast(u32x4, __builtin_shufflevector(hb[SL][J][0], hb[SL][J][1],
+                                                                              0, 1, 2, 3, 4, 5, 6, 7));
+        } else {
+            constexpr int I = R - 2 * FN;
+            fa[SL][I] = lds_read16<(AI ? S * SA * 2 : 0) + I * MF * BK * 2>(a_addr[AI ? 0 : S][KS]);
         }
-        static_for<FM>([&](auto i_tag) {
-            constexpr int I = decltype(i_tag)::value;
-            fa[SL][I] = lds_read16<I * MF * BK * 2>(a_addr[S][KS]);
-        });
     };
     auto wait_frags = [&](auto slot_tag) {
         constexpr int SL = decltype(slot_tag)::value;
@@ -202,83 +248,98 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(KArgs p) {
 #pragma unroll
         for (int i = 0; i < FM; ++i) tie(fa[SL][i]);
     };
-    auto mfmas = [&](auto slot_tag) {
+    // MFMA number Q (row-fragment major) of a sub-step, operands in slot SL
+    auto mfma_op = [&](auto slot_tag, auto q_tag) {
         constexpr int SL = decltype(slot_tag)::value;
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-            for (int j = 0; j < FN; ++j) acc[i][j] = mfma<MF, BF16>(fa[SL][i], fb[SL][j], acc[i][j]);
+        constexpr int Q = decltype(q_tag)::value;
+        constexpr int I = Q / FN, J = Q % FN;
+        acc[I][J] = mfma<MF, BF16>(fa[SL][I], fb[SL][J], acc[I][J]);
+    };
+    constexpr int NQ = FM * FN;       // MFMAs per sub-step
+
+    // The MFMAs of a sub-step with NOPS memory operations spread between them:
+    // operation o follows MFMA number o * SP; the last TAIL MFMAs carry none,
+    // so the LDS reads have landed when the sub-step ends.  Every pair is
+    // fenced, so the compiler keeps exactly this order.
+    auto interleave = [&](auto slot_tag, auto nops_tag, auto&& op) {
+        constexpr int SL = decltype(slot_tag)::value;
+        constexpr int NOPS = decltype(nops_tag)::value;
+        constexpr int TAIL = NQ / 4;
+        constexpr int SP = (NOPS == 0) ? 1 : ((NQ - TAIL) / NOPS > 0 ? (NQ - TAIL) / NOPS : 1);
+        static_for<NQ>([&](auto q_tag) {
+            constexpr int Q = decltype(q_tag)::value;
+            mfma_op(std::integral_constant<int, SL>{}, q_tag);
+            if constexpr (Q % SP == 0 && Q / SP < NOPS) op(std::integral_constant<int, Q / SP>{});
+            __builtin_amdgcn_sched_barrier(0);
+        });
+        // ops left over when there are more operations than MFMA slots
+        if constexpr (NOPS > NQ / SP) {
+            static_for<NOPS - NQ / SP>([&](auto o_tag) {
+                op(std::integral_constant<int, NQ / SP + decltype(o_tag)::value>{});
+            });
+        }
     };
 
     const int nkt = (K + BK - 1) / BK;
-    const int nfull = K / BK;
-    auto issue_tile = [&](int kt, int st) {
-        if (!edge && kt < nfull) issue(Unchecked{}, kt, st);
-        else issue(Checked{}, kt, st);
-    };
-
-    // Wait until tile `need` has landed: at most the tiles issued after it
-    // (up to `last_issued`) may still be in flight, L loads each.
-    auto wait_tile = [&](int need, int last_issued) {
-        const int after = last_issued - need;
-        static_for<ST>([&](auto i_tag) {
-            constexpr int I = decltype(i_tag)::value;
-            if (after == I) wait_vm<I * L>();
-        });
-    };
 
     // One K step (tile kt) on LDS stage S = kt % ST; U is kt's position in the
     // unrolled loop, which fixes which fragment slot holds which sub-step.  On
-    // entry the fragments of sub-step 0 are in slot (U * NKS) % 2.  Sub-step ks
-    // issues the reads of sub-step ks + 1 (or, at the last sub-step, waits for
-    // tile kt + 1, passes the barrier, refills this stage with tile kt + ST and
-    // reads tile kt + 1's first fragments), then runs its MFMAs, then waits for
-    // those reads.  Tile kt + ST goes into the stage of tile kt: every wave has
-    // read all of tile kt's fragments before the barrier.
+    // entry the fragments of sub-step 0 are in slot (U * NKS) % 2.  Sub-step
+    // ks runs its MFMAs with the reads of sub-step ks + 1 between them.  The
+    // last sub-step first waits for tile kt + 1 (tiles up to kt + ST - 1 have
+    // been issued, so ST - 2 tiles may stay in flight), passes the barrier
+    // (after it every wave has read all of tile kt, so its stage may be
+    // refilled), and runs its MFMAs with the reads of tile kt + 1's first
+    // sub-step and the loads of tile kt + ST into this stage between them.
+    // Every step does the same: tiles past the end of K are loaded from an
+    // empty range (zeros, no memory access) and read but never used.
     auto step = [&](auto u_tag, int kt) {
         constexpr int U = decltype(u_tag)::value;
         constexpr int S = U % ST;
+        constexpr int S1 = (S + 1) % ST;
         static_for<NKS>([&](auto ks_tag) {
             constexpr int KS = decltype(ks_tag)::value;
             constexpr int CUR = (U * NKS + KS) & 1, NXT = CUR ^ 1;
-            bool pending = true;
+            const auto cur = std::integral_constant<int, CUR>{};
+            const auto nxt = std::integral_constant<int, NXT>{};
             if constexpr (KS + 1 < NKS) {
-                read_frags(std::integral_constant<int, S>{}, std::integral_constant<int, KS + 1>{},
-                           std::integral_constant<int, NXT>{});
+                interleave(cur, std::integral_constant<int, NR>{}, [&](auto o_tag) {
+                    read_op(std::integral_constant<int, S>{}, std::integral_constant<int, KS + 1>{}, nxt, o_tag);
+                });
             } else {
-                pending = kt + 1 < nkt;
-                if (pending) {
-                    const int last_issued = (kt + ST - 1 < nkt - 1) ? kt + ST - 1 : nkt - 1;
-                    wait_tile(kt + 1, last_issued);
-                    __builtin_amdgcn_s_barrier();
-                    if (kt + ST < nkt) issue_tile(kt + ST, S);
-                    read_frags(std::integral_constant<int, (S + 1) % ST>{}, std::integral_constant<int, 0>{},
-                               std::integral_constant<int, NXT>{});
-                }
+                const Desc d = make_desc(kt + ST);
+                wait_vm<(ST - 2) * L>();
+                __builtin_amdgcn_s_barrier();
+                interleave(cur, std::integral_constant<int, NR + L>{}, [&](auto o_tag) {
+                    constexpr int O = decltype(o_tag)::value;
+                    if constexpr (O < NR)
+                        read_op(std::integral_constant<int, S1>{}, std::integral_constant<int, 0>{}, nxt, o_tag);
+                    else
+                        load_op(std::integral_constant<int, O - NR>{}, d, S);
+                });
             }
-            mfmas(std::integral_constant<int, CUR>{});
-            // keep every MFMA of this sub-step ahead of the wait
-            __builtin_amdgcn_sched_barrier(0);
-            if (pending) wait_frags(std::integral_constant<int, NXT>{});
+            wait_frags(nxt);
         });
     };
 
     // unroll so that both the stage and the fragment-slot parity repeat
     constexpr int UNROLL = ((ST * NKS) % 2 == 0) ? ST : 2 * ST;
     if (nkt > 0) {
-        const int first = (ST < nkt) ? ST : nkt;
-        for (int t = 0; t < first; ++t) issue_tile(t, t);
-        wait_tile(0, first - 1);
+        static_for<ST>([&](auto t_tag) { issue_tile(decltype(t_tag)::value, decltype(t_tag)::value); });
+        wait_vm<(ST - 1) * L>();
         __builtin_amdgcn_s_barrier();
-        read_frags(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{},
-                   std::integral_constant<int, 0>{});
+        static_for<NR>([&](auto r_tag) {
+            read_op(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{},
+                    std::integral_constant<int, 0>{}, r_tag);
+        });
         wait_frags(std::integral_constant<int, 0>{});
         for (int kt = 0; kt < nkt; kt += UNROLL) {
             static_for<UNROLL>([&](auto u_tag) {
-                constexpr int UU = decltype(u_tag)::value;
-                if (kt + UU < nkt) step(u_tag, kt + UU);
+                if (kt + decltype(u_tag)::value < nkt) step(u_tag, kt + decltype(u_tag)::value);
             });
         }
+        // no load may still be writing this workgroup's LDS when it exits
+        wait_vm<0>();
     }
 
     // ---- epilogue: + C in fp32, round, masked store

@@ -299,6 +299,50 @@ __global__ __launch_bounds__(64) void probe_lds_swizzle_kernel(uint32_t* out, Sw
     out[threadIdx.x + 64 * blockIdx.x] = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
 }
 
+
+// probe_mfma_rate: every wave of a workgroup of up to 8 waves issues `iters`
+// rounds of matrix instructions on register operands (16x16x32: 32
+// independent accumulators per round; 32x32x16: 8 accumulators, each used
+// twice), 524288 flop per wave per round either way.  Wave 0 of each
+// workgroup records the shader-clock count (s_memtime) and the 100 MHz
+// constant-rate count (s_memrealtime) across its loop into clk[2 * block];
+// the host derives the sustained matrix rate and the clock under that load.
+template <int MF>
+__global__ __launch_bounds__(512) void probe_mfma_rate_kernel(int iters, float* out, uint64_t* clk) {
+    const int l = threadIdx.x & 63;
+    u32x4 av, bv;
+    for (int d = 0; d < 4; ++d) {
+        av[d] = 0x3f803f80u ^ static_cast<uint32_t>((l * 7 + d) & 3);
+        bv[d] = 0x3c003c00u ^ static_cast<uint32_t>((l * 5 + d) & 3);
+    }
+    const bf16x8 a = __builtin_bit_cast(bf16x8, av), b = __builtin_bit_cast(bf16x8, bv);
+    const uint64_t t0 = __builtin_readcyclecounter();
+    const uint64_t r0 = __builtin_amdgcn_s_memrealtime();
+    float sum = 0.0f;
+    if constexpr (MF == 16) {
+        f32x4 acc[32];
+        for (int i = 0; i < 32; ++i) acc[i] = f32x4{static_cast<float>(i), 0, 0, 0};
+        for (int it = 0; it < iters; ++it)
+#pragma unroll
+            for (int i = 0; i < 32; ++i) acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[i], 0, 0, 0);
+        for (int i = 0; i < 32; ++i) sum += acc[i][0] + acc[i][3];
+    } else {
+        f32x16 acc[8];
+        for (int i = 0; i < 8; ++i) { acc[i] = f32x16{}; acc[i][0] = static_cast<float>(i); }
+        for (int it = 0; it < iters; ++it)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[i & 7] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[i & 7], 0, 0, 0);
+        for (int i = 0; i < 8; ++i) sum += acc[i][0] + acc[i][15];
+    }
+    const uint64_t r1 = __builtin_amdgcn_s_memrealtime();
+    const uint64_t t1 = __builtin_readcyclecounter();
+    out[blockIdx.x * blockDim.x + threadIdx.x] = sum;
+    if (threadIdx.x == 0) {
+        clk[2 * blockIdx.x] = t1 - t0;
+        clk[2 * blockIdx.x + 1] = r1 - r0;
+    }
+}
+
 }  // namespace
 
 extern "C" {
@@ -400,6 +444,17 @@ int probe_mfma(int mf, int dtype, const uint16_t* A, const uint16_t* B, float* D
 // in: 512 halfwords, out: 256 halfwords (device pointers).
 int probe_lds_read_tr(const uint16_t* in, uint16_t* out, void* stream) {
     hipLaunchKernelGGL(probe_lds_read_tr_kernel, dim3(1), dim3(64), 0, static_cast<hipStream_t>(stream), in, out);
+    return static_cast<int>(hipGetLastError());
+}
+
+// mf 16 or 32, waves per workgroup 1..8; out: grid * 64 * waves floats,
+// clk: 2 * grid uint64 (device pointers).  Returns a hipError_t value.
+int probe_mfma_rate(int mf, int waves, int iters, int grid, float* out, uint64_t* clk, void* stream) {
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (waves < 1 || waves > 8 || grid < 1 || iters < 0) return static_cast<int>(hipErrorInvalidValue);
+    if (mf == 16) hipLaunchKernelGGL(probe_mfma_rate_kernel<16>, dim3(grid), dim3(64 * waves), 0, s, iters, out, clk);
+    else if (mf == 32) hipLaunchKernelGGL(probe_mfma_rate_kernel<32>, dim3(grid), dim3(64 * waves), 0, s, iters, out, clk);
+    else return static_cast<int>(hipErrorInvalidValue);
     return static_cast<int>(hipGetLastError());
 }
 
