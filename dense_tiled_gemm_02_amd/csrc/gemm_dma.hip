@@ -248,12 +248,16 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(KArgs p) {
 #pragma unroll
         for (int i = 0; i < FM; ++i) tie(fa[SL][i]);
     };
-    // MFMA number Q (row-fragment major) of a sub-step, operands in slot SL
+    // MFMA number Q (row-fragment major) of a sub-step, operands in slot SL.
+    // The B fragment goes in as the instruction's first operand and the A
+    // fragment as its second, so each accumulator holds the transposed block:
+    // a lane's registers are consecutive columns of one row of D, stored as
+    // 8-byte vectors in the epilogue.
     auto mfma_op = [&](auto slot_tag, auto q_tag) {
         constexpr int SL = decltype(slot_tag)::value;
         constexpr int Q = decltype(q_tag)::value;
         constexpr int I = Q / FN, J = Q % FN;
-        acc[I][J] = mfma<MF, BF16>(fa[SL][I], fb[SL][J], acc[I][J]);
+        acc[I][J] = mfma<MF, BF16>(fb[SL][J], fa[SL][I], acc[I][J]);
     };
     constexpr int NQ = FM * FN;       // MFMAs per sub-step
 
@@ -342,22 +346,49 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(KArgs p) {
         wait_vm<0>();
     }
 
-    // ---- epilogue: + C in fp32, round, masked store
+    // ---- epilogue: + C in fp32, round, masked store.  Lane l holds, per
+    // block (i, j), row l % MF of the block and G runs of 4 consecutive
+    // columns (16x16x32: columns 4 (l / 16) + 0..3; 32x32x16: run q at
+    // columns 8 q + 4 (l / 32) + 0..3).
+    constexpr int G = AccT<MF>::regs / 4;
     const bool has_c = p.has_c != 0;
+    const bool dvec = (p.ldd % 4 == 0) && (reinterpret_cast<uintptr_t>(p.D) % 8 == 0);
+    const bool cvec = !has_c || ((p.ldc % 4 == 0) && (reinterpret_cast<uintptr_t>(p.C) % 8 == 0));
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
+        const int row = m0 + wm * TM + i * MF + (lane % MF);
+        if (row >= M) continue;
+        const int64_t drow = static_cast<int64_t>(row) * p.ldd;
+        const int64_t crow = static_cast<int64_t>(row) * p.ldc;
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
-            const int col = n0 + wn * TN + j * MF + (lane % MF);
 #pragma unroll
-            for (int r = 0; r < AccT<MF>::regs; ++r) {
-                int row;
-                if constexpr (MF == 16) row = m0 + wm * TM + i * 16 + 4 * (lane / 16) + r;
-                else row = m0 + wm * TM + i * 32 + 8 * (r / 4) + 4 * (lane / 32) + (r % 4);
-                if (row < M && col < N) {
-                    float v = acc[i][j][r];
-                    if (has_c) v += widen<BF16>(p.C[static_cast<int64_t>(row) * p.ldc + col]);
-                    p.D[static_cast<int64_t>(row) * p.ldd + col] = narrow<BF16>(v);
+            for (int q = 0; q < G; ++q) {
+                const int col = n0 + wn * TN + j * MF + 8 * q + 4 * (lane / MF);
+                float v[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) v[r] = acc[i][j][4 * q + r];
+                if (dvec && cvec && col + 4 <= N) {
+                    if (has_c) {
+                        const uint2 cv = *reinterpret_cast<const uint2*>(p.C + crow + col);
+                        v[0] += widen<BF16>(static_cast<uint16_t>(cv.x & 0xffffu));
+                        v[1] += widen<BF16>(static_cast<uint16_t>(cv.x >> 16));
+                        v[2] += widen<BF16>(static_cast<uint16_t>(cv.y & 0xffffu));
+                        v[3] += widen<BF16>(static_cast<uint16_t>(cv.y >> 16));
+                    }
+                    uint2 dv;
+                    dv.x = static_cast<uint32_t>(narrow<BF16>(v[0])) | (static_cast<uint32_t>(narrow<BF16>(v[1])) << 16);
+                    dv.y = static_cast<uint32_t>(narrow<BF16>(v[2])) | (static_cast<uint32_t>(narrow<BF16>(v[3])) << 16);
+                    *reinterpret_cast<uint2*>(p.D + drow + col) = dv;
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        if (col + r < N) {
+                            float w = v[r];
+                            if (has_c) w += widen<BF16>(p.C[crow + col + r]);
+                            p.D[drow + col + r] = narrow<BF16>(w);
+                        }
+                    }
                 }
             }
         }

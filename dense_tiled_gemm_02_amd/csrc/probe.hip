@@ -18,6 +18,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <utility>
+
 namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -343,6 +345,145 @@ __global__ __launch_bounds__(512) void probe_mfma_rate_kernel(int iters, float* 
     }
 }
 
+// probe_lds_fill_rate: each 8-wave workgroup owns 64 KiB of `src` (its block
+// index selects the slice; the slices stay in L2 after the first pass) and
+// fills its 64 KiB of LDS from it `iters` times; every wave moves 8 KiB per
+// pass, in 1 KiB instructions.  Modes:
+//   0  direct global -> LDS loads (buffer_load_dwordx4 ... lds)
+//   1  as 0, plus 24 16-byte LDS reads per wave per pass (the operand-read
+//      traffic of a 256 x 256 x 64 GEMM step)
+//   2  only the 24 LDS reads per wave per pass
+//   3  global -> VGPR loads (buffer_load_dwordx4) then 16-byte LDS writes
+//   4  as 3, plus the 24 LDS reads
+// Wave 0 records the shader-clock cycles of its loop in cyc[block]; every
+// access stays inside the workgroup's 64 KiB of src and of LDS.
+template <int MODE>
+__global__ __launch_bounds__(512) void probe_lds_fill_rate_kernel(const uint16_t* src, int iters, uint32_t* cyc,
+                                                                  uint32_t* sink) {
+    typedef __attribute__((address_space(3))) void lds_void;
+    __shared__ __attribute__((aligned(1024))) uint16_t lds[32768];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint16_t* base = src + static_cast<int64_t>(blockIdx.x) * 32768;
+    __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, 65536, 0x00020000);
+    const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+        (const __attribute__((address_space(3))) uint16_t*)lds));
+    u32x4 acc = {0, 0, 0, 0};
+    __syncthreads();
+    const uint64_t t0 = __builtin_readcyclecounter();
+    for (int it = 0; it < iters; ++it) {
+        if constexpr (MODE == 0 || MODE == 1) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(lds + (wave * 8 + i) * 512), 16,
+                                                        (wave * 8 + i) * 1024 + lane * 16, 0, 0, 0);
+        }
+        if constexpr (MODE == 3 || MODE == 4) {
+            u32x4 v[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                v[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                    r, (wave * 8 + i) * 1024 + lane * 16, 0, 0));
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const uint32_t a = lds0 + (wave * 8 + i) * 1024 + lane * 16;
+                asm volatile("ds_write_b128 %0, %1" : : "v"(a), "v"(v[i]) : "memory");
+            }
+        }
+        if constexpr (MODE == 1 || MODE == 2 || MODE == 4) {
+#pragma unroll
+            for (int j = 0; j < 24; ++j) {
+                u32x4 v;
+                const uint32_t a = lds0 + (((wave * 24 + j) * 1024 + lane * 16) & 65535);
+                asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(a));
+                acc ^= v;
+            }
+        }
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+        __syncthreads();
+    }
+    const uint64_t t1 = __builtin_readcyclecounter();
+    if (threadIdx.x == 0) cyc[blockIdx.x] = static_cast<uint32_t>(t1 - t0);
+    if (acc[0] == 0x9e3779b9u && acc[1] == 0x7f4a7c15u) sink[threadIdx.x] = acc[2] + lds[threadIdx.x];
+}
+
+template <typename Fn, int... I>
+__device__ __forceinline__ void static_for32_impl(Fn&& fn, std::integer_sequence<int, I...>) {
+    (fn(std::integral_constant<int, I>{}), ...);
+}
+template <typename Fn>
+__device__ __forceinline__ void static_for32(Fn&& fn) {
+    static_for32_impl(fn, std::make_integer_sequence<int, 32>{});
+}
+
+// probe_mfma_mix: every wave of an 8-wave workgroup runs `iters` rounds of 32
+// independent 16x16x32 MFMAs on register operands; after every 32 / NL of
+// them it issues one memory instruction of 1 KiB (NL per round), inside the
+// workgroup's own 64 KiB of src and of LDS:
+//   MODE 0  direct global -> LDS load       MODE 1  global -> VGPR load + LDS write
+//   MODE 2  16-byte LDS read                MODE 3  global -> VGPR load only
+// and waits for them at the end of the round.  Wave 0 records the
+// shader-clock cycles of its loop in cyc[block]: with NL = 0 the pure
+// matrix-core time, otherwise how the memory traffic slows it.
+template <int MODE, int NL>
+__global__ __launch_bounds__(512) void probe_mfma_mix_kernel(const uint16_t* src, int iters, uint32_t* cyc,
+                                                             float* out) {
+    typedef __attribute__((address_space(3))) void lds_void;
+    __shared__ __attribute__((aligned(1024))) uint16_t lds[32768];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint16_t* base = src + static_cast<int64_t>(blockIdx.x) * 32768;
+    __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, 65536, 0x00020000);
+    const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+        (const __attribute__((address_space(3))) uint16_t*)lds));
+    u32x4 av, bv;
+    for (int d = 0; d < 4; ++d) {
+        av[d] = 0x3f803f80u ^ static_cast<uint32_t>((lane * 7 + d) & 3);
+        bv[d] = 0x3c003c00u ^ static_cast<uint32_t>((lane * 5 + d) & 3);
+    }
+    const bf16x8 a = __builtin_bit_cast(bf16x8, av), b = __builtin_bit_cast(bf16x8, bv);
+    f32x4 acc[32];
+    for (int i = 0; i < 32; ++i) acc[i] = f32x4{static_cast<float>(i), 0, 0, 0};
+    u32x4 keep = {0, 0, 0, 0};
+    __syncthreads();
+    const uint64_t t0 = __builtin_readcyclecounter();
+    for (int it = 0; it < iters; ++it) {
+        static_for32([&](auto q_tag) {
+            constexpr int Q = decltype(q_tag)::value;
+            acc[Q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[Q], 0, 0, 0);
+            if constexpr (NL > 0 && Q % (32 / (NL > 0 ? NL : 1)) == 0) {
+                constexpr int X = Q / (32 / (NL > 0 ? NL : 1));
+                const int slot = (wave * 8 + ((it * NL + X) & 7));
+                if constexpr (MODE == 0) {
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(lds + slot * 512), 16, slot * 1024 + lane * 16,
+                                                            0, 0, 0);
+                } else if constexpr (MODE == 1 || MODE == 3) {
+                    u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                        r, slot * 1024 + lane * 16, 0, 0));
+                    if constexpr (MODE == 1) {
+                        const uint32_t ad = lds0 + slot * 1024 + lane * 16;
+                        asm volatile("ds_write_b128 %0, %1" : : "v"(ad), "v"(v) : "memory");
+                    } else {
+                        keep ^= v;
+                    }
+                } else {
+                    u32x4 v;
+                    const uint32_t ad = lds0 + slot * 1024 + lane * 16;
+                    asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(ad));
+                    keep ^= v;
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        });
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    }
+    const uint64_t t1 = __builtin_readcyclecounter();
+    if (threadIdx.x == 0) cyc[blockIdx.x] = static_cast<uint32_t>(t1 - t0);
+    float sum = static_cast<float>(keep[0] ^ keep[1] ^ keep[2] ^ keep[3]) * 1e-30f;
+    for (int i = 0; i < 32; ++i) sum += acc[i][0] + acc[i][3];
+    out[blockIdx.x * 512 + threadIdx.x] = sum;
+}
+
 }  // namespace
 
 extern "C" {
@@ -456,6 +597,41 @@ int probe_mfma_rate(int mf, int waves, int iters, int grid, float* out, uint64_t
     else if (mf == 32) hipLaunchKernelGGL(probe_mfma_rate_kernel<32>, dim3(grid), dim3(64 * waves), 0, s, iters, out, clk);
     else return static_cast<int>(hipErrorInvalidValue);
     return static_cast<int>(hipGetLastError());
+}
+
+// src: at least grid * 64 KiB readable bytes; cyc: grid uint32; sink: 512
+// uint32 (written only if a data-dependent test passes).  Device pointers.
+int probe_lds_fill_rate(int mode, const uint16_t* src, int64_t src_bytes, int grid, int iters, uint32_t* cyc,
+                        uint32_t* sink, void* stream) {
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (grid < 1 || iters < 1 || src_bytes < static_cast<int64_t>(grid) * 65536)
+        return static_cast<int>(hipErrorInvalidValue);
+    switch (mode) {
+        case 0: hipLaunchKernelGGL(probe_lds_fill_rate_kernel<0>, dim3(grid), dim3(512), 0, s, src, iters, cyc, sink); break;
+        case 1: hipLaunchKernelGGL(probe_lds_fill_rate_kernel<1>, dim3(grid), dim3(512), 0, s, src, iters, cyc, sink); break;
+        case 2: hipLaunchKernelGGL(probe_lds_fill_rate_kernel<2>, dim3(grid), dim3(512), 0, s, src, iters, cyc, sink); break;
+        case 3: hipLaunchKernelGGL(probe_lds_fill_rate_kernel<3>, dim3(grid), dim3(512), 0, s, src, iters, cyc, sink); break;
+        case 4: hipLaunchKernelGGL(probe_lds_fill_rate_kernel<4>, dim3(grid), dim3(512), 0, s, src, iters, cyc, sink); break;
+        default: return static_cast<int>(hipErrorInvalidValue);
+    }
+    return static_cast<int>(hipGetLastError());
+}
+
+// mode 0..3, nl in {0, 1, 2, 4, 8}; src: at least grid * 64 KiB readable bytes;
+// cyc: grid uint32; out: grid * 512 floats.  Device pointers.
+int probe_mfma_mix(int mode, int nl, const uint16_t* src, int64_t src_bytes, int grid, int iters, uint32_t* cyc,
+                   float* out, void* stream) {
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (grid < 1 || iters < 1 || src_bytes < static_cast<int64_t>(grid) * 65536)
+        return static_cast<int>(hipErrorInvalidValue);
+#define DTG_MIX(M, NLV) \
+    if (mode == M && nl == NLV) { hipLaunchKernelGGL((probe_mfma_mix_kernel<M, NLV>), dim3(grid), dim3(512), 0, s, src, iters, cyc, out); return static_cast<int>(hipGetLastError()); }
+#define DTG_MIX_ALL(M) DTG_MIX(M, 1) DTG_MIX(M, 2) DTG_MIX(M, 4) DTG_MIX(M, 8)
+    DTG_MIX(0, 0)
+    DTG_MIX_ALL(0) DTG_MIX_ALL(1) DTG_MIX_ALL(2) DTG_MIX_ALL(3)
+#undef DTG_MIX_ALL
+#undef DTG_MIX
+    return static_cast<int>(hipErrorInvalidValue);
 }
 
 }  // extern "C"
