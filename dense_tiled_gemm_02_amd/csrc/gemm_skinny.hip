@@ -262,11 +262,16 @@ __global__ __launch_bounds__(64 * NWV) void gemm_skinny_kernel(KArgs p) {
     int* counters = static_cast<int*>(p.ws);
     float* part = reinterpret_cast<float*>(static_cast<char*>(p.ws) + kCounterBytes) +
                   static_cast<int64_t>(slab) * S * 16 * BN;
-    for (int t = tid; t < 16 * BN; t += NT) {
+    constexpr int PT = (16 * BN + NT - 1) / NT;   // outputs per thread
+#pragma unroll
+    for (int j = 0; j < PT; ++j) {
+        const int t = tid + j * NT;
+        if (t >= 16 * BN) break;
         float v = 0.0f;
 #pragma unroll
         for (int w = 0; w < NWV; ++w) v += red[(w * 16 + t / BN) * BN + t % BN];
         __hip_atomic_store(&part[slice * 16 * BN + t], v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        red[t] = v;                              // only this thread reads position t
     }
     wait_vm<0>();
     __syncthreads();
@@ -275,24 +280,38 @@ __global__ __launch_bounds__(64 * NWV) void gemm_skinny_kernel(KArgs p) {
         *last = __hip_atomic_fetch_add(&counters[slab], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) == S - 1;
     __syncthreads();
     if (!*last) return;
-    for (int t = tid; t < 16 * BN; t += NT) {
+    // The other slices' partials are loaded in groups of up to 8 slices, all of
+    // a thread's outputs at once, then summed in slice order; this
+    // workgroup's own partial comes from LDS (bitwise the value it stored).
+    float v[PT];
+#pragma unroll
+    for (int j = 0; j < PT; ++j) v[j] = 0.0f;
+    for (int s0 = 0; s0 < S; s0 += 8) {
+        float x[8][PT];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+#pragma unroll
+            for (int j = 0; j < PT; ++j) {
+                const int t = (tid + j * NT < 16 * BN) ? tid + j * NT : 0;
+                x[u][j] = (s0 + u < S && s0 + u != slice)
+                              ? __hip_atomic_load(&part[(s0 + u) * 16 * BN + t], __ATOMIC_RELAXED,
+                                                  __HIP_MEMORY_SCOPE_SYSTEM)
+                              : red[t];
+            }
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+#pragma unroll
+            for (int j = 0; j < PT; ++j)
+                if (s0 + u < S) v[j] += x[u][j];
+    }
+#pragma unroll
+    for (int j = 0; j < PT; ++j) {
+        const int t = tid + j * NT;
         const int row = t / BN, col = t % BN;
-        float v = 0.0f;
-        // up to 8 slices' loads in flight at once, summed in slice order
-        for (int s0 = 0; s0 < S; s0 += 8) {
-            float x[8];
-#pragma unroll
-            for (int u = 0; u < 8; ++u)
-                x[u] = s0 + u < S ? __hip_atomic_load(&part[(s0 + u) * 16 * BN + t], __ATOMIC_RELAXED,
-                                                      __HIP_MEMORY_SCOPE_SYSTEM)
-                                  : 0.0f;
-#pragma unroll
-            for (int u = 0; u < 8; ++u)
-                if (s0 + u < S) v += x[u];
-        }
-        if (row < M && n0 + col < N) {
-            if (has_c) v += widen<BF16>(p.C[static_cast<int64_t>(row) * p.ldc + n0 + col]);
-            p.D[static_cast<int64_t>(row) * p.ldd + n0 + col] = narrow<BF16>(v);
+        if (t < 16 * BN && row < M && n0 + col < N) {
+            float o = v[j];
+            if (has_c) o += widen<BF16>(p.C[static_cast<int64_t>(row) * p.ldc + n0 + col]);
+            p.D[static_cast<int64_t>(row) * p.ldd + n0 + col] = narrow<BF16>(o);
         }
     }
     if (tid == 0) __hip_atomic_store(&counters[slab], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);

@@ -2,6 +2,11 @@
 
     python -m dense_tiled_gemm_02_amd.rocprof_summary DIR [--match SUBSTR]
     python -m dense_tiled_gemm_02_amd.rocprof_summary --traffic FETCH_DIR WRITE_DIR COPY_BYTES OUT.json
+    python -m dense_tiled_gemm_02_amd.rocprof_summary --report OUT MATCH "WORKLOAD" "WORK" COPY_BYTES
+
+--report composes the per-kernel summary kept under profiles/ from the five
+passes OUT/prof_{trace,fetch,write,mfma,lds} that profile_commands() lists,
+for the kernels whose name contains MATCH.
 
 DIR holds the CSV files of one or more rocprofv3 runs (kernel_stats,
 kernel_trace, counter_collection).  Prints, per kernel name: dispatch count
@@ -102,6 +107,70 @@ def summarise(d, match=None):
     return "\n".join(out)
 
 
+BENCH = "python3 bench.py --steps 100 --warmup 10 --no-cpu --copy-mb 512"
+PASSES = [("trace", "--kernel-trace --stats", "gemm"),
+          ("fetch", "--kernel-trace --pmc FETCH_SIZE", "p"),
+          ("write", "--kernel-trace --pmc WRITE_SIZE", "p"),
+          ("mfma", "--kernel-trace --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES SQ_INSTS_MFMA GRBM_GUI_ACTIVE", "p"),
+          ("lds", "--kernel-trace --pmc SQ_LDS_BANK_CONFLICT SQ_INSTS_LDS SQ_LDS_IDX_ACTIVE SQ_WAIT_INST_LDS", "p")]
+TITLES = {"trace": "kernel trace (rocprofv3 --kernel-trace --stats)", "fetch": "FETCH_SIZE pass",
+          "write": "WRITE_SIZE pass", "mfma": "MFMA / clock pass", "lds": "LDS pass"}
+
+
+def profile_commands(out="OUT"):
+    """The rocprofv3 runs behind a committed profile summary (one counter set per run)."""
+    return ["rocprofv3 %s -f csv -d %s/prof_%s -o %s -- %s" % (flags, out, name, o, BENCH)
+            for name, flags, o in PASSES]
+
+
+def report(out, match, workload, work, copy_bytes):
+    """Text summary of one kernel over the five passes under `out`."""
+    lines = []
+    names = set()
+    for name, _, _ in PASSES:
+        for t in glob.glob(os.path.join(out, "prof_" + name, "**", "*kernel_trace.csv"), recursive=True):
+            for r in csv.DictReader(open(t)):
+                if match in r["Kernel_Name"]:
+                    names.add(r["Kernel_Name"])
+    kname = sorted(names)[0] if names else match
+    short = kname.split("namespace)::")[-1].split("(dtg::")[0]
+    lines.append("Kernel:   " + short)
+    lines.append("Workload: " + workload)
+    lines.append("Algorithmic work per launch: " + work)
+    lines.append("")
+    lines.append("Commands (run from the repository root on one MI355X, after")
+    lines.append('"python -m dense_tiled_gemm_02_amd.build"; bench.py runs the bf16 4096^3 and the')
+    lines.append("skinny bf16 16x8192x8192 workloads back to back and ends with one 512 MiB device")
+    lines.append("copy used to calibrate the memory counters):")
+    for c in profile_commands():
+        lines.append("  " + c)
+    lines.append("  python3 -m dense_tiled_gemm_02_amd.rocprof_summary --traffic OUT/prof_fetch OUT/prof_write "
+                 "%d profiles/traffic.json" % copy_bytes)
+    lines.append('  python3 -m dense_tiled_gemm_02_amd.rocprof_summary --report OUT "%s" ...   (this file)' % match)
+    for name, _, _ in PASSES:
+        lines.append("")
+        lines.append("--- %s ---" % TITLES[name])
+        body = summarise(os.path.join(out, "prof_" + name), match)
+        under = False
+        for l in body.splitlines():
+            if l.startswith("    "):
+                if under:
+                    lines.append("  " + l.strip())
+            elif l.startswith("  "):
+                under = match in l
+                if under:
+                    lines.append(l.strip())
+        if name == "write":
+            t = traffic(os.path.join(out, "prof_fetch"), os.path.join(out, "prof_write"), copy_bytes)
+            for k, v in t["kernels"].items():
+                if match in k:
+                    lines.append("Calibration: the %d MiB copy kernel sets FETCH_SIZE x %.4f and WRITE_SIZE x %.4f,"
+                                 % (copy_bytes >> 20, t["fetch_scale"], t["write_scale"]))
+                    lines.append("so HBM-side traffic per launch = %.1f KiB x %.4f + %.1f KiB x %.4f = %.1f MB" % (
+                        v["fetch_kib"], t["fetch_scale"], v["write_kib"], t["write_scale"], v["bytes"] / 1e6))
+    return "\n".join(lines) + "\n"
+
+
 if __name__ == "__main__":
     args = sys.argv[1:]
     if args and args[0] == "--traffic":
@@ -113,6 +182,9 @@ if __name__ == "__main__":
                 _short(k, 100), v["fetch_kib"], v["write_kib"], v["bytes"] / 1e6))
         print("scales: fetch %.4f  write %.4f  (copy of %d bytes)" % (t["fetch_scale"], t["write_scale"],
                                                                      t["copy_bytes"]))
+        sys.exit(0)
+    if args and args[0] == "--report":
+        sys.stdout.write(report(args[1], args[2], args[3], args[4], int(args[5])))
         sys.exit(0)
     m = None
     if "--match" in args:
