@@ -216,18 +216,40 @@ def sweep(args):
                              dict(kernel=3, bm=256, bn=128, bk=64, stages=3, mfma=16, group_m=8),
                              dict(kernel=3, bm=128, bn=128, bk=64, stages=4, mfma=16, group_m=8),
                              dict(kernel=3, bm=128, bn=128, bk=64, stages=2, mfma=32, group_m=8)],
-        "square_f16_1024": [dict(bm=32, bn=32, bk=32), dict(bm=64, bn=64, bk=32), dict(bm=128, bn=128, bk=64),
-                            dict(bm=64, bn=64, bk=64)],
-        "square_f16_256": [dict(bm=32, bn=32, bk=32), dict(bm=64, bn=64, bk=32), dict(bm=64, bn=64, bk=64),
-                           dict(bm=16, bn=64, bk=64)],
+        "square_f16_1024": [dict(), dict(kernel=3, bm=128, bn=128, bk=64, stages=4, waves_m=2, waves_n=4),
+                            dict(kernel=3, bm=128, bn=128, bk=32, stages=4, waves_m=2, waves_n=4),
+                            dict(kernel=3, bm=128, bn=128, bk=32, stages=4, waves_m=2, waves_n=4, splitk=2),
+                            dict(kernel=3, bm=128, bn=128, bk=64, stages=4, waves_m=2, waves_n=4, splitk=2),
+                            dict(kernel=3, bm=128, bn=128, waves_m=2, waves_n=4, splitk=2),
+                            dict(kernel=3, bm=128, bn=128, waves_m=2, waves_n=4, splitk=8),
+                            dict(kernel=3, bm=128, bn=128, waves_m=2, waves_n=2, splitk=4),
+                            dict(kernel=3, bm=128, bn=128, waves_m=2, waves_n=4, splitk=1),
+                            dict(bm=64, bn=64, bk=64),
+                            dict(kernel=3, bm=128, bn=128, bk=64, stages=2, mfma=16),
+                            dict(kernel=3, bm=128, bn=128, bk=64, stages=2, mfma=32),
+                            dict(kernel=3, bm=256, bn=128, bk=64, stages=2, mfma=16)],
+        "square_f16_256": [dict(), dict(bm=64, bn=64, bk=64), dict(bm=16, bn=64, bk=64),
+                           dict(kernel=3, bm=128, bn=128, waves_m=2, waves_n=4, splitk=1)],
+        "deepk_bf16_512x512x32768": [dict(kernel=3, bm=128, bn=128, waves_m=2, waves_n=4, splitk=s)
+                                     for s in (1, 2, 4, 8, 12, 16)] +
+                                    [dict(kernel=3, bm=128, bn=128, waves_m=2, waves_n=2, splitk=s)
+                                     for s in (4, 16)] + [dict()],
         "skinny_bf16_16x8192": [dict(kernel=2, bn=32, waves_n=8, bk=64, stages=3, splitk=1)] +
                                [dict(kernel=2, bn=128, waves_n=8, bk=32, stages=2, splitk=s) for s in (4, 6)] +
                                [dict(kernel=2, bn=128, waves_n=4, bk=32, stages=st, splitk=s)
                                 for st in (3, 4) for s in (4, 6, 8)] +
                                [dict(kernel=2, bn=128, waves_n=2, bk=32, stages=st, splitk=s)
                                 for st in (6, 8) for s in (4, 8)],
-        "tail_f16_4000x3000x1000_c": [dict(bm=256, bn=128), dict(bm=128, bn=128, bk=64), dict(bm=256, bn=256),
-                                      dict(bm=128, bn=256)],
+        "tail_f16_4000x3000x1000_c": [dict(), dict(kernel=3, bm=256, bn=128, waves_m=4, waves_n=2),
+                                      dict(kernel=3, bm=128, bn=256, waves_m=2, waves_n=4),
+                                      dict(kernel=3, bm=128, bn=128, waves_m=2, waves_n=4),
+                                      dict(kernel=3, bm=256, bn=128, bk=64, stages=2, mfma=16),
+                                      dict(kernel=3, bm=256, bn=128, bk=64, stages=3, mfma=16),
+                                      dict(kernel=3, bm=128, bn=128, bk=64, stages=2, mfma=16),
+                                      dict(kernel=3, bm=128, bn=128, bk=64, stages=4, mfma=16),
+                                      dict(kernel=3, bm=256, bn=256, bk=64, stages=2, mfma=16),
+                                      dict(kernel=3, bm=128, bn=256, bk=64, stages=2, mfma=16),
+                                      dict(bm=128, bn=128, bk=64)],
     }[args.workload]
     w = gemm_inputs.WORKLOADS[args.workload]
     rot = 4 if w.name.startswith("skinny") else 1

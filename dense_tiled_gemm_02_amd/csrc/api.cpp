@@ -128,7 +128,7 @@ bool matches(const dtg::KernelEntry* e, const gemm_config& f) {
            (f.bn == 0 || f.bn == e->bn) && (f.bk == 0 || f.bk == e->bk) &&
            (f.stages == 0 || f.stages == e->stages) && (f.mfma == 0 || f.mfma == e->mfma) &&
            (f.waves_m == 0 || f.waves_m == e->waves_m) && (f.waves_n == 0 || f.waves_n == e->waves_n) &&
-           (f.splitk == 0 || e->splitk == 0 || f.splitk == e->splitk);
+           (f.splitk <= 1 || e->splitk == 0 || f.splitk <= e->splitk);   // e->splitk: most slices, 0 = any
 }
 
 // The first compiled variant that fits the device and matches `want`.
@@ -171,9 +171,11 @@ const std::vector<TunedKey>& tuned_table() {
 gemm_config heuristic(const gemm_problem* p, const gemm_device_info& dev, int* group_m, bool allow_ws) {
     const int64_t M = p->M, N = p->N, K = p->K;
     *group_m = 8;
-    if (M <= 16) {
-        // Stream B.  Each workgroup reads a 256-byte band of every row of its
-        // K slice (HBM needs >= 128-byte runs), and the K slices supply the
+    if (M <= 32) {
+        // Decode regime, bucketed by M: 16-row slabs for M <= 16, 32-row slabs
+        // (two MFMA row blocks) for M <= 32.  Stream B.  Each workgroup reads
+        // a 256-byte band of every row of its K slice (HBM needs >= 128-byte
+        // runs), and the K slices supply the
         // workgroups: S = CUs / slabs (one workgroup per CU: these kernels
         // hold most of the LDS), at most 8, each slice >= 512 k.
         if (allow_ws && cdiv(N, 128) <= 4096) {
@@ -182,31 +184,45 @@ gemm_config heuristic(const gemm_problem* p, const gemm_device_info& dev, int* g
             if (s > 8) s = 8;
             while (s > 1 && K / s < 512) --s;
             if (s < 1) s = 1;
-            gemm_config c = cfg_of(dtg::KF_SKINNY, 16, 128, 32, 2, 16, 1, 8);
+            gemm_config c = cfg_of(dtg::KF_SKINNY, M <= 16 ? 16 : 32, 128, 32, 2, 16, 1, 8);
             c.splitk = static_cast<int32_t>(s);
             return c;
         }
         // no workspace: one workgroup per 32-column slab, K split over its 8 waves
-        const int bn = (cdiv(N, 32) >= dev.cu_count) ? 32 : 16;
-        gemm_config c = cfg_of(dtg::KF_SKINNY, 16, bn, 64, 3, 16, 1, 8);
+        const int bn = (cdiv(N, 32) >= dev.cu_count || M > 16) ? 32 : 16;
+        gemm_config c = cfg_of(dtg::KF_SKINNY, M <= 16 ? 16 : 32, bn, M <= 16 ? 64 : 32, 3, 16, 1, 8);
         c.splitk = 1;
         return c;
     }
-    if (M <= 32) return cfg_of(dtg::KF_TILE, 32, 32, 32, 2, 16, 2, 2);
+    // Largest 8-wave direct-to-LDS tile that keeps at least half of the CUs
+    // busy (a 1-wave-per-SIMD tile hides far less latency, so 8 waves win even
+    // with a quarter of the CUs idle); below that, 128 x 128 tiles with K
+    // slices across workgroups (deterministic fused reduce) fill the CUs.
     struct C { int fam, bm, bn, bk, st, mf, wm, wn; };
     static const C ladder[] = {
-        {dtg::KF_DMA, 256, 256, 64, 2, 16, 2, 4}, {dtg::KF_DMA, 256, 128, 64, 2, 16, 2, 2},
-        {dtg::KF_DMA, 128, 128, 64, 2, 16, 2, 2}, {dtg::KF_TILE, 64, 64, 64, 2, 16, 2, 2},
-        {dtg::KF_TILE, 32, 32, 32, 2, 16, 2, 2},
+        {dtg::KF_DMA, 256, 256, 64, 2, 16, 2, 4}, {dtg::KF_DMA, 256, 128, 64, 2, 16, 4, 2},
+        {dtg::KF_DMA, 128, 256, 64, 2, 16, 2, 4}, {dtg::KF_DMA, 128, 128, 64, 2, 16, 2, 4},
     };
-    const C* best = nullptr;
-    int64_t best_tiles = -1;
     for (const C& c : ladder) {
         const int64_t tiles = cdiv(M, c.bm) * cdiv(N, c.bn);
-        if (tiles >= dev.cu_count) { best = &c; break; }
-        if (tiles > best_tiles) { best_tiles = tiles; best = &c; }
+        if (2 * tiles >= dev.cu_count)
+            return cfg_of(c.fam, c.bm, c.bn, c.bk, c.st, c.mf, c.wm, c.wn);
     }
-    return cfg_of(best->fam, best->bm, best->bn, best->bk, best->st, best->mf, best->wm, best->wn);
+    const C& small = ladder[3];
+    gemm_config c = cfg_of(small.fam, small.bm, small.bn, small.bk, small.st, small.mf, small.wm, small.wn);
+    const int64_t tiles = cdiv(M, small.bm) * cdiv(N, small.bn);
+    const int64_t nkt = cdiv(K, small.bk);
+    if (allow_ws && tiles <= dtg::kMaxCounters) {
+        // Slices of at least 16 K steps (the fused reduce costs a few memory
+        // round trips, ~4 us: at 1024^3, 16 steps per tile, no split is faster),
+        // at most 16 (the last arriver reads them all); measured on bf16
+        // 512 x 512 x 32768: 322 us unsplit, 42 us with 16 slices.
+        int64_t s = dev.cu_count / tiles;
+        if (s > nkt / 16) s = nkt / 16;
+        if (s > 16) s = 16;
+        if (s > 1) c.splitk = static_cast<int32_t>(s);
+    }
+    return c;
 }
 
 gemm_status plan_impl(const gemm_problem* prob, const gemm_device_info* dev, const gemm_config* force,
@@ -270,13 +286,16 @@ gemm_status plan_impl(const gemm_problem* prob, const gemm_device_info* dev, con
                         want.bm, want.bn, want.bk, want.stages, want.mfma, want.waves_m, want.waves_n,
                         want.kernel, (int)prob->dtype, (int)vec, (long long)dev->lds_per_wg);
     }
-    if (e->family == dtg::KF_SKINNY && prob->M > 16)
-        return fail(GEMM_ERR_UNSUPPORTED, "the skinny kernel family runs M <= 16 only (M=%lld)",
+    if (e->family == dtg::KF_SKINNY && prob->M > e->bm)
+        return fail(GEMM_ERR_UNSUPPORTED, "this skinny kernel runs M <= %d only (M=%lld)", e->bm,
                     (long long)prob->M);
     int splits = 1;
-    if (e->family == dtg::KF_SKINNY) {
+    if (e->family == dtg::KF_SKINNY || e->family == dtg::KF_DMA) {
         splits = want.splitk > 0 ? want.splitk : 1;
         if (splits > 64) return fail(GEMM_ERR_UNSUPPORTED, "at most 64 K slices (splitk=%d)", splits);
+        if (e->splitk > 0 && splits > e->splitk)
+            return fail(GEMM_ERR_UNSUPPORTED, "%s takes at most %d K slices (splitk=%d)", e->name, e->splitk,
+                        splits);
         if (splits > 1 && !allow_ws)
             return fail(GEMM_ERR_UNSUPPORTED, "K slices across workgroups need a workspace");
     }
@@ -289,15 +308,19 @@ gemm_status plan_impl(const gemm_problem* prob, const gemm_device_info* dev, con
     pl->num_pid_m = cdiv(prob->M, e->bm);
     pl->num_pid_n = cdiv(prob->N, e->bn);
     pl->grid = pl->num_pid_m * pl->num_pid_n * splits;
-    pl->ws_bytes = e->family == dtg::KF_SKINNY ? dtg::skinny_workspace_bytes(pl->num_pid_n, e->bn, splits) : 0;
+    pl->ws_bytes = e->family == dtg::KF_SKINNY ? dtg::skinny_workspace_bytes(pl->num_pid_n, e->bm, e->bn, splits)
+                   : e->family == dtg::KF_DMA
+                       ? dtg::dma_workspace_bytes(pl->num_pid_m * pl->num_pid_n, e->bm, e->bn, splits)
+                       : 0;
     if (pl->ws_bytes < 0) {
         delete pl;
-        return fail(GEMM_ERR_UNSUPPORTED, "K slices across workgroups support at most 4096 column slabs");
+        return fail(GEMM_ERR_UNSUPPORTED, "K slices across workgroups support at most %d column slabs or tiles",
+                    dtg::kMaxCounters);
     }
     if (group_m < 1) group_m = 1;
     gemm_config& c = pl->cfg;
     c = cfg_of(e->family, e->bm, e->bn, e->bk, e->stages, e->mfma, e->waves_m, e->waves_n);
-    c.splitk = e->family == dtg::KF_SKINNY ? splits : e->splitk;
+    c.splitk = splits;
     c.group_m = group_m;
     c.xcd_remap = (xcd && dev->xcd_count > 1) ? GEMM_XCD_ON : GEMM_XCD_OFF;
     if (log_enabled()) {
@@ -504,7 +527,9 @@ gemm_status gemm_run(const gemm_plan* plan, const void* A, const void* B, const 
     a.ldb = p.sb_k;
     a.ldc = p.has_c ? p.sc_m : 0;
     a.ldd = p.sd_m;
-    a.splits = (e == plan->entry && e->family == dtg::KF_SKINNY) ? plan->cfg.splitk : 1;
+    a.splits = (e == plan->entry && (e->family == dtg::KF_SKINNY || e->family == dtg::KF_DMA))
+                   ? plan->cfg.splitk
+                   : 1;   // the element-wise fallback runs the whole K range per tile
     a.ws = workspace;
     const int64_t grid = static_cast<int64_t>(a.num_pid_m) * a.num_pid_n * a.splits;
     hipError_t err = e->launch(a, grid, static_cast<hipStream_t>(stream));

@@ -84,6 +84,9 @@ typedef std::integral_constant<bool, false> Unchecked;  // interior loads
 
 constexpr uint32_t kRsrcWord3 = 0x00020000u;   // raw buffer of dwords
 constexpr uint32_t kOOB = 0x80000000u;         // offset past any descriptor range
+// cache-policy bits of a buffer access at system scope (sc0 | sc1): the
+// access goes past the per-XCD L2 caches, like a system-scope atomic
+constexpr int kSysScope = 1 | 16;
 constexpr int64_t kMaxRecords = 0x7ffffff0;
 
 template <int N, typename Fn>

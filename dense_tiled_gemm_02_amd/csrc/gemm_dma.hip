@@ -77,8 +77,18 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(KArgs p) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / WN, wn = wave % WN;
 
-    int pid_m, pid_n;
-    tile_of_workgroup<int>(blockIdx.x, p.num_pid_m, p.num_pid_n, p.group_m, p.xcds, &pid_m, &pid_n);
+    // Workgroup -> (K slice, output tile): the XCD permutation runs over the
+    // whole grid, consecutive positions are consecutive tiles (grouped order)
+    // of one slice.  With one slice this is tile_of_workgroup.
+    const int ntiles = p.num_pid_m * p.num_pid_n;
+    const int NS = p.splits;
+    int pid_m, pid_n, tile_lin, slice;
+    {
+        const int pos = xcd_permute<int>(blockIdx.x, ntiles * NS, p.xcds);
+        slice = pos / ntiles;
+        tile_lin = pos - slice * ntiles;
+        grouped_tile<int>(tile_lin, p.num_pid_m, p.num_pid_n, p.group_m, &pid_m, &pid_n);
+    }
     const int m0 = pid_m * BM, n0 = pid_n * BN;
     const int M = p.M, N = p.N, K = p.K;
     const bool edge = (m0 + BM > M) || (n0 + BN > N);
@@ -125,10 +135,15 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(KArgs p) {
         bool chk;    // edge tile or K tail: lanes test their own bounds
     };
     const int nfull = K / BK;
+    // this slice's K steps: [kt0, kt1)
+    const int nkt_all = (K + BK - 1) / BK;
+    const int per_slice = (nkt_all + NS - 1) / NS;
+    const int kt0 = slice * per_slice;
+    const int kt1 = (kt0 + per_slice < nkt_all) ? kt0 + per_slice : nkt_all;
     auto make_desc = [&](int kt) {
         Desc d;
         d.k0 = kt * BK;
-        const bool live = d.k0 < K;   // tiles past K (issued only to keep the ring uniform) read nothing
+        const bool live = kt < kt1;   // steps past the slice (issued only to keep the ring uniform) read nothing
         const uint16_t* abase = p.A + static_cast<int64_t>(m0) * p.lda + (live ? d.k0 : 0);
         d.ra = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<uint16_t*>(abase), 0,
@@ -284,7 +299,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(KArgs p) {
         }
     };
 
-    const int nkt = (K + BK - 1) / BK;
+    const int nkt = kt1 > kt0 ? kt1 - kt0 : 0;   // K steps of this slice
 
     // One K step (tile kt) on LDS stage S = kt % ST; U is kt's position in the
     // unrolled loop, which fixes which fragment slot holds which sub-step.  On
@@ -329,7 +344,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(KArgs p) {
     // unroll so that both the stage and the fragment-slot parity repeat
     constexpr int UNROLL = ((ST * NKS) % 2 == 0) ? ST : 2 * ST;
     if (nkt > 0) {
-        static_for<ST>([&](auto t_tag) { issue_tile(decltype(t_tag)::value, decltype(t_tag)::value); });
+        static_for<ST>([&](auto t_tag) { issue_tile(kt0 + decltype(t_tag)::value, decltype(t_tag)::value); });
         wait_vm<(ST - 1) * L>();
         __builtin_amdgcn_s_barrier();
         static_for<NR>([&](auto r_tag) {
@@ -337,13 +352,100 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(KArgs p) {
                     std::integral_constant<int, 0>{}, r_tag);
         });
         wait_frags(std::integral_constant<int, 0>{});
-        for (int kt = 0; kt < nkt; kt += UNROLL) {
+        for (int j = 0; j < nkt; j += UNROLL) {
             static_for<UNROLL>([&](auto u_tag) {
-                if (kt + decltype(u_tag)::value < nkt) step(u_tag, kt + decltype(u_tag)::value);
+                if (j + decltype(u_tag)::value < nkt) step(u_tag, kt0 + j + decltype(u_tag)::value);
             });
         }
         // no load may still be writing this workgroup's LDS when it exits
         wait_vm<0>();
+    }
+
+    // ---- K slices across workgroups: publish this slice's fp32 partial tile;
+    // the workgroup that arrives last at the tile's counter sums the slices
+    // in slice order (so the result does not depend on arrival order) into
+    // acc and goes on to the epilogue below; the others are done.  Partials
+    // are kept in register order, [tile][slice][wave][block][lane][4 floats],
+    // so each lane writes and reads back only its own 16-byte runs, with
+    // system-scope accesses (they bypass the per-XCD L2 caches).
+    constexpr int NB = FM * FN * (AccT<MF>::regs / 4);   // 16-byte runs per lane
+    // (two slices of partials are held in registers: only tiles of at most
+    // 64 accumulators per lane take K slices; the planner keeps the others at 1)
+    if constexpr (NB <= 16) if (NS > 1) {
+        constexpr int64_t WAVE_F = static_cast<int64_t>(NB) * 64 * 4;   // floats per wave per slice
+        int* counters = static_cast<int*>(p.ws);
+        float* tile_part = reinterpret_cast<float*>(static_cast<char*>(p.ws) + kCounterBytes) +
+                           static_cast<int64_t>(tile_lin) * NS * NW * WAVE_F;
+        const __amdgpu_buffer_rsrc_t pr = __builtin_amdgcn_make_buffer_rsrc(
+            tile_part, 0, clamp_records(static_cast<int64_t>(NS) * NW * WAVE_F * 4), kRsrcWord3);
+        auto run_off = [&](int sl, int b) {   // byte offset of lane's run b of slice sl
+            return static_cast<uint32_t>(((static_cast<int64_t>(sl) * NW + wave) * WAVE_F + (b * 64 + lane) * 4) * 4);
+        };
+        // run b = (i * FN + j) * G + g holds registers 4g..4g+3 of acc[i][j]
+        constexpr int G = AccT<MF>::regs / 4;
+        auto get_run = [&](auto b_tag) {
+            constexpr int B = decltype(b_tag)::value;
+            constexpr int I = B / G / FN, J = (B / G) % FN, Q = B % G;
+            f32x4 v;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) v[r] = acc[I][J][4 * Q + r];
+            return v;
+        };
+        auto set_run = [&](auto b_tag, const f32x4& v) {
+            constexpr int B = decltype(b_tag)::value;
+            constexpr int I = B / G / FN, J = (B / G) % FN, Q = B % G;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[I][J][4 * Q + r] = v[r];
+        };
+        static_for<NB>([&](auto b_tag) {
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, get_run(b_tag)), pr,
+                                                   run_off(slice, decltype(b_tag)::value), 0, kSysScope);
+        });
+        wait_vm<0>();
+        __syncthreads();
+        int* last = reinterpret_cast<int*>(smem);
+        if (tid == 0)
+            *last = __hip_atomic_fetch_add(&counters[tile_lin], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) ==
+                    NS - 1;
+        __syncthreads();
+        if (!*last) return;
+        // Sum the slices in order into acc (this slice's own runs are read back
+        // like the others: the same bits).  Loads go in units of HB runs, the
+        // next unit in flight while one is added: two units of registers.
+        constexpr int HB = (NB <= 8) ? NB : NB / 2;
+        constexpr int UPS = NB / HB;                  // units per slice
+        f32x4 buf[2][HB];
+        auto fetch = [&](int u, int bb) {
+            const int sl = u / UPS, b0 = (u % UPS) * HB;
+#pragma unroll
+            for (int b = 0; b < HB; ++b)
+                buf[bb][b] = __builtin_bit_cast(
+                    f32x4, __builtin_amdgcn_raw_buffer_load_b128(pr, run_off(sl, b0 + b), 0, kSysScope));
+        };
+        auto add = [&](int u, int bb) {
+            static_for<UPS>([&](auto h_tag) {
+                constexpr int H = decltype(h_tag)::value;
+                if (u % UPS == H) {
+                    static_for<HB>([&](auto b_tag) {
+                        constexpr int B = H * HB + decltype(b_tag)::value;
+                        const f32x4 cur = (u < UPS) ? f32x4{0.0f, 0.0f, 0.0f, 0.0f}
+                                                    : get_run(std::integral_constant<int, B>{});
+                        set_run(std::integral_constant<int, B>{}, cur + buf[bb][decltype(b_tag)::value]);
+                    });
+                }
+            });
+        };
+        const int nu = NS * UPS;
+        fetch(0, 0);
+        for (int u = 0; u < nu; u += 2) {
+            if (u + 1 < nu) fetch(u + 1, 1);
+            add(u, 0);
+            if (u + 1 < nu) {
+                if (u + 2 < nu) fetch(u + 2, 0);
+                add(u + 1, 1);
+            }
+        }
+        if (tid == 0) __hip_atomic_store(&counters[tile_lin], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     }
 
     // ---- epilogue: + C in fp32, round, masked store.  Lane l holds, per
@@ -395,6 +497,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(KArgs p) {
     }
 }
 
+constexpr int kMaxDmaSplits = 64;
+
 template <int BM, int BN, int BK, int WM, int WN, int MF, int ST, bool BF16>
 hipError_t launch_dma(const KArgs& a, int64_t grid, hipStream_t stream) {
     hipLaunchKernelGGL((gemm_dma_kernel<BM, BN, BK, WM, WN, MF, ST, BF16>),
@@ -405,7 +509,7 @@ hipError_t launch_dma(const KArgs& a, int64_t grid, hipStream_t stream) {
 #define DTG_STR2(x) #x
 #define DTG_STR(x) DTG_STR2(x)
 #define DMA_ENTRY(BM, BN, BK, WM, WN, MF, ST, BF)                                            \
-    {KF_DMA, BM, BN, BK, ST, MF, WM, WN, 1, BF, 1, 64 * WM * WN,                            \
+    {KF_DMA, BM, BN, BK, ST, MF, WM, WN, ((BM / WM) * (BN / WN) / 64 <= 64 ? kMaxDmaSplits : 1), BF, 1, 64 * WM * WN,                            \
      static_cast<int64_t>(ST) * (BM + BN) * BK * 2,                                         \
      &launch_dma<BM, BN, BK, WM, WN, MF, ST, (BF != 0)>,                                    \
      "gemm_dma_kernel<" DTG_STR(BM) "," DTG_STR(BN) "," DTG_STR(BK) "," DTG_STR(WM) ","     \
@@ -424,7 +528,22 @@ const KernelEntry kDmaTable[] = {
     DMA_BOTH(128, 128, 64, 2, 2, 16, 2),
     DMA_BOTH(128, 128, 64, 2, 2, 16, 4),
     DMA_BOTH(128, 128, 64, 2, 2, 32, 2),
+    DMA_BOTH(128, 128, 64, 2, 4, 16, 2),
+    DMA_BOTH(256, 128, 64, 4, 2, 16, 2),
+    DMA_BOTH(128, 256, 64, 2, 4, 16, 2),
+    DMA_BOTH(128, 128, 64, 2, 4, 16, 4),
+    DMA_BOTH(128, 128, 32, 2, 4, 16, 4),
 };
+
+}  // namespace
+
+int64_t dma_workspace_bytes(int64_t tiles, int bm, int bn, int splits) {
+    if (splits <= 1) return 0;
+    if (tiles > kMaxCounters) return -1;
+    return kCounterBytes + tiles * splits * static_cast<int64_t>(bm) * bn * 4;
+}
+
+namespace {
 
 }  // namespace
 

@@ -1,4 +1,4 @@
-// Skinny-M GEMM kernel for gfx950:  D = A x B (+ C) with M <= 16.
+// Skinny-M GEMM kernel for gfx950:  D = A x B (+ C) with M <= 32.
 //
 // With a handful of rows the product is bound by streaming B from HBM (the
 // decode regime of "Tuning Triton", section 4: a skinny M wants its own tile
@@ -51,11 +51,9 @@ using namespace dev;
 //  BN = 128, 256 (256-, 512-byte rows): chunk pairs XOR 2 * ((r & 3) | bit 3
 //          of r << 2).
 // All these maps are involutions.
-// The workspace starts with a fixed region of kMaxSlabs arrival counters, the
+// The workspace starts with the fixed region of kMaxCounters arrival counters, the
 // same for every plan, so plans of any slab count can share one workspace;
 // fp32 partial tiles follow.
-constexpr int kMaxSlabs = 4096;
-constexpr int64_t kCounterBytes = kMaxSlabs * 4;
 
 template <int BN>
 __device__ __forceinline__ int b_pos(int r) {
@@ -70,7 +68,8 @@ __device__ __forceinline__ int b_chunk(int r, int q) {
     else return q;
 }
 
-template <int BN, int NWV, int CK, int ST, bool BF16>
+// BMR: rows of the output slab (16 or 32: one or two 16-row MFMA blocks).
+template <int BN, int NWV, int CK, int ST, bool BF16, int BMR>
 __global__ __launch_bounds__(64 * NWV) void gemm_skinny_kernel(KArgs p) {
     constexpr int NT = 64 * NWV;
     constexpr int CHB = BN / 8;            // 16-byte chunks per B row
@@ -78,16 +77,18 @@ __global__ __launch_bounds__(64 * NWV) void gemm_skinny_kernel(KArgs p) {
     constexpr int IB = CK / RB;            // B instructions per chunk
     constexpr int CHA = CK / 8;            // 16-byte chunks per A row
     constexpr int RA = 64 / CHA;           // A rows per wave instruction
-    constexpr int IA = 16 / RA;            // A instructions per chunk
+    constexpr int IA = BMR / RA;           // A instructions per chunk
+    constexpr int MB = BMR / 16;           // 16-row MFMA blocks
     constexpr int FN = BN / 16;
     constexpr int KSN = CK / 32;
-    constexpr int SB = CK * BN, SAE = 16 * CK, STG = SB + SAE;   // elements
+    constexpr int SB = CK * BN, SAE = BMR * CK, STG = SB + SAE;  // elements
     constexpr int OPS = IB + IA;           // vector-memory ops per chunk
     static_assert(BN == 16 || BN == 32 || BN == 64 || BN == 128 || BN == 256, "BN");
     static_assert(CK == 32 || CK == 64, "CK");
     static_assert(IA >= 1 && IB >= 1, "load split");
     static_assert(ST >= 2 && ST <= 8 && (ST - 2) * OPS < 64, "stages");
-    static_assert(NWV * ST * STG * 2 >= NWV * 16 * BN * 4 + 4, "reduction buffer and flag");
+    static_assert(BMR == 16 || BMR == 32, "BMR");
+    static_assert(NWV * ST * STG * 2 >= NWV * BMR * BN * 4 + 4, "reduction buffer and flag");
     static_assert(OPS < 64, "vmcnt");
 
     __shared__ __attribute__((aligned(1024))) uint16_t smem[NWV * ST * STG];
@@ -166,12 +167,16 @@ __global__ __launch_bounds__(64 * NWV) void gemm_skinny_kernel(KArgs p) {
     };
 
     // ---- per-lane operand read offsets (LDS bytes within a stage)
-    uint32_t a_off[KSN], b_off[FN][KSN][2];
+    uint32_t a_off[MB][KSN], b_off[FN][KSN][2];
     {
-        const int i = lane & 15, g = lane >> 4;
+        const int g = lane >> 4;
 #pragma unroll
-        for (int ks = 0; ks < KSN; ++ks)
-            a_off[ks] = (SB + i * CK + (((ks * 4 + g) ^ swz<CHA>(i)) * 8)) * 2;   // chunk ks*4 + g of row i
+        for (int mb = 0; mb < MB; ++mb) {
+            const int i = mb * 16 + (lane & 15);
+#pragma unroll
+            for (int ks = 0; ks < KSN; ++ks)
+                a_off[mb][ks] = (SB + i * CK + (((ks * 4 + g) ^ swz<CHA>(i)) * 8)) * 2;   // chunk ks*4 + g of row i
+        }
         const int jq = lane & 15;
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn)
@@ -186,9 +191,11 @@ __global__ __launch_bounds__(64 * NWV) void gemm_skinny_kernel(KArgs p) {
                 }
     }
 
-    f32x4 acc[FN];
+    f32x4 acc[MB][FN];
 #pragma unroll
-    for (int fn = 0; fn < FN; ++fn) acc[fn] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) acc[mb][fn] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
     const uint32_t ring = lds_addr(smem) + wave * ST * STG * 2;
 #pragma unroll
@@ -205,9 +212,11 @@ __global__ __launch_bounds__(64 * NWV) void gemm_skinny_kernel(KArgs p) {
         const int slot = c % ST;
         if (c + ST - 1 < nc) issue(c + ST - 1, (c + ST - 1) % ST);
         const uint32_t base = ring + slot * STG * 2;
-        u32x4 af[KSN], bf[FN][KSN];
+        u32x4 af[MB][KSN], bf[FN][KSN];
 #pragma unroll
-        for (int ks = 0; ks < KSN; ++ks) af[ks] = lds_read16<0>(base + a_off[ks]);
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int ks = 0; ks < KSN; ++ks) af[mb][ks] = lds_read16<0>(base + a_off[mb][ks]);
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
@@ -218,7 +227,9 @@ __global__ __launch_bounds__(64 * NWV) void gemm_skinny_kernel(KArgs p) {
             }
         lds_wait_all();
 #pragma unroll
-        for (int ks = 0; ks < KSN; ++ks) tie(af[ks]);
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int ks = 0; ks < KSN; ++ks) tie(af[mb][ks]);
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
@@ -226,25 +237,29 @@ __global__ __launch_bounds__(64 * NWV) void gemm_skinny_kernel(KArgs p) {
 #pragma unroll
         for (int ks = 0; ks < KSN; ++ks)
 #pragma unroll
-            for (int fn = 0; fn < FN; ++fn) acc[fn] = mfma<16, BF16>(af[ks], bf[fn][ks], acc[fn]);
+            for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                for (int fn = 0; fn < FN; ++fn) acc[mb][fn] = mfma<16, BF16>(af[mb][ks], bf[fn][ks], acc[mb][fn]);
     }
 
     // ---- sum the wave partials in a fixed order, + C, round, store
     __syncthreads();                                   // every ring is drained
-    float* red = reinterpret_cast<float*>(smem);       // [NWV][16][BN]
+    float* red = reinterpret_cast<float*>(smem);       // [NWV][BMR][BN]
 #pragma unroll
-    for (int fn = 0; fn < FN; ++fn)
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-            red[(wave * 16 + 4 * (lane >> 4) + r) * BN + fn * 16 + (lane & 15)] = acc[fn][r];
+        for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                red[(wave * BMR + mb * 16 + 4 * (lane >> 4) + r) * BN + fn * 16 + (lane & 15)] = acc[mb][fn][r];
     __syncthreads();
     const bool has_c = p.has_c != 0;
     if (S == 1) {
-        for (int t = tid; t < 16 * BN; t += NT) {
+        for (int t = tid; t < BMR * BN; t += NT) {
             const int row = t / BN, col = t % BN;
             float v = 0.0f;
 #pragma unroll
-            for (int w = 0; w < NWV; ++w) v += red[(w * 16 + row) * BN + col];
+            for (int w = 0; w < NWV; ++w) v += red[(w * BMR + row) * BN + col];
             if (row < M && n0 + col < N) {
                 if (has_c) v += widen<BF16>(p.C[static_cast<int64_t>(row) * p.ldc + n0 + col]);
                 p.D[static_cast<int64_t>(row) * p.ldd + n0 + col] = narrow<BF16>(v);
@@ -261,21 +276,21 @@ __global__ __launch_bounds__(64 * NWV) void gemm_skinny_kernel(KArgs p) {
     // avoids writing back or invalidating whole L2 caches.
     int* counters = static_cast<int*>(p.ws);
     float* part = reinterpret_cast<float*>(static_cast<char*>(p.ws) + kCounterBytes) +
-                  static_cast<int64_t>(slab) * S * 16 * BN;
-    constexpr int PT = (16 * BN + NT - 1) / NT;   // outputs per thread
+                  static_cast<int64_t>(slab) * S * BMR * BN;
+    constexpr int PT = (BMR * BN + NT - 1) / NT;  // outputs per thread
 #pragma unroll
     for (int j = 0; j < PT; ++j) {
         const int t = tid + j * NT;
-        if (t >= 16 * BN) break;
+        if (t >= BMR * BN) break;
         float v = 0.0f;
 #pragma unroll
-        for (int w = 0; w < NWV; ++w) v += red[(w * 16 + t / BN) * BN + t % BN];
-        __hip_atomic_store(&part[slice * 16 * BN + t], v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        for (int w = 0; w < NWV; ++w) v += red[(w * BMR + t / BN) * BN + t % BN];
+        __hip_atomic_store(&part[slice * BMR * BN + t], v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
         red[t] = v;                              // only this thread reads position t
     }
     wait_vm<0>();
     __syncthreads();
-    int* last = reinterpret_cast<int*>(red + NWV * 16 * BN);   // just past the partial sums
+    int* last = reinterpret_cast<int*>(red + NWV * BMR * BN);   // just past the partial sums
     if (tid == 0)
         *last = __hip_atomic_fetch_add(&counters[slab], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) == S - 1;
     __syncthreads();
@@ -292,9 +307,9 @@ __global__ __launch_bounds__(64 * NWV) void gemm_skinny_kernel(KArgs p) {
         for (int u = 0; u < 8; ++u)
 #pragma unroll
             for (int j = 0; j < PT; ++j) {
-                const int t = (tid + j * NT < 16 * BN) ? tid + j * NT : 0;
+                const int t = (tid + j * NT < BMR * BN) ? tid + j * NT : 0;
                 x[u][j] = (s0 + u < S && s0 + u != slice)
-                              ? __hip_atomic_load(&part[(s0 + u) * 16 * BN + t], __ATOMIC_RELAXED,
+                              ? __hip_atomic_load(&part[(s0 + u) * BMR * BN + t], __ATOMIC_RELAXED,
                                                   __HIP_MEMORY_SCOPE_SYSTEM)
                               : red[t];
             }
@@ -308,7 +323,7 @@ __global__ __launch_bounds__(64 * NWV) void gemm_skinny_kernel(KArgs p) {
     for (int j = 0; j < PT; ++j) {
         const int t = tid + j * NT;
         const int row = t / BN, col = t % BN;
-        if (t < 16 * BN && row < M && n0 + col < N) {
+        if (t < BMR * BN && row < M && n0 + col < N) {
             float o = v[j];
             if (has_c) o += widen<BF16>(p.C[static_cast<int64_t>(row) * p.ldc + n0 + col]);
             p.D[static_cast<int64_t>(row) * p.ldd + n0 + col] = narrow<BF16>(o);
@@ -317,22 +332,23 @@ __global__ __launch_bounds__(64 * NWV) void gemm_skinny_kernel(KArgs p) {
     if (tid == 0) __hip_atomic_store(&counters[slab], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
-template <int BN, int NWV, int CK, int ST, bool BF16>
+template <int BN, int NWV, int CK, int ST, bool BF16, int BMR>
 hipError_t launch_skinny(const KArgs& a, int64_t grid, hipStream_t stream) {
-    hipLaunchKernelGGL((gemm_skinny_kernel<BN, NWV, CK, ST, BF16>), dim3(static_cast<unsigned>(grid)),
+    hipLaunchKernelGGL((gemm_skinny_kernel<BN, NWV, CK, ST, BF16, BMR>), dim3(static_cast<unsigned>(grid)),
                        dim3(64 * NWV), 0, stream, a);
     return hipGetLastError();
 }
 
 #define DTG_STR2(x) #x
 #define DTG_STR(x) DTG_STR2(x)
-#define SKINNY_ENTRY(BN, NWV, CK, ST, BF)                                                    \
-    {KF_SKINNY, 16, BN, CK, ST, 16, 1, NWV, 0, BF, 1, 64 * NWV,                             \
-     static_cast<int64_t>(NWV) * ST * (CK * BN + 16 * CK) * 2,                              \
-     &launch_skinny<BN, NWV, CK, ST, (BF != 0)>,                                            \
+#define SKINNY_ENTRY(BN, NWV, CK, ST, BF, BMR)                                               \
+    {KF_SKINNY, BMR, BN, CK, ST, 16, 1, NWV, 0, BF, 1, 64 * NWV,                            \
+     static_cast<int64_t>(NWV) * ST * (CK * BN + BMR * CK) * 2,                             \
+     &launch_skinny<BN, NWV, CK, ST, (BF != 0), BMR>,                                       \
      "gemm_skinny_kernel<" DTG_STR(BN) "," DTG_STR(NWV) "," DTG_STR(CK) "," DTG_STR(ST) ","  \
-     DTG_STR(BF) ">"}
-#define SKINNY_BOTH(BN, NWV, CK, ST) SKINNY_ENTRY(BN, NWV, CK, ST, 0), SKINNY_ENTRY(BN, NWV, CK, ST, 1)
+     DTG_STR(BF) "," DTG_STR(BMR) ">"}
+#define SKINNY_BOTH(BN, NWV, CK, ST) SKINNY_ENTRY(BN, NWV, CK, ST, 0, 16), SKINNY_ENTRY(BN, NWV, CK, ST, 1, 16)
+#define SKINNY32_BOTH(BN, NWV, CK, ST) SKINNY_ENTRY(BN, NWV, CK, ST, 0, 32), SKINNY_ENTRY(BN, NWV, CK, ST, 1, 32)
 
 const KernelEntry kSkinnyTable[] = {
     SKINNY_BOTH(256, 4, 32, 2),
@@ -345,6 +361,10 @@ const KernelEntry kSkinnyTable[] = {
     SKINNY_BOTH(64, 8, 64, 2),
     SKINNY_BOTH(32, 8, 64, 3),
     SKINNY_BOTH(16, 8, 64, 3),
+    SKINNY32_BOTH(128, 8, 32, 2),
+    SKINNY32_BOTH(128, 4, 32, 3),
+    SKINNY32_BOTH(64, 8, 32, 3),
+    SKINNY32_BOTH(32, 8, 32, 3),
 };
 
 }  // namespace
@@ -365,10 +385,10 @@ hipError_t zero_words(void* p, int64_t nwords, hipStream_t stream) {
     return hipGetLastError();
 }
 
-int64_t skinny_workspace_bytes(int64_t nslabs, int bn, int splits) {
+int64_t skinny_workspace_bytes(int64_t nslabs, int bm, int bn, int splits) {
     if (splits <= 1) return 0;
-    if (nslabs > kMaxSlabs) return -1;
-    return kCounterBytes + nslabs * splits * 16 * bn * 4;
+    if (nslabs > kMaxCounters) return -1;
+    return kCounterBytes + nslabs * splits * static_cast<int64_t>(bm) * bn * 4;
 }
 
 const KernelEntry* skinny_kernel_table(int* count) {

@@ -18,10 +18,17 @@ struct KArgs {
     int32_t group_m;
     int32_t xcds;        // 1: no XCD pre-permutation
     int32_t has_c;
-    int32_t splits;      // K slices across workgroups (skinny kernels; 1 = none)
+    int32_t splits;      // K slices across workgroups (1 = none)
     int64_t lda, ldb, ldc, ldd;
-    void* ws;            // workspace: per-slab counters, then fp32 partial tiles
+    void* ws;            // workspace: arrival counters, then fp32 partial tiles
 };
+
+// Workspace of every split-K launch: a fixed region of kMaxCounters 32-bit
+// arrival counters (one per output slab or tile, left at zero by every
+// launch), then the fp32 partial tiles.  The region is the same for every
+// plan, so one zero-filled workspace serves any sequence of plans.
+constexpr int kMaxCounters = 4096;
+constexpr int64_t kCounterBytes = kMaxCounters * 4;
 
 typedef hipError_t (*launch_fn)(const KArgs& args, int64_t grid, hipStream_t stream);
 
@@ -46,10 +53,15 @@ const KernelEntry* tile_kernel_table(int* count);
 const KernelEntry* skinny_kernel_table(int* count);
 const KernelEntry* dma_kernel_table(int* count);
 
-// Workspace bytes of a skinny launch over nslabs slabs of bn columns split
-// into `splits` K slices (0 when splits == 1, -1 when nslabs is above the
-// fixed counter region).
-int64_t skinny_workspace_bytes(int64_t nslabs, int bn, int splits);
+// Workspace bytes of a skinny launch over nslabs slabs of bm x bn split into
+// `splits` K slices (0 when splits == 1, -1 when nslabs is above the fixed
+// counter region).
+int64_t skinny_workspace_bytes(int64_t nslabs, int bm, int bn, int splits);
+
+// Workspace bytes of a direct-to-LDS launch over `tiles` output tiles of
+// bm x bn split into `splits` K slices (0 when splits == 1, -1 when tiles is
+// above the counter region).
+int64_t dma_workspace_bytes(int64_t tiles, int bm, int bn, int splits);
 
 // Enqueue a kernel that writes zeros to nwords 32-bit words at p.
 hipError_t zero_words(void* p, int64_t nwords, hipStream_t stream);

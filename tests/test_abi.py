@@ -100,10 +100,34 @@ def test_plans_for_the_five_workloads_fit_the_device():
         grid, threads, lds = g.gemm_plan_launch(p)
         assert lds <= 160 * 1024
         assert threads % 64 == 0 and threads <= 1024
-        assert grid == -(-M // cfg.bm) * -(-N // cfg.bn) * (cfg.splitk if cfg.kernel == 2 else 1) or cfg.kernel == 2
+        assert grid == -(-M // cfg.bm) * -(-N // cfg.bn) * cfg.splitk or cfg.kernel == 2
         assert lds == g.gemm_lds_bytes(cfg.bm, cfg.bn, cfg.bk, cfg.stages, dt) or cfg.kernel == 2
         assert "kernel=" in p.describe()
     assert plan(4096, 4096, 4096).config.kernel == 3          # direct-to-LDS family when aligned
+
+
+def test_few_tiles_and_deep_k_take_k_slices():
+    # 512 x 512 x 32768 at 128 x 128: 16 tiles, 512 K steps: 16 slices of 32 steps fill the CUs
+    p = plan(512, 512, 32768)
+    c = p.config
+    assert c.kernel == 3 and (c.bm, c.bn) == (128, 128) and c.splitk == 16
+    grid, _, _ = g.gemm_plan_launch(p)
+    assert grid == 16 * 16
+    need = g.gemm_workspace_size(p)
+    assert need >= 16384 + 16 * 16 * 128 * 128 * 4               # counters + fp32 partial tiles
+    # 1024^3: 16 K steps per tile, too shallow to pay for the fused reduce
+    assert plan(1024, 1024, 1024, g.GEMM_F16).config.splitk == 1
+    # one tile, K = 65536: capped at 16 slices
+    c = plan(128, 128, 65536).config
+    assert c.splitk == 16
+    # the one-shot path has no workspace: no slices
+    p = g.gemm_plan_create_for(g.problem(1024, 1024, 1024, g.GEMM_F16), fake_gfx950(), {"kernel": 3, "bm": 128,
+                                                                                     "bn": 128, "splitk": 4})
+    assert p.config.splitk == 4
+    # the 256 x 256 tile keeps too many accumulators per lane for K slices
+    with pytest.raises(g.GemmError) as e:
+        plan(1024, 1024, 1024, force={"kernel": 3, "bm": 256, "bn": 256, "splitk": 2})
+    assert e.value.status == g.GEMM_ERR_UNSUPPORTED
 
 
 def test_key_includes_m():

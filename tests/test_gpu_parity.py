@@ -38,7 +38,7 @@ def _inputs(M, N, K, dt, has_c, seed, dist="uniform", scale=1.0):
 
 
 @pytest.mark.parametrize("name", ["square_f16_256", "square_f16_1024", "skinny_bf16_16x8192",
-                                  "tail_f16_4000x3000x1000_c"])
+                                  "tail_f16_4000x3000x1000_c", "deepk_bf16_512x512x32768"])
 def test_workload_full_parity(name):
     w = gemm_inputs.WORKLOADS[name]
     A, B, C = gemm_inputs.make(w)
@@ -114,9 +114,66 @@ def _variants(dt):
                                        (256, 256, 64, 2, 32, 2, 4), (256, 256, 32, 4, 32, 2, 4),
                                        (256, 128, 64, 3, 16, 2, 2), (256, 128, 64, 2, 16, 2, 2),
                                        (128, 256, 64, 2, 16, 2, 2), (128, 128, 64, 2, 16, 2, 2),
-                                       (128, 128, 64, 4, 16, 2, 2), (128, 128, 64, 2, 32, 2, 2)]:
+                                       (128, 128, 64, 4, 16, 2, 2), (128, 128, 64, 2, 32, 2, 2),
+                                       (128, 128, 64, 2, 16, 2, 4), (256, 128, 64, 2, 16, 4, 2),
+                                       (128, 256, 64, 2, 16, 2, 4)]:
         seen.append(dict(bm=bm, bn=bn, bk=bk, stages=st, mfma=mf, waves_m=wm, waves_n=wn, kernel=3))
     return seen
+
+
+DMA_SPLIT = [(128, 128, 64, 2, 16, 2, 4), (128, 128, 64, 2, 16, 2, 2), (128, 128, 64, 2, 32, 2, 2),
+             (128, 128, 64, 4, 16, 2, 2), (256, 128, 64, 2, 16, 4, 2), (128, 256, 64, 2, 16, 2, 4)]
+
+
+@pytest.mark.parametrize("mnk", [(300, 200, 1000), (130, 264, 2056), (128, 128, 4096), (520, 264, 200)])
+def test_dma_split_k(mnk):
+    """K slices across workgroups in the direct-to-LDS kernel (last arriver sums
+    the fp32 partials in slice order): ragged M/N edges, a K tail inside the
+    last slice, slices left without K steps (16 slices of a 4-step K), with
+    and without C; every result inside the bound, and each config run twice
+    gives the same bits whichever workgroup happened to arrive last."""
+    M, N, K = mnk
+    for dt, has_c in (("bf16", True), ("f16", False)):
+        A, B, C = _inputs(M, N, K, dt, has_c, seed=3 * M + 5 * N + K)
+        Ab, Bb = gemm_inputs.bits(A), gemm_inputs.bits(B)
+        Cb = gemm_inputs.bits(C) if C is not None else None
+        ref, S = oracle.gemm_f64(Ab, Bb, Cb, dt)
+        for bm, bn, bk, st, mf, wm, wn in DMA_SPLIT:
+            for sk in (2, 3, 5, 16):
+                cfg = dict(kernel=3, bm=bm, bn=bn, bk=bk, stages=st, mfma=mf, waves_m=wm, waves_n=wn, splitk=sk)
+                D1 = gpu_run(A, B, C, config=cfg)
+                D2 = gpu_run(A, B, C, config=cfg)
+                n, worst, first = oracle.tol_check(gemm_inputs.bits(D1), ref, S, dt)
+                assert n == 0, "%s %s %s: %d outside the bound (worst %.3g, first %d)" % (dt, mnk, cfg, n, worst,
+                                                                                         first)
+                assert torch.equal(D1.view(torch.int16), D2.view(torch.int16)), (dt, mnk, cfg)
+
+
+def test_split_plans_share_one_workspace():
+    """A skinny split plan and a direct-to-LDS split plan take turns on one
+    workspace (the counters sit in the same fixed region and every launch
+    leaves them at zero): every result correct and repeatable."""
+    A1, B1, C1 = _inputs(16, 2048, 2048, "bf16", True, seed=5)
+    A2, B2, C2 = _inputs(384, 256, 3072, "bf16", True, seed=6)
+    d1 = [t.cuda() for t in (A1, B1, C1)]
+    d2 = [t.cuda() for t in (A2, B2, C2)]
+    pa = g.plan_for(*d1, None, dict(kernel=2, bn=128, splitk=4))
+    pb = g.plan_for(*d2, None, dict(kernel=3, bm=128, bn=128, waves_m=2, waves_n=4, splitk=6))
+    need = max(g.gemm_workspace_size(pa), g.gemm_workspace_size(pb))
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    st = torch.cuda.current_stream().cuda_stream
+    g.gemm_workspace_init(pb, ws.data_ptr(), need, st)
+    outs = []
+    for i in range(6):
+        pl, (a, b, c), (M, N) = (pa, d1, (16, 2048)) if i % 2 == 0 else (pb, d2, (384, 256))
+        D = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        g.gemm_run(pl, a.data_ptr(), b.data_ptr(), c.data_ptr(), D.data_ptr(), ws.data_ptr(), need, st)
+        outs.append(D)
+    torch.cuda.synchronize()
+    for i, D in enumerate(outs):
+        A, B, C = (A1, B1, C1) if i % 2 == 0 else (A2, B2, C2)
+        check(A, B, C, D.cpu(), "bf16", label="shared workspace %d" % i)
+        assert torch.equal(outs[i % 2].view(torch.int16), D.view(torch.int16))
 
 
 SKINNY = [(256, 4, 32, 2), (128, 4, 32, 3), (128, 4, 32, 4), (128, 2, 32, 8), (128, 2, 32, 6), (128, 8, 32, 2), (64, 4, 64, 3), (64, 8, 64, 2), (32, 8, 64, 3), (16, 8, 64, 3)]
@@ -143,6 +200,51 @@ def test_skinny_variants(mnk):
                     assert torch.equal(by_part[key].view(torch.int16), D.view(torch.int16)), cfg
                 else:
                     by_part[key] = D
+
+
+SKINNY32 = [(128, 8, 32, 2), (128, 4, 32, 3), (64, 8, 32, 3), (32, 8, 32, 3)]
+
+
+@pytest.mark.parametrize("mnk", [(17, 1000, 1000), (24, 520, 264), (32, 4096, 512), (32, 64, 64),
+                                 (20, 8, 1024)])
+def test_skinny32_variants(mnk):
+    """The 32-row skinny kernels (two MFMA row blocks) for 16 < M <= 32, with
+    ragged N and K, over 1-8 workgroup slices; equal K partitions agree bit
+    for bit whatever the slab width."""
+    M, N, K = mnk
+    for dt, has_c in (("bf16", True), ("f16", False)):
+        A, B, C = _inputs(M, N, K, dt, has_c, seed=M + 11 * N + 3 * K)
+        by_part = {}
+        for bn, nw, ck, st in SKINNY32:
+            for sk in (1, 2, 3, 8):
+                cfg = dict(kernel=2, bm=32, bn=bn, waves_n=nw, bk=ck, stages=st, splitk=sk)
+                D = gpu_run(A, B, C, config=cfg)
+                check(A, B, C, D, dt, label="%s %s %s" % (dt, mnk, cfg))
+                key = (nw, ck, sk)
+                if key in by_part:
+                    assert torch.equal(by_part[key].view(torch.int16), D.view(torch.int16)), cfg
+                else:
+                    by_part[key] = D
+
+
+@pytest.mark.parametrize("m", [1, 2, 4, 8, 16, 17, 24, 32])
+def test_decode_buckets(m):
+    """The planner's decode regime (M bucketed to 16- or 32-row slabs), with a
+    workspace (K slices) and through the one-shot entry point (none)."""
+    N, K = 4096, 4096
+    A, B, C = _inputs(m, N, K, "bf16", m % 2 == 0, seed=700 + m, dist="normal", scale=1 / 64)
+    D = gpu_run(A, B, C)
+    check(A, B, C, D, "bf16", label="decode M=%d" % m)
+    dA, dB = A.cuda(), B.cuda()
+    dC = C.cuda() if C is not None else None
+    pl = g.plan_for(dA, dB, dC, None)
+    assert pl.config.kernel == 2 and pl.config.bm == (16 if m <= 16 else 32), pl.describe()
+    D1 = torch.full((m, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+    strides = [K, 1, N, 1, N if C is not None else 0, 1 if C is not None else 0, N, 1]
+    g.gemm(dA.data_ptr(), dB.data_ptr(), dC.data_ptr() if dC is not None else None, D1.data_ptr(), m, N, K,
+           strides, g.GEMM_BF16, 1 if C is not None else 0, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    check(A, B, C, D1.cpu(), "bf16", label="decode one-shot M=%d" % m)
 
 
 def test_skinny_workspace_reuse():
