@@ -70,6 +70,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="square_bf16_4096")
     ap.add_argument("--sweep", action="store_true")
+    ap.add_argument("--decode", action="store_true",
+                    help="time the decode regime: M in {1,2,4,8,16,32}, N = K in {4096, 8192}, bf16")
     ap.add_argument("--rounds", type=int, default=30)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-skinny", action="store_true")
@@ -230,6 +232,10 @@ def sweep(args):
                             dict(kernel=3, bm=256, bn=128, bk=64, stages=2, mfma=16)],
         "square_f16_256": [dict(), dict(bm=64, bn=64, bk=64), dict(bm=16, bn=64, bk=64),
                            dict(kernel=3, bm=128, bn=128, waves_m=2, waves_n=4, splitk=1)],
+        "decode_bf16_1x4096x4096": [dict()] + [dict(kernel=2, bm=16, bn=bn, waves_n=w, bk=bk, stages=st, splitk=sk)
+                                             for (bn, w, bk, st) in ((128, 8, 32, 2), (64, 8, 64, 2), (32, 8, 64, 3),
+                                                                     (16, 8, 64, 3), (128, 4, 32, 3))
+                                             for sk in (1, 2, 4, 8)],
         "deepk_bf16_512x512x32768": [dict(kernel=3, bm=128, bn=128, waves_m=2, waves_n=4, splitk=s)
                                      for s in (1, 2, 4, 8, 12, 16)] +
                                     [dict(kernel=3, bm=128, bn=128, waves_m=2, waves_n=2, splitk=s)
@@ -252,7 +258,8 @@ def sweep(args):
                                       dict(bm=128, bn=128, bk=64)],
     }[args.workload]
     w = gemm_inputs.WORKLOADS[args.workload]
-    rot = 4 if w.name.startswith("skinny") else 1
+    # B rotated over enough copies (> 300 MB) that HBM-bound shapes read it from HBM
+    rot = max(4, -(-300 * (1 << 20) // (2 * w.K * w.N))) if w.M <= 32 else 1
     case = Case(w, rotate=rot)
     ls = []
     for v in variants:
@@ -283,6 +290,46 @@ def sweep(args):
     return rows
 
 
+def decode(args):
+    """The M-bucketed decode regime: for each M, the planner's plan against
+    torch.matmul, B rotated over enough copies (> 256 MB) that every launch
+    reads it from HBM.  One JSON line per (M, N)."""
+    import torch
+    import gemm_inputs
+    import dense_tiled_gemm_02_amd as g
+    for n in (4096, 8192):
+        k = n
+        copies = max(4, -(-300 * (1 << 20) // (2 * k * n)))
+        Bs = [gemm_inputs.draw((k, n), 900 + r, "bf16", "normal", 1 / 64).cuda() for r in range(copies)]
+        for m in (1, 2, 4, 8, 16, 32):
+            A = gemm_inputs.draw((m, k), 800 + m, "bf16", "normal", 1 / 64).cuda()
+            D = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+            pl = g.plan_for(A, Bs[0], None, D)
+            stream = torch.cuda.current_stream().cuda_stream
+            ws, wsb = g.workspace_for(pl, torch.cuda.current_device(), stream)
+            run = g.lib().gemm_run
+            st = {"i": 0}
+
+            def launch(c, st=st):
+                for _ in range(c):
+                    b = Bs[st["i"] % copies]
+                    assert run(pl.handle, A.data_ptr(), b.data_ptr(), None, D.data_ptr(), ws, wsb, stream) == 0
+                    st["i"] += 1
+
+            def launch_torch(c, st=st):
+                for _ in range(c):
+                    torch.matmul(A, Bs[st["i"] % copies], out=D)
+                    st["i"] += 1
+            ours = stats(batch_times(launch, 20, args.rounds))["median_ms"]
+            ref = stats(batch_times(launch_torch, 20, args.rounds))["median_ms"]
+            byt = 2.0 * (m * k + k * n + m * n)
+            print(json.dumps({"workload": "decode_bf16_%dx%dx%d" % (m, n, k), "M": m, "N": n, "K": k,
+                              "plan": pl.describe(), "us": ours * 1e3, "gbs": byt / ours / 1e6,
+                              "pct_hbm": 100 * byt / ours / 1e6 / PEAK_HBM_GBS,
+                              "torch_matmul_us": ref * 1e3}), flush=True)
+        del Bs
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -297,6 +344,9 @@ def main():
         sys.exit(1)
     if args.sweep:
         sweep(args)
+        return
+    if args.decode:
+        decode(args)
         return
     w = gemm_inputs.WORKLOADS[args.workload]
     case = Case(w, rotate=4 if w.name.startswith("skinny") else 1)

@@ -66,6 +66,8 @@ WORKLOADS = {
                  (401, 402, 403)),
         Workload("tail_f16_4000x3000x1000_c", 4000, 3000, 1000, "f16", "uniform", 1.0,
                  (501, 502, 503), has_c=True),
+        # decode: one row, the pages' M = 1, N = K = 4096 case
+        Workload("decode_bf16_1x4096x4096", 1, 4096, 4096, "bf16", "normal", 1.0 / 64.0, (701, 702, 703)),
         # few output tiles, deep K: the K-split regime (entries N(0,1)/sqrt(K))
         Workload("deepk_bf16_512x512x32768", 512, 512, 32768, "bf16", "normal", 1.0 / 181.0193359837562,
                  (601, 602, 603)),
