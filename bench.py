@@ -70,6 +70,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="square_bf16_4096")
     ap.add_argument("--sweep", action="store_true")
+    ap.add_argument("--layouts", action="store_true",
+                    help="time bf16 4096^3 with A and / or B stored transposed")
     ap.add_argument("--decode", action="store_true",
                     help="time the decode regime: M in {1,2,4,8,16,32}, N = K in {4096, 8192}, bf16")
     ap.add_argument("--rounds", type=int, default=30)
@@ -290,6 +292,40 @@ def sweep(args):
     return rows
 
 
+def layouts(args):
+    """bf16 4096^3 with each operand layout (A stored M x K or K x M, B stored
+    K x N or N x K), the planner's plan against torch.matmul on the same views.
+    One JSON line per layout."""
+    import torch
+    import gemm_inputs
+    import dense_tiled_gemm_02_amd as g
+    w = gemm_inputs.WORKLOADS["square_bf16_4096"]
+    A, B, _ = gemm_inputs.make(w)
+    D = torch.empty((w.M, w.N), dtype=torch.bfloat16, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    for ta in (False, True):
+        for tb in (False, True):
+            dA = A.t().contiguous().cuda().t() if ta else A.cuda()
+            dB = B.t().contiguous().cuda().t() if tb else B.cuda()
+            pl = g.plan_for(dA, dB, None, D)
+            ws, wsb = g.workspace_for(pl, torch.cuda.current_device(), stream)
+            run = g.lib().gemm_run
+
+            def launch(c):
+                for _ in range(c):
+                    assert run(pl.handle, dA.data_ptr(), dB.data_ptr(), None, D.data_ptr(), ws, wsb, stream) == 0
+
+            def launch_torch(c):
+                for _ in range(c):
+                    torch.matmul(dA, dB, out=D)
+            ours = stats(batch_times(launch, 10, args.rounds))["median_ms"]
+            ref = stats(batch_times(launch_torch, 10, args.rounds))["median_ms"]
+            print(json.dumps({"workload": w.name, "A": "K x M" if ta else "M x K", "B": "N x K" if tb else "K x N",
+                              "plan": pl.describe(), "us": ours * 1e3, "tflops": w.flops() / ours / 1e9,
+                              "torch_matmul_us": ref * 1e3}), flush=True)
+            del dA, dB
+
+
 def decode(args):
     """The M-bucketed decode regime: for each M, the planner's plan against
     torch.matmul, B rotated over enough copies (> 256 MB) that every launch
@@ -347,6 +383,9 @@ def main():
         return
     if args.decode:
         decode(args)
+        return
+    if args.layouts:
+        layouts(args)
         return
     w = gemm_inputs.WORKLOADS[args.workload]
     case = Case(w, rotate=4 if w.name.startswith("skinny") else 1)

@@ -238,12 +238,20 @@ def gemm_tile_of_workgroup(wg, num_pid_m, num_pid_n, group_m, xcd_count):
 
 # ---------------------------------------------------------------- torch convenience
 
-def problem(M, N, K, dtype, has_c=False, lda=None, ldb=None, ldc=None, ldd=None):
-    """A row-major gemm_problem."""
+def problem(M, N, K, dtype, has_c=False, lda=None, ldb=None, ldc=None, ldd=None, ta=False, tb=False):
+    """A gemm_problem with row-major C, D and, unless ta / tb, row-major A, B.
+    ta: A stored K x M (element (m, k) at m + k * lda); tb: B stored N x K
+    (element (k, n) at k + n * ldb)."""
     p = gemm_problem()
     p.M, p.N, p.K = M, N, K
-    p.sa_m, p.sa_k = (K if lda is None else lda), 1
-    p.sb_k, p.sb_n = (N if ldb is None else ldb), 1
+    if ta:
+        p.sa_m, p.sa_k = 1, (M if lda is None else lda)
+    else:
+        p.sa_m, p.sa_k = (K if lda is None else lda), 1
+    if tb:
+        p.sb_k, p.sb_n = 1, (K if ldb is None else ldb)
+    else:
+        p.sb_k, p.sb_n = (N if ldb is None else ldb), 1
     p.sc_m, p.sc_n = ((N if ldc is None else ldc), 1) if has_c else (0, 0)
     p.sd_m, p.sd_n = (N if ldd is None else ldd), 1
     p.dtype = dtype

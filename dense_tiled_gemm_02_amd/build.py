@@ -4,9 +4,10 @@
 
 Each HIP/C++ source is compiled with hipcc for gfx950 into an object under
 _build/, then linked into dense_tiled_gemm_02_amd/libgemm.so.  Packed fp32
-vector instructions are disabled for device code.  The gfx950 assembly of
-every kernel source is also written to _build/*.s, so the compiler's resource
-report (VGPRs, AGPRs, scratch, LDS, occupancy) can be checked.
+vector instructions are disabled for device code.  With DTG_ASM=1 (or -s) the
+gfx950 assembly of every kernel source is also written to _build/*.s, so the
+compiler's resource report (VGPRs, AGPRs, scratch, LDS, occupancy) can be
+checked.
 """
 import concurrent.futures as cf
 import os
@@ -21,7 +22,8 @@ LIB = os.path.join(PKG, "libgemm.so")
 PROBE_LIB = os.path.join(PKG, "libgemm_probe.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "gemm_tile.hip", "gemm_dma.hip", "gemm_skinny.hip"]
+SOURCES = ["api.cpp", "gemm_tile.hip", "gemm_dma.hip", "gemm_dma_more.hip", "gemm_dma_layouts.hip",
+           "gemm_skinny.hip"]
 PROBE_SOURCES = ["probe.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -43,12 +45,12 @@ def _run(cmd, verbose):
         print(out, flush=True)
 
 
-def _compile(src, verbose):
+def _compile(src, verbose, asm=False):
     path = os.path.join(CSRC, src)
     obj = os.path.join(BUILD, src + ".o")
     lang = ["-x", "hip"] if src.endswith(".hip") else []
     _run([HIPCC] + COMMON + lang + ["-c", path, "-o", obj], verbose)
-    if src.endswith(".hip"):
+    if asm and src.endswith(".hip"):
         asm = os.path.join(BUILD, src + ".s")
         _run([HIPCC] + COMMON + ["-x", "hip", "--cuda-device-only", "-S", path, "-o", asm], verbose)
     return obj
@@ -62,12 +64,15 @@ def _link(objs, out, verbose):
     os.replace(tmp, out)
 
 
-def build(verbose=False, jobs=None):
+def build(verbose=False, jobs=None, asm=None):
     os.makedirs(BUILD, exist_ok=True)
     jobs = jobs or min(8, os.cpu_count() or 1)
-    srcs = SOURCES + PROBE_SOURCES
+    if asm is None:
+        asm = os.environ.get("DTG_ASM", "0") not in ("", "0")
+    # the largest sources first, so they start at once
+    srcs = sorted(SOURCES + PROBE_SOURCES, key=lambda f: -os.path.getsize(os.path.join(CSRC, f)))
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = dict(zip(srcs, ex.map(lambda s: _compile(s, verbose), srcs)))
+        objs = dict(zip(srcs, ex.map(lambda s: _compile(s, verbose, asm), srcs)))
     _link([objs[s] for s in SOURCES], LIB, verbose)
     _link([objs[s] for s in PROBE_SOURCES], PROBE_LIB, verbose)
     return LIB
@@ -77,4 +82,4 @@ if __name__ == "__main__":
     j = None
     if "-j" in sys.argv:
         j = int(sys.argv[sys.argv.index("-j") + 1])
-    print(build(verbose="-v" in sys.argv, jobs=j))
+    print(build(verbose="-v" in sys.argv, jobs=j, asm=True if "-s" in sys.argv else None))

@@ -86,9 +86,9 @@ gemm_status validate(const gemm_problem* p) {
         const int64_t rows = (i == 0) ? p->M : (i == 1) ? p->K : p->M;
         const int64_t cols = (i == 0) ? p->K : p->N;
         if (rows == 0 || cols == 0) continue;
-        if (cs[i] != 1 && cols > 1)
+        if (i >= 2 && cs[i] != 1 && cols > 1)
             return fail(GEMM_ERR_UNSUPPORTED,
-                        "%s column stride %lld: only row-major operands (column stride 1) are supported",
+                        "%s column stride %lld: C and D must be row-major (column stride 1)",
                         nm[i], (long long)cs[i]);
         if (i == 3 && rows > 1 && rs[i] < cols)
             return fail(GEMM_ERR_INVALID_ARG, "D row stride %lld < N=%lld makes output rows overlap",
@@ -99,16 +99,41 @@ gemm_status validate(const gemm_problem* p) {
     return ok();
 }
 
+// How A and B sit in memory: 0 (both row-major), dtg::kLayTA (A stored
+// K x M: unit m stride), dtg::kLayTB (B stored N x K: unit k stride), both, or
+// -1 (any other strides: element-wise path only).  A single row or column
+// counts as row-major.
+int layout_of(const gemm_problem* p) {
+    const bool a_rm = p->K <= 1 || p->sa_k == 1;
+    const bool a_cm = !a_rm && (p->M <= 1 || p->sa_m == 1);
+    const bool b_rm = p->N <= 1 || p->sb_n == 1;
+    const bool b_cm = !b_rm && (p->K <= 1 || p->sb_k == 1);
+    if ((!a_rm && !a_cm) || (!b_rm && !b_cm)) return -1;
+    return (a_cm ? dtg::kLayTA : 0) | (b_cm ? dtg::kLayTB : 0);
+}
+
+// The 16-byte vector paths move 8 elements along each operand's contiguous
+// index: that index's extent and the other stride must be multiples of 8.
 bool vec_shape_ok(const gemm_problem* p) {
-    return p->K % 8 == 0 && p->N % 8 == 0 && p->sa_m % 8 == 0 && p->sb_k % 8 == 0;
+    const int lay = layout_of(p);
+    if (lay < 0) return false;
+    const bool a_ok = (lay & dtg::kLayTA) ? (p->M % 8 == 0 && p->sa_k % 8 == 0)
+                                          : (p->K % 8 == 0 && p->sa_m % 8 == 0);
+    const bool b_ok = (lay & dtg::kLayTB) ? (p->K % 8 == 0 && p->sb_n % 8 == 0)
+                                          : (p->N % 8 == 0 && p->sb_k % 8 == 0);
+    return a_ok && b_ok;
 }
 
 // The direct-to-LDS kernels address one BM-row panel of A and one BK-row slab
 // of B with 32-bit byte offsets from descriptors rebased every K step.
 bool dma_offsets_ok(const gemm_problem* p, const dtg::KernelEntry* e) {
     const int64_t lim = (int64_t(1) << 31) - 4096;
-    return static_cast<int64_t>(e->bm) * p->sa_m * 2 + e->bk * 2 < lim &&
-           static_cast<int64_t>(e->bk) * p->sb_k * 2 + e->bn * 2 < lim;
+    const bool ta = e->layout > 0 && (e->layout & dtg::kLayTA), tb = e->layout > 0 && (e->layout & dtg::kLayTB);
+    const int64_t a = ta ? static_cast<int64_t>(e->bk) * p->sa_k * 2 + e->bm * 2
+                         : static_cast<int64_t>(e->bm) * p->sa_m * 2 + e->bk * 2;
+    const int64_t b = tb ? static_cast<int64_t>(e->bn) * p->sb_n * 2 + e->bk * 2
+                         : static_cast<int64_t>(e->bk) * p->sb_k * 2 + e->bn * 2;
+    return a < lim && b < lim;
 }
 
 std::vector<const dtg::KernelEntry*> all_entries() {
@@ -131,11 +156,14 @@ bool matches(const dtg::KernelEntry* e, const gemm_config& f) {
            (f.splitk <= 1 || e->splitk == 0 || f.splitk <= e->splitk);   // e->splitk: most slices, 0 = any
 }
 
-// The first compiled variant that fits the device and matches `want`.
+// The first compiled variant that fits the device and the problem's layout
+// and matches `want`.
 const dtg::KernelEntry* find_entry(const gemm_config& want, int dtype, int vec,
                                    const gemm_device_info& dev, const gemm_problem* p) {
+    const int lay = layout_of(p);
     for (const dtg::KernelEntry* e : all_entries()) {
         if (e->dtype != dtype || e->vec != vec) continue;
+        if (e->layout != -1 && e->layout != lay) continue;
         if (e->lds_bytes > dev.lds_per_wg) continue;
         if (e->family == dtg::KF_DMA && !dma_offsets_ok(p, e)) continue;
         if (matches(e, want)) return e;
@@ -171,7 +199,7 @@ const std::vector<TunedKey>& tuned_table() {
 gemm_config heuristic(const gemm_problem* p, const gemm_device_info& dev, int* group_m, bool allow_ws) {
     const int64_t M = p->M, N = p->N, K = p->K;
     *group_m = 8;
-    if (M <= 32) {
+    if (M <= 32 && layout_of(p) == 0) {
         // Decode regime, bucketed by M: 16-row slabs for M <= 16, 32-row slabs
         // (two MFMA row blocks) for M <= 32.  Stream B.  Each workgroup reads
         // a 256-byte band of every row of its K slice (HBM needs >= 128-byte
@@ -271,6 +299,12 @@ gemm_status plan_impl(const gemm_problem* prob, const gemm_device_info* dev, con
     }
     const dtg::KernelEntry* fb =
         find_entry(cfg_of(dtg::KF_TILE, 0, 0, 0, 0, 16, 0, 0), prob->dtype, 0, *dev, prob);
+    const bool unforced = !force || (!force->kernel && !force->bm && !force->bn && !force->bk && !force->mfma &&
+                                     !force->waves_m && !force->waves_n && !force->stages && !force->splitk);
+    if (!e && vec && unforced && !tuned && layout_of(prob) != 0) {
+        // no vector variant for this layout and tile: the element-wise path
+        e = fb;
+    }
     if (!e) {
         if (!vec && (!force || want.kernel == 0 || want.kernel == dtg::KF_TILE)) {
             // element-wise path: any shape, any alignment (16x16x32 instruction)
@@ -349,10 +383,10 @@ gemm_status device_info_cached(int device, gemm_device_info* info) {
     return st;
 }
 
-// byte range [lo, hi) a row-major rows x cols matrix occupies
-void span(const void* p, int64_t rows, int64_t cols, int64_t ld, uintptr_t* lo, uintptr_t* hi) {
+// byte range [lo, hi) of a rows x cols matrix with strides (rs, cs)
+void span(const void* p, int64_t rows, int64_t cols, int64_t rs, int64_t cs, uintptr_t* lo, uintptr_t* hi) {
     *lo = reinterpret_cast<uintptr_t>(p);
-    *hi = *lo + static_cast<uintptr_t>(((rows - 1) * ld + cols) * 2);
+    *hi = *lo + static_cast<uintptr_t>(((rows - 1) * rs + (cols - 1) * cs + 1) * 2);
 }
 
 bool overlaps(uintptr_t a0, uintptr_t a1, uintptr_t b0, uintptr_t b1) { return a0 < b1 && b0 < a1; }
@@ -451,10 +485,10 @@ gemm_status gemm_plan_describe(const gemm_plan* plan, char* buf, size_t len) {
     const gemm_config& c = plan->cfg;
     snprintf(buf, len,
              "kernel=%s bm=%d bn=%d bk=%d stages=%d mfma=%d waves=%dx%d group_m=%d splitk=%d xcd_remap=%d "
-             "grid=%lld threads=%d lds=%lld vec=%d",
+             "grid=%lld threads=%d lds=%lld vec=%d layout=%d",
              plan->entry->name, c.bm, c.bn, c.bk, c.stages, c.mfma, c.waves_m, c.waves_n, c.group_m,
              c.splitk, c.xcd_remap, (long long)plan->grid, plan->entry->threads,
-             (long long)plan->entry->lds_bytes, plan->entry->vec);
+             (long long)plan->entry->lds_bytes, plan->entry->vec, layout_of(&plan->prob));
     return ok();
 }
 
@@ -485,17 +519,17 @@ gemm_status gemm_run(const gemm_plan* plan, const void* A, const void* B, const 
     if (!D) return fail(GEMM_ERR_INVALID_ARG, "D is NULL");
     if (p.K > 0 && (!A || !B)) return fail(GEMM_ERR_INVALID_ARG, "A or B is NULL");
     uintptr_t d0, d1;
-    span(D, p.M, p.N, p.sd_m, &d0, &d1);
+    span(D, p.M, p.N, p.sd_m, p.sd_n, &d0, &d1);
     if (p.K > 0) {
         uintptr_t a0, a1, b0, b1;
-        span(A, p.M, p.K, p.sa_m, &a0, &a1);
-        span(B, p.K, p.N, p.sb_k, &b0, &b1);
+        span(A, p.M, p.K, p.sa_m, p.sa_k, &a0, &a1);
+        span(B, p.K, p.N, p.sb_k, p.sb_n, &b0, &b1);
         if (overlaps(d0, d1, a0, a1)) return fail(GEMM_ERR_INVALID_ARG, "D overlaps A");
         if (overlaps(d0, d1, b0, b1)) return fail(GEMM_ERR_INVALID_ARG, "D overlaps B");
     }
     if (p.has_c) {
         uintptr_t c0, c1;
-        span(C, p.M, p.N, p.sc_m, &c0, &c1);
+        span(C, p.M, p.N, p.sc_m, p.sc_n, &c0, &c1);
         const bool same = (C == D) && (p.sc_m == p.sd_m || p.M == 1);
         if (!same && overlaps(d0, d1, c0, c1))
             return fail(GEMM_ERR_INVALID_ARG, "D overlaps C (only D == C with equal strides is allowed)");
@@ -527,6 +561,8 @@ gemm_status gemm_run(const gemm_plan* plan, const void* A, const void* B, const 
     a.ldb = p.sb_k;
     a.ldc = p.has_c ? p.sc_m : 0;
     a.ldd = p.sd_m;
+    a.sak = p.sa_k;
+    a.sbn = p.sb_n;
     a.splits = (e == plan->entry && (e->family == dtg::KF_SKINNY || e->family == dtg::KF_DMA))
                    ? plan->cfg.splitk
                    : 1;   // the element-wise fallback runs the whole K range per tile

@@ -1,541 +1,27 @@
-// Tiled GEMM kernel for gfx950 with direct global -> LDS staging:  D = A x B (+ C).
-//
-// Same tile walk as gemm_tile.hip (K loop over BM x BN x BK slabs, grouped
-// tile order, masked tails, fp32 accumulation, fp32 -> storage rounding in the
-// epilogue), with the staging done the gfx950 way:
-//  * global -> LDS without registers: buffer_load_dwordx4 ... lds writes each
-//    lane's 16 bytes at LDS byte 16 * lane past a wave-uniform base, so one
-//    wave instruction fills 1024 contiguous LDS bytes.  The LDS layout is
-//    chosen by which global chunk each lane fetches (an XOR swizzle of 16-byte
-//    chunks, for conflict-free operand reads).  Lanes outside the matrix (rows
-//    >= M, columns >= N, k >= K) get an offset past the buffer descriptor's
-//    range, which makes the hardware write zeros ("Hopper Support in Triton",
-//    slides 15-16: masked loads with other = 0);
-//  * an LDS ring of ST stages: the loads of K step k + ST - 1 are issued while
-//    step k is contracted, one barrier per step (FlagGems "Hygon
-//    optimization", section "Software pipelining"; "DCU K100 节点初探",
-//    section 5.6, double buffering);
-//  * A is stored as rows of BK contiguous k and read with one 16-byte LDS read
-//    per lane per fragment; B is stored as it is in memory (rows of BN
-//    contiguous n) and read with the transposing 64-bit LDS read, which hands
-//    each lane 4 consecutive k of one column: two reads make the 8 k of one
-//    MFMA operand.
-// Descriptors are rebased at every K step (scalar work only), so 32-bit
-// buffer offsets cover any matrix whose BM rows of A and BK rows of B span
-// less than 2 GiB.
+// Variants of the direct-to-LDS GEMM kernel (gemm_dma_kernel.h): the
+// planner's ladder tiles and the wide-tile experiments, row-major operands;
+// the table the planner sees joins the three variant files.
+#include <vector>
 
-#include <hip/hip_runtime.h>
-#include <stdint.h>
-
-#include <type_traits>
-
-#include "device_common.h"
-#include "kernels.h"
-#include "tile_order.h"
+#include "gemm_dma_kernel.h"
 
 namespace dtg {
 namespace {
 
-using namespace dev;
-
-// Swizzle of the B tile (rows of BN contiguous n, CHB 16-byte chunks per row):
-// physical chunk = logical chunk ^ bsw(r).  Even values keep the two chunks a
-// 16-lane group reads from one row adjacent; the 4 (or 8) rows one transposing
-// read touches land in distinct bank groups.
-template <int CHB>
-__device__ __forceinline__ int bsw(int r) {
-    if constexpr (CHB >= 16) return 2 * ((r & 3) | (((r >> 3) & 1) << 2));
-    else return 2 * (r & 3);
-}
-
-template <int BM, int BN, int BK, int WM, int WN, int MF, int ST, bool BF16>
-__global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(KArgs p) {
-    constexpr int NW = WM * WN;
-    constexpr int TM = BM / WM, TN = BN / WN;
-    constexpr int FM = TM / MF, FN = TN / MF;
-    constexpr int KI = (MF == 16) ? 32 : 16;
-    constexpr int CHA = BK / 8;                 // 16-byte chunks per A row
-    constexpr int RA = 64 / CHA;                // A rows per wave instruction
-    constexpr int IA_W = BM / RA / NW;          // A instructions per wave per stage
-    constexpr int CHB = BN / 8;                 // 16-byte chunks per B row
-    constexpr int RB = 64 / CHB;                // B rows per wave instruction
-    constexpr int IB_W = BK / RB / NW;
-    constexpr int SA = BM * BK, SB = BK * BN;   // elements per stage
-    constexpr int L = IA_W + IB_W;              // loads per wave per stage
-    constexpr int NKS = BK / KI;                // instruction k sub-steps per K step
-    static_assert(BM % (WM * MF) == 0 && BN % (WN * MF) == 0, "tile vs wave grid");
-    static_assert(BK % KI == 0 && (CHA == 4 || CHA == 8 || CHA == 16), "BK");
-    static_assert(CHB >= 8 && CHB <= 64 && 64 % CHB == 0, "BN");
-    static_assert((BM / RA) % NW == 0 && (BK / RB) % NW == 0 && IA_W > 0 && IB_W > 0, "load split");
-    static_assert(ST >= 2 && ST <= 5 && (ST - 1) * L < 64, "stages");
-    typedef typename AccT<MF>::type acc_t;
-
-    __shared__ __attribute__((aligned(1024))) uint16_t smem[ST * (SA + SB)];
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave / WN, wn = wave % WN;
-
-    // Workgroup -> (K slice, output tile): the XCD permutation runs over the
-    // whole grid, consecutive positions are consecutive tiles (grouped order)
-    // of one slice.  With one slice this is tile_of_workgroup.
-    const int ntiles = p.num_pid_m * p.num_pid_n;
-    const int NS = p.splits;
-    int pid_m, pid_n, tile_lin, slice;
-    {
-        const int pos = xcd_permute<int>(blockIdx.x, ntiles * NS, p.xcds);
-        slice = pos / ntiles;
-        tile_lin = pos - slice * ntiles;
-        grouped_tile<int>(tile_lin, p.num_pid_m, p.num_pid_n, p.group_m, &pid_m, &pid_n);
-    }
-    const int m0 = pid_m * BM, n0 = pid_n * BN;
-    const int M = p.M, N = p.N, K = p.K;
-    const bool edge = (m0 + BM > M) || (n0 + BN > N);
-
-    // ---- per-lane load offsets (bytes, relative to the rebased descriptors).
-    // Load X of the A tile fills rows X*NW*RA + wave*RA + lane/CHA, load Y of
-    // the B tile k rows Y*NW*RB + wave*RB + lane/CHB.  When NW*RA (NW*RB) is a
-    // multiple of the swizzle's period, every load of a wave has the same
-    // chunk permutation: one voffset serves them all and the row step goes
-    // into the scalar offset.  Otherwise each load keeps its own voffset.
-    constexpr bool PA = (NW * RA) % 16 == 0;
-    constexpr bool PB = (NW * RB) % ((CHB >= 16) ? 16 : 4) == 0;
-    constexpr int NVA = PA ? 1 : IA_W, NVB = PB ? 1 : IB_W;
-    const int a_row0 = wave * RA + lane / CHA;
-    const int b_row0 = wave * RB + lane / CHB;
-    uint32_t a_voff[NVA], b_voff[NVB];
-    int a_kc[NVA], b_c8[NVB];
-#pragma unroll
-    for (int i = 0; i < NVA; ++i) {
-        const int row = a_row0 + i * NW * RA;
-        const int c = (lane % CHA) ^ swz<CHA>(row);
-        a_voff[i] = static_cast<uint32_t>(static_cast<int64_t>(row) * p.lda * 2 + c * 16);
-        a_kc[i] = 8 * c;
-    }
-#pragma unroll
-    for (int i = 0; i < NVB; ++i) {
-        const int row = b_row0 + i * NW * RB;
-        const int c = (lane % CHB) ^ bsw<CHB>(row);
-        b_voff[i] = static_cast<uint32_t>(static_cast<int64_t>(row) * p.ldb * 2 + c * 16);
-        b_c8[i] = 8 * c;
-    }
-    const uint32_t a_step = static_cast<uint32_t>(NW * RA) * static_cast<uint32_t>(p.lda) * 2u;
-    const uint32_t b_step = static_cast<uint32_t>(NW * RB) * static_cast<uint32_t>(p.ldb) * 2u;
-
-    // LDS layout: the ST stages of A, then the ST stages of B.
-    const uint32_t smem0 = lds_addr(smem);
-
-    // Buffer descriptors of K step kt: A rows m0.. and B rows k0.. from column
-    // k0 (A) / n0 (B); the ranges end at the matrices' last element, so any
-    // offset past them reads zeros.
-    struct Desc {
-        __amdgpu_buffer_rsrc_t ra, rb;
-        int k0;
-        bool chk;    // edge tile or K tail: lanes test their own bounds
-    };
-    const int nfull = K / BK;
-    // this slice's K steps: [kt0, kt1)
-    const int nkt_all = (K + BK - 1) / BK;
-    const int per_slice = (nkt_all + NS - 1) / NS;
-    const int kt0 = slice * per_slice;
-    const int kt1 = (kt0 + per_slice < nkt_all) ? kt0 + per_slice : nkt_all;
-    auto make_desc = [&](int kt) {
-        Desc d;
-        d.k0 = kt * BK;
-        const bool live = kt < kt1;   // steps past the slice (issued only to keep the ring uniform) read nothing
-        const uint16_t* abase = p.A + static_cast<int64_t>(m0) * p.lda + (live ? d.k0 : 0);
-        d.ra = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<uint16_t*>(abase), 0,
-            live ? clamp_records((static_cast<int64_t>(M - 1 - m0) * p.lda + (K - d.k0)) * 2) : 0u, kRsrcWord3);
-        const uint16_t* bbase = p.B + (live ? static_cast<int64_t>(d.k0) * p.ldb : 0) + n0;
-        d.rb = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<uint16_t*>(bbase), 0,
-            live ? clamp_records((static_cast<int64_t>(K - 1 - d.k0) * p.ldb + (N - n0)) * 2) : 0u, kRsrcWord3);
-        d.chk = edge || kt >= nfull;
-        return d;
-    };
-    // Load number X (A loads first, then B) of a K step into LDS stage s.
-    auto load_op = [&](auto x_tag, const Desc& d, int s) {
-        constexpr int X = decltype(x_tag)::value;
-        if constexpr (X < IA_W) {
-            constexpr int V = PA ? 0 : X;
-            uint32_t v = a_voff[V];
-            const uint32_t so = PA ? X * a_step : 0u;
-            if (d.chk) v = (m0 + a_row0 + X * NW * RA < M && d.k0 + a_kc[V] < K) ? v : kOOB;
-            // (a non-const local: clang's host pass drops the kernel when the
-            // builtin is handed a member of a const reference)
-            __amdgpu_buffer_rsrc_t r = d.ra;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(smem + s * SA + (X * NW + wave) * 512), 16, v,
-                                                    so, 0, 0);
-        } else {
-            constexpr int Y = X - IA_W;
-            constexpr int V = PB ? 0 : Y;
-            uint32_t v = b_voff[V];
-            const uint32_t so = PB ? Y * b_step : 0u;
-            if (d.chk) v = (n0 + b_c8[V] < N && d.k0 + b_row0 + Y * NW * RB < K) ? v : kOOB;
-            __amdgpu_buffer_rsrc_t r = d.rb;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                r, (lds_void_t*)(smem + ST * SA + s * SB + (Y * NW + wave) * 512), 16, v, so, 0, 0);
-        }
-    };
-    auto issue_tile = [&](int kt, int s) {
-        const Desc d = make_desc(kt);
-        static_for<L>([&](auto x_tag) { load_op(x_tag, d, s); });
-    };
-
-    acc_t acc[FM][FN];
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-            for (int r = 0; r < AccT<MF>::regs; ++r) acc[i][j][r] = 0.0f;
-
-    // ---- per-lane operand read addresses (LDS bytes)
-    //  A fragment (i, ks): row wm*TM + i*MF + lane % MF, chunk ks*KI/8 + lane / MF
-    //  (XOR-swizzled); i*MF*BK*2 goes into the instruction's offset field.
-    //  B fragment (j, ks), half hh: the transposing read of k rows
-    //  ks*KI + 8 g + 4 hh + (jq >> 2) and 4 columns starting at
-    //  nb + 4 (jq & 3); (ks*KI + 4 hh) * BN * 2 goes into the offset field.
-    //  The stage offset goes there too when the 16-bit field can hold it
-    //  (AI / BI), else each stage keeps its own addresses.
-    constexpr bool AI = (ST - 1) * SA * 2 + (FM - 1) * MF * BK * 2 < 65536;
-    constexpr bool BI = (ST - 1) * SB * 2 + (BK - 4) * BN * 2 < 65536;
-    constexpr int NAS = AI ? 1 : ST, NBS = BI ? 1 : ST;
-    uint32_t a_addr[NAS][NKS], b_addr[NBS][FN];
-    {
-        const int a_row = wm * TM + lane % MF;
-        const int a_kc0 = lane / MF;
-        const int a_sw = swz<CHA>(lane % MF);
-        int jq, g, col;
-        if constexpr (MF == 16) { jq = lane & 15; g = lane >> 4; col = 0; }
-        else { jq = lane & 15; g = lane >> 5; col = 16 * ((lane >> 4) & 1); }
-        const int b_sw = (CHB >= 16) ? 2 * ((jq >> 2) | ((g & 1) << 2)) : 2 * (jq >> 2);
-        const int b_row = 8 * g + (jq >> 2);
-#pragma unroll
-        for (int st = 0; st < NAS; ++st) {
-            const uint32_t sa = smem0 + st * SA * 2;
-#pragma unroll
-            for (int ks = 0; ks < NKS; ++ks)
-                a_addr[st][ks] = sa + (a_row * BK + (((ks * (KI / 8) + a_kc0) ^ a_sw) * 8)) * 2;
-        }
-#pragma unroll
-        for (int st = 0; st < NBS; ++st) {
-            const uint32_t sb = smem0 + (ST * SA + st * SB) * 2;
-#pragma unroll
-            for (int j = 0; j < FN; ++j) {
-                const int nb = wn * TN + j * MF + col;
-                b_addr[st][j] = sb + (b_row * BN + (((nb >> 3) ^ b_sw) << 3) + 4 * (jq & 3)) * 2;
-            }
-        }
-    }
-
-    // Fragments, double-buffered across k sub-steps: A as one 16-byte read per
-    // fragment, B as two transposing reads (k 0..3 and 4..7 of the operand).
-    u32x4 fa[2][FM], fb[2][FN];
-    i16x4 hb[2][FN][2];               // B halves until their wait
-    constexpr int NR = 2 * FN + FM;   // LDS reads per sub-step
-
-    // LDS read number R of sub-step KS of stage S into slot SL: the B halves
-    // first, then the A fragments.
-    auto read_op = [&](auto stage_tag, auto ks_tag, auto slot_tag, auto r_tag) {
-        constexpr int S = decltype(stage_tag)::value;
-        constexpr int KS = decltype(ks_tag)::value;
-        constexpr int SL = decltype(slot_tag)::value;
-        constexpr int R = decltype(r_tag)::value;
-        if constexpr (R < 2 * FN) {
-            constexpr int J = R / 2, H = R % 2;
-            hb[SL][J][H] = lds_read_tr<(BI ? S * SB * 2 : 0) + (KS * KI + 4 * H) * BN * 2>(b_addr[BI ? 0 : S][J]);
-            if constexpr (H == 1)
-                fb[SL][J] = __builtin_bit_cast(u32x4, __builtin_shufflevector(hb[SL][J][0], hb[SL][J][1],
-                                                                              0, 1, 2, 3, 4, 5, 6, 7));
-        } else {
-            constexpr int I = R - 2 * FN;
-            fa[SL][I] = lds_read16<(AI ? S * SA * 2 : 0) + I * MF * BK * 2>(a_addr[AI ? 0 : S][KS]);
-        }
-    };
-    auto wait_frags = [&](auto slot_tag) {
-        constexpr int SL = decltype(slot_tag)::value;
-        lds_wait_all();
-#pragma unroll
-        for (int j = 0; j < FN; ++j) tie(fb[SL][j]);
-#pragma unroll
-        for (int i = 0; i < FM; ++i) tie(fa[SL][i]);
-    };
-    // MFMA number Q (row-fragment major) of a sub-step, operands in slot SL.
-    // The B fragment goes in as the instruction's first operand and the A
-    // fragment as its second, so each accumulator holds the transposed block:
-    // a lane's registers are consecutive columns of one row of D, stored as
-    // 8-byte vectors in the epilogue.
-    auto mfma_op = [&](auto slot_tag, auto q_tag) {
-        constexpr int SL = decltype(slot_tag)::value;
-        constexpr int Q = decltype(q_tag)::value;
-        constexpr int I = Q / FN, J = Q % FN;
-        acc[I][J] = mfma<MF, BF16>(fb[SL][J], fa[SL][I], acc[I][J]);
-    };
-    constexpr int NQ = FM * FN;       // MFMAs per sub-step
-
-    // The MFMAs of a sub-step with NOPS memory operations spread between them:
-    // operation o follows MFMA number o * SP; the last TAIL MFMAs carry none,
-    // so the LDS reads have landed when the sub-step ends.  Every pair is
-    // fenced, so the compiler keeps exactly this order.
-    auto interleave = [&](auto slot_tag, auto nops_tag, auto&& op) {
-        constexpr int SL = decltype(slot_tag)::value;
-        constexpr int NOPS = decltype(nops_tag)::value;
-        constexpr int TAIL = NQ / 4;
-        constexpr int SP = (NOPS == 0) ? 1 : ((NQ - TAIL) / NOPS > 0 ? (NQ - TAIL) / NOPS : 1);
-        static_for<NQ>([&](auto q_tag) {
-            constexpr int Q = decltype(q_tag)::value;
-            mfma_op(std::integral_constant<int, SL>{}, q_tag);
-            if constexpr (Q % SP == 0 && Q / SP < NOPS) op(std::integral_constant<int, Q / SP>{});
-            __builtin_amdgcn_sched_barrier(0);
-        });
-        // ops left over when there are more operations than MFMA slots
-        if constexpr (NOPS > NQ / SP) {
-            static_for<NOPS - NQ / SP>([&](auto o_tag) {
-                op(std::integral_constant<int, NQ / SP + decltype(o_tag)::value>{});
-            });
-        }
-    };
-
-    const int nkt = kt1 > kt0 ? kt1 - kt0 : 0;   // K steps of this slice
-
-    // One K step (tile kt) on LDS stage S = kt % ST; U is kt's position in the
-    // unrolled loop, which fixes which fragment slot holds which sub-step.  On
-    // entry the fragments of sub-step 0 are in slot (U * NKS) % 2.  Sub-step
-    // ks runs its MFMAs with the reads of sub-step ks + 1 between them.  The
-    // last sub-step first waits for tile kt + 1 (tiles up to kt + ST - 1 have
-    // been issued, so ST - 2 tiles may stay in flight), passes the barrier
-    // (after it every wave has read all of tile kt, so its stage may be
-    // refilled), and runs its MFMAs with the reads of tile kt + 1's first
-    // sub-step and the loads of tile kt + ST into this stage between them.
-    // Every step does the same: tiles past the end of K are loaded from an
-    // empty range (zeros, no memory access) and read but never used.
-    auto step = [&](auto u_tag, int kt) {
-        constexpr int U = decltype(u_tag)::value;
-        constexpr int S = U % ST;
-        constexpr int S1 = (S + 1) % ST;
-        static_for<NKS>([&](auto ks_tag) {
-            constexpr int KS = decltype(ks_tag)::value;
-            constexpr int CUR = (U * NKS + KS) & 1, NXT = CUR ^ 1;
-            const auto cur = std::integral_constant<int, CUR>{};
-            const auto nxt = std::integral_constant<int, NXT>{};
-            if constexpr (KS + 1 < NKS) {
-                interleave(cur, std::integral_constant<int, NR>{}, [&](auto o_tag) {
-                    read_op(std::integral_constant<int, S>{}, std::integral_constant<int, KS + 1>{}, nxt, o_tag);
-                });
-            } else {
-                const Desc d = make_desc(kt + ST);
-                wait_vm<(ST - 2) * L>();
-                __builtin_amdgcn_s_barrier();
-                interleave(cur, std::integral_constant<int, NR + L>{}, [&](auto o_tag) {
-                    constexpr int O = decltype(o_tag)::value;
-                    if constexpr (O < NR)
-                        read_op(std::integral_constant<int, S1>{}, std::integral_constant<int, 0>{}, nxt, o_tag);
-                    else
-                        load_op(std::integral_constant<int, O - NR>{}, d, S);
-                });
-            }
-            wait_frags(nxt);
-        });
-    };
-
-    // unroll so that both the stage and the fragment-slot parity repeat
-    constexpr int UNROLL = ((ST * NKS) % 2 == 0) ? ST : 2 * ST;
-    if (nkt > 0) {
-        static_for<ST>([&](auto t_tag) { issue_tile(kt0 + decltype(t_tag)::value, decltype(t_tag)::value); });
-        wait_vm<(ST - 1) * L>();
-        __builtin_amdgcn_s_barrier();
-        static_for<NR>([&](auto r_tag) {
-            read_op(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{},
-                    std::integral_constant<int, 0>{}, r_tag);
-        });
-        wait_frags(std::integral_constant<int, 0>{});
-        for (int j = 0; j < nkt; j += UNROLL) {
-            static_for<UNROLL>([&](auto u_tag) {
-                if (j + decltype(u_tag)::value < nkt) step(u_tag, kt0 + j + decltype(u_tag)::value);
-            });
-        }
-        // no load may still be writing this workgroup's LDS when it exits
-        wait_vm<0>();
-    }
-
-    // ---- K slices across workgroups: publish this slice's fp32 partial tile;
-    // the workgroup that arrives last at the tile's counter sums the slices
-    // in slice order (so the result does not depend on arrival order) into
-    // acc and goes on to the epilogue below; the others are done.  Partials
-    // are kept in register order, [tile][slice][wave][block][lane][4 floats],
-    // so each lane writes and reads back only its own 16-byte runs, with
-    // system-scope accesses (they bypass the per-XCD L2 caches).
-    constexpr int NB = FM * FN * (AccT<MF>::regs / 4);   // 16-byte runs per lane
-    // (two slices of partials are held in registers: only tiles of at most
-    // 64 accumulators per lane take K slices; the planner keeps the others at 1)
-    if constexpr (NB <= 16) if (NS > 1) {
-        constexpr int64_t WAVE_F = static_cast<int64_t>(NB) * 64 * 4;   // floats per wave per slice
-        int* counters = static_cast<int*>(p.ws);
-        float* tile_part = reinterpret_cast<float*>(static_cast<char*>(p.ws) + kCounterBytes) +
-                           static_cast<int64_t>(tile_lin) * NS * NW * WAVE_F;
-        const __amdgpu_buffer_rsrc_t pr = __builtin_amdgcn_make_buffer_rsrc(
-            tile_part, 0, clamp_records(static_cast<int64_t>(NS) * NW * WAVE_F * 4), kRsrcWord3);
-        auto run_off = [&](int sl, int b) {   // byte offset of lane's run b of slice sl
-            return static_cast<uint32_t>(((static_cast<int64_t>(sl) * NW + wave) * WAVE_F + (b * 64 + lane) * 4) * 4);
-        };
-        // run b = (i * FN + j) * G + g holds registers 4g..4g+3 of acc[i][j]
-        constexpr int G = AccT<MF>::regs / 4;
-        auto get_run = [&](auto b_tag) {
-            constexpr int B = decltype(b_tag)::value;
-            constexpr int I = B / G / FN, J = (B / G) % FN, Q = B % G;
-            f32x4 v;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) v[r] = acc[I][J][4 * Q + r];
-            return v;
-        };
-        auto set_run = [&](auto b_tag, const f32x4& v) {
-            constexpr int B = decltype(b_tag)::value;
-            constexpr int I = B / G / FN, J = (B / G) % FN, Q = B % G;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) acc[I][J][4 * Q + r] = v[r];
-        };
-        static_for<NB>([&](auto b_tag) {
-            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, get_run(b_tag)), pr,
-                                                   run_off(slice, decltype(b_tag)::value), 0, kSysScope);
-        });
-        wait_vm<0>();
-        __syncthreads();
-        int* last = reinterpret_cast<int*>(smem);
-        if (tid == 0)
-            *last = __hip_atomic_fetch_add(&counters[tile_lin], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) ==
-                    NS - 1;
-        __syncthreads();
-        if (!*last) return;
-        // Sum the slices in order into acc (this slice's own runs are read back
-        // like the others: the same bits).  Loads go in units of HB runs, the
-        // next unit in flight while one is added: two units of registers.
-        constexpr int HB = (NB <= 8) ? NB : NB / 2;
-        constexpr int UPS = NB / HB;                  // units per slice
-        f32x4 buf[2][HB];
-        auto fetch = [&](int u, int bb) {
-            const int sl = u / UPS, b0 = (u % UPS) * HB;
-#pragma unroll
-            for (int b = 0; b < HB; ++b)
-                buf[bb][b] = __builtin_bit_cast(
-                    f32x4, __builtin_amdgcn_raw_buffer_load_b128(pr, run_off(sl, b0 + b), 0, kSysScope));
-        };
-        auto add = [&](int u, int bb) {
-            static_for<UPS>([&](auto h_tag) {
-                constexpr int H = decltype(h_tag)::value;
-                if (u % UPS == H) {
-                    static_for<HB>([&](auto b_tag) {
-                        constexpr int B = H * HB + decltype(b_tag)::value;
-                        const f32x4 cur = (u < UPS) ? f32x4{0.0f, 0.0f, 0.0f, 0.0f}
-                                                    : get_run(std::integral_constant<int, B>{});
-                        set_run(std::integral_constant<int, B>{}, cur + buf[bb][decltype(b_tag)::value]);
-                    });
-                }
-            });
-        };
-        const int nu = NS * UPS;
-        fetch(0, 0);
-        for (int u = 0; u < nu; u += 2) {
-            if (u + 1 < nu) fetch(u + 1, 1);
-            add(u, 0);
-            if (u + 1 < nu) {
-                if (u + 2 < nu) fetch(u + 2, 0);
-                add(u + 1, 1);
-            }
-        }
-        if (tid == 0) __hip_atomic_store(&counters[tile_lin], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-    }
-
-    // ---- epilogue: + C in fp32, round, masked store.  Lane l holds, per
-    // block (i, j), row l % MF of the block and G runs of 4 consecutive
-    // columns (16x16x32: columns 4 (l / 16) + 0..3; 32x32x16: run q at
-    // columns 8 q + 4 (l / 32) + 0..3).
-    constexpr int G = AccT<MF>::regs / 4;
-    const bool has_c = p.has_c != 0;
-    const bool dvec = (p.ldd % 4 == 0) && (reinterpret_cast<uintptr_t>(p.D) % 8 == 0);
-    const bool cvec = !has_c || ((p.ldc % 4 == 0) && (reinterpret_cast<uintptr_t>(p.C) % 8 == 0));
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-        const int row = m0 + wm * TM + i * MF + (lane % MF);
-        if (row >= M) continue;
-        const int64_t drow = static_cast<int64_t>(row) * p.ldd;
-        const int64_t crow = static_cast<int64_t>(row) * p.ldc;
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-#pragma unroll
-            for (int q = 0; q < G; ++q) {
-                const int col = n0 + wn * TN + j * MF + 8 * q + 4 * (lane / MF);
-                float v[4];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) v[r] = acc[i][j][4 * q + r];
-                if (dvec && cvec && col + 4 <= N) {
-                    if (has_c) {
-                        const uint2 cv = *reinterpret_cast<const uint2*>(p.C + crow + col);
-                        v[0] += widen<BF16>(static_cast<uint16_t>(cv.x & 0xffffu));
-                        v[1] += widen<BF16>(static_cast<uint16_t>(cv.x >> 16));
-                        v[2] += widen<BF16>(static_cast<uint16_t>(cv.y & 0xffffu));
-                        v[3] += widen<BF16>(static_cast<uint16_t>(cv.y >> 16));
-                    }
-                    uint2 dv;
-                    dv.x = static_cast<uint32_t>(narrow<BF16>(v[0])) | (static_cast<uint32_t>(narrow<BF16>(v[1])) << 16);
-                    dv.y = static_cast<uint32_t>(narrow<BF16>(v[2])) | (static_cast<uint32_t>(narrow<BF16>(v[3])) << 16);
-                    *reinterpret_cast<uint2*>(p.D + drow + col) = dv;
-                } else {
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        if (col + r < N) {
-                            float w = v[r];
-                            if (has_c) w += widen<BF16>(p.C[crow + col + r]);
-                            p.D[drow + col + r] = narrow<BF16>(w);
-                        }
-                    }
-                }
-            }
-        }
-    }
-}
-
-constexpr int kMaxDmaSplits = 64;
-
-template <int BM, int BN, int BK, int WM, int WN, int MF, int ST, bool BF16>
-hipError_t launch_dma(const KArgs& a, int64_t grid, hipStream_t stream) {
-    hipLaunchKernelGGL((gemm_dma_kernel<BM, BN, BK, WM, WN, MF, ST, BF16>),
-                       dim3(static_cast<unsigned>(grid)), dim3(64 * WM * WN), 0, stream, a);
-    return hipGetLastError();
-}
-
-#define DTG_STR2(x) #x
-#define DTG_STR(x) DTG_STR2(x)
-#define DMA_ENTRY(BM, BN, BK, WM, WN, MF, ST, BF)                                            \
-    {KF_DMA, BM, BN, BK, ST, MF, WM, WN, ((BM / WM) * (BN / WN) / 64 <= 64 ? kMaxDmaSplits : 1), BF, 1, 64 * WM * WN,                            \
-     static_cast<int64_t>(ST) * (BM + BN) * BK * 2,                                         \
-     &launch_dma<BM, BN, BK, WM, WN, MF, ST, (BF != 0)>,                                    \
-     "gemm_dma_kernel<" DTG_STR(BM) "," DTG_STR(BN) "," DTG_STR(BK) "," DTG_STR(WM) ","     \
-     DTG_STR(WN) "," DTG_STR(MF) "," DTG_STR(ST) "," DTG_STR(BF) ">"}
-#define DMA_BOTH(BM, BN, BK, WM, WN, MF, ST) \
-    DMA_ENTRY(BM, BN, BK, WM, WN, MF, ST, 0), DMA_ENTRY(BM, BN, BK, WM, WN, MF, ST, 1)
-
-const KernelEntry kDmaTable[] = {
+const KernelEntry kTable[] = {
     DMA_BOTH(256, 256, 64, 2, 4, 16, 2),
+    DMA_BOTH(256, 128, 64, 4, 2, 16, 2),
+    DMA_BOTH(128, 256, 64, 2, 4, 16, 2),
+    DMA_BOTH(128, 128, 64, 2, 4, 16, 2),
     DMA_BOTH(256, 256, 32, 2, 4, 16, 4),
     DMA_BOTH(256, 256, 64, 2, 4, 32, 2),
     DMA_BOTH(256, 256, 32, 2, 4, 32, 4),
-    DMA_BOTH(256, 128, 64, 2, 2, 16, 3),
-    DMA_BOTH(256, 128, 64, 2, 2, 16, 2),
-    DMA_BOTH(128, 256, 64, 2, 2, 16, 2),
-    DMA_BOTH(128, 128, 64, 2, 2, 16, 2),
-    DMA_BOTH(128, 128, 64, 2, 2, 16, 4),
-    DMA_BOTH(128, 128, 64, 2, 2, 32, 2),
-    DMA_BOTH(128, 128, 64, 2, 4, 16, 2),
-    DMA_BOTH(256, 128, 64, 4, 2, 16, 2),
-    DMA_BOTH(128, 256, 64, 2, 4, 16, 2),
-    DMA_BOTH(128, 128, 64, 2, 4, 16, 4),
-    DMA_BOTH(128, 128, 32, 2, 4, 16, 4),
 };
 
 }  // namespace
+
+const KernelEntry* dma_kernel_table_more(int* count);
+const KernelEntry* dma_kernel_table_layouts(int* count);
 
 int64_t dma_workspace_bytes(int64_t tiles, int bm, int bn, int splits) {
     if (splits <= 1) return 0;
@@ -543,13 +29,18 @@ int64_t dma_workspace_bytes(int64_t tiles, int bm, int bn, int splits) {
     return kCounterBytes + tiles * splits * static_cast<int64_t>(bm) * bn * 4;
 }
 
-namespace {
-
-}  // namespace
-
 const KernelEntry* dma_kernel_table(int* count) {
-    *count = static_cast<int>(sizeof(kDmaTable) / sizeof(kDmaTable[0]));
-    return kDmaTable;
+    static const std::vector<KernelEntry> all = [] {
+        std::vector<KernelEntry> v(kTable, kTable + sizeof(kTable) / sizeof(kTable[0]));
+        int n = 0;
+        const KernelEntry* t = dma_kernel_table_more(&n);
+        v.insert(v.end(), t, t + n);
+        t = dma_kernel_table_layouts(&n);
+        v.insert(v.end(), t, t + n);
+        return v;
+    }();
+    *count = static_cast<int>(all.size());
+    return all.data();
 }
 
 }  // namespace dtg

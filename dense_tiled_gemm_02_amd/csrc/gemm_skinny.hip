@@ -346,7 +346,7 @@ hipError_t launch_skinny(const KArgs& a, int64_t grid, hipStream_t stream) {
      static_cast<int64_t>(NWV) * ST * (CK * BN + BMR * CK) * 2,                             \
      &launch_skinny<BN, NWV, CK, ST, (BF != 0), BMR>,                                       \
      "gemm_skinny_kernel<" DTG_STR(BN) "," DTG_STR(NWV) "," DTG_STR(CK) "," DTG_STR(ST) ","  \
-     DTG_STR(BF) "," DTG_STR(BMR) ">"}
+     DTG_STR(BF) "," DTG_STR(BMR) ">", 0}
 #define SKINNY_BOTH(BN, NWV, CK, ST) SKINNY_ENTRY(BN, NWV, CK, ST, 0, 16), SKINNY_ENTRY(BN, NWV, CK, ST, 1, 16)
 #define SKINNY32_BOTH(BN, NWV, CK, ST) SKINNY_ENTRY(BN, NWV, CK, ST, 0, 32), SKINNY_ENTRY(BN, NWV, CK, ST, 1, 32)
 

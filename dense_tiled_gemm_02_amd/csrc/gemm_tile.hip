@@ -86,7 +86,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile_kernel(KArgs p) {
         const int row = q / CH, c = q % CH;
         const bool inq = (A_CHUNKS % NT == 0) || (q < A_CHUNKS);
         a_ok[i] = inq && (m0 + row < M);
-        a_off[i] = static_cast<int64_t>(a_ok[i] ? m0 + row : 0) * p.lda + 8 * c;
+        a_off[i] = static_cast<int64_t>(a_ok[i] ? m0 + row : 0) * p.lda + 8 * c * (VEC ? 1 : p.sak);
         a_kc[i] = 8 * c;
         a_lds[i] = row * BK + ((c ^ swz<CH>(row)) * 8);
     }
@@ -103,7 +103,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile_kernel(KArgs p) {
         b_in[i] = (B_BLOCKS % NT == 0) || (b < B_BLOCKS);
         b_col[i] = n0 + 8 * nb;
         b_kc[i] = 8 * kc;
-        b_off[i] = static_cast<int64_t>(8 * kc) * p.ldb + (b_in[i] ? b_col[i] : 0);
+        b_off[i] = static_cast<int64_t>(8 * kc) * p.ldb + static_cast<int64_t>(b_in[i] ? b_col[i] : 0) * (VEC ? 1 : p.sbn);
         b_lds[i] = (8 * nb) * BK + kc * 8;   // row 8*nb (+ c added per row), chunk kc
     }
 
@@ -112,7 +112,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile_kernel(KArgs p) {
 
     auto gload = [&](int kt, bool check) {
         const int k0 = kt * BK;
-        const uint16_t* Ak = p.A + k0;
+        const uint16_t* Ak = p.A + static_cast<int64_t>(k0) * (VEC ? 1 : p.sak);
         const uint16_t* Bk = p.B + static_cast<int64_t>(k0) * p.ldb;
 #pragma unroll
         for (int i = 0; i < A_PT; ++i) {
@@ -129,8 +129,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile_kernel(KArgs p) {
 #pragma unroll
                 for (int e = 0; e < 8; e += 2) {
                     const int k = k0 + a_kc[i] + e;
-                    const uint32_t x0 = (a_ok[i] && k < K) ? Ak[a_off[i] + e] : 0u;
-                    const uint32_t x1 = (a_ok[i] && k + 1 < K) ? Ak[a_off[i] + e + 1] : 0u;
+                    const uint32_t x0 = (a_ok[i] && k < K) ? Ak[a_off[i] + e * p.sak] : 0u;
+                    const uint32_t x1 = (a_ok[i] && k + 1 < K) ? Ak[a_off[i] + (e + 1) * p.sak] : 0u;
                     w[e / 2] = x0 | (x1 << 16);
                 }
                 ra[i] = u32x4{w[0], w[1], w[2], w[3]};
@@ -153,8 +153,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile_kernel(KArgs p) {
                     uint32_t w[4];
 #pragma unroll
                     for (int e = 0; e < 8; e += 2) {
-                        const uint32_t x0 = (krow && b_col[i] + e < N) ? src[e] : 0u;
-                        const uint32_t x1 = (krow && b_col[i] + e + 1 < N) ? src[e + 1] : 0u;
+                        const uint32_t x0 = (krow && b_col[i] + e < N) ? src[e * p.sbn] : 0u;
+                        const uint32_t x1 = (krow && b_col[i] + e + 1 < N) ? src[(e + 1) * p.sbn] : 0u;
                         w[e / 2] = x0 | (x1 << 16);
                     }
                     rb[i][r] = u32x4{w[0], w[1], w[2], w[3]};
@@ -277,7 +277,7 @@ hipError_t launch_tile(const KArgs& a, int64_t grid, hipStream_t stream) {
      static_cast<int64_t>(ST) * (BM + BN) * BK * 2,                                          \
      &launch_tile<BM, BN, BK, WM, WN, MF, ST, (BF != 0), (VEC != 0)>,                        \
      "gemm_tile_kernel<" DTG_STR(BM) "," DTG_STR(BN) "," DTG_STR(BK) "," DTG_STR(WM) ","     \
-     DTG_STR(WN) "," DTG_STR(MF) "," DTG_STR(ST) "," DTG_STR(BF) "," DTG_STR(VEC) ">"}
+     DTG_STR(WN) "," DTG_STR(MF) "," DTG_STR(ST) "," DTG_STR(BF) "," DTG_STR(VEC) ">", (VEC) ? 0 : -1}
 
 #define TILE_BOTH(BM, BN, BK, WM, WN, MF, ST, VEC) \
     TILE_ENTRY(BM, BN, BK, WM, WN, MF, ST, 0, VEC), TILE_ENTRY(BM, BN, BK, WM, WN, MF, ST, 1, VEC)

@@ -6,8 +6,10 @@
 
 namespace dtg {
 
-// Arguments of every GEMM kernel.  Row-major operands; leading strides in
-// elements.  M, N, K < 2^31 (the planner rejects larger).
+// Arguments of every GEMM kernel; strides in elements.  A element (m, k) is
+// A[m * lda + k * sak], B element (k, n) is B[k * ldb + n * sbn]; C and D are
+// row-major with leading strides ldc, ldd.  M, N, K < 2^31 (the planner
+// rejects larger).
 struct KArgs {
     const uint16_t* A;
     const uint16_t* B;
@@ -20,6 +22,7 @@ struct KArgs {
     int32_t has_c;
     int32_t splits;      // K slices across workgroups (1 = none)
     int64_t lda, ldb, ldc, ldd;
+    int64_t sak, sbn;    // 1 for row-major A and B
     void* ws;            // workspace: arrival counters, then fp32 partial tiles
 };
 
@@ -46,7 +49,11 @@ struct KernelEntry {
     int64_t lds_bytes;
     launch_fn launch;
     const char* name;
+    int32_t layout;      // operands in memory: bit 0 A stored K x M, bit 1 B stored N x K; -1 any strides
 };
+
+// Layout code of a problem's A and B (see KernelEntry::layout).
+constexpr int kLayTA = 1, kLayTB = 2;
 
 // All compiled variants (tile kernels followed by skinny kernels).
 const KernelEntry* tile_kernel_table(int* count);

@@ -90,6 +90,7 @@ def plan(M, N, K, dt=g.GEMM_BF16, has_c=False, force=None, **ld):
     return g.gemm_plan_create_for(g.problem(M, N, K, dt, has_c, **ld), fake_gfx950(), force)
 
 
+
 def test_plans_for_the_five_workloads_fit_the_device():
     cases = [(256, 256, 256, g.GEMM_F16, False), (1024, 1024, 1024, g.GEMM_F16, False),
              (4096, 4096, 4096, g.GEMM_BF16, False), (16, 8192, 8192, g.GEMM_BF16, False),
@@ -157,9 +158,9 @@ def test_forced_config_is_honoured_or_rejected():
 def test_unaligned_shapes_take_the_element_path():
     p = plan(100, 30, 17, g.GEMM_F16)
     assert "VEC" not in p.describe()
-    assert p.describe().endswith("vec=0")
+    assert "vec=0 " in p.describe()
     p = plan(128, 64, 64, g.GEMM_F16)
-    assert p.describe().endswith("vec=1")
+    assert "vec=1 " in p.describe()
 
 
 def test_validation_errors():
@@ -179,10 +180,13 @@ def test_validation_errors():
     p = g.problem(4, 4, 4, g.GEMM_F16)
     p.has_c = 2
     assert status(p) == g.GEMM_ERR_INVALID_ARG
-    p = g.problem(4, 4, 4, g.GEMM_F16)
-    p.sa_k = 2                                   # column-strided A: not this version
+    p = g.problem(4, 4, 4, g.GEMM_F16, True)
+    p.sc_n = 2                                   # C and D must stay row-major
     assert status(p) == g.GEMM_ERR_UNSUPPORTED
     assert "column stride" in g.gemm_last_error()
+    p = g.problem(4, 4, 4, g.GEMM_F16)
+    p.sa_k = 2                                   # any A and B strides: element-wise path
+    assert status(p) == g.GEMM_OK
     p = g.problem(4, 8, 4, g.GEMM_F16, ldd=4)    # output rows would overlap
     assert status(p) == g.GEMM_ERR_INVALID_ARG
     p = g.problem(1 << 31, 4, 4, g.GEMM_F16)
@@ -236,3 +240,27 @@ def test_split_k_plans_need_and_check_a_workspace():
     assert e.value.status == g.GEMM_ERR_WORKSPACE
     p1 = plan(16, 8192, 8192, force={"kernel": 2, "bn": 32, "splitk": 1})
     assert g.gemm_workspace_size(p1) == 0
+
+
+def test_layouts_pick_matching_kernels():
+    # A stored K x M and/or B stored N x K: direct-to-LDS variants of that layout
+    for ta, tb in ((False, True), (True, False), (True, True)):
+        p = plan(4096, 4096, 4096, ta=ta, tb=tb)
+        lay = (1 if ta else 0) | (2 if tb else 0)
+        assert p.config.kernel == 3 and p.describe().endswith("vec=1 layout=%d" % lay)
+        assert ",lay%d>" % lay in p.describe()
+    # row-major: the plain variants
+    assert plan(4096, 4096, 4096).describe().endswith("vec=1 layout=0")
+    # a transposed operand whose contiguous extent is not a multiple of 8: element path
+    p = plan(4000, 1000, 1004, ta=True)             # M = 4000 is fine, but
+    assert p.describe().endswith("vec=1 layout=1")
+    p = plan(4004 - 2, 1000, 1000, ta=True)         # M % 8 != 0 for a K x M A
+    assert p.describe().endswith("vec=0 layout=1")
+    # strides that are neither (element-wise path, layout -1)
+    pr = g.problem(64, 64, 64, g.GEMM_F16)
+    pr.sa_m, pr.sa_k = 130, 2
+    p = g.gemm_plan_create_for(pr, fake_gfx950())
+    assert p.describe().endswith("vec=0 layout=-1")
+    # the decode regime needs row-major operands; a transposed B goes to the tile ladder
+    assert plan(16, 8192, 8192).config.kernel == 2
+    assert plan(16, 8192, 8192, tb=True).config.kernel != 2

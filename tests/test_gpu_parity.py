@@ -406,3 +406,74 @@ def test_one_shot_entry_point():
            [K, 1, N, 1, N, 1, N, 1], g.GEMM_BF16, 1, torch.cuda.current_stream().cuda_stream)
     torch.cuda.synchronize()
     check(A, B, C, D.cpu(), "bf16", label="one-shot")
+
+
+# ---------------------------------------------------------------- operand layouts
+
+
+def _placed(X, transposed, pad):
+    """X (CPU, rows x cols) on the GPU as a view with X's shape whose storage is
+    row-major (rows x (cols + pad)) or, transposed, (cols x (rows + pad))."""
+    r, c = X.shape
+    if transposed:
+        st = torch.zeros((c, r + pad), dtype=X.dtype)
+        st[:, :r] = X.t()
+        return st.cuda()[:, :r].t()
+    st = torch.zeros((r, c + pad), dtype=X.dtype)
+    st[:, :c] = X
+    return st.cuda()[:, :c]
+
+
+LAYOUT_TILES = [dict(kernel=3, bm=256, bn=256, waves_m=2, waves_n=4), dict(kernel=3, bm=256, bn=128, waves_m=4, waves_n=2),
+                dict(kernel=3, bm=128, bn=256, waves_m=2, waves_n=4), dict(kernel=3, bm=128, bn=128, waves_m=2, waves_n=4),
+                dict(kernel=3, bm=128, bn=128, waves_m=2, waves_n=4, splitk=3), None]
+
+
+@pytest.mark.parametrize("mnk", [(520, 264, 200), (384, 640, 1000), (136, 1000, 520)])
+def test_operand_layouts(mnk):
+    """A stored K x M and / or B stored N x K (padded leading dimensions):
+    the direct-to-LDS variants for each layout, and the planner's choice, all
+    inside the bound; for a fixed tile every layout gives the same bits (the
+    fragments, hence the accumulation order, do not depend on the layout)."""
+    M, N, K = mnk
+    for dt, has_c in (("bf16", True), ("f16", False)):
+        A, B, C = _inputs(M, N, K, dt, has_c, seed=M + 2 * N + 5 * K)
+        Ab, Bb = gemm_inputs.bits(A), gemm_inputs.bits(B)
+        Cb = gemm_inputs.bits(C) if C is not None else None
+        ref, S = oracle.gemm_f64(Ab, Bb, Cb, dt)
+        dC = C.cuda() if C is not None else None
+        for cfg in LAYOUT_TILES:
+            outs = {}
+            for ta in (False, True):
+                for tb in (False, True):
+                    dA, dB = _placed(A, ta, 8), _placed(B, tb, 16)
+                    D = torch.full((M, N), float("nan"), dtype=A.dtype, device="cuda")
+                    g.matmul(dA, dB, dC, out=D, config=cfg)
+                    torch.cuda.synchronize()
+                    Dh = D.cpu()
+                    n, worst, first = oracle.tol_check(gemm_inputs.bits(Dh), ref, S, dt)
+                    assert n == 0, "%s %s %s ta=%d tb=%d: %d outside (worst %.3g)" % (dt, mnk, cfg, ta, tb, n, worst)
+                    outs[(ta, tb)] = Dh
+            if cfg is not None:
+                base = outs[(False, False)].view(torch.int16)
+                for key, Dh in outs.items():
+                    assert torch.equal(base, Dh.view(torch.int16)), (dt, mnk, cfg, key)
+
+
+def test_general_strides_take_the_element_path():
+    """Operands with neither stride 1 (every other row and column of a larger
+    array) and odd extents: the element-wise kernel, inside the bound."""
+    M, N, K = 70, 45, 33
+    for dt in ("bf16", "f16"):
+        A, B, C = _inputs(M, N, K, dt, True, seed=77)
+        bigA = torch.zeros((2 * M, 3 * K), dtype=A.dtype)
+        bigA[::2, ::3] = A
+        bigB = torch.zeros((3 * K, 2 * N), dtype=B.dtype)
+        bigB[::3, ::2] = B
+        dA = bigA.cuda()[::2, ::3]
+        dB = bigB.cuda()[::3, ::2]
+        pl = g.plan_for(dA, dB, C.cuda(), None)
+        assert "layout=-1" in pl.describe() and "vec=0" in pl.describe()
+        D = g.matmul(dA, dB, C.cuda())
+        torch.cuda.synchronize()
+        check(A, B, C, D.cpu(), dt, label="general strides %s" % dt)
