@@ -20,11 +20,16 @@
  *
  * Layout.  Every matrix is addressed by two element strides (row, column), as
  * in the pointer arithmetic of "Hopper Support in Triton", slide 6
- * (stride_am, stride_ak, stride_bk, stride_bn, stride_cm, stride_cn).  This
- * version runs row-major operands only: the column strides must be 1 and the
- * row strides >= 0 (GEMM_ERR_UNSUPPORTED otherwise).  Row strides that are
- * multiples of 8 elements with 16-byte aligned bases take the vector path;
- * anything else still runs, on an element-wise path.
+ * (stride_am, stride_ak, stride_bk, stride_bn, stride_cm, stride_cn), through
+ * which those slides reach any operand layout (slides 6 and 15, the block
+ * pointers' strides).  Strides are >= 0 (GEMM_ERR_UNSUPPORTED otherwise).  C
+ * and D must be row-major (column stride 1).  A and B may have any strides:
+ *   - A row-major (stride_ak = 1) or stored K x M (stride_am = 1),
+ *   - B row-major (stride_bn = 1) or stored N x K (stride_bk = 1),
+ * run on the vector paths when the operand's contiguous extent and its other
+ * stride are multiples of 8 elements and the bases are 16-byte aligned (the
+ * four combinations give bitwise identical results for one tile
+ * configuration); any other strides run on an element-wise path.
  *
  * Tiling.  The kernel walks a K loop over BLOCK_M x BLOCK_N x BLOCK_K tiles,
  * visits output tiles in GROUP_M bands for L2 reuse of B (FlagGems "Hygon
@@ -91,8 +96,10 @@ typedef struct gemm_problem {
  *   waves_m/_n    wavefront grid inside one workgroup (64 lanes per wave)
  *   group_m       GROUP_M of the grouped tile order (1 = row-major order)
  *   splitk        K slices across workgroups, summed in slice order by the
- *                 last workgroup of each output slab (skinny family; needs a
- *                 workspace when > 1); 1 for the tile families
+ *                 last workgroup to finish each output slab or tile (skinny
+ *                 family; direct-to-LDS family for tiles of at most 64 fp32
+ *                 accumulators per lane); needs a workspace when > 1; 1 for
+ *                 the register-staged family
  *   xcd_remap     GEMM_XCD_ON: pre-permute workgroup ids so each XCD gets a
  *                 contiguous band of the tile order; GEMM_XCD_OFF: plain ids
  *                 (0 in a forced configuration: the planner's choice)
