@@ -19,9 +19,22 @@ marshals numpy arrays into it:
 Inputs are numpy uint16 arrays holding the raw fp16/bf16 bit patterns (any
 element strides); dtype is "f16" or "bf16".
 
-Every function here is pinned by tests/test_oracle.py against exhaustive
-library conversions, exact rational arithmetic, BLAS in float64 and closed
-forms (identity, permutation, rank-1, integer-valued inputs).
+Block-scaled (MX) operands, arithmetic in oracle_mx.c:
+
+  mx_decode(codes, fmt) / e8m0_decode(codes)  exact element and scale values
+  mx_gemm_f64(A, SA, B, SB, K, fa, fb, C)     (ref, S) of the scaled product
+  mx_gemm_f64_at(..., ii, jj)                 the same at chosen positions
+  ulp_f32 / tol_check_f32                     acceptance rule for binary32 outputs
+
+MX operands are numpy uint8 arrays of raw bytes, one row per output row
+(A: M rows) or column (B: N rows, k along the row), with unit stride along
+the row; fmt is "e4m3", "e5m2" or "e2m1" (two elements per byte, even k in
+the low nibble); scales are uint8 arrays of E8M0 exponents, one per 32 k.
+
+Every function here is pinned by tests/test_oracle.py and
+tests/test_oracle_mx.py against exhaustive library conversions, exact
+rational arithmetic, BLAS in float64 and closed forms (identity, permutation,
+rank-1, integer-valued inputs, single scaled blocks).
 """
 import ctypes
 import os
@@ -69,6 +82,22 @@ def _load():
     lib.oracle_tol_check.restype = _i64
     lib.oracle_tol_check.argtypes = [_i64, _p, _p, _p, ctypes.c_int,
                                      ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_i64)]
+    for f in ("e4m3", "e5m2", "e2m1", "e8m0"):
+        fn = getattr(lib, "oracle_decode_" + f)
+        fn.restype = ctypes.c_double
+        fn.argtypes = [ctypes.c_uint8]
+    lib.oracle_mx_gemm_f64.restype = ctypes.c_int
+    lib.oracle_mx_gemm_f64.argtypes = [_i64, _i64, _i64, ctypes.c_int, ctypes.c_int,
+                                       _p, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _i64, _i64, _p, _p]
+    lib.oracle_mx_gemm_f64_at.restype = ctypes.c_int
+    lib.oracle_mx_gemm_f64_at.argtypes = [_i64, ctypes.c_int, ctypes.c_int,
+                                          _p, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _i64, _i64,
+                                          _i64, _p, _p, _p, _p]
+    lib.oracle_ulp_f32.restype = ctypes.c_double
+    lib.oracle_ulp_f32.argtypes = [ctypes.c_double]
+    lib.oracle_tol_check_f32.restype = _i64
+    lib.oracle_tol_check_f32.argtypes = [_i64, _p, _p, _p, ctypes.POINTER(ctypes.c_double),
+                                         ctypes.POINTER(_i64)]
     lib.oracle_num_threads.restype = ctypes.c_int
     lib.oracle_num_threads.argtypes = []
     _lib = lib
@@ -222,3 +251,120 @@ def grouped_order(num_pid_m, num_pid_n, group_m):
             for m in band:
                 order.append((m, n))
     return order
+
+
+# ---------------------------------------------------------------------------
+# Block-scaled (MX) operands
+
+MX_FORMATS = {"e4m3": 0, "e5m2": 1, "e2m1": 4}
+MX_ELEMENT_BITS = {"e4m3": 8, "e5m2": 8, "e2m1": 4}
+
+
+def _mxf(fmt):
+    try:
+        return MX_FORMATS[fmt]
+    except KeyError:
+        raise ValueError("MX element format must be one of %s, got %r" % (sorted(MX_FORMATS), fmt))
+
+
+def mx_decode(codes, fmt):
+    """Exact binary64 value of each element code (for e2m1 the low 4 bits)."""
+    _mxf(fmt)
+    fn = getattr(_load(), "oracle_decode_" + fmt)
+    c = np.asarray(codes, dtype=np.uint8)
+    return np.array([fn(int(x)) for x in c.ravel()], dtype=np.float64).reshape(c.shape)
+
+
+def e8m0_decode(codes):
+    """Exact binary64 value of each E8M0 scale code (NaN for 255)."""
+    fn = _load().oracle_decode_e8m0
+    c = np.asarray(codes, dtype=np.uint8)
+    return np.array([fn(int(x)) for x in c.ravel()], dtype=np.float64).reshape(c.shape)
+
+
+def _rows(x, name):
+    if not isinstance(x, np.ndarray) or x.dtype != np.uint8 or x.ndim != 2:
+        raise TypeError("%s must be a 2-D numpy uint8 array" % name)
+    if x.size and x.shape[1] > 1 and x.strides[1] != 1:
+        raise ValueError("%s must have unit stride along its rows" % name)
+    return x
+
+
+def _mx_args(A, SA, B, SB, K, fmt_a, fmt_b, C, M, N):
+    A, SA, B, SB = _rows(A, "A"), _rows(SA, "SA"), _rows(B, "B"), _rows(SB, "SB")
+    if A.shape[0] != M or SA.shape[0] != M or B.shape[0] != N or SB.shape[0] != N:
+        raise ValueError("row counts of A/SA (M) and B/SB (N) disagree")
+    nblk = (K + 31) // 32
+    for x, f, nm in ((A, fmt_a, "A"), (B, fmt_b, "B")):
+        if x.shape[1] * 8 < K * MX_ELEMENT_BITS[f]:
+            raise ValueError("%s rows hold fewer than K elements" % nm)
+    if SA.shape[1] < nblk or SB.shape[1] < nblk:
+        raise ValueError("scale rows hold fewer than ceil(K/32) scales")
+    if C is not None:
+        C = np.asarray(C, dtype=np.float64)
+        cs = (C.strides[0] // 8, C.strides[1] // 8)
+        cptr = C.ctypes.data
+    else:
+        cs, cptr = (0, 0), None
+    return A, SA, B, SB, C, cs, cptr
+
+
+def mx_gemm_f64(A, SA, B, SB, K, fmt_a, fmt_b, C=None):
+    """ref = A x B (+ C) and S = sum_k |a_ik b_kj| on MX operands, binary64.
+
+    A: M rows of element bytes, SA: M rows of scales; B: N rows (the columns
+    of B, k along the row), SB: N rows; C: optional M x N binary64 addend."""
+    M, N = A.shape[0], B.shape[0]
+    A, SA, B, SB, C, cs, cptr = _mx_args(A, SA, B, SB, K, fmt_a, fmt_b, C, M, N)
+    ref = np.empty((M, N), dtype=np.float64)
+    S = np.empty((M, N), dtype=np.float64)
+    rc = _load().oracle_mx_gemm_f64(M, N, K, _mxf(fmt_a), _mxf(fmt_b),
+                                    A.ctypes.data, A.strides[0], SA.ctypes.data, SA.strides[0],
+                                    B.ctypes.data, B.strides[0], SB.ctypes.data, SB.strides[0],
+                                    cptr, cs[0], cs[1], ref.ctypes.data, S.ctypes.data)
+    if rc != 0:
+        raise RuntimeError("oracle_mx_gemm_f64 failed (%d)" % rc)
+    return ref, S
+
+
+def mx_gemm_f64_at(A, SA, B, SB, K, fmt_a, fmt_b, C, ii, jj):
+    """ref and S of the MX product at output positions (ii[t], jj[t])."""
+    M, N = A.shape[0], B.shape[0]
+    A, SA, B, SB, C, cs, cptr = _mx_args(A, SA, B, SB, K, fmt_a, fmt_b, C, M, N)
+    ii = np.ascontiguousarray(ii, dtype=np.int64)
+    jj = np.ascontiguousarray(jj, dtype=np.int64)
+    if ii.shape != jj.shape or ii.ndim != 1:
+        raise ValueError("ii and jj must be 1-D and of equal length")
+    if ii.size and (ii.min() < 0 or ii.max() >= M or jj.min() < 0 or jj.max() >= N):
+        raise IndexError("sample position outside the output")
+    ref = np.empty(ii.shape, dtype=np.float64)
+    S = np.empty(ii.shape, dtype=np.float64)
+    rc = _load().oracle_mx_gemm_f64_at(K, _mxf(fmt_a), _mxf(fmt_b),
+                                       A.ctypes.data, A.strides[0], SA.ctypes.data, SA.strides[0],
+                                       B.ctypes.data, B.strides[0], SB.ctypes.data, SB.strides[0],
+                                       cptr, cs[0], cs[1], ii.size, ii.ctypes.data, jj.ctypes.data,
+                                       ref.ctypes.data, S.ctypes.data)
+    if rc != 0:
+        raise RuntimeError("oracle_mx_gemm_f64_at failed (%d)" % rc)
+    return ref, S
+
+
+def ulp_f32(x):
+    """One ulp of binary32 in the binade of |x| (2^-149 below 2^-126)."""
+    fn = _load().oracle_ulp_f32
+    v = np.asarray(x, dtype=np.float64)
+    return np.array([fn(float(t)) for t in v.ravel()], dtype=np.float64).reshape(v.shape)
+
+
+def tol_check_f32(got, ref, S):
+    """Acceptance rule for binary32 outputs: (n_fail, worst, first_bad) as tol_check."""
+    g = np.ascontiguousarray(got, dtype=np.float32).ravel()
+    r = np.ascontiguousarray(ref, dtype=np.float64).ravel()
+    s = np.ascontiguousarray(S, dtype=np.float64).ravel()
+    if not (g.size == r.size == s.size):
+        raise ValueError("got, ref and S differ in size")
+    worst = ctypes.c_double(0.0)
+    first = ctypes.c_int64(-1)
+    n = _load().oracle_tol_check_f32(g.size, g.ctypes.data, r.ctypes.data, s.ctypes.data,
+                                     ctypes.byref(worst), ctypes.byref(first))
+    return int(n), float(worst.value), int(first.value)

@@ -2,7 +2,7 @@
 
     python -m oracle.build        # or: python oracle/build.py
 
-Compiles oracle.c with gcc into oracle/liboracle.so: -O2, no floating-point
+Compiles oracle.c and oracle_mx.c with gcc into oracle/liboracle.so: -O2, no floating-point
 contraction, no fast-math, OpenMP over output rows.
 """
 import os
@@ -10,14 +10,14 @@ import subprocess
 import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-SRC = os.path.join(HERE, "oracle.c")
+SRCS = [os.path.join(HERE, "oracle.c"), os.path.join(HERE, "oracle_mx.c")]
 LIB = os.path.join(HERE, "liboracle.so")
 
 
 def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = ["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fopenmp",
-           "-fPIC", "-shared", "-Wall", "-Wextra", "-o", tmp, SRC, "-lm"]
+           "-fPIC", "-shared", "-Wall", "-Wextra", "-o", tmp] + SRCS + ["-lm"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
