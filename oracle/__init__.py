@@ -25,6 +25,7 @@ Block-scaled (MX) operands, arithmetic in oracle_mx.c:
   mx_gemm_f64(A, SA, B, SB, K, fa, fb, C)     (ref, S) of the scaled product
   mx_gemm_f64_at(..., ii, jj)                 the same at chosen positions
   ulp_f32 / tol_check_f32                     acceptance rule for binary32 outputs
+  mx_tol_check(got, out, ref, S, S8)          the MX acceptance rule (run term 2^-10 S8)
 
 MX operands are numpy uint8 arrays of raw bytes, one row per output row
 (A: M rows) or column (B: N rows, k along the row), with unit stride along
@@ -88,11 +89,14 @@ def _load():
         fn.argtypes = [ctypes.c_uint8]
     lib.oracle_mx_gemm_f64.restype = ctypes.c_int
     lib.oracle_mx_gemm_f64.argtypes = [_i64, _i64, _i64, ctypes.c_int, ctypes.c_int,
-                                       _p, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _i64, _i64, _p, _p]
+                                       _p, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _i64, _i64, _p, _p, _p]
     lib.oracle_mx_gemm_f64_at.restype = ctypes.c_int
     lib.oracle_mx_gemm_f64_at.argtypes = [_i64, ctypes.c_int, ctypes.c_int,
                                           _p, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _i64, _i64,
-                                          _i64, _p, _p, _p, _p]
+                                          _i64, _p, _p, _p, _p, _p]
+    lib.oracle_mx_tol_check.restype = _i64
+    lib.oracle_mx_tol_check.argtypes = [_i64, _p, ctypes.c_int, _p, _p, _p, ctypes.POINTER(ctypes.c_double),
+                                        ctypes.POINTER(_i64)]
     lib.oracle_ulp_f32.restype = ctypes.c_double
     lib.oracle_ulp_f32.argtypes = [ctypes.c_double]
     lib.oracle_tol_check_f32.restype = _i64
@@ -309,8 +313,10 @@ def _mx_args(A, SA, B, SB, K, fmt_a, fmt_b, C, M, N):
     return A, SA, B, SB, C, cs, cptr
 
 
-def mx_gemm_f64(A, SA, B, SB, K, fmt_a, fmt_b, C=None):
-    """ref = A x B (+ C) and S = sum_k |a_ik b_kj| on MX operands, binary64.
+def mx_gemm_f64(A, SA, B, SB, K, fmt_a, fmt_b, C=None, runs=False):
+    """ref = A x B (+ C) and S = sum_k |a_ik b_kj| on MX operands, binary64;
+    with runs=True also S8 = sum over runs of 8 consecutive k of the largest
+    |product| (the run term of the MX acceptance rule).
 
     A: M rows of element bytes, SA: M rows of scales; B: N rows (the columns
     of B, k along the row), SB: N rows; C: optional M x N binary64 addend."""
@@ -318,17 +324,19 @@ def mx_gemm_f64(A, SA, B, SB, K, fmt_a, fmt_b, C=None):
     A, SA, B, SB, C, cs, cptr = _mx_args(A, SA, B, SB, K, fmt_a, fmt_b, C, M, N)
     ref = np.empty((M, N), dtype=np.float64)
     S = np.empty((M, N), dtype=np.float64)
+    S8 = np.empty((M, N), dtype=np.float64) if runs else None
     rc = _load().oracle_mx_gemm_f64(M, N, K, _mxf(fmt_a), _mxf(fmt_b),
                                     A.ctypes.data, A.strides[0], SA.ctypes.data, SA.strides[0],
                                     B.ctypes.data, B.strides[0], SB.ctypes.data, SB.strides[0],
-                                    cptr, cs[0], cs[1], ref.ctypes.data, S.ctypes.data)
+                                    cptr, cs[0], cs[1], ref.ctypes.data, S.ctypes.data,
+                                    S8.ctypes.data if runs else None)
     if rc != 0:
         raise RuntimeError("oracle_mx_gemm_f64 failed (%d)" % rc)
-    return ref, S
+    return (ref, S, S8) if runs else (ref, S)
 
 
-def mx_gemm_f64_at(A, SA, B, SB, K, fmt_a, fmt_b, C, ii, jj):
-    """ref and S of the MX product at output positions (ii[t], jj[t])."""
+def mx_gemm_f64_at(A, SA, B, SB, K, fmt_a, fmt_b, C, ii, jj, runs=False):
+    """ref and S (and S8 with runs=True) of the MX product at output positions (ii[t], jj[t])."""
     M, N = A.shape[0], B.shape[0]
     A, SA, B, SB, C, cs, cptr = _mx_args(A, SA, B, SB, K, fmt_a, fmt_b, C, M, N)
     ii = np.ascontiguousarray(ii, dtype=np.int64)
@@ -339,14 +347,15 @@ def mx_gemm_f64_at(A, SA, B, SB, K, fmt_a, fmt_b, C, ii, jj):
         raise IndexError("sample position outside the output")
     ref = np.empty(ii.shape, dtype=np.float64)
     S = np.empty(ii.shape, dtype=np.float64)
+    S8 = np.empty(ii.shape, dtype=np.float64) if runs else None
     rc = _load().oracle_mx_gemm_f64_at(K, _mxf(fmt_a), _mxf(fmt_b),
                                        A.ctypes.data, A.strides[0], SA.ctypes.data, SA.strides[0],
                                        B.ctypes.data, B.strides[0], SB.ctypes.data, SB.strides[0],
                                        cptr, cs[0], cs[1], ii.size, ii.ctypes.data, jj.ctypes.data,
-                                       ref.ctypes.data, S.ctypes.data)
+                                       ref.ctypes.data, S.ctypes.data, S8.ctypes.data if runs else None)
     if rc != 0:
         raise RuntimeError("oracle_mx_gemm_f64_at failed (%d)" % rc)
-    return ref, S
+    return (ref, S, S8) if runs else (ref, S)
 
 
 def ulp_f32(x):
@@ -367,4 +376,26 @@ def tol_check_f32(got, ref, S):
     first = ctypes.c_int64(-1)
     n = _load().oracle_tol_check_f32(g.size, g.ctypes.data, r.ctypes.data, s.ctypes.data,
                                      ctypes.byref(worst), ctypes.byref(first))
+    return int(n), float(worst.value), int(first.value)
+
+
+_OUT_KIND = {"f16": 0, "bf16": 1, "f32": 2}
+
+
+def mx_tol_check(got, out, ref, S, S8):
+    """MX acceptance rule |g - ref| <= ulp_out(ref) + 2^-20 S + 2^-10 S8 for
+    outputs of type out ("f16", "bf16": raw uint16 bits; "f32": float32
+    values).  S8=None drops the run term.  Returns (n_fail, worst, first_bad)."""
+    kind = _OUT_KIND[out]
+    g = np.ascontiguousarray(got, dtype=np.float32 if kind == 2 else np.uint16).ravel()
+    r = np.ascontiguousarray(ref, dtype=np.float64).ravel()
+    s = np.ascontiguousarray(S, dtype=np.float64).ravel()
+    s8 = None if S8 is None else np.ascontiguousarray(S8, dtype=np.float64).ravel()
+    if not (g.size == r.size == s.size) or (s8 is not None and s8.size != r.size):
+        raise ValueError("got, ref, S and S8 differ in size")
+    worst = ctypes.c_double(0.0)
+    first = ctypes.c_int64(-1)
+    n = _load().oracle_mx_tol_check(g.size, g.ctypes.data, kind, r.ctypes.data, s.ctypes.data,
+                                    s8.ctypes.data if s8 is not None else None,
+                                    ctypes.byref(worst), ctypes.byref(first))
     return int(n), float(worst.value), int(first.value)

@@ -374,3 +374,94 @@ def test_mx_pins_reject_planted_mistakes():
     for bad in (block_of_16, scales_swapped, block_shifted, nibbles_swapped, last_block_dropped,
                 b_transposed, scale_unbiased):
         assert not _mx_pins_pass(bad), bad.__name__
+
+
+# ---------------------------------------------------------------- MX acceptance rule
+
+
+def test_run_sums_closed_forms():
+    """S8 = sum over runs of 8 consecutive k of the largest |product|."""
+    for K in (64, 100):                     # 100: a last run of 4
+        A, B = _ones(3, K, "e4m3"), _ones(2, K, "e4m3")
+        SA = np.full((3, 4), 127, np.uint8)
+        SB = np.full((2, 4), 127, np.uint8)
+        ref, S, S8 = oracle.mx_gemm_f64(A, SA, B, SB, K, "e4m3", "e4m3", runs=True)
+        assert np.array_equal(S8, np.full((3, 2), float(-(-K // 8))))
+        # one product of 2 (code 0x40) at the start of every run: each run's max is 2
+        A2 = A.copy()
+        A2[:, 0::8] = 0x40
+        ref, S, S8 = oracle.mx_gemm_f64(A2, SA, B, SB, K, "e4m3", "e4m3", runs=True)
+        assert np.array_equal(S8, np.full((3, 2), 2.0 * -(-K // 8)))
+        assert np.array_equal(S, np.full((3, 2), float(K + -(-K // 8))))
+
+
+def test_run_sums_bounds_and_sampled_positions():
+    rng = np.random.default_rng(12)
+    M, N, K = 9, 7, 200
+    for fmt in FMTS:
+        A, B = _rand_codes(rng, M, K, fmt), _rand_codes(rng, N, K, fmt)
+        SA = rng.integers(120, 135, (M, 7), dtype=np.uint8)
+        SB = rng.integers(120, 135, (N, 7), dtype=np.uint8)
+        ref, S, S8 = oracle.mx_gemm_f64(A, SA, B, SB, K, fmt, fmt, runs=True)
+        assert np.all(S8 <= S) and np.all(8 * S8 >= S)
+        Av = _values(A, K, fmt) * _expanded_scales(SA, K)
+        Bv = _values(B, K, fmt) * _expanded_scales(SB, K)
+        P = np.abs(Av[:, None, :] * Bv[None, :, :])
+        want = sum(P[:, :, 8 * q:8 * q + 8].max(axis=2) for q in range(K // 8))
+        assert np.array_equal(S8, want)
+        ii, jj = rng.integers(0, M, 20), rng.integers(0, N, 20)
+        r2, s2, s82 = oracle.mx_gemm_f64_at(A, SA, B, SB, K, fmt, fmt, None, ii, jj, runs=True)
+        assert np.array_equal(s82, S8[ii, jj]) and np.array_equal(r2, ref[ii, jj])
+
+
+@pytest.mark.parametrize("out", ["bf16", "f16", "f32"])
+def test_mx_rule_bound_is_the_sum_of_its_three_terms(out):
+    rng = np.random.default_rng(8)
+    ref = rng.standard_normal(500) * 4
+    S = np.abs(ref) * 8
+    S8 = S / 3
+    if out == "f32":
+        ulp = oracle.ulp_f32(ref)
+    else:
+        ulp = oracle.ulp_out(ref, out)
+    bound = ulp + np.ldexp(S, -20) + np.ldexp(S8, -10)
+    dt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[out]
+
+    def enc(x):
+        t = torch.from_numpy(x).to(dt)
+        return t.numpy() if out == "f32" else t.view(torch.int16).numpy().view(np.uint16)
+
+    inside = ref + 0.9 * bound * np.sign(rng.standard_normal(500))
+    g = enc(inside)
+    # the stored value may round past the bound only by the rounding of the output type
+    back = g.astype(np.float64) if out == "f32" else oracle.decode(g, out)
+    ok = np.abs(back - ref) <= bound
+    n, worst, _ = oracle.mx_tol_check(g, out, ref, S, S8)
+    assert n == int((~ok).sum())
+    outside = enc(ref + 4 * bound)
+    n, worst, first = oracle.mx_tol_check(outside, out, ref, S, S8)
+    assert n == 500 and first == 0 and worst > 1
+    # without the run term the rule is the 16-bit contract
+    if out != "f32":
+        g2 = enc(ref)
+        assert oracle.mx_tol_check(g2, out, ref, S, None)[0] == oracle.tol_check(g2, ref, S, out)[0] == 0
+
+
+def test_mx_rule_rejects_one_misscaled_block():
+    """The run term is loose enough for the instruction and tight enough to
+    catch a wrong scale on a single 32-k block of one row."""
+    rng = np.random.default_rng(13)
+    M, N, K = 16, 16, 1024
+    for fmt in ("e4m3", "e5m2", "e2m1"):
+        A, B = _rand_codes(rng, M, K, fmt, fmt != "e2m1"), _rand_codes(rng, N, K, fmt, fmt != "e2m1")
+        SA = rng.integers(122, 127, (M, 32), dtype=np.uint8)
+        SB = rng.integers(122, 127, (N, 32), dtype=np.uint8)
+        ref, S, S8 = oracle.mx_gemm_f64(A, SA, B, SB, K, fmt, fmt, runs=True)
+        SA2 = SA.copy()
+        SA2[5, 17] += 1                     # block 17 of row 5 counted twice
+        bad, _ = oracle.mx_gemm_f64(A, SA2, B, SB, K, fmt, fmt)
+        g = torch.from_numpy(bad.astype(np.float32)).numpy()
+        n, _, _ = oracle.mx_tol_check(g, "f32", ref, S, S8)
+        rows = np.unique(np.argwhere(np.abs(bad - ref) > 0)[:, 0])
+        assert list(rows) == [5]
+        assert n >= 8, (fmt, n)             # at least half of row 5's 16 outputs are caught
