@@ -37,6 +37,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 256 * 2.4e9 * 4096 / 1e12        # 2516.6
+PEAK_MX_TFLOPS = {"e4m3": 5000.0, "e5m2": 5000.0, "e2m1": 10100.0}   # MI355X dense fp8 / fp4
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
 
@@ -74,6 +75,8 @@ def parse():
                     help="time bf16 4096^3 with A and / or B stored transposed")
     ap.add_argument("--decode", action="store_true",
                     help="time the decode regime: M in {1,2,4,8,16,32}, N = K in {4096, 8192}, bf16")
+    ap.add_argument("--mx", action="store_true",
+                    help="block-scaled (MX) workloads: FP8 / FP4 elements with E8M0 scales per 32 k")
     ap.add_argument("--rounds", type=int, default=30)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-skinny", action="store_true")
@@ -366,6 +369,77 @@ def decode(args):
         del Bs
 
 
+def mx(args):
+    """Block-scaled (MX) workloads: the planner's plan, median and spread over
+    interleaved rounds, against the dense MFMA peak of the element type (square)
+    or HBM (M = 16, B rotated over > 256 MB of copies).  A per-tensor scaled
+    fp8 GEMM of torch (torch._scaled_mm, hipBLASLt) on the same bytes is timed
+    beside the fp8 case as a library reference (no block scales).  One JSON
+    line per workload."""
+    import torch
+    import gemm_inputs
+    import dense_tiled_gemm_02_amd.mx as mxb
+    for name in sorted(gemm_inputs.MX_WORKLOADS):
+        w = gemm_inputs.MX_WORKLOADS[name]
+        A, SA, B, SB, _ = gemm_inputs.make_mx(w)
+        dA, dSA = torch.from_numpy(A).cuda(), torch.from_numpy(SA).cuda()
+        copies = 1
+        if w.M <= 32:
+            copies = max(4, -(-300 * (1 << 20) // B.nbytes))
+        Bs = [torch.from_numpy(B).cuda()]
+        SBs = [torch.from_numpy(SB).cuda()]
+        for r in range(1, copies):
+            b2, s2 = gemm_inputs.draw_mx(w.N, w.K, w.fmt_b, w.seeds[1] + 1000 * r)
+            Bs.append(torch.from_numpy(b2).cuda())
+            SBs.append(torch.from_numpy(s2).cuda())
+        D = torch.empty((w.M, w.N), dtype=torch.bfloat16, device="cuda")
+        p = mxb.mx_problem(w.M, w.N, w.K, w.fmt_a, w.fmt_b, mxb.GEMM_MX_OUT_BF16, lda=A.shape[1], ldb=B.shape[1],
+                           ldsa=SA.shape[1], ldsb=SB.shape[1])
+        pl = mxb.gemm_mx_plan_create(p, torch.cuda.current_device())
+        stream = torch.cuda.current_stream().cuda_stream
+        run = mxb.mxlib().gemm_mx_run
+        st = {"i": 0}
+
+        def launch(c, st=st):
+            for _ in range(c):
+                i = st["i"] % copies
+                assert run(pl.handle, dA.data_ptr(), dSA.data_ptr(), Bs[i].data_ptr(), SBs[i].data_ptr(), None,
+                           D.data_ptr(), stream) == 0
+                st["i"] += 1
+        launch(5)
+        torch.cuda.synchronize()
+        ts = stats(batch_times(launch, 20, args.rounds))
+        ms = ts["median_ms"]
+        rec = {"workload": name, **w.describe(), "plan": pl.describe(), "us": ms * 1e3, "spread": ts["spread"],
+               "tflops": w.flops() / ms / 1e9}
+        if w.M <= 32:
+            gbs = w.bytes() / ms / 1e6
+            rec["roofline"] = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                               "frac": gbs / PEAK_HBM_GBS}
+        else:
+            peak = PEAK_MX_TFLOPS[w.fmt_a]
+            rec["roofline"] = {"bound": "mfma", "achieved": round(rec["tflops"], 1), "peak": peak,
+                               "unit": "TFLOP/s", "frac": rec["tflops"] / peak}
+        if w.fmt_a == "e4m3" and w.fmt_b == "e4m3":
+            try:
+                a8 = dA.view(torch.float8_e4m3fn)
+                b8 = Bs[0].view(torch.float8_e4m3fn)
+                one = torch.ones((), dtype=torch.float32, device="cuda")
+
+                def launch_torch(c):
+                    for _ in range(c):
+                        torch._scaled_mm(a8, b8.t(), scale_a=one, scale_b=one, out_dtype=torch.bfloat16)
+                launch_torch(3)
+                torch.cuda.synchronize()
+                rec["torch_scaled_mm_per_tensor_us"] = stats(batch_times(launch_torch, 20, args.rounds))[
+                    "median_ms"] * 1e3
+            except Exception as e:   # not every build has a scaled fp8 GEMM
+                rec["torch_scaled_mm_per_tensor_us"] = None
+                rec["torch_scaled_mm_error"] = str(e)[:200]
+        print(json.dumps(rec), flush=True)
+        del Bs, SBs, dA, dSA
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -386,6 +460,9 @@ def main():
         return
     if args.layouts:
         layouts(args)
+        return
+    if args.mx:
+        mx(args)
         return
     w = gemm_inputs.WORKLOADS[args.workload]
     case = Case(w, rotate=4 if w.name.startswith("skinny") else 1)

@@ -22,7 +22,8 @@ LIB = os.path.join(PKG, "libgemm.so")
 PROBE_LIB = os.path.join(PKG, "libgemm_probe.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "gemm_tile.hip", "gemm_dma.hip", "gemm_dma_more.hip", "gemm_dma_layouts.hip",
+SOURCES = ["api.cpp", "api_mx.cpp", "gemm_tile.hip", "gemm_dma.hip", "gemm_dma_more.hip", "gemm_dma_layouts.hip",
+           "gemm_mx.hip",
            "gemm_skinny.hip"]
 PROBE_SOURCES = ["probe.hip"]
 

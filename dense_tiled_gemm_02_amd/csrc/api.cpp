@@ -25,6 +25,7 @@
 #include <vector>
 
 #include "../../include/gemm.h"
+#include "api_internal.h"
 #include "kernels.h"
 #include "tile_order.h"
 
@@ -403,6 +404,14 @@ std::mutex g_cache_mu;
 std::map<CacheKey, std::unique_ptr<gemm_plan>> g_cache;
 
 }  // namespace
+
+namespace dtg {
+gemm_status record_error(gemm_status st, const char* msg) {
+    g_err = msg;
+    return st;
+}
+gemm_status cached_device_info(int device, gemm_device_info* info) { return device_info_cached(device, info); }
+}  // namespace dtg
 
 extern "C" {
 

@@ -1,0 +1,299 @@
+// C ABI of the block-scaled (MX) GEMM: validation, tile choice and launch.
+// Declarations and the contract of every entry point are in include/gemm_mx.h.
+//
+// The tile choice follows the 16-bit planner: the largest 8-wave tile that
+// still gives at least half of the CUs a workgroup, else 128 x 128 ("Tuning
+// Triton kernels", sections 3-4: the choice is keyed on every tiled dimension
+// and separates regimes).
+#include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <new>
+
+#include "../../include/gemm_mx.h"
+#include "api_internal.h"
+#include "kernels_mx.h"
+
+struct gemm_mx_plan {
+    gemm_mx_problem prob;
+    gemm_device_info dev;
+    gemm_config cfg;
+    const dtg::MxEntry* entry;
+    int64_t num_pid_m, num_pid_n, grid;
+};
+
+namespace {
+
+gemm_status fail(gemm_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+gemm_status fail(gemm_status st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    return dtg::record_error(st, buf);
+}
+
+constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
+constexpr int kKernelMx = 4;   // gemm_config.kernel of the block-scaled tile kernel
+
+bool fmt_ok(int f) { return f == GEMM_MX_E4M3 || f == GEMM_MX_E5M2 || f == GEMM_MX_E2M1; }
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Bytes of k of one row: K elements of 8 or 4 bits.
+int64_t row_bytes(const gemm_mx_problem* p) { return p->fmt_a == GEMM_MX_E2M1 ? p->K / 2 : p->K; }
+
+gemm_status validate(const gemm_mx_problem* p) {
+    if (!p) return fail(GEMM_ERR_INVALID_ARG, "problem is NULL");
+    if (p->M < 0 || p->N < 0 || p->K < 0)
+        return fail(GEMM_ERR_INVALID_ARG, "negative size M=%lld N=%lld K=%lld", (long long)p->M, (long long)p->N,
+                    (long long)p->K);
+    if (!fmt_ok(p->fmt_a) || !fmt_ok(p->fmt_b))
+        return fail(GEMM_ERR_INVALID_ARG, "element formats %d / %d: expected GEMM_MX_E4M3, _E5M2 or _E2M1",
+                    (int)p->fmt_a, (int)p->fmt_b);
+    if (p->out != GEMM_MX_OUT_F16 && p->out != GEMM_MX_OUT_BF16 && p->out != GEMM_MX_OUT_F32)
+        return fail(GEMM_ERR_INVALID_ARG, "output type %d is not a gemm_mx_out value", (int)p->out);
+    if (p->has_c != 0 && p->has_c != 1)
+        return fail(GEMM_ERR_INVALID_ARG, "has_c must be 0 or 1, got %d", (int)p->has_c);
+    if (p->M > kMaxDim || p->N > kMaxDim || p->K > kMaxDim)
+        return fail(GEMM_ERR_UNSUPPORTED, "dimensions above 2^31-1 are not supported");
+    if ((p->fmt_a == GEMM_MX_E2M1) != (p->fmt_b == GEMM_MX_E2M1))
+        return fail(GEMM_ERR_UNSUPPORTED, "A and B must both be 8-bit formats or both E2M1");
+    const int64_t kq = p->fmt_a == GEMM_MX_E2M1 ? 32 : 16;
+    if (p->K % kq != 0)
+        return fail(GEMM_ERR_UNSUPPORTED, "K=%lld must be a multiple of %lld for this element format",
+                    (long long)p->K, (long long)kq);
+    const int64_t kb = row_bytes(p), nblk = cdiv(p->K, 32);
+    if (p->lda < 0 || p->ldb < 0 || p->ldsa < 0 || p->ldsb < 0 || p->ldc < 0 || p->ldd < 0)
+        return fail(GEMM_ERR_INVALID_ARG, "negative stride");
+    if (p->lda % 16 || p->ldb % 16)
+        return fail(GEMM_ERR_UNSUPPORTED, "lda=%lld and ldb=%lld must be multiples of 16 bytes", (long long)p->lda,
+                    (long long)p->ldb);
+    if (p->ldsa % 4 || p->ldsb % 4)
+        return fail(GEMM_ERR_UNSUPPORTED, "ldsa=%lld and ldsb=%lld must be multiples of 4 bytes",
+                    (long long)p->ldsa, (long long)p->ldsb);
+    if ((p->M > 1 && p->lda < kb) || (p->N > 1 && p->ldb < kb))
+        return fail(GEMM_ERR_INVALID_ARG, "lda / ldb below the %lld bytes of a row", (long long)kb);
+    if ((p->M > 0 && p->ldsa < nblk) || (p->N > 0 && p->ldsb < nblk))
+        return fail(GEMM_ERR_INVALID_ARG, "ldsa / ldsb below ceil(K/32) = %lld", (long long)nblk);
+    if (p->M > 1 && p->N > 0 && p->ldd < p->N)
+        return fail(GEMM_ERR_INVALID_ARG, "D row stride %lld < N=%lld makes output rows overlap",
+                    (long long)p->ldd, (long long)p->N);
+    // 32-bit buffer offsets cover one tile's rows of every operand
+    const int64_t lim = (int64_t(1) << 31) - 4096;
+    if (256 * p->lda >= lim || 256 * p->ldb >= lim || 256 * p->ldsa >= lim || 256 * p->ldsb >= lim)
+        return fail(GEMM_ERR_UNSUPPORTED, "row strides too large for 32-bit tile offsets");
+    return GEMM_OK;
+}
+
+const dtg::MxEntry* find_entry(const gemm_config& w, const gemm_mx_problem* p, const gemm_device_info& dev) {
+    int n = 0;
+    const dtg::MxEntry* t = dtg::mx_kernel_table(&n);
+    for (int i = 0; i < n; ++i) {
+        const dtg::MxEntry* e = &t[i];
+        if (e->fmt_a != p->fmt_a || e->fmt_b != p->fmt_b || e->lds_bytes > dev.lds_per_wg) continue;
+        if ((w.bm && w.bm != e->bm) || (w.bn && w.bn != e->bn) || (w.stages && w.stages != e->stages) ||
+            (w.waves_m && w.waves_m != e->waves_m) || (w.waves_n && w.waves_n != e->waves_n) ||
+            (w.bk && w.bk != e->bk) || (w.mfma && w.mfma != e->mfma))
+            continue;
+        return e;
+    }
+    return nullptr;
+}
+
+gemm_status plan_impl(const gemm_mx_problem* prob, const gemm_device_info* dev, const gemm_config* force,
+                      gemm_mx_plan** out) {
+    if (!out) return fail(GEMM_ERR_INVALID_ARG, "out is NULL");
+    *out = nullptr;
+    gemm_status st = validate(prob);
+    if (st != GEMM_OK) return st;
+    if (!dev || dev->cu_count <= 0 || dev->lds_per_wg <= 0)
+        return fail(GEMM_ERR_INVALID_ARG, "device info missing, or without CUs or LDS");
+    gemm_config want;
+    memset(&want, 0, sizeof want);
+    int group_m = 8, xcd = 1;
+    static const int ladder[][2] = {{256, 128}, {128, 256}, {128, 128}};
+    bool picked = false;
+    for (const auto& t : ladder) {
+        if (2 * cdiv(prob->M, t[0]) * cdiv(prob->N, t[1]) >= dev->cu_count) {
+            want.bm = t[0];
+            want.bn = t[1];
+            picked = true;
+            break;
+        }
+    }
+    if (!picked) {
+        want.bm = 128;
+        want.bn = 128;
+    }
+    if (force) {
+        const gemm_config& f = *force;
+        if (f.group_m < 0 || f.xcd_remap < 0 || f.xcd_remap > 2)
+            return fail(GEMM_ERR_INVALID_ARG, "group_m must be >= 0 and xcd_remap one of 0, 1, 2");
+        if ((f.kernel && f.kernel != kKernelMx) || (f.splitk > 1) || (f.mfma && f.mfma != 32))
+            return fail(GEMM_ERR_UNSUPPORTED, "the block-scaled path runs kernel %d, mfma 32, splitk 1 only",
+                        kKernelMx);
+        if (f.bm || f.bn || f.stages || f.waves_m || f.waves_n || f.bk) {
+            want = f;
+            want.kernel = 0;
+            want.splitk = 0;
+        }
+        if (f.group_m) group_m = f.group_m;
+        if (f.xcd_remap) xcd = (f.xcd_remap == GEMM_XCD_ON);
+    }
+    const dtg::MxEntry* e = find_entry(want, prob, *dev);
+    if (!e)
+        return fail(GEMM_ERR_UNSUPPORTED,
+                    "no block-scaled kernel for bm=%d bn=%d bk=%d stages=%d waves=%dx%d, formats %d/%d, within "
+                    "%lld bytes of LDS",
+                    want.bm, want.bn, want.bk, want.stages, want.waves_m, want.waves_n, (int)prob->fmt_a,
+                    (int)prob->fmt_b, (long long)dev->lds_per_wg);
+    gemm_mx_plan* pl = new (std::nothrow) gemm_mx_plan;
+    if (!pl) return fail(GEMM_ERR_INVALID_ARG, "out of host memory");
+    pl->prob = *prob;
+    pl->dev = *dev;
+    pl->entry = e;
+    pl->num_pid_m = cdiv(prob->M, e->bm);
+    pl->num_pid_n = cdiv(prob->N, e->bn);
+    pl->grid = pl->num_pid_m * pl->num_pid_n;
+    if (pl->grid > kMaxDim) {
+        delete pl;
+        return fail(GEMM_ERR_UNSUPPORTED, "output too large for one launch");
+    }
+    gemm_config& c = pl->cfg;
+    memset(&c, 0, sizeof c);
+    c.kernel = kKernelMx;
+    c.bm = e->bm;
+    c.bn = e->bn;
+    c.bk = e->bk;
+    c.stages = e->stages;
+    c.mfma = e->mfma;
+    c.waves_m = e->waves_m;
+    c.waves_n = e->waves_n;
+    c.splitk = 1;
+    c.group_m = group_m < 1 ? 1 : group_m;
+    c.xcd_remap = (xcd && dev->xcd_count > 1) ? GEMM_XCD_ON : GEMM_XCD_OFF;
+    *out = pl;
+    return GEMM_OK;
+}
+
+bool overlaps(uintptr_t a0, uintptr_t a1, uintptr_t b0, uintptr_t b1) { return a0 < b1 && b0 < a1; }
+
+}  // namespace
+
+extern "C" {
+
+gemm_status gemm_mx_plan_create_for(const gemm_mx_problem* prob, const gemm_device_info* info,
+                                    const gemm_config* force, gemm_mx_plan** out) {
+    return plan_impl(prob, info, force, out);
+}
+
+gemm_status gemm_mx_plan_create(const gemm_mx_problem* prob, int device, const gemm_config* force,
+                                gemm_mx_plan** out) {
+    if (out) *out = nullptr;
+    gemm_status st = validate(prob);
+    if (st != GEMM_OK) return st;
+    gemm_device_info info;
+    st = dtg::cached_device_info(device, &info);
+    if (st != GEMM_OK) return st;
+    return plan_impl(prob, &info, force, out);
+}
+
+void gemm_mx_plan_destroy(gemm_mx_plan* plan) { delete plan; }
+
+gemm_status gemm_mx_plan_config(const gemm_mx_plan* plan, gemm_config* out) {
+    if (!plan || !out) return fail(GEMM_ERR_INVALID_ARG, "plan or out is NULL");
+    *out = plan->cfg;
+    return GEMM_OK;
+}
+
+gemm_status gemm_mx_plan_launch(const gemm_mx_plan* plan, int64_t* grid, int32_t* threads, int64_t* lds) {
+    if (!plan) return fail(GEMM_ERR_INVALID_ARG, "plan is NULL");
+    if (grid) *grid = plan->grid;
+    if (threads) *threads = plan->entry->threads;
+    if (lds) *lds = plan->entry->lds_bytes;
+    return GEMM_OK;
+}
+
+gemm_status gemm_mx_plan_describe(const gemm_mx_plan* plan, char* buf, size_t len) {
+    if (!plan || !buf || len == 0) return fail(GEMM_ERR_INVALID_ARG, "plan or buf is NULL");
+    const gemm_config& c = plan->cfg;
+    snprintf(buf, len,
+             "kernel=%s bm=%d bn=%d bk=%d stages=%d mfma=%d waves=%dx%d group_m=%d splitk=%d xcd_remap=%d "
+             "grid=%lld threads=%d lds=%lld fmt=%d/%d out=%d",
+             plan->entry->name, c.bm, c.bn, c.bk, c.stages, c.mfma, c.waves_m, c.waves_n, c.group_m, c.splitk,
+             c.xcd_remap, (long long)plan->grid, plan->entry->threads, (long long)plan->entry->lds_bytes,
+             (int)plan->prob.fmt_a, (int)plan->prob.fmt_b, (int)plan->prob.out);
+    return GEMM_OK;
+}
+
+gemm_status gemm_mx_run(const gemm_mx_plan* plan, const void* A, const void* SA, const void* B, const void* SB,
+                        const void* C, void* D, void* stream) {
+    if (!plan) return fail(GEMM_ERR_INVALID_ARG, "plan is NULL");
+    const gemm_mx_problem& p = plan->prob;
+    if (p.has_c && !C) return fail(GEMM_ERR_INVALID_ARG, "problem has C but C is NULL");
+    if (!p.has_c && C) return fail(GEMM_ERR_INVALID_ARG, "C given but the problem has has_c = 0");
+    if (p.M == 0 || p.N == 0) return GEMM_OK;
+    if (!D) return fail(GEMM_ERR_INVALID_ARG, "D is NULL");
+    const int esz = p.out == GEMM_MX_OUT_F32 ? 4 : 2;
+    if (reinterpret_cast<uintptr_t>(D) % esz || (C && reinterpret_cast<uintptr_t>(C) % esz))
+        return fail(GEMM_ERR_UNSUPPORTED, "C and D must be aligned to their element size");
+    const uintptr_t d0 = reinterpret_cast<uintptr_t>(D);
+    const uintptr_t d1 = d0 + static_cast<uintptr_t>(((p.M - 1) * p.ldd + p.N) * esz);
+    if (p.K > 0) {
+        if (!A || !B || !SA || !SB) return fail(GEMM_ERR_INVALID_ARG, "A, SA, B or SB is NULL");
+        if ((reinterpret_cast<uintptr_t>(A) & 15) || (reinterpret_cast<uintptr_t>(B) & 15))
+            return fail(GEMM_ERR_UNSUPPORTED, "A and B must be 16-byte aligned");
+        if ((reinterpret_cast<uintptr_t>(SA) & 3) || (reinterpret_cast<uintptr_t>(SB) & 3))
+            return fail(GEMM_ERR_UNSUPPORTED, "SA and SB must be 4-byte aligned");
+        const int64_t kb = row_bytes(&p);
+        const struct { const void* ptr; int64_t bytes; const char* name; } in[4] = {
+            {A, (p.M - 1) * p.lda + kb, "A"},
+            {B, (p.N - 1) * p.ldb + kb, "B"},
+            {SA, p.M * p.ldsa, "SA"},
+            {SB, p.N * p.ldsb, "SB"}};
+        for (const auto& x : in) {
+            const uintptr_t x0 = reinterpret_cast<uintptr_t>(x.ptr);
+            if (overlaps(d0, d1, x0, x0 + static_cast<uintptr_t>(x.bytes)))
+                return fail(GEMM_ERR_INVALID_ARG, "D overlaps %s", x.name);
+        }
+    }
+    if (p.has_c) {
+        const uintptr_t c0 = reinterpret_cast<uintptr_t>(C);
+        const uintptr_t c1 = c0 + static_cast<uintptr_t>(((p.M - 1) * p.ldc + p.N) * esz);
+        const bool same = (C == D) && (p.ldc == p.ldd || p.M == 1);
+        if (!same && overlaps(d0, d1, c0, c1))
+            return fail(GEMM_ERR_INVALID_ARG, "D overlaps C (only D == C with equal strides is allowed)");
+    }
+    dtg::MxArgs a;
+    a.A = static_cast<const uint8_t*>(A);
+    a.B = static_cast<const uint8_t*>(B);
+    a.SA = static_cast<const uint8_t*>(SA);
+    a.SB = static_cast<const uint8_t*>(SB);
+    a.C = C;
+    a.D = D;
+    a.M = static_cast<int32_t>(p.M);
+    a.N = static_cast<int32_t>(p.N);
+    a.K = static_cast<int32_t>(p.K);
+    a.num_pid_m = static_cast<int32_t>(plan->num_pid_m);
+    a.num_pid_n = static_cast<int32_t>(plan->num_pid_n);
+    a.group_m = plan->cfg.group_m;
+    a.xcds = (plan->cfg.xcd_remap == GEMM_XCD_ON) ? plan->dev.xcd_count : 1;
+    a.has_c = p.has_c;
+    a.out = static_cast<int32_t>(p.out);
+    a.lda = p.lda;
+    a.ldb = p.ldb;
+    a.ldsa = p.ldsa;
+    a.ldsb = p.ldsb;
+    a.ldc = p.has_c ? p.ldc : 0;
+    a.ldd = p.ldd;
+    hipError_t err = plan->entry->launch(a, plan->grid, static_cast<hipStream_t>(stream));
+    if (err != hipSuccess)
+        return fail(GEMM_ERR_HIP, "launch of %s: %s", plan->entry->name, hipGetErrorString(err));
+    return GEMM_OK;
+}
+
+}  // extern "C"

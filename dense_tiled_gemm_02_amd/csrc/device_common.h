@@ -126,12 +126,27 @@ __device__ __forceinline__ i16x4 lds_read_tr(uint32_t addr) {
     return v;
 }
 
+// 2-byte (zero-extended) and 4-byte reads at addr + OFF.
+template <int OFF>
+__device__ __forceinline__ uint32_t lds_read_u16(uint32_t addr) {
+    uint32_t v;
+    asm volatile("ds_read_u16 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
+    return v;
+}
+template <int OFF>
+__device__ __forceinline__ uint32_t lds_read_b32(uint32_t addr) {
+    uint32_t v;
+    asm volatile("ds_read_b32 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
+    return v;
+}
+
 __device__ __forceinline__ void lds_wait_all() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 // Make `v` depend on the preceding lds_wait_all() (volatile asm keeps its
 // order), so no use of v is scheduled before the wait.
 __device__ __forceinline__ void tie(u32x4& v) { asm volatile("" : "+v"(v)); }
 __device__ __forceinline__ void tie(i16x4& v) { asm volatile("" : "+v"(v)); }
+__device__ __forceinline__ void tie(uint32_t& v) { asm volatile("" : "+v"(v)); }
 
 __device__ __forceinline__ uint32_t lds_addr(const uint16_t* p) {
     return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) uint16_t*)p));

@@ -1,0 +1,491 @@
+// Block-scaled (MX) tiled GEMM for gfx950:  D = A x B (+ C), where A and B
+// hold 8-bit (E4M3, E5M2) or 4-bit (E2M1) floating-point elements and every 32
+// consecutive k of a row of A (of a column of B) share one E8M0 power-of-two
+// scale.  The scaled matrix instruction of gfx950 (v_mfma_scale_f32_32x32x64
+// _f8f6f4) applies the scales inside the contraction ("Tuning Triton
+// kernels", section 6: the gfx950 instruction set adds a scaled MFMA as the
+// way to the microscaled types; the FP4 x FP4 kernel of the same section runs
+// on it), so the kernel is the direct-to-LDS tile kernel of gemm_dma_kernel.h
+// with wider elements and a scale pipeline beside the operand pipeline:
+//
+//  * both operands are k-contiguous (A row-major M x K, B stored N x K, the
+//    block runs along k in both), kept in LDS as rows of 128 bytes of k per
+//    K step (128 k of an 8-bit format, 256 k of E2M1), with the same XOR chunk
+//    swizzle and direct global -> LDS loads (masked lanes read zeros);
+//  * the scales of a K step (4 or 8 per row) are loaded the same way, 4 bytes
+//    per lane, into an LDS scale tile [row][block] per stage;
+//  * operand lane layouts of the 32x32x64 instruction (pinned by the probe
+//    tests): lane l = r + 32 g holds row (column) r; an 8-bit operand holds
+//    k = 16 g .. 16 g + 15 in its first 16 bytes and k = 32 + 16 g .. in the
+//    next 16, a 4-bit operand k = 32 g .. 32 g + 31 in its 16 bytes; the scale
+//    of row r and of the instruction's 32-k block b is taken from byte
+//    `opsel` of lane r + 32 b's scale register.  The kernel feeds the
+//    instruction of k sub-step ks the K step's blocks ks and NKS + ks (8-bit;
+//    block h of the instruction is block h * NKS + ks of the K step) or
+//    g * NKS + ks (4-bit), so lane g's scales for the NKS sub-steps are NKS
+//    consecutive bytes of its row: one 2- or 4-byte LDS read per fragment per
+//    K step, sub-step ks selecting byte ks;
+//  * scales of blocks past ceil(K / 32) (the end of the last K step) are
+//    replaced by 1.0 in registers: their elements are zero (masked loads) and
+//    whatever bytes sit there must not inject a NaN.
+//
+// The operand order is swapped (B fragment first) so each accumulator holds
+// the transposed block and a lane's registers are 4 consecutive columns of one
+// output row.  K steps past the end of K are loaded from an empty range, so
+// every step of the software pipeline is uniform.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "device_common.h"
+#include "kernels_mx.h"
+#include "tile_order.h"
+
+namespace dtg {
+namespace {
+
+using namespace dev;
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// One scaled 32x32x64 instruction: c += (x scaled by sx) x (y scaled by sy)^T,
+// formats FX / FY, scale bytes OPS of sx and sy.
+template <int FX, int FY, int OPS>
+__device__ __forceinline__ f32x16 mfma_mx(i32x8 x, i32x8 y, int sx, int sy, f32x16 c) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(x, y, c, FX, FY, OPS, sx, OPS, sy);
+}
+
+// 8-bit operand: two 16-byte halves; 4-bit operand: one (the upper 4 dwords
+// of the register tuple are not read).
+__device__ __forceinline__ i32x8 operand(const u32x4 (&h)[2]) {
+    return __builtin_shufflevector(__builtin_bit_cast(i32x4, h[0]), __builtin_bit_cast(i32x4, h[1]), 0, 1, 2, 3,
+                                   4, 5, 6, 7);
+}
+__device__ __forceinline__ i32x8 operand(const u32x4 (&h)[1]) {
+    const i32x4 v = __builtin_bit_cast(i32x4, h[0]);
+    return __builtin_shufflevector(v, v, 0, 1, 2, 3, -1, -1, -1, -1);
+}
+
+template <bool BF16>
+__device__ __forceinline__ void store4_16(uint16_t* d, const uint16_t* c, bool vec, int n_ok, const float (&v)[4]) {
+    float w[4] = {v[0], v[1], v[2], v[3]};
+    if (vec) {
+        if (c) {
+            const uint2 cv = *reinterpret_cast<const uint2*>(c);
+            w[0] += widen<BF16>(static_cast<uint16_t>(cv.x & 0xffffu));
+            w[1] += widen<BF16>(static_cast<uint16_t>(cv.x >> 16));
+            w[2] += widen<BF16>(static_cast<uint16_t>(cv.y & 0xffffu));
+            w[3] += widen<BF16>(static_cast<uint16_t>(cv.y >> 16));
+        }
+        uint2 dv;
+        dv.x = static_cast<uint32_t>(narrow<BF16>(w[0])) | (static_cast<uint32_t>(narrow<BF16>(w[1])) << 16);
+        dv.y = static_cast<uint32_t>(narrow<BF16>(w[2])) | (static_cast<uint32_t>(narrow<BF16>(w[3])) << 16);
+        *reinterpret_cast<uint2*>(d) = dv;
+    } else {
+        for (int r = 0; r < 4; ++r)
+            if (r < n_ok) d[r] = narrow<BF16>(c ? w[r] + widen<BF16>(c[r]) : w[r]);
+    }
+}
+
+__device__ __forceinline__ void store4_32(float* d, const float* c, bool vec, int n_ok, const float (&v)[4]) {
+    if (vec) {
+        f32x4 w = {v[0], v[1], v[2], v[3]};
+        if (c) w += *reinterpret_cast<const f32x4*>(c);
+        *reinterpret_cast<f32x4*>(d) = w;
+    } else {
+        for (int r = 0; r < 4; ++r)
+            if (r < n_ok) d[r] = c ? v[r] + c[r] : v[r];
+    }
+}
+
+template <int BM, int BN, int WM, int WN, int ST, int FA, int FB>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_mx_kernel(MxArgs p) {
+    constexpr int NW = WM * WN;
+    constexpr int TM = BM / WM, TN = BN / WN;
+    constexpr int FM = TM / 32, FN = TN / 32;
+    constexpr int EB = (FA == kMxE2M1) ? 4 : 8;       // element bits (both operands)
+    static_assert((FA == kMxE2M1) == (FB == kMxE2M1), "A and B elements of one width");
+    constexpr int ROWB = 128;                          // bytes of k per row and K step
+    constexpr int BKE = ROWB * 8 / EB;                 // k per K step
+    constexpr int NKS = BKE / 64;                      // instructions (k sub-steps) per K step
+    constexpr int NBLK = BKE / 32;                     // scale blocks per K step
+    constexpr int FR = (EB == 8) ? 2 : 1;              // 16-byte LDS reads per fragment per sub-step
+    constexpr int R = 8;                               // LDS rows per load instruction (8 chunks each)
+    constexpr int IA_W = BM / R / NW, IB_W = BN / R / NW;
+    static_assert(BM % (R * NW) == 0 && BN % (R * NW) == 0, "load split");
+    static_assert(TM % 32 == 0 && TN % 32 == 0, "tile vs wave grid");
+    // scale loads: 64 lanes x 4 bytes = 256 bytes of [row][NBLK] per instruction
+    constexpr int SRPI = 256 / NBLK;                   // scale rows per instruction
+    constexpr int SIA = BM / SRPI, SIB = BN / SRPI, SI = SIA + SIB;
+    static_assert(BM % SRPI == 0 && BN % SRPI == 0, "scale split");
+    constexpr int NSL = (SI + NW - 1) / NW;            // scale loads per wave (some may be empty)
+    constexpr int L = IA_W + IB_W + NSL;               // loads per wave per K step
+    static_assert(ST >= 2 && ST <= 4 && (ST - 1) * L < 64, "stages");
+
+    constexpr int SA_B = BM * ROWB, SB_B = BN * ROWB;  // bytes per stage
+    constexpr int SSA_B = BM * NBLK, SSB_B = BN * NBLK;
+    constexpr int OFF_B = ST * SA_B;
+    constexpr int OFF_S = ST * (SA_B + SB_B);
+    constexpr int OFF_SB = OFF_S + ST * SSA_B;
+    constexpr int OFF_DUMMY = OFF_SB + ST * SSB_B;
+    constexpr int LDS_BYTES = OFF_DUMMY + 256;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS_BYTES];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / WN, wn = wave % WN;
+
+    int pid_m, pid_n;
+    tile_of_workgroup<int>(blockIdx.x, p.num_pid_m, p.num_pid_n, p.group_m, p.xcds, &pid_m, &pid_n);
+    const int m0 = pid_m * BM, n0 = pid_n * BN;
+    const int M = p.M, N = p.N, K = p.K;
+    const int kbytes = K / (8 / EB);                   // K is a multiple of the 16-byte chunk
+    const int nblocks = (K + 31) / 32;
+    const bool edge = (m0 + BM > M) || (n0 + BN > N);
+
+    // ---- per-lane operand load offsets: load X of an operand fills LDS rows
+    // X*NW*R + wave*R + lane/8 with the lane's 16-byte chunk lane % 8 of the
+    // row; the lane fetches the chunk that the swizzle puts there.
+    const int ld_row = wave * R + lane / 8;
+    const int ld_chunk = (lane % 8) ^ swz<8>(ld_row);
+    const uint32_t a_voff = static_cast<uint32_t>(static_cast<int64_t>(ld_row) * p.lda + ld_chunk * 16);
+    const uint32_t b_voff = static_cast<uint32_t>(static_cast<int64_t>(ld_row) * p.ldb + ld_chunk * 16);
+    const uint32_t a_step = static_cast<uint32_t>(NW * R) * static_cast<uint32_t>(p.lda);
+    const uint32_t b_step = static_cast<uint32_t>(NW * R) * static_cast<uint32_t>(p.ldb);
+    // scale loads: instruction si = s * NW + wave covers SRPI rows of A's
+    // (si < SIA) or B's scale tile; lane -> (row, dword)
+    constexpr int DPR = NBLK / 4;                      // dwords per scale row
+    uint32_t s_voff[NSL];
+    int s_row[NSL];
+#pragma unroll
+    for (int s = 0; s < NSL; ++s) {
+        const int si = s * NW + wave;
+        const int rr = (si < SIA ? si : si - SIA) * SRPI + lane / DPR;
+        s_row[s] = rr;
+        s_voff[s] = static_cast<uint32_t>(static_cast<int64_t>(rr) * (si < SIA ? p.ldsa : p.ldsb) + 4 * (lane % DPR));
+    }
+
+    const uint32_t smem0 = lds_addr(reinterpret_cast<const uint16_t*>(smem));
+
+    struct Desc {
+        __amdgpu_buffer_rsrc_t ra, rb, rsa, rsb;
+        int kb0;      // first byte of k of this step
+        bool chk;
+    };
+    const int nkt = (K + BKE - 1) / BKE;
+    const int nfull = K / BKE;
+    auto make_desc = [&](int kt) {
+        Desc d;
+        d.kb0 = kt * ROWB;
+        const bool live = kt < nkt;
+        const int kb = live ? d.kb0 : 0;
+        const int sb = live ? kt * NBLK : 0;
+        d.ra = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p.A + static_cast<int64_t>(m0) * p.lda + kb), 0,
+                                                 live ? clamp_records(static_cast<int64_t>(M - 1 - m0) * p.lda +
+                                                                      (kbytes - d.kb0))
+                                                      : 0u,
+                                                 kRsrcWord3);
+        d.rb = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p.B + static_cast<int64_t>(n0) * p.ldb + kb), 0,
+                                                 live ? clamp_records(static_cast<int64_t>(N - 1 - n0) * p.ldb +
+                                                                      (kbytes - d.kb0))
+                                                      : 0u,
+                                                 kRsrcWord3);
+        // scale rows are read whole up to their row stride (a multiple of 4)
+        d.rsa = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint8_t*>(p.SA + static_cast<int64_t>(m0) * p.ldsa + sb), 0,
+            live ? clamp_records(static_cast<int64_t>(M - m0) * p.ldsa - sb) : 0u, kRsrcWord3);
+        d.rsb = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint8_t*>(p.SB + static_cast<int64_t>(n0) * p.ldsb + sb), 0,
+            live ? clamp_records(static_cast<int64_t>(N - n0) * p.ldsb - sb) : 0u, kRsrcWord3);
+        d.chk = edge || kt >= nfull;
+        return d;
+    };
+    // Load number X of a K step into stage s: A's operand loads, B's, then the scale loads.
+    auto load_op = [&](auto x_tag, const Desc& d, int s) {
+        constexpr int X = decltype(x_tag)::value;
+        if constexpr (X < IA_W + IB_W) {
+            constexpr bool IS_A = X < IA_W;
+            constexpr int Y = IS_A ? X : X - IA_W;
+            uint32_t v = IS_A ? a_voff : b_voff;
+            const uint32_t so = Y * (IS_A ? a_step : b_step);
+            if (d.chk) {
+                const int row = ld_row + Y * NW * R;
+                const bool ok = (IS_A ? m0 + row < M : n0 + row < N) && d.kb0 + ld_chunk * 16 < kbytes;
+                v = ok ? v : kOOB;
+            }
+            // (a non-const local: clang's host pass drops the kernel when the
+            // builtin is handed a member of a const reference)
+            __amdgpu_buffer_rsrc_t r = IS_A ? d.ra : d.rb;
+            const int dst = (IS_A ? s * SA_B : OFF_B + s * SB_B) + (Y * NW + wave) * 1024;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(smem + dst), 16, v, so, 0, 0);
+        } else {
+            constexpr int S = X - IA_W - IB_W;
+            const int si = S * NW + wave;
+            __amdgpu_buffer_rsrc_t r = si < SIA ? d.rsa : d.rsb;
+            const bool in_rows = si < SIA ? m0 + s_row[S] < M : n0 + s_row[S] < N;
+            uint32_t v = (si < SI && in_rows) ? s_voff[S] : kOOB;
+            const int dst = si < SIA ? OFF_S + s * SSA_B + si * 256
+                            : si < SI ? OFF_SB + s * SSB_B + (si - SIA) * 256
+                                      : OFF_DUMMY;   // no row left for this wave: zeros into a scratch slot
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(smem + dst), 4, v, 0, 0, 0);
+        }
+    };
+    auto issue_tile = [&](int kt, int s) {
+        const Desc d = make_desc(kt);
+        static_for<L>([&](auto x_tag) { load_op(x_tag, d, s); });
+    };
+
+    f32x16 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    // ---- per-lane read addresses.  Fragment f of a wave covers rows
+    // w*T + 32 f .. + 31 (its offset 32 f * 128 bytes goes into the read's
+    // offset field, with the stage offset); lane l reads row l % 32 at the
+    // chunk of sub-step ks and half h: 8-bit: block h*NKS + ks, bytes
+    // 16 g .. 16 g + 15 of it (chunk 2 (h NKS + ks) + g); 4-bit: block
+    // g NKS + ks (chunk g NKS + ks).
+    const int g = lane / 32;
+    const int fr = lane % 32;
+    uint32_t a_addr[NKS][FR], b_addr[NKS][FR];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+        for (int h = 0; h < FR; ++h) {
+            const int c = (EB == 8) ? 2 * (h * NKS + ks) + g : g * NKS + ks;
+            const int pc = (c ^ swz<8>(fr)) * 16;
+            a_addr[ks][h] = smem0 + (wm * TM + fr) * ROWB + pc;
+            b_addr[ks][h] = smem0 + OFF_B + (wn * TN + fr) * ROWB + pc;
+        }
+    const uint32_t sa_addr = smem0 + OFF_S + (wm * TM + fr) * NBLK + g * NKS;
+    const uint32_t sb_addr = smem0 + OFF_SB + (wn * TN + fr) * NBLK + g * NKS;
+    static_assert((ST - 1) * SA_B + (FM - 1) * 32 * ROWB < 65536 && (ST - 1) * SB_B + (FN - 1) * 32 * ROWB < 65536,
+                  "stage and fragment offsets fit the read's offset field");
+
+    u32x4 fa[2][FM][FR], fb[2][FN][FR];
+    uint32_t ssa[2][FM], ssb[2][FN];
+    constexpr int NRF = (FM + FN) * FR;               // operand reads per sub-step
+    constexpr int NRS = FM + FN;                      // scale reads per K step
+
+    // LDS read R of sub-step KS of stage S into fragment slot SL (scales: tile slot TS).
+    auto read_op = [&](auto stage_tag, auto ks_tag, auto slot_tag, auto ts_tag, auto r_tag) {
+        constexpr int S = decltype(stage_tag)::value;
+        constexpr int KS = decltype(ks_tag)::value;
+        constexpr int SL = decltype(slot_tag)::value;
+        constexpr int TS = decltype(ts_tag)::value;
+        constexpr int RR = decltype(r_tag)::value;
+        if constexpr (RR < FN * FR) {
+            constexpr int J = RR / FR, H = RR % FR;
+            fb[SL][J][H] = lds_read16<S * SB_B + J * 32 * ROWB>(b_addr[KS][H]);
+        } else if constexpr (RR < NRF) {
+            constexpr int I = (RR - FN * FR) / FR, H = (RR - FN * FR) % FR;
+            fa[SL][I][H] = lds_read16<S * SA_B + I * 32 * ROWB>(a_addr[KS][H]);
+        } else if constexpr (RR - NRF < FN) {
+            constexpr int J = RR - NRF;
+            if constexpr (NKS == 2) ssb[TS][J] = lds_read_u16<S * SSB_B + J * 32 * NBLK>(sb_addr);
+            else ssb[TS][J] = lds_read_b32<S * SSB_B + J * 32 * NBLK>(sb_addr);
+        } else {
+            constexpr int I = RR - NRF - FN;
+            if constexpr (NKS == 2) ssa[TS][I] = lds_read_u16<S * SSA_B + I * 32 * NBLK>(sa_addr);
+            else ssa[TS][I] = lds_read_b32<S * SSA_B + I * 32 * NBLK>(sa_addr);
+        }
+    };
+    auto wait_frags = [&](auto slot_tag) {
+        constexpr int SL = decltype(slot_tag)::value;
+        lds_wait_all();
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int h = 0; h < FR; ++h) tie(fb[SL][j][h]);
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int h = 0; h < FR; ++h) tie(fa[SL][i][h]);
+    };
+    // Scales of tile kt (slot TS), after their reads landed: bytes of blocks
+    // at or past ceil(K / 32) become 127 (2^0).
+    auto mask_scales = [&](auto ts_tag, int kt) {
+        constexpr int TS = decltype(ts_tag)::value;
+        const int v = nblocks - kt * NBLK - g * NKS;    // valid bytes of this lane's NKS
+        const uint32_t keep = v >= NKS ? 0xffffffffu : v <= 0 ? 0u : (1u << (8 * v)) - 1u;
+        const uint32_t fill = 0x7f7f7f7fu & ~keep;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) { tie(ssb[TS][j]); ssb[TS][j] = (ssb[TS][j] & keep) | fill; }
+#pragma unroll
+        for (int i = 0; i < FM; ++i) { tie(ssa[TS][i]); ssa[TS][i] = (ssa[TS][i] & keep) | fill; }
+    };
+    auto mfma_op = [&](auto slot_tag, auto ts_tag, auto ks_tag, auto q_tag) {
+        constexpr int SL = decltype(slot_tag)::value;
+        constexpr int TS = decltype(ts_tag)::value;
+        constexpr int KS = decltype(ks_tag)::value;
+        constexpr int Q = decltype(q_tag)::value;
+        constexpr int I = Q / FN, J = Q % FN;
+        acc[I][J] = mfma_mx<FB, FA, KS>(operand(fb[SL][J]), operand(fa[SL][I]), static_cast<int>(ssb[TS][J]),
+                                        static_cast<int>(ssa[TS][I]), acc[I][J]);
+    };
+    constexpr int NQ = FM * FN;
+
+    // The MFMAs of a sub-step with NOPS memory operations spread between them
+    // (operation o after MFMA o * SP; the last NQ/4 MFMAs carry none).
+    auto interleave = [&](auto slot_tag, auto ts_tag, auto ks_tag, auto nops_tag, auto&& op) {
+        constexpr int NOPS = decltype(nops_tag)::value;
+        constexpr int TAIL = NQ / 4;
+        constexpr int SP = (NOPS == 0) ? 1 : ((NQ - TAIL) / NOPS > 0 ? (NQ - TAIL) / NOPS : 1);
+        static_for<NQ>([&](auto q_tag) {
+            constexpr int Q = decltype(q_tag)::value;
+            mfma_op(slot_tag, ts_tag, ks_tag, q_tag);
+            if constexpr (Q % SP == 0 && Q / SP < NOPS) op(std::integral_constant<int, Q / SP>{});
+            __builtin_amdgcn_sched_barrier(0);
+        });
+        if constexpr (NOPS > NQ / SP) {
+            static_for<NOPS - NQ / SP>([&](auto o_tag) {
+                op(std::integral_constant<int, NQ / SP + decltype(o_tag)::value>{});
+            });
+        }
+    };
+
+    // One K step (tile kt) on stage S = U % ST, tile slot U % 2; sub-step ks
+    // uses fragment slot (U NKS + ks) % 2.  The last sub-step waits for tile
+    // kt + 1, passes the barrier, and runs its MFMAs with the reads of tile
+    // kt + 1 (its first sub-step's fragments and its scales) and the loads of
+    // tile kt + ST into this stage between them.
+    auto step = [&](auto u_tag, int kt) {
+        constexpr int U = decltype(u_tag)::value;
+        constexpr int S = U % ST, S1 = (U + 1) % ST;
+        constexpr int TS = U % 2, TS1 = (U + 1) % 2;
+        static_for<NKS>([&](auto ks_tag) {
+            constexpr int KS = decltype(ks_tag)::value;
+            constexpr int CUR = (U * NKS + KS) & 1, NXT = CUR ^ 1;
+            const auto cur = std::integral_constant<int, CUR>{};
+            const auto nxt = std::integral_constant<int, NXT>{};
+            const auto ts = std::integral_constant<int, TS>{};
+            if constexpr (KS + 1 < NKS) {
+                interleave(cur, ts, ks_tag, std::integral_constant<int, NRF>{}, [&](auto o_tag) {
+                    read_op(std::integral_constant<int, S>{}, std::integral_constant<int, KS + 1>{}, nxt, ts, o_tag);
+                });
+                wait_frags(nxt);
+            } else {
+                const Desc d = make_desc(kt + ST);
+                wait_vm<(ST - 2) * L>();
+                __builtin_amdgcn_s_barrier();
+                interleave(cur, ts, ks_tag, std::integral_constant<int, NRF + NRS + L>{}, [&](auto o_tag) {
+                    constexpr int O = decltype(o_tag)::value;
+                    if constexpr (O < NRF + NRS)
+                        read_op(std::integral_constant<int, S1>{}, std::integral_constant<int, 0>{}, nxt,
+                                std::integral_constant<int, TS1>{}, o_tag);
+                    else
+                        load_op(std::integral_constant<int, O - NRF - NRS>{}, d, S);
+                });
+                wait_frags(nxt);
+                mask_scales(std::integral_constant<int, TS1>{}, kt + 1);
+            }
+        });
+    };
+
+    constexpr int UNROLL = (ST % 2 == 0) ? ST : 2 * ST;   // stage, fragment and tile slots repeat
+    if (nkt > 0) {
+        static_for<ST>([&](auto t_tag) { issue_tile(decltype(t_tag)::value, decltype(t_tag)::value); });
+        wait_vm<(ST - 1) * L>();
+        __builtin_amdgcn_s_barrier();
+        static_for<NRF + NRS>([&](auto r_tag) {
+            read_op(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{},
+                    std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, r_tag);
+        });
+        wait_frags(std::integral_constant<int, 0>{});
+        mask_scales(std::integral_constant<int, 0>{}, 0);
+        for (int j = 0; j < nkt; j += UNROLL) {
+            static_for<UNROLL>([&](auto u_tag) {
+                if (j + decltype(u_tag)::value < nkt) step(u_tag, j + decltype(u_tag)::value);
+            });
+        }
+        // no load may still be writing this workgroup's LDS when it exits
+        wait_vm<0>();
+    }
+
+    // ---- epilogue: + C in fp32, round to the output type, masked store.
+    // Lane l holds, per block (i, j), row l % 32 and, for q = 0..3, columns
+    // 8 q + 4 (l / 32) + 0..3 in registers 4 q .. 4 q + 3.
+    const bool has_c = p.has_c != 0;
+    const int out = p.out;
+    const int esz = out == 2 ? 4 : 2;
+    const int vq = out == 2 ? 4 : 4;   // elements per vector store
+    const bool dvec = (p.ldd % vq == 0) && (reinterpret_cast<uintptr_t>(p.D) % (vq * esz) == 0);
+    const bool cvec = !has_c || ((p.ldc % vq == 0) && (reinterpret_cast<uintptr_t>(p.C) % (vq * esz) == 0));
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+        const int row = m0 + wm * TM + i * 32 + fr;
+        if (row >= M) continue;
+        const int64_t drow = static_cast<int64_t>(row) * p.ldd;
+        const int64_t crow = static_cast<int64_t>(row) * p.ldc;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int col = n0 + wn * TN + j * 32 + 8 * q + 4 * g;
+                if (col >= N) continue;
+                float v[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) v[r] = acc[i][j][4 * q + r];
+                const bool vec = dvec && cvec && col + 4 <= N;
+                const int n_ok = N - col;
+                if (out == 2) {
+                    store4_32(static_cast<float*>(p.D) + drow + col,
+                              has_c ? static_cast<const float*>(p.C) + crow + col : nullptr, vec, n_ok, v);
+                } else if (out == 1) {
+                    store4_16<true>(static_cast<uint16_t*>(p.D) + drow + col,
+                                    has_c ? static_cast<const uint16_t*>(p.C) + crow + col : nullptr, vec, n_ok, v);
+                } else {
+                    store4_16<false>(static_cast<uint16_t*>(p.D) + drow + col,
+                                     has_c ? static_cast<const uint16_t*>(p.C) + crow + col : nullptr, vec, n_ok, v);
+                }
+            }
+        }
+    }
+}
+
+template <int BM, int BN, int WM, int WN, int ST, int FA, int FB>
+hipError_t launch_mx(const MxArgs& a, int64_t grid, hipStream_t stream) {
+    hipLaunchKernelGGL((gemm_mx_kernel<BM, BN, WM, WN, ST, FA, FB>), dim3(static_cast<unsigned>(grid)),
+                       dim3(64 * WM * WN), 0, stream, a);
+    return hipGetLastError();
+}
+
+constexpr int64_t mx_lds(int bm, int bn, int st, int fa) {
+    return static_cast<int64_t>(st) * (bm + bn) * 128 + static_cast<int64_t>(st) * (bm + bn) * (fa == kMxE2M1 ? 8 : 4) +
+           256;
+}
+
+#define DTG_STR2(x) #x
+#define DTG_STR(x) DTG_STR2(x)
+#define MX_ENTRY(BM, BN, WM, WN, ST, FA, FB)                                                                    \
+    {BM, BN, (FA == kMxE2M1 ? 256 : 128), ST, 32, WM, WN, FA, FB, 64 * WM * WN, mx_lds(BM, BN, ST, FA),      \
+     &launch_mx<BM, BN, WM, WN, ST, FA, FB>,                                                                   \
+     "gemm_mx_kernel<" DTG_STR(BM) "," DTG_STR(BN) "," DTG_STR(WM) "," DTG_STR(WN) "," DTG_STR(ST) ","        \
+     DTG_STR(FA) "," DTG_STR(FB) ">"}
+#define MX_FORMATS(BM, BN, WM, WN, ST)                                                                       \
+    MX_ENTRY(BM, BN, WM, WN, ST, 0, 0), MX_ENTRY(BM, BN, WM, WN, ST, 1, 1), MX_ENTRY(BM, BN, WM, WN, ST, 0, 1), \
+    MX_ENTRY(BM, BN, WM, WN, ST, 1, 0), MX_ENTRY(BM, BN, WM, WN, ST, 4, 4)
+
+// (a 256 x 256 tile needs more than the 256 registers a lane has at two
+// waves per SIMD: 128 accumulators plus two slots of 8-bit fragments)
+const MxEntry kMxTable[] = {
+    MX_FORMATS(256, 128, 4, 2, 2),
+    MX_FORMATS(128, 256, 2, 4, 2),
+    MX_FORMATS(128, 128, 2, 2, 3),
+};
+
+}  // namespace
+
+const MxEntry* mx_kernel_table(int* count) {
+    *count = static_cast<int>(sizeof(kMxTable) / sizeof(kMxTable[0]));
+    return kMxTable;
+}
+
+}  // namespace dtg

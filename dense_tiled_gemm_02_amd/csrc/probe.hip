@@ -65,6 +65,35 @@ __global__ __launch_bounds__(64) void probe_mfma_kernel(const uint16_t* A, const
     }
 }
 
+// One scaled matrix instruction (v_mfma_scale_f32_{16x16x128,32x32x64}_f8f6f4)
+// on raw per-lane registers: lane l supplies a[8l..8l+7] and b[8l..8l+7] as
+// its A and B operand registers (only the first 4 dwords are used for the
+// 4-bit format), sa[l] and sb[l] as its scale registers, of which the byte
+// selected by OSA / OSB is the scale; the accumulator starts at zero and
+// lane l's result registers go to out[R l .. R l + R - 1] (R = 4 or 16).
+// Format codes FA / FB: 0 E4M3, 1 E5M2, 4 E2M1.
+template <int MF, int FA, int FB, int OSA, int OSB>
+__global__ __launch_bounds__(64) void probe_mfma_scaled_kernel(const uint32_t* a, const uint32_t* b,
+                                                               const uint32_t* sa, const uint32_t* sb, float* out) {
+    typedef int i32x8 __attribute__((ext_vector_type(8)));
+    const int l = threadIdx.x;
+    i32x8 av, bv;
+    for (int d = 0; d < 8; ++d) {
+        av[d] = static_cast<int>(a[8 * l + d]);
+        bv[d] = static_cast<int>(b[8 * l + d]);
+    }
+    const int s_a = static_cast<int>(sa[l]), s_b = static_cast<int>(sb[l]);
+    if constexpr (MF == 16) {
+        f32x4 c = {0, 0, 0, 0};
+        c = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, FA, FB, OSA, s_a, OSB, s_b);
+        for (int r = 0; r < 4; ++r) out[4 * l + r] = c[r];
+    } else {
+        f32x16 c = {};
+        c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, c, FA, FB, OSA, s_a, OSB, s_b);
+        for (int r = 0; r < 16; ++r) out[16 * l + r] = c[r];
+    }
+}
+
 __global__ __launch_bounds__(64) void probe_lds_read_tr_kernel(const uint16_t* in, uint16_t* out) {
     __shared__ __attribute__((aligned(16))) uint16_t lds[512];
     const int l = threadIdx.x;
@@ -580,6 +609,30 @@ int probe_mfma(int mf, int dtype, const uint16_t* A, const uint16_t* B, float* D
     else if (mf == 32 && dtype == 0) hipLaunchKernelGGL((probe_mfma_kernel<32, false>), dim3(1), dim3(64), 0, s, A, B, D);
     else return static_cast<int>(hipErrorInvalidValue);
     return static_cast<int>(hipGetLastError());
+}
+
+// Scaled matrix instruction on raw lane registers (probe_mfma_scaled_kernel).
+// mf 16 or 32; (fa, fb, osa, osb) one of the instantiated combinations below.
+// a, b: 512 dwords; sa, sb: 64 dwords; out: 64 * (mf == 16 ? 4 : 16) floats
+// (device pointers).  Returns a hipError_t value.
+int probe_mfma_scaled(int mf, int fa, int fb, int osa, int osb, const uint32_t* a, const uint32_t* b,
+                      const uint32_t* sa, const uint32_t* sb, float* out, void* stream) {
+    hipStream_t s = static_cast<hipStream_t>(stream);
+#define PROBE_SC(MF_, FA_, FB_, OA_, OB_)                                                                  \
+    if (mf == MF_ && fa == FA_ && fb == FB_ && osa == OA_ && osb == OB_) {                                \
+        hipLaunchKernelGGL((probe_mfma_scaled_kernel<MF_, FA_, FB_, OA_, OB_>), dim3(1), dim3(64), 0, s, a, b, \
+                           sa, sb, out);                                                                   \
+        return static_cast<int>(hipGetLastError());                                                        \
+    }
+#define PROBE_SC_MF(MF_)                                                                     \
+    PROBE_SC(MF_, 0, 0, 0, 0) PROBE_SC(MF_, 1, 1, 0, 0) PROBE_SC(MF_, 4, 4, 0, 0)            \
+    PROBE_SC(MF_, 0, 1, 0, 0) PROBE_SC(MF_, 0, 0, 1, 2) PROBE_SC(MF_, 0, 0, 3, 1)            \
+    PROBE_SC(MF_, 4, 4, 2, 3)
+    PROBE_SC_MF(16)
+    PROBE_SC_MF(32)
+#undef PROBE_SC_MF
+#undef PROBE_SC
+    return static_cast<int>(hipErrorInvalidValue);
 }
 
 // in: 512 halfwords, out: 256 halfwords (device pointers).

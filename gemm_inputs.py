@@ -18,6 +18,15 @@ distributions apply to every operand):
   skinny_bf16_16x8192 bf16 M=16, N=K=8192, N(0,1)*0.02  (decode-like shape,
                       "Tuning Triton", section 4 regime split)
   tail_f16_4000x3000x1000_c  fp16 4000x3000x1000 plus addend C, U[-1,1]
+
+Block-scaled (MX) workloads draw element codes and E8M0 scale codes directly
+(MX_WORKLOADS, draw_mx): 8-bit elements are N(0,1)*8 rounded to the format by
+torch's float8 conversion; E2M1 codes are drawn with a fixed probability per
+magnitude code (a bell shape, peak at the middle codes) and a fair sign; each
+32-k block gets a scale code of base + U{-2..2} (base 124 for 8-bit
+elements, 126 for E2M1).  Scale rows are padded to a multiple of 4 bytes with
+0xFF (the NaN code), which the library must never use.  Nothing here decodes
+a code: both sides take the same stored bytes.
 """
 import numpy as np
 import torch
@@ -114,3 +123,84 @@ def from_bits(b, dtype):
     """CPU torch tensor of dtype 'f16'/'bf16' holding the given uint16 bit patterns."""
     arr = np.ascontiguousarray(b, dtype=np.uint16)
     return torch.from_numpy(arr.view(np.int16).copy()).view(TORCH_DTYPES[dtype])
+
+
+# ---------------------------------------------------------------- block-scaled (MX)
+
+MX_ELEMENT_BITS = {"e4m3": 8, "e5m2": 8, "e2m1": 4}
+MX_SCALE_BASE = {"e4m3": 124, "e5m2": 124, "e2m1": 126}
+_E2M1_MAG_P = np.array([0.08, 0.14, 0.17, 0.17, 0.15, 0.13, 0.10, 0.06])   # magnitude codes 0..7
+
+
+class MxWorkload:
+    def __init__(self, name, M, N, K, fmt_a, fmt_b, out, seeds, has_c=False):
+        self.name = name
+        self.M, self.N, self.K = M, N, K
+        self.fmt_a, self.fmt_b = fmt_a, fmt_b
+        self.out = out            # "bf16", "f16" or "f32"
+        self.seeds = seeds        # (A, B, C)
+        self.has_c = has_c
+
+    def flops(self):
+        return 2.0 * self.M * self.N * self.K
+
+    def bytes(self):
+        nb = (self.K + 31) // 32
+        osz = 4 if self.out == "f32" else 2
+        n = (self.M * self.K * MX_ELEMENT_BITS[self.fmt_a] + self.N * self.K * MX_ELEMENT_BITS[self.fmt_b]) / 8.0
+        n += (self.M + self.N) * nb + self.M * self.N * osz * (2 if self.has_c else 1)
+        return n
+
+    def describe(self):
+        return {"workload": self.name, "M": self.M, "N": self.N, "K": self.K,
+                "elements": "%s x %s" % (self.fmt_a, self.fmt_b), "scales": "E8M0 per 32 k",
+                "out": self.out, "layout": "A M x K, B stored N x K (k contiguous), D M x N row-major",
+                "has_c": self.has_c, "seeds": list(self.seeds[: 3 if self.has_c else 2])}
+
+
+MX_WORKLOADS = {
+    w.name: w for w in [
+        # the pages' microscaled GEMM is FP4 x FP4 ("afp4wfp4"); 4096^3 as the square bf16 case
+        MxWorkload("mx_e2m1_4096", 4096, 4096, 4096, "e2m1", "e2m1", "bf16", (801, 802, 803)),
+        MxWorkload("mx_e4m3_4096", 4096, 4096, 4096, "e4m3", "e4m3", "bf16", (811, 812, 813)),
+        # the decode shape at which the pages split K for the FP4 kernel (M = 16)
+        MxWorkload("mx_e2m1_16x8192x8192", 16, 8192, 8192, "e2m1", "e2m1", "bf16", (821, 822, 823)),
+    ]
+}
+
+
+def draw_mx(rows, K, fmt, seed):
+    """(codes, scales) numpy uint8 arrays for `rows` rows of K elements: codes
+    rows of K bytes (8-bit formats) or K/2 bytes (E2M1, even k in the low
+    nibble); scales rows of ceil(K/32) codes padded with 0xFF to a multiple of 4."""
+    rng = np.random.default_rng(seed)
+    if fmt in ("e4m3", "e5m2"):
+        x = torch.from_numpy(rng.standard_normal((rows, K)).astype(np.float32) * 8.0)
+        dt = torch.float8_e4m3fn if fmt == "e4m3" else torch.float8_e5m2
+        codes = x.to(dt).view(torch.uint8).numpy()
+    elif fmt == "e2m1":
+        if K % 2:
+            raise ValueError("E2M1 rows need an even K")
+        mag = rng.choice(8, size=(rows, K), p=_E2M1_MAG_P).astype(np.uint8)
+        nib = mag | (rng.integers(0, 2, (rows, K)).astype(np.uint8) << 3)
+        codes = (nib[:, 0::2] | (nib[:, 1::2] << 4)).astype(np.uint8)
+    else:
+        raise ValueError("unknown MX element format %r" % (fmt,))
+    nb = (K + 31) // 32
+    ld = -(-nb // 4) * 4
+    scales = np.full((rows, ld), 0xFF, dtype=np.uint8)
+    scales[:, :nb] = (MX_SCALE_BASE[fmt] + rng.integers(-2, 3, (rows, nb))).astype(np.uint8)
+    return np.ascontiguousarray(codes), scales
+
+
+def make_mx(workload):
+    """(A, SA, B, SB, C) numpy arrays for an MxWorkload (C: float64 values
+    already in the output type, or None)."""
+    w = MX_WORKLOADS[workload] if isinstance(workload, str) else workload
+    A, SA = draw_mx(w.M, w.K, w.fmt_a, w.seeds[0])
+    B, SB = draw_mx(w.N, w.K, w.fmt_b, w.seeds[1])
+    C = None
+    if w.has_c:
+        dt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[w.out]
+        C = draw((w.M, w.N), w.seeds[2], "f16", "uniform").to(dt)
+    return A, SA, B, SB, C

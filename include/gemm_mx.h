@@ -1,0 +1,126 @@
+/*
+ * gemm_mx.h - C ABI of the block-scaled (MX) matrix multiply on MI355X (gfx950).
+ *
+ *     D = A x B (+ C)
+ *
+ * Operation.  A (M x K) and B (K x N) hold 8-bit or 4-bit floating-point
+ * elements; each run of 32 consecutive k of a row of A, and of a column of B,
+ * shares one power-of-two scale.  gfx950's scaled matrix instruction is the
+ * entry point to these "microscaled" types ("Tuning Triton kernels", section 6,
+ * Gluon: the cdna4 instruction set adds mfma_scaled, which gfx942 lacks; the
+ * FP4 x FP4 GEMM kernel tuned in that section runs on it).  The pages do not
+ * define the types; this library takes the OCP Microscaling (MX) formats:
+ *   - elements: FP8 E4M3 (GEMM_MX_E4M3), FP8 E5M2 (GEMM_MX_E5M2) or FP4 E2M1
+ *     (GEMM_MX_E2M1);
+ *   - scales: E8M0, the byte e meaning 2^(e - 127) (255 is NaN);
+ *   - D[i][j] = sum_k (a_ik * 2^(sa_i,k/32 - 127)) * (b_kj * 2^(sb_j,k/32 - 127))
+ *     (+ c_ij), accumulated in fp32 and rounded once to the output type,
+ *     nearest-even.
+ * Accuracy contract.  The pages fix no precision for this product; the bound
+ * follows the arithmetic of the scaled instruction, measured on gfx950: it
+ * adds each run of 8 consecutive products after aligning them to the largest,
+ * keeping 13 bits below that product's leading bit, and the run sums are
+ * accumulated in fp32.  So for finite inputs
+ *     |d_ij - ref_ij| <= ulp_out(ref_ij) + 2^-20 * S_ij + 2^-10 * S8_ij,
+ * S = sum_k |scaled a_ik * scaled b_kj|, S8 = the sum over runs of 8
+ * consecutive k (k = 8q .. 8q + 7) of the largest such |product|; ulp_out of
+ * binary32 for GEMM_MX_OUT_F32.  (E2M1 products never lose a bit: an E2M1
+ * result is the exact sum, accumulated in fp32.)  Bitwise reproducible for a
+ * fixed plan.
+ *
+ * Layout.  Both operands are stored with k contiguous, the block's direction:
+ *   - A: M rows, row i at byte A + i * lda, element k of the row at byte k
+ *     (8-bit formats) or in byte k / 2, low nibble for even k (E2M1);
+ *   - B: stored N x K, column j of B at byte B + j * ldb, its elements as A's;
+ *   - SA: M rows of ldsa bytes, the scale of block t of row i at SA[i*ldsa + t];
+ *     SB: N rows of ldsb bytes likewise (column j of B);
+ *   - C and D: row-major M x N of the output type, row strides ldc / ldd in
+ *     elements.
+ * Requirements (else GEMM_ERR_UNSUPPORTED): K a multiple of 16 (8-bit) or 32
+ * (E2M1) elements, so every 16-byte chunk of a row is wholly inside or outside
+ * K; lda and ldb multiples of 16 bytes and A, B 16-byte aligned; ldsa and ldsb
+ * multiples of 4, at least ceil(K/32), SA and SB 4-byte aligned, and the scale
+ * arrays readable for M * ldsa and N * ldsb bytes (the kernel reads whole
+ * 4-byte groups of a row; scale bytes past ceil(K/32) are read but never
+ * used); A and B both 8-bit or both E2M1.  M and N tails are masked: any M,
+ * N >= 0.
+ *
+ * Tiling.  The direct-to-LDS tile kernel of gemm.h with 128 bytes of k per K
+ * step (128 k of an 8-bit format, 256 of E2M1), GROUP_M tile order, an LDS ring
+ * of stages, and the scales of each K step staged beside the operands.
+ *
+ * Ownership, errors and streams as in gemm.h: the caller owns every buffer,
+ * the library allocates no device memory and never synchronizes; plans are
+ * immutable; every entry point returns a status.
+ */
+#ifndef DTG_GEMM_MX_H
+#define DTG_GEMM_MX_H
+
+#include "gemm.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum gemm_mx_format {
+    GEMM_MX_E4M3 = 0,   /* FP8: 4 exponent bits (bias 7), 3 fraction bits, no infinities */
+    GEMM_MX_E5M2 = 1,   /* FP8: 5 exponent bits (bias 15), 2 fraction bits, IEEE-style specials */
+    GEMM_MX_E2M1 = 4    /* FP4: 2 exponent bits (bias 1), 1 fraction bit; two per byte */
+} gemm_mx_format;
+
+typedef enum gemm_mx_out {
+    GEMM_MX_OUT_F16 = 0,
+    GEMM_MX_OUT_BF16 = 1,
+    GEMM_MX_OUT_F32 = 2
+} gemm_mx_out;
+
+typedef struct gemm_mx_problem {
+    int64_t M, N, K;            /* K in elements */
+    int64_t lda, ldb;           /* bytes between rows of A / stored rows (columns) of B */
+    int64_t ldsa, ldsb;         /* bytes between rows of SA / SB */
+    int64_t ldc, ldd;           /* elements between rows of C / D (ldc ignored when has_c == 0) */
+    gemm_mx_format fmt_a, fmt_b;
+    gemm_mx_out out;            /* storage type of C and D */
+    int32_t has_c;              /* 1: D = A x B + C;  0: D = A x B */
+} gemm_mx_problem;
+
+typedef struct gemm_mx_plan gemm_mx_plan;   /* opaque, immutable after creation */
+
+/* Validate *prob and choose a tile configuration for HIP device `device`.
+ * force may be NULL; its non-zero fields bm, bn, stages, waves_m, waves_n,
+ * group_m and xcd_remap override the planner (kernel, bk, mfma and splitk
+ * must be 0 or the values the plan reports).  No device work. */
+gemm_status gemm_mx_plan_create(const gemm_mx_problem* prob, int device, const gemm_config* force,
+                                gemm_mx_plan** out);
+
+/* Same with explicit device facts; touches no device. */
+gemm_status gemm_mx_plan_create_for(const gemm_mx_problem* prob, const gemm_device_info* info,
+                                    const gemm_config* force, gemm_mx_plan** out);
+
+/* Free a plan.  NULL is a no-op. */
+void gemm_mx_plan_destroy(gemm_mx_plan* plan);
+
+/* The configuration a plan runs: kernel = 4 (block-scaled tile kernel),
+ * bk = k per K step in elements, mfma = 32 (32x32x64 scaled instruction),
+ * splitk = 1. */
+gemm_status gemm_mx_plan_config(const gemm_mx_plan* plan, gemm_config* out);
+
+/* Launch geometry: grid (workgroups), threads per workgroup, LDS bytes. */
+gemm_status gemm_mx_plan_launch(const gemm_mx_plan* plan, int64_t* grid, int32_t* threads, int64_t* lds_bytes);
+
+/* One-line NUL-terminated description of the plan into buf[0..len). */
+gemm_status gemm_mx_plan_describe(const gemm_mx_plan* plan, char* buf, size_t len);
+
+/* Enqueue D = A x B (+ C) on `stream`.  A, SA, B, SB, D are device pointers; C
+ * is a device pointer when has_c = 1 and NULL otherwise.  D may equal C (same
+ * ldc and ldd); any other overlap of D with an input is GEMM_ERR_INVALID_ARG.
+ * M = 0 or N = 0 launches nothing; K = 0 writes D = C (or zeros).  Alignment
+ * or stride violations are GEMM_ERR_UNSUPPORTED. */
+gemm_status gemm_mx_run(const gemm_mx_plan* plan, const void* A, const void* SA, const void* B, const void* SB,
+                        const void* C, void* D, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DTG_GEMM_MX_H */

@@ -11,6 +11,7 @@ import re
 import pytest
 
 import dense_tiled_gemm_02_amd as g
+import dense_tiled_gemm_02_amd.mx as mx
 import oracle
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -24,8 +25,8 @@ def fake_gfx950():
     return d
 
 
-def declared_functions():
-    src = open(os.path.join(ROOT, "include", "gemm.h")).read()
+def declared_functions(header="gemm.h"):
+    src = open(os.path.join(ROOT, "include", header)).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(gemm\w*)\s*\(", src, flags=re.M)))
 
@@ -37,6 +38,14 @@ def test_library_exports_every_declared_function():
     for n in names:
         assert hasattr(L, n), n
     assert sorted(n for n, _, _ in g.SIGNATURES) == names
+    mx_names = declared_functions("gemm_mx.h")
+    assert len(mx_names) == 7
+    L = mx.mxlib()
+    for n in mx_names:
+        assert hasattr(L, n), n
+    assert sorted(n for n, _, _ in mx.MX_SIGNATURES) == mx_names
+    # every header under include/ is covered
+    assert sorted(os.listdir(os.path.join(ROOT, "include"))) == ["gemm.h", "gemm_mx.h"]
 
 
 def test_status_strings():
@@ -264,3 +273,81 @@ def test_layouts_pick_matching_kernels():
     # the decode regime needs row-major operands; a transposed B goes to the tile ladder
     assert plan(16, 8192, 8192).config.kernel == 2
     assert plan(16, 8192, 8192, tb=True).config.kernel != 2
+
+
+# ---------------------------------------------------------------- block-scaled (MX) path
+
+
+def mx_plan(M, N, K, fmt="e4m3", **kw):
+    return mx.gemm_mx_plan_create_for(mx.mx_problem(M, N, K, fmt, **kw), fake_gfx950())
+
+
+def test_mx_plans_fit_the_device_and_pick_by_tile_count():
+    for fmt in ("e4m3", "e5m2", "e2m1"):
+        for (M, N, K) in [(4096, 4096, 4096), (512, 512, 1024), (16, 8192, 8192), (1000, 3000, 992)]:
+            p = mx_plan(M, N, K, fmt)
+            c = p.config
+            grid, threads, lds = mx.gemm_mx_plan_launch(p)
+            assert c.kernel == mx.KERNEL_MX and c.mfma == 32 and c.splitk == 1
+            assert c.bk == (256 if fmt == "e2m1" else 128)
+            assert lds <= 160 * 1024 and threads in (256, 512)
+            assert grid == -(-M // c.bm) * -(-N // c.bn)
+            assert ("fmt=%d/%d" % (mx.FORMATS[fmt], mx.FORMATS[fmt])) in p.describe()
+    assert (mx_plan(4096, 4096, 4096).config.bm, mx_plan(4096, 4096, 4096).config.bn) == (256, 128)
+    assert (mx_plan(512, 512, 1024).config.bm, mx_plan(512, 512, 1024).config.bn) == (128, 128)
+    p = mx_plan(4096, 4096, 4096, fmt_b="e5m2")
+    assert "fmt=0/1" in p.describe()
+
+
+def test_mx_forced_config_is_honoured_or_rejected():
+    p = mx.gemm_mx_plan_create_for(mx.mx_problem(4096, 4096, 4096), fake_gfx950(), {"bm": 128, "bn": 256})
+    assert (p.config.bm, p.config.bn) == (128, 256)
+    for bad in ({"bm": 64}, {"splitk": 2}, {"mfma": 16}, {"kernel": 3}):
+        with pytest.raises(g.GemmError) as e:
+            mx.gemm_mx_plan_create_for(mx.mx_problem(4096, 4096, 4096), fake_gfx950(), bad)
+        assert e.value.status == g.GEMM_ERR_UNSUPPORTED, bad
+
+
+@pytest.mark.parametrize("kw,status", [
+    ({"K": 40}, g.GEMM_ERR_UNSUPPORTED),                       # K not a multiple of 16
+    ({"K": 48, "fmt_a": "e2m1"}, g.GEMM_ERR_UNSUPPORTED),      # E2M1: K a multiple of 32
+    ({"lda": 136}, g.GEMM_ERR_UNSUPPORTED),                    # row stride not a multiple of 16
+    ({"ldsb": 6}, g.GEMM_ERR_UNSUPPORTED),                     # scale stride not a multiple of 4
+    ({"ldsa": 0}, g.GEMM_ERR_INVALID_ARG),                     # below ceil(K/32)
+    ({"lda": 64}, g.GEMM_ERR_INVALID_ARG),                     # below the row's bytes
+    ({"ldd": 100}, g.GEMM_ERR_INVALID_ARG),                    # output rows overlap
+    ({"fmt_a": "e4m3", "fmt_b": "e2m1"}, g.GEMM_ERR_UNSUPPORTED),
+    ({"out": 3}, g.GEMM_ERR_INVALID_ARG),
+    ({"M": -1}, g.GEMM_ERR_INVALID_ARG),
+])
+def test_mx_validation_errors(kw, status):
+    args = dict(M=256, N=128, K=128, fmt_a="e4m3", fmt_b=None)
+    for k in ("M", "N", "K", "fmt_a", "fmt_b"):
+        if k in kw:
+            args[k] = kw.pop(k)
+    p = mx.mx_problem(args["M"], args["N"], args["K"], args["fmt_a"], args["fmt_b"], **kw)
+    with pytest.raises(g.GemmError) as e:
+        mx.gemm_mx_plan_create_for(p, fake_gfx950())
+    assert e.value.status == status
+    assert g.gemm_last_error()
+
+
+def test_mx_run_rejects_bad_pointers_without_launching():
+    p = mx_plan(256, 128, 128)
+    with pytest.raises(g.GemmError) as e:
+        mx.gemm_mx_run(p, 0x1000, 0x2000, 0x3000, 0x4000, None, None)
+    assert e.value.status == g.GEMM_ERR_INVALID_ARG            # D is NULL
+    with pytest.raises(g.GemmError) as e:
+        mx.gemm_mx_run(p, 0x1008, 0x20000, 0x30000, 0x40000, None, 0x100000)
+    assert e.value.status == g.GEMM_ERR_UNSUPPORTED            # A not 16-byte aligned
+    with pytest.raises(g.GemmError) as e:
+        mx.gemm_mx_run(p, 0x10000, 0x20002, 0x30000, 0x40000, None, 0x100000)
+    assert e.value.status == g.GEMM_ERR_UNSUPPORTED            # SA not 4-byte aligned
+    with pytest.raises(g.GemmError) as e:
+        mx.gemm_mx_run(p, 0x10000, 0x20000, 0x30000, 0x40000, 0x50000, 0x100000)
+    assert e.value.status == g.GEMM_ERR_INVALID_ARG            # C given without has_c
+    with pytest.raises(g.GemmError) as e:                      # D overlaps A
+        mx.gemm_mx_run(p, 0x100000, 0x200000, 0x300000, 0x400000, None, 0x100100)
+    assert e.value.status == g.GEMM_ERR_INVALID_ARG
+    # an empty output launches nothing and succeeds without any pointer
+    mx.gemm_mx_run(mx_plan(0, 128, 128), None, None, None, None, None, None)

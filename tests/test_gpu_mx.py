@@ -1,0 +1,165 @@
+"""Parity of the block-scaled (MX) GEMM with the oracle (GPU).
+
+Every case runs the HIP kernel through the C ABI (gemm_mx_plan_create /
+gemm_mx_run) on seeded inputs from gemm_inputs.draw_mx and checks every
+output (or, at the full 4096^3 size, sampled outputs) against the binary64
+oracle with the MX acceptance rule
+|d - ref| <= ulp_out(ref) + 2^-20 * S + 2^-10 * S8,
+S = sum_k |scaled a * scaled b|, S8 = sum over runs of 8 consecutive k of
+the largest such product (the scaled instruction's own rounding of a run).
+Scale rows are padded with the NaN code 0xFF, so a read of a scale past
+ceil(K/32) would show as a non-finite output.
+"""
+import numpy as np
+import pytest
+import torch
+
+import dense_tiled_gemm_02_amd as g
+import dense_tiled_gemm_02_amd.mx as mx
+import gemm_inputs
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+PAIRS = [("e4m3", "e4m3"), ("e5m2", "e5m2"), ("e4m3", "e5m2"), ("e5m2", "e4m3"), ("e2m1", "e2m1")]
+TILES = [(256, 128), (128, 256), (128, 128)]
+OUT = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    assert torch.cuda.is_available(), "GPU test run without a GPU"
+    mx.mxlib()
+
+
+def _dev(x):
+    return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+
+def _check(D, ref, S, S8, out, what):
+    got = D.cpu().numpy() if out == "f32" else gemm_inputs.bits(D.cpu())
+    n, worst, first = oracle.mx_tol_check(got, out, ref, S, S8)
+    assert n == 0, "%s: %d outputs outside the bound (worst %.3g, first flat index %d)" % (what, n, worst, first)
+    return worst
+
+
+def _run(A, SA, B, SB, K, fa, fb, out="bf16", config=None):
+    D = mx.mx_matmul(_dev(A), _dev(SA), _dev(B), _dev(SB), K, fa, fb, out_dtype=OUT[out], config=config)
+    torch.cuda.synchronize()
+    return D
+
+
+def _case(M, N, K, fa, fb, seed):
+    A, SA = gemm_inputs.draw_mx(M, K, fa, seed)
+    B, SB = gemm_inputs.draw_mx(N, K, fb, seed + 1)
+    return A, SA, B, SB
+
+
+@pytest.mark.parametrize("tile", TILES)
+@pytest.mark.parametrize("fa,fb", PAIRS)
+def test_tiles_with_ragged_tails_match_oracle(fa, fb, tile):
+    """M, N not tile multiples; K ends inside a K step and inside a scale block."""
+    K = 1056 if fa != "e2m1" else 1088
+    M, N = 520, 392
+    A, SA, B, SB = _case(M, N, K, fa, fb, 31 + len(fa + fb) + tile[0] // 64)
+    print("mx case", fa, fb, tile, M, N, K, flush=True)
+    D = _run(A, SA, B, SB, K, fa, fb, config={"bm": tile[0], "bn": tile[1]})
+    ref, S, S8 = oracle.mx_gemm_f64(A, SA, B, SB, K, fa, fb, runs=True)
+    _check(D, ref, S, S8, "bf16", "%s x %s tile %s" % (fa, fb, tile))
+
+
+@pytest.mark.parametrize("out", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("fmt", ["e4m3", "e2m1"])
+def test_output_types_and_addend(fmt, out):
+    M, N, K = 300, 260, 512
+    A, SA, B, SB = _case(M, N, K, fmt, fmt, 77)
+    C = np.random.default_rng(5).uniform(-4, 4, (M, N)).astype(np.float32)
+    Ct = torch.from_numpy(C).to(OUT[out])
+    print("mx out", fmt, out, flush=True)
+    D = mx.mx_matmul(_dev(A), _dev(SA), _dev(B), _dev(SB), K, fmt, fmt, C=Ct.cuda(), out_dtype=OUT[out])
+    torch.cuda.synchronize()
+    ref, S, S8 = oracle.mx_gemm_f64(A, SA, B, SB, K, fmt, fmt, Ct.to(torch.float64).numpy(), runs=True)
+    _check(D, ref, S, S8, out, "%s out %s + C" % (fmt, out))
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e2m1"])
+def test_padded_rows_and_scale_strides(fmt):
+    """Row strides above the packed size (A, B, scales and D)."""
+    M, N, K = 200, 136, 768
+    A0, SA0, B0, SB0 = _case(M, N, K, fmt, fmt, 91)
+    pad = lambda x, extra, fill: np.concatenate([x, np.full((x.shape[0], extra), fill, np.uint8)], 1)
+    A, B = pad(A0, 48, 0x7E), pad(B0, 16, 0x7E)            # padding holds large finite values
+    SA, SB = pad(SA0, 8, 0xFF), pad(SB0, 4, 0xFF)
+    Dbig = torch.full((M, N + 24), float("nan"), dtype=torch.bfloat16, device="cuda")
+    D = Dbig[:, :N]
+    print("mx padded", fmt, flush=True)
+    mx.mx_matmul(_dev(A), _dev(SA), _dev(B), _dev(SB), K, fmt, fmt, out=D)
+    torch.cuda.synchronize()
+    ref, S, S8 = oracle.mx_gemm_f64(A0, SA0, B0, SB0, K, fmt, fmt, runs=True)
+    _check(D.contiguous(), ref, S, S8, "bf16", "padded " + fmt)
+    assert torch.isnan(Dbig[:, N:].float()).all()           # nothing written past N
+
+
+def test_small_and_degenerate_shapes():
+    for (M, N, K) in [(1, 1, 32), (7, 33, 64), (33, 7, 96), (129, 257, 160), (64, 64, 4096)]:
+        for fmt in ("e4m3", "e2m1"):
+            A, SA, B, SB = _case(M, N, K, fmt, fmt, M + N + K)
+            print("mx small", fmt, M, N, K, flush=True)
+            D = _run(A, SA, B, SB, K, fmt, fmt)
+            ref, S, S8 = oracle.mx_gemm_f64(A, SA, B, SB, K, fmt, fmt, runs=True)
+            _check(D, ref, S, S8, "bf16", "%s %dx%dx%d" % (fmt, M, N, K))
+
+
+def test_k_zero_writes_the_addend_and_empty_outputs_launch_nothing():
+    M, N = 40, 24
+    C = torch.randn(M, N, device="cuda").to(torch.bfloat16)
+    e = torch.zeros((M, 0), dtype=torch.uint8, device="cuda")
+    s = torch.zeros((M, 4), dtype=torch.uint8, device="cuda")
+    eb = torch.zeros((N, 0), dtype=torch.uint8, device="cuda")
+    sb = torch.zeros((N, 4), dtype=torch.uint8, device="cuda")
+    p = mx.mx_problem(M, N, 0, "e4m3", has_c=True, lda=16, ldb=16, ldsa=4, ldsb=4)
+    pl = mx.gemm_mx_plan_create(p, 0)
+    D = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+    mx.gemm_mx_run(pl, e.data_ptr(), s.data_ptr(), eb.data_ptr(), sb.data_ptr(), C.data_ptr(), D.data_ptr(),
+                   torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert torch.equal(D, C)
+    p0 = mx.mx_problem(0, N, 64, "e4m3")
+    mx.gemm_mx_run(mx.gemm_mx_plan_create(p0, 0), None, None, None, None, None, None, None)
+
+
+def test_runs_are_bitwise_reproducible():
+    A, SA, B, SB = _case(512, 512, 2048, "e4m3", "e4m3", 5)
+    D1 = _run(A, SA, B, SB, 2048, "e4m3", "e4m3")
+    D2 = _run(A, SA, B, SB, 2048, "e4m3", "e4m3")
+    assert torch.equal(D1.view(torch.int16), D2.view(torch.int16))
+
+
+@pytest.mark.parametrize("name", sorted(gemm_inputs.MX_WORKLOADS))
+def test_full_size_workloads_sampled(name):
+    """The benchmark's workloads at full size, in the launch configuration the
+    benchmark times, on 3000 sampled outputs (all corners and edges included)."""
+    w = gemm_inputs.MX_WORKLOADS[name]
+    A, SA, B, SB, _ = gemm_inputs.make_mx(w)
+    print("mx full", name, flush=True)
+    D = _run(A, SA, B, SB, w.K, w.fmt_a, w.fmt_b, w.out)
+    rng = np.random.default_rng(17)
+    ii = np.concatenate([rng.integers(0, w.M, 3000), [0, 0, w.M - 1, w.M - 1]])
+    jj = np.concatenate([rng.integers(0, w.N, 3000), [0, w.N - 1, 0, w.N - 1]])
+    ref, S, S8 = oracle.mx_gemm_f64_at(A, SA, B, SB, w.K, w.fmt_a, w.fmt_b, None, ii, jj, runs=True)
+    got = gemm_inputs.bits(D.cpu())[ii, jj]
+    n, worst, first = oracle.mx_tol_check(got, w.out, ref, S, S8)
+    assert n == 0, "%s: %d sampled outputs outside the bound (worst %.3g)" % (name, n, worst)
+    assert torch.isfinite(D.float()).all()
+
+
+def test_e2m1_products_are_exact_in_binary32():
+    """Every E2M1 product has at most 4 significant bits and a run of 8 within one
+    block spans few binades, so the instruction's run rounding never bites:
+    with a binary32 output the result is the exact sum rounded once."""
+    M, N, K = 256, 256, 1024
+    A, SA, B, SB = _case(M, N, K, "e2m1", "e2m1", 21)
+    D = _run(A, SA, B, SB, K, "e2m1", "e2m1", "f32")
+    ref, S = oracle.mx_gemm_f64(A, SA, B, SB, K, "e2m1", "e2m1")
+    n, worst, _ = oracle.mx_tol_check(D.cpu().numpy(), "f32", ref, S, None)
+    assert n == 0
