@@ -397,6 +397,7 @@ def mx(args):
                            ldsa=SA.shape[1], ldsb=SB.shape[1])
         pl = mxb.gemm_mx_plan_create(p, torch.cuda.current_device())
         stream = torch.cuda.current_stream().cuda_stream
+        ws, wsb = mxb._workspace(pl, torch.cuda.current_device(), stream)
         run = mxb.mxlib().gemm_mx_run
         st = {"i": 0}
 
@@ -404,7 +405,7 @@ def mx(args):
             for _ in range(c):
                 i = st["i"] % copies
                 assert run(pl.handle, dA.data_ptr(), dSA.data_ptr(), Bs[i].data_ptr(), SBs[i].data_ptr(), None,
-                           D.data_ptr(), stream) == 0
+                           D.data_ptr(), ws, wsb, stream) == 0
                 st["i"] += 1
         launch(5)
         torch.cuda.synchronize()

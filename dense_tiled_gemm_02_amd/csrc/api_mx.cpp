@@ -15,6 +15,7 @@
 
 #include "../../include/gemm_mx.h"
 #include "api_internal.h"
+#include "kernels.h"
 #include "kernels_mx.h"
 
 struct gemm_mx_plan {
@@ -23,6 +24,7 @@ struct gemm_mx_plan {
     gemm_config cfg;
     const dtg::MxEntry* entry;
     int64_t num_pid_m, num_pid_n, grid;
+    int64_t ws_bytes;
 };
 
 namespace {
@@ -82,9 +84,11 @@ gemm_status validate(const gemm_mx_problem* p) {
     if (p->M > 1 && p->N > 0 && p->ldd < p->N)
         return fail(GEMM_ERR_INVALID_ARG, "D row stride %lld < N=%lld makes output rows overlap",
                     (long long)p->ldd, (long long)p->N);
-    // 32-bit buffer offsets cover one tile's rows of every operand
+    // 32-bit buffer offsets and ranges cover one tile's rows of every operand
+    // plus the K extent (descriptors move along k from the tile's corner)
     const int64_t lim = (int64_t(1) << 31) - 4096;
-    if (256 * p->lda >= lim || 256 * p->ldb >= lim || 256 * p->ldsa >= lim || 256 * p->ldsb >= lim)
+    if (256 * p->lda + kb >= lim || 256 * p->ldb + kb >= lim || 256 * p->ldsa + nblk >= lim ||
+        256 * p->ldsb + nblk >= lim)
         return fail(GEMM_ERR_UNSUPPORTED, "row strides too large for 32-bit tile offsets");
     return GEMM_OK;
 }
@@ -97,7 +101,7 @@ const dtg::MxEntry* find_entry(const gemm_config& w, const gemm_mx_problem* p, c
         if (e->fmt_a != p->fmt_a || e->fmt_b != p->fmt_b || e->lds_bytes > dev.lds_per_wg) continue;
         if ((w.bm && w.bm != e->bm) || (w.bn && w.bn != e->bn) || (w.stages && w.stages != e->stages) ||
             (w.waves_m && w.waves_m != e->waves_m) || (w.waves_n && w.waves_n != e->waves_n) ||
-            (w.bk && w.bk != e->bk) || (w.mfma && w.mfma != e->mfma))
+            (w.bk && w.bk != e->bk) || (w.mfma && w.mfma != e->mfma) || (w.splitk > e->splitk))
             continue;
         return e;
     }
@@ -115,31 +119,48 @@ gemm_status plan_impl(const gemm_mx_problem* prob, const gemm_device_info* dev, 
     gemm_config want;
     memset(&want, 0, sizeof want);
     int group_m = 8, xcd = 1;
-    static const int ladder[][2] = {{256, 128}, {128, 256}, {128, 128}};
-    bool picked = false;
-    for (const auto& t : ladder) {
-        if (2 * cdiv(prob->M, t[0]) * cdiv(prob->N, t[1]) >= dev->cu_count) {
-            want.bm = t[0];
-            want.bn = t[1];
-            picked = true;
-            break;
+    const int64_t bke = prob->fmt_a == GEMM_MX_E2M1 ? 256 : 128;   // k per K step
+    const int64_t nkt = cdiv(prob->K, bke);
+    // K slices: enough workgroups for the CUs, at least 2 K steps per slice, at most 16
+    auto slices = [&](int64_t tiles, int64_t min_steps) {
+        int64_t s = dev->cu_count / (tiles > 0 ? tiles : 1);
+        if (s > nkt / min_steps) s = nkt / min_steps;
+        if (s > 16) s = 16;
+        if (tiles > dtg::kMaxCounters) s = 1;
+        return static_cast<int32_t>(s > 1 ? s : 1);
+    };
+    if (prob->M <= 32) {
+        // decode regime: 32-row slabs of 256 columns, K sliced to fill the CUs
+        want.bm = 32;
+        want.bn = 256;
+        want.splitk = slices(cdiv(prob->N, 256), 2);
+    } else {
+        static const int ladder[][2] = {{256, 256}, {256, 128}, {128, 256}, {128, 128}};
+        bool picked = false;
+        for (const auto& t : ladder) {
+            if (2 * cdiv(prob->M, t[0]) * cdiv(prob->N, t[1]) >= dev->cu_count) {
+                want.bm = t[0];
+                want.bn = t[1];
+                picked = true;
+                break;
+            }
         }
-    }
-    if (!picked) {
-        want.bm = 128;
-        want.bn = 128;
+        if (!picked) {
+            want.bm = 128;
+            want.bn = 128;
+            want.splitk = slices(cdiv(prob->M, 128) * cdiv(prob->N, 128), 8);
+        }
     }
     if (force) {
         const gemm_config& f = *force;
         if (f.group_m < 0 || f.xcd_remap < 0 || f.xcd_remap > 2)
             return fail(GEMM_ERR_INVALID_ARG, "group_m must be >= 0 and xcd_remap one of 0, 1, 2");
-        if ((f.kernel && f.kernel != kKernelMx) || (f.splitk > 1) || (f.mfma && f.mfma != 32))
-            return fail(GEMM_ERR_UNSUPPORTED, "the block-scaled path runs kernel %d, mfma 32, splitk 1 only",
+        if ((f.kernel && f.kernel != kKernelMx) || (f.mfma && f.mfma != 32) || f.splitk < 0 || f.splitk > 64)
+            return fail(GEMM_ERR_UNSUPPORTED, "the block-scaled path runs kernel %d, mfma 32, splitk 0..64",
                         kKernelMx);
-        if (f.bm || f.bn || f.stages || f.waves_m || f.waves_n || f.bk) {
+        if (f.bm || f.bn || f.stages || f.waves_m || f.waves_n || f.bk || f.splitk) {
             want = f;
             want.kernel = 0;
-            want.splitk = 0;
         }
         if (f.group_m) group_m = f.group_m;
         if (f.xcd_remap) xcd = (f.xcd_remap == GEMM_XCD_ON);
@@ -158,10 +179,17 @@ gemm_status plan_impl(const gemm_mx_problem* prob, const gemm_device_info* dev, 
     pl->entry = e;
     pl->num_pid_m = cdiv(prob->M, e->bm);
     pl->num_pid_n = cdiv(prob->N, e->bn);
-    pl->grid = pl->num_pid_m * pl->num_pid_n;
+    const int32_t splits = want.splitk > 1 ? want.splitk : 1;
+    pl->grid = pl->num_pid_m * pl->num_pid_n * splits;
     if (pl->grid > kMaxDim) {
         delete pl;
         return fail(GEMM_ERR_UNSUPPORTED, "output too large for one launch");
+    }
+    pl->ws_bytes = dtg::dma_workspace_bytes(pl->num_pid_m * pl->num_pid_n, e->bm, e->bn, splits);
+    if (pl->ws_bytes < 0) {
+        delete pl;
+        return fail(GEMM_ERR_UNSUPPORTED, "K slices across workgroups support at most %d output tiles",
+                    dtg::kMaxCounters);
     }
     gemm_config& c = pl->cfg;
     memset(&c, 0, sizeof c);
@@ -173,7 +201,7 @@ gemm_status plan_impl(const gemm_mx_problem* prob, const gemm_device_info* dev, 
     c.mfma = e->mfma;
     c.waves_m = e->waves_m;
     c.waves_n = e->waves_n;
-    c.splitk = 1;
+    c.splitk = splits;
     c.group_m = group_m < 1 ? 1 : group_m;
     c.xcd_remap = (xcd && dev->xcd_count > 1) ? GEMM_XCD_ON : GEMM_XCD_OFF;
     *out = pl;
@@ -230,8 +258,25 @@ gemm_status gemm_mx_plan_describe(const gemm_mx_plan* plan, char* buf, size_t le
     return GEMM_OK;
 }
 
+gemm_status gemm_mx_workspace_size(const gemm_mx_plan* plan, size_t* bytes) {
+    if (!plan || !bytes) return fail(GEMM_ERR_INVALID_ARG, "plan or bytes is NULL");
+    *bytes = static_cast<size_t>(plan->ws_bytes);
+    return GEMM_OK;
+}
+
+gemm_status gemm_mx_workspace_init(const gemm_mx_plan* plan, void* workspace, size_t workspace_bytes, void* stream) {
+    if (!plan) return fail(GEMM_ERR_INVALID_ARG, "plan is NULL");
+    if (plan->ws_bytes == 0) return GEMM_OK;
+    if (!workspace || workspace_bytes < static_cast<size_t>(plan->ws_bytes))
+        return fail(GEMM_ERR_WORKSPACE, "workspace of %zu bytes given, %lld needed", workspace_bytes,
+                    (long long)plan->ws_bytes);
+    hipError_t e = dtg::zero_words(workspace, plan->ws_bytes / 4, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(GEMM_ERR_HIP, "workspace zero fill: %s", hipGetErrorString(e));
+    return GEMM_OK;
+}
+
 gemm_status gemm_mx_run(const gemm_mx_plan* plan, const void* A, const void* SA, const void* B, const void* SB,
-                        const void* C, void* D, void* stream) {
+                        const void* C, void* D, void* workspace, size_t workspace_bytes, void* stream) {
     if (!plan) return fail(GEMM_ERR_INVALID_ARG, "plan is NULL");
     const gemm_mx_problem& p = plan->prob;
     if (p.has_c && !C) return fail(GEMM_ERR_INVALID_ARG, "problem has C but C is NULL");
@@ -268,6 +313,13 @@ gemm_status gemm_mx_run(const gemm_mx_plan* plan, const void* A, const void* SA,
         if (!same && overlaps(d0, d1, c0, c1))
             return fail(GEMM_ERR_INVALID_ARG, "D overlaps C (only D == C with equal strides is allowed)");
     }
+    if (plan->ws_bytes > 0) {
+        if (!workspace || workspace_bytes < static_cast<size_t>(plan->ws_bytes))
+            return fail(GEMM_ERR_WORKSPACE, "plan needs a workspace of %lld bytes (%zu given)",
+                        (long long)plan->ws_bytes, workspace ? workspace_bytes : static_cast<size_t>(0));
+        if (reinterpret_cast<uintptr_t>(workspace) & 255)
+            return fail(GEMM_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    }
     dtg::MxArgs a;
     a.A = static_cast<const uint8_t*>(A);
     a.B = static_cast<const uint8_t*>(B);
@@ -290,6 +342,8 @@ gemm_status gemm_mx_run(const gemm_mx_plan* plan, const void* A, const void* SA,
     a.ldsb = p.ldsb;
     a.ldc = p.has_c ? p.ldc : 0;
     a.ldd = p.ldd;
+    a.splits = plan->cfg.splitk;
+    a.ws = workspace;
     hipError_t err = plan->entry->launch(a, plan->grid, static_cast<hipStream_t>(stream));
     if (err != hipSuccess)
         return fail(GEMM_ERR_HIP, "launch of %s: %s", plan->entry->name, hipGetErrorString(err));

@@ -39,6 +39,7 @@
 #include <type_traits>
 
 #include "device_common.h"
+#include "kernels.h"
 #include "kernels_mx.h"
 #include "tile_order.h"
 
@@ -118,14 +119,16 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mx_kernel(MxArgs p) {
     static_assert(TM % 32 == 0 && TN % 32 == 0, "tile vs wave grid");
     // scale loads: 64 lanes x 4 bytes = 256 bytes of [row][NBLK] per instruction
     constexpr int SRPI = 256 / NBLK;                   // scale rows per instruction
-    constexpr int SIA = BM / SRPI, SIB = BN / SRPI, SI = SIA + SIB;
-    static_assert(BM % SRPI == 0 && BN % SRPI == 0, "scale split");
-    constexpr int NSL = (SI + NW - 1) / NW;            // scale loads per wave (some may be empty)
+    // instructions per stage for A's and B's scales; a tile of fewer rows than
+    // one instruction covers pads its scale region to the instruction's 256 bytes
+    constexpr int SIA = (BM + SRPI - 1) / SRPI, SIB = (BN + SRPI - 1) / SRPI;
+    constexpr int NSA = (SIA + NW - 1) / NW, NSB = (SIB + NW - 1) / NW;   // per wave (some may be empty)
+    constexpr int NSL = NSA + NSB;
     constexpr int L = IA_W + IB_W + NSL;               // loads per wave per K step
     static_assert(ST >= 2 && ST <= 4 && (ST - 1) * L < 64, "stages");
 
     constexpr int SA_B = BM * ROWB, SB_B = BN * ROWB;  // bytes per stage
-    constexpr int SSA_B = BM * NBLK, SSB_B = BN * NBLK;
+    constexpr int SSA_B = SIA * 256, SSB_B = SIB * 256;
     constexpr int OFF_B = ST * SA_B;
     constexpr int OFF_S = ST * (SA_B + SB_B);
     constexpr int OFF_SB = OFF_S + ST * SSA_B;
@@ -138,69 +141,106 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mx_kernel(MxArgs p) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / WN, wn = wave % WN;
 
-    int pid_m, pid_n;
-    tile_of_workgroup<int>(blockIdx.x, p.num_pid_m, p.num_pid_n, p.group_m, p.xcds, &pid_m, &pid_n);
+    // Workgroup -> (K slice, output tile): the XCD permutation runs over the
+    // whole grid, consecutive positions are consecutive tiles (grouped order)
+    // of one slice.  With one slice this is tile_of_workgroup.
+    const int ntiles = p.num_pid_m * p.num_pid_n;
+    const int NS = p.splits;
+    int pid_m, pid_n, tile_lin, slice;
+    {
+        const int pos = xcd_permute<int>(blockIdx.x, ntiles * NS, p.xcds);
+        slice = pos / ntiles;
+        tile_lin = pos - slice * ntiles;
+        grouped_tile<int>(tile_lin, p.num_pid_m, p.num_pid_n, p.group_m, &pid_m, &pid_n);
+    }
     const int m0 = pid_m * BM, n0 = pid_n * BN;
     const int M = p.M, N = p.N, K = p.K;
     const int kbytes = K / (8 / EB);                   // K is a multiple of the 16-byte chunk
     const int nblocks = (K + 31) / 32;
-    const bool edge = (m0 + BM > M) || (n0 + BN > N);
 
     // ---- per-lane operand load offsets: load X of an operand fills LDS rows
     // X*NW*R + wave*R + lane/8 with the lane's 16-byte chunk lane % 8 of the
-    // row; the lane fetches the chunk that the swizzle puts there.
+    // row; the lane fetches the chunk that the swizzle puts there.  Rows past
+    // the matrix get an offset past any range (fixed for the kernel); the K
+    // tail is a per-lane bit OR'd in at each step.  Masking is arithmetic, so
+    // the loop has no data-dependent branches.
     const int ld_row = wave * R + lane / 8;
     const int ld_chunk = (lane % 8) ^ swz<8>(ld_row);
-    const uint32_t a_voff = static_cast<uint32_t>(static_cast<int64_t>(ld_row) * p.lda + ld_chunk * 16);
-    const uint32_t b_voff = static_cast<uint32_t>(static_cast<int64_t>(ld_row) * p.ldb + ld_chunk * 16);
-    const uint32_t a_step = static_cast<uint32_t>(NW * R) * static_cast<uint32_t>(p.lda);
-    const uint32_t b_step = static_cast<uint32_t>(NW * R) * static_cast<uint32_t>(p.ldb);
-    // scale loads: instruction si = s * NW + wave covers SRPI rows of A's
-    // (si < SIA) or B's scale tile; lane -> (row, dword)
+    uint32_t a_vo[IA_W], b_vo[IB_W];
+#pragma unroll
+    for (int y = 0; y < IA_W; ++y) {
+        const int row = ld_row + y * NW * R;
+        a_vo[y] = m0 + row < M ? static_cast<uint32_t>(static_cast<int64_t>(row) * p.lda + ld_chunk * 16) : kOOB;
+    }
+#pragma unroll
+    for (int y = 0; y < IB_W; ++y) {
+        const int row = ld_row + y * NW * R;
+        b_vo[y] = n0 + row < N ? static_cast<uint32_t>(static_cast<int64_t>(row) * p.ldb + ld_chunk * 16) : kOOB;
+    }
+    // scale loads: A's instruction X of a wave is number si = X * NW + wave of
+    // the stage (SRPI rows of the scale tile), B's likewise.  A wave whose si is
+    // past the tile loads nothing (offset past the range) into a scratch slot;
+    // lanes past the matrix's rows read zeros.  Per-lane offsets, LDS
+    // destinations and their stage strides are fixed for the whole kernel, so
+    // the loop holds no wave-dependent control flow.
     constexpr int DPR = NBLK / 4;                      // dwords per scale row
     uint32_t s_voff[NSL];
-    int s_row[NSL];
+    int s_dst[NSL], s_stage[NSL];
 #pragma unroll
-    for (int s = 0; s < NSL; ++s) {
-        const int si = s * NW + wave;
-        const int rr = (si < SIA ? si : si - SIA) * SRPI + lane / DPR;
-        s_row[s] = rr;
-        s_voff[s] = static_cast<uint32_t>(static_cast<int64_t>(rr) * (si < SIA ? p.ldsa : p.ldsb) + 4 * (lane % DPR));
+    for (int x = 0; x < NSL; ++x) {
+        const bool is_a = x < NSA;
+        const int si = (is_a ? x : x - NSA) * NW + wave;
+        const bool valid = si < (is_a ? SIA : SIB);
+        const int rr = si * SRPI + lane / DPR;
+        const bool in_rows = rr < (is_a ? BM : BN) && (is_a ? m0 + rr < M : n0 + rr < N);
+        s_voff[x] = (valid && in_rows)
+                        ? static_cast<uint32_t>(static_cast<int64_t>(rr) * (is_a ? p.ldsa : p.ldsb) + 4 * (lane % DPR))
+                        : kOOB;
+        s_dst[x] = valid ? (is_a ? OFF_S : OFF_SB) + si * 256 : OFF_DUMMY;
+        s_stage[x] = valid ? (is_a ? SSA_B : SSB_B) : 0;
     }
 
     const uint32_t smem0 = lds_addr(reinterpret_cast<const uint16_t*>(smem));
 
     struct Desc {
         __amdgpu_buffer_rsrc_t ra, rb, rsa, rsb;
-        int kb0;      // first byte of k of this step
-        bool chk;
+        uint32_t kmask;   // kOOB for this lane's chunk when it is past K, else 0
     };
-    const int nkt = (K + BKE - 1) / BKE;
-    const int nfull = K / BKE;
+    // this slice's K steps: [kt0, kt1)
+    const int nkt_all = (K + BKE - 1) / BKE;
+    const int per_slice = (nkt_all + NS - 1) / NS;
+    const int kt0 = slice * per_slice;
+    const int kt1 = kt0 + per_slice < nkt_all ? kt0 + per_slice : nkt_all;
+    const int nkt = kt1 > kt0 ? kt1 - kt0 : 0;
+    // Descriptor ranges, clamped once: each step's descriptor starts at the
+    // step's first byte of k, so its range is the tile's range less that
+    // offset (the planner keeps 256 rows plus K bytes under 2^31, so a clamped
+    // range still covers every offset a step uses); scale rows are read whole
+    // up to their row stride (a multiple of 4).  Per step this is 32-bit
+    // scalar arithmetic only.
+    const uint8_t* a_base = p.A + static_cast<int64_t>(m0) * p.lda;
+    const uint8_t* b_base = p.B + static_cast<int64_t>(n0) * p.ldb;
+    const uint8_t* sa_base = p.SA + static_cast<int64_t>(m0) * p.ldsa;
+    const uint8_t* sb_base = p.SB + static_cast<int64_t>(n0) * p.ldsb;
+    const uint32_t a_rec = clamp_records(static_cast<int64_t>(M - 1 - m0) * p.lda + kbytes);
+    const uint32_t b_rec = clamp_records(static_cast<int64_t>(N - 1 - n0) * p.ldb + kbytes);
+    const uint32_t sa_rec = clamp_records(static_cast<int64_t>(M - m0) * p.ldsa);
+    const uint32_t sb_rec = clamp_records(static_cast<int64_t>(N - n0) * p.ldsb);
     auto make_desc = [&](int kt) {
         Desc d;
-        d.kb0 = kt * ROWB;
-        const bool live = kt < nkt;
-        const int kb = live ? d.kb0 : 0;
-        const int sb = live ? kt * NBLK : 0;
-        d.ra = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p.A + static_cast<int64_t>(m0) * p.lda + kb), 0,
-                                                 live ? clamp_records(static_cast<int64_t>(M - 1 - m0) * p.lda +
-                                                                      (kbytes - d.kb0))
-                                                      : 0u,
+        const int kb0 = kt * ROWB;
+        const bool live = kt < kt1;   // steps past the slice (kept for a uniform ring) read nothing
+        const uint32_t kb = live ? static_cast<uint32_t>(kb0) : 0u;
+        const uint32_t sb = live ? static_cast<uint32_t>(kt * NBLK) : 0u;
+        d.ra = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a_base + kb), 0, live ? a_rec - kb : 0u,
                                                  kRsrcWord3);
-        d.rb = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p.B + static_cast<int64_t>(n0) * p.ldb + kb), 0,
-                                                 live ? clamp_records(static_cast<int64_t>(N - 1 - n0) * p.ldb +
-                                                                      (kbytes - d.kb0))
-                                                      : 0u,
+        d.rb = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(b_base + kb), 0, live ? b_rec - kb : 0u,
                                                  kRsrcWord3);
-        // scale rows are read whole up to their row stride (a multiple of 4)
-        d.rsa = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<uint8_t*>(p.SA + static_cast<int64_t>(m0) * p.ldsa + sb), 0,
-            live ? clamp_records(static_cast<int64_t>(M - m0) * p.ldsa - sb) : 0u, kRsrcWord3);
-        d.rsb = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<uint8_t*>(p.SB + static_cast<int64_t>(n0) * p.ldsb + sb), 0,
-            live ? clamp_records(static_cast<int64_t>(N - n0) * p.ldsb - sb) : 0u, kRsrcWord3);
-        d.chk = edge || kt >= nfull;
+        d.rsa = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(sa_base + sb), 0, live ? sa_rec - sb : 0u,
+                                                  kRsrcWord3);
+        d.rsb = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(sb_base + sb), 0, live ? sb_rec - sb : 0u,
+                                                  kRsrcWord3);
+        d.kmask = kb0 + ld_chunk * 16 < kbytes ? 0u : kOOB;
         return d;
     };
     // Load number X of a K step into stage s: A's operand loads, B's, then the scale loads.
@@ -209,28 +249,17 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mx_kernel(MxArgs p) {
         if constexpr (X < IA_W + IB_W) {
             constexpr bool IS_A = X < IA_W;
             constexpr int Y = IS_A ? X : X - IA_W;
-            uint32_t v = IS_A ? a_voff : b_voff;
-            const uint32_t so = Y * (IS_A ? a_step : b_step);
-            if (d.chk) {
-                const int row = ld_row + Y * NW * R;
-                const bool ok = (IS_A ? m0 + row < M : n0 + row < N) && d.kb0 + ld_chunk * 16 < kbytes;
-                v = ok ? v : kOOB;
-            }
+            const uint32_t v = (IS_A ? a_vo[Y] : b_vo[Y]) | d.kmask;
             // (a non-const local: clang's host pass drops the kernel when the
             // builtin is handed a member of a const reference)
             __amdgpu_buffer_rsrc_t r = IS_A ? d.ra : d.rb;
             const int dst = (IS_A ? s * SA_B : OFF_B + s * SB_B) + (Y * NW + wave) * 1024;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(smem + dst), 16, v, so, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(smem + dst), 16, v, 0, 0, 0);
         } else {
             constexpr int S = X - IA_W - IB_W;
-            const int si = S * NW + wave;
-            __amdgpu_buffer_rsrc_t r = si < SIA ? d.rsa : d.rsb;
-            const bool in_rows = si < SIA ? m0 + s_row[S] < M : n0 + s_row[S] < N;
-            uint32_t v = (si < SI && in_rows) ? s_voff[S] : kOOB;
-            const int dst = si < SIA ? OFF_S + s * SSA_B + si * 256
-                            : si < SI ? OFF_SB + s * SSB_B + (si - SIA) * 256
-                                      : OFF_DUMMY;   // no row left for this wave: zeros into a scratch slot
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(smem + dst), 4, v, 0, 0, 0);
+            __amdgpu_buffer_rsrc_t r = (S < NSA) ? d.rsa : d.rsb;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(smem + s_dst[S] + s * s_stage[S]), 4, s_voff[S],
+                                                    0, 0, 0);
         }
     };
     auto issue_tile = [&](int kt, int s) {
@@ -391,7 +420,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mx_kernel(MxArgs p) {
 
     constexpr int UNROLL = (ST % 2 == 0) ? ST : 2 * ST;   // stage, fragment and tile slots repeat
     if (nkt > 0) {
-        static_for<ST>([&](auto t_tag) { issue_tile(decltype(t_tag)::value, decltype(t_tag)::value); });
+        static_for<ST>([&](auto t_tag) { issue_tile(kt0 + decltype(t_tag)::value, decltype(t_tag)::value); });
         wait_vm<(ST - 1) * L>();
         __builtin_amdgcn_s_barrier();
         static_for<NRF + NRS>([&](auto r_tag) {
@@ -399,14 +428,96 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mx_kernel(MxArgs p) {
                     std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, r_tag);
         });
         wait_frags(std::integral_constant<int, 0>{});
-        mask_scales(std::integral_constant<int, 0>{}, 0);
+        mask_scales(std::integral_constant<int, 0>{}, kt0);
         for (int j = 0; j < nkt; j += UNROLL) {
             static_for<UNROLL>([&](auto u_tag) {
-                if (j + decltype(u_tag)::value < nkt) step(u_tag, j + decltype(u_tag)::value);
+                if (j + decltype(u_tag)::value < nkt) step(u_tag, kt0 + j + decltype(u_tag)::value);
             });
         }
         // no load may still be writing this workgroup's LDS when it exits
         wait_vm<0>();
+    }
+
+    // ---- K slices across workgroups: each slice publishes its fp32 partial
+    // tile in register order, [tile][slice][wave][block][lane][4 floats]; the
+    // workgroup that arrives last at the tile's counter adds the slices in
+    // slice order (so the result does not depend on arrival order) into acc
+    // and goes on to the epilogue; the others are done.  Partials move with
+    // system-scope accesses (past the per-XCD L2 caches).
+    constexpr int NB = FM * FN * 4;                   // 16-byte runs per lane
+    if constexpr (NB <= 16) if (NS > 1) {
+        constexpr int64_t WAVE_F = static_cast<int64_t>(NB) * 64 * 4;   // floats per wave per slice
+        int* counters = static_cast<int*>(p.ws);
+        float* tile_part = reinterpret_cast<float*>(static_cast<char*>(p.ws) + kCounterBytes) +
+                           static_cast<int64_t>(tile_lin) * NS * NW * WAVE_F;
+        const __amdgpu_buffer_rsrc_t pr = __builtin_amdgcn_make_buffer_rsrc(
+            tile_part, 0, clamp_records(static_cast<int64_t>(NS) * NW * WAVE_F * 4), kRsrcWord3);
+        auto run_off = [&](int sl, int b) {
+            return static_cast<uint32_t>(((static_cast<int64_t>(sl) * NW + wave) * WAVE_F + (b * 64 + lane) * 4) * 4);
+        };
+        // run b = (i * FN + j) * 4 + q holds registers 4q..4q+3 of acc[i][j]
+        auto get_run = [&](auto b_tag) {
+            constexpr int B = decltype(b_tag)::value;
+            constexpr int I = B / 4 / FN, J = (B / 4) % FN, Q = B % 4;
+            f32x4 v;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) v[r] = acc[I][J][4 * Q + r];
+            return v;
+        };
+        auto set_run = [&](auto b_tag, const f32x4& v) {
+            constexpr int B = decltype(b_tag)::value;
+            constexpr int I = B / 4 / FN, J = (B / 4) % FN, Q = B % 4;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[I][J][4 * Q + r] = v[r];
+        };
+        static_for<NB>([&](auto b_tag) {
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, get_run(b_tag)), pr,
+                                                   run_off(slice, decltype(b_tag)::value), 0, kSysScope);
+        });
+        wait_vm<0>();
+        __syncthreads();
+        int* last = reinterpret_cast<int*>(smem);
+        if (tid == 0)
+            *last = __hip_atomic_fetch_add(&counters[tile_lin], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) ==
+                    NS - 1;
+        __syncthreads();
+        if (!*last) return;
+        // slices in order into acc, in units of HB runs, the next unit in
+        // flight while one is added (two units of registers)
+        constexpr int HB = (NB <= 8) ? NB : NB / 2;
+        constexpr int UPS = NB / HB;
+        f32x4 buf[2][HB];
+        auto fetch = [&](int u, int bb) {
+            const int sl = u / UPS, b0 = (u % UPS) * HB;
+#pragma unroll
+            for (int b = 0; b < HB; ++b)
+                buf[bb][b] = __builtin_bit_cast(
+                    f32x4, __builtin_amdgcn_raw_buffer_load_b128(pr, run_off(sl, b0 + b), 0, kSysScope));
+        };
+        auto add = [&](int u, int bb) {
+            static_for<UPS>([&](auto h_tag) {
+                constexpr int H = decltype(h_tag)::value;
+                if (u % UPS == H) {
+                    static_for<HB>([&](auto b_tag) {
+                        constexpr int B = H * HB + decltype(b_tag)::value;
+                        const f32x4 cur = (u < UPS) ? f32x4{0.0f, 0.0f, 0.0f, 0.0f}
+                                                    : get_run(std::integral_constant<int, B>{});
+                        set_run(std::integral_constant<int, B>{}, cur + buf[bb][decltype(b_tag)::value]);
+                    });
+                }
+            });
+        };
+        const int nu = NS * UPS;
+        fetch(0, 0);
+        for (int u = 0; u < nu; u += 2) {
+            if (u + 1 < nu) fetch(u + 1, 1);
+            add(u, 0);
+            if (u + 1 < nu) {
+                if (u + 2 < nu) fetch(u + 2, 0);
+                add(u + 1, 1);
+            }
+        }
+        if (tid == 0) __hip_atomic_store(&counters[tile_lin], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     }
 
     // ---- epilogue: + C in fp32, round to the output type, masked store.
@@ -457,15 +568,22 @@ hipError_t launch_mx(const MxArgs& a, int64_t grid, hipStream_t stream) {
     return hipGetLastError();
 }
 
+constexpr int kMaxMxSplits = 64;
+
+// LDS bytes: operand stages, scale stages (each operand's region a whole
+// number of 256-byte load instructions), one scratch slot.
 constexpr int64_t mx_lds(int bm, int bn, int st, int fa) {
-    return static_cast<int64_t>(st) * (bm + bn) * 128 + static_cast<int64_t>(st) * (bm + bn) * (fa == kMxE2M1 ? 8 : 4) +
+    return static_cast<int64_t>(st) * (bm + bn) * 128 +
+           static_cast<int64_t>(st) * 256 *
+               ((bm * (fa == kMxE2M1 ? 8 : 4) + 255) / 256 + (bn * (fa == kMxE2M1 ? 8 : 4) + 255) / 256) +
            256;
 }
 
 #define DTG_STR2(x) #x
 #define DTG_STR(x) DTG_STR2(x)
 #define MX_ENTRY(BM, BN, WM, WN, ST, FA, FB)                                                                    \
-    {BM, BN, (FA == kMxE2M1 ? 256 : 128), ST, 32, WM, WN, FA, FB, 64 * WM * WN, mx_lds(BM, BN, ST, FA),      \
+    {BM, BN, (FA == kMxE2M1 ? 256 : 128), ST, 32, WM, WN, FA, FB,                                            \
+     ((BM / WM / 32) * (BN / WN / 32) * 4 <= 16 ? kMaxMxSplits : 1), 64 * WM * WN, mx_lds(BM, BN, ST, FA),   \
      &launch_mx<BM, BN, WM, WN, ST, FA, FB>,                                                                   \
      "gemm_mx_kernel<" DTG_STR(BM) "," DTG_STR(BN) "," DTG_STR(WM) "," DTG_STR(WN) "," DTG_STR(ST) ","        \
      DTG_STR(FA) "," DTG_STR(FB) ">"}
@@ -473,12 +591,13 @@ constexpr int64_t mx_lds(int bm, int bn, int st, int fa) {
     MX_ENTRY(BM, BN, WM, WN, ST, 0, 0), MX_ENTRY(BM, BN, WM, WN, ST, 1, 1), MX_ENTRY(BM, BN, WM, WN, ST, 0, 1), \
     MX_ENTRY(BM, BN, WM, WN, ST, 1, 0), MX_ENTRY(BM, BN, WM, WN, ST, 4, 4)
 
-// (a 256 x 256 tile needs more than the 256 registers a lane has at two
-// waves per SIMD: 128 accumulators plus two slots of 8-bit fragments)
 const MxEntry kMxTable[] = {
+    MX_FORMATS(256, 256, 2, 4, 2),
     MX_FORMATS(256, 128, 4, 2, 2),
     MX_FORMATS(128, 256, 2, 4, 2),
     MX_FORMATS(128, 128, 2, 2, 3),
+    // decode regime: 32-row slabs, K slices across workgroups
+    MX_FORMATS(32, 256, 1, 4, 2),
 };
 
 }  // namespace

@@ -26,6 +26,8 @@ struct MxArgs {
     int32_t out;         // output type: 0 fp16, 1 bf16, 2 fp32
     int64_t lda, ldb, ldsa, ldsb;
     int64_t ldc, ldd;
+    int32_t splits;      // K slices across workgroups (1 = none)
+    void* ws;            // workspace of the K slices (same layout as the 16-bit kernels')
 };
 
 typedef hipError_t (*mx_launch_fn)(const MxArgs& args, int64_t grid, hipStream_t stream);
@@ -39,6 +41,7 @@ struct MxEntry {
     int32_t bk;          // k per K step (elements): 128 bytes of k per row
     int32_t stages, mfma, waves_m, waves_n;
     int32_t fmt_a, fmt_b;
+    int32_t splitk;      // most K slices the variant takes (1: none)
     int32_t threads;
     int64_t lds_bytes;
     mx_launch_fn launch;

@@ -374,6 +374,49 @@ __global__ __launch_bounds__(512) void probe_mfma_rate_kernel(int iters, float* 
     }
 }
 
+// Register-only loop of scaled matrix instructions (v_mfma_scale_f32_*_f8f6f4,
+// element format FMT for both operands, scale 1.0): the issue rate of the
+// block-scaled contraction with no memory traffic.  Same clocks as
+// probe_mfma_rate_kernel.
+template <int MF, int FMT>
+__global__ __launch_bounds__(512) void probe_mfma_scaled_rate_kernel(int iters, float* out, uint64_t* clk) {
+    typedef int i32x8 __attribute__((ext_vector_type(8)));
+    const int l = threadIdx.x & 63;
+    i32x8 a, b;
+    for (int d = 0; d < 8; ++d) {
+        a[d] = static_cast<int>(0x38383838u ^ static_cast<uint32_t>((l * 7 + d) & 3));
+        b[d] = static_cast<int>(0x30303030u ^ static_cast<uint32_t>((l * 5 + d) & 3));
+    }
+    const int sc = 0x7f7f7f7f;
+    const uint64_t t0 = __builtin_readcyclecounter();
+    const uint64_t r0 = __builtin_amdgcn_s_memrealtime();
+    float sum = 0.0f;
+    if constexpr (MF == 16) {
+        f32x4 acc[32];
+        for (int i = 0; i < 32; ++i) acc[i] = f32x4{static_cast<float>(i), 0, 0, 0};
+        for (int it = 0; it < iters; ++it)
+#pragma unroll
+            for (int i = 0; i < 32; ++i)
+                acc[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc[i], FMT, FMT, 0, sc, 0, sc);
+        for (int i = 0; i < 32; ++i) sum += acc[i][0] + acc[i][3];
+    } else {
+        f32x16 acc[8];
+        for (int i = 0; i < 8; ++i) { acc[i] = f32x16{}; acc[i][0] = static_cast<float>(i); }
+        for (int it = 0; it < iters; ++it)
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                acc[i & 7] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc[i & 7], FMT, FMT, 0, sc, 0, sc);
+        for (int i = 0; i < 8; ++i) sum += acc[i][0] + acc[i][15];
+    }
+    const uint64_t r1 = __builtin_amdgcn_s_memrealtime();
+    const uint64_t t1 = __builtin_readcyclecounter();
+    out[blockIdx.x * blockDim.x + threadIdx.x] = sum;
+    if (threadIdx.x == 0) {
+        clk[2 * blockIdx.x] = t1 - t0;
+        clk[2 * blockIdx.x + 1] = r1 - r0;
+    }
+}
+
 // probe_lds_fill_rate: each 8-wave workgroup owns 64 KiB of `src` (its block
 // index selects the slice; the slices stay in L2 after the first pass) and
 // fills its 64 KiB of LDS from it `iters` times; every wave moves 8 KiB per
@@ -648,6 +691,21 @@ int probe_mfma_rate(int mf, int waves, int iters, int grid, float* out, uint64_t
     if (waves < 1 || waves > 8 || grid < 1 || iters < 0) return static_cast<int>(hipErrorInvalidValue);
     if (mf == 16) hipLaunchKernelGGL(probe_mfma_rate_kernel<16>, dim3(grid), dim3(64 * waves), 0, s, iters, out, clk);
     else if (mf == 32) hipLaunchKernelGGL(probe_mfma_rate_kernel<32>, dim3(grid), dim3(64 * waves), 0, s, iters, out, clk);
+    else return static_cast<int>(hipErrorInvalidValue);
+    return static_cast<int>(hipGetLastError());
+}
+
+// Scaled-instruction rate: mf 16 or 32, fmt 0 (E4M3) or 4 (E2M1), waves 1..8;
+// out: grid * 64 * waves floats, clk: 2 * grid uint64.  Returns a hipError_t value.
+int probe_mfma_scaled_rate(int mf, int fmt, int waves, int iters, int grid, float* out, uint64_t* clk,
+                           void* stream) {
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (waves < 1 || waves > 8 || grid < 1 || iters < 0) return static_cast<int>(hipErrorInvalidValue);
+    const dim3 g(grid), b(64 * waves);
+    if (mf == 16 && fmt == 0) hipLaunchKernelGGL((probe_mfma_scaled_rate_kernel<16, 0>), g, b, 0, s, iters, out, clk);
+    else if (mf == 16 && fmt == 4) hipLaunchKernelGGL((probe_mfma_scaled_rate_kernel<16, 4>), g, b, 0, s, iters, out, clk);
+    else if (mf == 32 && fmt == 0) hipLaunchKernelGGL((probe_mfma_scaled_rate_kernel<32, 0>), g, b, 0, s, iters, out, clk);
+    else if (mf == 32 && fmt == 4) hipLaunchKernelGGL((probe_mfma_scaled_rate_kernel<32, 4>), g, b, 0, s, iters, out, clk);
     else return static_cast<int>(hipErrorInvalidValue);
     return static_cast<int>(hipGetLastError());
 }

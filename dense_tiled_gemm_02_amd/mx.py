@@ -39,7 +39,9 @@ MX_SIGNATURES = [
     ("gemm_mx_plan_config", ctypes.c_int, [_p, ctypes.POINTER(gemm_config)]),
     ("gemm_mx_plan_launch", ctypes.c_int, [_p, ctypes.POINTER(_i64), ctypes.POINTER(_i32), ctypes.POINTER(_i64)]),
     ("gemm_mx_plan_describe", ctypes.c_int, [_p, ctypes.c_char_p, ctypes.c_size_t]),
-    ("gemm_mx_run", ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _p]),
+    ("gemm_mx_workspace_size", ctypes.c_int, [_p, ctypes.POINTER(ctypes.c_size_t)]),
+    ("gemm_mx_workspace_init", ctypes.c_int, [_p, _p, ctypes.c_size_t, _p]),
+    ("gemm_mx_run", ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _p, ctypes.c_size_t, _p]),
 ]
 
 _ready = False
@@ -117,9 +119,19 @@ def gemm_mx_plan_describe(plan):
     return buf.value.decode()
 
 
-def gemm_mx_run(plan, A, SA, B, SB, C, D, stream=None):
+def gemm_mx_workspace_size(plan):
+    n = ctypes.c_size_t()
+    _check(mxlib().gemm_mx_workspace_size(plan.handle, ctypes.byref(n)))
+    return n.value
+
+
+def gemm_mx_workspace_init(plan, workspace, workspace_bytes, stream=None):
+    _check(mxlib().gemm_mx_workspace_init(plan.handle, workspace, workspace_bytes, stream))
+
+
+def gemm_mx_run(plan, A, SA, B, SB, C, D, workspace=None, workspace_bytes=0, stream=None):
     """Device addresses (integers or None) and a hipStream_t (or None)."""
-    _check(mxlib().gemm_mx_run(plan.handle, A, SA, B, SB, C, D, stream))
+    _check(mxlib().gemm_mx_run(plan.handle, A, SA, B, SB, C, D, workspace, workspace_bytes, stream))
 
 
 # ---------------------------------------------------------------- torch convenience
@@ -188,9 +200,27 @@ def mx_matmul(A, SA, B, SB, K, fmt_a="e4m3", fmt_b=None, C=None, out=None, out_d
         stream = torch.cuda.current_stream(A.device).cuda_stream
     elif hasattr(stream, "cuda_stream"):
         stream = stream.cuda_stream
+    ws, ws_bytes = _workspace(pl, dev, stream)
     gemm_mx_run(pl, A.data_ptr(), SA.data_ptr(), B.data_ptr(), SB.data_ptr(),
-                C.data_ptr() if C is not None else None, out.data_ptr(), stream)
+                C.data_ptr() if C is not None else None, out.data_ptr(), ws, ws_bytes, stream)
     return out
+
+
+_ws = {}
+
+
+def _workspace(plan, device, stream):
+    """A zero-filled workspace of at least the plan's size, one per (device,
+    stream), grown on demand (launches leave it ready for reuse)."""
+    import torch
+    need = gemm_mx_workspace_size(plan)
+    if need == 0:
+        return None, 0
+    buf = _ws.get((device, stream))
+    if buf is None or buf.numel() < need:
+        buf = torch.zeros(max(need, 1 << 20), dtype=torch.uint8, device="cuda:%d" % device)
+        _ws[(device, stream)] = buf
+    return buf.data_ptr(), buf.numel()
 
 
 __all__ = ["GemmError", "gemm_last_error"] + [n for n, _, _ in MX_SIGNATURES]

@@ -2,11 +2,12 @@
 
     python -m dense_tiled_gemm_02_amd.probes
 
-Runs three probe kernels of libgemm_probe.so on 256 workgroups of 8 waves
+Runs the probe kernels of libgemm_probe.so on 256 workgroups of 8 waves
 and prints one table each:
   * matrix-core rate: register-only MFMA loops (16x16x32 and 32x32x16 bf16),
     with the shader clock under that load (s_memtime against the 100 MHz
-    s_memrealtime);
+    s_memrealtime), and the same for the block-scaled instructions (E4M3 and
+    E2M1 operands);
   * LDS fill rate: bytes per clock per CU that reach LDS from L2-resident
     data, by direct global -> LDS loads and by global -> VGPR loads plus LDS
     writes, alone and beside 16-byte LDS reads;
@@ -28,6 +29,7 @@ def _lib():
     L.probe_mfma_rate.argtypes = [ctypes.c_int] * 4 + [ctypes.c_void_p] * 3
     L.probe_lds_fill_rate.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
                                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    L.probe_mfma_scaled_rate.argtypes = [ctypes.c_int] * 5 + [ctypes.c_void_p] * 3
     L.probe_mfma_mix.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
                                  ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
     return L
@@ -55,6 +57,26 @@ def mfma_rate(L, stream):
         ghz = (c[:, 0] / (c[:, 1] / 100e6) / 1e9).mean().item()
         flop = grid * waves * iters * 524288
         print("  %dx%d: %.0f TFLOP/s, shader clock %.2f GHz" % (mf, mf, flop / ms / 1e9, ghz))
+
+
+def mfma_scaled_rate(L, stream):
+    print("block-scaled matrix-core rate (v_mfma_scale_*_f8f6f4), register operands, 8 waves, 256 workgroups")
+    grid, iters, waves = 256, 2000, 8
+    out = torch.empty(grid * 64 * waves, device="cuda")
+    clk = torch.zeros(2 * grid, dtype=torch.int64, device="cuda")
+    for mf in (16, 32):
+        for fmt, name in ((0, "E4M3"), (4, "E2M1")):
+            assert L.probe_mfma_scaled_rate(mf, fmt, waves, 10, grid, out.data_ptr(), clk.data_ptr(), stream) == 0
+            torch.cuda.synchronize()
+            ms = _timed(lambda: L.probe_mfma_scaled_rate(mf, fmt, waves, iters, grid, out.data_ptr(),
+                                                         clk.data_ptr(), stream))
+            c = clk.cpu().view(-1, 2).double()
+            ghz = (c[:, 0] / (c[:, 1] / 100e6) / 1e9).mean().item()
+            per = 32 if mf == 16 else 16                          # instructions per iteration
+            flop = grid * waves * iters * per * (2 * 16 * 16 * 128 if mf == 16 else 2 * 32 * 32 * 64)
+            cyc = c[:, 0].mean().item() / (iters * per) * 4 / waves   # SIMD cycles per instruction (2 waves/SIMD)
+            print("  %dx%d %s: %.0f TFLOP/s, shader clock %.2f GHz, %.1f cycles per instruction per SIMD" % (
+                mf, mf, name, flop / ms / 1e9, ghz, cyc))
 
 
 def lds_fill(L, stream):
@@ -108,6 +130,7 @@ def main():
     L = _lib()
     stream = torch.cuda.current_stream().cuda_stream
     mfma_rate(L, stream)
+    mfma_scaled_rate(L, stream)
     lds_fill(L, stream)
     mfma_mix(L, stream)
 

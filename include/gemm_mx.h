@@ -88,8 +88,11 @@ typedef struct gemm_mx_plan gemm_mx_plan;   /* opaque, immutable after creation 
 
 /* Validate *prob and choose a tile configuration for HIP device `device`.
  * force may be NULL; its non-zero fields bm, bn, stages, waves_m, waves_n,
- * group_m and xcd_remap override the planner (kernel, bk, mfma and splitk
- * must be 0 or the values the plan reports).  No device work. */
+ * splitk, group_m and xcd_remap override the planner (kernel, bk and mfma
+ * must be 0 or the values the plan reports).  Plans whose output has few
+ * tiles split K across workgroups ("Tuning Triton kernels", section 6: a K
+ * split of 2 is the one knob that helped the FP4 GEMM at M = 16) and need a
+ * workspace (gemm_mx_workspace_size).  No device work. */
 gemm_status gemm_mx_plan_create(const gemm_mx_problem* prob, int device, const gemm_config* force,
                                 gemm_mx_plan** out);
 
@@ -102,7 +105,8 @@ void gemm_mx_plan_destroy(gemm_mx_plan* plan);
 
 /* The configuration a plan runs: kernel = 4 (block-scaled tile kernel),
  * bk = k per K step in elements, mfma = 32 (32x32x64 scaled instruction),
- * splitk = 1. */
+ * splitk = K slices across workgroups (their fp32 partial tiles summed in
+ * slice order by the last workgroup of each tile: deterministic). */
 gemm_status gemm_mx_plan_config(const gemm_mx_plan* plan, gemm_config* out);
 
 /* Launch geometry: grid (workgroups), threads per workgroup, LDS bytes. */
@@ -111,13 +115,26 @@ gemm_status gemm_mx_plan_launch(const gemm_mx_plan* plan, int64_t* grid, int32_t
 /* One-line NUL-terminated description of the plan into buf[0..len). */
 gemm_status gemm_mx_plan_describe(const gemm_mx_plan* plan, char* buf, size_t len);
 
+/* Device workspace the plan needs in bytes (0 unless splitk > 1).  Same layout
+ * as gemm.h's: a fixed 16 KiB region of per-tile arrival counters, then the
+ * fp32 partial tiles, so one workspace serves plans of both headers. */
+gemm_status gemm_mx_workspace_size(const gemm_mx_plan* plan, size_t* bytes);
+
+/* Zero-fill a workspace for the plan on `stream` (as gemm_workspace_init):
+ * needed once before its first use; every launch leaves it ready again.
+ * GEMM_ERR_WORKSPACE if NULL or smaller than gemm_mx_workspace_size. */
+gemm_status gemm_mx_workspace_init(const gemm_mx_plan* plan, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Enqueue D = A x B (+ C) on `stream`.  A, SA, B, SB, D are device pointers; C
  * is a device pointer when has_c = 1 and NULL otherwise.  D may equal C (same
  * ldc and ldd); any other overlap of D with an input is GEMM_ERR_INVALID_ARG.
+ * workspace may be NULL when gemm_mx_workspace_size reports 0; otherwise at
+ * least that many bytes, 256-byte aligned, prepared by gemm_mx_workspace_init
+ * (else GEMM_ERR_WORKSPACE); one workspace serves one launch at a time.
  * M = 0 or N = 0 launches nothing; K = 0 writes D = C (or zeros).  Alignment
  * or stride violations are GEMM_ERR_UNSUPPORTED. */
 gemm_status gemm_mx_run(const gemm_mx_plan* plan, const void* A, const void* SA, const void* B, const void* SB,
-                        const void* C, void* D, void* stream);
+                        const void* C, void* D, void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

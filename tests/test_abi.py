@@ -39,7 +39,7 @@ def test_library_exports_every_declared_function():
         assert hasattr(L, n), n
     assert sorted(n for n, _, _ in g.SIGNATURES) == names
     mx_names = declared_functions("gemm_mx.h")
-    assert len(mx_names) == 7
+    assert len(mx_names) == 9
     L = mx.mxlib()
     for n in mx_names:
         assert hasattr(L, n), n
@@ -288,13 +288,23 @@ def test_mx_plans_fit_the_device_and_pick_by_tile_count():
             p = mx_plan(M, N, K, fmt)
             c = p.config
             grid, threads, lds = mx.gemm_mx_plan_launch(p)
-            assert c.kernel == mx.KERNEL_MX and c.mfma == 32 and c.splitk == 1
+            assert c.kernel == mx.KERNEL_MX and c.mfma == 32 and c.splitk >= 1
             assert c.bk == (256 if fmt == "e2m1" else 128)
             assert lds <= 160 * 1024 and threads in (256, 512)
-            assert grid == -(-M // c.bm) * -(-N // c.bn)
+            assert grid == -(-M // c.bm) * -(-N // c.bn) * c.splitk
+            assert (mx.gemm_mx_workspace_size(p) > 0) == (c.splitk > 1)
             assert ("fmt=%d/%d" % (mx.FORMATS[fmt], mx.FORMATS[fmt])) in p.describe()
-    assert (mx_plan(4096, 4096, 4096).config.bm, mx_plan(4096, 4096, 4096).config.bn) == (256, 128)
+    assert (mx_plan(4096, 4096, 4096).config.bm, mx_plan(4096, 4096, 4096).config.bn) == (256, 256)
     assert (mx_plan(512, 512, 1024).config.bm, mx_plan(512, 512, 1024).config.bn) == (128, 128)
+    # decode regime: 32-row slabs with K slices and a workspace
+    d = mx_plan(16, 8192, 8192, "e2m1")
+    c = d.config
+    assert (c.bm, c.bn, c.splitk) == (32, 256, 8)
+    assert mx.gemm_mx_workspace_size(d) == 16384 + 32 * 8 * 32 * 256 * 4
+    assert mx.gemm_mx_workspace_size(mx_plan(4096, 4096, 4096)) == 0
+    # few square tiles over a deep K: slices of at least 8 K steps
+    c = mx_plan(512, 512, 32768).config
+    assert (c.bm, c.bn, c.splitk) == (128, 128, 16)
     p = mx_plan(4096, 4096, 4096, fmt_b="e5m2")
     assert "fmt=0/1" in p.describe()
 
@@ -302,7 +312,7 @@ def test_mx_plans_fit_the_device_and_pick_by_tile_count():
 def test_mx_forced_config_is_honoured_or_rejected():
     p = mx.gemm_mx_plan_create_for(mx.mx_problem(4096, 4096, 4096), fake_gfx950(), {"bm": 128, "bn": 256})
     assert (p.config.bm, p.config.bn) == (128, 256)
-    for bad in ({"bm": 64}, {"splitk": 2}, {"mfma": 16}, {"kernel": 3}):
+    for bad in ({"bm": 64}, {"bm": 256, "bn": 256, "splitk": 2}, {"mfma": 16}, {"kernel": 3}, {"splitk": 65}):
         with pytest.raises(g.GemmError) as e:
             mx.gemm_mx_plan_create_for(mx.mx_problem(4096, 4096, 4096), fake_gfx950(), bad)
         assert e.value.status == g.GEMM_ERR_UNSUPPORTED, bad
@@ -349,5 +359,12 @@ def test_mx_run_rejects_bad_pointers_without_launching():
     with pytest.raises(g.GemmError) as e:                      # D overlaps A
         mx.gemm_mx_run(p, 0x100000, 0x200000, 0x300000, 0x400000, None, 0x100100)
     assert e.value.status == g.GEMM_ERR_INVALID_ARG
+    d = mx_plan(16, 8192, 8192, "e2m1")                        # needs a workspace
+    with pytest.raises(g.GemmError) as e:
+        mx.gemm_mx_run(d, 0x100000, 0x2000000, 0x3000000, 0x8000000, None, 0x9000000)
+    assert e.value.status == g.GEMM_ERR_WORKSPACE
+    with pytest.raises(g.GemmError) as e:
+        mx.gemm_mx_run(d, 0x100000, 0x2000000, 0x3000000, 0x8000000, None, 0x9000000, 0xA000010, 1 << 24)
+    assert e.value.status == g.GEMM_ERR_WORKSPACE              # not 256-byte aligned
     # an empty output launches nothing and succeeds without any pointer
     mx.gemm_mx_run(mx_plan(0, 128, 128), None, None, None, None, None, None)

@@ -22,7 +22,7 @@ import oracle
 pytestmark = pytest.mark.gpu
 
 PAIRS = [("e4m3", "e4m3"), ("e5m2", "e5m2"), ("e4m3", "e5m2"), ("e5m2", "e4m3"), ("e2m1", "e2m1")]
-TILES = [(256, 128), (128, 256), (128, 128)]
+TILES = [(256, 256), (256, 128), (128, 256), (128, 128)]
 OUT = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}
 
 
@@ -121,11 +121,11 @@ def test_k_zero_writes_the_addend_and_empty_outputs_launch_nothing():
     pl = mx.gemm_mx_plan_create(p, 0)
     D = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
     mx.gemm_mx_run(pl, e.data_ptr(), s.data_ptr(), eb.data_ptr(), sb.data_ptr(), C.data_ptr(), D.data_ptr(),
-                   torch.cuda.current_stream().cuda_stream)
+                   stream=torch.cuda.current_stream().cuda_stream)
     torch.cuda.synchronize()
     assert torch.equal(D, C)
     p0 = mx.mx_problem(0, N, 64, "e4m3")
-    mx.gemm_mx_run(mx.gemm_mx_plan_create(p0, 0), None, None, None, None, None, None, None)
+    mx.gemm_mx_run(mx.gemm_mx_plan_create(p0, 0), None, None, None, None, None, None)
 
 
 def test_runs_are_bitwise_reproducible():
@@ -163,3 +163,32 @@ def test_e2m1_products_are_exact_in_binary32():
     ref, S = oracle.mx_gemm_f64(A, SA, B, SB, K, "e2m1", "e2m1")
     n, worst, _ = oracle.mx_tol_check(D.cpu().numpy(), "f32", ref, S, None)
     assert n == 0
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e2m1"])
+@pytest.mark.parametrize("M", [1, 16, 32])
+def test_decode_slabs_with_k_slices(fmt, M):
+    """The decode regime (32-row slabs, K split over workgroups, fused
+    deterministic reduce) against the oracle, with a ragged N and a K whose
+    slices end inside a K step."""
+    N, K = 1000, 3072 + 64
+    A, SA, B, SB = _case(M, N, K, fmt, fmt, 40 + M)
+    p = mx.mx_problem(M, N, K, fmt, lda=A.shape[1], ldb=B.shape[1], ldsa=SA.shape[1], ldsb=SB.shape[1])
+    cfg = mx.gemm_mx_plan_create(p, 0).config
+    assert (cfg.bm, cfg.bn) == (32, 256) and cfg.splitk > 1
+    print("mx decode", fmt, M, cfg.splitk, flush=True)
+    D = _run(A, SA, B, SB, K, fmt, fmt)
+    ref, S, S8 = oracle.mx_gemm_f64(A, SA, B, SB, K, fmt, fmt, runs=True)
+    _check(D, ref, S, S8, "bf16", "decode %s M=%d" % (fmt, M))
+    D2 = _run(A, SA, B, SB, K, fmt, fmt)          # the workspace is left ready for reuse
+    assert torch.equal(D.view(torch.int16), D2.view(torch.int16))
+
+
+@pytest.mark.parametrize("splits", [2, 3, 7])
+def test_forced_k_slices_on_a_square_tile(splits):
+    M, N, K = 300, 200, 2048
+    A, SA, B, SB = _case(M, N, K, "e4m3", "e4m3", 60 + splits)
+    print("mx split", splits, flush=True)
+    D = _run(A, SA, B, SB, K, "e4m3", "e4m3", config={"bm": 128, "bn": 128, "splitk": splits})
+    ref, S, S8 = oracle.mx_gemm_f64(A, SA, B, SB, K, "e4m3", "e4m3", runs=True)
+    _check(D, ref, S, S8, "bf16", "split %d" % splits)
