@@ -126,7 +126,10 @@ bool vec_shape_ok(const gemm_problem* p) {
 }
 
 // The direct-to-LDS kernels address one BM-row panel of A and one BK-row slab
-// of B with 32-bit byte offsets from descriptors rebased every K step.
+// of B with 32-bit byte offsets from descriptors rebased every K step, and
+// rely on the descriptor's range to zero the rows past K of an operand kept
+// as rows of k (A stored K x M, row-major B): that needs its row stride to be
+// at least its contiguous extent (M or N), else the element-wise path runs.
 bool dma_offsets_ok(const gemm_problem* p, const dtg::KernelEntry* e) {
     const int64_t lim = (int64_t(1) << 31) - 4096;
     const bool ta = e->layout > 0 && (e->layout & dtg::kLayTA), tb = e->layout > 0 && (e->layout & dtg::kLayTB);
@@ -134,6 +137,8 @@ bool dma_offsets_ok(const gemm_problem* p, const dtg::KernelEntry* e) {
                          : static_cast<int64_t>(e->bm) * p->sa_m * 2 + e->bk * 2;
     const int64_t b = tb ? static_cast<int64_t>(e->bn) * p->sb_n * 2 + e->bk * 2
                          : static_cast<int64_t>(e->bk) * p->sb_k * 2 + e->bn * 2;
+    if (ta && p->K > 1 && p->sa_k < p->M) return false;
+    if (!tb && p->K > 1 && p->sb_k < p->N) return false;
     return a < lim && b < lim;
 }
 

@@ -156,5 +156,16 @@ __device__ __forceinline__ uint32_t clamp_records(int64_t bytes) {
     return static_cast<uint32_t>(bytes < kMaxRecords ? bytes : kMaxRecords);
 }
 
+// Range of a descriptor that starts `off` bytes into a region of `full` bytes
+// (off <= full), capped at kMaxRecords, in 32-bit operations: with uniform
+// arguments it stays on the scalar unit, with no branch.  A capped range is
+// still inside the region, and covers every offset below the cap.
+__device__ __forceinline__ uint32_t capped_records(uint64_t full, uint64_t off) {
+    const uint64_t r = full - off;
+    const uint32_t hi = static_cast<uint32_t>(r >> 32), lo = static_cast<uint32_t>(r);
+    const uint32_t cap = static_cast<uint32_t>(kMaxRecords);
+    return hi != 0u ? cap : (lo < cap ? lo : cap);
+}
+
 }  // namespace dev
 }  // namespace dtg

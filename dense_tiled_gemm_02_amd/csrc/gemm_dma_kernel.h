@@ -120,7 +120,6 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(KArgs p) {
     }
     const int m0 = pid_m * BM, n0 = pid_n * BN;
     const int M = p.M, N = p.N, K = p.K;
-    const bool edge = (m0 + BM > M) || (n0 + BN > N);
 
     // leading strides of the two operands as they sit in memory (elements)
     const int64_t lda = TA ? p.sak : p.lda;
@@ -129,7 +128,14 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(KArgs p) {
     // ---- per-lane load offsets (bytes, relative to the rebased descriptors).
     // Load X of an operand fills LDS rows X*NW*R + wave*R + lane/CH (its E
     // index when KC, its k index otherwise); c8 is the first element of the
-    // lane's 16-byte chunk along the other index.
+    // lane's 16-byte chunk along the other index.  Bounds cost no branch:
+    //  * KC operand (rows of m or n): rows past the matrix lie past the
+    //    descriptor's range (it ends at the last element and the row stride is
+    //    at least K); the K tail is a per-lane bit OR'd into the offset;
+    //  * operand kept as rows of k: chunks past M (N) get an offset past any
+    //    range once for the kernel; rows past K lie past the range (the row
+    //    stride is at least M or N).
+    // The planner admits only strides for which these hold.
     const int a_row0 = wave * OA::R + lane / OA::CH;
     const int b_row0 = wave * OB::R + lane / OB::CH;
     uint32_t a_voff[OA::NV], b_voff[OB::NV];
@@ -139,6 +145,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(KArgs p) {
         const int row = a_row0 + i * NW * OA::R;
         const int c = (lane % OA::CH) ^ OA::sw(row);
         a_voff[i] = static_cast<uint32_t>(static_cast<int64_t>(row) * lda * 2 + c * 16);
+        if (!AKC && m0 + 8 * c >= M) a_voff[i] = kOOB;
         a_c8[i] = 8 * c;
     }
 #pragma unroll
@@ -146,6 +153,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(KArgs p) {
         const int row = b_row0 + i * NW * OB::R;
         const int c = (lane % OB::CH) ^ OB::sw(row);
         b_voff[i] = static_cast<uint32_t>(static_cast<int64_t>(row) * ldb * 2 + c * 16);
+        if (!BKC && n0 + 8 * c >= N) b_voff[i] = kOOB;
         b_c8[i] = 8 * c;
     }
     const uint32_t a_step = static_cast<uint32_t>(NW * OA::R) * static_cast<uint32_t>(lda) * 2u;
@@ -156,37 +164,37 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(KArgs p) {
 
     // Buffer descriptors of K step kt: each starts at the tile's first element
     // of that step (k0 and m0 / n0) and ends at the matrix's last element, so
-    // any offset past it reads zeros.
+    // any offset past it reads zeros.  The range is the tile's whole range
+    // (64-bit, once) less the step's offset, capped in 32-bit scalar
+    // arithmetic; no per-step branch.
     struct Desc {
         __amdgpu_buffer_rsrc_t ra, rb;
         int k0;
-        bool chk;    // edge tile or K tail: lanes test their own bounds
     };
-    const int nfull = K / BK;
     // this slice's K steps: [kt0, kt1)
     const int nkt_all = (K + BK - 1) / BK;
     const int per_slice = (nkt_all + NS - 1) / NS;
     const int kt0 = slice * per_slice;
     const int kt1 = (kt0 + per_slice < nkt_all) ? kt0 + per_slice : nkt_all;
+    const uint64_t a_full = 2u * static_cast<uint64_t>(AKC ? static_cast<int64_t>(M - 1 - m0) * lda + K
+                                                           : static_cast<int64_t>(K - 1) * lda + (M - m0));
+    const uint64_t b_full = 2u * static_cast<uint64_t>(BKC ? static_cast<int64_t>(N - 1 - n0) * ldb + K
+                                                           : static_cast<int64_t>(K - 1) * ldb + (N - n0));
+    const uint16_t* a_tile = AKC ? p.A + static_cast<int64_t>(m0) * lda : p.A + m0;
+    const uint16_t* b_tile = BKC ? p.B + static_cast<int64_t>(n0) * ldb : p.B + n0;
     auto make_desc = [&](int kt) {
         Desc d;
         d.k0 = kt * BK;
         const bool live = kt < kt1;   // steps past the slice (issued only to keep the ring uniform) read nothing
         const int kb = live ? d.k0 : 0;
-        // k-contiguous: rows of the outer index; otherwise rows of k
-        const uint16_t* abase = AKC ? p.A + static_cast<int64_t>(m0) * lda + kb
-                                    : p.A + static_cast<int64_t>(kb) * lda + m0;
-        const int64_t arec = AKC ? static_cast<int64_t>(M - 1 - m0) * lda + (K - d.k0)
-                                 : static_cast<int64_t>(K - 1 - d.k0) * lda + (M - m0);
-        d.ra = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(abase), 0,
-                                                 live ? clamp_records(arec * 2) : 0u, kRsrcWord3);
-        const uint16_t* bbase = BKC ? p.B + static_cast<int64_t>(n0) * ldb + kb
-                                    : p.B + static_cast<int64_t>(kb) * ldb + n0;
-        const int64_t brec = BKC ? static_cast<int64_t>(N - 1 - n0) * ldb + (K - d.k0)
-                                 : static_cast<int64_t>(K - 1 - d.k0) * ldb + (N - n0);
-        d.rb = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(bbase), 0,
-                                                 live ? clamp_records(brec * 2) : 0u, kRsrcWord3);
-        d.chk = edge || kt >= nfull;
+        const int64_t aoff = AKC ? kb : static_cast<int64_t>(kb) * lda;   // elements
+        const int64_t boff = BKC ? kb : static_cast<int64_t>(kb) * ldb;
+        d.ra = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a_tile + aoff), 0,
+                                                 live ? capped_records(a_full, 2u * static_cast<uint64_t>(aoff)) : 0u,
+                                                 kRsrcWord3);
+        d.rb = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(b_tile + boff), 0,
+                                                 live ? capped_records(b_full, 2u * static_cast<uint64_t>(boff)) : 0u,
+                                                 kRsrcWord3);
         return d;
     };
     // Load number X (A loads first, then B) of a K step into LDS stage s.
@@ -196,11 +204,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(KArgs p) {
             constexpr int V = OA::SHARED ? 0 : X;
             uint32_t v = a_voff[V];
             const uint32_t so = OA::SHARED ? X * a_step : 0u;
-            const int row = a_row0 + X * NW * OA::R;
-            if (d.chk) {
-                const bool ok = AKC ? (m0 + row < M && d.k0 + a_c8[V] < K) : (d.k0 + row < K && m0 + a_c8[V] < M);
-                v = ok ? v : kOOB;
-            }
+            if constexpr (AKC) v |= (d.k0 + a_c8[V] < K) ? 0u : kOOB;
             // (a non-const local: clang's host pass drops the kernel when the
             // builtin is handed a member of a const reference)
             __amdgpu_buffer_rsrc_t r = d.ra;
@@ -211,11 +215,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(KArgs p) {
             constexpr int V = OB::SHARED ? 0 : Y;
             uint32_t v = b_voff[V];
             const uint32_t so = OB::SHARED ? Y * b_step : 0u;
-            const int row = b_row0 + Y * NW * OB::R;
-            if (d.chk) {
-                const bool ok = BKC ? (n0 + row < N && d.k0 + b_c8[V] < K) : (d.k0 + row < K && n0 + b_c8[V] < N);
-                v = ok ? v : kOOB;
-            }
+            if constexpr (BKC) v |= (d.k0 + b_c8[V] < K) ? 0u : kOOB;
             __amdgpu_buffer_rsrc_t r = d.rb;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 r, (lds_void_t*)(smem + ST * SA + s * SB + (Y * NW + wave) * 512), 16, v, so, 0, 0);
