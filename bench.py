@@ -40,15 +40,16 @@ PEAK_BF16_TFLOPS = 256 * 2.4e9 * 4096 / 1e12        # 2516.6
 PEAK_MX_TFLOPS = {"e4m3": 5000.0, "e5m2": 5000.0, "e2m1": 10100.0}   # MI355X dense fp8 / fp4
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
+TRAFFIC_MX_JSON = os.path.join(ROOT, "profiles", "traffic_mx.json")
 
 
-def measured_traffic(kernel_name):
+def measured_traffic(kernel_name, path=TRAFFIC_JSON):
     """HBM bytes per launch of this kernel from the committed counter runs, or
     None if there are none or the kernel sources changed since."""
     try:
         import json as _json
         from dense_tiled_gemm_02_amd import rocprof_summary
-        t = _json.load(open(TRAFFIC_JSON))
+        t = _json.load(open(path))
         if t.get("source_sha256") != rocprof_summary.source_hash():
             return None
         for k, v in t["kernels"].items():
@@ -421,6 +422,7 @@ def mx(args):
             peak = PEAK_MX_TFLOPS[w.fmt_a]
             rec["roofline"] = {"bound": "mfma", "achieved": round(rec["tflops"], 1), "peak": peak,
                                "unit": "TFLOP/s", "frac": rec["tflops"] / peak}
+        rec["roofline"]["traffic"] = measured_traffic(kernel_of(pl.describe()), TRAFFIC_MX_JSON)
         if w.fmt_a == "e4m3" and w.fmt_b == "e4m3":
             try:
                 a8 = dA.view(torch.float8_e4m3fn)
@@ -439,6 +441,19 @@ def mx(args):
                 rec["torch_scaled_mm_error"] = str(e)[:200]
         print(json.dumps(rec), flush=True)
         del Bs, SBs, dA, dSA
+    if args.copy_mb:
+        copy_calibration(args.copy_mb)
+
+
+def copy_calibration(mb):
+    """One device copy of `mb` MiB, the reference kernel of the memory counters."""
+    import torch
+    n = mb * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    return 4 * n
 
 
 def main():
@@ -505,13 +520,7 @@ def main():
                          "tflops": sw.flops() / sms / 1e9}
         del sc
     if args.copy_mb:
-        n = args.copy_mb * (1 << 20) // 4
-        src = torch.ones(n, dtype=torch.float32, device="cuda")
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        rec["copy_calibration_bytes"] = 4 * n
-        del src, dst
+        rec["copy_calibration_bytes"] = copy_calibration(args.copy_mb)
     if not args.no_cpu:
         cb = cpu_baseline(w, args.cpu_seconds)
         cb["host_cpu"] = host_cpu_model()

@@ -74,9 +74,7 @@ def mfma_scaled_rate(L, stream):
             ghz = (c[:, 0] / (c[:, 1] / 100e6) / 1e9).mean().item()
             per = 32 if mf == 16 else 16                          # instructions per iteration
             flop = grid * waves * iters * per * (2 * 16 * 16 * 128 if mf == 16 else 2 * 32 * 32 * 64)
-            cyc = c[:, 0].mean().item() / (iters * per) * 4 / waves   # SIMD cycles per instruction (2 waves/SIMD)
-            print("  %dx%d %s: %.0f TFLOP/s, shader clock %.2f GHz, %.1f cycles per instruction per SIMD" % (
-                mf, mf, name, flop / ms / 1e9, ghz, cyc))
+            print("  %dx%d %s: %.0f TFLOP/s, shader clock %.2f GHz" % (mf, mf, name, flop / ms / 1e9, ghz))
 
 
 def lds_fill(L, stream):

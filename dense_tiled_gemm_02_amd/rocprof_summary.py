@@ -3,10 +3,12 @@
     python -m dense_tiled_gemm_02_amd.rocprof_summary DIR [--match SUBSTR]
     python -m dense_tiled_gemm_02_amd.rocprof_summary --traffic FETCH_DIR WRITE_DIR COPY_BYTES OUT.json
     python -m dense_tiled_gemm_02_amd.rocprof_summary --report OUT MATCH "WORKLOAD" "WORK" COPY_BYTES
+    python -m dense_tiled_gemm_02_amd.rocprof_summary --report-mx OUT MATCH "WORKLOAD" "WORK" COPY_BYTES
 
 --report composes the per-kernel summary kept under profiles/ from the five
 passes OUT/prof_{trace,fetch,write,mfma,lds} that profile_commands() lists,
-for the kernels whose name contains MATCH.
+for the kernels whose name contains MATCH; --report-mx does the same from the
+OUT/mxprof_* passes of bench.py --mx.
 
 DIR holds the CSV files of one or more rocprofv3 runs (kernel_stats,
 kernel_trace, counter_collection).  Prints, per kernel name: dispatch count
@@ -36,14 +38,26 @@ def source_hash():
     return h.hexdigest()
 
 
-def counter_means(d, name):
-    """{kernel name: mean per dispatch of counter `name`} from a --pmc run."""
+def counter_dispatches(d, name):
+    """{kernel name: {dispatch id: counter `name`}} from a --pmc run."""
     per = defaultdict(lambda: defaultdict(float))
     for c in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
         for r in csv.DictReader(open(c)):
             if r["Counter_Name"] == name:
                 per[r["Kernel_Name"]][r.get("Dispatch_Id")] += float(r["Counter_Value"])
-    return {k: sum(v.values()) / len(v) for k, v in per.items()}
+    return per
+
+
+def counter_means(d, name):
+    """{kernel name: mean per dispatch of counter `name`} from a --pmc run."""
+    return {k: sum(v.values()) / len(v) for k, v in counter_dispatches(d, name).items()}
+
+
+def _largest_copy(d, name):
+    """The counter of the largest copy dispatch (the calibration copy; the runs
+    also hold small host-to-device copies of the inputs)."""
+    vals = [x for k, v in counter_dispatches(d, name).items() if "copy" in k.lower() for x in v.values()]
+    return max(vals) if vals else None
 
 
 def traffic(fetch_dir, write_dir, copy_bytes):
@@ -52,12 +66,12 @@ def traffic(fetch_dir, write_dir, copy_bytes):
     writes exactly copy_bytes."""
     fetch = counter_means(fetch_dir, "FETCH_SIZE")
     write = counter_means(write_dir, "WRITE_SIZE")
-    copy_f = [v for k, v in fetch.items() if "copy" in k.lower()]
-    copy_w = [v for k, v in write.items() if "copy" in k.lower()]
+    copy_f = _largest_copy(fetch_dir, "FETCH_SIZE")
+    copy_w = _largest_copy(write_dir, "WRITE_SIZE")
     if not copy_f or not copy_w:
         raise SystemExit("no copy kernel in the counter runs")
-    ff = copy_bytes / (copy_f[0] * 1024.0)
-    fw = copy_bytes / (copy_w[0] * 1024.0)
+    ff = copy_bytes / (copy_f * 1024.0)
+    fw = copy_bytes / (copy_w * 1024.0)
     out = {"source_sha256": source_hash(), "copy_bytes": copy_bytes,
            "fetch_scale": ff, "write_scale": fw, "kernels": {}}
     for k in fetch:
@@ -108,6 +122,7 @@ def summarise(d, match=None):
 
 
 BENCH = "python3 bench.py --steps 100 --warmup 10 --no-cpu --copy-mb 512"
+BENCH_MX = "python3 bench.py --mx --rounds 3 --copy-mb 512"
 PASSES = [("trace", "--kernel-trace --stats", "gemm"),
           ("fetch", "--kernel-trace --pmc FETCH_SIZE", "p"),
           ("write", "--kernel-trace --pmc WRITE_SIZE", "p"),
@@ -117,18 +132,22 @@ TITLES = {"trace": "kernel trace (rocprofv3 --kernel-trace --stats)", "fetch": "
           "write": "WRITE_SIZE pass", "mfma": "MFMA / clock pass", "lds": "LDS pass"}
 
 
-def profile_commands(out="OUT"):
+def profile_commands(out="OUT", bench=BENCH, prefix="prof_"):
     """The rocprofv3 runs behind a committed profile summary (one counter set per run)."""
-    return ["rocprofv3 %s -f csv -d %s/prof_%s -o %s -- %s" % (flags, out, name, o, BENCH)
+    return ["rocprofv3 %s -f csv -d %s/%s%s -o %s -- %s" % (flags, out, prefix, name, o, bench)
             for name, flags, o in PASSES]
 
 
-def report(out, match, workload, work, copy_bytes):
-    """Text summary of one kernel over the five passes under `out`."""
+def report(out, match, workload, work, copy_bytes, mx=False):
+    """Text summary of one kernel over the five passes under `out` (the
+    prof_* passes of the default benchmark, or the mxprof_* passes of
+    bench.py --mx with mx=True)."""
+    prefix = "mxprof_" if mx else "prof_"
+    bench = BENCH_MX if mx else BENCH
     lines = []
     names = set()
     for name, _, _ in PASSES:
-        for t in glob.glob(os.path.join(out, "prof_" + name, "**", "*kernel_trace.csv"), recursive=True):
+        for t in glob.glob(os.path.join(out, prefix + name, "**", "*kernel_trace.csv"), recursive=True):
             for r in csv.DictReader(open(t)):
                 if match in r["Kernel_Name"]:
                     names.add(r["Kernel_Name"])
@@ -139,18 +158,23 @@ def report(out, match, workload, work, copy_bytes):
     lines.append("Algorithmic work per launch: " + work)
     lines.append("")
     lines.append("Commands (run from the repository root on one MI355X, after")
-    lines.append('"python -m dense_tiled_gemm_02_amd.build"; bench.py runs the bf16 4096^3 and the')
-    lines.append("skinny bf16 16x8192x8192 workloads back to back and ends with one 512 MiB device")
+    if mx:
+        lines.append('"python -m dense_tiled_gemm_02_amd.build"; bench.py --mx runs the three block-scaled')
+        lines.append("workloads (FP4 16x8192x8192, FP4 4096^3, E4M3 4096^3) and ends with one 512 MiB device")
+    else:
+        lines.append('"python -m dense_tiled_gemm_02_amd.build"; bench.py runs the bf16 4096^3 and the')
+        lines.append("skinny bf16 16x8192x8192 workloads back to back and ends with one 512 MiB device")
     lines.append("copy used to calibrate the memory counters):")
-    for c in profile_commands():
+    for c in profile_commands(bench=bench, prefix=prefix):
         lines.append("  " + c)
-    lines.append("  python3 -m dense_tiled_gemm_02_amd.rocprof_summary --traffic OUT/prof_fetch OUT/prof_write "
-                 "%d profiles/traffic.json" % copy_bytes)
-    lines.append('  python3 -m dense_tiled_gemm_02_amd.rocprof_summary --report OUT "%s" ...   (this file)' % match)
+    lines.append("  python3 -m dense_tiled_gemm_02_amd.rocprof_summary --traffic OUT/%sfetch OUT/%swrite "
+                 "%d profiles/%s" % (prefix, prefix, copy_bytes, "traffic_mx.json" if mx else "traffic.json"))
+    lines.append('  python3 -m dense_tiled_gemm_02_amd.rocprof_summary --report%s OUT "%s" ...   (this file)' % (
+        "-mx" if mx else "", match))
     for name, _, _ in PASSES:
         lines.append("")
         lines.append("--- %s ---" % TITLES[name])
-        body = summarise(os.path.join(out, "prof_" + name), match)
+        body = summarise(os.path.join(out, prefix + name), match)
         under = False
         for l in body.splitlines():
             if l.startswith("    "):
@@ -161,7 +185,7 @@ def report(out, match, workload, work, copy_bytes):
                 if under:
                     lines.append(l.strip())
         if name == "write":
-            t = traffic(os.path.join(out, "prof_fetch"), os.path.join(out, "prof_write"), copy_bytes)
+            t = traffic(os.path.join(out, prefix + "fetch"), os.path.join(out, prefix + "write"), copy_bytes)
             for k, v in t["kernels"].items():
                 if match in k:
                     lines.append("Calibration: the %d MiB copy kernel sets FETCH_SIZE x %.4f and WRITE_SIZE x %.4f,"
@@ -183,8 +207,8 @@ if __name__ == "__main__":
         print("scales: fetch %.4f  write %.4f  (copy of %d bytes)" % (t["fetch_scale"], t["write_scale"],
                                                                      t["copy_bytes"]))
         sys.exit(0)
-    if args and args[0] == "--report":
-        sys.stdout.write(report(args[1], args[2], args[3], args[4], int(args[5])))
+    if args and args[0] in ("--report", "--report-mx"):
+        sys.stdout.write(report(args[1], args[2], args[3], args[4], int(args[5]), mx=args[0] == "--report-mx"))
         sys.exit(0)
     m = None
     if "--match" in args:
