@@ -298,17 +298,17 @@ gemm_status plan_impl(const gemm_problem* prob, const gemm_device_info* dev, con
     const dtg::KernelEntry* e = nullptr;
     if (vec) e = find_entry(want, prob->dtype, 1, *dev, prob);
     if (!e && vec && !tuned && (!force || force->kernel == 0) && want.kernel == dtg::KF_DMA) {
-        // no direct-to-LDS variant fits (offset range): same tile, register-staged kernel
-        gemm_config w2 = want;
-        w2.kernel = dtg::KF_TILE;
+        // no direct-to-LDS variant fits (offset range, row strides): the
+        // register-staged kernel with the same tile, any wave grid and depth
+        gemm_config w2 = cfg_of(dtg::KF_TILE, want.bm, want.bn, 0, 0, want.mfma, 0, 0);
         e = find_entry(w2, prob->dtype, 1, *dev, prob);
     }
     const dtg::KernelEntry* fb =
         find_entry(cfg_of(dtg::KF_TILE, 0, 0, 0, 0, 16, 0, 0), prob->dtype, 0, *dev, prob);
     const bool unforced = !force || (!force->kernel && !force->bm && !force->bn && !force->bk && !force->mfma &&
                                      !force->waves_m && !force->waves_n && !force->stages && !force->splitk);
-    if (!e && vec && unforced && !tuned && layout_of(prob) != 0) {
-        // no vector variant for this layout and tile: the element-wise path
+    if (!e && vec && unforced && !tuned) {
+        // no vector variant for this layout, tile or stride: the element-wise path
         e = fb;
     }
     if (!e) {

@@ -29,10 +29,11 @@ CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
 
 
 def source_hash():
-    """sha256 over the kernel sources; measured counters are valid only for it."""
+    """sha256 over the device-code sources (kernels and the headers they
+    include; not the host-side planner); measured counters are valid only for it."""
     h = hashlib.sha256()
     for f in sorted(glob.glob(os.path.join(CSRC, "*"))):
-        if f.endswith((".hip", ".h", ".cpp")):
+        if f.endswith((".hip", ".h")):
             h.update(os.path.basename(f).encode())
             h.update(open(f, "rb").read())
     return h.hexdigest()

@@ -368,3 +368,20 @@ def test_mx_run_rejects_bad_pointers_without_launching():
     assert e.value.status == g.GEMM_ERR_WORKSPACE              # not 256-byte aligned
     # an empty output launches nothing and succeeds without any pointer
     mx.gemm_mx_run(mx_plan(0, 128, 128), None, None, None, None, None, None)
+
+
+def test_rows_of_k_with_short_row_stride_leave_the_direct_kernel():
+    """The direct-to-LDS kernel zeroes the rows past K of a row-major B (or a
+    K x M A) through the descriptor range, which needs the row stride to be at
+    least N (M); overlapping rows go to the register-staged kernel."""
+    ok = plan(512, 512, 512)
+    assert ok.config.kernel == 3
+    pr = g.problem(512, 512, 512, g.GEMM_BF16, ldb=256)     # B rows overlap (ldb < N)
+    p = g.gemm_plan_create_for(pr, fake_gfx950())
+    assert p.config.kernel == 1
+    pr = g.problem(512, 512, 512, g.GEMM_BF16, ta=True, lda=256)   # A stored K x M, lda < M
+    p = g.gemm_plan_create_for(pr, fake_gfx950())
+    assert p.config.kernel == 1
+    # a k-contiguous operand may overlap its rows: the K tail is masked per lane
+    pr = g.problem(512, 512, 512, g.GEMM_BF16, lda=256)     # A row-major, lda < K
+    assert g.gemm_plan_create_for(pr, fake_gfx950()).config.kernel == 3

@@ -477,3 +477,26 @@ def test_general_strides_take_the_element_path():
         D = g.matmul(dA, dB, C.cuda())
         torch.cuda.synchronize()
         check(A, B, C, D.cpu(), dt, label="general strides %s" % dt)
+
+
+def test_overlapping_rows_of_k():
+    """Operands whose rows of k overlap in memory (row-major B with row stride
+    below N, A stored K x M with row stride below M): not the direct-to-LDS
+    kernel, whose K tail relies on the descriptor range; the result is the
+    product of the overlapping views, inside the bound.  A k-contiguous A with
+    overlapping rows stays on the direct kernel (per-lane K-tail masks)."""
+    M = N = K = 264
+    for dt in ("bf16", "f16"):
+        A, B, C = _inputs(M, N, K, dt, True, seed=91)
+        bufB = gemm_inputs.draw(((K - 1) * 128 + N,), 93, dt).cuda()
+        dB = torch.as_strided(bufB, (K, N), (128, 1))          # row k starts 128 elements after row k-1
+        bufA = gemm_inputs.draw(((K - 1) * 136 + M,), 95, dt).cuda()
+        dA_t = torch.as_strided(bufA, (M, K), (1, 136))         # A stored K x M, lda = 136 < M
+        bufA2 = gemm_inputs.draw(((M - 1) * 200 + K,), 97, dt).cuda()
+        dA_r = torch.as_strided(bufA2, (M, K), (200, 1))        # row-major A, lda = 200 < K
+        for dA, dBx, want_dma in ((A.cuda(), dB, False), (dA_t, B.cuda(), False), (dA_r, B.cuda(), True)):
+            pl = g.plan_for(dA, dBx, C.cuda(), None)
+            assert ("gemm_dma_kernel" in pl.describe()) == want_dma, pl.describe()
+            D = g.matmul(dA, dBx, C.cuda())
+            torch.cuda.synchronize()
+            check(dA.cpu(), dBx.cpu(), C, D.cpu(), dt, label="overlapping rows %s %s" % (dt, pl.describe()[:40]))
