@@ -78,6 +78,8 @@ def parse():
                     help="time the decode regime: M in {1,2,4,8,16,32}, N = K in {4096, 8192}, bf16")
     ap.add_argument("--mx", action="store_true",
                     help="block-scaled (MX) workloads: FP8 / FP4 elements with E8M0 scales per 32 k")
+    ap.add_argument("--mx-sweep", action="store_true",
+                    help="block-scaled tile / slice variants of the decode and square workloads, interleaved")
     ap.add_argument("--rounds", type=int, default=30)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-skinny", action="store_true")
@@ -445,6 +447,62 @@ def mx(args):
         copy_calibration(args.copy_mb)
 
 
+def mx_sweep(args):
+    """The block-scaled workloads in their planned configuration beside other
+    tiles / K-slice counts, interleaved in seeded-random order (median and
+    spread over the rounds)."""
+    import torch
+    import gemm_inputs
+    import dense_tiled_gemm_02_amd.mx as mxb
+    cases = {
+        "mx_e2m1_16x8192x8192": [dict()] + [dict(bm=32, bn=64, splitk=k) for k in (1, 3, 4, 8)],
+        "mx_e4m3_4096": [dict()] + [dict(bm=bm, bn=bn) for (bm, bn) in ((256, 128), (128, 256), (128, 128))],
+        "mx_e2m1_4096": [dict()] + [dict(bm=bm, bn=bn) for (bm, bn) in ((256, 128), (128, 256), (128, 128))],
+    }
+    for name, variants in cases.items():
+        w = gemm_inputs.MX_WORKLOADS[name]
+        A, SA, B, SB, _ = gemm_inputs.make_mx(w)
+        copies = max(4, -(-300 * (1 << 20) // B.nbytes)) if w.M <= 32 else 1
+        dA, dSA = torch.from_numpy(A).cuda(), torch.from_numpy(SA).cuda()
+        Bs = [torch.from_numpy(B).cuda()] + [torch.from_numpy(gemm_inputs.draw_mx(w.N, w.K, w.fmt_b, 5000 + r)[0]).cuda()
+                                             for r in range(1, copies)]
+        dSB = torch.from_numpy(SB).cuda()
+        D = torch.empty((w.M, w.N), dtype=torch.bfloat16, device="cuda")
+        stream = torch.cuda.current_stream().cuda_stream
+        run = mxb.mxlib().gemm_mx_run
+        ls = []
+        for v in variants:
+            p = mxb.mx_problem(w.M, w.N, w.K, w.fmt_a, w.fmt_b, mxb.GEMM_MX_OUT_BF16, lda=A.shape[1], ldb=B.shape[1],
+                               ldsa=SA.shape[1], ldsb=SB.shape[1])
+            pl = mxb.gemm_mx_plan_create(p, torch.cuda.current_device(), v or None)
+            ws, wsb = mxb._workspace(pl, torch.cuda.current_device(), stream)
+            st = {"i": 0}
+
+            def launch(c, pl=pl, ws=ws, wsb=wsb, st=st):
+                for _ in range(c):
+                    b = Bs[st["i"] % copies]
+                    assert run(pl.handle, dA.data_ptr(), dSA.data_ptr(), b.data_ptr(), dSB.data_ptr(), None,
+                               D.data_ptr(), ws, wsb, stream) == 0
+                    st["i"] += 1
+            launch(3)
+            ls.append((v, launch, pl))
+        torch.cuda.synchronize()
+        times = {i: [] for i in range(len(ls))}
+        rng = random.Random(99)
+        for _ in range(args.rounds):
+            order = list(range(len(ls)))
+            rng.shuffle(order)
+            for i in order:
+                times[i].extend(batch_times(ls[i][1], 20, 1))
+        for i, (v, _, pl) in enumerate(ls):
+            s = stats(times[i])
+            ms = s["median_ms"]
+            rec = {"workload": name, "variant": v, "plan": pl.describe(), "us": ms * 1e3, "spread": s["spread"],
+                   "tflops": w.flops() / ms / 1e9, "gbs": w.bytes() / ms / 1e6}
+            print(json.dumps(rec), flush=True)
+        del Bs
+
+
 def copy_calibration(mb):
     """One device copy of `mb` MiB, the reference kernel of the memory counters."""
     import torch
@@ -479,6 +537,9 @@ def main():
         return
     if args.mx:
         mx(args)
+        return
+    if args.mx_sweep:
+        mx_sweep(args)
         return
     w = gemm_inputs.WORKLOADS[args.workload]
     case = Case(w, rotate=4 if w.name.startswith("skinny") else 1)

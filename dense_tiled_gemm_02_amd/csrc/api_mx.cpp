@@ -130,10 +130,12 @@ gemm_status plan_impl(const gemm_mx_problem* prob, const gemm_device_info* dev, 
         return static_cast<int32_t>(s > 1 ? s : 1);
     };
     if (prob->M <= 32) {
-        // decode regime: 32-row slabs of 256 columns, K sliced to fill the CUs
+        // decode regime: 32-row slabs of 64 columns, K sliced to fill the CUs
+        // (more slices per tile cost more in the fp32 partial-tile reduction
+        // than they gain in load parallelism)
         want.bm = 32;
-        want.bn = 256;
-        want.splitk = slices(cdiv(prob->N, 256), 2);
+        want.bn = 64;
+        want.splitk = slices(cdiv(prob->N, 64), 2);
     } else {
         static const int ladder[][2] = {{256, 256}, {256, 128}, {128, 256}, {128, 128}};
         bool picked = false;

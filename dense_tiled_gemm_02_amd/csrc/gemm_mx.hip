@@ -125,7 +125,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mx_kernel(MxArgs p) {
     constexpr int NSA = (SIA + NW - 1) / NW, NSB = (SIB + NW - 1) / NW;   // per wave (some may be empty)
     constexpr int NSL = NSA + NSB;
     constexpr int L = IA_W + IB_W + NSL;               // loads per wave per K step
-    static_assert(ST >= 2 && ST <= 4 && (ST - 1) * L < 64, "stages");
+    static_assert(ST >= 2 && ST <= 8 && (ST - 1) * L < 64, "stages");
 
     constexpr int SA_B = BM * ROWB, SB_B = BN * ROWB;  // bytes per stage
     constexpr int SSA_B = SIA * 256, SSB_B = SIB * 256;
@@ -158,25 +158,21 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mx_kernel(MxArgs p) {
     const int kbytes = K / (8 / EB);                   // K is a multiple of the 16-byte chunk
     const int nblocks = (K + 31) / 32;
 
-    // ---- per-lane operand load offsets: load X of an operand fills LDS rows
-    // X*NW*R + wave*R + lane/8 with the lane's 16-byte chunk lane % 8 of the
-    // row; the lane fetches the chunk that the swizzle puts there.  Rows past
-    // the matrix get an offset past any range (fixed for the kernel); the K
-    // tail is a per-lane bit OR'd in at each step.  Masking is arithmetic, so
-    // the loop has no data-dependent branches.
+    // ---- per-lane operand load offsets: load Y of an operand fills LDS rows
+    // Y*NW*R + wave*R + lane/8 with the lane's 16-byte chunk lane % 8 of the
+    // row; the lane fetches the chunk that the swizzle puts there, at byte
+    // offset vo0 + Y * (NW*R rows).  Rows past the matrix need no mask: the
+    // descriptor's range ends K's bytes into the last row, and the next row
+    // starts a row stride (>= K's bytes) after that row.  The K tail is a
+    // per-lane bit OR'd in at each step.  One base offset per operand (not
+    // one per load) keeps the 8-bit 256 x 256 tile clear of register spills,
+    // whose reloads would drain the load ring; masking is arithmetic, so the
+    // loop has no data-dependent branches.
     const int ld_row = wave * R + lane / 8;
     const int ld_chunk = (lane % 8) ^ swz<8>(ld_row);
-    uint32_t a_vo[IA_W], b_vo[IB_W];
-#pragma unroll
-    for (int y = 0; y < IA_W; ++y) {
-        const int row = ld_row + y * NW * R;
-        a_vo[y] = m0 + row < M ? static_cast<uint32_t>(static_cast<int64_t>(row) * p.lda + ld_chunk * 16) : kOOB;
-    }
-#pragma unroll
-    for (int y = 0; y < IB_W; ++y) {
-        const int row = ld_row + y * NW * R;
-        b_vo[y] = n0 + row < N ? static_cast<uint32_t>(static_cast<int64_t>(row) * p.ldb + ld_chunk * 16) : kOOB;
-    }
+    const uint32_t a_vo0 = static_cast<uint32_t>(static_cast<int64_t>(ld_row) * p.lda + ld_chunk * 16);
+    const uint32_t b_vo0 = static_cast<uint32_t>(static_cast<int64_t>(ld_row) * p.ldb + ld_chunk * 16);
+    const uint32_t a_ys = static_cast<uint32_t>(NW * R * p.lda), b_ys = static_cast<uint32_t>(NW * R * p.ldb);
     // scale loads: A's instruction X of a wave is number si = X * NW + wave of
     // the stage (SRPI rows of the scale tile), B's likewise.  A wave whose si is
     // past the tile loads nothing (offset past the range) into a scratch slot;
@@ -241,6 +237,9 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mx_kernel(MxArgs p) {
         d.rsb = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(sb_base + sb), 0, live ? sb_rec - sb : 0u,
                                                   kRsrcWord3);
         d.kmask = kb0 + ld_chunk * 16 < kbytes ? 0u : kOOB;
+        // opaque to the compiler, so it cannot fold the K-tail bit into
+        // per-load offsets hoisted out of the loop (one register per load)
+        tie(d.kmask);
         return d;
     };
     // Load number X of a K step into stage s: A's operand loads, B's, then the scale loads.
@@ -249,7 +248,9 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mx_kernel(MxArgs p) {
         if constexpr (X < IA_W + IB_W) {
             constexpr bool IS_A = X < IA_W;
             constexpr int Y = IS_A ? X : X - IA_W;
-            const uint32_t v = (IS_A ? a_vo[Y] : b_vo[Y]) | d.kmask;
+            // Y * stride < 2^31 (the planner bounds a tile's rows), so OR-ing
+            // the K-tail bit adds it; the sum stays below 2^32
+            const uint32_t v = (IS_A ? a_vo0 : b_vo0) + ((Y * (IS_A ? a_ys : b_ys)) | d.kmask);
             // (a non-const local: clang's host pass drops the kernel when the
             // builtin is handed a member of a const reference)
             __amdgpu_buffer_rsrc_t r = IS_A ? d.ra : d.rb;
@@ -361,30 +362,27 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mx_kernel(MxArgs p) {
     };
     constexpr int NQ = FM * FN;
 
-    // The MFMAs of a sub-step with NOPS memory operations spread between them
-    // (operation o after MFMA o * SP; the last NQ/4 MFMAs carry none).
+    // The MFMAs of a sub-step with NOPS memory operations between them,
+    // ceil(NOPS / NQ) after each MFMA from the first on, so the loads and
+    // reads of the sub-step are all in flight early.
     auto interleave = [&](auto slot_tag, auto ts_tag, auto ks_tag, auto nops_tag, auto&& op) {
         constexpr int NOPS = decltype(nops_tag)::value;
-        constexpr int TAIL = NQ / 4;
-        constexpr int SP = (NOPS == 0) ? 1 : ((NQ - TAIL) / NOPS > 0 ? (NQ - TAIL) / NOPS : 1);
+        constexpr int PER = (NOPS + NQ - 1) / NQ;
         static_for<NQ>([&](auto q_tag) {
             constexpr int Q = decltype(q_tag)::value;
             mfma_op(slot_tag, ts_tag, ks_tag, q_tag);
-            if constexpr (Q % SP == 0 && Q / SP < NOPS) op(std::integral_constant<int, Q / SP>{});
+            static_for<NOPS>([&](auto o_tag) {
+                if constexpr (decltype(o_tag)::value / PER == Q) op(o_tag);
+            });
             __builtin_amdgcn_sched_barrier(0);
         });
-        if constexpr (NOPS > NQ / SP) {
-            static_for<NOPS - NQ / SP>([&](auto o_tag) {
-                op(std::integral_constant<int, NQ / SP + decltype(o_tag)::value>{});
-            });
-        }
     };
 
     // One K step (tile kt) on stage S = U % ST, tile slot U % 2; sub-step ks
     // uses fragment slot (U NKS + ks) % 2.  The last sub-step waits for tile
-    // kt + 1, passes the barrier, and runs its MFMAs with the reads of tile
-    // kt + 1 (its first sub-step's fragments and its scales) and the loads of
-    // tile kt + ST into this stage between them.
+    // kt + 1, passes the barrier, and runs its MFMAs with the loads of tile
+    // kt + ST into this stage and the reads of tile kt + 1 (its first
+    // sub-step's fragments and its scales) between them.
     auto step = [&](auto u_tag, int kt) {
         constexpr int U = decltype(u_tag)::value;
         constexpr int S = U % ST, S1 = (U + 1) % ST;
@@ -404,13 +402,15 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mx_kernel(MxArgs p) {
                 const Desc d = make_desc(kt + ST);
                 wait_vm<(ST - 2) * L>();
                 __builtin_amdgcn_s_barrier();
+                // the loads first: from here to the same point of the next
+                // step (one K step) is the time they have to land
                 interleave(cur, ts, ks_tag, std::integral_constant<int, NRF + NRS + L>{}, [&](auto o_tag) {
                     constexpr int O = decltype(o_tag)::value;
-                    if constexpr (O < NRF + NRS)
-                        read_op(std::integral_constant<int, S1>{}, std::integral_constant<int, 0>{}, nxt,
-                                std::integral_constant<int, TS1>{}, o_tag);
+                    if constexpr (O < L)
+                        load_op(std::integral_constant<int, O>{}, d, S);
                     else
-                        load_op(std::integral_constant<int, O - NRF - NRS>{}, d, S);
+                        read_op(std::integral_constant<int, S1>{}, std::integral_constant<int, 0>{}, nxt,
+                                std::integral_constant<int, TS1>{}, std::integral_constant<int, O - L>{});
                 });
                 wait_frags(nxt);
                 mask_scales(std::integral_constant<int, TS1>{}, kt + 1);
@@ -596,8 +596,9 @@ const MxEntry kMxTable[] = {
     MX_FORMATS(256, 128, 4, 2, 2),
     MX_FORMATS(128, 256, 2, 4, 2),
     MX_FORMATS(128, 128, 2, 2, 3),
-    // decode regime: 32-row slabs, K slices across workgroups
-    MX_FORMATS(32, 256, 1, 4, 2),
+    // decode regime: 32 x 64 slabs of two waves, a 4-deep ring, K slices
+    // across workgroups
+    MX_FORMATS(32, 64, 1, 2, 4),
 };
 
 }  // namespace

@@ -175,7 +175,7 @@ def test_decode_slabs_with_k_slices(fmt, M):
     A, SA, B, SB = _case(M, N, K, fmt, fmt, 40 + M)
     p = mx.mx_problem(M, N, K, fmt, lda=A.shape[1], ldb=B.shape[1], ldsa=SA.shape[1], ldsb=SB.shape[1])
     cfg = mx.gemm_mx_plan_create(p, 0).config
-    assert (cfg.bm, cfg.bn) == (32, 256) and cfg.splitk > 1
+    assert (cfg.bm, cfg.bn) == (32, 64) and cfg.splitk > 1
     print("mx decode", fmt, M, cfg.splitk, flush=True)
     D = _run(A, SA, B, SB, K, fmt, fmt)
     ref, S, S8 = oracle.mx_gemm_f64(A, SA, B, SB, K, fmt, fmt, runs=True)
@@ -192,3 +192,17 @@ def test_forced_k_slices_on_a_square_tile(splits):
     D = _run(A, SA, B, SB, K, "e4m3", "e4m3", config={"bm": 128, "bn": 128, "splitk": splits})
     ref, S, S8 = oracle.mx_gemm_f64(A, SA, B, SB, K, "e4m3", "e4m3", runs=True)
     _check(D, ref, S, S8, "bf16", "split %d" % splits)
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e2m1"])
+@pytest.mark.parametrize("M", [1, 16, 32])
+@pytest.mark.parametrize("splits", [1, 4])
+def test_decode_slab_with_forced_slices(fmt, M, splits):
+    """The decode tile without K slices and with a forced count, ragged N and
+    K ending inside a K step."""
+    N, K = 1000, 3072 + 64
+    A, SA, B, SB = _case(M, N, K, fmt, fmt, 50 + M + splits)
+    print("mx decode forced", fmt, M, splits, flush=True)
+    D = _run(A, SA, B, SB, K, fmt, fmt, config={"bm": 32, "bn": 64, "splitk": splits})
+    ref, S, S8 = oracle.mx_gemm_f64(A, SA, B, SB, K, fmt, fmt, runs=True)
+    _check(D, ref, S, S8, "bf16", "decode %s M=%d splits=%d" % (fmt, M, splits))
