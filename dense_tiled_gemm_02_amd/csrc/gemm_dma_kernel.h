@@ -516,11 +516,64 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(KArgs p) {
         if (tid == 0) __hip_atomic_store(&counters[tile_lin], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     }
 
-    // ---- epilogue: + C in fp32, round, masked store.  Lane l holds, per
-    // block (i, j), row l % MF of the block and G runs of 4 consecutive
-    // columns (16x16x32: columns 4 (l / 16) + 0..3; 32x32x16: run q at
-    // columns 8 q + 4 (l / 32) + 0..3).
+    // ---- epilogue.  Lane l holds, per block (i, j), row l % MF of the block
+    // and G runs of 4 consecutive columns (16x16x32: columns 4 (l / 16) +
+    // 0..3; 32x32x16: run q at columns 8 q + 4 (l / 32) + 0..3).
     constexpr int G = AccT<MF>::regs / 4;
+
+    // Without an addend the tile, rounded, is staged through the (now idle)
+    // LDS and written out as whole 16-byte chunks of rows: a store
+    // instruction then covers two or four complete tile rows instead of 16
+    // rows x 32 bytes, and the output goes out at the rate of a plain fill.
+    // Chunk c of tile row r sits at chunk position c ^ (r mod CPR) of the
+    // row, which spreads a write instruction's rows over the banks.
+    constexpr int CPR = BN / 8;                       // 16-byte chunks per tile row
+    if constexpr (BM * BN <= ST * (SA + SB)) {
+        if (p.has_c == 0) {
+            uint8_t* const stage = reinterpret_cast<uint8_t*>(smem);
+            __syncthreads();   // every wave is past its last operand read
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+#pragma unroll
+                    for (int q = 0; q < G; ++q) {
+                        const int row = wm * TM + i * MF + (lane % MF);
+                        const int col = wn * TN + j * MF + 8 * q + 4 * (lane / MF);
+                        uint2 dv;
+                        dv.x = static_cast<uint32_t>(narrow<BF16>(acc[i][j][4 * q])) |
+                               (static_cast<uint32_t>(narrow<BF16>(acc[i][j][4 * q + 1])) << 16);
+                        dv.y = static_cast<uint32_t>(narrow<BF16>(acc[i][j][4 * q + 2])) |
+                               (static_cast<uint32_t>(narrow<BF16>(acc[i][j][4 * q + 3])) << 16);
+                        const int pos = ((col / 8) ^ (row % CPR)) * 16 + (col % 8) * 2;
+                        *reinterpret_cast<uint2*>(stage + row * (BN * 2) + pos) = dv;
+                    }
+            __syncthreads();
+            constexpr int NT = 64 * NW;
+            static_assert((BM * CPR) % NT == 0, "whole chunk rounds");
+            const bool vec8 = (p.ldd % 8 == 0) && (reinterpret_cast<uintptr_t>(p.D) % 16 == 0);
+#pragma unroll
+            for (int x0 = 0; x0 < BM * CPR; x0 += NT) {
+                const int x = x0 + tid;
+                const int row = x / CPR, cc = x % CPR;
+                const int gr = m0 + row, gc = n0 + cc * 8;
+                if (gr < M && gc < N) {
+                    const uint4 v = *reinterpret_cast<const uint4*>(stage + row * (BN * 2) + (cc ^ (row % CPR)) * 16);
+                    uint16_t* d = p.D + static_cast<int64_t>(gr) * p.ldd + gc;
+                    if (vec8 && gc + 8 <= N) {
+                        *reinterpret_cast<uint4*>(d) = v;
+                    } else {
+                        const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+                        for (int e = 0; e < 8 && gc + e < N; ++e)
+                            d[e] = static_cast<uint16_t>(u[e / 2] >> (16 * (e % 2)));
+                    }
+                }
+            }
+            return;
+        }
+    }
+
+    // With an addend: + C in fp32, round once, masked store from registers.
     const bool has_c = p.has_c != 0;
     const bool dvec = (p.ldd % 4 == 0) && (reinterpret_cast<uintptr_t>(p.D) % 8 == 0);
     const bool cvec = !has_c || ((p.ldc % 4 == 0) && (reinterpret_cast<uintptr_t>(p.C) % 8 == 0));

@@ -20,11 +20,12 @@
 //    next 16, a 4-bit operand k = 32 g .. 32 g + 31 in its 16 bytes; the scale
 //    of row r and of the instruction's 32-k block b is taken from byte
 //    `opsel` of lane r + 32 b's scale register.  The kernel feeds the
-//    instruction of k sub-step ks the K step's blocks ks and NKS + ks (8-bit;
-//    block h of the instruction is block h * NKS + ks of the K step) or
-//    g * NKS + ks (4-bit), so lane g's scales for the NKS sub-steps are NKS
-//    consecutive bytes of its row: one 2- or 4-byte LDS read per fragment per
-//    K step, sub-step ks selecting byte ks;
+//    instruction of k step m (of NKI per K step) the K step's blocks m and
+//    NKI + m (8-bit; block h of the instruction is block h * NKI + m of the K
+//    step) or g * NKI + m (4-bit), so lane g's scales for the NKI
+//    instructions are NKI consecutive bytes of its row: one 2- or 4-byte LDS
+//    read per fragment per K step, instruction m selecting byte m.  A
+//    sub-step covers 128 k: one instruction per block (8-bit) or two (4-bit);
 //  * scales of blocks past ceil(K / 32) (the end of the last K step) are
 //    replaced by 1.0 in registers: their elements are zero (masked loads) and
 //    whatever bytes sit there must not inject a NaN.
@@ -64,8 +65,8 @@ __device__ __forceinline__ i32x8 operand(const u32x4 (&h)[2]) {
     return __builtin_shufflevector(__builtin_bit_cast(i32x4, h[0]), __builtin_bit_cast(i32x4, h[1]), 0, 1, 2, 3,
                                    4, 5, 6, 7);
 }
-__device__ __forceinline__ i32x8 operand(const u32x4 (&h)[1]) {
-    const i32x4 v = __builtin_bit_cast(i32x4, h[0]);
+__device__ __forceinline__ i32x8 operand(const u32x4& h) {
+    const i32x4 v = __builtin_bit_cast(i32x4, h);
     return __builtin_shufflevector(v, v, 0, 1, 2, 3, -1, -1, -1, -1);
 }
 
@@ -90,6 +91,15 @@ __device__ __forceinline__ void store4_16(uint16_t* d, const uint16_t* c, bool v
     }
 }
 
+// Four fp32 values rounded to 16 bits, packed little-end first.
+template <bool BF16>
+__device__ __forceinline__ uint2 pack4(const float (&w)[4]) {
+    uint2 dv;
+    dv.x = static_cast<uint32_t>(narrow<BF16>(w[0])) | (static_cast<uint32_t>(narrow<BF16>(w[1])) << 16);
+    dv.y = static_cast<uint32_t>(narrow<BF16>(w[2])) | (static_cast<uint32_t>(narrow<BF16>(w[3])) << 16);
+    return dv;
+}
+
 __device__ __forceinline__ void store4_32(float* d, const float* c, bool vec, int n_ok, const float (&v)[4]) {
     if (vec) {
         f32x4 w = {v[0], v[1], v[2], v[3]};
@@ -110,9 +120,11 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mx_kernel(MxArgs p) {
     static_assert((FA == kMxE2M1) == (FB == kMxE2M1), "A and B elements of one width");
     constexpr int ROWB = 128;                          // bytes of k per row and K step
     constexpr int BKE = ROWB * 8 / EB;                 // k per K step
-    constexpr int NKS = BKE / 64;                      // instructions (k sub-steps) per K step
+    constexpr int NKI = BKE / 64;                      // instruction k steps per K step
+    constexpr int MPS = (EB == 8) ? 1 : 2;             // instruction k steps per sub-step
+    constexpr int NKS = NKI / MPS;                     // sub-steps per K step (2)
     constexpr int NBLK = BKE / 32;                     // scale blocks per K step
-    constexpr int FR = (EB == 8) ? 2 : 1;              // 16-byte LDS reads per fragment per sub-step
+    constexpr int FR = 2;                              // 16-byte LDS reads per fragment per sub-step
     constexpr int R = 8;                               // LDS rows per load instruction (8 chunks each)
     constexpr int IA_W = BM / R / NW, IB_W = BN / R / NW;
     static_assert(BM % (R * NW) == 0 && BN % (R * NW) == 0, "load split");
@@ -280,8 +292,9 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mx_kernel(MxArgs p) {
     // w*T + 32 f .. + 31 (its offset 32 f * 128 bytes goes into the read's
     // offset field, with the stage offset); lane l reads row l % 32 at the
     // chunk of sub-step ks and half h: 8-bit: block h*NKS + ks, bytes
-    // 16 g .. 16 g + 15 of it (chunk 2 (h NKS + ks) + g); 4-bit: block
-    // g NKS + ks (chunk g NKS + ks).
+    // 16 g .. 16 g + 15 of it (chunk 2 (h NKS + ks) + g), the two halves one
+    // instruction's operand; 4-bit: block g NKI + 2 ks + h (chunk likewise),
+    // half h the operand of instruction k step 2 ks + h.
     const int g = lane / 32;
     const int fr = lane % 32;
     uint32_t a_addr[NKS][FR], b_addr[NKS][FR];
@@ -289,13 +302,13 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mx_kernel(MxArgs p) {
     for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
         for (int h = 0; h < FR; ++h) {
-            const int c = (EB == 8) ? 2 * (h * NKS + ks) + g : g * NKS + ks;
+            const int c = (EB == 8) ? 2 * (h * NKS + ks) + g : g * NKI + MPS * ks + h;
             const int pc = (c ^ swz<8>(fr)) * 16;
             a_addr[ks][h] = smem0 + (wm * TM + fr) * ROWB + pc;
             b_addr[ks][h] = smem0 + OFF_B + (wn * TN + fr) * ROWB + pc;
         }
-    const uint32_t sa_addr = smem0 + OFF_S + (wm * TM + fr) * NBLK + g * NKS;
-    const uint32_t sb_addr = smem0 + OFF_SB + (wn * TN + fr) * NBLK + g * NKS;
+    const uint32_t sa_addr = smem0 + OFF_S + (wm * TM + fr) * NBLK + g * NKI;
+    const uint32_t sb_addr = smem0 + OFF_SB + (wn * TN + fr) * NBLK + g * NKI;
     static_assert((ST - 1) * SA_B + (FM - 1) * 32 * ROWB < 65536 && (ST - 1) * SB_B + (FN - 1) * 32 * ROWB < 65536,
                   "stage and fragment offsets fit the read's offset field");
 
@@ -319,11 +332,11 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mx_kernel(MxArgs p) {
             fa[SL][I][H] = lds_read16<S * SA_B + I * 32 * ROWB>(a_addr[KS][H]);
         } else if constexpr (RR - NRF < FN) {
             constexpr int J = RR - NRF;
-            if constexpr (NKS == 2) ssb[TS][J] = lds_read_u16<S * SSB_B + J * 32 * NBLK>(sb_addr);
+            if constexpr (NKI == 2) ssb[TS][J] = lds_read_u16<S * SSB_B + J * 32 * NBLK>(sb_addr);
             else ssb[TS][J] = lds_read_b32<S * SSB_B + J * 32 * NBLK>(sb_addr);
         } else {
             constexpr int I = RR - NRF - FN;
-            if constexpr (NKS == 2) ssa[TS][I] = lds_read_u16<S * SSA_B + I * 32 * NBLK>(sa_addr);
+            if constexpr (NKI == 2) ssa[TS][I] = lds_read_u16<S * SSA_B + I * 32 * NBLK>(sa_addr);
             else ssa[TS][I] = lds_read_b32<S * SSA_B + I * 32 * NBLK>(sa_addr);
         }
     };
@@ -343,8 +356,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mx_kernel(MxArgs p) {
     // at or past ceil(K / 32) become 127 (2^0).
     auto mask_scales = [&](auto ts_tag, int kt) {
         constexpr int TS = decltype(ts_tag)::value;
-        const int v = nblocks - kt * NBLK - g * NKS;    // valid bytes of this lane's NKS
-        const uint32_t keep = v >= NKS ? 0xffffffffu : v <= 0 ? 0u : (1u << (8 * v)) - 1u;
+        const int v = nblocks - kt * NBLK - g * NKI;    // valid bytes of this lane's NKI
+        const uint32_t keep = v >= NKI ? 0xffffffffu : v <= 0 ? 0u : (1u << (8 * v)) - 1u;
         const uint32_t fill = 0x7f7f7f7fu & ~keep;
 #pragma unroll
         for (int j = 0; j < FN; ++j) { tie(ssb[TS][j]); ssb[TS][j] = (ssb[TS][j] & keep) | fill; }
@@ -356,11 +369,20 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mx_kernel(MxArgs p) {
         constexpr int TS = decltype(ts_tag)::value;
         constexpr int KS = decltype(ks_tag)::value;
         constexpr int Q = decltype(q_tag)::value;
-        constexpr int I = Q / FN, J = Q % FN;
-        acc[I][J] = mfma_mx<FB, FA, KS>(operand(fb[SL][J]), operand(fa[SL][I]), static_cast<int>(ssb[TS][J]),
-                                        static_cast<int>(ssa[TS][I]), acc[I][J]);
+        if constexpr (EB == 8) {
+            constexpr int I = Q / FN, J = Q % FN;
+            acc[I][J] = mfma_mx<FB, FA, KS>(operand(fb[SL][J]), operand(fa[SL][I]), static_cast<int>(ssb[TS][J]),
+                                            static_cast<int>(ssa[TS][I]), acc[I][J]);
+        } else {
+            // all blocks of half 0, then of half 1: an accumulator's two
+            // instructions are FM * FN instructions apart
+            constexpr int H = Q / (FM * FN), I = (Q % (FM * FN)) / FN, J = Q % FN;
+            acc[I][J] = mfma_mx<FB, FA, MPS * KS + H>(operand(fb[SL][J][H]), operand(fa[SL][I][H]),
+                                                      static_cast<int>(ssb[TS][J]), static_cast<int>(ssa[TS][I]),
+                                                      acc[I][J]);
+        }
     };
-    constexpr int NQ = FM * FN;
+    constexpr int NQ = FM * FN * MPS;                 // instructions per sub-step
 
     // The MFMAs of a sub-step with NOPS memory operations between them,
     // ceil(NOPS / NQ) after each MFMA from the first on, so the loads and
@@ -518,6 +540,57 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mx_kernel(MxArgs p) {
             }
         }
         if (tid == 0) __hip_atomic_store(&counters[tile_lin], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    }
+
+    // ---- epilogue, 16-bit output without an addend: the tile, rounded, is
+    // staged through the (now idle) LDS and written out as whole 16-byte
+    // chunks of rows, a wave covering two 512-byte rows per store.  The
+    // register layout would write 32 rows x 16 bytes per store instruction;
+    // staged, the 32 MB output of a 4096^3 product goes out ~2x faster.  Rows
+    // are padded by 16 bytes so the 8-byte LDS writes of a wave's 32 rows
+    // spread over the banks.
+    constexpr int OPITCH = BN * 2 + 16;
+    if constexpr (BM * OPITCH <= LDS_BYTES) {
+        if (p.has_c == 0 && p.out != 2) {
+            const bool bf = p.out == 1;
+            __syncthreads();   // every wave is past its last operand read
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const float w[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                                            acc[i][j][4 * q + 3]};
+                        const int row = wm * TM + i * 32 + fr, col = wn * TN + j * 32 + 8 * q + 4 * g;
+                        *reinterpret_cast<uint2*>(smem + row * OPITCH + col * 2) = bf ? pack4<true>(w)
+                                                                                      : pack4<false>(w);
+                    }
+            __syncthreads();
+            constexpr int CPR = BN / 8;                   // 16-byte chunks per tile row
+            constexpr int NT = 64 * NW;
+            static_assert((BM * CPR) % NT == 0, "whole chunk rounds");
+            const bool dvec = (p.ldd % 8 == 0) && (reinterpret_cast<uintptr_t>(p.D) % 16 == 0);
+            uint16_t* const D = static_cast<uint16_t*>(p.D);
+#pragma unroll
+            for (int x0 = 0; x0 < BM * CPR; x0 += NT) {
+                const int x = x0 + tid;
+                const int row = x / CPR, cc = x % CPR;
+                const int gr = m0 + row, gc = n0 + cc * 8;
+                if (gr < M && gc < N) {
+                    const uint4 v = *reinterpret_cast<const uint4*>(smem + row * OPITCH + cc * 16);
+                    uint16_t* d = D + static_cast<int64_t>(gr) * p.ldd + gc;
+                    if (dvec && gc + 8 <= N) {
+                        *reinterpret_cast<uint4*>(d) = v;
+                    } else {
+                        const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+                        for (int e = 0; e < 8 && gc + e < N; ++e)
+                            d[e] = static_cast<uint16_t>(u[e / 2] >> (16 * (e % 2)));
+                    }
+                }
+            }
+            return;
+        }
     }
 
     // ---- epilogue: + C in fp32, round to the output type, masked store.
