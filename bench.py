@@ -43,6 +43,22 @@ TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
 TRAFFIC_MX_JSON = os.path.join(ROOT, "profiles", "traffic_mx.json")
 
 
+def plan_kernel_name(profiled):
+    """A profiler's demangled kernel name in the form plans describe it:
+    'void dtg::(anonymous namespace)::gemm_dma_kernel<256, 256, 64, 2, 4, 16,
+    2, true, false, false>(dtg::KArgs)' -> 'gemm_dma_kernel<256,256,64,2,4,16,
+    2,1,lay0>' (booleans as 0 / 1; the direct-to-LDS kernel's two layout flags
+    as its layout code, bit 0 for A stored K x M, bit 1 for B stored N x K)."""
+    n = profiled.replace(" ", "").split("(dtg::")[0].split("::")[-1]
+    if "<" not in n:
+        return n
+    head, args = n[:-1].split("<", 1)
+    a = ["1" if x == "true" else "0" if x == "false" else x for x in args.split(",")]
+    if head == "gemm_dma_kernel" and len(a) == 10:
+        a = a[:8] + ["lay%d" % (int(a[8]) + 2 * int(a[9]))]
+    return "%s<%s>" % (head, ",".join(a))
+
+
 def measured_traffic(kernel_name, path=TRAFFIC_JSON):
     """HBM bytes per launch of this kernel from the committed counter runs, or
     None if there are none or the kernel sources changed since."""
@@ -53,7 +69,7 @@ def measured_traffic(kernel_name, path=TRAFFIC_JSON):
         if t.get("source_sha256") != rocprof_summary.source_hash():
             return None
         for k, v in t["kernels"].items():
-            if kernel_name in k.replace(" ", ""):
+            if plan_kernel_name(k) == kernel_name:
                 return v["bytes"]
     except (OSError, ValueError, KeyError):
         return None
