@@ -119,6 +119,16 @@ __device__ __forceinline__ u32x4 lds_read16(uint32_t addr) {
 // Transposing 64-bit read (ds_read_b64_tr_b16) at addr + OFF: within each
 // 16-lane group the 16 addressed 8-byte pieces, in lane order, form a 4 x 16
 // matrix of halfwords (lanes 4i..4i+3 give row i); lane t receives column t.
+// The same for any non-negative offset: whole multiples of 64 KiB (past the
+// instruction's 16-bit offset field) are added to the address.
+template <int OFF>
+__device__ __forceinline__ u32x4 lds_read16_any(uint32_t addr) {
+    if constexpr (OFF < 65536)
+        return lds_read16<OFF>(addr);
+    else
+        return lds_read16<OFF % 65536>(addr + static_cast<uint32_t>(OFF / 65536) * 65536u);
+}
+
 template <int OFF>
 __device__ __forceinline__ i16x4 lds_read_tr(uint32_t addr) {
     i16x4 v;

@@ -309,8 +309,6 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mx_kernel(MxArgs p) {
         }
     const uint32_t sa_addr = smem0 + OFF_S + (wm * TM + fr) * NBLK + g * NKI;
     const uint32_t sb_addr = smem0 + OFF_SB + (wn * TN + fr) * NBLK + g * NKI;
-    static_assert((ST - 1) * SA_B + (FM - 1) * 32 * ROWB < 65536 && (ST - 1) * SB_B + (FN - 1) * 32 * ROWB < 65536,
-                  "stage and fragment offsets fit the read's offset field");
 
     u32x4 fa[2][FM][FR], fb[2][FN][FR];
     uint32_t ssa[2][FM], ssb[2][FN];
@@ -326,10 +324,10 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mx_kernel(MxArgs p) {
         constexpr int RR = decltype(r_tag)::value;
         if constexpr (RR < FN * FR) {
             constexpr int J = RR / FR, H = RR % FR;
-            fb[SL][J][H] = lds_read16<S * SB_B + J * 32 * ROWB>(b_addr[KS][H]);
+            fb[SL][J][H] = lds_read16_any<S * SB_B + J * 32 * ROWB>(b_addr[KS][H]);
         } else if constexpr (RR < NRF) {
             constexpr int I = (RR - FN * FR) / FR, H = (RR - FN * FR) % FR;
-            fa[SL][I][H] = lds_read16<S * SA_B + I * 32 * ROWB>(a_addr[KS][H]);
+            fa[SL][I][H] = lds_read16_any<S * SA_B + I * 32 * ROWB>(a_addr[KS][H]);
         } else if constexpr (RR - NRF < FN) {
             constexpr int J = RR - NRF;
             if constexpr (NKI == 2) ssb[TS][J] = lds_read_u16<S * SSB_B + J * 32 * NBLK>(sb_addr);

@@ -206,3 +206,28 @@ def test_decode_slab_with_forced_slices(fmt, M, splits):
     D = _run(A, SA, B, SB, K, fmt, fmt, config={"bm": 32, "bn": 64, "splitk": splits})
     ref, S, S8 = oracle.mx_gemm_f64(A, SA, B, SB, K, fmt, fmt, runs=True)
     _check(D, ref, S, S8, "bf16", "decode %s M=%d splits=%d" % (fmt, M, splits))
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e2m1"])
+@pytest.mark.parametrize("tile", TILES + [(32, 64)])
+def test_staged_epilogue_partial_chunks(fmt, tile):
+    """16-bit output without an addend goes out as 16-byte row chunks: N = 203
+    in a view of row stride 216 ends every row in a partial chunk, the guard
+    band around the view stays untouched (NaN), and a contiguous D of odd row
+    stride takes element-wise stores."""
+    M, N, K = 200 if tile[0] > 32 else 24, 203, 512
+    A, SA, B, SB = _case(M, N, K, fmt, fmt, 90 + tile[1] // 32)
+    ref, S, S8 = oracle.mx_gemm_f64(A, SA, B, SB, K, fmt, fmt, runs=True)
+    cfg = {"bm": tile[0], "bn": tile[1]}
+    print("mx staged", fmt, tile, flush=True)
+    big = torch.full((M + 16, 216 + 8), float("nan"), dtype=torch.bfloat16, device="cuda")
+    view = big[8:8 + M, 8:8 + N]
+    mx.mx_matmul(_dev(A), _dev(SA), _dev(B), _dev(SB), K, fmt, fmt, out=view, config=cfg)
+    torch.cuda.synchronize()
+    host = big.cpu()
+    mask = torch.ones_like(host, dtype=torch.bool)
+    mask[8:8 + M, 8:8 + N] = False
+    assert torch.isnan(host[mask].float()).all()
+    _check(host[8:8 + M, 8:8 + N].contiguous(), ref, S, S8, "bf16", "strided %s %s" % (fmt, tile))
+    D = _run(A, SA, B, SB, K, fmt, fmt, config=cfg)
+    _check(D, ref, S, S8, "bf16", "contiguous %s %s" % (fmt, tile))

@@ -500,3 +500,46 @@ def test_overlapping_rows_of_k():
             D = g.matmul(dA, dBx, C.cuda())
             torch.cuda.synchronize()
             check(dA.cpu(), dBx.cpu(), C, D.cpu(), dt, label="overlapping rows %s %s" % (dt, pl.describe()[:40]))
+
+
+# ---------------------------------------------------------------- epilogue without an addend
+
+DMA_TILES = [v for v in _variants("bf16") if v["kernel"] == 3]
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+def test_staged_epilogue_every_dma_variant(dt):
+    """Without C the direct-to-LDS kernel writes D from a tile staged in LDS:
+    every variant, forced, on ragged M / N / K (N a multiple of 8, as this
+    kernel's B rows require).  D is written contiguous (16-byte stores), into
+    a view of odd row stride 219 (element-wise stores) and into a view of row
+    stride 224 (16-byte stores); the guard bands around the views must stay
+    untouched."""
+    M, N, K = 300, 200, 136
+    A, B, _ = _inputs(M, N, K, dt, False, seed=71)
+    dA, dB = A.cuda(), B.cuda()
+    for cfg in DMA_TILES:
+        D = torch.full((M, N), float("nan"), dtype=A.dtype, device="cuda")
+        g.matmul(dA, dB, None, out=D, config=cfg)
+        torch.cuda.synchronize()
+        check(A, B, None, D.cpu(), dt, label="%s contiguous %s" % (dt, cfg))
+        for pitch in (219, 224):
+            big = torch.full((M + 16, pitch), 7.0, dtype=A.dtype, device="cuda")
+            view = big[8:8 + M, 8:8 + N]
+            g.matmul(dA, dB, None, out=view, config=cfg)
+            torch.cuda.synchronize()
+            host = big.cpu()
+            mask = torch.ones_like(host, dtype=torch.bool)
+            mask[8:8 + M, 8:8 + N] = False
+            assert torch.all(host[mask] == 7.0), (cfg, pitch)
+            check(A, B, None, host[8:8 + M, 8:8 + N].contiguous(), dt, label="%s pitch %d %s" % (dt, pitch, cfg))
+
+
+def test_staged_epilogue_unaligned_output():
+    """D based 2 bytes past a 16-byte boundary: element-wise stores only."""
+    M, N, K = 260, 264, 192
+    A, B, _ = _inputs(M, N, K, "bf16", False, seed=72)
+    flat = torch.full((M * N + 1,), float("nan"), dtype=torch.bfloat16, device="cuda")
+    view = flat[1:].view(M, N)
+    gpu_run(A, B, None, config=dict(kernel=3, bm=256, bn=256), out=view)
+    check(A, B, None, view.cpu(), "bf16", label="unaligned D")
