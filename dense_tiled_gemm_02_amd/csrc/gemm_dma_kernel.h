@@ -573,7 +573,80 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(KArgs p) {
         }
     }
 
-    // With an addend: + C in fp32, round once, masked store from registers.
+    // With an addend the fp32 tile is staged instead, in P passes of BM / P
+    // rows (the waves of WM / P wave rows each), so that C is read and D
+    // written as whole 16-byte row chunks: acc + C in fp32, rounded once, as
+    // in the register path below.  16-byte chunks of 4 floats sit at chunk
+    // position c ^ (r mod 16) of their row, which keeps a 16-lane write
+    // group's 16 rows on distinct banks.
+    constexpr int P = (BM * BN * 4 <= ST * (SA + SB) * 2)       ? 1
+                      : (WM % 2 == 0 && BM * BN * 2 <= ST * (SA + SB) * 2) ? 2
+                      : (WM % 4 == 0 && BM * BN <= ST * (SA + SB) * 2)     ? 4
+                                                                           : 0;
+    if constexpr (P > 0) {
+        if (p.has_c != 0) {
+            constexpr int PR = BM / P;                    // tile rows per pass
+            constexpr int WPP = WM / P;                   // wave rows per pass
+            constexpr int C32 = BN / 4;                   // fp32 chunks per tile row
+            constexpr int NT = 64 * NW;
+            static_assert((PR * (BN / 8)) % NT == 0, "whole rounds of 8-element runs");
+            uint8_t* const stage = reinterpret_cast<uint8_t*>(smem);
+            const bool vec8 = (p.ldd % 8 == 0) && (reinterpret_cast<uintptr_t>(p.D) % 16 == 0) &&
+                              (p.ldc % 8 == 0) && (reinterpret_cast<uintptr_t>(p.C) % 16 == 0);
+#pragma unroll
+            for (int pass = 0; pass < P; ++pass) {
+                __syncthreads();   // operand reads (first pass) or the previous pass's reads are done
+                if (wm / WPP == pass) {
+#pragma unroll
+                    for (int i = 0; i < FM; ++i)
+#pragma unroll
+                        for (int j = 0; j < FN; ++j)
+#pragma unroll
+                            for (int q = 0; q < G; ++q) {
+                                const int row = (wm % WPP) * TM + i * MF + (lane % MF);
+                                const int col = wn * TN + j * MF + 8 * q + 4 * (lane / MF);
+                                const f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                                                 acc[i][j][4 * q + 3]};
+                                *reinterpret_cast<f32x4*>(stage + row * (BN * 4) + ((col / 4) ^ (row % 16)) * 16) = v;
+                            }
+                }
+                __syncthreads();
+#pragma unroll
+                for (int x0 = 0; x0 < PR * (BN / 8); x0 += NT) {
+                    const int x = x0 + tid;
+                    const int row = x / (BN / 8), c8 = x % (BN / 8);
+                    const int gr = m0 + pass * PR + row, gc = n0 + c8 * 8;
+                    if (gr < M && gc < N) {
+                        const f32x4 lo = *reinterpret_cast<const f32x4*>(stage + row * (BN * 4) +
+                                                                         ((2 * c8) ^ (row % 16)) * 16);
+                        const f32x4 hi = *reinterpret_cast<const f32x4*>(stage + row * (BN * 4) +
+                                                                         ((2 * c8 + 1) ^ (row % 16)) * 16);
+                        const float v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                        const uint16_t* c = p.C + static_cast<int64_t>(gr) * p.ldc + gc;
+                        uint16_t* d = p.D + static_cast<int64_t>(gr) * p.ldd + gc;
+                        if (vec8 && gc + 8 <= N) {
+                            const uint4 cv = *reinterpret_cast<const uint4*>(c);
+                            const uint32_t cu[4] = {cv.x, cv.y, cv.z, cv.w};
+                            uint32_t du[4];
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                const float w0 = v[2 * e] + widen<BF16>(static_cast<uint16_t>(cu[e] & 0xffffu));
+                                const float w1 = v[2 * e + 1] + widen<BF16>(static_cast<uint16_t>(cu[e] >> 16));
+                                du[e] = static_cast<uint32_t>(narrow<BF16>(w0)) |
+                                        (static_cast<uint32_t>(narrow<BF16>(w1)) << 16);
+                            }
+                            *reinterpret_cast<uint4*>(d) = uint4{du[0], du[1], du[2], du[3]};
+                        } else {
+                            for (int e = 0; e < 8 && gc + e < N; ++e) d[e] = narrow<BF16>(v[e] + widen<BF16>(c[e]));
+                        }
+                    }
+                }
+            }
+            return;
+        }
+    }
+
+    // Otherwise: + C in fp32, round once, masked store from registers.
     const bool has_c = p.has_c != 0;
     const bool dvec = (p.ldd % 4 == 0) && (reinterpret_cast<uintptr_t>(p.D) % 8 == 0);
     const bool cvec = !has_c || ((p.ldc % 4 == 0) && (reinterpret_cast<uintptr_t>(p.C) % 8 == 0));
