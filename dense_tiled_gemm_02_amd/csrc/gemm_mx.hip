@@ -591,7 +591,107 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mx_kernel(MxArgs p) {
         }
     }
 
-    // ---- epilogue: + C in fp32, round to the output type, masked store.
+    // ---- epilogue with an addend or an fp32 output: the fp32 tile is staged
+    // in P passes of BM / P rows (the waves of WM / P wave rows each); C is
+    // read and D written as runs of 8 elements of a row (16- or 32-byte
+    // accesses), acc + C added in fp32 and rounded once, as in the register
+    // path below.  16-byte chunks of 4 floats sit at chunk position
+    // c ^ (r mod SW) of their row, SW = min(32, chunks per row).
+    constexpr int P32 = (BM * BN * 4 <= LDS_BYTES)                     ? 1
+                        : (WM % 2 == 0 && BM * BN * 2 <= LDS_BYTES) ? 2
+                        : (WM % 4 == 0 && BM * BN <= LDS_BYTES)     ? 4
+                                                                    : 0;
+    if constexpr (P32 > 0) {
+        constexpr int PR = BM / P32, WPP = WM / P32;
+        constexpr int C32 = BN / 4;                       // fp32 chunks per tile row
+        constexpr int SW = C32 < 32 ? C32 : 32;
+        constexpr int NT = 64 * NW;
+        static_assert((PR * (BN / 8)) % NT == 0, "whole rounds of 8-element runs");
+        const bool has_c = p.has_c != 0;
+        const int out = p.out;
+        const int esz = out == 2 ? 4 : 2;
+        const bool vec = (p.ldd % 8 == 0) && (reinterpret_cast<uintptr_t>(p.D) % (8 * esz) == 0) &&
+                         (!has_c || ((p.ldc % 8 == 0) && (reinterpret_cast<uintptr_t>(p.C) % (8 * esz) == 0)));
+#pragma unroll
+        for (int pass = 0; pass < P32; ++pass) {
+            __syncthreads();   // operand reads (first pass) or the previous pass's reads are done
+            if (wm / WPP == pass) {
+#pragma unroll
+                for (int i = 0; i < FM; ++i)
+#pragma unroll
+                    for (int j = 0; j < FN; ++j)
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            const int row = (wm % WPP) * TM + i * 32 + fr;
+                            const int col = wn * TN + j * 32 + 8 * q + 4 * g;
+                            const f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                                             acc[i][j][4 * q + 3]};
+                            *reinterpret_cast<f32x4*>(smem + row * (BN * 4) + ((col / 4) ^ (row % SW)) * 16) = v;
+                        }
+            }
+            __syncthreads();
+#pragma unroll
+            for (int x0 = 0; x0 < PR * (BN / 8); x0 += NT) {
+                const int x = x0 + tid;
+                const int row = x / (BN / 8), c8 = x % (BN / 8);
+                const int gr = m0 + pass * PR + row, gc = n0 + c8 * 8;
+                if (gr < M && gc < N) {
+                    const f32x4 lo = *reinterpret_cast<const f32x4*>(smem + row * (BN * 4) + ((2 * c8) ^ (row % SW)) * 16);
+                    const f32x4 hi =
+                        *reinterpret_cast<const f32x4*>(smem + row * (BN * 4) + ((2 * c8 + 1) ^ (row % SW)) * 16);
+                    float v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                    const int64_t doff = static_cast<int64_t>(gr) * p.ldd + gc;
+                    const int64_t coff = static_cast<int64_t>(gr) * p.ldc + gc;
+                    const int n_ok = N - gc;
+                    if (out == 2) {
+                        float* d = static_cast<float*>(p.D) + doff;
+                        const float* c = has_c ? static_cast<const float*>(p.C) + coff : nullptr;
+                        if (vec && n_ok >= 8) {
+                            f32x4 w0 = lo, w1 = hi;
+                            if (c) {
+                                w0 += *reinterpret_cast<const f32x4*>(c);
+                                w1 += *reinterpret_cast<const f32x4*>(c + 4);
+                            }
+                            *reinterpret_cast<f32x4*>(d) = w0;
+                            *reinterpret_cast<f32x4*>(d + 4) = w1;
+                        } else {
+                            for (int e = 0; e < 8 && e < n_ok; ++e) d[e] = c ? v[e] + c[e] : v[e];
+                        }
+                    } else {
+                        uint16_t* d = static_cast<uint16_t*>(p.D) + doff;
+                        const uint16_t* c = has_c ? static_cast<const uint16_t*>(p.C) + coff : nullptr;
+                        const bool bf = out == 1;
+                        if (vec && n_ok >= 8) {
+                            if (c) {
+                                const uint4 cv = *reinterpret_cast<const uint4*>(c);
+                                const uint32_t cu[4] = {cv.x, cv.y, cv.z, cv.w};
+#pragma unroll
+                                for (int e = 0; e < 4; ++e) {
+                                    const uint16_t c0 = static_cast<uint16_t>(cu[e] & 0xffffu);
+                                    const uint16_t c1 = static_cast<uint16_t>(cu[e] >> 16);
+                                    v[2 * e] += bf ? widen<true>(c0) : widen<false>(c0);
+                                    v[2 * e + 1] += bf ? widen<true>(c1) : widen<false>(c1);
+                                }
+                            }
+                            const float w0[4] = {v[0], v[1], v[2], v[3]}, w1[4] = {v[4], v[5], v[6], v[7]};
+                            const uint2 a = bf ? pack4<true>(w0) : pack4<false>(w0);
+                            const uint2 b = bf ? pack4<true>(w1) : pack4<false>(w1);
+                            *reinterpret_cast<uint4*>(d) = uint4{a.x, a.y, b.x, b.y};
+                        } else {
+                            for (int e = 0; e < 8 && e < n_ok; ++e) {
+                                float w = v[e];
+                                if (c) w += bf ? widen<true>(c[e]) : widen<false>(c[e]);
+                                d[e] = bf ? narrow<true>(w) : narrow<false>(w);
+                            }
+                        }
+                    }
+                }
+            }
+        }
+        return;
+    }
+
+    // ---- otherwise: + C in fp32, round to the output type, masked store.
     // Lane l holds, per block (i, j), row l % 32 and, for q = 0..3, columns
     // 8 q + 4 (l / 32) + 0..3 in registers 4 q .. 4 q + 3.
     const bool has_c = p.has_c != 0;

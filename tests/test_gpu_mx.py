@@ -231,3 +231,38 @@ def test_staged_epilogue_partial_chunks(fmt, tile):
     _check(host[8:8 + M, 8:8 + N].contiguous(), ref, S, S8, "bf16", "strided %s %s" % (fmt, tile))
     D = _run(A, SA, B, SB, K, fmt, fmt, config=cfg)
     _check(D, ref, S, S8, "bf16", "contiguous %s %s" % (fmt, tile))
+
+
+@pytest.mark.parametrize("out,has_c", [("f32", False), ("f32", True), ("bf16", True), ("f16", True)])
+@pytest.mark.parametrize("tile", TILES + [(32, 64)])
+def test_staged_epilogue_fp32_passes(tile, out, has_c):
+    """An addend or an fp32 output stages the fp32 tile in row passes: C and D
+    views of row stride 224 (16- or 32-byte accesses, a partial last run per
+    row at N = 203), guard band untouched; contiguous C / D of odd row stride
+    (element-wise accesses)."""
+    fmt = "e4m3"
+    M, N, K = 200 if tile[0] > 32 else 24, 203, 512
+    A, SA, B, SB = _case(M, N, K, fmt, fmt, 120 + tile[1] // 32 + 7 * has_c)
+    dt = OUT[out]
+    Cf = np.random.default_rng(9).uniform(-4, 4, (M, N)).astype(np.float32)
+    Ct = torch.from_numpy(Cf).to(dt)
+    ref, S, S8 = oracle.mx_gemm_f64(A, SA, B, SB, K, fmt, fmt, Ct.to(torch.float64).numpy() if has_c else None,
+                                    runs=True)
+    cfg = {"bm": tile[0], "bn": tile[1]}
+    print("mx staged fp32", tile, out, has_c, flush=True)
+    Cbig = torch.zeros((M + 16, 224), dtype=dt, device="cuda")
+    Cbig[8:8 + M, 8:8 + N] = Ct.cuda()
+    Cview = Cbig[8:8 + M, 8:8 + N] if has_c else None
+    big = torch.full((M + 16, 224), float("nan"), dtype=dt, device="cuda")
+    view = big[8:8 + M, 8:8 + N]
+    mx.mx_matmul(_dev(A), _dev(SA), _dev(B), _dev(SB), K, fmt, fmt, C=Cview, out=view, config=cfg)
+    torch.cuda.synchronize()
+    host = big.cpu()
+    mask = torch.ones_like(host, dtype=torch.bool)
+    mask[8:8 + M, 8:8 + N] = False
+    assert torch.isnan(host[mask].float()).all()
+    _check(host[8:8 + M, 8:8 + N].contiguous(), ref, S, S8, out, "strided %s %s c=%d" % (tile, out, has_c))
+    D = mx.mx_matmul(_dev(A), _dev(SA), _dev(B), _dev(SB), K, fmt, fmt, C=Ct.cuda() if has_c else None,
+                     out_dtype=dt, config=cfg)
+    torch.cuda.synchronize()
+    _check(D, ref, S, S8, out, "contiguous %s %s c=%d" % (tile, out, has_c))
