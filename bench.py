@@ -393,8 +393,9 @@ def mx(args):
     interleaved rounds, against the dense MFMA peak of the element type (square)
     or HBM (M = 16, B rotated over > 256 MB of copies).  A per-tensor scaled
     fp8 GEMM of torch (torch._scaled_mm, hipBLASLt) on the same bytes is timed
-    beside the fp8 case as a library reference (no block scales).  One JSON
-    line per workload."""
+    beside the fp8 case as a library reference (no block scales), and the same
+    block-scaled product through torch._scaled_mm where the build has it.  One
+    JSON line per workload."""
     import torch
     import gemm_inputs
     import dense_tiled_gemm_02_amd.mx as mxb
@@ -457,6 +458,33 @@ def mx(args):
             except Exception as e:   # not every build has a scaled fp8 GEMM
                 rec["torch_scaled_mm_per_tensor_us"] = None
                 rec["torch_scaled_mm_error"] = str(e)[:200]
+        # the same block-scaled product through torch._scaled_mm (E8M0 scales per
+        # 32 k), where the build has it: time, and the largest difference from
+        # this library's D relative to max |D|
+        nb = w.K // 32
+        if w.M > 32 and w.K % 32 == 0 and SA.shape[1] >= nb:
+            try:
+                el = {"e4m3": torch.float8_e4m3fn, "e5m2": torch.float8_e5m2}.get(w.fmt_a)
+                if w.fmt_a == "e2m1" and w.fmt_b == "e2m1":
+                    el = torch.float4_e2m1fn_x2
+                if el is None or w.fmt_b != w.fmt_a:
+                    raise ValueError("no torch element type for %s x %s" % (w.fmt_a, w.fmt_b))
+                ta, tb = dA.view(el), Bs[0].view(el)
+                tsa = dSA[:, :nb].contiguous().view(torch.float8_e8m0fnu)
+                tsb = SBs[0][:, :nb].contiguous().view(torch.float8_e8m0fnu)
+
+                def launch_block(c):
+                    for _ in range(c):
+                        torch._scaled_mm(ta, tb.t(), scale_a=tsa, scale_b=tsb, out_dtype=torch.bfloat16)
+                Dt = torch._scaled_mm(ta, tb.t(), scale_a=tsa, scale_b=tsb, out_dtype=torch.bfloat16)
+                launch(1)
+                torch.cuda.synchronize()
+                rec["torch_scaled_mm_block_us"] = stats(batch_times(launch_block, 20, args.rounds))["median_ms"] * 1e3
+                ours = D.float()
+                rec["torch_block_max_rel_diff"] = ((Dt.float() - ours).abs().max() / ours.abs().max()).item()
+            except Exception as e:
+                rec["torch_scaled_mm_block_us"] = None
+                rec["torch_scaled_mm_block_error"] = str(e)[:200]
         print(json.dumps(rec), flush=True)
         del Bs, SBs, dA, dSA
     if args.copy_mb:
