@@ -137,21 +137,30 @@ gemm_status plan_impl(const gemm_mx_problem* prob, const gemm_device_info* dev, 
         want.bn = 64;
         want.splitk = slices(cdiv(prob->N, 64), 2);
     } else {
-        static const int ladder[][2] = {{256, 256}, {256, 128}, {128, 256}, {128, 128}};
-        bool picked = false;
-        for (const auto& t : ladder) {
-            if (2 * cdiv(prob->M, t[0]) * cdiv(prob->N, t[1]) >= dev->cu_count) {
-                want.bm = t[0];
-                want.bn = t[1];
-                picked = true;
-                break;
+        // Tile by estimated time: ceil(tiles / CUs) rounds of workgroups times
+        // the tile's cost per round relative to 256 x 256, fitted to forced
+        // runs (E4M3 / E2M1 medians): 4096^3 and 3072^2 x 4096 pick 256 x 256
+        // (69 / 54 us; 256 x 128 90 / 75 us), 4096 x 2048 x 8192 256 x 128 or
+        // 128 x 256 (79 us; 256 x 256 99 us), 2560^2 x 4096 128 x 256 (40 us;
+        // 128 x 128 48 us, 256 x 256 52 us), 2048^2 x 4096 128 x 128 (27 us;
+        // 256 x 128 37 us, 256 x 256 50 us).  When even 128 x 128 tiles leave
+        // more than half of the CUs idle, K slices across workgroups fill them.
+        struct T { int bm, bn; double cost; };
+        static const T ladder[] = {{256, 256, 1.0}, {256, 128, 0.65}, {128, 256, 0.65}, {128, 128, 0.4}};
+        const T* best = nullptr;
+        double best_t = 0.0;
+        for (const T& t : ladder) {
+            const int64_t tiles = cdiv(prob->M, t.bm) * cdiv(prob->N, t.bn);
+            const double est = static_cast<double>(cdiv(tiles, dev->cu_count)) * t.cost;
+            if (!best || est < best_t) {
+                best = &t;
+                best_t = est;
             }
         }
-        if (!picked) {
-            want.bm = 128;
-            want.bn = 128;
-            want.splitk = slices(cdiv(prob->M, 128) * cdiv(prob->N, 128), 8);
-        }
+        want.bm = best->bm;
+        want.bn = best->bn;
+        const int64_t tiles = cdiv(prob->M, want.bm) * cdiv(prob->N, want.bn);
+        if (best == &ladder[3] && 2 * tiles < dev->cu_count) want.splitk = slices(tiles, 8);
     }
     if (force) {
         const gemm_config& f = *force;

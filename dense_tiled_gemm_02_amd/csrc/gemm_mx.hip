@@ -764,8 +764,8 @@ constexpr int64_t mx_lds(int bm, int bn, int st, int fa) {
 
 const MxEntry kMxTable[] = {
     MX_FORMATS(256, 256, 2, 4, 2),
-    MX_FORMATS(256, 128, 4, 2, 2),
-    MX_FORMATS(128, 256, 2, 4, 2),
+    MX_FORMATS(256, 128, 4, 2, 3),
+    MX_FORMATS(128, 256, 2, 4, 3),
     MX_FORMATS(128, 128, 2, 2, 3),
     // decode regime: 32 x 64 slabs of two waves, a 4-deep ring, K slices
     // across workgroups

@@ -385,3 +385,29 @@ def test_rows_of_k_with_short_row_stride_leave_the_direct_kernel():
     # a k-contiguous operand may overlap its rows: the K tail is masked per lane
     pr = g.problem(512, 512, 512, g.GEMM_BF16, lda=256)     # A row-major, lda < K
     assert g.gemm_plan_create_for(pr, fake_gfx950()).config.kernel == 3
+
+
+def test_tile_choice_by_rounds_of_workgroups():
+    """The 8-wave tile is chosen by ceil(tiles / CUs) times the tile's relative
+    cost per round (fitted to forced runs on the device): a 256 x 256 tile that
+    leaves CUs idle loses to smaller tiles that fill them in one round."""
+    def tile(M, N, K):
+        c = plan(M, N, K).config
+        return (c.bm, c.bn)
+    assert tile(4096, 4096, 4096) == (256, 256)        # 256 tiles: one full round
+    assert tile(3072, 3072, 4096) == (256, 256)        # 144 tiles still beat 3 rounds of 128 x 128
+    assert tile(2048, 2048, 4096) == (128, 128)        # 64 tiles of 256 x 256 would idle 3/4 of the CUs
+    assert tile(2560, 2560, 4096) == (128, 128)
+    assert tile(4096, 2048, 8192) != (256, 256)        # 128 tiles of 256 x 256: half the CUs
+    assert tile(4000, 3000, 1000) == (256, 256)        # 192 tiles in one round
+
+
+def test_mx_tile_choice_by_rounds_of_workgroups():
+    def cfg(M, N, K):
+        c = mx_plan(M, N, K).config
+        return (c.bm, c.bn, c.stages)
+    assert cfg(4096, 4096, 4096) == (256, 256, 2)
+    assert cfg(3072, 3072, 4096) == (256, 256, 2)
+    assert cfg(2048, 2048, 4096) == (128, 128, 3)
+    assert cfg(2560, 2560, 4096)[:2] in ((256, 128), (128, 256)) and cfg(2560, 2560, 4096)[2] == 3
+    assert cfg(4096, 2048, 8192)[:2] in ((256, 128), (128, 256))
