@@ -266,3 +266,21 @@ def test_staged_epilogue_fp32_passes(tile, out, has_c):
                      out_dtype=dt, config=cfg)
     torch.cuda.synchronize()
     _check(D, ref, S, S8, out, "contiguous %s %s c=%d" % (tile, out, has_c))
+
+
+@pytest.mark.parametrize("out", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("splits", [2, 5])
+def test_decode_slices_with_addend(out, splits):
+    """K slices across workgroups with an addend and each output type: the last
+    workgroup of a tile sums the fp32 partials in slice order, adds C and
+    rounds once."""
+    M, N, K, fmt = 20, 520, 2560 + 32, "e4m3"
+    A, SA, B, SB = _case(M, N, K, fmt, fmt, 130 + splits)
+    dt = OUT[out]
+    Ct = torch.from_numpy(np.random.default_rng(11).uniform(-4, 4, (M, N)).astype(np.float32)).to(dt)
+    ref, S, S8 = oracle.mx_gemm_f64(A, SA, B, SB, K, fmt, fmt, Ct.to(torch.float64).numpy(), runs=True)
+    print("mx decode addend", out, splits, flush=True)
+    D = mx.mx_matmul(_dev(A), _dev(SA), _dev(B), _dev(SB), K, fmt, fmt, C=Ct.cuda(), out_dtype=dt,
+                     config={"bm": 32, "bn": 64, "splitk": splits})
+    torch.cuda.synchronize()
+    _check(D, ref, S, S8, out, "decode + C %s splits %d" % (out, splits))
