@@ -228,36 +228,41 @@ gemm_config heuristic(const gemm_problem* p, const gemm_device_info& dev, int* g
         c.splitk = 1;
         return c;
     }
-    // 8-wave direct-to-LDS tiles chosen by estimated time: ceil(tiles / CUs)
-    // rounds of workgroups times the tile's cost per round relative to
-    // 256 x 256 (a 1-wave-per-SIMD tile hides far less latency, so the ladder
-    // holds 8-wave tiles only).  The relative costs are fitted to forced runs
-    // of each tile (bf16, medians): 4096^3 picks 256 x 256 (99 us; 128 x 128
-    // 121 us), 3072^2 x 4096 256 x 256 (75 us; 128 x 128 102 us), 2048^2 x
-    // 4096 128 x 128 (47 us; 256 x 128 60 us, 256 x 256 75 us), 2560^2 x 4096
-    // 128 x 128 (54 us; 128 x 256 61 us), 4096 x 2048 x 8192 128 x 256 or
-    // 128 x 128 (119-120 us; 256 x 256 150 us), 4000 x 3000 x 1000 + C
-    // 256 x 256 (41 us; 128 x 128 43 us).  When even 128 x 128 tiles leave
-    // more than half of the CUs idle, K slices across workgroups
-    // (deterministic fused reduce) fill them.
-    struct C { int fam, bm, bn, bk, st, mf, wm, wn; double cost; };
+    // 8-wave direct-to-LDS tiles chosen by estimated time: rounds of
+    // workgroups, ceil(tiles / (CUs x workgroups resident per CU)), times the
+    // tile's cost per round relative to 256 x 256 (a 1-wave-per-SIMD tile
+    // hides far less latency, so the ladder holds 8-wave tiles only).  The
+    // mid tiles run 3-stage rings, 128 x 128 a 4-stage ring (one workgroup per
+    // CU) or a 2-stage one (64 KiB: two per CU).  Relative costs fitted to
+    // forced runs of every candidate at nine shapes (bf16 medians, one box,
+    // interleaved): 4096^3 256 x 256 101 us (256 x 128 117, 128 x 128 125),
+    // 3072^2 x 4096 256 x 256 82 us (99), 3584^2 x 4096 256 x 256 86 us (102),
+    // 2560^2 x 4096 256 x 128 51 us (128 x 128 55, 256 x 256 76), 2048^2 x
+    // 4096 128 x 128 / 4 stages 36 us (256 x 128 47, 256 x 256 75), 1536^2 x
+    // 8192 128 x 128 / 4 stages 60 us (85), 4096 x 2048 x 8192 256 x 128
+    // 111 us (128 x 128 120, 256 x 256 159), 4000 x 3000 x 1000 256 x 256
+    // 31 us (128 x 256 36).  When even 128 x 128 tiles leave more than half of
+    // the CUs idle, K slices across workgroups (deterministic fused reduce)
+    // fill them.
+    struct C { int fam, bm, bn, bk, st, mf, wm, wn, per_cu; double cost; };
     static const C ladder[] = {
-        {dtg::KF_DMA, 256, 256, 64, 2, 16, 2, 4, 1.0}, {dtg::KF_DMA, 256, 128, 64, 2, 16, 4, 2, 0.75},
-        {dtg::KF_DMA, 128, 256, 64, 2, 16, 2, 4, 0.70}, {dtg::KF_DMA, 128, 128, 64, 2, 16, 2, 4, 0.34},
+        {dtg::KF_DMA, 256, 256, 64, 2, 16, 2, 4, 1, 1.0},  {dtg::KF_DMA, 256, 128, 64, 3, 16, 4, 2, 1, 0.64},
+        {dtg::KF_DMA, 128, 256, 64, 3, 16, 2, 4, 1, 0.64}, {dtg::KF_DMA, 128, 128, 64, 4, 16, 2, 4, 1, 0.43},
+        {dtg::KF_DMA, 128, 128, 64, 2, 16, 2, 4, 2, 0.68},
     };
     const C* best = nullptr;
     double best_t = 0.0;
     for (const C& c : ladder) {
         const int64_t tiles = cdiv(M, c.bm) * cdiv(N, c.bn);
-        const double t = static_cast<double>(cdiv(tiles, dev.cu_count)) * c.cost;
+        const double t = static_cast<double>(cdiv(tiles, static_cast<int64_t>(dev.cu_count) * c.per_cu)) * c.cost;
         if (!best || t < best_t) {
             best = &c;
             best_t = t;
         }
     }
-    if (best != &ladder[3] || 2 * cdiv(M, ladder[3].bm) * cdiv(N, ladder[3].bn) >= dev.cu_count)
+    if (2 * cdiv(M, 128) * cdiv(N, 128) >= dev.cu_count)
         return cfg_of(best->fam, best->bm, best->bn, best->bk, best->st, best->mf, best->wm, best->wn);
-    const C& small = ladder[3];
+    const C& small = ladder[4];
     gemm_config c = cfg_of(small.fam, small.bm, small.bn, small.bk, small.st, small.mf, small.wm, small.wn);
     const int64_t tiles = cdiv(M, small.bm) * cdiv(N, small.bn);
     const int64_t nkt = cdiv(K, small.bk);

@@ -9,6 +9,9 @@ const KernelEntry kTable[] = {
     DMA_LAYOUTS(256, 128, 64, 4, 2, 16, 2),
     DMA_LAYOUTS(128, 256, 64, 2, 4, 16, 2),
     DMA_LAYOUTS(128, 128, 64, 2, 4, 16, 2),
+    DMA_LAYOUTS(256, 128, 64, 4, 2, 16, 3),
+    DMA_LAYOUTS(128, 256, 64, 2, 4, 16, 3),
+    DMA_LAYOUTS(128, 128, 64, 2, 4, 16, 4),
 };
 
 }  // namespace

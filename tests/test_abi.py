@@ -388,18 +388,27 @@ def test_rows_of_k_with_short_row_stride_leave_the_direct_kernel():
 
 
 def test_tile_choice_by_rounds_of_workgroups():
-    """The 8-wave tile is chosen by ceil(tiles / CUs) times the tile's relative
-    cost per round (fitted to forced runs on the device): a 256 x 256 tile that
-    leaves CUs idle loses to smaller tiles that fill them in one round."""
+    """The 8-wave tile and its ring depth are chosen by rounds of workgroups
+    (tiles / (CUs x workgroups resident per CU)) times the tile's relative
+    cost per round (fitted to forced runs on the device): a 256 x 256 grid
+    that leaves CUs idle loses to smaller tiles that fill them."""
     def tile(M, N, K):
         c = plan(M, N, K).config
-        return (c.bm, c.bn)
-    assert tile(4096, 4096, 4096) == (256, 256)        # 256 tiles: one full round
-    assert tile(3072, 3072, 4096) == (256, 256)        # 144 tiles still beat 3 rounds of 128 x 128
-    assert tile(2048, 2048, 4096) == (128, 128)        # 64 tiles of 256 x 256 would idle 3/4 of the CUs
-    assert tile(2560, 2560, 4096) == (128, 128)
-    assert tile(4096, 2048, 8192) != (256, 256)        # 128 tiles of 256 x 256: half the CUs
-    assert tile(4000, 3000, 1000) == (256, 256)        # 192 tiles in one round
+        return (c.bm, c.bn, c.stages)
+    assert tile(4096, 4096, 4096) == (256, 256, 2)     # 256 tiles: one full round
+    assert tile(3072, 3072, 4096) == (256, 256, 2)     # 144 tiles beat 2 rounds of smaller tiles
+    assert tile(3584, 3584, 4096) == (256, 256, 2)
+    assert tile(4000, 3000, 1000) == (256, 256, 2)     # 192 tiles in one round
+    assert tile(2560, 2560, 4096) == (256, 128, 3)     # 200 tiles, 3-stage ring
+    assert tile(4096, 2048, 8192) == (256, 128, 3)
+    assert tile(2048, 2048, 4096) == (128, 128, 4)     # 256 tiles, one per CU: 4-stage ring
+    assert tile(1536, 1536, 8192) == (128, 128, 4)
+    c = plan(1024, 1024, 1024).config                  # 64 tiles: the 2-stage tile, K too short to slice
+    assert (c.bm, c.bn, c.stages, c.splitk) == (128, 128, 2, 1)
+    for ta, tb in ((True, False), (False, True), (True, True)):   # every layout has the ladder's variants
+        for shape in ((2560, 2560, 4096), (2048, 2048, 4096)):
+            p = plan(*shape, ta=ta, tb=tb)
+            assert p.config.kernel == 3 and (p.config.bm, p.config.bn, p.config.stages) == tile(*shape)
 
 
 def test_mx_tile_choice_by_rounds_of_workgroups():

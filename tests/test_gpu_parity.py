@@ -543,3 +543,32 @@ def test_staged_epilogue_unaligned_output():
     view = flat[1:].view(M, N)
     gpu_run(A, B, None, config=dict(kernel=3, bm=256, bn=256), out=view)
     check(A, B, None, view.cpu(), "bf16", label="unaligned D")
+
+
+@pytest.mark.parametrize("shape,ring", [((2048, 2048, 192), (128, 128, 4)), ((2560, 2560, 136), (256, 128, 3))])
+def test_planned_ring_depths_every_layout(shape, ring):
+    """Shapes whose planned tile is the 4-stage 128 x 128 or the 3-stage
+    256 x 128 ring, in all four operand layouts: the plan is that tile, every
+    sampled output is inside the bound, and the layouts agree bit for bit."""
+    M, N, K = shape
+    A, B, _ = _inputs(M, N, K, "bf16", False, seed=M + K)
+    Ab, Bb = gemm_inputs.bits(A), gemm_inputs.bits(B)
+    ii, jj = sample_positions(M, N, 4000, 5)
+    ref, S = oracle.gemm_f64_at(Ab, Bb, None, ii, jj, "bf16")
+    outs = {}
+    for ta in (False, True):
+        for tb in (False, True):
+            dA, dB = _placed(A, ta, 8), _placed(B, tb, 16)
+            D = torch.full((M, N), float("nan"), dtype=A.dtype, device="cuda")
+            pl = g.plan_for(dA, dB, None, D)
+            c = pl.config
+            assert (c.kernel, c.bm, c.bn, c.stages) == (3,) + ring, (ta, tb, pl.describe())
+            g.matmul(dA, dB, None, out=D)
+            torch.cuda.synchronize()
+            Dh = D.cpu()
+            n, worst, _ = oracle.tol_check(gemm_inputs.bits(Dh)[ii, jj], ref, S, "bf16")
+            assert n == 0, "%s ta=%d tb=%d: %d outside (worst %.3g)" % (shape, ta, tb, n, worst)
+            assert not torch.isnan(Dh.float()).any()
+            outs[(ta, tb)] = Dh.view(torch.int16)
+    for key, Dh in outs.items():
+        assert torch.equal(outs[(False, False)], Dh), key
