@@ -561,7 +561,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(KArgs p) {
                     const uint4 v = *reinterpret_cast<const uint4*>(stage + row * (BN * 2) + (cc ^ (row % CPR)) * 16);
                     uint16_t* d = p.D + static_cast<int64_t>(gr) * p.ldd + gc;
                     if (vec8 && gc + 8 <= N) {
-                        *reinterpret_cast<uint4*>(d) = v;
+                        store16_nt(d, v.x, v.y, v.z, v.w);
                     } else {
                         const uint32_t u[4] = {v.x, v.y, v.z, v.w};
                         for (int e = 0; e < 8 && gc + e < N; ++e)
@@ -635,7 +635,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(KArgs p) {
                                 du[e] = static_cast<uint32_t>(narrow<BF16>(w0)) |
                                         (static_cast<uint32_t>(narrow<BF16>(w1)) << 16);
                             }
-                            *reinterpret_cast<uint4*>(d) = uint4{du[0], du[1], du[2], du[3]};
+                            store16_nt(d, du[0], du[1], du[2], du[3]);
                         } else {
                             for (int e = 0; e < 8 && gc + e < N; ++e) d[e] = narrow<BF16>(v[e] + widen<BF16>(c[e]));
                         }

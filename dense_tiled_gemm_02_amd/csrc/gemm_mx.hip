@@ -579,7 +579,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mx_kernel(MxArgs p) {
                     const uint4 v = *reinterpret_cast<const uint4*>(smem + row * OPITCH + cc * 16);
                     uint16_t* d = D + static_cast<int64_t>(gr) * p.ldd + gc;
                     if (dvec && gc + 8 <= N) {
-                        *reinterpret_cast<uint4*>(d) = v;
+                        store16_nt(d, v.x, v.y, v.z, v.w);
                     } else {
                         const uint32_t u[4] = {v.x, v.y, v.z, v.w};
                         for (int e = 0; e < 8 && gc + e < N; ++e)
@@ -652,8 +652,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mx_kernel(MxArgs p) {
                                 w0 += *reinterpret_cast<const f32x4*>(c);
                                 w1 += *reinterpret_cast<const f32x4*>(c + 4);
                             }
-                            *reinterpret_cast<f32x4*>(d) = w0;
-                            *reinterpret_cast<f32x4*>(d + 4) = w1;
+                            store16_nt(d, w0);
+                            store16_nt(d + 4, w1);
                         } else {
                             for (int e = 0; e < 8 && e < n_ok; ++e) d[e] = c ? v[e] + c[e] : v[e];
                         }
@@ -676,7 +676,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mx_kernel(MxArgs p) {
                             const float w0[4] = {v[0], v[1], v[2], v[3]}, w1[4] = {v[4], v[5], v[6], v[7]};
                             const uint2 a = bf ? pack4<true>(w0) : pack4<false>(w0);
                             const uint2 b = bf ? pack4<true>(w1) : pack4<false>(w1);
-                            *reinterpret_cast<uint4*>(d) = uint4{a.x, a.y, b.x, b.y};
+                            store16_nt(d, a.x, a.y, b.x, b.y);
                         } else {
                             for (int e = 0; e < 8 && e < n_ok; ++e) {
                                 float w = v[e];
