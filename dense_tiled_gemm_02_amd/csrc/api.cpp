@@ -241,14 +241,17 @@ gemm_config heuristic(const gemm_problem* p, const gemm_device_info& dev, int* g
     // 4096 128 x 128 / 4 stages 36 us (256 x 128 47, 256 x 256 75), 1536^2 x
     // 8192 128 x 128 / 4 stages 60 us (85), 4096 x 2048 x 8192 256 x 128
     // 111 us (128 x 128 120, 256 x 256 159), 4000 x 3000 x 1000 256 x 256
-    // 31 us (128 x 256 36).  When even 128 x 128 tiles leave more than half of
-    // the CUs idle, K slices across workgroups (deterministic fused reduce)
-    // fill them.
+    // 31 us (128 x 256 36); and for small problems the 4-wave 64 x 64 tile
+    // (64 KiB: two per CU) with a 4-stage ring, fp16: 1024^3 8.3 us
+    // (128 x 128 11.2), 512^3 5.5 us (7.3), 768^2 x 2048 11.7 us (23.1),
+    // 1024^2 x 4096 20.3 us (128 x 128 44.4).  When even 128 x 128 tiles
+    // leave more than half of the CUs idle and K is deep enough, K slices
+    // across workgroups (deterministic fused reduce) fill them instead.
     struct C { int fam, bm, bn, bk, st, mf, wm, wn, per_cu; double cost; };
     static const C ladder[] = {
         {dtg::KF_DMA, 256, 256, 64, 2, 16, 2, 4, 1, 1.0},  {dtg::KF_DMA, 256, 128, 64, 3, 16, 4, 2, 1, 0.64},
         {dtg::KF_DMA, 128, 256, 64, 3, 16, 2, 4, 1, 0.64}, {dtg::KF_DMA, 128, 128, 64, 4, 16, 2, 4, 1, 0.43},
-        {dtg::KF_DMA, 128, 128, 64, 2, 16, 2, 4, 2, 0.68},
+        {dtg::KF_DMA, 128, 128, 64, 2, 16, 2, 4, 2, 0.68}, {dtg::KF_DMA, 64, 64, 64, 4, 16, 2, 2, 2, 0.27},
     };
     const C* best = nullptr;
     double best_t = 0.0;
@@ -260,13 +263,10 @@ gemm_config heuristic(const gemm_problem* p, const gemm_device_info& dev, int* g
             best_t = t;
         }
     }
-    if (2 * cdiv(M, 128) * cdiv(N, 128) >= dev.cu_count)
-        return cfg_of(best->fam, best->bm, best->bn, best->bk, best->st, best->mf, best->wm, best->wn);
     const C& small = ladder[4];
-    gemm_config c = cfg_of(small.fam, small.bm, small.bn, small.bk, small.st, small.mf, small.wm, small.wn);
     const int64_t tiles = cdiv(M, small.bm) * cdiv(N, small.bn);
     const int64_t nkt = cdiv(K, small.bk);
-    if (allow_ws && tiles <= dtg::kMaxCounters) {
+    if (allow_ws && 2 * tiles < dev.cu_count && tiles <= dtg::kMaxCounters) {
         // Slices of at least 16 K steps (the fused reduce costs a few memory
         // round trips, ~4 us: at 1024^3, 16 steps per tile, no split is faster),
         // at most 16 (the last arriver reads them all); measured on bf16
@@ -274,9 +274,13 @@ gemm_config heuristic(const gemm_problem* p, const gemm_device_info& dev, int* g
         int64_t s = dev.cu_count / tiles;
         if (s > nkt / 16) s = nkt / 16;
         if (s > 16) s = 16;
-        if (s > 1) c.splitk = static_cast<int32_t>(s);
+        if (s > 1) {
+            gemm_config c = cfg_of(small.fam, small.bm, small.bn, small.bk, small.st, small.mf, small.wm, small.wn);
+            c.splitk = static_cast<int32_t>(s);
+            return c;
+        }
     }
-    return c;
+    return cfg_of(best->fam, best->bm, best->bn, best->bk, best->st, best->mf, best->wm, best->wn);
 }
 
 gemm_status plan_impl(const gemm_problem* prob, const gemm_device_info* dev, const gemm_config* force,

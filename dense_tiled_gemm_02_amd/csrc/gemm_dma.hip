@@ -15,6 +15,7 @@ const KernelEntry kTable[] = {
     DMA_BOTH(128, 128, 64, 2, 4, 16, 2),
     DMA_BOTH(256, 128, 64, 4, 2, 16, 3),
     DMA_BOTH(128, 256, 64, 2, 4, 16, 3),
+    DMA_BOTH(64, 64, 64, 2, 2, 16, 4),
     DMA_BOTH(256, 256, 32, 2, 4, 16, 4),
     DMA_BOTH(256, 256, 64, 2, 4, 32, 2),
     DMA_BOTH(256, 256, 32, 2, 4, 32, 4),

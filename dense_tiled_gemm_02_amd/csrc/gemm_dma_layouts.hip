@@ -12,6 +12,7 @@ const KernelEntry kTable[] = {
     DMA_LAYOUTS(256, 128, 64, 4, 2, 16, 3),
     DMA_LAYOUTS(128, 256, 64, 2, 4, 16, 3),
     DMA_LAYOUTS(128, 128, 64, 2, 4, 16, 4),
+    DMA_LAYOUTS(64, 64, 64, 2, 2, 16, 4),
 };
 
 }  // namespace

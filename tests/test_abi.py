@@ -403,10 +403,13 @@ def test_tile_choice_by_rounds_of_workgroups():
     assert tile(4096, 2048, 8192) == (256, 128, 3)
     assert tile(2048, 2048, 4096) == (128, 128, 4)     # 256 tiles, one per CU: 4-stage ring
     assert tile(1536, 1536, 8192) == (128, 128, 4)
-    c = plan(1024, 1024, 1024).config                  # 64 tiles: the 2-stage tile, K too short to slice
-    assert (c.bm, c.bn, c.stages, c.splitk) == (128, 128, 2, 1)
+    c = plan(1024, 1024, 1024).config                  # small: 256 tiles of the 4-wave 64 x 64, no slices
+    assert (c.bm, c.bn, c.stages, c.splitk, c.waves_m, c.waves_n) == (64, 64, 4, 1, 2, 2)
+    assert tile(512, 512, 512) == (64, 64, 4)
+    c = plan(512, 512, 32768).config                   # few tiles, deep K: K slices of 128 x 128 tiles
+    assert (c.bm, c.bn, c.splitk) == (128, 128, 16)
     for ta, tb in ((True, False), (False, True), (True, True)):   # every layout has the ladder's variants
-        for shape in ((2560, 2560, 4096), (2048, 2048, 4096)):
+        for shape in ((2560, 2560, 4096), (2048, 2048, 4096), (1024, 1024, 1024)):
             p = plan(*shape, ta=ta, tb=tb)
             assert p.config.kernel == 3 and (p.config.bm, p.config.bn, p.config.stages) == tile(*shape)
 

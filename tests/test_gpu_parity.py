@@ -116,7 +116,8 @@ def _variants(dt):
                                        (128, 256, 64, 2, 16, 2, 2), (128, 128, 64, 2, 16, 2, 2),
                                        (128, 128, 64, 4, 16, 2, 2), (128, 128, 64, 2, 32, 2, 2),
                                        (128, 128, 64, 2, 16, 2, 4), (256, 128, 64, 2, 16, 4, 2),
-                                       (128, 256, 64, 2, 16, 2, 4)]:
+                                       (128, 256, 64, 2, 16, 2, 4), (256, 128, 64, 3, 16, 4, 2),
+                                       (128, 256, 64, 3, 16, 2, 4), (64, 64, 64, 4, 16, 2, 2)]:
         seen.append(dict(bm=bm, bn=bn, bk=bk, stages=st, mfma=mf, waves_m=wm, waves_n=wn, kernel=3))
     return seen
 
@@ -545,7 +546,8 @@ def test_staged_epilogue_unaligned_output():
     check(A, B, None, view.cpu(), "bf16", label="unaligned D")
 
 
-@pytest.mark.parametrize("shape,ring", [((2048, 2048, 192), (128, 128, 4)), ((2560, 2560, 136), (256, 128, 3))])
+@pytest.mark.parametrize("shape,ring", [((2048, 2048, 192), (128, 128, 4)), ((2560, 2560, 136), (256, 128, 3)),
+                                        ((1000, 1024, 200), (64, 64, 4))])
 def test_planned_ring_depths_every_layout(shape, ring):
     """Shapes whose planned tile is the 4-stage 128 x 128 or the 3-stage
     256 x 128 ring, in all four operand layouts: the plan is that tile, every
