@@ -244,9 +244,10 @@ gemm_config heuristic(const gemm_problem* p, const gemm_device_info& dev, int* g
     // 31 us (128 x 256 36); and for small problems the 4-wave 64 x 64 tile
     // (64 KiB: two per CU) with a 4-stage ring, fp16: 1024^3 8.3 us
     // (128 x 128 11.2), 512^3 5.5 us (7.3), 768^2 x 2048 11.7 us (23.1),
-    // 1024^2 x 4096 20.3 us (128 x 128 44.4).  When even 128 x 128 tiles
-    // leave more than half of the CUs idle and K is deep enough, K slices
-    // across workgroups (deterministic fused reduce) fill them instead.
+    // 1024^2 x 4096 20.3 us (128 x 128 44.4).  When even 64 x 64 tiles leave
+    // more than half of the CUs idle and K is deep enough, K slices of
+    // 128 x 128 tiles across workgroups (deterministic fused reduce) fill
+    // them instead.
     struct C { int fam, bm, bn, bk, st, mf, wm, wn, per_cu; double cost; };
     static const C ladder[] = {
         {dtg::KF_DMA, 256, 256, 64, 2, 16, 2, 4, 1, 1.0},  {dtg::KF_DMA, 256, 128, 64, 3, 16, 4, 2, 1, 0.64},
@@ -266,7 +267,8 @@ gemm_config heuristic(const gemm_problem* p, const gemm_device_info& dev, int* g
     const C& small = ladder[4];
     const int64_t tiles = cdiv(M, small.bm) * cdiv(N, small.bn);
     const int64_t nkt = cdiv(K, small.bk);
-    if (allow_ws && 2 * tiles < dev.cu_count && tiles <= dtg::kMaxCounters) {
+    const int64_t tiles64 = cdiv(M, ladder[5].bm) * cdiv(N, ladder[5].bn);
+    if (allow_ws && 2 * tiles64 < dev.cu_count && tiles <= dtg::kMaxCounters) {
         // Slices of at least 16 K steps (the fused reduce costs a few memory
         // round trips, ~4 us: at 1024^3, 16 steps per tile, no split is faster),
         // at most 16 (the last arriver reads them all); measured on bf16

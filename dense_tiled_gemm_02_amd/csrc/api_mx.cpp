@@ -143,10 +143,11 @@ gemm_status plan_impl(const gemm_mx_problem* prob, const gemm_device_info* dev, 
         // (69 / 54 us; 256 x 128 90 / 75 us), 4096 x 2048 x 8192 256 x 128 or
         // 128 x 256 (79 us; 256 x 256 99 us), 2560^2 x 4096 128 x 256 (40 us;
         // 128 x 128 48 us, 256 x 256 52 us), 2048^2 x 4096 128 x 128 (27 us;
-        // 256 x 128 37 us, 256 x 256 50 us).  When even 128 x 128 tiles leave
-        // more than half of the CUs idle, K slices across workgroups fill them.
+        // 256 x 128 37 us, 256 x 256 50 us), 1024^2 x 4096 64 x 64 (12.6 us;
+        // 128 x 128 22.8 us), 768^2 x 4096 64 x 64 (12.1 us; 20.3 us).
         struct T { int bm, bn; double cost; };
-        static const T ladder[] = {{256, 256, 1.0}, {256, 128, 0.65}, {128, 256, 0.65}, {128, 128, 0.4}};
+        static const T ladder[] = {{256, 256, 1.0}, {256, 128, 0.65}, {128, 256, 0.65}, {128, 128, 0.4},
+                                   {64, 64, 0.25}};
         const T* best = nullptr;
         double best_t = 0.0;
         for (const T& t : ladder) {
@@ -159,8 +160,20 @@ gemm_status plan_impl(const gemm_mx_problem* prob, const gemm_device_info* dev, 
         }
         want.bm = best->bm;
         want.bn = best->bn;
-        const int64_t tiles = cdiv(prob->M, want.bm) * cdiv(prob->N, want.bn);
-        if (best == &ladder[3] && 2 * tiles < dev->cu_count) want.splitk = slices(tiles, 8);
+        // K slices of 128 x 128 tiles when even 64 x 64 tiles leave more than
+        // half of the CUs idle and K gives at least 4 slices of 8 K steps
+        // (E4M3 512^2 x 16384: 27.5 us with 16 slices, 41.0 us as 64 x 64;
+        // 1024^2 x 4096: 64 x 64 12.6 us, 21.0 us with 4 slices)
+        const int64_t tiles64 = cdiv(prob->M, 64) * cdiv(prob->N, 64);
+        const int64_t tiles128 = cdiv(prob->M, 128) * cdiv(prob->N, 128);
+        if (2 * tiles64 < dev->cu_count) {
+            const int32_t s = slices(tiles128, 8);
+            if (s >= 4) {
+                want.bm = 128;
+                want.bn = 128;
+                want.splitk = s;
+            }
+        }
     }
     if (force) {
         const gemm_config& f = *force;

@@ -295,7 +295,7 @@ def test_mx_plans_fit_the_device_and_pick_by_tile_count():
             assert (mx.gemm_mx_workspace_size(p) > 0) == (c.splitk > 1)
             assert ("fmt=%d/%d" % (mx.FORMATS[fmt], mx.FORMATS[fmt])) in p.describe()
     assert (mx_plan(4096, 4096, 4096).config.bm, mx_plan(4096, 4096, 4096).config.bn) == (256, 256)
-    assert (mx_plan(512, 512, 1024).config.bm, mx_plan(512, 512, 1024).config.bn) == (128, 128)
+    assert (mx_plan(512, 512, 1024).config.bm, mx_plan(512, 512, 1024).config.bn) == (64, 64)
     # decode regime: 32-row slabs with K slices and a workspace
     d = mx_plan(16, 8192, 8192, "e2m1")
     c = d.config
@@ -312,7 +312,7 @@ def test_mx_plans_fit_the_device_and_pick_by_tile_count():
 def test_mx_forced_config_is_honoured_or_rejected():
     p = mx.gemm_mx_plan_create_for(mx.mx_problem(4096, 4096, 4096), fake_gfx950(), {"bm": 128, "bn": 256})
     assert (p.config.bm, p.config.bn) == (128, 256)
-    for bad in ({"bm": 64}, {"bm": 256, "bn": 256, "splitk": 2}, {"mfma": 16}, {"kernel": 3}, {"splitk": 65}):
+    for bad in ({"bm": 96}, {"bm": 256, "bn": 256, "splitk": 2}, {"mfma": 16}, {"kernel": 3}, {"splitk": 65}):
         with pytest.raises(g.GemmError) as e:
             mx.gemm_mx_plan_create_for(mx.mx_problem(4096, 4096, 4096), fake_gfx950(), bad)
         assert e.value.status == g.GEMM_ERR_UNSUPPORTED, bad
@@ -423,3 +423,7 @@ def test_mx_tile_choice_by_rounds_of_workgroups():
     assert cfg(2048, 2048, 4096) == (128, 128, 3)
     assert cfg(2560, 2560, 4096)[:2] in ((256, 128), (128, 256)) and cfg(2560, 2560, 4096)[2] == 3
     assert cfg(4096, 2048, 8192)[:2] in ((256, 128), (128, 256))
+    assert cfg(1024, 1024, 4096) == (64, 64, 3)          # 256 small tiles beat 4 K slices of 128 x 128
+    assert cfg(512, 512, 2048) == (64, 64, 3)            # too shallow for slices
+    c = mx_plan(512, 512, 16384).config                  # few tiles, deep K: K slices
+    assert (c.bm, c.bn, c.splitk) == (128, 128, 16)
