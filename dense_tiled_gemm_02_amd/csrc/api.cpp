@@ -268,15 +268,19 @@ gemm_config heuristic(const gemm_problem* p, const gemm_device_info& dev, int* g
     const int64_t tiles = cdiv(M, small.bm) * cdiv(N, small.bn);
     const int64_t nkt = cdiv(K, small.bk);
     const int64_t tiles64 = cdiv(M, ladder[5].bm) * cdiv(N, ladder[5].bn);
-    if (allow_ws && 2 * tiles64 < dev.cu_count && tiles <= dtg::kMaxCounters) {
+    if (allow_ws && 2 * tiles < dev.cu_count && tiles <= dtg::kMaxCounters) {
         // Slices of at least 16 K steps (the fused reduce costs a few memory
         // round trips, ~4 us: at 1024^3, 16 steps per tile, no split is faster),
         // at most 16 (the last arriver reads them all); measured on bf16
-        // 512 x 512 x 32768: 322 us unsplit, 42 us with 16 slices.
+        // 512 x 512 x 32768: 322 us unsplit, 42 us with 16 slices.  They win
+        // over the ladder when even 64 x 64 tiles leave half of the CUs idle,
+        // or when K is deep (>= 128 steps) and gives at least 4 slices:
+        // 768^2 x 8192 29 us with 4 slices against 34 us as 64 x 64,
+        // 1024^2 x 16384 55 against 65 us; 1024^2 x 4096 24 against 21 us.
         int64_t s = dev.cu_count / tiles;
         if (s > nkt / 16) s = nkt / 16;
         if (s > 16) s = 16;
-        if (s > 1) {
+        if (s > 1 && (2 * tiles64 < dev.cu_count || (nkt >= 128 && s >= 4))) {
             gemm_config c = cfg_of(small.fam, small.bm, small.bn, small.bk, small.st, small.mf, small.wm, small.wn);
             c.splitk = static_cast<int32_t>(s);
             return c;
