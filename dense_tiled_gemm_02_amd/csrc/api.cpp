@@ -244,10 +244,8 @@ gemm_config heuristic(const gemm_problem* p, const gemm_device_info& dev, int* g
     // 31 us (128 x 256 36); and for small problems the 4-wave 64 x 64 tile
     // (64 KiB: two per CU) with a 4-stage ring, fp16: 1024^3 8.3 us
     // (128 x 128 11.2), 512^3 5.5 us (7.3), 768^2 x 2048 11.7 us (23.1),
-    // 1024^2 x 4096 20.3 us (128 x 128 44.4).  When even 64 x 64 tiles leave
-    // more than half of the CUs idle and K is deep enough, K slices of
-    // 128 x 128 tiles across workgroups (deterministic fused reduce) fill
-    // them instead.
+    // 1024^2 x 4096 20.3 us (128 x 128 44.4).  K slices across workgroups
+    // (deterministic fused reduce) replace the ladder where they fit (below).
     struct C { int fam, bm, bn, bk, st, mf, wm, wn, per_cu; double cost; };
     static const C ladder[] = {
         {dtg::KF_DMA, 256, 256, 64, 2, 16, 2, 4, 1, 1.0},  {dtg::KF_DMA, 256, 128, 64, 3, 16, 4, 2, 1, 0.64},
@@ -264,24 +262,27 @@ gemm_config heuristic(const gemm_problem* p, const gemm_device_info& dev, int* g
             best_t = t;
         }
     }
-    const C& small = ladder[4];
-    const int64_t tiles = cdiv(M, small.bm) * cdiv(N, small.bn);
-    const int64_t nkt = cdiv(K, small.bk);
-    const int64_t tiles64 = cdiv(M, ladder[5].bm) * cdiv(N, ladder[5].bn);
-    if (allow_ws && 2 * tiles < dev.cu_count && tiles <= dtg::kMaxCounters) {
-        // Slices of at least 16 K steps (the fused reduce costs a few memory
-        // round trips, ~4 us: at 1024^3, 16 steps per tile, no split is faster),
-        // at most 16 (the last arriver reads them all); measured on bf16
-        // 512 x 512 x 32768: 322 us unsplit, 42 us with 16 slices.  They win
-        // over the ladder when even 64 x 64 tiles leave half of the CUs idle,
-        // or when K is deep (>= 128 steps) and gives at least 4 slices:
-        // 768^2 x 8192 29 us with 4 slices against 34 us as 64 x 64,
-        // 1024^2 x 16384 55 against 65 us; 1024^2 x 4096 24 against 21 us.
+    // K slices of the 4-stage 128 x 128 tile (one workgroup per CU) whenever
+    // at least two slices of >= 16 K steps fit in the CUs: few tiles with a
+    // deep K, and the wide, short problems (M <= 256) the ladder serves
+    // poorly.  Slices of at least 16 K steps (the fused reduce costs a few
+    // memory round trips, ~4 us), at most 16 (the last arriver reads them
+    // all).  Measured (bf16, medians): 512^2 x 32768 36.5 us with 16 slices
+    // (2-stage tile 42.0, unsplit 322), 1024^2 x 16384 42.6 us with 4 (64 x 64
+    // 65.0), 768^2 x 8192 23.9 us with 4 (64 x 64 34.3), 192 x 8192 x 8192
+    // 38.1 us with 2 (64 x 64 46.6), 256 x 8192 x 8192 48.4 us with 2
+    // (64 x 64 80.3), 64 x 8192 x 8192 34.7 us with 4, 128 x 4096 x 4096
+    // 16.8 us with 4 (64 x 64 19.1); 1024^2 x 4096 20.7 us with 4 (64 x 64
+    // 20.0).
+    const C& split = ladder[3];
+    const int64_t tiles = cdiv(M, split.bm) * cdiv(N, split.bn);
+    const int64_t nkt = cdiv(K, split.bk);
+    if (allow_ws && tiles <= dtg::kMaxCounters) {
         int64_t s = dev.cu_count / tiles;
         if (s > nkt / 16) s = nkt / 16;
         if (s > 16) s = 16;
-        if (s > 1 && (2 * tiles64 < dev.cu_count || (nkt >= 128 && s >= 4))) {
-            gemm_config c = cfg_of(small.fam, small.bm, small.bn, small.bk, small.st, small.mf, small.wm, small.wn);
+        if (s > 1) {
+            gemm_config c = cfg_of(split.fam, split.bm, split.bn, split.bk, split.st, split.mf, split.wm, split.wn);
             c.splitk = static_cast<int32_t>(s);
             return c;
         }

@@ -122,7 +122,8 @@ def _variants(dt):
     return seen
 
 
-DMA_SPLIT = [(128, 128, 64, 2, 16, 2, 4), (128, 128, 64, 2, 16, 2, 2), (128, 128, 64, 2, 32, 2, 2),
+DMA_SPLIT = [(128, 128, 64, 2, 16, 2, 4), (128, 128, 64, 4, 16, 2, 4), (128, 128, 64, 2, 16, 2, 2),
+             (128, 128, 64, 2, 32, 2, 2),
              (128, 128, 64, 4, 16, 2, 2), (256, 128, 64, 2, 16, 4, 2), (128, 256, 64, 2, 16, 2, 4)]
 
 
