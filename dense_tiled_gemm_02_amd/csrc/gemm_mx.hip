@@ -137,6 +137,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mx_kernel(MxArgs p) {
     constexpr int NSA = (SIA + NW - 1) / NW, NSB = (SIB + NW - 1) / NW;   // per wave (some may be empty)
     constexpr int NSL = NSA + NSB;
     constexpr int L = IA_W + IB_W + NSL;               // loads per wave per K step
+    constexpr int LA = IA_W + IB_W;                    // operand loads (load numbers 0 .. LA - 1)
     static_assert(ST >= 2 && ST <= 8 && (ST - 1) * L < 64, "stages");
 
     constexpr int SA_B = BM * ROWB, SB_B = BN * ROWB;  // bytes per stage
@@ -400,9 +401,13 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mx_kernel(MxArgs p) {
 
     // One K step (tile kt) on stage S = U % ST, tile slot U % 2; sub-step ks
     // uses fragment slot (U NKS + ks) % 2.  The last sub-step waits for tile
-    // kt + 1, passes the barrier, and runs its MFMAs with the loads of tile
-    // kt + ST into this stage and the reads of tile kt + 1 (its first
-    // sub-step's fragments and its scales) between them.
+    // kt + 1, passes the barrier, and runs its MFMAs with the operand loads of
+    // tile kt + ST into this stage and the reads of tile kt + 1 (its first
+    // sub-step's fragments and its scales) between them.  The scale loads of
+    // a tile follow one sub-step later, in the first sub-step of the next K
+    // step (their stage is free since the same barrier): measured against
+    // issuing all loads together, E4M3 4096^3 65.8 -> 63.6 us, E2M1 41.6 ->
+    // 41.1 us, E2M1 16 x 8192 x 8192 11.07 -> 10.80 us, bitwise-identical.
     auto step = [&](auto u_tag, int kt) {
         constexpr int U = decltype(u_tag)::value;
         constexpr int S = U % ST, S1 = (U + 1) % ST;
@@ -414,8 +419,16 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mx_kernel(MxArgs p) {
             const auto nxt = std::integral_constant<int, NXT>{};
             const auto ts = std::integral_constant<int, TS>{};
             if constexpr (KS + 1 < NKS) {
-                interleave(cur, ts, ks_tag, std::integral_constant<int, NRF>{}, [&](auto o_tag) {
-                    read_op(std::integral_constant<int, S>{}, std::integral_constant<int, KS + 1>{}, nxt, ts, o_tag);
+                // (KS == 0: the scale loads of tile kt + ST - 1, into its stage)
+                constexpr int LS = (KS == 0) ? L - LA : 0;
+                const Desc ds = make_desc(kt + ST - 1);
+                interleave(cur, ts, ks_tag, std::integral_constant<int, LS + NRF>{}, [&](auto o_tag) {
+                    constexpr int O = decltype(o_tag)::value;
+                    if constexpr (O < LS)
+                        load_op(std::integral_constant<int, LA + O>{}, ds, (S + ST - 1) % ST);
+                    else
+                        read_op(std::integral_constant<int, S>{}, std::integral_constant<int, KS + 1>{}, nxt, ts,
+                                std::integral_constant<int, O - LS>{});
                 });
                 wait_frags(nxt);
             } else {
@@ -424,13 +437,13 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mx_kernel(MxArgs p) {
                 __builtin_amdgcn_s_barrier();
                 // the loads first: from here to the same point of the next
                 // step (one K step) is the time they have to land
-                interleave(cur, ts, ks_tag, std::integral_constant<int, NRF + NRS + L>{}, [&](auto o_tag) {
+                interleave(cur, ts, ks_tag, std::integral_constant<int, NRF + NRS + LA>{}, [&](auto o_tag) {
                     constexpr int O = decltype(o_tag)::value;
-                    if constexpr (O < L)
+                    if constexpr (O < LA)
                         load_op(std::integral_constant<int, O>{}, d, S);
                     else
                         read_op(std::integral_constant<int, S1>{}, std::integral_constant<int, 0>{}, nxt,
-                                std::integral_constant<int, TS1>{}, std::integral_constant<int, O - L>{});
+                                std::integral_constant<int, TS1>{}, std::integral_constant<int, O - LA>{});
                 });
                 wait_frags(nxt);
                 mask_scales(std::integral_constant<int, TS1>{}, kt + 1);
@@ -440,8 +453,14 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mx_kernel(MxArgs p) {
 
     constexpr int UNROLL = (ST % 2 == 0) ? ST : 2 * ST;   // stage, fragment and tile slots repeat
     if (nkt > 0) {
-        static_for<ST>([&](auto t_tag) { issue_tile(kt0 + decltype(t_tag)::value, decltype(t_tag)::value); });
-        wait_vm<(ST - 1) * L>();
+        // tiles kt0 .. kt0 + ST - 2 whole, tile kt0 + ST - 1 without its
+        // scales (the first step loads them); then wait for tile kt0
+        static_for<ST - 1>([&](auto t_tag) { issue_tile(kt0 + decltype(t_tag)::value, decltype(t_tag)::value); });
+        {
+            const Desc d = make_desc(kt0 + ST - 1);
+            static_for<LA>([&](auto x_tag) { load_op(x_tag, d, ST - 1); });
+        }
+        wait_vm<(ST - 2) * L + LA>();
         __builtin_amdgcn_s_barrier();
         static_for<NRF + NRS>([&](auto r_tag) {
             read_op(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{},
