@@ -244,17 +244,28 @@ gemm_config heuristic(const gemm_problem* p, const gemm_device_info& dev, int* g
     // 31 us (128 x 256 36); and for small problems the 4-wave 64 x 64 tile
     // (64 KiB: two per CU) with a 4-stage ring, fp16: 1024^3 8.3 us
     // (128 x 128 11.2), 512^3 5.5 us (7.3), 768^2 x 2048 11.7 us (23.1),
-    // 1024^2 x 4096 20.3 us (128 x 128 44.4).  K slices across workgroups
-    // (deterministic fused reduce) replace the ladder where they fit (below).
-    struct C { int fam, bm, bn, bk, st, mf, wm, wn, per_cu; double cost; };
+    // 1024^2 x 4096 20.3 us (128 x 128 44.4).  The 192 x 256 tile (compiled
+    // for row-major A and B only) covers the band where 256 x 256 tiles leave
+    // CUs idle and 256 x 128 tiles need a second round: 3072^2 x 4096 73.3 us
+    // (256 x 256 86.5), 4000 x 3000 x 1000 + C 35.2 us (38.7), bitwise the
+    // same result; 2560^2 x 4096 66.2 us against 49.6 for 256 x 128.  K
+    // slices across workgroups (deterministic fused reduce) replace the
+    // ladder where they fit (below).
+    struct C { int fam, bm, bn, bk, st, mf, wm, wn, per_cu; double cost; bool row_major_only; };
     static const C ladder[] = {
-        {dtg::KF_DMA, 256, 256, 64, 2, 16, 2, 4, 1, 1.0},  {dtg::KF_DMA, 256, 128, 64, 3, 16, 4, 2, 1, 0.64},
-        {dtg::KF_DMA, 128, 256, 64, 3, 16, 2, 4, 1, 0.64}, {dtg::KF_DMA, 128, 128, 64, 4, 16, 2, 4, 1, 0.43},
-        {dtg::KF_DMA, 128, 128, 64, 2, 16, 2, 4, 2, 0.68}, {dtg::KF_DMA, 64, 64, 64, 4, 16, 2, 2, 2, 0.27},
+        {dtg::KF_DMA, 256, 256, 64, 2, 16, 2, 4, 1, 1.0, false},
+        {dtg::KF_DMA, 256, 128, 64, 3, 16, 4, 2, 1, 0.64, false},
+        {dtg::KF_DMA, 128, 256, 64, 3, 16, 2, 4, 1, 0.64, false},
+        {dtg::KF_DMA, 128, 128, 64, 4, 16, 2, 4, 1, 0.43, false},
+        {dtg::KF_DMA, 128, 128, 64, 2, 16, 2, 4, 2, 0.68, false},
+        {dtg::KF_DMA, 64, 64, 64, 4, 16, 2, 2, 2, 0.27, false},
+        {dtg::KF_DMA, 192, 256, 64, 2, 16, 2, 4, 1, 0.85, true},
     };
+    const bool row_major_vec = layout_of(p) == 0 && vec_shape_ok(p);
     const C* best = nullptr;
     double best_t = 0.0;
     for (const C& c : ladder) {
+        if (c.row_major_only && !row_major_vec) continue;
         const int64_t tiles = cdiv(M, c.bm) * cdiv(N, c.bn);
         const double t = static_cast<double>(cdiv(tiles, static_cast<int64_t>(dev.cu_count) * c.per_cu)) * c.cost;
         if (!best || t < best_t) {

@@ -13,6 +13,7 @@ const KernelEntry kTable[] = {
     DMA_BOTH(128, 128, 64, 2, 2, 32, 2),
     DMA_BOTH(128, 128, 64, 2, 4, 16, 4),
     DMA_BOTH(128, 128, 32, 2, 4, 16, 4),
+    DMA_BOTH(192, 256, 64, 2, 4, 16, 2),
 };
 
 }  // namespace

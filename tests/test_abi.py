@@ -396,9 +396,9 @@ def test_tile_choice_by_rounds_of_workgroups():
         c = plan(M, N, K).config
         return (c.bm, c.bn, c.stages)
     assert tile(4096, 4096, 4096) == (256, 256, 2)     # 256 tiles: one full round
-    assert tile(3072, 3072, 4096) == (256, 256, 2)     # 144 tiles beat 2 rounds of smaller tiles
-    assert tile(3584, 3584, 4096) == (256, 256, 2)
-    assert tile(4000, 3000, 1000) == (256, 256, 2)     # 192 tiles in one round
+    assert tile(3072, 3072, 4096) == (192, 256, 2)     # 192 tiles in one round (256 x 256: 144)
+    assert tile(3584, 3584, 4096) == (256, 256, 2)     # 192 x 256 would need a second round
+    assert tile(4000, 3000, 1000) == (192, 256, 2)     # 252 tiles in one round (256 x 256: 192)
     assert tile(2560, 2560, 4096) == (256, 128, 3)     # 200 tiles, 3-stage ring
     assert tile(4096, 2048, 8192) == (256, 128, 3)
     assert tile(2048, 2048, 4096) == (128, 128, 4)     # 256 tiles, one per CU: 4-stage ring
@@ -417,6 +417,12 @@ def test_tile_choice_by_rounds_of_workgroups():
         for shape in ((2560, 2560, 4096), (2048, 2048, 4096), (1024, 1024, 1024)):
             p = plan(*shape, ta=ta, tb=tb)
             assert p.config.kernel == 3 and (p.config.bm, p.config.bn, p.config.stages) == tile(*shape)
+        # the 192 x 256 tile is compiled for row-major operands only: the
+        # other layouts keep 256 x 256 there, on the direct-to-LDS kernel
+        p = plan(3072, 3072, 4096, ta=ta, tb=tb)
+        assert p.config.kernel == 3 and (p.config.bm, p.config.bn, p.config.stages) == (256, 256, 2)
+    c = plan(3072, 3072, 4092).config                  # K not a multiple of 8: no vector path, no 192 x 256
+    assert (c.bm, c.bn) != (192, 256)
 
 
 def test_mx_tile_choice_by_rounds_of_workgroups():

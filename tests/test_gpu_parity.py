@@ -117,7 +117,8 @@ def _variants(dt):
                                        (128, 128, 64, 4, 16, 2, 2), (128, 128, 64, 2, 32, 2, 2),
                                        (128, 128, 64, 2, 16, 2, 4), (256, 128, 64, 2, 16, 4, 2),
                                        (128, 256, 64, 2, 16, 2, 4), (256, 128, 64, 3, 16, 4, 2),
-                                       (128, 256, 64, 3, 16, 2, 4), (64, 64, 64, 4, 16, 2, 2)]:
+                                       (128, 256, 64, 3, 16, 2, 4), (64, 64, 64, 4, 16, 2, 2),
+                                       (192, 256, 64, 2, 16, 2, 4)]:
         seen.append(dict(bm=bm, bn=bn, bk=bk, stages=st, mfma=mf, waves_m=wm, waves_n=wn, kernel=3))
     return seen
 
