@@ -144,10 +144,13 @@ gemm_status plan_impl(const gemm_mx_problem* prob, const gemm_device_info* dev, 
         // 128 x 256 (79 us; 256 x 256 99 us), 2560^2 x 4096 128 x 256 (40 us;
         // 128 x 128 48 us, 256 x 256 52 us), 2048^2 x 4096 128 x 128 (27 us;
         // 256 x 128 37 us, 256 x 256 50 us), 1024^2 x 4096 64 x 64 (12.6 us;
-        // 128 x 128 22.8 us), 768^2 x 4096 64 x 64 (12.1 us; 20.3 us).
+        // 128 x 128 22.8 us), 768^2 x 4096 64 x 64 (12.1 us; 20.3 us); 192 x 256
+        // where 256 x 256 leaves CUs idle and the mid tiles need a second
+        // round: 3072^2 x 4096 49.3 / 31.6 us (256 x 256 54.9 / 34.4),
+        // 4000 x 3000 x 1024 21.5 / 17.6 us (23.6 / 18.8), bitwise the same.
         struct T { int bm, bn; double cost; };
         static const T ladder[] = {{256, 256, 1.0}, {256, 128, 0.65}, {128, 256, 0.65}, {128, 128, 0.4},
-                                   {64, 64, 0.25}};
+                                   {64, 64, 0.25},   {192, 256, 0.9}};
         const T* best = nullptr;
         double best_t = 0.0;
         for (const T& t : ladder) {

@@ -787,6 +787,7 @@ const MxEntry kMxTable[] = {
     MX_FORMATS(128, 256, 2, 4, 3),
     MX_FORMATS(128, 128, 2, 2, 3),
     MX_FORMATS(64, 64, 2, 2, 3),
+    MX_FORMATS(192, 256, 2, 4, 2),
     // decode regime: 32 x 64 slabs of two waves, a 4-deep ring, K slices
     // across workgroups
     MX_FORMATS(32, 64, 1, 2, 4),

@@ -430,7 +430,9 @@ def test_mx_tile_choice_by_rounds_of_workgroups():
         c = mx_plan(M, N, K).config
         return (c.bm, c.bn, c.stages)
     assert cfg(4096, 4096, 4096) == (256, 256, 2)
-    assert cfg(3072, 3072, 4096) == (256, 256, 2)
+    assert cfg(3072, 3072, 4096) == (192, 256, 2)     # 192 tiles in one round (256 x 256: 144)
+    assert cfg(4000, 3000, 1024) == (192, 256, 2)
+    assert cfg(3584, 3584, 4096) == (256, 256, 2)     # 192 x 256 would need a second round
     assert cfg(2048, 2048, 4096) == (128, 128, 3)
     assert cfg(2560, 2560, 4096)[:2] in ((256, 128), (128, 256)) and cfg(2560, 2560, 4096)[2] == 3
     assert cfg(4096, 2048, 8192)[:2] in ((256, 128), (128, 256))

@@ -22,7 +22,7 @@ import oracle
 pytestmark = pytest.mark.gpu
 
 PAIRS = [("e4m3", "e4m3"), ("e5m2", "e5m2"), ("e4m3", "e5m2"), ("e5m2", "e4m3"), ("e2m1", "e2m1")]
-TILES = [(256, 256), (256, 128), (128, 256), (128, 128), (64, 64)]
+TILES = [(256, 256), (256, 128), (128, 256), (128, 128), (64, 64), (192, 256)]
 OUT = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}
 
 
