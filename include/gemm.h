@@ -45,7 +45,10 @@
  * gemm_run enqueues its kernels on the given stream and returns.  Errors in a
  * running kernel surface at the caller's next synchronization; launch
  * errors are returned as GEMM_ERR_HIP.  Plans are immutable after creation,
- * so one plan may be run concurrently on several streams.
+ * so one plan may be run concurrently on several streams.  Because gemm_run
+ * only enqueues kernels (no allocation, memset or synchronization), a call
+ * may be captured in a HIP graph and the graph replayed any number of times;
+ * a K-sliced plan's workspace is prepared once, before the capture.
  *
  * Errors.  Every entry point returns a status and never aborts.  The detail of
  * the last failure on the calling thread is available from gemm_last_error().

@@ -51,7 +51,8 @@
  *
  * Ownership, errors and streams as in gemm.h: the caller owns every buffer,
  * the library allocates no device memory and never synchronizes; plans are
- * immutable; every entry point returns a status.
+ * immutable; every entry point returns a status; gemm_mx_run may be captured
+ * in a HIP graph like gemm_run.
  */
 #ifndef DTG_GEMM_MX_H
 #define DTG_GEMM_MX_H
