@@ -273,12 +273,16 @@ gemm_config heuristic(const gemm_problem* p, const gemm_device_info& dev, int* g
             best_t = t;
         }
     }
-    // K slices of the 4-stage 128 x 128 tile (one workgroup per CU) whenever
-    // at least two slices of >= 16 K steps fit in the CUs: few tiles with a
-    // deep K, and the wide, short problems (M <= 256) the ladder serves
-    // poorly.  Slices of at least 16 K steps (the fused reduce costs a few
-    // memory round trips, ~4 us), at most 16 (the last arriver reads them
-    // all).  Measured (bf16, medians): 512^2 x 32768 36.5 us with 16 slices
+    // K slices of the 4-stage 128 x 128 tile (one workgroup per CU) when at
+    // least two slices of >= 16 K steps fit in the CUs and the estimate says
+    // they win: few tiles with a deep K, and the wide, short problems
+    // (M <= 256) the ladder serves poorly.  Slices of at least 16 K steps,
+    // at most 16 (the last arriver reads them all).  Estimate, in K steps of
+    // a full round of 256 x 256 tiles: the ladder's best takes best_t x nkt,
+    // the slices 0.43 x nkt / S plus ~3.3 for the fused reduce (a few
+    // dependent memory round trips, ~5 us): 768^2 x 2048 stays on 64 x 64
+    // tiles (12.1 us; 2 slices 16.4 us), 768^2 x 8192 takes 7 slices (24.9
+    // us; 64 x 64 34.3 us).  Measured (bf16, medians): 512^2 x 32768 36.5 us with 16 slices
     // (2-stage tile 42.0, unsplit 322), 1024^2 x 16384 42.6 us with 4 (64 x 64
     // 65.0), 768^2 x 8192 23.9 us with 4 (64 x 64 34.3), 192 x 8192 x 8192
     // 38.1 us with 2 (64 x 64 46.6), 256 x 8192 x 8192 48.4 us with 2
@@ -292,7 +296,8 @@ gemm_config heuristic(const gemm_problem* p, const gemm_device_info& dev, int* g
         int64_t s = dev.cu_count / tiles;
         if (s > nkt / 16) s = nkt / 16;
         if (s > 16) s = 16;
-        if (s > 1) {
+        const double steps = static_cast<double>(nkt);
+        if (s > 1 && split.cost * steps / static_cast<double>(s) + 3.3 < best_t * steps) {
             gemm_config c = cfg_of(split.fam, split.bm, split.bn, split.bk, split.st, split.mf, split.wm, split.wn);
             c.splitk = static_cast<int32_t>(s);
             return c;
