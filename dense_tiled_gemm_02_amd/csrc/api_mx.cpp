@@ -177,6 +177,16 @@ gemm_status plan_impl(const gemm_mx_problem* prob, const gemm_device_info* dev, 
                 want.splitk = s;
             }
         }
+        // Two K slices of the 128 x 128 tiles the ladder chose when both
+        // slices fit in one round and each keeps >= 16 K steps (E4M3 192 x
+        // 8192 x 8192 38.6 -> 30.4 us, 512 x 4096 x 8192 39.7 -> 32.0 us,
+        // 256 x 8192 x 16384 69.7 -> 50.8 us, E2M1 256 x 8192 x 16384 41.6 ->
+        // 33.9 us, 384 x 4096 x 8192 23.2 -> 21.2 us; with 16 K steps or
+        // fewer per slice they lose: E2M1 256 x 8192 x 4096 14.1 -> 18.6 us;
+        // 4 slices lose everywhere here)
+        if (want.bm == 128 && want.bn == 128 && want.splitk == 0 && 2 * tiles128 <= dev->cu_count &&
+            nkt >= 32 && tiles128 <= dtg::kMaxCounters)
+            want.splitk = 2;
     }
     if (force) {
         const gemm_config& f = *force;

@@ -437,6 +437,13 @@ def test_mx_tile_choice_by_rounds_of_workgroups():
     assert cfg(4000, 3000, 1024) == (192, 256, 2)
     assert cfg(3584, 3584, 4096) == (256, 256, 2)     # 192 x 256 would need a second round
     assert cfg(2048, 2048, 4096) == (128, 128, 3)
+    # two K slices of the ladder's 128 x 128 tiles when both fit in one round
+    # and each keeps >= 16 K steps; not with fewer steps, not for 64 x 64
+    for (M, N, K, fmt), s in (((192, 8192, 8192, "e4m3"), 2), ((256, 8192, 16384, "e2m1"), 2),
+                              ((256, 8192, 4096, "e2m1"), 1), ((2048, 2048, 4096, "e4m3"), 1),
+                              ((256, 4096, 8192, "e4m3"), 1)):
+        c = mx_plan(M, N, K, fmt).config
+        assert c.splitk == s, (M, N, K, fmt, c.bm, c.bn, c.splitk)
     assert cfg(2560, 2560, 4096)[:2] in ((256, 128), (128, 256)) and cfg(2560, 2560, 4096)[2] == 3
     assert cfg(4096, 2048, 8192)[:2] in ((256, 128), (128, 256))
     assert cfg(1024, 1024, 4096) == (64, 64, 3)          # 256 small tiles beat 4 K slices of 128 x 128

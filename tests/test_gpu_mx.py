@@ -153,6 +153,27 @@ def test_full_size_workloads_sampled(name):
     assert torch.isfinite(D.float()).all()
 
 
+@pytest.mark.parametrize("fmt,M,N,K", [("e4m3", 192, 8192, 4096), ("e2m1", 200, 8192, 8224)])
+def test_wide_problems_take_two_k_slices(fmt, M, N, K):
+    """Wide problems whose 128 x 128 tiles fill half the CUs or fewer run two
+    K slices (planned, not forced); ragged M and K; sampled outputs, whole
+    first / last rows and columns included, plus the result is repeatable."""
+    A, SA, B, SB = _case(M, N, K, fmt, fmt, 91)
+    p = mx.gemm_mx_plan_create(mx.mx_problem(M, N, K, fmt, fmt), 0, None)
+    cfg = p.config
+    print("mx wide", fmt, M, N, K, cfg.bm, cfg.bn, cfg.splitk, flush=True)
+    assert (cfg.bm, cfg.bn, cfg.splitk) == (128, 128, 2)
+    D = _run(A, SA, B, SB, K, fmt, fmt)
+    D2 = _run(A, SA, B, SB, K, fmt, fmt)
+    assert torch.equal(D.view(torch.int16), D2.view(torch.int16))
+    from helpers import sample_positions
+    ii, jj = sample_positions(M, N, 2000, 19)
+    ref, S, S8 = oracle.mx_gemm_f64_at(A, SA, B, SB, K, fmt, fmt, None, ii, jj, runs=True)
+    got = gemm_inputs.bits(D.cpu())[ii, jj]
+    n, worst, first = oracle.mx_tol_check(got, "bf16", ref, S, S8)
+    assert n == 0, "%s wide: %d sampled outputs outside the bound (worst %.3g)" % (fmt, n, worst)
+
+
 def test_e2m1_products_are_exact_in_binary32():
     """Every E2M1 product has at most 4 significant bits and a run of 8 within one
     block spans few binades, so the instruction's run rounding never bites:
