@@ -103,8 +103,24 @@ __global__ __launch_bounds__(64 * NWV) void gemm_skinny_kernel(KArgs p) {
     const int S = p.splits;
     const int pos = xcd_permute<int>(blockIdx.x, gridDim.x, p.xcds);
     const int slab = pos % nslabs, slice = pos / nslabs;
-    const int n0 = slab * BN;
     const int M = p.M, N = p.N, K = p.K;
+    // Columns of the slab: its first and second halves start at colx and
+    // coly.  A 128-column slab of a whole run of 512 columns (1 KiB of a row)
+    // takes 64-column blocks 0 and 2, 1 and 3, 4 and 6 or 5 and 7 of the run
+    // rather than two adjacent ones, so that each workgroup reads two
+    // different 256-byte quarters of every 1 KiB (slabs that read only the
+    // second quarter of each 1 KiB were measured to finish last): 16 x 8192
+    // x 8192 31.0 -> 30.5 us, bitwise the same.  Otherwise the slab is BN
+    // contiguous columns.
+    int colx = slab * BN, coly = slab * BN + BN / 2;
+    if constexpr (BN == 128) {
+        const int grp = slab / 4, i = slab % 4;
+        if (grp * 512 + 512 <= N) {
+            colx = grp * 512 + ((i < 2) ? i : i + 2) * 64;
+            coly = colx + 128;
+        }
+    }
+    auto real_col = [&](int c) { return c < BN / 2 ? colx + c : coly + (c - BN / 2); };
 
     // chunks of this slice, then of this wave
     const int nck = (K + CK - 1) / CK;
@@ -127,8 +143,8 @@ __global__ __launch_bounds__(64 * NWV) void gemm_skinny_kernel(KArgs p) {
         const int r = b_pos<BN>(pos);
         const int q = b_chunk<BN>(r, lane % CHB);
         b_row[i] = r;
-        b_ok[i] = n0 + 8 * q < N;
-        b_voff[i] = static_cast<uint32_t>(static_cast<int64_t>(r) * p.ldb * 2 + q * 16);
+        b_ok[i] = real_col(8 * q) < N;
+        b_voff[i] = static_cast<uint32_t>(static_cast<int64_t>(r) * p.ldb * 2 + real_col(8 * q) * 2);
     }
     uint32_t a_voff[IA];
     int a_kc[IA];
@@ -144,10 +160,10 @@ __global__ __launch_bounds__(64 * NWV) void gemm_skinny_kernel(KArgs p) {
 
     auto issue = [&](int c, int slot) {
         const int k0 = (c_first + c) * CK;
-        const uint16_t* bbase = p.B + static_cast<int64_t>(k0) * p.ldb + n0;
+        const uint16_t* bbase = p.B + static_cast<int64_t>(k0) * p.ldb;
         const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<uint16_t*>(bbase), 0,
-            clamp_records((static_cast<int64_t>(K - 1 - k0) * p.ldb + (N - n0)) * 2), kRsrcWord3);
+            clamp_records((static_cast<int64_t>(K - 1 - k0) * p.ldb + N) * 2), kRsrcWord3);
         const uint16_t* abase = p.A + k0;
         const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<uint16_t*>(abase), 0,
@@ -260,9 +276,10 @@ __global__ __launch_bounds__(64 * NWV) void gemm_skinny_kernel(KArgs p) {
             float v = 0.0f;
 #pragma unroll
             for (int w = 0; w < NWV; ++w) v += red[(w * BMR + row) * BN + col];
-            if (row < M && n0 + col < N) {
-                if (has_c) v += widen<BF16>(p.C[static_cast<int64_t>(row) * p.ldc + n0 + col]);
-                p.D[static_cast<int64_t>(row) * p.ldd + n0 + col] = narrow<BF16>(v);
+            const int gc = real_col(col);
+            if (row < M && gc < N) {
+                if (has_c) v += widen<BF16>(p.C[static_cast<int64_t>(row) * p.ldc + gc]);
+                p.D[static_cast<int64_t>(row) * p.ldd + gc] = narrow<BF16>(v);
             }
         }
         return;
@@ -323,10 +340,11 @@ __global__ __launch_bounds__(64 * NWV) void gemm_skinny_kernel(KArgs p) {
     for (int j = 0; j < PT; ++j) {
         const int t = tid + j * NT;
         const int row = t / BN, col = t % BN;
-        if (t < BMR * BN && row < M && n0 + col < N) {
+        const int gc = real_col(col);
+        if (t < BMR * BN && row < M && gc < N) {
             float o = v[j];
-            if (has_c) o += widen<BF16>(p.C[static_cast<int64_t>(row) * p.ldc + n0 + col]);
-            p.D[static_cast<int64_t>(row) * p.ldd + n0 + col] = narrow<BF16>(o);
+            if (has_c) o += widen<BF16>(p.C[static_cast<int64_t>(row) * p.ldc + gc]);
+            p.D[static_cast<int64_t>(row) * p.ldd + gc] = narrow<BF16>(o);
         }
     }
     if (tid == 0) __hip_atomic_store(&counters[slab], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
