@@ -94,6 +94,8 @@ def parse():
                     help="time the decode regime: M in {1,2,4,8,16,32}, N = K in {4096, 8192}, bf16")
     ap.add_argument("--mx", action="store_true",
                     help="block-scaled (MX) workloads: FP8 / FP4 elements with E8M0 scales per 32 k")
+    ap.add_argument("--configs", action="store_true",
+                    help="every named workload against torch.matmul, batches of 10 launches captured in a HIP graph")
     ap.add_argument("--mx-sweep", action="store_true",
                     help="block-scaled tile / slice variants of the decode and square workloads, interleaved")
     ap.add_argument("--rounds", type=int, default=30)
@@ -388,6 +390,69 @@ def decode(args):
         del Bs
 
 
+def configs(args):
+    """Every named workload (the planner's plan) against torch.matmul (torch.addmm
+    with an addend): each timed batch is one HIP graph of 10 launches, so host
+    launch cost is out of both; rounds in seeded-random order, medians.  The
+    skinny and decode workloads rotate B over 4 copies (read from HBM).  One
+    JSON line per workload."""
+    import random
+    import torch
+    import gemm_inputs
+    import dense_tiled_gemm_02_amd as g
+    for name, w in gemm_inputs.WORKLOADS.items():
+        A, B, C = gemm_inputs.make(name)
+        dA = A.cuda()
+        ncopy = 4 if w.M <= 16 else 1
+        Bs = [B.cuda()] + [gemm_inputs.draw((w.K, w.N), 990 + r, w.dtype, w.dist, w.scale).cuda()
+                           for r in range(1, ncopy)]
+        dC = C.cuda() if C is not None else None
+        D1 = torch.empty((w.M, w.N), dtype=dA.dtype, device="cuda")
+        D2 = torch.empty_like(D1)
+
+        def ours(i):
+            g.matmul(dA, Bs[i % ncopy], dC, out=D1)
+
+        def theirs(i):
+            if dC is None:
+                torch.matmul(dA, Bs[i % ncopy], out=D2)
+            else:
+                torch.addmm(dC, dA, Bs[i % ncopy], out=D2)
+        graphs = {}
+        side = torch.cuda.Stream()
+        # a K-sliced plan's workspace for the capture stream, zero-filled before the capture
+        g.workspace_for(g.plan_for(dA, Bs[0], dC, D1), torch.cuda.current_device(), side.cuda_stream)
+        for key, f in (("ours", ours), ("torch", theirs)):
+            for i in range(3):
+                f(i)
+            torch.cuda.synchronize()
+            gr = torch.cuda.CUDAGraph()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.graph(gr, stream=side):
+                for i in range(10):
+                    f(i)
+            torch.cuda.synchronize()
+            graphs[key] = gr
+        t = {k: [] for k in graphs}
+        rng = random.Random(1)
+        for _ in range(args.rounds):
+            order = list(graphs)
+            rng.shuffle(order)
+            for k in order:
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                graphs[k].replay()
+                e1.record()
+                torch.cuda.synchronize()
+                t[k].append(e0.elapsed_time(e1) / 10)
+        us = {k: stats(v)["median_ms"] * 1e3 for k, v in t.items()}
+        byt = 2.0 * (w.M * w.K + w.K * w.N + w.M * w.N * (2 if dC is not None else 1))
+        print(json.dumps({"workload": name, "plan": g.plan_for(dA, Bs[0], dC, D1).describe().split(" bm=")[0],
+                          "us": round(us["ours"], 2), "torch_us": round(us["torch"], 2),
+                          "tflops": round(w.flops() / us["ours"] / 1e6, 1), "gbs": round(byt / us["ours"] / 1e3, 1)}),
+              flush=True)
+
+
 def mx(args):
     """Block-scaled (MX) workloads: the planner's plan, median and spread over
     interleaved rounds, against the dense MFMA peak of the element type (square)
@@ -575,6 +640,9 @@ def main():
         return
     if args.decode:
         decode(args)
+        return
+    if args.configs:
+        configs(args)
         return
     if args.layouts:
         layouts(args)
