@@ -7,6 +7,8 @@ the kernel, and checks whole first / last rows and columns plus random
 outputs against the binary64 oracle with the acceptance rule of the parity
 tests.  The block-scaled cases do the same for random format pairs.
 """
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -26,7 +28,11 @@ def gpu():
     torch.cuda.init()
 
 
-def _cases(n=96, seed=2024):
+# more cases on request (DTG_FUZZ_CASES=600 python -m pytest tests/test_gpu_fuzz.py)
+N_CASES = int(os.environ.get("DTG_FUZZ_CASES", "96"))
+
+
+def _cases(n=N_CASES, seed=2024):
     rng = np.random.default_rng(seed)
     out = []
     for i in range(n):
@@ -72,7 +78,7 @@ def test_random_problem_matches_oracle(case):
     check(A, B, C, D.cpu(), dt, sample=sample_positions(M, N, 600, seed % 1000), label="fuzz %s" % (case,))
 
 
-def _mx_cases(n=32, seed=77):
+def _mx_cases(n=max(8, N_CASES // 3), seed=77):
     rng = np.random.default_rng(seed)
     pairs = [("e4m3", "e4m3"), ("e5m2", "e5m2"), ("e4m3", "e5m2"), ("e5m2", "e4m3"), ("e2m1", "e2m1")]
     out = []
