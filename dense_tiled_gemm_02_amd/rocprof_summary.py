@@ -4,6 +4,7 @@
     python -m dense_tiled_gemm_02_amd.rocprof_summary --traffic FETCH_DIR WRITE_DIR COPY_BYTES OUT.json
     python -m dense_tiled_gemm_02_amd.rocprof_summary --report OUT MATCH "WORKLOAD" "WORK" COPY_BYTES
     python -m dense_tiled_gemm_02_amd.rocprof_summary --report-mx OUT MATCH "WORKLOAD" "WORK" COPY_BYTES
+    python -m dense_tiled_gemm_02_amd.rocprof_summary --report-cmd OUT PREFIX "BENCH" MATCH "WORKLOAD" "WORK" COPY_BYTES TRAFFIC
 
 --report composes the per-kernel summary kept under profiles/ from the five
 passes OUT/prof_{trace,fetch,write,mfma,lds} that profile_commands() lists,
@@ -139,12 +140,14 @@ def profile_commands(out="OUT", bench=BENCH, prefix="prof_"):
             for name, flags, o in PASSES]
 
 
-def report(out, match, workload, work, copy_bytes, mx=False):
+def report(out, match, workload, work, copy_bytes, mx=False, bench=None, prefix=None, traffic_file=None):
     """Text summary of one kernel over the five passes under `out` (the
-    prof_* passes of the default benchmark, or the mxprof_* passes of
-    bench.py --mx with mx=True)."""
-    prefix = "mxprof_" if mx else "prof_"
-    bench = BENCH_MX if mx else BENCH
+    prof_* passes of the default benchmark, the mxprof_* passes of
+    bench.py --mx with mx=True, or the passes `prefix`* of another bench.py
+    command `bench`)."""
+    custom = bench is not None
+    prefix = prefix or ("mxprof_" if mx else "prof_")
+    bench = bench or (BENCH_MX if mx else BENCH)
     lines = []
     names = set()
     for name, _, _ in PASSES:
@@ -159,7 +162,10 @@ def report(out, match, workload, work, copy_bytes, mx=False):
     lines.append("Algorithmic work per launch: " + work)
     lines.append("")
     lines.append("Commands (run from the repository root on one MI355X, after")
-    if mx:
+    if custom:
+        lines.append('"python -m dense_tiled_gemm_02_amd.build"; the bench.py command runs the workload named')
+        lines.append("above and ends with one 512 MiB device")
+    elif mx:
         lines.append('"python -m dense_tiled_gemm_02_amd.build"; bench.py --mx runs the three block-scaled')
         lines.append("workloads (FP4 16x8192x8192, FP4 4096^3, E4M3 4096^3) and ends with one 512 MiB device")
     else:
@@ -169,9 +175,14 @@ def report(out, match, workload, work, copy_bytes, mx=False):
     for c in profile_commands(bench=bench, prefix=prefix):
         lines.append("  " + c)
     lines.append("  python3 -m dense_tiled_gemm_02_amd.rocprof_summary --traffic OUT/%sfetch OUT/%swrite "
-                 "%d profiles/%s" % (prefix, prefix, copy_bytes, "traffic_mx.json" if mx else "traffic.json"))
-    lines.append('  python3 -m dense_tiled_gemm_02_amd.rocprof_summary --report%s OUT "%s" ...   (this file)' % (
-        "-mx" if mx else "", match))
+                 "%d profiles/%s" % (prefix, prefix, copy_bytes,
+                                     traffic_file or ("traffic_mx.json" if mx else "traffic.json")))
+    if custom:
+        lines.append('  python3 -m dense_tiled_gemm_02_amd.rocprof_summary --report-cmd OUT %s "%s" "%s" ...   '
+                     '(this file)' % (prefix, bench, match))
+    else:
+        lines.append('  python3 -m dense_tiled_gemm_02_amd.rocprof_summary --report%s OUT "%s" ...   (this file)' % (
+            "-mx" if mx else "", match))
     for name, _, _ in PASSES:
         lines.append("")
         lines.append("--- %s ---" % TITLES[name])
@@ -207,6 +218,11 @@ if __name__ == "__main__":
                 _short(k, 100), v["fetch_kib"], v["write_kib"], v["bytes"] / 1e6))
         print("scales: fetch %.4f  write %.4f  (copy of %d bytes)" % (t["fetch_scale"], t["write_scale"],
                                                                      t["copy_bytes"]))
+        sys.exit(0)
+    if args and args[0] == "--report-cmd":
+        # --report-cmd OUT PREFIX "BENCH COMMAND" MATCH WORKLOAD WORK COPY_BYTES TRAFFIC_FILE
+        sys.stdout.write(report(args[1], args[4], args[5], args[6], int(args[7]), bench=args[3], prefix=args[2],
+                                traffic_file=args[8]))
         sys.exit(0)
     if args and args[0] in ("--report", "--report-mx"):
         sys.stdout.write(report(args[1], args[2], args[3], args[4], int(args[5]), mx=args[0] == "--report-mx"))
