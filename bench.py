@@ -237,13 +237,17 @@ def host_cpu_model():
 def sweep(args):
     import gemm_inputs
     variants = {
-        "square_bf16_4096": [dict(kernel=3, bm=256, bn=256, bk=64, stages=2, mfma=16, group_m=gm) for gm in (1, 8)] +
-                            [dict(kernel=3, bm=256, bn=256, bk=32, stages=4, mfma=16, group_m=gm) for gm in (1, 8)] +
-                            [dict(kernel=3, bm=256, bn=256, bk=64, stages=2, mfma=32, group_m=8),
-                             dict(kernel=3, bm=256, bn=256, bk=32, stages=4, mfma=32, group_m=8),
+        # GROUP_M {1, 4, 8} x instruction {16x16x32, 32x32x16} at the 256 x 256
+        # tile with 8 waves (2 per SIMD) and with 4 (one per SIMD, AGPR
+        # accumulators), deeper rings of 32-deep K steps, and the smaller tiles
+        "square_bf16_4096": [dict(kernel=3, bm=256, bn=256, bk=64, stages=2, mfma=mf, waves_m=2, waves_n=wn,
+                                  group_m=gm) for wn in (4, 2) for mf in (16, 32) for gm in (1, 4, 8)] +
+                            [dict(kernel=3, bm=256, bn=256, bk=32, stages=st, mfma=32, waves_m=2, waves_n=2,
+                                  group_m=8) for st in (4, 5)] +
+                            [dict(kernel=3, bm=256, bn=256, bk=32, stages=4, mfma=16, waves_m=2, waves_n=4,
+                                  group_m=8),
                              dict(kernel=3, bm=256, bn=128, bk=64, stages=3, mfma=16, group_m=8),
-                             dict(kernel=3, bm=128, bn=128, bk=64, stages=4, mfma=16, group_m=8),
-                             dict(kernel=3, bm=128, bn=128, bk=64, stages=2, mfma=32, group_m=8)],
+                             dict(kernel=3, bm=128, bn=128, bk=64, stages=4, mfma=16, group_m=8)],
         "square_f16_1024": [dict(), dict(kernel=3, bm=128, bn=128, bk=64, stages=4, waves_m=2, waves_n=4),
                             dict(kernel=3, bm=128, bn=128, bk=32, stages=4, waves_m=2, waves_n=4),
                             dict(kernel=3, bm=128, bn=128, bk=32, stages=4, waves_m=2, waves_n=4, splitk=2),

@@ -46,6 +46,38 @@ __device__ __forceinline__ typename AccT<MF>::type mfma(u32x4 a, u32x4 b,
     }
 }
 
+// The same contraction with the accumulator held in AGPRs ("+a"), for tiles
+// whose accumulators fill the whole AGPR file (256 per lane at one wave per
+// SIMD): left to itself the register allocator splits such an accumulator
+// between VGPRs and AGPRs and spills.  The operands come from LDS reads that
+// the kernel waits for explicitly; the caller pads the hazard between the
+// last instruction and the first read of the result (agpr_settle).
+template <int MF, bool BF16>
+__device__ __forceinline__ void mfma_agpr(typename AccT<MF>::type& c, u32x4 a, u32x4 b) {
+    if constexpr (MF == 32) {
+        if constexpr (BF16) asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+        else asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+    } else {
+        if constexpr (BF16) asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+        else asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+    }
+}
+
+// Wait states between the last matrix instruction writing an AGPR
+// accumulator and the first VALU read of it: the compiler does not see into
+// the asm above, so the longest required gap (below 32) is padded by hand.
+__device__ __forceinline__ void agpr_settle() {
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+}
+
+// Element of an AGPR-held accumulator, moved to a VGPR here and not earlier
+// (the allocator would otherwise copy the whole tile out at once and spill).
+__device__ __forceinline__ float agpr_get(float a) {
+    float v;
+    asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v) : "a"(a));
+    return v;
+}
+
 template <bool BF16>
 __device__ __forceinline__ float widen(uint16_t h) {
     if constexpr (BF16) return __uint_as_float(static_cast<uint32_t>(h) << 16);

@@ -98,6 +98,9 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(KArgs p) {
     static_assert(BK % KI == 0, "BK");
     static_assert(ST >= 2 && ST <= 5 && (ST - 1) * L < 64, "stages");
     typedef typename AccT<MF>::type acc_t;
+    // accumulators per lane; above 128 (one wave per SIMD holding a
+    // 128 x 128 wave tile) they live in AGPRs, placed there explicitly
+    constexpr bool AGPR = FM * FN * AccT<MF>::regs > 128;
 
     __shared__ __attribute__((aligned(1024))) uint16_t smem[ST * (SA + SB)];
 
@@ -340,27 +343,45 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(KArgs p) {
         constexpr int SL = decltype(slot_tag)::value;
         constexpr int Q = decltype(q_tag)::value;
         constexpr int I = Q / FN, J = Q % FN;
-        acc[I][J] = mfma<MF, BF16>(fb[SL][J], fa[SL][I], acc[I][J]);
+        if constexpr (AGPR) mfma_agpr<MF, BF16>(acc[I][J], fb[SL][J], fa[SL][I]);
+        else acc[I][J] = mfma<MF, BF16>(fb[SL][J], fa[SL][I], acc[I][J]);
+    };
+    // accumulator element (i, j, r) in a VGPR, for the reduce and the epilogue
+    auto acc_at = [&](int i, int j, int r) -> float {
+        if constexpr (AGPR) return agpr_get(acc[i][j][r]);
+        else return acc[i][j][r];
     };
     constexpr int NQ = FM * FN;       // MFMAs per sub-step
 
     // The MFMAs of a sub-step with NOPS memory operations spread between them:
     // operation o follows MFMA number o * SP; the last TAIL MFMAs carry none,
-    // so the LDS reads have landed when the sub-step ends.  Every pair is
-    // fenced, so the compiler keeps exactly this order.
+    // so the LDS reads have landed when the sub-step ends.  When there are
+    // more operations than MFMA slots, PER of them follow each MFMA from the
+    // first on (one-wave-per-SIMD tiles; the others leave the surplus after
+    // the last MFMA).  Every group is fenced, so the compiler keeps exactly
+    // this order.
     auto interleave = [&](auto slot_tag, auto nops_tag, auto&& op) {
         constexpr int SL = decltype(slot_tag)::value;
         constexpr int NOPS = decltype(nops_tag)::value;
         constexpr int TAIL = NQ / 4;
-        constexpr int SP = (NOPS == 0) ? 1 : ((NQ - TAIL) / NOPS > 0 ? (NQ - TAIL) / NOPS : 1);
+        constexpr int SLOTS = NQ - TAIL;
+        constexpr int SP = (NOPS == 0) ? 1 : (SLOTS / NOPS > 0 ? SLOTS / NOPS : 1);
+        constexpr int PER = (!AGPR || SLOTS / NOPS > 0) ? 1 : (NOPS + SLOTS - 1) / SLOTS;
         static_for<NQ>([&](auto q_tag) {
             constexpr int Q = decltype(q_tag)::value;
             mfma_op(std::integral_constant<int, SL>{}, q_tag);
-            if constexpr (Q % SP == 0 && Q / SP < NOPS) op(std::integral_constant<int, Q / SP>{});
+            if constexpr (PER == 1) {
+                if constexpr (Q % SP == 0 && Q / SP < NOPS) op(std::integral_constant<int, Q / SP>{});
+            } else {
+                static_for<PER>([&](auto e_tag) {
+                    constexpr int O = Q * PER + decltype(e_tag)::value;
+                    if constexpr (O < NOPS) op(std::integral_constant<int, O>{});
+                });
+            }
             __builtin_amdgcn_sched_barrier(0);
         });
         // ops left over when there are more operations than MFMA slots
-        if constexpr (NOPS > NQ / SP) {
+        if constexpr (PER == 1 && NOPS > NQ / SP) {
             static_for<NOPS - NQ / SP>([&](auto o_tag) {
                 op(std::integral_constant<int, NQ / SP + decltype(o_tag)::value>{});
             });
@@ -420,14 +441,25 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(KArgs p) {
                     std::integral_constant<int, 0>{}, r_tag);
         });
         wait_frags(std::integral_constant<int, 0>{});
-        for (int j = 0; j < nkt; j += UNROLL) {
-            static_for<UNROLL>([&](auto u_tag) {
-                if (j + decltype(u_tag)::value < nkt) step(u_tag, kt0 + j + decltype(u_tag)::value);
-            });
+        if constexpr (AGPR) {
+            // Whole unrolled groups only: a conditional step inside the loop
+            // makes the allocator move AGPR accumulators through scratch.  A
+            // step past the slice contracts the zeros its empty-range loads
+            // wrote, which leaves every accumulator unchanged (an exact +0
+            // added to a sum that started at +0).
+            for (int j = 0; j < nkt; j += UNROLL)
+                static_for<UNROLL>([&](auto u_tag) { step(u_tag, kt0 + j + decltype(u_tag)::value); });
+        } else {
+            for (int j = 0; j < nkt; j += UNROLL) {
+                static_for<UNROLL>([&](auto u_tag) {
+                    if (j + decltype(u_tag)::value < nkt) step(u_tag, kt0 + j + decltype(u_tag)::value);
+                });
+            }
         }
         // no load may still be writing this workgroup's LDS when it exits
         wait_vm<0>();
     }
+    if constexpr (AGPR) agpr_settle();
 
     // ---- K slices across workgroups: publish this slice's fp32 partial tile;
     // the workgroup that arrives last at the tile's counter sums the slices
@@ -439,6 +471,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(KArgs p) {
     constexpr int NB = FM * FN * (AccT<MF>::regs / 4);   // 16-byte runs per lane
     // (two slices of partials are held in registers: only tiles of at most
     // 64 accumulators per lane take K slices; the planner keeps the others at 1)
+    static_assert(NB > 16 || !AGPR, "K slices keep their partials in VGPRs");
     if constexpr (NB <= 16) if (NS > 1) {
         constexpr int64_t WAVE_F = static_cast<int64_t>(NB) * 64 * 4;   // floats per wave per slice
         int* counters = static_cast<int*>(p.ws);
@@ -541,10 +574,10 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(KArgs p) {
                         const int row = wm * TM + i * MF + (lane % MF);
                         const int col = wn * TN + j * MF + 8 * q + 4 * (lane / MF);
                         uint2 dv;
-                        dv.x = static_cast<uint32_t>(narrow<BF16>(acc[i][j][4 * q])) |
-                               (static_cast<uint32_t>(narrow<BF16>(acc[i][j][4 * q + 1])) << 16);
-                        dv.y = static_cast<uint32_t>(narrow<BF16>(acc[i][j][4 * q + 2])) |
-                               (static_cast<uint32_t>(narrow<BF16>(acc[i][j][4 * q + 3])) << 16);
+                        dv.x = static_cast<uint32_t>(narrow<BF16>(acc_at(i, j, 4 * q))) |
+                               (static_cast<uint32_t>(narrow<BF16>(acc_at(i, j, 4 * q + 1))) << 16);
+                        dv.y = static_cast<uint32_t>(narrow<BF16>(acc_at(i, j, 4 * q + 2))) |
+                               (static_cast<uint32_t>(narrow<BF16>(acc_at(i, j, 4 * q + 3))) << 16);
                         const int pos = ((col / 8) ^ (row % CPR)) * 16 + (col % 8) * 2;
                         *reinterpret_cast<uint2*>(stage + row * (BN * 2) + pos) = dv;
                     }
@@ -605,8 +638,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(KArgs p) {
                             for (int q = 0; q < G; ++q) {
                                 const int row = (wm % WPP) * TM + i * MF + (lane % MF);
                                 const int col = wn * TN + j * MF + 8 * q + 4 * (lane / MF);
-                                const f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
-                                                 acc[i][j][4 * q + 3]};
+                                const f32x4 v = {acc_at(i, j, 4 * q), acc_at(i, j, 4 * q + 1),
+                                                 acc_at(i, j, 4 * q + 2), acc_at(i, j, 4 * q + 3)};
                                 *reinterpret_cast<f32x4*>(stage + row * (BN * 4) + ((col / 4) ^ (row % 16)) * 16) = v;
                             }
                 }
@@ -663,7 +696,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(KArgs p) {
                 const int col = n0 + wn * TN + j * MF + 8 * q + 4 * (lane / MF);
                 float v[4];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) v[r] = acc[i][j][4 * q + r];
+                for (int r = 0; r < 4; ++r) v[r] = acc_at(i, j, 4 * q + r);
                 if (dvec && cvec && col + 4 <= N) {
                     if (has_c) {
                         const uint2 cv = *reinterpret_cast<const uint2*>(p.C + crow + col);
