@@ -5,12 +5,18 @@
                     [--sweep] [--no-cpu] [--config k=v,...]
 
 A step is one launch of the whole hot path, D = A x B (+C), on the workload's
-synthetic inputs, which are resident in HBM before timing starts.  The timed
-region is K launches on one stream between two HIP events, preceded and
+synthetic inputs, which are resident in HBM before timing starts.  First the
+median and its spread: 12 (--batches, at least 10) batches of >= 1 ms, at
+least 10 launches each, every batch timed between two HIP events on the
+launch stream ("Tuning Triton", section 2: report the median with its
+spread).  Then, in the same warm regime, the timed region: W untimed launches,
+then exactly K launches on one stream between two HIP events, preceded and
 followed by a device synchronization; ms_per_step is elapsed / K.
 
 One JSON line is printed (rank 0, N = 1):
-  value     TFLOP/s of the headline workload (bf16 4096^3 by default)
+  value     TFLOP/s of the headline workload (bf16 4096^3 by default) over
+            the timed region; spread.median_ms and spread.tflops_at_median
+            give the batches' median beside it
   roofline  the kernel's achieved flop rate against the dense bf16 MFMA peak
             (256 CUs x 2.4 GHz x 4096 flop/clk/CU = 2516.6 TFLOP/s), plus the
             HBM roofline figures of the skinny workload (bf16 16 x 8192 x 8192,
@@ -41,6 +47,10 @@ PEAK_MX_TFLOPS = {"e4m3": 5000.0, "e5m2": 5000.0, "e2m1": 10100.0}   # MI355X de
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
 TRAFFIC_MX_JSON = os.path.join(ROOT, "profiles", "traffic_mx.json")
+# What the counters behind "traffic" count: FETCH_SIZE and WRITE_SIZE are the
+# L2's requests to the memory fabric, so re-reads that hit the last-level
+# cache in front of HBM (the 256 MB MALL) count too.
+TRAFFIC_KIND = "L2-to-fabric bytes per launch (FETCH_SIZE x 2 + WRITE_SIZE, copy-calibrated; MALL hits included)"
 
 
 def plan_kernel_name(profiled):
@@ -104,6 +114,9 @@ def parse():
     ap.add_argument("--config", default="", help="forced config fields, e.g. bm=128,bn=128,mfma=32")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--out", default="")
+    ap.add_argument("--save", default="", help="sweep modes: write the records and the command to this JSON file")
+    ap.add_argument("--batches", type=int, default=12,
+                    help="batches of >= 1 ms for the headline median and spread (at least 10)")
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="after timing, run one device copy of this many MiB (counter calibration)")
     return ap.parse_args()
@@ -199,6 +212,26 @@ def stats(ts):
             "min_ms": min(ts), "max_ms": max(ts), "n": len(ts)}
 
 
+def batch_len(launch, target_ms=1.0, least=10):
+    """Launches per timed batch: at least `least`, and enough for >= target_ms."""
+    probe = time_region(launch, 5, 3)
+    return max(least, int(-(-target_ms // max(probe, 1e-4))))
+
+
+def headline_times(launch, steps, warmup, rounds):
+    """The headline measurement of one kernel, in one warm regime:
+    `rounds` batches of >= 1 ms (>= 10 launches) each timed between two
+    events on the launch stream, for the median and its spread; then the
+    timed region proper, `warmup` untimed launches and exactly `steps`
+    launches between two events (ms_per_step).  Returns (ms_per_step,
+    stats of the batches with the batch length added)."""
+    batch = batch_len(launch)
+    st = stats(batch_times(launch, batch, rounds))
+    st["batch_launches"] = batch
+    ms = time_region(launch, steps, warmup)
+    return ms, st
+
+
 def cpu_baseline(w, seconds):
     """Time the CPU oracle on the first rows of the workload (bounded sample)."""
     import oracle
@@ -248,7 +281,11 @@ def sweep(args):
                                   group_m=8),
                              dict(kernel=3, bm=256, bn=128, bk=64, stages=3, mfma=16, group_m=8),
                              dict(kernel=3, bm=128, bn=128, bk=64, stages=4, mfma=16, group_m=8)],
-        "square_f16_1024": [dict(), dict(kernel=3, bm=128, bn=128, bk=64, stages=4, waves_m=2, waves_n=4),
+        # the planner's plan, the three tiles of the tile-size sweep (32^3 and 64 x 64 x 32 register-staged,
+        # 128 x 128 x 64 both ways), then other direct-to-LDS tiles and K slices
+        "square_f16_1024": [dict(), dict(kernel=1, bm=32, bn=32, bk=32), dict(kernel=1, bm=64, bn=64, bk=32, stages=2),
+                            dict(kernel=1, bm=128, bn=128, bk=64, stages=2),
+                            dict(kernel=3, bm=128, bn=128, bk=64, stages=4, waves_m=2, waves_n=4),
                             dict(kernel=3, bm=128, bn=128, bk=32, stages=4, waves_m=2, waves_n=4),
                             dict(kernel=3, bm=128, bn=128, bk=32, stages=4, waves_m=2, waves_n=4, splitk=2),
                             dict(kernel=3, bm=128, bn=128, bk=64, stages=4, waves_m=2, waves_n=4, splitk=2),
@@ -312,12 +349,25 @@ def sweep(args):
     for i, (v, _, pl) in enumerate(ls):
         st = stats(times[i])
         ms = st["median_ms"]
-        rec = {"workload": w.name, "variant": v, "plan": pl.describe(), **st,
+        rec = {"workload": w.name, "variant": v, "plan": pl.describe(), **st, "batch_launches": batch,
                "tflops": w.flops() / ms / 1e9, "pct_mfma": 100 * w.flops() / ms / 1e9 / PEAK_BF16_TFLOPS,
                "gbs": w.bytes() / ms / 1e6, "pct_hbm": 100 * w.bytes() / ms / 1e6 / PEAK_HBM_GBS}
         rows.append(rec)
         print(json.dumps(rec), flush=True)
+    if args.save:
+        save_rows(args.save, rows, "interleaved sweep of %s: %d rounds in seeded-random order, one batch of %d "
+                                   "launches per variant per round" % (w.name, args.rounds, batch))
     return rows
+
+
+def save_rows(path, rows, what):
+    """Sweep records with the command that made them and the device, as one JSON file."""
+    import torch
+    doc = {"what": what, "command": "python " + " ".join(sys.argv), "device": torch.cuda.get_device_name(0),
+           "rows": rows}
+    with open(path, "w") as f:
+        json.dump(doc, f, indent=1)
+        f.write("\n")
 
 
 def layouts(args):
@@ -661,10 +711,12 @@ def main():
     case = Case(w, rotate=4 if w.name.startswith("skinny") else 1)
     launch, pl = case.launcher(_cfg(args.config))
     torch.cuda.synchronize()
-    ms = time_region(launch, args.steps, args.warmup)
-    spread = stats(batch_times(launch, max(1, args.steps // 10), 10))
+    rounds = max(10, args.batches)
+    ms, spread = headline_times(launch, args.steps, args.warmup, rounds)
     flops = w.flops()
     tflops = flops / ms / 1e9
+    spread["tflops_at_median"] = flops / spread["median_ms"] / 1e9
+    spread["region_within_spread"] = spread["min_ms"] <= ms <= spread["max_ms"]
     rec = {
         "metric": "GEMM TFLOPS + % of MFMA peak at 4096^3 bf16; % HBM BW on skinny",
         "value": round(tflops, 2),
@@ -682,18 +734,22 @@ def main():
         "spread": spread,
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": round(PEAK_BF16_TFLOPS, 1),
                      "unit": "TFLOP/s", "frac": tflops / PEAK_BF16_TFLOPS,
-                     "traffic": measured_traffic(kernel_of(pl.describe()))},
+                     "traffic": measured_traffic(kernel_of(pl.describe())), "traffic_kind": TRAFFIC_KIND},
     }
     if not args.no_skinny and args.workload != "skinny_bf16_16x8192":
         sw = gemm_inputs.WORKLOADS["skinny_bf16_16x8192"]
         sc = Case(sw, rotate=4)
         sl, spl = sc.launcher()
-        sms = time_region(sl, max(40, args.steps), 8)
+        sms, sspread = headline_times(sl, max(40, args.steps), 8, rounds)
         gbs = sw.bytes() / sms / 1e6
-        rec["skinny"] = {"workload": sw.name, "plan": spl.describe(), "ms_per_step": sms,
+        sspread["gbs_at_median"] = sw.bytes() / sspread["median_ms"] / 1e6
+        sspread["region_within_spread"] = sspread["min_ms"] <= sms <= sspread["max_ms"]
+        rec["skinny"] = {"workload": sw.name, "plan": spl.describe(), "ms_per_step": sms, "steps": max(40, args.steps),
+                         "spread": sspread,
                          "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                                       "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
-                                      "traffic": measured_traffic(kernel_of(spl.describe()))},
+                                      "traffic": measured_traffic(kernel_of(spl.describe())),
+                                      "traffic_kind": TRAFFIC_KIND},
                          "tflops": sw.flops() / sms / 1e9}
         del sc
     if args.copy_mb:

@@ -82,21 +82,28 @@ def test_output_types_and_addend(fmt, out):
     _check(D, ref, S, S8, out, "%s out %s + C" % (fmt, out))
 
 
-@pytest.mark.parametrize("fmt", ["e4m3", "e2m1"])
-def test_padded_rows_and_scale_strides(fmt):
-    """Row strides above the packed size (A, B, scales and D)."""
-    M, N, K = 200, 136, 768
+@pytest.mark.parametrize("K", [768, 736])
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2", "e2m1"])
+def test_padded_rows_and_scale_strides(fmt, K):
+    """Row strides above the packed size (A, B, scales and D).  The bytes past
+    K in every row of A and B are NaN codes (0x7F in both 8-bit formats;
+    E2M1 has none, so its largest magnitude, 0x77), and K = 736 ends inside a
+    K step: a K-tail mask missing on either operand shows as a non-finite or
+    far-off output."""
+    M, N = 200, 136
     A0, SA0, B0, SB0 = _case(M, N, K, fmt, fmt, 91)
     pad = lambda x, extra, fill: np.concatenate([x, np.full((x.shape[0], extra), fill, np.uint8)], 1)
-    A, B = pad(A0, 48, 0x7E), pad(B0, 16, 0x7E)            # padding holds large finite values
+    fill = 0x77 if fmt == "e2m1" else 0x7F
+    A, B = pad(A0, 48, fill), pad(B0, 16, fill)
     SA, SB = pad(SA0, 8, 0xFF), pad(SB0, 4, 0xFF)
     Dbig = torch.full((M, N + 24), float("nan"), dtype=torch.bfloat16, device="cuda")
     D = Dbig[:, :N]
-    print("mx padded", fmt, flush=True)
+    print("mx padded", fmt, K, flush=True)
     mx.mx_matmul(_dev(A), _dev(SA), _dev(B), _dev(SB), K, fmt, fmt, out=D)
     torch.cuda.synchronize()
     ref, S, S8 = oracle.mx_gemm_f64(A0, SA0, B0, SB0, K, fmt, fmt, runs=True)
-    _check(D.contiguous(), ref, S, S8, "bf16", "padded " + fmt)
+    assert torch.isfinite(D.float()).all()
+    _check(D.contiguous(), ref, S, S8, "bf16", "padded %s K=%d" % (fmt, K))
     assert torch.isnan(Dbig[:, N:].float()).all()           # nothing written past N
 
 

@@ -47,11 +47,15 @@ def test_workload_full_parity(name):
     check(A, B, C, D, w.dtype, label=name)
 
 
-def test_workload_4096_sampled_parity():
+def test_workload_4096_full_parity():
+    """Every one of the 16.8 M outputs of the benchmark's workload, in the
+    launch configuration the benchmark times (the planner's plan), against
+    the full binary64 product (a few seconds of the oracle on the host)."""
     w = gemm_inputs.WORKLOADS["square_bf16_4096"]
     A, B, C = gemm_inputs.make(w)
+    print("case", w.name, g.plan_for(A.cuda(), B.cuda(), None, None).describe(), flush=True)
     D = gpu_run(A, B, C)
-    check(A, B, C, D, w.dtype, sample=sample_positions(w.M, w.N, 20000, 7), label=w.name)
+    check(A, B, C, D, w.dtype, label=w.name)
     # every output finite and of the expected scale (property at any size)
     Df = D.float()
     assert torch.isfinite(Df).all()
