@@ -19,13 +19,11 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libgemm.so")
-PROBE_LIB = os.path.join(PKG, "libgemm_probe.so")
 ARCH = "gfx950"
 
 SOURCES = ["api.cpp", "api_mx.cpp", "gemm_tile.hip", "gemm_dma.hip", "gemm_dma_more.hip", "gemm_dma_layouts.hip",
            "gemm_mx.hip",
            "gemm_skinny.hip"]
-PROBE_SOURCES = ["probe.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 COMMON = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH,
@@ -71,11 +69,10 @@ def build(verbose=False, jobs=None, asm=None):
     if asm is None:
         asm = os.environ.get("DTG_ASM", "0") not in ("", "0")
     # the largest sources first, so they start at once
-    srcs = sorted(SOURCES + PROBE_SOURCES, key=lambda f: -os.path.getsize(os.path.join(CSRC, f)))
+    srcs = sorted(SOURCES, key=lambda f: -os.path.getsize(os.path.join(CSRC, f)))
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
         objs = dict(zip(srcs, ex.map(lambda s: _compile(s, verbose, asm), srcs)))
     _link([objs[s] for s in SOURCES], LIB, verbose)
-    _link([objs[s] for s in PROBE_SOURCES], PROBE_LIB, verbose)
     return LIB
 
 

@@ -142,6 +142,18 @@ bool dma_offsets_ok(const gemm_problem* p, const dtg::KernelEntry* e) {
     return a < lim && b < lim;
 }
 
+// The skinny kernels address a CK-row chunk of B (and of A's rows) with
+// 32-bit byte offsets from a descriptor rebased at every chunk: row r of the
+// chunk, column c at r * ldb * 2 + c * 2 (A: row i at i * lda * 2 + k * 2).
+// Beyond the descriptor range cap the loads would read zeros, so such strides
+// go to another kernel.
+bool skinny_offsets_ok(const gemm_problem* p, const dtg::KernelEntry* e) {
+    const int64_t lim = (int64_t(1) << 31) - 4096;
+    const int64_t b = static_cast<int64_t>(e->bk) * p->sb_k * 2 + p->N * 2 + 256;
+    const int64_t a = static_cast<int64_t>(e->bm) * p->sa_m * 2 + static_cast<int64_t>(e->bk) * 2 + 256;
+    return a < lim && b < lim;
+}
+
 std::vector<const dtg::KernelEntry*> all_entries() {
     std::vector<const dtg::KernelEntry*> v;
     int n = 0;
@@ -172,6 +184,7 @@ const dtg::KernelEntry* find_entry(const gemm_config& want, int dtype, int vec,
         if (e->layout != -1 && e->layout != lay) continue;
         if (e->lds_bytes > dev.lds_per_wg) continue;
         if (e->family == dtg::KF_DMA && !dma_offsets_ok(p, e)) continue;
+        if (e->family == dtg::KF_SKINNY && !skinny_offsets_ok(p, e)) continue;
         if (matches(e, want)) return e;
     }
     return nullptr;
@@ -404,7 +417,10 @@ gemm_status plan_impl(const gemm_problem* prob, const gemm_device_info* dev, con
         return fail(GEMM_ERR_UNSUPPORTED, "K slices across workgroups support at most %d column slabs or tiles",
                     dtg::kMaxCounters);
     }
+    // a band taller than the grid orders the tiles exactly as a band of the
+    // whole grid: clamping keeps the kernels' band arithmetic in 32 bits
     if (group_m < 1) group_m = 1;
+    if (group_m > pl->num_pid_m) group_m = static_cast<int>(pl->num_pid_m);
     gemm_config& c = pl->cfg;
     c = cfg_of(e->family, e->bm, e->bn, e->bk, e->stages, e->mfma, e->waves_m, e->waves_n);
     c.splitk = splits;
@@ -689,7 +705,8 @@ gemm_status gemm_tile_of_workgroup(int64_t wg, int64_t num_pid_m, int64_t num_pi
     if (num_pid_m <= 0 || num_pid_n <= 0 || group_m <= 0 || xcd_count <= 0)
         return fail(GEMM_ERR_INVALID_ARG, "grid sizes, group_m and xcd_count must be positive");
     if (wg < 0 || wg >= num_pid_m * num_pid_n) return fail(GEMM_ERR_INVALID_ARG, "workgroup outside the grid");
-    dtg::tile_of_workgroup<int64_t>(wg, num_pid_m, num_pid_n, group_m, xcd_count, pid_m, pid_n);
+    const int64_t gm = group_m < num_pid_m ? group_m : num_pid_m;   // as the planners clamp it
+    dtg::tile_of_workgroup<int64_t>(wg, num_pid_m, num_pid_n, gm, xcd_count, pid_m, pid_n);
     return ok();
 }
 

@@ -239,7 +239,9 @@ gemm_status plan_impl(const gemm_mx_problem* prob, const gemm_device_info* dev, 
     c.waves_m = e->waves_m;
     c.waves_n = e->waves_n;
     c.splitk = splits;
-    c.group_m = group_m < 1 ? 1 : group_m;
+    // a band taller than the grid orders the tiles exactly as a band of the
+    // whole grid: clamping keeps the kernels' band arithmetic in 32 bits
+    c.group_m = static_cast<int32_t>(group_m < 1 ? 1 : group_m > pl->num_pid_m ? pl->num_pid_m : group_m);
     c.xcd_remap = (xcd && dev->xcd_count > 1) ? GEMM_XCD_ON : GEMM_XCD_OFF;
     *out = pl;
     return GEMM_OK;

@@ -148,11 +148,8 @@ __device__ __forceinline__ u32x4 lds_read16(uint32_t addr) {
     return v;
 }
 
-// Transposing 64-bit read (ds_read_b64_tr_b16) at addr + OFF: within each
-// 16-lane group the 16 addressed 8-byte pieces, in lane order, form a 4 x 16
-// matrix of halfwords (lanes 4i..4i+3 give row i); lane t receives column t.
-// The same for any non-negative offset: whole multiples of 64 KiB (past the
-// instruction's 16-bit offset field) are added to the address.
+// lds_read16 for any non-negative offset: whole multiples of 64 KiB (past
+// the instruction's 16-bit offset field) are added to the address.
 template <int OFF>
 __device__ __forceinline__ u32x4 lds_read16_any(uint32_t addr) {
     if constexpr (OFF < 65536)
@@ -161,6 +158,9 @@ __device__ __forceinline__ u32x4 lds_read16_any(uint32_t addr) {
         return lds_read16<OFF % 65536>(addr + static_cast<uint32_t>(OFF / 65536) * 65536u);
 }
 
+// Transposing 64-bit read (ds_read_b64_tr_b16) at addr + OFF: within each
+// 16-lane group the 16 addressed 8-byte pieces, in lane order, form a 4 x 16
+// matrix of halfwords (lanes 4i..4i+3 give row i); lane t receives column t.
 template <int OFF>
 __device__ __forceinline__ i16x4 lds_read_tr(uint32_t addr) {
     i16x4 v;
@@ -168,7 +168,6 @@ __device__ __forceinline__ i16x4 lds_read_tr(uint32_t addr) {
     return v;
 }
 
-// 2-byte (zero-extended) and 4-byte reads at addr + OFF.
 // 16-byte global store marked non-temporal (streamed out; an output written
 // once is not worth keeping in the caches): ~0.8 us less for a 32 MB output.
 __device__ __forceinline__ void store16_nt(void* p, uint32_t x, uint32_t y, uint32_t z, uint32_t w) {
@@ -183,6 +182,7 @@ __device__ __forceinline__ void store16_nt(void* p, const f32x4& v) {
     __builtin_nontemporal_store(__builtin_bit_cast(nt_u32x4, v), static_cast<nt_u32x4*>(p));
 }
 
+// 2-byte (zero-extended) and 4-byte reads at addr + OFF.
 template <int OFF>
 __device__ __forceinline__ uint32_t lds_read_u16(uint32_t addr) {
     uint32_t v;
@@ -194,6 +194,27 @@ __device__ __forceinline__ uint32_t lds_read_b32(uint32_t addr) {
     uint32_t v;
     asm volatile("ds_read_b32 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
     return v;
+}
+
+// Arrival of one K slice at its output tile's (or slab's) counter; true on
+// the last arriver.  The partials are written and read with system-coherent
+// accesses (SC0 SC1: stores are written through the per-XCD L2 caches to
+// memory, loads miss them), and every wave waits until its stores are
+// acknowledged before the barrier that precedes the count: when the count
+// reaches `slices`, every partial is in memory, and the last arriver's loads
+// read memory.  The HIP memory model orders such an exchange only with an
+// agent-scope release / acquire pair; on gfx950 the release is an L2
+// write-back, which measured +7.8 us on the 30 us bf16 16 x 8192 x 8192
+// product with one per workgroup (3.3x with one per wave) and changes
+// nothing these accesses see, so the count stays relaxed.  flag is a word of
+// LDS.
+__device__ __forceinline__ bool arrive_last(int* counter, int slices, int* flag) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (threadIdx.x == 0)
+        *flag = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) == slices - 1;
+    __syncthreads();
+    return *flag != 0;
 }
 
 __device__ __forceinline__ void lds_wait_all() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }

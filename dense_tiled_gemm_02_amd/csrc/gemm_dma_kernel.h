@@ -467,7 +467,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(KArgs p) {
     // acc and goes on to the epilogue below; the others are done.  Partials
     // are kept in register order, [tile][slice][wave][block][lane][4 floats],
     // so each lane writes and reads back only its own 16-byte runs, with
-    // system-scope accesses (they bypass the per-XCD L2 caches).
+    // system-coherent accesses (they bypass the per-XCD L2 caches); see
+    // arrive_last for the ordering.
     constexpr int NB = FM * FN * (AccT<MF>::regs / 4);   // 16-byte runs per lane
     // (two slices of partials are held in registers: only tiles of at most
     // 64 accumulators per lane take K slices; the planner keeps the others at 1)
@@ -502,14 +503,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(KArgs p) {
             __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, get_run(b_tag)), pr,
                                                    run_off(slice, decltype(b_tag)::value), 0, kSysScope);
         });
-        wait_vm<0>();
-        __syncthreads();
-        int* last = reinterpret_cast<int*>(smem);
-        if (tid == 0)
-            *last = __hip_atomic_fetch_add(&counters[tile_lin], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) ==
-                    NS - 1;
-        __syncthreads();
-        if (!*last) return;
+        if (!arrive_last(&counters[tile_lin], NS, reinterpret_cast<int*>(smem))) return;
         // Sum the slices in order into acc (this slice's own runs are read back
         // like the others: the same bits).  Loads go in units of HB runs, the
         // next unit in flight while one is added: two units of registers.

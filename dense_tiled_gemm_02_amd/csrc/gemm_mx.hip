@@ -513,14 +513,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mx_kernel(MxArgs p) {
             __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, get_run(b_tag)), pr,
                                                    run_off(slice, decltype(b_tag)::value), 0, kSysScope);
         });
-        wait_vm<0>();
-        __syncthreads();
-        int* last = reinterpret_cast<int*>(smem);
-        if (tid == 0)
-            *last = __hip_atomic_fetch_add(&counters[tile_lin], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) ==
-                    NS - 1;
-        __syncthreads();
-        if (!*last) return;
+        if (!arrive_last(&counters[tile_lin], NS, reinterpret_cast<int*>(smem))) return;
         // slices in order into acc, in units of HB runs, the next unit in
         // flight while one is added (two units of registers)
         constexpr int HB = (NB <= 8) ? NB : NB / 2;

@@ -285,12 +285,9 @@ __global__ __launch_bounds__(64 * NWV) void gemm_skinny_kernel(KArgs p) {
         return;
     }
     // ---- S > 1: partial tile -> workspace; the last workgroup of the slab sums.
-    // The partials are written and read with system-scope accesses, which go
-    // past the (per-XCD, mutually non-coherent) L2 caches to memory; each wave
-    // waits until its writes have completed before the barrier that precedes
-    // the arrival count, so a workgroup that counts itself in has its partial
-    // in memory, and the last arriver reads every partial from memory.  This
-    // avoids writing back or invalidating whole L2 caches.
+    // The partials are written and read with system-scope atomic accesses,
+    // which go past the (per-XCD, mutually non-coherent) L2 caches to memory;
+    // see arrive_last for the ordering.
     int* counters = static_cast<int*>(p.ws);
     float* part = reinterpret_cast<float*>(static_cast<char*>(p.ws) + kCounterBytes) +
                   static_cast<int64_t>(slab) * S * BMR * BN;
@@ -305,13 +302,8 @@ __global__ __launch_bounds__(64 * NWV) void gemm_skinny_kernel(KArgs p) {
         __hip_atomic_store(&part[slice * BMR * BN + t], v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
         red[t] = v;                              // only this thread reads position t
     }
-    wait_vm<0>();
-    __syncthreads();
-    int* last = reinterpret_cast<int*>(red + NWV * BMR * BN);   // just past the partial sums
-    if (tid == 0)
-        *last = __hip_atomic_fetch_add(&counters[slab], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) == S - 1;
-    __syncthreads();
-    if (!*last) return;
+    // just past the partial sums: the arrival flag
+    if (!arrive_last(&counters[slab], S, reinterpret_cast<int*>(red + NWV * BMR * BN))) return;
     // The other slices' partials are loaded in groups of up to 8 slices, all of
     // a thread's outputs at once, then summed in slice order; this
     // workgroup's own partial comes from LDS (bitwise the value it stored).

@@ -23,21 +23,24 @@ __host__ __device__ inline I xcd_permute(I wg, I grid, I xcds) {
 }
 
 // Grouped tile order (FlagGems "Hygon optimization", section "Grouped
-// scheduling: improve L2 data reuse"): the M tiles are cut into bands of
-// group_m tiles (the last band keeps what remains); positions walk down the
-// band's M tiles for one N tile, then move to the next N tile, so consecutive
-// workgroups reuse one K x N panel of B.  group_m = 1 is plain row-major order.
+// scheduling: improve L2 data reuse").  Definition: the M tiles form bands of
+// group_m consecutive rows of tiles (the last band holds what is left); the
+// order visits the bands top to bottom, and inside a band it takes the N tiles
+// left to right, for each one every row of the band top to bottom, so
+// consecutive workgroups share one K x N panel of B.  Position pos lies in
+// band pos / (group_m * num_pid_n) (every band before the last is full);
+// inside it, its offset counts whole columns of the band's height first.
+// group_m = 1 is plain row-major order.
 template <typename I>
 __host__ __device__ inline void grouped_tile(I pos, I num_pid_m, I num_pid_n, I group_m,
                                              I* pid_m, I* pid_n) {
-    const I band_tiles = group_m * num_pid_n;
-    const I band = pos / band_tiles;
-    const I first = band * group_m;
-    const I left = num_pid_m - first;
-    const I rows = left < group_m ? left : group_m;
-    const I within = pos - band * band_tiles;
-    *pid_m = first + within % rows;
-    *pid_n = within / rows;
+    const I full_band = group_m * num_pid_n;          // positions in a band of group_m rows
+    const I band = pos / full_band;
+    const I top = band * group_m;                     // first M tile of the band
+    const I height = (num_pid_m - top < group_m) ? num_pid_m - top : group_m;
+    const I off = pos - band * full_band;             // position inside the band
+    *pid_n = off / height;                            // a column of the band per `height` positions
+    *pid_m = top + off % height;
 }
 
 template <typename I>

@@ -1,0 +1,189 @@
+// Single-instruction probe kernels: test infrastructure, built into
+// tests/gpu_probes/libgemm_probe.so by tests/gpu_probes/build.py (never part
+// of the GEMM library).  They pin the lane layouts the kernels assume.
+//
+// probe_mfma runs ONE matrix instruction in one wavefront with the operand and
+// result lane layouts the tile kernel assumes, on a small A (rows x k) and
+// B (k x cols) given in row-major order, and writes the rows x cols result in
+// row-major order.  A test with exact integer inputs then pins those layouts
+// (the single-instruction kernel of "DCU K100 节点初探", section 5.4, used as a
+// layout check).
+//
+// probe_lds_dma records where the direct global -> LDS loads put each lane's
+// 16 bytes, and that the buffer form writes zeros for offsets past the
+// descriptor's range.
+//
+// probe_lds_read_tr fills 1024 bytes of LDS from `in` and has every lane run one
+// transposing 64-bit LDS read at byte address 8 * lane; the 4 halfwords each
+// lane receives are written to out[4 * lane + 0..3].  It reports the lane
+// mapping of that instruction; every address is inside the 1024 bytes.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <utility>
+
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+template <int MF, bool BF16>
+__global__ __launch_bounds__(64) void probe_mfma_kernel(const uint16_t* A, const uint16_t* B, float* D) {
+    constexpr int KI = (MF == 16) ? 32 : 16;
+    const int l = threadIdx.x;
+    const int rc = l % MF, g = l / MF;
+    uint16_t a[8], b[8];
+    for (int t = 0; t < 8; ++t) {
+        a[t] = A[rc * KI + 8 * g + t];       // A row rc, k = 8g + t
+        b[t] = B[(8 * g + t) * MF + rc];     // B column rc, k = 8g + t
+    }
+    u32x4 av, bv;
+    for (int d = 0; d < 4; ++d) {
+        av[d] = a[2 * d] | (static_cast<uint32_t>(a[2 * d + 1]) << 16);
+        bv[d] = b[2 * d] | (static_cast<uint32_t>(b[2 * d + 1]) << 16);
+    }
+    if constexpr (MF == 16) {
+        f32x4 c = {0, 0, 0, 0};
+        if constexpr (BF16)
+            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av),
+                                                        __builtin_bit_cast(bf16x8, bv), c, 0, 0, 0);
+        else
+            c = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, av),
+                                                       __builtin_bit_cast(f16x8, bv), c, 0, 0, 0);
+        for (int r = 0; r < 4; ++r) D[(4 * g + r) * 16 + rc] = c[r];
+    } else {
+        f32x16 c = {};
+        if constexpr (BF16)
+            c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av),
+                                                        __builtin_bit_cast(bf16x8, bv), c, 0, 0, 0);
+        else
+            c = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, av),
+                                                       __builtin_bit_cast(f16x8, bv), c, 0, 0, 0);
+        for (int r = 0; r < 16; ++r) D[(8 * (r / 4) + 4 * g + (r % 4)) * 32 + rc] = c[r];
+    }
+}
+
+// One scaled matrix instruction (v_mfma_scale_f32_{16x16x128,32x32x64}_f8f6f4)
+// on raw per-lane registers: lane l supplies a[8l..8l+7] and b[8l..8l+7] as
+// its A and B operand registers (only the first 4 dwords are used for the
+// 4-bit format), sa[l] and sb[l] as its scale registers, of which the byte
+// selected by OSA / OSB is the scale; the accumulator starts at zero and
+// lane l's result registers go to out[R l .. R l + R - 1] (R = 4 or 16).
+// Format codes FA / FB: 0 E4M3, 1 E5M2, 4 E2M1.
+template <int MF, int FA, int FB, int OSA, int OSB>
+__global__ __launch_bounds__(64) void probe_mfma_scaled_kernel(const uint32_t* a, const uint32_t* b,
+                                                               const uint32_t* sa, const uint32_t* sb, float* out) {
+    typedef int i32x8 __attribute__((ext_vector_type(8)));
+    const int l = threadIdx.x;
+    i32x8 av, bv;
+    for (int d = 0; d < 8; ++d) {
+        av[d] = static_cast<int>(a[8 * l + d]);
+        bv[d] = static_cast<int>(b[8 * l + d]);
+    }
+    const int s_a = static_cast<int>(sa[l]), s_b = static_cast<int>(sb[l]);
+    if constexpr (MF == 16) {
+        f32x4 c = {0, 0, 0, 0};
+        c = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, FA, FB, OSA, s_a, OSB, s_b);
+        for (int r = 0; r < 4; ++r) out[4 * l + r] = c[r];
+    } else {
+        f32x16 c = {};
+        c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, c, FA, FB, OSA, s_a, OSB, s_b);
+        for (int r = 0; r < 16; ++r) out[16 * l + r] = c[r];
+    }
+}
+
+__global__ __launch_bounds__(64) void probe_lds_read_tr_kernel(const uint16_t* in, uint16_t* out) {
+    __shared__ __attribute__((aligned(16))) uint16_t lds[512];
+    const int l = threadIdx.x;
+    for (int i = l; i < 512; i += 64) lds[i] = in[i];
+    __syncthreads();
+    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+    i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(lds + 4 * l));
+    for (int i = 0; i < 4; ++i) out[4 * l + i] = static_cast<uint16_t>(v[i]);
+}
+
+// 64 lanes, one 16-byte load each, straight into LDS.  LDS halfwords
+// [0, 512): buffer loads through a descriptor covering the first num_records
+// bytes of `in`; lane l < 48 fetches 16-byte chunk (7 l) mod 64, lanes 48..55
+// use offset 0x80000000 and lanes 56..63 offsets num_records + 16 (l - 56),
+// both past num_records (the descriptor's range check must return zeros).
+// LDS halfwords [512, 1024): plain global loads, lane l fetches chunk (5 l)
+// mod 64.  LDS starts filled with 0xFFFF; all of it is copied to out.
+// `in` must hold at least num_records + 128 bytes and num_records >= 1024.
+__global__ __launch_bounds__(64) void probe_lds_dma_kernel(const uint16_t* in, uint16_t* out,
+                                                           int num_records) {
+    __shared__ __attribute__((aligned(16))) uint16_t lds[1024];
+    const int l = threadIdx.x;
+    for (int i = l; i < 1024; i += 64) lds[i] = 0xFFFF;
+    __syncthreads();
+    __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)in, 0, num_records, 0x00020000);
+    const unsigned voff = (l < 48) ? ((l * 7) % 64) * 16
+                        : (l < 56) ? 0x80000000u : static_cast<unsigned>(num_records + 16 * (l - 56));
+    typedef __attribute__((address_space(3))) void lds_void;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voff, 0, 0, 0);
+    __builtin_amdgcn_global_load_lds((const void*)(in + 8 * ((l * 5) % 64)), (lds_void*)(lds + 512), 16, 0, 0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    for (int i = l; i < 1024; i += 64) out[i] = lds[i];
+}
+
+}  // namespace
+
+extern "C" {
+
+// in: >= num_records + 128 bytes, out: 1024 halfwords (device pointers).
+int probe_lds_dma(const uint16_t* in, uint16_t* out, int num_records, void* stream) {
+    if (num_records < 1024) return static_cast<int>(hipErrorInvalidValue);
+    hipLaunchKernelGGL(probe_lds_dma_kernel, dim3(1), dim3(64), 0, static_cast<hipStream_t>(stream), in, out,
+                       num_records);
+    return static_cast<int>(hipGetLastError());
+}
+
+// mf: 16 (A 16x32, B 32x16, D 16x16) or 32 (A 32x16, B 16x32, D 32x32).
+// dtype: 0 fp16, 1 bf16.  All pointers are device pointers.  Returns a
+// hipError_t value (0 = success); the kernel runs on `stream`.
+int probe_mfma(int mf, int dtype, const uint16_t* A, const uint16_t* B, float* D, void* stream) {
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (mf == 16 && dtype == 1) hipLaunchKernelGGL((probe_mfma_kernel<16, true>), dim3(1), dim3(64), 0, s, A, B, D);
+    else if (mf == 16 && dtype == 0) hipLaunchKernelGGL((probe_mfma_kernel<16, false>), dim3(1), dim3(64), 0, s, A, B, D);
+    else if (mf == 32 && dtype == 1) hipLaunchKernelGGL((probe_mfma_kernel<32, true>), dim3(1), dim3(64), 0, s, A, B, D);
+    else if (mf == 32 && dtype == 0) hipLaunchKernelGGL((probe_mfma_kernel<32, false>), dim3(1), dim3(64), 0, s, A, B, D);
+    else return static_cast<int>(hipErrorInvalidValue);
+    return static_cast<int>(hipGetLastError());
+}
+
+// Scaled matrix instruction on raw lane registers (probe_mfma_scaled_kernel).
+// mf 16 or 32; (fa, fb, osa, osb) one of the instantiated combinations below.
+// a, b: 512 dwords; sa, sb: 64 dwords; out: 64 * (mf == 16 ? 4 : 16) floats
+// (device pointers).  Returns a hipError_t value.
+int probe_mfma_scaled(int mf, int fa, int fb, int osa, int osb, const uint32_t* a, const uint32_t* b,
+                      const uint32_t* sa, const uint32_t* sb, float* out, void* stream) {
+    hipStream_t s = static_cast<hipStream_t>(stream);
+#define PROBE_SC(MF_, FA_, FB_, OA_, OB_)                                                                  \
+    if (mf == MF_ && fa == FA_ && fb == FB_ && osa == OA_ && osb == OB_) {                                \
+        hipLaunchKernelGGL((probe_mfma_scaled_kernel<MF_, FA_, FB_, OA_, OB_>), dim3(1), dim3(64), 0, s, a, b, \
+                           sa, sb, out);                                                                   \
+        return static_cast<int>(hipGetLastError());                                                        \
+    }
+#define PROBE_SC_MF(MF_)                                                                     \
+    PROBE_SC(MF_, 0, 0, 0, 0) PROBE_SC(MF_, 1, 1, 0, 0) PROBE_SC(MF_, 4, 4, 0, 0)            \
+    PROBE_SC(MF_, 0, 1, 0, 0) PROBE_SC(MF_, 0, 0, 1, 2) PROBE_SC(MF_, 0, 0, 3, 1)            \
+    PROBE_SC(MF_, 4, 4, 2, 3)
+    PROBE_SC_MF(16)
+    PROBE_SC_MF(32)
+#undef PROBE_SC_MF
+#undef PROBE_SC
+    return static_cast<int>(hipErrorInvalidValue);
+}
+
+// in: 512 halfwords, out: 256 halfwords (device pointers).
+int probe_lds_read_tr(const uint16_t* in, uint16_t* out, void* stream) {
+    hipLaunchKernelGGL(probe_lds_read_tr_kernel, dim3(1), dim3(64), 0, static_cast<hipStream_t>(stream), in, out);
+    return static_cast<int>(hipGetLastError());
+}
+
+}  // extern "C"

@@ -450,3 +450,31 @@ def test_mx_tile_choice_by_rounds_of_workgroups():
     assert cfg(512, 512, 2048) == (64, 64, 3)            # too shallow for slices
     c = mx_plan(512, 512, 16384).config                  # few tiles, deep K: K slices
     assert (c.bm, c.bn, c.splitk) == (128, 128, 16)
+
+
+def test_forced_group_m_is_clamped_to_the_grid():
+    """A forced GROUP_M above the number of M tiles orders the tiles exactly as
+    a band of the whole grid; the planners store the clamped value (the
+    kernels' band arithmetic is 32-bit) and the exported tile order agrees."""
+    huge = 1 << 30
+    p = plan(1024, 1024, 1024, force={"group_m": huge})
+    npm = -(-1024 // p.config.bm)
+    assert p.config.group_m == npm
+    q = mx.gemm_mx_plan_create_for(mx.mx_problem(1024, 1024, 1024, "e4m3"), fake_gfx950(), {"group_m": huge})
+    assert q.config.group_m == -(-1024 // q.config.bm)
+    npm, npn = 5, 7
+    for w in range(npm * npn):
+        assert g.gemm_tile_of_workgroup(w, npm, npn, huge, 8) == g.gemm_tile_of_workgroup(w, npm, npn, npm, 8)
+
+
+def test_skinny_kernel_needs_its_offsets_in_32_bits():
+    """The decode kernels address a chunk of B with 32-bit byte offsets: a row
+    of B wider than ~1 GiB / (chunk rows), or a row stride that large, goes to
+    another kernel instead of reading zeros past the descriptor's range."""
+    assert "gemm_skinny_kernel" in plan(16, 8192, 8192).describe()
+    wide = plan(16, 17_000_000, 64)                    # 64 rows x 34 MB of a chunk > 2 GiB
+    assert "gemm_skinny_kernel" not in wide.describe(), wide.describe()
+    strided = plan(16, 1024, 4096, ldb=1 << 25)        # B row stride of 64 MiB
+    assert "gemm_skinny_kernel" not in strided.describe(), strided.describe()
+    near = plan(16, 1024, 4096, ldb=1 << 20)           # 2 MiB row stride: chunk offsets fit
+    assert "gemm_skinny_kernel" in near.describe(), near.describe()

@@ -17,7 +17,7 @@ import gemm_inputs
 
 pytestmark = pytest.mark.gpu
 
-PROBE = os.path.join(os.path.dirname(g.LIB_PATH), "libgemm_probe.so")
+PROBE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "gpu_probes", "libgemm_probe.so")
 
 
 @pytest.fixture(scope="module")
