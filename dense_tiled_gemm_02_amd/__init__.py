@@ -24,6 +24,7 @@ GEMM_ERR_HIP = 3
 GEMM_ERR_WORKSPACE = 4
 GEMM_XCD_ON = 1
 GEMM_XCD_OFF = 2
+GEMM_STATIC_SCRATCH_BYTES = 24 << 20   # include/gemm.h: the workspace gemm_run_static provides
 KERNEL_TILE = 1
 KERNEL_SKINNY = 2
 
@@ -78,6 +79,7 @@ SIGNATURES = [
     ("gemm_workspace_size", ctypes.c_int, [_p, ctypes.POINTER(ctypes.c_size_t)]),
     ("gemm_workspace_init", ctypes.c_int, [_p, _p, ctypes.c_size_t, _p]),
     ("gemm_run", ctypes.c_int, [_p, _p, _p, _p, _p, _p, ctypes.c_size_t, _p]),
+    ("gemm_run_static", ctypes.c_int, [_p, _p, _p, _p, _p, _p]),
     ("gemm", ctypes.c_int, [_p, _p, _p, _p, _i64, _i64, _i64, ctypes.POINTER(_i64), ctypes.c_int, _i32, _p]),
     ("gemm_cache_clear", None, []),
     ("gemm_lds_bytes", _i64, [_i32, _i32, _i32, _i32, ctypes.c_int]),

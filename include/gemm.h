@@ -194,6 +194,25 @@ gemm_status gemm_workspace_init(const gemm_plan* plan, void* workspace, size_t w
 gemm_status gemm_run(const gemm_plan* plan, const void* A, const void* B, const void* C,
                      void* D, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Largest workspace, in bytes, that gemm_run_static provides (24 MiB). */
+#define GEMM_STATIC_SCRATCH_BYTES (24u * 1024u * 1024u)
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): gemm_run
+ * with the plan's workspace taken from a fixed device array of
+ * GEMM_STATIC_SCRATCH_BYTES that each device the library runs on holds until
+ * the process ends.  Allocates nothing and calls no allocating routine.  A, B,
+ * C, D and stream as for gemm_run; the kernels run on the stream's device.
+ * A plan whose gemm_workspace_size is 0 runs exactly as gemm_run.  The first
+ * call on a device looks the array up (with that device current) and
+ * zero-fills its counter region on `stream`; every launch leaves the counters
+ * at zero again.  GEMM_ERR_WORKSPACE (before any device call) if the plan's
+ * workspace exceeds GEMM_STATIC_SCRATCH_BYTES.  All calls on one device share
+ * the array: calls that overlap in time on one device (several streams or
+ * threads) race, and the caller must serialize them. */
+gemm_status gemm_run_static(const gemm_plan* plan, const void* A, const void* B, const void* C,
+                            void* D, void* stream);
+
 /* One call: plan (cached per problem key and device, thread-safe) and run on
  * the current HIP device.  strides = {sa_m, sa_k, sb_k, sb_n, sc_m, sc_n,
  * sd_m, sd_n}.  Plans needing a workspace are not chosen here. */

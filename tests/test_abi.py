@@ -478,3 +478,22 @@ def test_skinny_kernel_needs_its_offsets_in_32_bits():
     assert "gemm_skinny_kernel" not in strided.describe(), strided.describe()
     near = plan(16, 1024, 4096, ldb=1 << 20)           # 2 MiB row stride: chunk offsets fit
     assert "gemm_skinny_kernel" in near.describe(), near.describe()
+
+
+def test_static_scratch_entry_point_rejects_large_workspaces_before_any_device_call():
+    """gemm_run_static (for callers that cannot allocate) provides at most
+    GEMM_STATIC_SCRATCH_BYTES of workspace; a plan needing more is refused with
+    GEMM_ERR_WORKSPACE and a message naming both sizes, before any device call
+    (so this runs without a GPU)."""
+    hdr = open(os.path.join(ROOT, "include", "gemm.h")).read()
+    m = re.search(r"#define GEMM_STATIC_SCRATCH_BYTES \((\d+)u \* 1024u \* 1024u\)", hdr)
+    assert m and int(m.group(1)) << 20 == g.GEMM_STATIC_SCRATCH_BYTES
+    big = plan(2048, 2048, 65536, force={"kernel": 3, "bm": 128, "bn": 128, "waves_m": 2, "waves_n": 4,
+                                         "stages": 4, "splitk": 16})
+    need = ctypes.c_size_t()
+    assert g.lib().gemm_workspace_size(big.handle, ctypes.byref(need)) == 0
+    assert need.value > g.GEMM_STATIC_SCRATCH_BYTES
+    st = g.lib().gemm_run_static(big.handle, None, None, None, None, None)
+    assert st == g.GEMM_ERR_WORKSPACE
+    msg = g.gemm_last_error()
+    assert str(need.value) in msg and str(g.GEMM_STATIC_SCRATCH_BYTES) in msg, msg
