@@ -275,8 +275,6 @@ def sweep(args):
         # accumulators), deeper rings of 32-deep K steps, and the smaller tiles
         "square_bf16_4096": [dict(kernel=3, bm=256, bn=256, bk=64, stages=2, mfma=mf, waves_m=2, waves_n=wn,
                                   group_m=gm) for wn in (4, 2) for mf in (16, 32) for gm in (1, 4, 8)] +
-                            [dict(kernel=3, bm=256, bn=256, bk=32, stages=st, mfma=32, waves_m=2, waves_n=2,
-                                  group_m=8) for st in (4, 5)] +
                             [dict(kernel=3, bm=256, bn=256, bk=32, stages=4, mfma=16, waves_m=2, waves_n=4,
                                   group_m=8),
                              dict(kernel=3, bm=256, bn=128, bk=64, stages=3, mfma=16, group_m=8),

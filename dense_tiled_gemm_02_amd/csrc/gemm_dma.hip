@@ -21,8 +21,6 @@ const KernelEntry kTable[] = {
     DMA_BOTH(256, 256, 32, 2, 4, 32, 4),
     // one wave per SIMD, 128 x 128 wave tiles, accumulators in AGPRs
     DMA_BOTH(256, 256, 64, 2, 2, 32, 2),
-    DMA_BOTH(256, 256, 32, 2, 2, 32, 4),
-    DMA_BOTH(256, 256, 32, 2, 2, 32, 5),
     DMA_BOTH(256, 256, 64, 2, 2, 16, 2),
 };
 

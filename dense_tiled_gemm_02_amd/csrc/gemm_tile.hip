@@ -283,7 +283,6 @@ hipError_t launch_tile(const KArgs& a, int64_t grid, hipStream_t stream) {
     TILE_ENTRY(BM, BN, BK, WM, WN, MF, ST, 0, VEC), TILE_ENTRY(BM, BN, BK, WM, WN, MF, ST, 1, VEC)
 
 const KernelEntry kTileTable[] = {
-    TILE_BOTH(256, 256, 64, 2, 4, 16, 2, 1),
     TILE_BOTH(256, 256, 64, 2, 4, 32, 2, 1),
     TILE_BOTH(256, 128, 64, 2, 2, 16, 2, 1),
     TILE_BOTH(256, 128, 64, 2, 2, 32, 2, 1),

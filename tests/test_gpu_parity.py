@@ -106,7 +106,7 @@ def test_every_compiled_variant(shape):
 def _variants(dt):
     import ctypes
     seen = []
-    for bm, bn, bk, st, mf, wm, wn in [(256, 256, 64, 2, 16, 2, 4), (256, 256, 64, 2, 32, 2, 4),
+    for bm, bn, bk, st, mf, wm, wn in [(256, 256, 64, 2, 32, 2, 4),
                                        (256, 128, 64, 2, 16, 2, 2), (256, 128, 64, 2, 32, 2, 2),
                                        (128, 256, 64, 2, 16, 2, 2), (128, 128, 64, 2, 16, 2, 2),
                                        (128, 128, 64, 2, 32, 2, 2), (128, 128, 64, 1, 16, 2, 2),
@@ -124,8 +124,7 @@ def _variants(dt):
                                        (128, 256, 64, 3, 16, 2, 4), (64, 64, 64, 4, 16, 2, 2),
                                        (192, 256, 64, 2, 16, 2, 4),
                                        # one wave per SIMD, accumulators in AGPRs
-                                       (256, 256, 64, 2, 32, 2, 2), (256, 256, 32, 4, 32, 2, 2),
-                                       (256, 256, 32, 5, 32, 2, 2), (256, 256, 64, 2, 16, 2, 2)]:
+                                       (256, 256, 64, 2, 32, 2, 2), (256, 256, 64, 2, 16, 2, 2)]:
         seen.append(dict(bm=bm, bn=bn, bk=bk, stages=st, mfma=mf, waves_m=wm, waves_n=wn, kernel=3))
     return seen
 
