@@ -32,8 +32,15 @@ MX operands are numpy uint8 arrays of raw bytes, one row per output row
 the row; fmt is "e4m3", "e5m2" or "e2m1" (two elements per byte, even k in
 the low nibble); scales are uint8 arrays of E8M0 exponents, one per 32 k.
 
-Every function here is pinned by tests/test_oracle.py and
-tests/test_oracle_mx.py against exhaustive library conversions, exact
+Integer operands, arithmetic in oracle_i8.c:
+
+  gemm_i8(A, B, C)                 -> (D, exact)  int8 A (M x K) and B (K x N),
+                                      optional int32 C; exact int64 sums and D,
+                                      their residues modulo 2^32 as int32
+  wrap_i32(x)                      the residue of one int64 modulo 2^32
+
+Every function here is pinned by tests/test_oracle.py, tests/test_oracle_i8.py
+and tests/test_oracle_mx.py against exhaustive library conversions, exact
 rational arithmetic, BLAS in float64 and closed forms (identity, permutation,
 rank-1, integer-valued inputs, single scaled blocks).
 """
@@ -102,6 +109,10 @@ def _load():
     lib.oracle_tol_check_f32.restype = _i64
     lib.oracle_tol_check_f32.argtypes = [_i64, _p, _p, _p, ctypes.POINTER(ctypes.c_double),
                                          ctypes.POINTER(_i64)]
+    lib.oracle_gemm_i8.restype = ctypes.c_int
+    lib.oracle_gemm_i8.argtypes = [_i64, _i64, _i64, _p, _i64, _i64, _p, _i64, _i64, _p, _i64, _i64, _p, _p]
+    lib.oracle_wrap_i32.restype = ctypes.c_int32
+    lib.oracle_wrap_i32.argtypes = [_i64]
     lib.oracle_num_threads.restype = ctypes.c_int
     lib.oracle_num_threads.argtypes = []
     _lib = lib
@@ -399,3 +410,44 @@ def mx_tol_check(got, out, ref, S, S8):
                                     s8.ctypes.data if s8 is not None else None,
                                     ctypes.byref(worst), ctypes.byref(first))
     return int(n), float(worst.value), int(first.value)
+
+
+# ---------------------------------------------------------------- integer operands
+
+
+def _i8(x, name):
+    x = np.asarray(x)
+    if x.dtype != np.int8 or x.ndim != 2:
+        raise TypeError("%s must be a 2-D int8 array" % name)
+    return x
+
+
+def gemm_i8(A, B, C=None):
+    """(D, exact) of D = A x B (+ C): A int8 M x K, B int8 K x N (any element
+    strides: a B stored N x K is passed as its transposed view), C int32 M x N
+    or None.  exact: int64 sums (+ c); D: their residues modulo 2^32 as int32
+    (oracle_i8.c)."""
+    A, B = _i8(A, "A"), _i8(B, "B")
+    M, K = A.shape
+    K2, N = B.shape
+    if K2 != K:
+        raise ValueError("inner dimensions differ")
+    if C is not None:
+        C = np.asarray(C)
+        if C.dtype != np.int32 or C.shape != (M, N):
+            raise TypeError("C must be an int32 M x N array")
+    exact = np.zeros((M, N), np.int64)
+    D = np.zeros((M, N), np.int32)
+    sa, sb = A.strides, B.strides
+    sc = C.strides if C is not None else (0, 0)
+    rc = _load().oracle_gemm_i8(M, N, K, A.ctypes.data, sa[0], sa[1], B.ctypes.data, sb[0], sb[1],
+                                C.ctypes.data if C is not None else None, sc[0] // 4, sc[1] // 4,
+                                exact.ctypes.data, D.ctypes.data)
+    if rc != 0:
+        raise RuntimeError("oracle_gemm_i8 failed (%d)" % rc)
+    return D, exact
+
+
+def wrap_i32(x):
+    """x (a Python or numpy integer) modulo 2^32 as a two's-complement int32."""
+    return int(_load().oracle_wrap_i32(int(x)))

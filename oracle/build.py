@@ -2,7 +2,7 @@
 
     python -m oracle.build        # or: python oracle/build.py
 
-Compiles oracle.c and oracle_mx.c with gcc into oracle/liboracle.so: -O2, no floating-point
+Compiles oracle.c, oracle_mx.c and oracle_i8.c with gcc into oracle/liboracle.so: -O2, no floating-point
 contraction, no fast-math, OpenMP over output rows.
 """
 import os
@@ -10,7 +10,7 @@ import subprocess
 import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-SRCS = [os.path.join(HERE, "oracle.c"), os.path.join(HERE, "oracle_mx.c")]
+SRCS = [os.path.join(HERE, "oracle.c"), os.path.join(HERE, "oracle_mx.c"), os.path.join(HERE, "oracle_i8.c")]
 LIB = os.path.join(HERE, "liboracle.so")
 
 
