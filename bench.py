@@ -106,6 +106,8 @@ def parse():
                     help="block-scaled (MX) workloads: FP8 / FP4 elements with E8M0 scales per 32 k")
     ap.add_argument("--configs", action="store_true",
                     help="every named workload against torch.matmul, batches of 10 launches captured in a HIP graph")
+    ap.add_argument("--i8", action="store_true",
+                    help="int8 workloads (int8 operands, int32 output) against the dense int8 peak")
     ap.add_argument("--mx-sweep", action="store_true",
                     help="block-scaled tile / slice variants of the decode and square workloads, interleaved")
     ap.add_argument("--rounds", type=int, default=30)
@@ -664,6 +666,70 @@ def mx_sweep(args):
         del Bs
 
 
+PEAK_I8_TOPS = 5000.0   # MI355X dense int8 matrix peak (2:1 sparsity excluded)
+
+
+def i8(args):
+    """int8 workloads (int8 A and B stored N x K, int32 D): the planner's plan
+    and the 32 x 32 x 32 instruction at the same tile, timed in interleaved
+    rounds of >= 1 ms batches (median, spread), against the dense int8 peak.
+    One JSON line per workload and variant."""
+    import torch
+    import gemm_inputs
+    import dense_tiled_gemm_02_amd as g
+    rows = []
+    for name, w in gemm_inputs.I8_WORKLOADS.items():
+        A, Bt, C = gemm_inputs.make_i8(w)
+        dA, dBt = torch.from_numpy(A).cuda(), torch.from_numpy(Bt).cuda()
+        dC = torch.from_numpy(C).cuda() if C is not None else None
+        D = torch.empty((w.M, w.N), dtype=torch.int32, device="cuda")
+        stream = torch.cuda.current_stream().cuda_stream
+        variants = [None]
+        base = g.plan_for(dA, dBt.t(), dC, D).config
+        if base.mfma == 16:
+            variants.append(dict(kernel=3, bm=base.bm, bn=base.bn, bk=base.bk, waves_m=base.waves_m,
+                                 waves_n=base.waves_n, stages=base.stages, mfma=32))
+        ls = []
+        for v in variants:
+            try:
+                pl = g.plan_for(dA, dBt.t(), dC, D, v)
+            except g.GemmError:
+                continue
+            run = g.lib().gemm_run
+
+            def launch(n, pl=pl):
+                for _ in range(n):
+                    st = run(pl.handle, dA.data_ptr(), dBt.data_ptr(), dC.data_ptr() if dC is not None else None,
+                             D.data_ptr(), None, 0, stream)
+                    if st != 0:
+                        raise g.GemmError(st, g.gemm_last_error())
+            launch(3)
+            ls.append((v, launch, pl))
+        torch.cuda.synchronize()
+        batch = batch_len(ls[0][1])
+        times = {i: [] for i in range(len(ls))}
+        rng = random.Random(7)
+        for _ in range(args.rounds):
+            order = list(range(len(ls)))
+            rng.shuffle(order)
+            for i in order:
+                times[i].extend(batch_times(ls[i][1], batch, 1))
+        for i, (v, _, pl) in enumerate(ls):
+            st = stats(times[i])
+            tops = w.flops() / st["median_ms"] / 1e9
+            rec = {"workload": name, **w.describe(), "variant": v, "plan": pl.describe(), "us": st["median_ms"] * 1e3,
+                   "spread": st["spread"], "batch_launches": batch,
+                   "roofline": {"bound": "mfma", "achieved": round(tops, 1), "peak": PEAK_I8_TOPS, "unit": "TOP/s",
+                                "frac": tops / PEAK_I8_TOPS},
+                   "gbs": w.bytes() / st["median_ms"] / 1e6}
+            rows.append(rec)
+            print(json.dumps(rec), flush=True)
+        del dA, dBt, dC, D
+    if args.save:
+        save_rows(args.save, rows, "int8 workloads: planner plan and the other instruction shape, %d interleaved "
+                                   "rounds" % args.rounds)
+
+
 def copy_calibration(mb):
     """One device copy of `mb` MiB, the reference kernel of the memory counters."""
     import torch
@@ -704,6 +770,9 @@ def main():
         return
     if args.mx_sweep:
         mx_sweep(args)
+        return
+    if args.i8:
+        i8(args)
         return
     w = gemm_inputs.WORKLOADS[args.workload]
     case = Case(w, rotate=4 if w.name.startswith("skinny") else 1)

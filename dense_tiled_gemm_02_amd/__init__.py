@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libgemm.so")
 
 GEMM_F16 = 0
 GEMM_BF16 = 1
+GEMM_I8 = 2     # int8 A and B (k contiguous), int32 C and D
 GEMM_OK = 0
 GEMM_ERR_INVALID_ARG = 1
 GEMM_ERR_UNSUPPORTED = 2
@@ -267,7 +268,15 @@ def _dtype_code(t):
         return GEMM_F16
     if t.dtype == torch.bfloat16:
         return GEMM_BF16
-    raise TypeError("only float16 and bfloat16 tensors are supported, got %s" % t.dtype)
+    if t.dtype == torch.int8:
+        return GEMM_I8
+    raise TypeError("only float16, bfloat16 and int8 operands are supported, got %s" % t.dtype)
+
+
+def out_dtype(t):
+    """The dtype of C and D for operands of t's dtype (int32 for int8 operands)."""
+    import torch
+    return torch.int32 if t.dtype == torch.int8 else t.dtype
 
 
 def problem_for(A, B, C=None, D=None):
@@ -279,9 +288,10 @@ def problem_for(A, B, C=None, D=None):
     if K2 != K:
         raise ValueError("inner dimensions differ: %s x %s" % (tuple(A.shape), tuple(B.shape)))
     dt = _dtype_code(A)
-    for name, t in (("B", B), ("C", C), ("D", D)):
-        if t is not None and t.dtype != A.dtype:
-            raise TypeError("%s has dtype %s, A has %s" % (name, t.dtype, A.dtype))
+    od = out_dtype(A)
+    for name, t, want in (("B", B, A.dtype), ("C", C, od), ("D", D, od)):
+        if t is not None and t.dtype != want:
+            raise TypeError("%s has dtype %s, expected %s for %s operands" % (name, t.dtype, want, A.dtype))
     for name, t in (("C", C), ("D", D)):
         if t is not None and tuple(t.shape) != (M, N):
             raise ValueError("%s must be %dx%d" % (name, M, N))
@@ -337,7 +347,9 @@ def plan_for(A, B, C=None, D=None, config=None):
 def matmul(A, B, C=None, out=None, config=None, stream=None):
     """D = A x B (+ C) on the GPU through libgemm.so; returns D (torch tensor).
 
-    A, B, C, out: CUDA (HIP) torch tensors of one dtype (float16 / bfloat16).
+    A, B, C, out: CUDA (HIP) torch tensors of one dtype (float16 / bfloat16),
+    or int8 A and B with int32 C and out (B k-contiguous: the transposed view
+    of an N x K tensor).
     config: optional dict of gemm_config fields to force.  The call is
     asynchronous on `stream` (default: torch's current stream)."""
     import torch
@@ -345,7 +357,7 @@ def matmul(A, B, C=None, out=None, config=None, stream=None):
         if t is not None and not t.is_cuda:
             raise ValueError("%s must be a GPU tensor" % name)
     if out is None:
-        out = torch.empty((A.shape[0], B.shape[1]), dtype=A.dtype, device=A.device)
+        out = torch.empty((A.shape[0], B.shape[1]), dtype=out_dtype(A), device=A.device)
     pl = plan_for(A, B, C, out, config)
     if stream is None:
         stream = torch.cuda.current_stream(A.device).cuda_stream

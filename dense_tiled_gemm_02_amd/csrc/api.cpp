@@ -31,6 +31,7 @@
 
 struct gemm_plan {
     gemm_problem prob;
+    gemm_problem view;                  // the problem in the kernels' units (int8: pairs of k)
     gemm_device_info dev;
     gemm_config cfg;
     const dtg::KernelEntry* entry;      // the chosen variant
@@ -71,8 +72,8 @@ gemm_status validate(const gemm_problem* p) {
     if (p->M < 0 || p->N < 0 || p->K < 0)
         return fail(GEMM_ERR_INVALID_ARG, "negative size M=%lld N=%lld K=%lld", (long long)p->M,
                     (long long)p->N, (long long)p->K);
-    if (p->dtype != GEMM_F16 && p->dtype != GEMM_BF16)
-        return fail(GEMM_ERR_INVALID_ARG, "dtype %d is neither GEMM_F16 nor GEMM_BF16", (int)p->dtype);
+    if (p->dtype != GEMM_F16 && p->dtype != GEMM_BF16 && p->dtype != GEMM_I8)
+        return fail(GEMM_ERR_INVALID_ARG, "dtype %d is none of GEMM_F16, GEMM_BF16, GEMM_I8", (int)p->dtype);
     if (p->has_c != 0 && p->has_c != 1)
         return fail(GEMM_ERR_INVALID_ARG, "has_c must be 0 or 1, got %d", (int)p->has_c);
     if (p->M > kMaxDim || p->N > kMaxDim || p->K > kMaxDim)
@@ -113,10 +114,38 @@ int layout_of(const gemm_problem* p) {
     return (a_cm ? dtg::kLayTA : 0) | (b_cm ? dtg::kLayTB : 0);
 }
 
+// The operand layout the kernels take a problem in: int8 operands are always
+// A row-major and B stored N x K (k contiguous), also when a single row or
+// column would read as either.
+int kernel_layout(const gemm_problem* p) { return p->dtype == GEMM_I8 ? dtg::kLayTB : layout_of(p); }
+
+// The problem in the units the tile kernels address: for GEMM_I8 one unit is
+// a pair of int8 along k (K and the leading strides of A and B halved; C and
+// D keep their int32 strides); otherwise the problem itself.
+// GEMM_ERR_UNSUPPORTED for int8 operands the kernels cannot take.
+gemm_status kernel_view(const gemm_problem* p, gemm_problem* v) {
+    *v = *p;
+    if (p->dtype != GEMM_I8 || p->K == 0) return GEMM_OK;
+    const bool a_ok = (p->K <= 1 || p->sa_k == 1) && (p->M <= 1 || p->sa_m % 16 == 0);
+    const bool b_ok = (p->K <= 1 || p->sb_k == 1) && (p->N <= 1 || p->sb_n % 16 == 0);
+    if (p->K % 16 != 0 || !a_ok || !b_ok)
+        return fail(GEMM_ERR_UNSUPPORTED,
+                    "int8 operands must have k contiguous (A row-major, B stored N x K), K and their leading "
+                    "strides multiples of 16 (K=%lld, A strides %lld,%lld, B strides %lld,%lld)",
+                    (long long)p->K, (long long)p->sa_m, (long long)p->sa_k, (long long)p->sb_k,
+                    (long long)p->sb_n);
+    v->K = p->K / 2;
+    v->sa_k = 1;
+    v->sa_m = p->M > 1 ? p->sa_m / 2 : v->K;
+    v->sb_k = 1;
+    v->sb_n = p->N > 1 ? p->sb_n / 2 : v->K;
+    return GEMM_OK;
+}
+
 // The 16-byte vector paths move 8 elements along each operand's contiguous
 // index: that index's extent and the other stride must be multiples of 8.
 bool vec_shape_ok(const gemm_problem* p) {
-    const int lay = layout_of(p);
+    const int lay = kernel_layout(p);
     if (lay < 0) return false;
     const bool a_ok = (lay & dtg::kLayTA) ? (p->M % 8 == 0 && p->sa_k % 8 == 0)
                                           : (p->K % 8 == 0 && p->sa_m % 8 == 0);
@@ -161,6 +190,8 @@ std::vector<const dtg::KernelEntry*> all_entries() {
     for (int i = 0; i < n; ++i) v.push_back(&t[i]);
     t = dtg::dma_kernel_table(&n);
     for (int i = 0; i < n; ++i) v.push_back(&t[i]);
+    t = dtg::i8_kernel_table(&n);
+    for (int i = 0; i < n; ++i) v.push_back(&t[i]);
     t = dtg::skinny_kernel_table(&n);
     for (int i = 0; i < n; ++i) v.push_back(&t[i]);
     return v;
@@ -178,7 +209,7 @@ bool matches(const dtg::KernelEntry* e, const gemm_config& f) {
 // and matches `want`.
 const dtg::KernelEntry* find_entry(const gemm_config& want, int dtype, int vec,
                                    const gemm_device_info& dev, const gemm_problem* p) {
-    const int lay = layout_of(p);
+    const int lay = kernel_layout(p);
     for (const dtg::KernelEntry* e : all_entries()) {
         if (e->dtype != dtype || e->vec != vec) continue;
         if (e->layout != -1 && e->layout != lay) continue;
@@ -218,7 +249,7 @@ const std::vector<TunedKey>& tuned_table() {
 gemm_config heuristic(const gemm_problem* p, const gemm_device_info& dev, int* group_m, bool allow_ws) {
     const int64_t M = p->M, N = p->N, K = p->K;
     *group_m = 8;
-    if (M <= 32 && layout_of(p) == 0) {
+    if (M <= 32 && kernel_layout(p) == 0) {
         // Decode regime, bucketed by M: 16-row slabs for M <= 16, 32-row slabs
         // (two MFMA row blocks) for M <= 32.  Stream B.  Each workgroup reads
         // a 256-byte band of every row of its K slice (HBM needs >= 128-byte
@@ -274,7 +305,7 @@ gemm_config heuristic(const gemm_problem* p, const gemm_device_info& dev, int* g
         {dtg::KF_DMA, 64, 64, 64, 4, 16, 2, 2, 2, 0.27, false},
         {dtg::KF_DMA, 192, 256, 64, 2, 16, 2, 4, 1, 0.85, true},
     };
-    const bool row_major_vec = layout_of(p) == 0 && vec_shape_ok(p);
+    const bool row_major_vec = kernel_layout(p) == 0 && vec_shape_ok(p);
     const C* best = nullptr;
     double best_t = 0.0;
     for (const C& c : ladder) {
@@ -305,7 +336,7 @@ gemm_config heuristic(const gemm_problem* p, const gemm_device_info& dev, int* g
     const C& split = ladder[3];
     const int64_t tiles = cdiv(M, split.bm) * cdiv(N, split.bn);
     const int64_t nkt = cdiv(K, split.bk);
-    if (allow_ws && tiles <= dtg::kMaxCounters) {
+    if (allow_ws && tiles <= dtg::kMaxCounters && p->dtype != GEMM_I8) {   // int8: no K slices
         int64_t s = dev.cu_count / tiles;
         if (s > nkt / 16) s = nkt / 16;
         if (s > 16) s = 16;
@@ -319,12 +350,16 @@ gemm_config heuristic(const gemm_problem* p, const gemm_device_info& dev, int* g
     return cfg_of(best->fam, best->bm, best->bn, best->bk, best->st, best->mf, best->wm, best->wn);
 }
 
-gemm_status plan_impl(const gemm_problem* prob, const gemm_device_info* dev, const gemm_config* force,
+gemm_status plan_impl(const gemm_problem* given, const gemm_device_info* dev, const gemm_config* force,
                       gemm_plan** out, bool allow_ws = true) {
     if (!out) return fail(GEMM_ERR_INVALID_ARG, "out is NULL");
     *out = nullptr;
-    gemm_status st = validate(prob);
+    gemm_status st = validate(given);
     if (st != GEMM_OK) return st;
+    gemm_problem view;
+    st = kernel_view(given, &view);
+    if (st != GEMM_OK) return st;
+    const gemm_problem* prob = &view;   // everything below plans in the kernels' units
     if (!dev) return fail(GEMM_ERR_INVALID_ARG, "device info is NULL");
     if (dev->cu_count <= 0 || dev->lds_per_wg <= 0)
         return fail(GEMM_ERR_INVALID_ARG, "device info has no CUs or no LDS");
@@ -401,7 +436,8 @@ gemm_status plan_impl(const gemm_problem* prob, const gemm_device_info* dev, con
     }
     gemm_plan* pl = new (std::nothrow) gemm_plan;
     if (!pl) return fail(GEMM_ERR_INVALID_ARG, "out of host memory");
-    pl->prob = *prob;
+    pl->prob = *given;
+    pl->view = view;
     pl->dev = *dev;
     pl->entry = e;
     pl->fallback = fb;
@@ -429,8 +465,8 @@ gemm_status plan_impl(const gemm_problem* prob, const gemm_device_info* dev, con
     if (log_enabled()) {
         char buf[512];
         gemm_plan_describe(pl, buf, sizeof buf);
-        fprintf(stderr, "[gemm] M=%lld N=%lld K=%lld dtype=%d has_c=%d: %s%s\n", (long long)prob->M,
-                (long long)prob->N, (long long)prob->K, (int)prob->dtype, (int)prob->has_c, buf,
+        fprintf(stderr, "[gemm] M=%lld N=%lld K=%lld dtype=%d has_c=%d: %s%s\n", (long long)given->M,
+                (long long)given->N, (long long)given->K, (int)given->dtype, (int)given->has_c, buf,
                 tuned ? " (tuned)" : "");
     }
     *out = pl;
@@ -452,10 +488,12 @@ gemm_status device_info_cached(int device, gemm_device_info* info) {
     return st;
 }
 
-// byte range [lo, hi) of a rows x cols matrix with strides (rs, cs)
-void span(const void* p, int64_t rows, int64_t cols, int64_t rs, int64_t cs, uintptr_t* lo, uintptr_t* hi) {
+// byte range [lo, hi) of a rows x cols matrix of elem-byte elements with
+// strides (rs, cs) in elements
+void span(const void* p, int64_t rows, int64_t cols, int64_t rs, int64_t cs, int64_t elem, uintptr_t* lo,
+          uintptr_t* hi) {
     *lo = reinterpret_cast<uintptr_t>(p);
-    *hi = *lo + static_cast<uintptr_t>(((rows - 1) * rs + (cols - 1) * cs + 1) * 2);
+    *hi = *lo + static_cast<uintptr_t>(((rows - 1) * rs + (cols - 1) * cs + 1) * elem);
 }
 
 bool overlaps(uintptr_t a0, uintptr_t a1, uintptr_t b0, uintptr_t b1) { return a0 < b1 && b0 < a1; }
@@ -565,7 +603,7 @@ gemm_status gemm_plan_describe(const gemm_plan* plan, char* buf, size_t len) {
              "grid=%lld threads=%d lds=%lld vec=%d layout=%d",
              plan->entry->name, c.bm, c.bn, c.bk, c.stages, c.mfma, c.waves_m, c.waves_n, c.group_m,
              c.splitk, c.xcd_remap, (long long)plan->grid, plan->entry->threads,
-             (long long)plan->entry->lds_bytes, plan->entry->vec, layout_of(&plan->prob));
+             (long long)plan->entry->lds_bytes, plan->entry->vec, kernel_layout(&plan->view));
     return ok();
 }
 
@@ -595,18 +633,20 @@ gemm_status gemm_run(const gemm_plan* plan, const void* A, const void* B, const 
     if (p.M == 0 || p.N == 0) return ok();
     if (!D) return fail(GEMM_ERR_INVALID_ARG, "D is NULL");
     if (p.K > 0 && (!A || !B)) return fail(GEMM_ERR_INVALID_ARG, "A or B is NULL");
+    const bool i8 = p.dtype == GEMM_I8;
+    const int64_t eab = i8 ? 1 : 2, ecd = i8 ? 4 : 2;   // element bytes of A, B and of C, D
     uintptr_t d0, d1;
-    span(D, p.M, p.N, p.sd_m, p.sd_n, &d0, &d1);
+    span(D, p.M, p.N, p.sd_m, p.sd_n, ecd, &d0, &d1);
     if (p.K > 0) {
         uintptr_t a0, a1, b0, b1;
-        span(A, p.M, p.K, p.sa_m, p.sa_k, &a0, &a1);
-        span(B, p.K, p.N, p.sb_k, p.sb_n, &b0, &b1);
+        span(A, p.M, p.K, p.sa_m, p.sa_k, eab, &a0, &a1);
+        span(B, p.K, p.N, p.sb_k, p.sb_n, eab, &b0, &b1);
         if (overlaps(d0, d1, a0, a1)) return fail(GEMM_ERR_INVALID_ARG, "D overlaps A");
         if (overlaps(d0, d1, b0, b1)) return fail(GEMM_ERR_INVALID_ARG, "D overlaps B");
     }
     if (p.has_c) {
         uintptr_t c0, c1;
-        span(C, p.M, p.N, p.sc_m, p.sc_n, &c0, &c1);
+        span(C, p.M, p.N, p.sc_m, p.sc_n, ecd, &c0, &c1);
         const bool same = (C == D) && (p.sc_m == p.sd_m || p.M == 1);
         if (!same && overlaps(d0, d1, c0, c1))
             return fail(GEMM_ERR_INVALID_ARG, "D overlaps C (only D == C with equal strides is allowed)");
@@ -619,8 +659,12 @@ gemm_status gemm_run(const gemm_plan* plan, const void* A, const void* B, const 
     if (needs_ws && (reinterpret_cast<uintptr_t>(workspace) & 255))
         return fail(GEMM_ERR_WORKSPACE, "workspace must be 256-byte aligned");
     if (e->vec && p.K > 0 &&
-        ((reinterpret_cast<uintptr_t>(A) & 15) || (reinterpret_cast<uintptr_t>(B) & 15)))
+        ((reinterpret_cast<uintptr_t>(A) & 15) || (reinterpret_cast<uintptr_t>(B) & 15))) {
+        if (!plan->fallback)
+            return fail(GEMM_ERR_UNSUPPORTED, "int8 operands must be 16-byte aligned (no element-wise int8 path)");
         e = plan->fallback;   // element-wise loads; bitwise identical for 16x16x32 plans
+    }
+    const gemm_problem& v = plan->view;   // A, B and K in the kernels' units
     dtg::KArgs a;
     a.A = static_cast<const uint16_t*>(A);
     a.B = static_cast<const uint16_t*>(B);
@@ -628,18 +672,18 @@ gemm_status gemm_run(const gemm_plan* plan, const void* A, const void* B, const 
     a.D = static_cast<uint16_t*>(D);
     a.M = static_cast<int32_t>(p.M);
     a.N = static_cast<int32_t>(p.N);
-    a.K = static_cast<int32_t>(p.K);
+    a.K = static_cast<int32_t>(v.K);
     a.num_pid_m = static_cast<int32_t>((p.M + e->bm - 1) / e->bm);
     a.num_pid_n = static_cast<int32_t>((p.N + e->bn - 1) / e->bn);
     a.group_m = plan->cfg.group_m;
     a.xcds = (plan->cfg.xcd_remap == GEMM_XCD_ON) ? plan->dev.xcd_count : 1;
     a.has_c = p.has_c;
-    a.lda = p.sa_m;
-    a.ldb = p.sb_k;
+    a.lda = v.sa_m;
+    a.ldb = v.sb_k;
     a.ldc = p.has_c ? p.sc_m : 0;
     a.ldd = p.sd_m;
-    a.sak = p.sa_k;
-    a.sbn = p.sb_n;
+    a.sak = v.sa_k;
+    a.sbn = v.sb_n;
     a.splits = (e == plan->entry && (e->family == dtg::KF_SKINNY || e->family == dtg::KF_DMA))
                    ? plan->cfg.splitk
                    : 1;   // the element-wise fallback runs the whole K range per tile
@@ -695,8 +739,8 @@ void gemm_cache_clear(void) {
 
 int64_t gemm_lds_bytes(int32_t bm, int32_t bn, int32_t bk, int32_t stages, gemm_dtype dtype) {
     if (bm <= 0 || bn <= 0 || bk <= 0 || stages <= 0) return -1;
-    if (dtype != GEMM_F16 && dtype != GEMM_BF16) return -1;
-    return static_cast<int64_t>(stages) * (bm + bn) * bk * 2;
+    if (dtype != GEMM_F16 && dtype != GEMM_BF16 && dtype != GEMM_I8) return -1;
+    return static_cast<int64_t>(stages) * (bm + bn) * bk * (dtype == GEMM_I8 ? 1 : 2);
 }
 
 gemm_status gemm_tile_of_workgroup(int64_t wg, int64_t num_pid_m, int64_t num_pid_n, int32_t group_m,

@@ -46,6 +46,24 @@ __device__ __forceinline__ typename AccT<MF>::type mfma(u32x4 a, u32x4 b,
     }
 }
 
+// acc += a x b on 8-bit integers (each 16-byte operand register set holds 16
+// consecutive k): v_mfma_i32_16x16x64_i8 / 32x32x32_i8, int32 accumulation
+// that wraps modulo 2^32.  The accumulator is carried in float vectors as
+// raw bits, like the floating-point tiles' (zero bits are integer zero).
+template <int MF>
+__device__ __forceinline__ typename AccT<MF>::type mfma_i8(u32x4 a, u32x4 b, typename AccT<MF>::type c) {
+    typedef int i32x4 __attribute__((ext_vector_type(4)));
+    typedef int i32x16 __attribute__((ext_vector_type(16)));
+    if constexpr (MF == 16)
+        return __builtin_bit_cast(f32x4, __builtin_amdgcn_mfma_i32_16x16x64_i8(
+                                             __builtin_bit_cast(i32x4, a), __builtin_bit_cast(i32x4, b),
+                                             __builtin_bit_cast(i32x4, c), 0, 0, 0));
+    else
+        return __builtin_bit_cast(f32x16, __builtin_amdgcn_mfma_i32_32x32x32_i8(
+                                              __builtin_bit_cast(i32x4, a), __builtin_bit_cast(i32x4, b),
+                                              __builtin_bit_cast(i32x16, c), 0, 0, 0));
+}
+
 // The same contraction with the accumulator held in AGPRs ("+a"), for tiles
 // whose accumulators fill the whole AGPR file (256 per lane at one wave per
 // SIMD): left to itself the register allocator splits such an accumulator

@@ -81,8 +81,17 @@ struct OpShape {
     }
 };
 
-template <int BM, int BN, int BK, int WM, int WN, int MF, int ST, bool BF16, bool TA, bool TB>
-__global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(KArgs p) {
+// Element kinds of the tile body: 16-bit floating point (fp16, bf16) with fp32
+// accumulation and a 16-bit output, or 8-bit integers with int32 accumulation
+// and output.  The int8 operands are staged and read as pairs of bytes (one
+// 16-bit element holds two consecutive k), so the K loop is the same code;
+// K, BK and the strides are in those 16-bit units.
+enum { kElF16 = 0, kElBF16 = 1, kElI8 = 2 };
+
+template <int BM, int BN, int BK, int WM, int WN, int MF, int ST, int EL, bool TA, bool TB>
+__device__ __forceinline__ void dma_tile(const KArgs& p) {
+    constexpr bool BF16 = EL == kElBF16;
+    constexpr bool I8 = EL == kElI8;
     constexpr int NW = WM * WN;
     constexpr int TM = BM / WM, TN = BN / WN;
     constexpr int FM = TM / MF, FN = TN / MF;
@@ -101,6 +110,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(KArgs p) {
     // accumulators per lane; above 128 (one wave per SIMD holding a
     // 128 x 128 wave tile) they live in AGPRs, placed there explicitly
     constexpr bool AGPR = FM * FN * AccT<MF>::regs > 128;
+    static_assert(!(I8 && AGPR), "int8 tiles keep their accumulators in VGPRs");
 
     __shared__ __attribute__((aligned(1024))) uint16_t smem[ST * (SA + SB)];
 
@@ -343,7 +353,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(KArgs p) {
         constexpr int SL = decltype(slot_tag)::value;
         constexpr int Q = decltype(q_tag)::value;
         constexpr int I = Q / FN, J = Q % FN;
-        if constexpr (AGPR) mfma_agpr<MF, BF16>(acc[I][J], fb[SL][J], fa[SL][I]);
+        if constexpr (I8) acc[I][J] = mfma_i8<MF>(fb[SL][J], fa[SL][I], acc[I][J]);
+        else if constexpr (AGPR) mfma_agpr<MF, BF16>(acc[I][J], fb[SL][J], fa[SL][I]);
         else acc[I][J] = mfma<MF, BF16>(fb[SL][J], fa[SL][I], acc[I][J]);
     };
     // accumulator element (i, j, r) in a VGPR, for the reduce and the epilogue
@@ -473,7 +484,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(KArgs p) {
     // (two slices of partials are held in registers: only tiles of at most
     // 64 accumulators per lane take K slices; the planner keeps the others at 1)
     static_assert(NB > 16 || !AGPR, "K slices keep their partials in VGPRs");
-    if constexpr (NB <= 16) if (NS > 1) {
+    if constexpr (NB <= 16 && !I8) if (NS > 1) {
         constexpr int64_t WAVE_F = static_cast<int64_t>(NB) * 64 * 4;   // floats per wave per slice
         int* counters = static_cast<int*>(p.ws);
         float* tile_part = reinterpret_cast<float*>(static_cast<char*>(p.ws) + kCounterBytes) +
@@ -547,6 +558,68 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(KArgs p) {
     // and G runs of 4 consecutive columns (16x16x32: columns 4 (l / 16) +
     // 0..3; 32x32x16: run q at columns 8 q + 4 (l / 32) + 0..3).
     constexpr int G = AccT<MF>::regs / 4;
+
+    if constexpr (I8) {
+        // int32 results: the tile is staged through LDS in P8 passes of BM / P8
+        // rows (16-byte chunks of 4 values at chunk position c ^ (r mod 16) of
+        // their row), then each thread adds C to a 4-value row chunk and
+        // writes it as one 16-byte store.  Integer sums wrap modulo 2^32, as
+        // the instruction's accumulator does.
+        constexpr int LDSB = ST * (SA + SB) * 2;
+        constexpr int P8 = (BM * BN * 4 <= LDSB)                       ? 1
+                           : (WM % 2 == 0 && BM * BN * 2 <= LDSB)     ? 2
+                           : (WM % 4 == 0 && BM * BN <= LDSB)         ? 4
+                                                                      : 0;
+        static_assert(P8 > 0, "the int32 tile must fit the LDS in at most 4 passes");
+        constexpr int PR = BM / P8, WPP = WM / P8, C4 = BN / 4, NT = 64 * NW;
+        static_assert((PR * C4) % NT == 0 && C4 >= 16, "whole rounds of 4-value chunks");
+        typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+        uint8_t* const stage = reinterpret_cast<uint8_t*>(smem);
+        uint32_t* const D32 = reinterpret_cast<uint32_t*>(p.D);
+        const uint32_t* const C32 = reinterpret_cast<const uint32_t*>(p.C);
+        const bool has_c = p.has_c != 0;
+        const bool vec4 = (p.ldd % 4 == 0) && (reinterpret_cast<uintptr_t>(p.D) % 16 == 0) &&
+                          (!has_c || ((p.ldc % 4 == 0) && (reinterpret_cast<uintptr_t>(p.C) % 16 == 0)));
+#pragma unroll
+        for (int pass = 0; pass < P8; ++pass) {
+            __syncthreads();   // operand reads (first pass) or the previous pass's reads are done
+            if (wm / WPP == pass) {
+#pragma unroll
+                for (int i = 0; i < FM; ++i)
+#pragma unroll
+                    for (int j = 0; j < FN; ++j)
+#pragma unroll
+                        for (int q = 0; q < G; ++q) {
+                            const int row = (wm % WPP) * TM + i * MF + (lane % MF);
+                            const int col = wn * TN + j * MF + 8 * q + 4 * (lane / MF);
+                            const v4u v = {__float_as_uint(acc[i][j][4 * q]), __float_as_uint(acc[i][j][4 * q + 1]),
+                                           __float_as_uint(acc[i][j][4 * q + 2]),
+                                           __float_as_uint(acc[i][j][4 * q + 3])};
+                            *reinterpret_cast<v4u*>(stage + row * (BN * 4) + ((col / 4) ^ (row % 16)) * 16) = v;
+                        }
+            }
+            __syncthreads();
+#pragma unroll
+            for (int x0 = 0; x0 < PR * C4; x0 += NT) {
+                const int x = x0 + tid;
+                const int row = x / C4, c4 = x % C4;
+                const int gr = m0 + pass * PR + row, gc = n0 + c4 * 4;
+                if (gr < M && gc < N) {
+                    v4u v = *reinterpret_cast<const v4u*>(stage + row * (BN * 4) + (c4 ^ (row % 16)) * 16);
+                    uint32_t* d = D32 + static_cast<int64_t>(gr) * p.ldd + gc;
+                    const uint32_t* c = has_c ? C32 + static_cast<int64_t>(gr) * p.ldc + gc : nullptr;
+                    if (vec4 && gc + 4 <= N) {
+                        if (has_c) v += *reinterpret_cast<const v4u*>(c);
+                        typedef unsigned int nt_u32x4 __attribute__((ext_vector_type(4)));
+                        __builtin_nontemporal_store(__builtin_bit_cast(nt_u32x4, v), reinterpret_cast<nt_u32x4*>(d));
+                    } else {
+                        for (int e = 0; e < 4 && gc + e < N; ++e) d[e] = v[e] + (has_c ? c[e] : 0u);
+                    }
+                }
+            }
+        }
+        return;
+    } else {
 
     // Without an addend the tile, rounded, is staged through the (now idle)
     // LDS and written out as whole 16-byte chunks of rows: a store
@@ -716,6 +789,19 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(KArgs p) {
             }
         }
     }
+    }   // 16-bit epilogues
+}
+
+template <int BM, int BN, int BK, int WM, int WN, int MF, int ST, bool BF16, bool TA, bool TB>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(KArgs p) {
+    dma_tile<BM, BN, BK, WM, WN, MF, ST, BF16 ? kElBF16 : kElF16, TA, TB>(p);
+}
+
+// int8 A (M x K, k contiguous) times int8 B stored N x K (k contiguous),
+// int32 C and D: the tile body with the integer instruction.
+template <int BM, int BN, int BK, int WM, int WN, int MF, int ST>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_i8_kernel(KArgs p) {
+    dma_tile<BM, BN, BK, WM, WN, MF, ST, kElI8, false, true>(p);
 }
 
 constexpr int kMaxDmaSplits = 64;
@@ -724,6 +810,13 @@ template <int BM, int BN, int BK, int WM, int WN, int MF, int ST, bool BF16, boo
 hipError_t launch_dma(const KArgs& a, int64_t grid, hipStream_t stream) {
     hipLaunchKernelGGL((gemm_dma_kernel<BM, BN, BK, WM, WN, MF, ST, BF16, TA, TB>),
                        dim3(static_cast<unsigned>(grid)), dim3(64 * WM * WN), 0, stream, a);
+    return hipGetLastError();
+}
+
+template <int BM, int BN, int BK, int WM, int WN, int MF, int ST>
+hipError_t launch_i8(const KArgs& a, int64_t grid, hipStream_t stream) {
+    hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, BK, WM, WN, MF, ST>), dim3(static_cast<unsigned>(grid)),
+                       dim3(64 * WM * WN), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -742,6 +835,13 @@ hipError_t launch_dma(const KArgs& a, int64_t grid, hipStream_t stream) {
     DMA_ENTRY(BM, BN, BK, WM, WN, MF, ST, 0, 1), DMA_ENTRY(BM, BN, BK, WM, WN, MF, ST, 1, 1),     \
     DMA_ENTRY(BM, BN, BK, WM, WN, MF, ST, 0, 2), DMA_ENTRY(BM, BN, BK, WM, WN, MF, ST, 1, 2),     \
     DMA_ENTRY(BM, BN, BK, WM, WN, MF, ST, 0, 3), DMA_ENTRY(BM, BN, BK, WM, WN, MF, ST, 1, 3)
+
+// int8 variants: dtype 2, B stored N x K; BK in 16-bit units (2 k each); no K slices.
+#define I8_ENTRY(BM, BN, BK, WM, WN, MF, ST)                                                     \
+    {KF_DMA, BM, BN, BK, ST, MF, WM, WN, 1, 2, 1, 64 * WM * WN,                                  \
+     static_cast<int64_t>(ST) * (BM + BN) * BK * 2, &launch_i8<BM, BN, BK, WM, WN, MF, ST>,       \
+     "gemm_i8_kernel<" DTG_STR(BM) "," DTG_STR(BN) "," DTG_STR(BK) "," DTG_STR(WM) "," DTG_STR(WN) \
+     "," DTG_STR(MF) "," DTG_STR(ST) ">", kLayTB}
 
 }  // namespace
 }  // namespace dtg

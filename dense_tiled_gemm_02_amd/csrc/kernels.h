@@ -43,7 +43,7 @@ enum KernelFamily { KF_TILE = 1, KF_SKINNY = 2, KF_DMA = 3 };
 struct KernelEntry {
     int32_t family;
     int32_t bm, bn, bk, stages, mfma, waves_m, waves_n, splitk;
-    int32_t dtype;       // 0 fp16, 1 bf16
+    int32_t dtype;       // 0 fp16, 1 bf16, 2 int8 operands with int32 C and D
     int32_t vec;
     int32_t threads;
     int64_t lds_bytes;
@@ -59,6 +59,7 @@ constexpr int kLayTA = 1, kLayTB = 2;
 const KernelEntry* tile_kernel_table(int* count);
 const KernelEntry* skinny_kernel_table(int* count);
 const KernelEntry* dma_kernel_table(int* count);
+const KernelEntry* i8_kernel_table(int* count);   // dtype 2: int8 operands, int32 C and D
 
 // Workspace bytes of a skinny launch over nslabs slabs of bm x bn split into
 // `splits` K slices (0 when splits == 1, -1 when nslabs is above the fixed

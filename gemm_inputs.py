@@ -27,6 +27,11 @@ magnitude code (a bell shape, peak at the middle codes) and a fair sign; each
 elements, 126 for E2M1).  Scale rows are padded to a multiple of 4 bytes with
 0xFF (the NaN code), which the library must never use.  Nothing here decodes
 a code: both sides take the same stored bytes.
+
+Integer workloads (I8_WORKLOADS, draw_i8): int8 codes uniform over [-128, 127],
+A row-major M x K and B stored N x K, int32 addends uniform over
+[-2^20, 2^20].  The pages measure no integer GEMM; the shapes are the 4096^3
+and ragged tail shapes of the 16-bit workloads.
 """
 import numpy as np
 import torch
@@ -204,3 +209,56 @@ def make_mx(workload):
         dt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[w.out]
         C = draw((w.M, w.N), w.seeds[2], "f16", "uniform").to(dt)
     return A, SA, B, SB, C
+
+
+# ---------------------------------------------------------------- 8-bit integers
+
+class I8Workload:
+    """int8 A (M x K, row-major) and B stored N x K (k contiguous), int32 C and
+    D; entries uniform over the full int8 range [-128, 127] (C, where present,
+    uniform over [-2^20, 2^20])."""
+
+    def __init__(self, name, M, N, K, seeds, has_c=False):
+        self.name = name
+        self.M, self.N, self.K = M, N, K
+        self.seeds = seeds
+        self.has_c = has_c
+
+    def flops(self):          # integer operations, counted like flops: 2 per multiply-add
+        return 2.0 * self.M * self.N * self.K
+
+    def bytes(self):
+        return float(self.M * self.K + self.N * self.K + 4 * self.M * self.N * (2 if self.has_c else 1))
+
+    def describe(self):
+        return {"workload": self.name, "M": self.M, "N": self.N, "K": self.K, "dtype": "int8 -> int32",
+                "layout": "row-major A (MxK), B stored NxK (k contiguous), int32 D (MxN)", "has_c": self.has_c,
+                "values": "uniform integers in [-128, 127]", "seeds": list(self.seeds[: 3 if self.has_c else 2])}
+
+
+I8_WORKLOADS = {
+    w.name: w for w in [
+        I8Workload("square_i8_4096", 4096, 4096, 4096, (901, 902, 903)),
+        I8Workload("tail_i8_4000x3000x1008_c", 4000, 3000, 1008, (911, 912, 913), has_c=True),
+    ]
+}
+
+
+def draw_i8(shape, seed):
+    """A numpy int8 array of uniform codes in [-128, 127]."""
+    return np.random.default_rng(seed).integers(-128, 128, shape).astype(np.int8)
+
+
+def draw_i32(shape, seed, bound=1 << 20):
+    """A numpy int32 array of uniform integers in [-bound, bound]."""
+    return np.random.default_rng(seed).integers(-bound, bound + 1, shape).astype(np.int32)
+
+
+def make_i8(workload):
+    """(A, Bt, C) numpy arrays of an I8Workload: A M x K, Bt N x K (B's
+    columns as rows), C int32 M x N or None."""
+    w = I8_WORKLOADS[workload] if isinstance(workload, str) else workload
+    A = draw_i8((w.M, w.K), w.seeds[0])
+    Bt = draw_i8((w.N, w.K), w.seeds[1])
+    C = draw_i32((w.M, w.N), w.seeds[2]) if w.has_c else None
+    return A, Bt, C

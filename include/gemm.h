@@ -69,8 +69,23 @@ extern "C" {
 
 typedef enum gemm_dtype {
     GEMM_F16 = 0,   /* IEEE binary16 storage, fp32 accumulate */
-    GEMM_BF16 = 1   /* bfloat16 storage, fp32 accumulate */
+    GEMM_BF16 = 1,  /* bfloat16 storage, fp32 accumulate */
+    GEMM_I8 = 2     /* int8 A and B, int32 accumulate, int32 C and D (below) */
 } gemm_dtype;
+
+/* GEMM_I8 (FlagGems "Hygon optimization", section "DUMMA matrix instruction
+ * shapes": the matrix unit takes integer inputs, which cover more k per
+ * instruction): D[i][j] = sum_k A[i][k] B[k][j] (+ C[i][j]) modulo 2^32, as a
+ * two's-complement int32 (the instruction's int32 accumulator wraps; the
+ * exact sum is its residue whatever the order of addition).  A is int8 with
+ * k contiguous (sa_k = 1: row-major M x K), B is int8 with k contiguous
+ * (sb_k = 1: stored N x K, the layout of a weight matrix), C and D int32
+ * row-major; strides in elements (bytes for A and B).  K, sa_m and sb_n must
+ * be multiples of 16 and A, B 16-byte aligned; M and N are free.  Anything
+ * else is GEMM_ERR_UNSUPPORTED (there is no element-wise int8 path), and so
+ * are forced K slices.  The tile knobs keep their meaning with bk in pairs
+ * of k (bk = 64 is a 128-deep K step) and mfma 16 / 32 selecting
+ * v_mfma_i32_16x16x64_i8 / 32x32x32_i8. */
 
 typedef enum gemm_status {
     GEMM_OK = 0,
@@ -224,7 +239,8 @@ gemm_status gemm(const void* A, const void* B, const void* C, void* D,
 void gemm_cache_clear(void);
 
 /* Bytes of one A/B tile pair staged per pipeline stage, summed over stages:
- * stages * (bm + bn) * bk * element bytes (FlagGems "Hygon optimization",
+ * stages * (bm + bn) * bk * element bytes, bk in elements of dtype (2 bytes,
+ * or 1 for GEMM_I8) (FlagGems "Hygon optimization",
  * section "Software pipelining": (BLOCK_M + BLOCK_N) x BLOCK_K x 2 bytes per
  * pair, 8 KiB at 64 x 64 x 32 fp16).  Returns -1 on a bad argument. */
 int64_t gemm_lds_bytes(int32_t bm, int32_t bn, int32_t bk, int32_t stages, gemm_dtype dtype);

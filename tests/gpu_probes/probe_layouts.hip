@@ -67,6 +67,37 @@ __global__ __launch_bounds__(64) void probe_mfma_kernel(const uint16_t* A, const
     }
 }
 
+// One integer matrix instruction (v_mfma_i32_16x16x64_i8 or 32x32x32_i8) in
+// one wavefront with the lane layouts the int8 tile kernel assumes: lane l
+// holds row / column l % MF and the 16 consecutive k 16 (l / MF) .. + 15 of A
+// (rows x k, row-major int8) and of B (k x cols, row-major int8); the int32
+// result goes out in row-major order with the floating-point instructions'
+// result layout.
+template <int MF>
+__global__ __launch_bounds__(64) void probe_mfma_i8_kernel(const int8_t* A, const int8_t* B, int* D) {
+    typedef int i32x4 __attribute__((ext_vector_type(4)));
+    typedef int i32x16 __attribute__((ext_vector_type(16)));
+    constexpr int KI = (MF == 16) ? 64 : 32;
+    const int l = threadIdx.x;
+    const int rc = l % MF, g = l / MF;
+    uint32_t a[4] = {0, 0, 0, 0}, b[4] = {0, 0, 0, 0};
+    for (int t = 0; t < 16; ++t) {
+        a[t / 4] |= static_cast<uint32_t>(static_cast<uint8_t>(A[rc * KI + 16 * g + t])) << (8 * (t % 4));
+        b[t / 4] |= static_cast<uint32_t>(static_cast<uint8_t>(B[(16 * g + t) * MF + rc])) << (8 * (t % 4));
+    }
+    const i32x4 av = {static_cast<int>(a[0]), static_cast<int>(a[1]), static_cast<int>(a[2]), static_cast<int>(a[3])};
+    const i32x4 bv = {static_cast<int>(b[0]), static_cast<int>(b[1]), static_cast<int>(b[2]), static_cast<int>(b[3])};
+    if constexpr (MF == 16) {
+        i32x4 c = {0, 0, 0, 0};
+        c = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, bv, c, 0, 0, 0);
+        for (int r = 0; r < 4; ++r) D[(4 * g + r) * 16 + rc] = c[r];
+    } else {
+        i32x16 c = {};
+        c = __builtin_amdgcn_mfma_i32_32x32x32_i8(av, bv, c, 0, 0, 0);
+        for (int r = 0; r < 16; ++r) D[(8 * (r / 4) + 4 * g + (r % 4)) * 32 + rc] = c[r];
+    }
+}
+
 // One scaled matrix instruction (v_mfma_scale_f32_{16x16x128,32x32x64}_f8f6f4)
 // on raw per-lane registers: lane l supplies a[8l..8l+7] and b[8l..8l+7] as
 // its A and B operand registers (only the first 4 dwords are used for the
@@ -178,6 +209,16 @@ int probe_mfma_scaled(int mf, int fa, int fb, int osa, int osb, const uint32_t* 
 #undef PROBE_SC_MF
 #undef PROBE_SC
     return static_cast<int>(hipErrorInvalidValue);
+}
+
+// mf: 16 (A 16x64, B 64x16, D 16x16) or 32 (A 32x32, B 32x32, D 32x32); int8
+// A and B, int32 D (device pointers).  Returns a hipError_t value.
+int probe_mfma_i8(int mf, const int8_t* A, const int8_t* B, int* D, void* stream) {
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (mf == 16) hipLaunchKernelGGL(probe_mfma_i8_kernel<16>, dim3(1), dim3(64), 0, s, A, B, D);
+    else if (mf == 32) hipLaunchKernelGGL(probe_mfma_i8_kernel<32>, dim3(1), dim3(64), 0, s, A, B, D);
+    else return static_cast<int>(hipErrorInvalidValue);
+    return static_cast<int>(hipGetLastError());
 }
 
 // in: 512 halfwords, out: 256 halfwords (device pointers).

@@ -51,6 +51,27 @@ def test_mfma_lane_layout(probe, mf, dt):
     assert np.array_equal(D.cpu().numpy(), (Ai @ Bi).astype(np.float32))
 
 
+@pytest.mark.parametrize("mf", [16, 32])
+def test_int8_mfma_lane_layout(probe, mf):
+    """v_mfma_i32_16x16x64_i8 / 32x32x32_i8 with the operand layout the int8
+    tile kernel assumes (lane l: row / column l % MF, k = 16 (l / MF) + 0..15)
+    and the floating-point result layout; full-range codes, so the int32 sums
+    are exact integers and the comparison is bit for bit."""
+    L = probe
+    L.probe_mfma_i8.restype = ctypes.c_int
+    L.probe_mfma_i8.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    ki = 64 if mf == 16 else 32
+    rng = np.random.default_rng(90 + mf)
+    Ai = rng.integers(-128, 128, (mf, ki)).astype(np.int8)
+    Bi = rng.integers(-128, 128, (ki, mf)).astype(np.int8)
+    A, B = torch.from_numpy(Ai).cuda(), torch.from_numpy(Bi).cuda()
+    D = torch.full((mf, mf), -7, dtype=torch.int32, device="cuda")
+    rc = L.probe_mfma_i8(mf, A.data_ptr(), B.data_ptr(), D.data_ptr(), torch.cuda.current_stream().cuda_stream)
+    assert rc == 0
+    torch.cuda.synchronize()
+    assert np.array_equal(D.cpu().numpy(), Ai.astype(np.int64) @ Bi.astype(np.int64))
+
+
 def test_lds_transpose_read_lane_map(probe):
     """The transposing 64-bit LDS read (ds_read_b64_tr_b16): within each group of
     16 lanes, the 16 addressed 8-byte pieces, taken in lane order, form a 4 x 16
