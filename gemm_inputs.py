@@ -133,7 +133,7 @@ def from_bits(b, dtype):
 # ---------------------------------------------------------------- block-scaled (MX)
 
 MX_ELEMENT_BITS = {"e4m3": 8, "e5m2": 8, "e2m1": 4}
-MX_SCALE_BASE = {"e4m3": 124, "e5m2": 124, "e2m1": 126}
+MX_SCALE_BASE = {"e2m3": 125, "e3m2": 124, "e4m3": 124, "e5m2": 124, "e2m1": 126}
 _E2M1_MAG_P = np.array([0.08, 0.14, 0.17, 0.17, 0.15, 0.13, 0.10, 0.06])   # magnitude codes 0..7
 
 
@@ -189,6 +189,8 @@ def draw_mx(rows, K, fmt, seed):
         mag = rng.choice(8, size=(rows, K), p=_E2M1_MAG_P).astype(np.uint8)
         nib = mag | (rng.integers(0, 2, (rows, K)).astype(np.uint8) << 3)
         codes = (nib[:, 0::2] | (nib[:, 1::2] << 4)).astype(np.uint8)
+    elif fmt in ("e2m3", "e3m2"):
+        codes = pack_fp6(rng.integers(0, 64, (rows, K)).astype(np.uint8))
     else:
         raise ValueError("unknown MX element format %r" % (fmt,))
     nb = (K + 31) // 32
@@ -196,6 +198,20 @@ def draw_mx(rows, K, fmt, seed):
     scales = np.full((rows, ld), 0xFF, dtype=np.uint8)
     scales[:, :nb] = (MX_SCALE_BASE[fmt] + rng.integers(-2, 3, (rows, nb))).astype(np.uint8)
     return np.ascontiguousarray(codes), scales
+
+
+def pack_fp6(codes):
+    """Rows of 6-bit codes (numpy uint8, K a multiple of 4) packed four per
+    three bytes: each row is one little-endian bit string, code k in bits
+    6k .. 6k + 5."""
+    c = np.asarray(codes, dtype=np.uint32)
+    rows, K = c.shape
+    if K % 4:
+        raise ValueError("FP6 rows need K a multiple of 4")
+    q = c.reshape(rows, K // 4, 4)
+    v = q[:, :, 0] | (q[:, :, 1] << 6) | (q[:, :, 2] << 12) | (q[:, :, 3] << 18)
+    out = np.stack([v & 0xFF, (v >> 8) & 0xFF, (v >> 16) & 0xFF], axis=2).astype(np.uint8)
+    return np.ascontiguousarray(out.reshape(rows, 3 * K // 4))
 
 
 def make_mx(workload):

@@ -29,8 +29,10 @@ Block-scaled (MX) operands, arithmetic in oracle_mx.c:
 
 MX operands are numpy uint8 arrays of raw bytes, one row per output row
 (A: M rows) or column (B: N rows, k along the row), with unit stride along
-the row; fmt is "e4m3", "e5m2" or "e2m1" (two elements per byte, even k in
-the low nibble); scales are uint8 arrays of E8M0 exponents, one per 32 k.
+the row; fmt is "e4m3", "e5m2", "e2m3", "e3m2" (FP6: four elements per
+three bytes, element k in bits 6k .. 6k + 5 of the row read as a
+little-endian bit string) or "e2m1" (two elements per byte, even k in the low
+nibble); scales are uint8 arrays of E8M0 exponents, one per 32 k.
 
 Integer operands, arithmetic in oracle_i8.c:
 
@@ -90,10 +92,12 @@ def _load():
     lib.oracle_tol_check.restype = _i64
     lib.oracle_tol_check.argtypes = [_i64, _p, _p, _p, ctypes.c_int,
                                      ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_i64)]
-    for f in ("e4m3", "e5m2", "e2m1", "e8m0"):
+    for f in ("e4m3", "e5m2", "e2m3", "e3m2", "e2m1", "e8m0"):
         fn = getattr(lib, "oracle_decode_" + f)
         fn.restype = ctypes.c_double
         fn.argtypes = [ctypes.c_uint8]
+    lib.oracle_fp6_code.restype = ctypes.c_uint8
+    lib.oracle_fp6_code.argtypes = [_p, _i64]
     lib.oracle_mx_gemm_f64.restype = ctypes.c_int
     lib.oracle_mx_gemm_f64.argtypes = [_i64, _i64, _i64, ctypes.c_int, ctypes.c_int,
                                        _p, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _i64, _i64, _p, _p, _p]
@@ -271,8 +275,8 @@ def grouped_order(num_pid_m, num_pid_n, group_m):
 # ---------------------------------------------------------------------------
 # Block-scaled (MX) operands
 
-MX_FORMATS = {"e4m3": 0, "e5m2": 1, "e2m1": 4}
-MX_ELEMENT_BITS = {"e4m3": 8, "e5m2": 8, "e2m1": 4}
+MX_FORMATS = {"e4m3": 0, "e5m2": 1, "e2m3": 2, "e3m2": 3, "e2m1": 4}
+MX_ELEMENT_BITS = {"e4m3": 8, "e5m2": 8, "e2m3": 6, "e3m2": 6, "e2m1": 4}
 
 
 def _mxf(fmt):
@@ -282,8 +286,18 @@ def _mxf(fmt):
         raise ValueError("MX element format must be one of %s, got %r" % (sorted(MX_FORMATS), fmt))
 
 
+def fp6_codes(row, K):
+    """The K element codes of one stored FP6 row (numpy uint8 bytes), as the
+    oracle reads them (oracle_fp6_code: element k in bits 6k .. 6k + 5 of the
+    row read as a little-endian bit string)."""
+    row = np.ascontiguousarray(row, dtype=np.uint8)
+    fn = _load().oracle_fp6_code
+    return np.array([fn(row.ctypes.data, k) for k in range(K)], dtype=np.uint8)
+
+
 def mx_decode(codes, fmt):
-    """Exact binary64 value of each element code (for e2m1 the low 4 bits)."""
+    """Exact binary64 value of each element code (for e2m1 the low 4 bits,
+    for e2m3 / e3m2 the low 6)."""
     _mxf(fmt)
     fn = getattr(_load(), "oracle_decode_" + fmt)
     c = np.asarray(codes, dtype=np.uint8)

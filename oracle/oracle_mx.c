@@ -20,7 +20,9 @@
  *     e = 255 is NaN);
  *   - elements are FP8 E4M3 (bias 7, 3 fraction bits, no infinities, NaN is
  *     S.1111.111), FP8 E5M2 (bias 15, 2 fraction bits, IEEE-style infinities
- *     and NaNs) or FP4 E2M1 (bias 1, 1 fraction bit, no infinities or NaNs);
+ *     and NaNs), FP6 E2M3 (bias 1, 3 fraction bits) or E3M2 (bias 3, 2
+ *     fraction bits), or FP4 E2M1 (bias 1, 1 fraction bit); the FP6 and FP4
+ *     formats have no infinities or NaNs;
  *   - the dot product of two MX vectors is the sum over blocks of
  *     X_a * X_b * sum_i (a_i * b_i), i.e. the sum over k of the scaled
  *     element products.
@@ -50,7 +52,10 @@
  * of an 8-bit format are one byte each, element k of row i at byte
  * A[i * lda + k]; FP4 elements are packed two per byte, element k at byte
  * A[i * lda + k / 2], in the low nibble for even k and the high nibble for odd
- * k.  The scale of block t of row i is byte SA[i * ldsa + t].  B is stored the
+ * k; FP6 elements are packed four per three bytes, the row read as one
+ * little-endian bit string with element k in bits 6k .. 6k + 5 (element k
+ * starts in byte 6k / 8).  The scale of block t of row i is byte
+ * SA[i * ldsa + t].  B is stored the
  * same way with its columns as rows: element (k, j) at B[j * ldb + k] (FP8).
  *
  * Build: compiled into liboracle.so together with oracle.c (build.py).
@@ -63,6 +68,8 @@
 /* element format codes of this file's entry points */
 #define MX_E4M3 0
 #define MX_E5M2 1
+#define MX_E2M3 2
+#define MX_E3M2 3
 #define MX_E2M1 4
 
 /* FP8 E4M3: sign, 4 exponent bits (bias 7), 3 fraction bits.  Exponent field
@@ -98,9 +105,40 @@ double oracle_decode_e2m1(uint8_t c) {
     return s ? -v : v;
 }
 
+/* FP6 E2M3 (the low 6 bits of c): sign, 2 exponent bits (bias 1), 3 fraction
+ * bits; exponent 0 is subnormal (m/8), no infinities or NaNs (largest 7.5). */
+double oracle_decode_e2m3(uint8_t c) {
+    int s = (c >> 5) & 1, e = (c >> 3) & 3, m = c & 7;
+    double v;
+    if (e == 0) v = ldexp((double)m, -3);                 /* m/8 */
+    else v = ldexp((double)(8 + m), e - 4);               /* (1 + m/8) * 2^(e-1) */
+    return s ? -v : v;
+}
+
+/* FP6 E3M2 (the low 6 bits of c): sign, 3 exponent bits (bias 3), 2 fraction
+ * bits; exponent 0 is subnormal (m/4 * 2^-2), no infinities or NaNs (largest 28). */
+double oracle_decode_e3m2(uint8_t c) {
+    int s = (c >> 5) & 1, e = (c >> 2) & 7, m = c & 3;
+    double v;
+    if (e == 0) v = ldexp((double)m, -4);                 /* m/4 * 2^-2 */
+    else v = ldexp((double)(4 + m), e - 5);               /* (1 + m/4) * 2^(e-3) */
+    return s ? -v : v;
+}
+
 /* E8M0 scale: 2^(c - 127); c = 255 is NaN. */
 double oracle_decode_e8m0(uint8_t c) {
     return c == 255 ? NAN : ldexp(1.0, (int)c - 127);
+}
+
+/* Code of FP6 element k of a stored row: the row's bytes read as one
+ * little-endian bit string, element k in bits 6k .. 6k + 5. */
+uint8_t oracle_fp6_code(const uint8_t* row, int64_t k) {
+    const int64_t bit = 6 * k;
+    const int64_t byte = bit / 8;
+    const int off = (int)(bit % 8);
+    unsigned v = row[byte] >> off;
+    if (off > 2) v |= (unsigned)row[byte + 1] << (8 - off);   /* the code continues in the next byte */
+    return (uint8_t)(v & 63u);
 }
 
 /* Element k of one stored row. */
@@ -109,10 +147,14 @@ static double mx_element(const uint8_t* row, int64_t k, int fmt) {
         const uint8_t b = row[k >> 1];
         return oracle_decode_e2m1((k & 1) ? (uint8_t)(b >> 4) : (uint8_t)(b & 15));
     }
+    if (fmt == MX_E2M3) return oracle_decode_e2m3(oracle_fp6_code(row, k));
+    if (fmt == MX_E3M2) return oracle_decode_e3m2(oracle_fp6_code(row, k));
     return fmt == MX_E4M3 ? oracle_decode_e4m3(row[k]) : oracle_decode_e5m2(row[k]);
 }
 
-static int fmt_ok(int fmt) { return fmt == MX_E4M3 || fmt == MX_E5M2 || fmt == MX_E2M1; }
+static int fmt_ok(int fmt) {
+    return fmt == MX_E4M3 || fmt == MX_E5M2 || fmt == MX_E2M3 || fmt == MX_E3M2 || fmt == MX_E2M1;
+}
 
 /* Scaled values of one stored row: out[k] = element k * its block's scale. */
 static void scaled_row(const uint8_t* row, const uint8_t* srow, int64_t K, int fmt, double* out) {

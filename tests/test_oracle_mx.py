@@ -465,3 +465,98 @@ def test_mx_rule_rejects_one_misscaled_block():
         rows = np.unique(np.argwhere(np.abs(bad - ref) > 0)[:, 0])
         assert list(rows) == [5]
         assert n >= 8, (fmt, n)             # at least half of row 5's 16 outputs are caught
+
+
+# ---------------------------------------------------------------- FP6 elements and mixed widths
+
+FP6 = {"e2m3": (2, 3, 1), "e3m2": (3, 2, 3)}   # exponent bits, fraction bits, bias
+
+
+def _fp6_embedding(c, fmt):
+    """Value of a 6-bit code through binary32: a normal code (s, e, m) is the
+    binary32 number with exponent field e - bias + 127 and the fraction bits
+    m at the top of its fraction; a subnormal one is m units of the smallest
+    subnormal, 2^(1 - bias - fraction bits)."""
+    eb, mb, bias = FP6[fmt]
+    s, e, m = c >> 5, (c >> mb) & ((1 << eb) - 1), c & ((1 << mb) - 1)
+    if e == 0:
+        v = m * 2.0 ** (1 - bias - mb)
+    else:
+        v = float(np.uint32((e - bias + 127) << 23 | m << (23 - mb)).view(np.float32))
+    return -v if s else v
+
+
+@pytest.mark.parametrize("fmt", ["e2m3", "e3m2"])
+def test_fp6_decode_matches_binary32_embedding_and_fp8_subsets(fmt):
+    codes = np.arange(64, dtype=np.uint8)
+    got = oracle.mx_decode(codes, fmt)
+    for c in range(64):
+        assert got[c] == _fp6_embedding(c, fmt), (fmt, c)
+    assert np.array_equal(oracle.mx_decode(codes | 0xC0, fmt), got)    # only the low 6 bits
+    # OCP MX extremes: E2M3 max 7.5, min normal 1, min subnormal 1/8;
+    # E3M2 max 28, min normal 1/4, min subnormal 1/16; no infinities or NaNs
+    pos = np.sort(got[:32])
+    want = {"e2m3": (7.5, 1.0, 0.125), "e3m2": (28.0, 0.25, 0.0625)}[fmt]
+    assert (pos[-1], pos[1]) == (want[0], want[2]) and np.isfinite(got).all()
+    assert np.min(np.abs(got[(codes & 31) >= (8 if fmt == "e2m3" else 4)])) == want[1]
+    assert len(set(pos.tolist())) == 32 and np.all(np.diff(got[:32]) > 0)   # increasing in the code
+    assert np.array_equal(got[32:], -got[:32])
+    # every E2M3 value is a float8 E4M3 value and every E3M2 one a float8 E5M2
+    # value: torch's float8 conversion returns each exactly
+    dt = torch.float8_e4m3fn if fmt == "e2m3" else torch.float8_e5m2
+    t = torch.from_numpy(got.astype(np.float32)).to(dt).to(torch.float64).numpy()
+    assert np.array_equal(t, got)
+
+
+def _unpack6(row, K):
+    """FP6 codes of a stored row by a route of the test's own: the bytes as
+    one big little-endian integer, 6 bits at a time."""
+    big = int.from_bytes(bytes(row.tolist()), "little")
+    return np.array([(big >> (6 * k)) & 63 for k in range(K)], dtype=np.uint8)
+
+
+def test_fp6_packing_worked_example_and_round_trip():
+    import gemm_inputs
+    # bytes 0xC1 0x0F 0x40: bits (low first) 100000 111111 000000 000010
+    row = np.array([0xC1, 0x0F, 0x40], np.uint8)
+    assert list(oracle.fp6_codes(row, 4)) == [1, 63, 0, 16]
+    rng = np.random.default_rng(3)
+    codes = rng.integers(0, 64, (5, 96)).astype(np.uint8)
+    packed = gemm_inputs.pack_fp6(codes)
+    assert packed.shape == (5, 72)
+    for i in range(5):
+        assert np.array_equal(oracle.fp6_codes(packed[i], 96), codes[i])
+        assert np.array_equal(_unpack6(packed[i], 96), codes[i])
+
+
+def _codes_any(rng, rows, K, fmt):
+    """Random codes of any supported format, packed as it is stored."""
+    import gemm_inputs
+    if fmt in FP6:
+        return gemm_inputs.pack_fp6(rng.integers(0, 64, (rows, K)).astype(np.uint8))
+    return _rand_codes(rng, rows, K, fmt)
+
+
+def _values_any(codes, K, fmt):
+    if fmt in FP6:
+        table = np.array([_fp6_embedding(c, fmt) for c in range(64)])
+        return np.stack([table[_unpack6(r, K)] for r in codes])
+    return _values(codes, K, fmt)
+
+
+@pytest.mark.parametrize("fa,fb", [("e2m3", "e2m3"), ("e3m2", "e3m2"), ("e2m3", "e3m2"), ("e4m3", "e2m1"),
+                                   ("e2m1", "e5m2"), ("e3m2", "e2m1"), ("e4m3", "e2m3")])
+def test_fp6_and_mixed_width_products_equal_blas(fa, fb):
+    """Products of FP6 operands and of operands of different widths against
+    BLAS on operands dequantized by the test's own route (its own unpacking
+    and binary32 embedding, torch's float8 decoders); every sum is exact."""
+    rng = np.random.default_rng(len(fa) * 7 + len(fb) + ord(fa[1]) + 3 * ord(fb[3]))
+    M, N, K = 9, 11, 160
+    A, B = _codes_any(rng, M, K, fa), _codes_any(rng, N, K, fb)
+    SA = rng.integers(120, 135, (M, 5), dtype=np.uint8)
+    SB = rng.integers(120, 135, (N, 5), dtype=np.uint8)
+    ref, S = oracle.mx_gemm_f64(A, SA, B, SB, K, fa, fb)
+    Av = _values_any(A, K, fa) * _expanded_scales(SA, K)
+    Bv = _values_any(B, K, fb) * _expanded_scales(SB, K)
+    assert np.array_equal(ref, Av @ Bv.T)
+    assert np.array_equal(S, np.abs(Av) @ np.abs(Bv).T)
