@@ -43,7 +43,14 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 256 * 2.4e9 * 4096 / 1e12        # 2516.6
-PEAK_MX_TFLOPS = {"e4m3": 5000.0, "e5m2": 5000.0, "e2m1": 10100.0}   # MI355X dense fp8 / fp4
+PEAK_MX_TFLOPS = {"e4m3": 5000.0, "e5m2": 5000.0, "e2m3": 10100.0, "e3m2": 10100.0,
+                  "e2m1": 10100.0}   # MI355X dense fp8 / fp6 / fp4
+
+
+def mx_peak(fa, fb):
+    """Dense peak of a block-scaled pair: the slower operand's rate (an 8-bit
+    operand runs the instruction at the fp8 rate)."""
+    return min(PEAK_MX_TFLOPS[fa], PEAK_MX_TFLOPS[fb])
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
 TRAFFIC_MX_JSON = os.path.join(ROOT, "profiles", "traffic_mx.json")
@@ -557,7 +564,7 @@ def mx(args):
             rec["roofline"] = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                "frac": gbs / PEAK_HBM_GBS}
         else:
-            peak = PEAK_MX_TFLOPS[w.fmt_a]
+            peak = mx_peak(w.fmt_a, w.fmt_b)
             rec["roofline"] = {"bound": "mfma", "achieved": round(rec["tflops"], 1), "peak": peak,
                                "unit": "TFLOP/s", "frac": rec["tflops"] / peak}
         rec["roofline"]["traffic"] = measured_traffic(kernel_of(pl.describe()), TRAFFIC_MX_JSON)

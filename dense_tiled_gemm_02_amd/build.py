@@ -28,7 +28,8 @@ ARCH = "gfx950"
 
 SOURCES = ["api.cpp", "api_mx.cpp", "gemm_tile.hip", "gemm_dma.hip", "gemm_dma_more.hip", "gemm_dma_layouts.hip",
            "gemm_mx.hip",
-           "gemm_skinny.hip", "gemm_static.hip", "gemm_i8.hip"]
+           "gemm_skinny.hip", "gemm_static.hip", "gemm_i8.hip",
+           "gemm_mx_direct.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 COMMON = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH,

@@ -40,13 +40,21 @@ gemm_status fail(gemm_status st, const char* fmt, ...) {
 }
 
 constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
-constexpr int kKernelMx = 4;   // gemm_config.kernel of the block-scaled tile kernel
-
-bool fmt_ok(int f) { return f == GEMM_MX_E4M3 || f == GEMM_MX_E5M2 || f == GEMM_MX_E2M1; }
+bool fmt_ok(int f) {
+    return f == GEMM_MX_E4M3 || f == GEMM_MX_E5M2 || f == GEMM_MX_E2M3 || f == GEMM_MX_E3M2 || f == GEMM_MX_E2M1;
+}
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+int elem_bits(int f) { return f == GEMM_MX_E2M1 ? 4 : (f == GEMM_MX_E2M3 || f == GEMM_MX_E3M2) ? 6 : 8; }
 
-// Bytes of k of one row: K elements of 8 or 4 bits.
-int64_t row_bytes(const gemm_mx_problem* p) { return p->fmt_a == GEMM_MX_E2M1 ? p->K / 2 : p->K; }
+// Bytes of k of one row of a format: K elements of 8, 6 or 4 bits.
+int64_t row_bytes(int64_t K, int fmt) { return K * elem_bits(fmt) / 8; }
+
+// The LDS-staged tile kernel takes pairs of one width, both 8-bit or both
+// E2M1; every other pair runs on the register-direct kernel.
+bool staged_pair(const gemm_mx_problem* p) {
+    const int a = elem_bits(p->fmt_a), b = elem_bits(p->fmt_b);
+    return a == b && a != 6;
+}
 
 gemm_status validate(const gemm_mx_problem* p) {
     if (!p) return fail(GEMM_ERR_INVALID_ARG, "problem is NULL");
@@ -54,21 +62,23 @@ gemm_status validate(const gemm_mx_problem* p) {
         return fail(GEMM_ERR_INVALID_ARG, "negative size M=%lld N=%lld K=%lld", (long long)p->M, (long long)p->N,
                     (long long)p->K);
     if (!fmt_ok(p->fmt_a) || !fmt_ok(p->fmt_b))
-        return fail(GEMM_ERR_INVALID_ARG, "element formats %d / %d: expected GEMM_MX_E4M3, _E5M2 or _E2M1",
-                    (int)p->fmt_a, (int)p->fmt_b);
+        return fail(GEMM_ERR_INVALID_ARG,
+                    "element formats %d / %d: expected GEMM_MX_E4M3, _E5M2, _E2M3, _E3M2 or _E2M1", (int)p->fmt_a,
+                    (int)p->fmt_b);
     if (p->out != GEMM_MX_OUT_F16 && p->out != GEMM_MX_OUT_BF16 && p->out != GEMM_MX_OUT_F32)
         return fail(GEMM_ERR_INVALID_ARG, "output type %d is not a gemm_mx_out value", (int)p->out);
     if (p->has_c != 0 && p->has_c != 1)
         return fail(GEMM_ERR_INVALID_ARG, "has_c must be 0 or 1, got %d", (int)p->has_c);
     if (p->M > kMaxDim || p->N > kMaxDim || p->K > kMaxDim)
         return fail(GEMM_ERR_UNSUPPORTED, "dimensions above 2^31-1 are not supported");
-    if ((p->fmt_a == GEMM_MX_E2M1) != (p->fmt_b == GEMM_MX_E2M1))
-        return fail(GEMM_ERR_UNSUPPORTED, "A and B must both be 8-bit formats or both E2M1");
-    const int64_t kq = p->fmt_a == GEMM_MX_E2M1 ? 32 : 16;
+    // K granularity: a whole 16-byte chunk of 8-bit elements (16 k), a whole
+    // 32-k block of 6- and 4-bit ones (24 and 16 bytes)
+    const int64_t kq = (elem_bits(p->fmt_a) == 8 && elem_bits(p->fmt_b) == 8) ? 16 : 32;
     if (p->K % kq != 0)
-        return fail(GEMM_ERR_UNSUPPORTED, "K=%lld must be a multiple of %lld for this element format",
+        return fail(GEMM_ERR_UNSUPPORTED, "K=%lld must be a multiple of %lld for these element formats",
                     (long long)p->K, (long long)kq);
-    const int64_t kb = row_bytes(p), nblk = cdiv(p->K, 32);
+    const int64_t kba = row_bytes(p->K, p->fmt_a), kbb = row_bytes(p->K, p->fmt_b), nblk = cdiv(p->K, 32);
+    const int64_t kb = kba > kbb ? kba : kbb;
     if (p->lda < 0 || p->ldb < 0 || p->ldsa < 0 || p->ldsb < 0 || p->ldc < 0 || p->ldd < 0)
         return fail(GEMM_ERR_INVALID_ARG, "negative stride");
     if (p->lda % 16 || p->ldb % 16)
@@ -77,8 +87,9 @@ gemm_status validate(const gemm_mx_problem* p) {
     if (p->ldsa % 4 || p->ldsb % 4)
         return fail(GEMM_ERR_UNSUPPORTED, "ldsa=%lld and ldsb=%lld must be multiples of 4 bytes",
                     (long long)p->ldsa, (long long)p->ldsb);
-    if ((p->M > 1 && p->lda < kb) || (p->N > 1 && p->ldb < kb))
-        return fail(GEMM_ERR_INVALID_ARG, "lda / ldb below the %lld bytes of a row", (long long)kb);
+    if ((p->M > 1 && p->lda < kba) || (p->N > 1 && p->ldb < kbb))
+        return fail(GEMM_ERR_INVALID_ARG, "lda / ldb below the %lld / %lld bytes of a row", (long long)kba,
+                    (long long)kbb);
     if ((p->M > 0 && p->ldsa < nblk) || (p->N > 0 && p->ldsb < nblk))
         return fail(GEMM_ERR_INVALID_ARG, "ldsa / ldsb below ceil(K/32) = %lld", (long long)nblk);
     if (p->M > 1 && p->N > 0 && p->ldd < p->N)
@@ -94,11 +105,13 @@ gemm_status validate(const gemm_mx_problem* p) {
 }
 
 const dtg::MxEntry* find_entry(const gemm_config& w, const gemm_mx_problem* p, const gemm_device_info& dev) {
-    int n = 0;
+    int n = 0, nd = 0;
     const dtg::MxEntry* t = dtg::mx_kernel_table(&n);
-    for (int i = 0; i < n; ++i) {
-        const dtg::MxEntry* e = &t[i];
+    const dtg::MxEntry* td = dtg::mx_direct_kernel_table(&nd);
+    for (int i = 0; i < n + nd; ++i) {
+        const dtg::MxEntry* e = i < n ? &t[i] : &td[i - n];
         if (e->fmt_a != p->fmt_a || e->fmt_b != p->fmt_b || e->lds_bytes > dev.lds_per_wg) continue;
+        if (w.kernel && w.kernel != e->kind) continue;
         if ((w.bm && w.bm != e->bm) || (w.bn && w.bn != e->bn) || (w.stages && w.stages != e->stages) ||
             (w.waves_m && w.waves_m != e->waves_m) || (w.waves_n && w.waves_n != e->waves_n) ||
             (w.bk && w.bk != e->bk) || (w.mfma && w.mfma != e->mfma) || (w.splitk > e->splitk))
@@ -119,7 +132,7 @@ gemm_status plan_impl(const gemm_mx_problem* prob, const gemm_device_info* dev, 
     gemm_config want;
     memset(&want, 0, sizeof want);
     int group_m = 8, xcd = 1;
-    const int64_t bke = prob->fmt_a == GEMM_MX_E2M1 ? 256 : 128;   // k per K step
+    const int64_t bke = prob->fmt_a == GEMM_MX_E2M1 ? 256 : 128;   // k per K step of the staged kernel
     const int64_t nkt = cdiv(prob->K, bke);
     // K slices: enough workgroups for the CUs, at least 2 K steps per slice, at most 16
     auto slices = [&](int64_t tiles, int64_t min_steps) {
@@ -129,7 +142,13 @@ gemm_status plan_impl(const gemm_mx_problem* prob, const gemm_device_info* dev, 
         if (tiles > dtg::kMaxCounters) s = 1;
         return static_cast<int32_t>(s > 1 ? s : 1);
     };
-    if (prob->M <= 32) {
+    if (!staged_pair(prob)) {
+        // FP6 elements or operands of different widths: the register-direct
+        // kernel, 128 x 128 tiles, no K slices
+        want.kernel = dtg::kMxKernelDirect;
+        want.bm = 128;
+        want.bn = 128;
+    } else if (prob->M <= 32) {
         // decode regime: 32-row slabs of 64 columns, K sliced to fill the CUs
         // (more slices per tile cost more in the fp32 partial-tile reduction
         // than they gain in load parallelism)
@@ -192,13 +211,11 @@ gemm_status plan_impl(const gemm_mx_problem* prob, const gemm_device_info* dev, 
         const gemm_config& f = *force;
         if (f.group_m < 0 || f.xcd_remap < 0 || f.xcd_remap > 2)
             return fail(GEMM_ERR_INVALID_ARG, "group_m must be >= 0 and xcd_remap one of 0, 1, 2");
-        if ((f.kernel && f.kernel != kKernelMx) || (f.mfma && f.mfma != 32) || f.splitk < 0 || f.splitk > 64)
-            return fail(GEMM_ERR_UNSUPPORTED, "the block-scaled path runs kernel %d, mfma 32, splitk 0..64",
-                        kKernelMx);
-        if (f.bm || f.bn || f.stages || f.waves_m || f.waves_n || f.bk || f.splitk) {
-            want = f;
-            want.kernel = 0;
-        }
+        if ((f.kernel && f.kernel != dtg::kMxKernelTile && f.kernel != dtg::kMxKernelDirect) ||
+            (f.mfma && f.mfma != 32) || f.splitk < 0 || f.splitk > 64)
+            return fail(GEMM_ERR_UNSUPPORTED, "the block-scaled path runs kernels %d and %d, mfma 32, splitk 0..64",
+                        dtg::kMxKernelTile, dtg::kMxKernelDirect);
+        if (f.bm || f.bn || f.stages || f.waves_m || f.waves_n || f.bk || f.splitk || f.kernel) want = f;
         if (f.group_m) group_m = f.group_m;
         if (f.xcd_remap) xcd = (f.xcd_remap == GEMM_XCD_ON);
     }
@@ -230,7 +247,7 @@ gemm_status plan_impl(const gemm_mx_problem* prob, const gemm_device_info* dev, 
     }
     gemm_config& c = pl->cfg;
     memset(&c, 0, sizeof c);
-    c.kernel = kKernelMx;
+    c.kernel = e->kind;
     c.bm = e->bm;
     c.bn = e->bn;
     c.bk = e->bk;
@@ -333,10 +350,9 @@ gemm_status gemm_mx_run(const gemm_mx_plan* plan, const void* A, const void* SA,
             return fail(GEMM_ERR_UNSUPPORTED, "A and B must be 16-byte aligned");
         if ((reinterpret_cast<uintptr_t>(SA) & 3) || (reinterpret_cast<uintptr_t>(SB) & 3))
             return fail(GEMM_ERR_UNSUPPORTED, "SA and SB must be 4-byte aligned");
-        const int64_t kb = row_bytes(&p);
         const struct { const void* ptr; int64_t bytes; const char* name; } in[4] = {
-            {A, (p.M - 1) * p.lda + kb, "A"},
-            {B, (p.N - 1) * p.ldb + kb, "B"},
+            {A, (p.M - 1) * p.lda + row_bytes(p.K, p.fmt_a), "A"},
+            {B, (p.N - 1) * p.ldb + row_bytes(p.K, p.fmt_b), "B"},
             {SA, p.M * p.ldsa, "SA"},
             {SB, p.N * p.ldsb, "SB"}};
         for (const auto& x : in) {

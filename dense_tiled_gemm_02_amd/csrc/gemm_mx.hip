@@ -769,7 +769,7 @@ constexpr int64_t mx_lds(int bm, int bn, int st, int fa) {
      ((BM / WM / 32) * (BN / WN / 32) * 4 <= 16 ? kMaxMxSplits : 1), 64 * WM * WN, mx_lds(BM, BN, ST, FA),   \
      &launch_mx<BM, BN, WM, WN, ST, FA, FB>,                                                                   \
      "gemm_mx_kernel<" DTG_STR(BM) "," DTG_STR(BN) "," DTG_STR(WM) "," DTG_STR(WN) "," DTG_STR(ST) ","        \
-     DTG_STR(FA) "," DTG_STR(FB) ">"}
+     DTG_STR(FA) "," DTG_STR(FB) ">", kMxKernelTile}
 #define MX_FORMATS(BM, BN, WM, WN, ST)                                                                       \
     MX_ENTRY(BM, BN, WM, WN, ST, 0, 0), MX_ENTRY(BM, BN, WM, WN, ST, 1, 1), MX_ENTRY(BM, BN, WM, WN, ST, 0, 1), \
     MX_ENTRY(BM, BN, WM, WN, ST, 1, 0), MX_ENTRY(BM, BN, WM, WN, ST, 4, 4)

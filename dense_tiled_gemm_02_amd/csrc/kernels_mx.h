@@ -33,7 +33,12 @@ struct MxArgs {
 typedef hipError_t (*mx_launch_fn)(const MxArgs& args, int64_t grid, hipStream_t stream);
 
 // Element format codes (the matrix instruction's own operand-type codes).
-constexpr int kMxE4M3 = 0, kMxE5M2 = 1, kMxE2M1 = 4;
+constexpr int kMxE4M3 = 0, kMxE5M2 = 1, kMxE2M3 = 2, kMxE3M2 = 3, kMxE2M1 = 4;
+
+// gemm_config.kernel values of the two block-scaled kernels: the LDS-staged
+// tile kernel (gemm_mx.hip; pairs of one width, 8-bit or E2M1) and the
+// register-direct kernel (gemm_mx_direct.hip; every pair of formats).
+constexpr int kMxKernelTile = 4, kMxKernelDirect = 5;
 
 // One compiled MX kernel variant.
 struct MxEntry {
@@ -46,8 +51,10 @@ struct MxEntry {
     int64_t lds_bytes;
     mx_launch_fn launch;
     const char* name;
+    int32_t kind;        // kMxKernelTile or kMxKernelDirect
 };
 
 const MxEntry* mx_kernel_table(int* count);
+const MxEntry* mx_direct_kernel_table(int* count);
 
 }  // namespace dtg

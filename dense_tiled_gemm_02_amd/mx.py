@@ -14,12 +14,17 @@ from . import (GemmError, _check, _force, _i32, _i64, _p, gemm_config, gemm_devi
 
 GEMM_MX_E4M3 = 0
 GEMM_MX_E5M2 = 1
+GEMM_MX_E2M3 = 2
+GEMM_MX_E3M2 = 3
 GEMM_MX_E2M1 = 4
 GEMM_MX_OUT_F16 = 0
 GEMM_MX_OUT_BF16 = 1
 GEMM_MX_OUT_F32 = 2
-KERNEL_MX = 4
-FORMATS = {"e4m3": GEMM_MX_E4M3, "e5m2": GEMM_MX_E5M2, "e2m1": GEMM_MX_E2M1}
+KERNEL_MX = 4           # the LDS-staged tile kernel (pairs of one width: 8-bit or E2M1)
+KERNEL_MX_DIRECT = 5    # the register-direct kernel (every pair of formats)
+FORMATS = {"e4m3": GEMM_MX_E4M3, "e5m2": GEMM_MX_E5M2, "e2m3": GEMM_MX_E2M3, "e3m2": GEMM_MX_E3M2,
+           "e2m1": GEMM_MX_E2M1}
+ELEMENT_BITS = {GEMM_MX_E4M3: 8, GEMM_MX_E5M2: 8, GEMM_MX_E2M3: 6, GEMM_MX_E3M2: 6, GEMM_MX_E2M1: 4}
 
 
 class gemm_mx_problem(ctypes.Structure):
@@ -142,12 +147,12 @@ def mx_problem(M, N, K, fmt_a="e4m3", fmt_b=None, out=GEMM_MX_OUT_BF16, has_c=Fa
     elements, ldsa = ldsb = ceil(K/32) rounded up to 4, ldc = ldd = N."""
     fa = FORMATS[fmt_a] if isinstance(fmt_a, str) else fmt_a
     fb = fa if fmt_b is None else (FORMATS[fmt_b] if isinstance(fmt_b, str) else fmt_b)
-    kb = K // 2 if fa == GEMM_MX_E2M1 else K
+    kba, kbb = K * ELEMENT_BITS[fa] // 8, K * ELEMENT_BITS[fb] // 8
     ns = -(-((K + 31) // 32) // 4) * 4
     p = gemm_mx_problem()
     p.M, p.N, p.K = M, N, K
-    p.lda = kb if lda is None else lda
-    p.ldb = kb if ldb is None else ldb
+    p.lda = kba if lda is None else lda
+    p.ldb = kbb if ldb is None else ldb
     p.ldsa = ns if ldsa is None else ldsa
     p.ldsb = ns if ldsb is None else ldsb
     p.ldc = (N if ldc is None else ldc) if has_c else 0

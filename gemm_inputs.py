@@ -132,7 +132,7 @@ def from_bits(b, dtype):
 
 # ---------------------------------------------------------------- block-scaled (MX)
 
-MX_ELEMENT_BITS = {"e4m3": 8, "e5m2": 8, "e2m1": 4}
+MX_ELEMENT_BITS = {"e4m3": 8, "e5m2": 8, "e2m3": 6, "e3m2": 6, "e2m1": 4}
 MX_SCALE_BASE = {"e2m3": 125, "e3m2": 124, "e4m3": 124, "e5m2": 124, "e2m1": 126}
 _E2M1_MAG_P = np.array([0.08, 0.14, 0.17, 0.17, 0.15, 0.13, 0.10, 0.06])   # magnitude codes 0..7
 
@@ -170,13 +170,17 @@ MX_WORKLOADS = {
         MxWorkload("mx_e4m3_4096", 4096, 4096, 4096, "e4m3", "e4m3", "bf16", (811, 812, 813)),
         # the decode shape at which the pages split K for the FP4 kernel (M = 16)
         MxWorkload("mx_e2m1_16x8192x8192", 16, 8192, 8192, "e2m1", "e2m1", "bf16", (821, 822, 823)),
+        # FP6 elements, and an FP8 x FP4 pair of different widths (register-direct kernel)
+        MxWorkload("mx_e2m3_4096", 4096, 4096, 4096, "e2m3", "e2m3", "bf16", (831, 832, 833)),
+        MxWorkload("mx_e4m3xe2m1_4096", 4096, 4096, 4096, "e4m3", "e2m1", "bf16", (841, 842, 843)),
     ]
 }
 
 
 def draw_mx(rows, K, fmt, seed):
     """(codes, scales) numpy uint8 arrays for `rows` rows of K elements: codes
-    rows of K bytes (8-bit formats) or K/2 bytes (E2M1, even k in the low
+    rows of K bytes (8-bit formats), 3K/4 bytes (FP6, packed by pack_fp6;
+    codes uniform over the 64 values) or K/2 bytes (E2M1, even k in the low
     nibble); scales rows of ceil(K/32) codes padded with 0xFF to a multiple of 4."""
     rng = np.random.default_rng(seed)
     if fmt in ("e4m3", "e5m2"):

@@ -3,15 +3,15 @@
  *
  *     D = A x B (+ C)
  *
- * Operation.  A (M x K) and B (K x N) hold 8-bit or 4-bit floating-point
- * elements; each run of 32 consecutive k of a row of A, and of a column of B,
+ * Operation.  A (M x K) and B (K x N) hold 8-, 6- or 4-bit floating-point
+ * elements (each operand its own format); each run of 32 consecutive k of a row of A, and of a column of B,
  * shares one power-of-two scale.  gfx950's scaled matrix instruction is the
  * entry point to these "microscaled" types ("Tuning Triton kernels", section 6,
  * Gluon: the cdna4 instruction set adds mfma_scaled, which gfx942 lacks; the
  * FP4 x FP4 GEMM kernel tuned in that section runs on it).  The pages do not
  * define the types; this library takes the OCP Microscaling (MX) formats:
- *   - elements: FP8 E4M3 (GEMM_MX_E4M3), FP8 E5M2 (GEMM_MX_E5M2) or FP4 E2M1
- *     (GEMM_MX_E2M1);
+ *   - elements: FP8 E4M3 (GEMM_MX_E4M3), FP8 E5M2 (GEMM_MX_E5M2), FP6 E2M3
+ *     (GEMM_MX_E2M3), FP6 E3M2 (GEMM_MX_E3M2) or FP4 E2M1 (GEMM_MX_E2M1);
  *   - scales: E8M0, the byte e meaning 2^(e - 127) (255 is NaN);
  *   - D[i][j] = sum_k (a_ik * 2^(sa_i,k/32 - 127)) * (b_kj * 2^(sb_j,k/32 - 127))
  *     (+ c_ij), accumulated in fp32 and rounded once to the output type,
@@ -30,24 +30,29 @@
  *
  * Layout.  Both operands are stored with k contiguous, the block's direction:
  *   - A: M rows, row i at byte A + i * lda, element k of the row at byte k
- *     (8-bit formats) or in byte k / 2, low nibble for even k (E2M1);
+ *     (8-bit formats), in byte k / 2, low nibble for even k (E2M1), or in
+ *     bits 6k .. 6k + 5 of the row read as one little-endian bit string (FP6:
+ *     four elements per three bytes);
  *   - B: stored N x K, column j of B at byte B + j * ldb, its elements as A's;
  *   - SA: M rows of ldsa bytes, the scale of block t of row i at SA[i*ldsa + t];
  *     SB: N rows of ldsb bytes likewise (column j of B);
  *   - C and D: row-major M x N of the output type, row strides ldc / ldd in
  *     elements.
- * Requirements (else GEMM_ERR_UNSUPPORTED): K a multiple of 16 (8-bit) or 32
- * (E2M1) elements, so every 16-byte chunk of a row is wholly inside or outside
- * K; lda and ldb multiples of 16 bytes and A, B 16-byte aligned; ldsa and ldsb
+ * Requirements (else GEMM_ERR_UNSUPPORTED): K a multiple of 16 when both
+ * formats are 8-bit, else of 32 (a whole scale block), so every chunk a lane
+ * loads is wholly inside or outside K; lda and ldb multiples of 16 bytes and A, B 16-byte aligned; ldsa and ldsb
  * multiples of 4, at least ceil(K/32), SA and SB 4-byte aligned, and the scale
  * arrays readable for M * ldsa and N * ldsb bytes (the kernel reads whole
  * 4-byte groups of a row; scale bytes past ceil(K/32) are read but never
- * used); A and B both 8-bit or both E2M1.  M and N tails are masked: any M,
- * N >= 0.
+ * used).  M and N tails are masked: any M, N >= 0.
  *
- * Tiling.  The direct-to-LDS tile kernel of gemm.h with 128 bytes of k per K
- * step (128 k of an 8-bit format, 256 of E2M1), GROUP_M tile order, an LDS ring
- * of stages, and the scales of each K step staged beside the operands.
+ * Tiling.  Pairs of one width (both 8-bit, or both E2M1) run the
+ * direct-to-LDS tile kernel of gemm.h with 128 bytes of k per K step (128 k of
+ * an 8-bit format, 256 of E2M1), GROUP_M tile order, an LDS ring of stages,
+ * and the scales of each K step staged beside the operands (kernel 4).  FP6
+ * operands and operands of different widths run a register-direct kernel
+ * (kernel 5): 128 x 128 tiles of 2 x 2 waves, each lane loading its operand
+ * registers and scale bytes straight from memory, no K slices.
  *
  * Ownership, errors and streams as in gemm.h: the caller owns every buffer,
  * the library allocates no device memory and never synchronizes; plans are
@@ -66,6 +71,8 @@ extern "C" {
 typedef enum gemm_mx_format {
     GEMM_MX_E4M3 = 0,   /* FP8: 4 exponent bits (bias 7), 3 fraction bits, no infinities */
     GEMM_MX_E5M2 = 1,   /* FP8: 5 exponent bits (bias 15), 2 fraction bits, IEEE-style specials */
+    GEMM_MX_E2M3 = 2,   /* FP6: 2 exponent bits (bias 1), 3 fraction bits; four per three bytes */
+    GEMM_MX_E3M2 = 3,   /* FP6: 3 exponent bits (bias 3), 2 fraction bits; four per three bytes */
     GEMM_MX_E2M1 = 4    /* FP4: 2 exponent bits (bias 1), 1 fraction bit; two per byte */
 } gemm_mx_format;
 
@@ -104,8 +111,8 @@ gemm_status gemm_mx_plan_create_for(const gemm_mx_problem* prob, const gemm_devi
 /* Free a plan.  NULL is a no-op. */
 void gemm_mx_plan_destroy(gemm_mx_plan* plan);
 
-/* The configuration a plan runs: kernel = 4 (block-scaled tile kernel),
- * bk = k per K step in elements, mfma = 32 (32x32x64 scaled instruction),
+/* The configuration a plan runs: kernel = 4 (block-scaled tile kernel) or 5
+ * (register-direct kernel), bk = k per K step in elements, mfma = 32 (32x32x64 scaled instruction),
  * splitk = K slices across workgroups (their fp32 partial tiles summed in
  * slice order by the last workgroup of each tile: deterministic). */
 gemm_status gemm_mx_plan_config(const gemm_mx_plan* plan, gemm_config* out);

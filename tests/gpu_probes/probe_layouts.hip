@@ -101,10 +101,11 @@ __global__ __launch_bounds__(64) void probe_mfma_i8_kernel(const int8_t* A, cons
 // One scaled matrix instruction (v_mfma_scale_f32_{16x16x128,32x32x64}_f8f6f4)
 // on raw per-lane registers: lane l supplies a[8l..8l+7] and b[8l..8l+7] as
 // its A and B operand registers (only the first 4 dwords are used for the
-// 4-bit format), sa[l] and sb[l] as its scale registers, of which the byte
+// 4-bit format, the first 6 for the 6-bit ones), sa[l] and sb[l] as its
+// scale registers, of which the byte
 // selected by OSA / OSB is the scale; the accumulator starts at zero and
 // lane l's result registers go to out[R l .. R l + R - 1] (R = 4 or 16).
-// Format codes FA / FB: 0 E4M3, 1 E5M2, 4 E2M1.
+// Format codes FA / FB: 0 E4M3, 1 E5M2, 2 E2M3, 3 E3M2, 4 E2M1.
 template <int MF, int FA, int FB, int OSA, int OSB>
 __global__ __launch_bounds__(64) void probe_mfma_scaled_kernel(const uint32_t* a, const uint32_t* b,
                                                                const uint32_t* sa, const uint32_t* sb, float* out) {
@@ -203,7 +204,9 @@ int probe_mfma_scaled(int mf, int fa, int fb, int osa, int osb, const uint32_t* 
 #define PROBE_SC_MF(MF_)                                                                     \
     PROBE_SC(MF_, 0, 0, 0, 0) PROBE_SC(MF_, 1, 1, 0, 0) PROBE_SC(MF_, 4, 4, 0, 0)            \
     PROBE_SC(MF_, 0, 1, 0, 0) PROBE_SC(MF_, 0, 0, 1, 2) PROBE_SC(MF_, 0, 0, 3, 1)            \
-    PROBE_SC(MF_, 4, 4, 2, 3)
+    PROBE_SC(MF_, 4, 4, 2, 3) PROBE_SC(MF_, 2, 2, 0, 0) PROBE_SC(MF_, 3, 3, 0, 0)            \
+    PROBE_SC(MF_, 2, 3, 0, 0) PROBE_SC(MF_, 0, 4, 0, 0) PROBE_SC(MF_, 4, 0, 0, 0)            \
+    PROBE_SC(MF_, 2, 4, 0, 0) PROBE_SC(MF_, 4, 3, 0, 0) PROBE_SC(MF_, 1, 2, 0, 0)
     PROBE_SC_MF(16)
     PROBE_SC_MF(32)
 #undef PROBE_SC_MF

@@ -326,7 +326,8 @@ def test_mx_forced_config_is_honoured_or_rejected():
     ({"ldsa": 0}, g.GEMM_ERR_INVALID_ARG),                     # below ceil(K/32)
     ({"lda": 64}, g.GEMM_ERR_INVALID_ARG),                     # below the row's bytes
     ({"ldd": 100}, g.GEMM_ERR_INVALID_ARG),                    # output rows overlap
-    ({"fmt_a": "e4m3", "fmt_b": "e2m1"}, g.GEMM_ERR_UNSUPPORTED),
+    ({"K": 48, "fmt_a": "e4m3", "fmt_b": "e2m1"}, g.GEMM_ERR_UNSUPPORTED),   # mixed widths: K a multiple of 32
+    ({"K": 80, "fmt_a": "e2m3", "fmt_b": "e2m3"}, g.GEMM_ERR_UNSUPPORTED),   # FP6: K a multiple of 32
     ({"out": 3}, g.GEMM_ERR_INVALID_ARG),
     ({"M": -1}, g.GEMM_ERR_INVALID_ARG),
 ])
@@ -497,3 +498,26 @@ def test_static_scratch_entry_point_rejects_large_workspaces_before_any_device_c
     assert st == g.GEMM_ERR_WORKSPACE
     msg = g.gemm_last_error()
     assert str(need.value) in msg and str(g.GEMM_STATIC_SCRATCH_BYTES) in msg, msg
+
+
+def test_mx_routes_fp6_and_mixed_widths_to_the_direct_kernel():
+    """Pairs of one width (8-bit, or E2M1) run the LDS-staged tile kernel
+    (kernel 4); FP6 operands and operands of different widths run the
+    register-direct kernel (kernel 5, 128 x 128 tiles, no K slices); either
+    may be forced where it applies."""
+    dev = fake_gfx950()
+    for fa, fb in (("e4m3", "e4m3"), ("e5m2", "e4m3"), ("e2m1", "e2m1")):
+        assert mx.gemm_mx_plan_create_for(mx.mx_problem(4096, 4096, 4096, fa, fb), dev).config.kernel == 4
+    for fa, fb in (("e2m3", "e2m3"), ("e3m2", "e2m3"), ("e4m3", "e2m1"), ("e2m1", "e5m2"), ("e3m2", "e4m3")):
+        pl = mx.gemm_mx_plan_create_for(mx.mx_problem(4096, 4096, 4096, fa, fb), dev)
+        c = pl.config
+        assert (c.kernel, c.bm, c.bn, c.splitk) == (5, 128, 128, 1), (fa, fb, pl.describe())
+        assert "gemm_mx_direct_kernel<%d,%d>" % (mx.FORMATS[fa], mx.FORMATS[fb]) in pl.describe()
+        with pytest.raises(g.GemmError) as e:
+            mx.gemm_mx_plan_create_for(mx.mx_problem(4096, 4096, 4096, fa, fb), dev, {"kernel": 4})
+        assert e.value.status == g.GEMM_ERR_UNSUPPORTED
+    forced = mx.gemm_mx_plan_create_for(mx.mx_problem(1024, 1024, 1024), dev, {"kernel": 5})
+    assert forced.config.kernel == 5
+    # FP6 rows: 3K/4 bytes, the default leading dimension
+    p = mx.mx_problem(64, 64, 256, "e2m3", "e3m2")
+    assert (p.lda, p.ldb) == (192, 192)

@@ -312,3 +312,83 @@ def test_decode_slices_with_addend(out, splits):
                      config={"bm": 32, "bn": 64, "splitk": splits})
     torch.cuda.synchronize()
     _check(D, ref, S, S8, out, "decode + C %s splits %d" % (out, splits))
+
+
+# ---------------------------------------------------------------- FP6 elements and mixed widths
+
+DIRECT_PAIRS = [("e2m3", "e2m3"), ("e3m2", "e3m2"), ("e2m3", "e3m2"), ("e4m3", "e2m1"), ("e2m1", "e4m3"),
+                ("e5m2", "e2m1"), ("e2m1", "e3m2"), ("e3m2", "e5m2"), ("e4m3", "e2m3")]
+
+
+@pytest.mark.parametrize("fa,fb", DIRECT_PAIRS)
+def test_fp6_and_mixed_widths_match_oracle(fa, fb):
+    """FP6 operands and operands of different widths (the register-direct
+    kernel): ragged M / N, a K that ends inside the instruction's 64 k, every
+    output type, with and without an addend."""
+    # rows padded to a multiple of 16 bytes (an FP6 row is 3K/4 bytes) with 0xFF
+    pad16 = lambda x: np.concatenate([x, np.full((x.shape[0], -x.shape[1] % 16), 0xFF, np.uint8)], 1)
+    for (M, N, K) in [(200, 136, 736), (129, 257, 160), (1, 1, 32), (64, 300, 4096)]:
+        A, SA, B, SB = _case(M, N, K, fa, fb, M + N + K)
+        A, B = pad16(A), pad16(B)
+        for out in ("bf16", "f16", "f32"):
+            C = torch.from_numpy(np.random.default_rng(K).standard_normal((M, N)).astype(np.float32)).to(OUT[out])
+            for c in (None, C):
+                print("mx direct", fa, fb, M, N, K, out, c is not None, flush=True)
+                D = mx.mx_matmul(_dev(A), _dev(SA), _dev(B), _dev(SB), K, fa, fb, out_dtype=OUT[out],
+                                 C=c.cuda() if c is not None else None)
+                torch.cuda.synchronize()
+                cref = c.to(torch.float64).numpy() if c is not None else None
+                ref, S, S8 = oracle.mx_gemm_f64(A, SA, B, SB, K, fa, fb, cref, runs=True)
+                assert torch.isfinite(D.float()).all()
+                _check(D, ref, S, S8, out, "%s x %s %dx%dx%d out %s c=%d" % (fa, fb, M, N, K, out, c is not None))
+
+
+@pytest.mark.parametrize("fa,fb", [("e4m3", "e4m3"), ("e2m1", "e2m1"), ("e5m2", "e4m3")])
+def test_direct_kernel_forced_on_single_width_pairs(fa, fb):
+    """The register-direct kernel also runs the pairs the tile kernel takes:
+    forced, inside the same bound on ragged shapes."""
+    M, N, K = 200, 136, 736
+    A, SA, B, SB = _case(M, N, K, fa, fb, 5)
+    D = mx.mx_matmul(_dev(A), _dev(SA), _dev(B), _dev(SB), K, fa, fb, out_dtype=torch.bfloat16,
+                     config={"kernel": 5})
+    torch.cuda.synchronize()
+    ref, S, S8 = oracle.mx_gemm_f64(A, SA, B, SB, K, fa, fb, runs=True)
+    _check(D, ref, S, S8, "bf16", "forced direct %s x %s" % (fa, fb))
+
+
+@pytest.mark.parametrize("fa,fb", [("e2m3", "e3m2"), ("e4m3", "e2m1")])
+def test_direct_kernel_padding_never_enters_a_sum(fa, fb):
+    """Row bytes past K hold 0xFF (the most negative FP6 / FP4 magnitudes, a
+    NaN in E4M3) and scale bytes past ceil(K/32) the NaN code: every output
+    stays finite and inside the bound with K ending mid-instruction."""
+    M, N, K = 136, 200, 736
+    A0, SA0, B0, SB0 = _case(M, N, K, fa, fb, 9)
+    pad = lambda x, extra, fill: np.concatenate([x, np.full((x.shape[0], extra), fill, np.uint8)], 1)
+    A, B = pad(A0, 16 - A0.shape[1] % 16 + 32, 0xFF), pad(B0, 16 - B0.shape[1] % 16 + 16, 0xFF)
+    SA, SB = pad(SA0, 8, 0xFF), pad(SB0, 4, 0xFF)
+    p = mx.mx_problem(M, N, K, fa, fb, mx.GEMM_MX_OUT_BF16, lda=A.shape[1], ldb=B.shape[1], ldsa=SA.shape[1],
+                      ldsb=SB.shape[1])
+    pl = mx.gemm_mx_plan_create(p, 0)
+    D = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+    dA, dSA, dB, dSB = _dev(A), _dev(SA), _dev(B), _dev(SB)
+    st = mx.mxlib().gemm_mx_run(pl.handle, dA.data_ptr(), dSA.data_ptr(), dB.data_ptr(), dSB.data_ptr(), None,
+                                D.data_ptr(), None, 0, torch.cuda.current_stream().cuda_stream)
+    assert st == 0, g.gemm_last_error()
+    torch.cuda.synchronize()
+    assert torch.isfinite(D.float()).all()
+    ref, S, S8 = oracle.mx_gemm_f64(A0, SA0, B0, SB0, K, fa, fb, runs=True)
+    _check(D, ref, S, S8, "bf16", "padded direct %s x %s" % (fa, fb))
+
+
+@pytest.mark.parametrize("name", ["mx_e2m3_4096", "mx_e4m3xe2m1_4096"])
+def test_direct_workloads_sampled(name):
+    w = gemm_inputs.MX_WORKLOADS[name]
+    A, SA, B, SB, _ = gemm_inputs.make_mx(w)
+    D = mx.mx_matmul(_dev(A), _dev(SA), _dev(B), _dev(SB), w.K, w.fmt_a, w.fmt_b, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    from helpers import sample_positions
+    ii, jj = sample_positions(w.M, w.N, 3000, 23)
+    ref, S, S8 = oracle.mx_gemm_f64_at(A, SA, B, SB, w.K, w.fmt_a, w.fmt_b, None, ii, jj, runs=True)
+    got = gemm_inputs.bits(D.cpu())[ii, jj]
+    n, worst, first = oracle.mx_tol_check(got, "bf16", ref, S, S8)
+    assert n == 0, "%s: %d outside (worst %.3g)" % (name, n, worst)

@@ -111,8 +111,11 @@ def test_direct_lds_loads_place_lane_data_contiguously_and_zero_out_of_range(pro
 # Scaled matrix instruction: (mf, format of A, format of B, scale byte of A, of B)
 SCALED = [(mf, fa, fb, oa, ob) for mf in (16, 32)
           for (fa, fb, oa, ob) in [(0, 0, 0, 0), (1, 1, 0, 0), (4, 4, 0, 0), (0, 1, 0, 0),
-                                   (0, 0, 1, 2), (0, 0, 3, 1), (4, 4, 2, 3)]]
-FMT_NAME = {0: "e4m3", 1: "e5m2", 4: "e2m1"}
+                                   (0, 0, 1, 2), (0, 0, 3, 1), (4, 4, 2, 3),
+                                   # FP6 elements and operands of different widths
+                                   (2, 2, 0, 0), (3, 3, 0, 0), (2, 3, 0, 0), (0, 4, 0, 0),
+                                   (4, 0, 0, 0), (2, 4, 0, 0), (4, 3, 0, 0), (1, 2, 0, 0)]]
+FMT_NAME = {0: "e4m3", 1: "e5m2", 2: "e2m3", 3: "e3m2", 4: "e2m1"}
 
 
 def _small_codes(rng, shape, fmt):
@@ -120,6 +123,11 @@ def _small_codes(rng, shape, fmt):
     if fmt == "e2m1":
         return rng.integers(0, 16, shape).astype(np.uint8)
     vals = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6, -0.5, -1, -2, -3, -4, -6], dtype=np.float32)
+    if fmt in ("e2m3", "e3m2"):                  # the codes of those values, looked up
+        import oracle
+        table = oracle.mx_decode(np.arange(64, dtype=np.uint8), fmt)
+        lut = np.array([int(np.flatnonzero(table == v)[0]) for v in vals], np.uint8)
+        return lut[rng.integers(0, len(vals), shape)]
     v = torch.from_numpy(vals[rng.integers(0, len(vals), shape)])
     dt = torch.float8_e4m3fn if fmt == "e4m3" else torch.float8_e5m2
     return v.to(dt).view(torch.uint8).numpy()
@@ -131,8 +139,16 @@ def _lane_bytes(codes_row, g, KI, fmt):
       8-bit formats: dwords 0-3 hold k = 16 g + 0..15, dwords 4-7 hold
         k = KI/2 + 16 g + 0..15 (one byte each);
       4-bit format: dwords 0-3 hold k = 32 g + 0..31, two per byte with the
-        even k in the low nibble; dwords 4-7 are not read (nonzero filler)."""
-    if fmt == "e2m1":
+        even k in the low nibble; dwords 4-7 are not read (nonzero filler);
+      6-bit formats: dwords 0-5 hold k = 32 g + 0..31 as one little-endian
+        bit string, k = 32 g + t in bits 6 t .. 6 t + 5; dwords 6-7 are not
+        read (nonzero filler)."""
+    if fmt in ("e2m3", "e3m2"):
+        c = codes_row[32 * g:32 * g + 32].astype(object)
+        bits = sum(int(v) << (6 * t) for t, v in enumerate(c))
+        b = np.frombuffer(bits.to_bytes(24, "little"), np.uint8)
+        b = np.concatenate([b, np.full(8, 0x5A, np.uint8)])
+    elif fmt == "e2m1":
         c = codes_row[32 * g:32 * g + 32]
         b = (c[0::2] | (c[1::2] << 4)).astype(np.uint8)
         b = np.concatenate([b, np.full(16, 0x77, np.uint8)])
