@@ -88,6 +88,19 @@ struct OpShape {
 // K, BK and the strides are in those 16-bit units.
 enum { kElF16 = 0, kElBF16 = 1, kElI8 = 2 };
 
+// Operation O of NR reads and NL loads issued in one sequence with the loads
+// spread evenly: load j sits at position floor((2 j + 1) (NR + NL) / (2 NL)).
+// Returns the load's number, or -(read number) - 1.
+constexpr int mix_loads(int O, int NR, int NL) {
+    int loads_before = 0;
+    for (int j = 0; j < NL; ++j) {
+        const int at = ((2 * j + 1) * (NR + NL)) / (2 * NL);
+        if (at == O) return j;
+        if (at < O) ++loads_before;
+    }
+    return -(O - loads_before) - 1;
+}
+
 template <int BM, int BN, int BK, int WM, int WN, int MF, int ST, int EL, bool TA, bool TB>
 __device__ __forceinline__ void dma_tile(const KArgs& p) {
     constexpr bool BF16 = EL == kElBF16;
@@ -431,10 +444,21 @@ __device__ __forceinline__ void dma_tile(const KArgs& p) {
                 __builtin_amdgcn_s_barrier();
                 interleave(cur, std::integral_constant<int, NR + L>{}, [&](auto o_tag) {
                     constexpr int O = decltype(o_tag)::value;
-                    if constexpr (O < NR)
+                    if constexpr (AGPR) {
+                        // one wave per SIMD: the loads spread evenly among the
+                        // reads (a burst of them fills the address unit's
+                        // command queue and stalls the only wave)
+                        constexpr int Q = mix_loads(O, NR, L);
+                        if constexpr (Q >= 0)
+                            load_op(std::integral_constant<int, Q>{}, d, S);
+                        else
+                            read_op(std::integral_constant<int, S1>{}, std::integral_constant<int, 0>{}, nxt,
+                                    std::integral_constant<int, -Q - 1>{});
+                    } else if constexpr (O < NR) {
                         read_op(std::integral_constant<int, S1>{}, std::integral_constant<int, 0>{}, nxt, o_tag);
-                    else
+                    } else {
                         load_op(std::integral_constant<int, O - NR>{}, d, S);
+                    }
                 });
             }
             wait_frags(nxt);

@@ -291,52 +291,65 @@ __global__ __launch_bounds__(64 * NWV) void gemm_skinny_kernel(KArgs p) {
     int* counters = static_cast<int*>(p.ws);
     float* part = reinterpret_cast<float*>(static_cast<char*>(p.ws) + kCounterBytes) +
                   static_cast<int64_t>(slab) * S * BMR * BN;
-    constexpr int PT = (BMR * BN + NT - 1) / NT;  // outputs per thread
+    // Each thread owns runs of 4 consecutive outputs of one row (16 bytes of
+    // partial): 16-byte LDS reads of the wave partials, one 16-byte
+    // system-coherent store of its slice's partial, one 16-byte load per other
+    // slice.  Summation order as ever: waves 0..NWV-1, then slices 0..S-1.
+    constexpr int RUNS = BMR * BN / 4;                // 4-output runs of the tile
+    constexpr int PR = (RUNS + NT - 1) / NT;          // runs per thread
+    const __amdgpu_buffer_rsrc_t pr =
+        __builtin_amdgcn_make_buffer_rsrc(part, 0, clamp_records(static_cast<int64_t>(S) * BMR * BN * 4), kRsrcWord3);
+    f32x4 mine[PR];
 #pragma unroll
-    for (int j = 0; j < PT; ++j) {
-        const int t = tid + j * NT;
+    for (int j = 0; j < PR; ++j) {
+        const int t = 4 * (tid + j * NT);
+        mine[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
         if (t >= BMR * BN) break;
-        float v = 0.0f;
 #pragma unroll
-        for (int w = 0; w < NWV; ++w) v += red[(w * BMR + t / BN) * BN + t % BN];
-        __hip_atomic_store(&part[slice * BMR * BN + t], v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-        red[t] = v;                              // only this thread reads position t
+        for (int w = 0; w < NWV; ++w) mine[j] += *reinterpret_cast<const f32x4*>(&red[w * BMR * BN + t]);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, mine[j]), pr,
+                                               static_cast<uint32_t>((slice * BMR * BN + t) * 4), 0, kSysScope);
     }
-    // just past the partial sums: the arrival flag
+    // the arrival flag lives just past the wave partials
     if (!arrive_last(&counters[slab], S, reinterpret_cast<int*>(red + NWV * BMR * BN))) return;
-    // The other slices' partials are loaded in groups of up to 8 slices, all of
-    // a thread's outputs at once, then summed in slice order; this
-    // workgroup's own partial comes from LDS (bitwise the value it stored).
-    float v[PT];
+    // The other slices' partials are loaded in groups of up to 8 slices, all at
+    // once, then summed in slice order; this slice's own comes from registers
+    // (bitwise the value it stored).
+    f32x4 v[PR];
 #pragma unroll
-    for (int j = 0; j < PT; ++j) v[j] = 0.0f;
+    for (int j = 0; j < PR; ++j) v[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     for (int s0 = 0; s0 < S; s0 += 8) {
-        float x[8][PT];
+        f32x4 x[8][PR];
 #pragma unroll
         for (int u = 0; u < 8; ++u)
 #pragma unroll
-            for (int j = 0; j < PT; ++j) {
-                const int t = (tid + j * NT < BMR * BN) ? tid + j * NT : 0;
-                x[u][j] = (s0 + u < S && s0 + u != slice)
-                              ? __hip_atomic_load(&part[(s0 + u) * BMR * BN + t], __ATOMIC_RELAXED,
-                                                  __HIP_MEMORY_SCOPE_SYSTEM)
-                              : red[t];
+            for (int j = 0; j < PR; ++j) {
+                const int t = 4 * (tid + j * NT);
+                const bool other = s0 + u < S && s0 + u != slice && t < BMR * BN;
+                x[u][j] = other ? __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                                pr, static_cast<uint32_t>(((s0 + u) * BMR * BN + t) * 4),
+                                                                0, kSysScope))
+                                : mine[j];
             }
 #pragma unroll
         for (int u = 0; u < 8; ++u)
 #pragma unroll
-            for (int j = 0; j < PT; ++j)
+            for (int j = 0; j < PR; ++j)
                 if (s0 + u < S) v[j] += x[u][j];
     }
 #pragma unroll
-    for (int j = 0; j < PT; ++j) {
-        const int t = tid + j * NT;
+    for (int j = 0; j < PR; ++j) {
+        const int t = 4 * (tid + j * NT);
         const int row = t / BN, col = t % BN;
-        const int gc = real_col(col);
+        const int gc = real_col(col);             // 4 consecutive columns (a run never crosses a half slab)
         if (t < BMR * BN && row < M && gc < N) {
-            float o = v[j];
-            if (has_c) o += widen<BF16>(p.C[static_cast<int64_t>(row) * p.ldc + gc]);
-            p.D[static_cast<int64_t>(row) * p.ldd + gc] = narrow<BF16>(o);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                if (gc + e >= N) break;
+                float o = v[j][e];
+                if (has_c) o += widen<BF16>(p.C[static_cast<int64_t>(row) * p.ldc + gc + e]);
+                p.D[static_cast<int64_t>(row) * p.ldd + gc + e] = narrow<BF16>(o);
+            }
         }
     }
     if (tid == 0) __hip_atomic_store(&counters[slab], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
