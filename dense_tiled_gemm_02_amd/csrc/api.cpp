@@ -22,6 +22,7 @@
 #include <mutex>
 #include <string>
 #include <tuple>
+#include <cstdlib>
 #include <vector>
 
 #include "../../include/gemm.h"
@@ -231,8 +232,12 @@ gemm_config cfg_of(int fam, int bm, int bn, int bk, int st, int mf, int wm, int 
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Measured choices for exact problem keys (M, N, K, dtype, has_c).  Anything
-// not listed falls back to the regime heuristic below.
+// Measured choices for exact problem keys (M, N, K, dtype, has_c; row-major
+// operands on the vector path), the winners of the interleaved races of
+// dense_tiled_gemm_02_amd/tune.py (a pruned sweep, every candidate probed in
+// its own process; a winner must beat the heuristic's plan beyond the
+// noise), frozen into tuned_table.inc.  Anything not listed, or listed with
+// a configuration this device cannot run, takes the regime heuristic below.
 struct TunedKey {
     int64_t M, N, K;
     int dtype, has_c;
@@ -240,8 +245,17 @@ struct TunedKey {
     int group_m, xcd;
 };
 const std::vector<TunedKey>& tuned_table() {
-    static const std::vector<TunedKey> t = {};
-    return t;
+    static const std::vector<TunedKey> t = {
+#include "tuned_table.inc"
+    };
+    // GEMM_TUNED_TABLE=0 plans every shape by the heuristic alone (a re-tune
+    // races the candidates against the heuristic, not against the old table)
+    static const std::vector<TunedKey> none;
+    static const bool off = [] {
+        const char* v = std::getenv("GEMM_TUNED_TABLE");
+        return v && v[0] == '0';
+    }();
+    return off ? none : t;
 }
 
 // Regime heuristic.  Square / tail problems take the largest tile that still
@@ -368,14 +382,17 @@ gemm_status plan_impl(const gemm_problem* given, const gemm_device_info* dev, co
     int group_m = 8, xcd = 1;
     gemm_config want;
     bool tuned = false;
-    for (const TunedKey& t : tuned_table()) {
-        if (t.M == prob->M && t.N == prob->N && t.K == prob->K && t.dtype == prob->dtype &&
-            t.has_c == prob->has_c) {
-            want = t.cfg;
-            group_m = t.group_m;
-            xcd = t.xcd;
-            tuned = true;
-            break;
+    if (vec && layout_of(prob) == 0) {
+        for (const TunedKey& t : tuned_table()) {
+            if (t.M == prob->M && t.N == prob->N && t.K == prob->K && t.dtype == prob->dtype &&
+                t.has_c == prob->has_c && (allow_ws || t.cfg.splitk <= 1) &&
+                find_entry(t.cfg, prob->dtype, 1, *dev, prob)) {
+                want = t.cfg;
+                group_m = t.group_m;
+                xcd = t.xcd;
+                tuned = true;
+                break;
+            }
         }
     }
     if (!tuned) want = heuristic(prob, *dev, &group_m, allow_ws);
