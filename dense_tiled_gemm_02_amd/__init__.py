@@ -101,6 +101,12 @@ def lib():
             if not os.path.exists(LIB_PATH):
                 raise RuntimeError("libgemm.so is not built (%s); run "
                                    "'python -m dense_tiled_gemm_02_amd.build'" % LIB_PATH)
+            # torch's HIP runtime first: libgemm then binds to that same
+            # runtime (it provides libgemm's libamdhip64.so.7), so torch's
+            # streams and device pointers are valid in libgemm.  Loaded the
+            # other way round, torch loads a second runtime of its own, and
+            # the one initialised second finds no device.
+            import torch  # noqa: F401
             L = ctypes.CDLL(LIB_PATH)
             for name, res, args in SIGNATURES:
                 fn = getattr(L, name)

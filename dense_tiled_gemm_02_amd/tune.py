@@ -76,6 +76,17 @@ WAVES = ((1, 2), (1, 4), (1, 8), (2, 1), (2, 2), (2, 4), (4, 2), (4, 1))
 SPLITS = (1, 2, 4, 8, 16)
 
 
+def parse_shape(s):
+    """(name, (M, N, K, dtype, has_c)) of a named workload or of MxNxK[f16|bf16][+C]."""
+    if s in NAMED:
+        return s, NAMED[s]
+    has_c = s.endswith("+C")
+    body = s[:-2] if has_c else s
+    dt = "bf16" if body.endswith("bf16") else "f16"
+    m, n, k = (int(x) for x in body.replace("bf16", "").replace("f16", "").split("x"))
+    return s, (m, n, k, dt, has_c)
+
+
 def _fake_gfx950():
     import dense_tiled_gemm_02_amd as g
     d = g.gemm_device_info()
@@ -156,10 +167,12 @@ def _launcher(A, Bs, C, D, cfg):
     import dense_tiled_gemm_02_amd as g
     pl = g.plan_for(A, Bs[0], C, D, cfg)
     stream = torch.cuda.current_stream().cuda_stream
-    ws, wsb = g.workspace_for(pl, torch.cuda.current_device(), stream)
+    dev = torch.cuda.current_device()
     st = {"i": 0}
 
     def launch(n):
+        # the shared workspace grows when a later plan needs more: fetch it per batch
+        ws, wsb = g.workspace_for(pl, dev, stream)
         for _ in range(n):
             b = Bs[st["i"] % len(Bs)]
             g.gemm_run(pl, A.data_ptr(), b.data_ptr(), C.data_ptr() if C is not None else None, D.data_ptr(),
@@ -307,8 +320,17 @@ def emit(paths, inc=INC, merged=os.path.join(ROOT, "profiles", "tuned_table.json
         d = json.load(open(p))
         doc["commands"].append(d.get("command", ""))
         doc["shapes"].update(d["shapes"])
+    slim = {"commands": doc["commands"], "shapes": {}}
+    for name, s in doc["shapes"].items():
+        t = dict(s)
+        if "probed" in t:   # one line per probe: the configuration's fields in CFG_KEYS order, us or the error
+            t["probed"] = ["%s: %s" % ("/".join(str(p["config"][k]) for k in CFG_KEYS),
+                                       "%.2f us" % p["us"] if p.get("exit") == 0 else "exit %d %s" %
+                                       (p.get("exit", -1), p.get("error", ""))) for p in t["probed"]]
+            t["probed_fields"] = "/".join(CFG_KEYS)
+        slim["shapes"][name] = t
     with open(merged, "w") as f:
-        json.dump(doc, f, indent=1)
+        json.dump(slim, f, indent=1)
         f.write("\n")
     head = ["// Generated by python -m dense_tiled_gemm_02_amd.tune --emit (from %s); do not edit." %
             os.path.relpath(merged, ROOT),

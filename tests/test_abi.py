@@ -7,6 +7,8 @@ with a hand-made gfx950 device description: 256 CUs, 8 XCDs, 2.4 GHz,
 import ctypes
 import os
 import re
+import subprocess
+import sys
 
 import pytest
 
@@ -521,3 +523,15 @@ def test_mx_routes_fp6_and_mixed_widths_to_the_direct_kernel():
     # FP6 rows: 3K/4 bytes, the default leading dimension
     p = mx.mx_problem(64, 64, 256, "e2m3", "e3m2")
     assert (p.lda, p.ldb) == (192, 192)
+
+
+def test_library_binds_to_torchs_hip_runtime():
+    """Loading libgemm before torch would put two HIP runtimes in one process
+    (torch's libraries ask for libamdhip64.so, libgemm for .so.7): the binding
+    imports torch first, so the process holds one runtime."""
+    code = ("import sys; import dense_tiled_gemm_02_amd as g; assert 'torch' not in sys.modules; g.lib(); "
+            "assert 'torch' in sys.modules; "
+            "maps = open('/proc/self/maps').read(); "
+            "paths = {l.split()[-1] for l in maps.splitlines() if 'libamdhip64' in l}; "
+            "print(len(paths)); assert len(paths) == 1, paths")
+    subprocess.run([sys.executable, "-c", code], cwd=ROOT, check=True)
