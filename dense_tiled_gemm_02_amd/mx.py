@@ -171,6 +171,7 @@ def _out_code(dtype):
 
 
 _plans = {}
+_cache_lock = threading.Lock()   # guards _plans and _ws (callers on several threads)
 
 
 def mx_matmul(A, SA, B, SB, K, fmt_a="e4m3", fmt_b=None, C=None, out=None, out_dtype=None, config=None,
@@ -198,9 +199,10 @@ def mx_matmul(A, SA, B, SB, K, fmt_a="e4m3", fmt_b=None, C=None, out=None, out_d
     dev = A.device.index if A.device.index is not None else 0
     key = (dev, tuple(getattr(p, f) for f, _ in gemm_mx_problem._fields_),
            tuple(sorted(config.items())) if isinstance(config, dict) else None)
-    pl = _plans.get(key)
-    if pl is None:
-        pl = _plans[key] = gemm_mx_plan_create(p, dev, config)
+    with _cache_lock:
+        pl = _plans.get(key)
+        if pl is None:
+            pl = _plans[key] = gemm_mx_plan_create(p, dev, config)
     if stream is None:
         stream = torch.cuda.current_stream(A.device).cuda_stream
     elif hasattr(stream, "cuda_stream"):
@@ -221,10 +223,11 @@ def _workspace(plan, device, stream):
     need = gemm_mx_workspace_size(plan)
     if need == 0:
         return None, 0
-    buf = _ws.get((device, stream))
-    if buf is None or buf.numel() < need:
-        buf = torch.zeros(max(need, 1 << 20), dtype=torch.uint8, device="cuda:%d" % device)
-        _ws[(device, stream)] = buf
+    with _cache_lock:
+        buf = _ws.get((device, stream))
+        if buf is None or buf.numel() < need:
+            buf = torch.zeros(max(need, 1 << 20), dtype=torch.uint8, device="cuda:%d" % device)
+            _ws[(device, stream)] = buf
     return buf.data_ptr(), buf.numel()
 
 

@@ -18,6 +18,8 @@ import pytest
 from dense_tiled_gemm_02_amd import build
 
 LDS_BYTES = 160 * 1024   # per workgroup on gfx950
+FAMILIES = ("gemm_dma_kernel", "gemm_tile_kernel", "gemm_skinny_kernel", "gemm_mx_kernel", "gemm_i8_kernel",
+            "gemm_mx_direct_kernel")
 
 
 @pytest.fixture(scope="module")
@@ -39,11 +41,12 @@ def test_report_covers_every_kernel_family(report):
     names = _demangle(list(report["kernels"]))
     fam = {}
     for d in names.values():
-        for f in ("gemm_dma_kernel", "gemm_tile_kernel", "gemm_skinny_kernel", "gemm_mx_kernel"):
-            if f in d:
+        for f in FAMILIES:
+            if f + "<" in d:
                 fam[f] = fam.get(f, 0) + 1
-    assert set(fam) == {"gemm_dma_kernel", "gemm_tile_kernel", "gemm_skinny_kernel", "gemm_mx_kernel"}, fam
+    assert set(fam) == set(FAMILIES), fam
     assert fam["gemm_dma_kernel"] >= 40 and fam["gemm_mx_kernel"] >= 10, fam
+    assert fam["gemm_i8_kernel"] >= 7 and fam["gemm_mx_direct_kernel"] >= 25, fam
 
 
 def test_no_kernel_uses_scratch_or_spills_vector_registers(report):
