@@ -54,6 +54,7 @@ def mx_peak(fa, fb):
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
 TRAFFIC_MX_JSON = os.path.join(ROOT, "profiles", "traffic_mx.json")
+TRAFFIC_I8_JSON = os.path.join(ROOT, "profiles", "traffic_i8.json")
 # What the counters behind "traffic" count: FETCH_SIZE and WRITE_SIZE are the
 # L2's requests to the memory fabric, so re-reads that hit the last-level
 # cache in front of HBM (the 256 MB MALL) count too.
@@ -685,7 +686,9 @@ def i8(args):
     import gemm_inputs
     import dense_tiled_gemm_02_amd as g
     rows = []
-    for name, w in gemm_inputs.I8_WORKLOADS.items():
+    names = [args.workload] if args.workload in gemm_inputs.I8_WORKLOADS else list(gemm_inputs.I8_WORKLOADS)
+    for name in names:
+        w = gemm_inputs.I8_WORKLOADS[name]
         A, Bt, C = gemm_inputs.make_i8(w)
         dA, dBt = torch.from_numpy(A).cuda(), torch.from_numpy(Bt).cuda()
         dC = torch.from_numpy(C).cuda() if C is not None else None
@@ -727,7 +730,8 @@ def i8(args):
             rec = {"workload": name, **w.describe(), "variant": v, "plan": pl.describe(), "us": st["median_ms"] * 1e3,
                    "spread": st["spread"], "batch_launches": batch,
                    "roofline": {"bound": "mfma", "achieved": round(tops, 1), "peak": PEAK_I8_TOPS, "unit": "TOP/s",
-                                "frac": tops / PEAK_I8_TOPS},
+                                "frac": tops / PEAK_I8_TOPS,
+                                "traffic": measured_traffic(kernel_of(pl.describe()), TRAFFIC_I8_JSON)},
                    "gbs": w.bytes() / st["median_ms"] / 1e6}
             rows.append(rec)
             print(json.dumps(rec), flush=True)
@@ -735,6 +739,8 @@ def i8(args):
     if args.save:
         save_rows(args.save, rows, "int8 workloads: planner plan and the other instruction shape, %d interleaved "
                                    "rounds" % args.rounds)
+    if args.copy_mb:
+        copy_calibration(args.copy_mb)
 
 
 def copy_calibration(mb):

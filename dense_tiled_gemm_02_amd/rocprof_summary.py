@@ -166,8 +166,9 @@ def report(out, match, workload, work, copy_bytes, mx=False, bench=None, prefix=
         lines.append('"python -m dense_tiled_gemm_02_amd.build"; the bench.py command runs the workload named')
         lines.append("above and ends with one 512 MiB device")
     elif mx:
-        lines.append('"python -m dense_tiled_gemm_02_amd.build"; bench.py --mx runs the three block-scaled')
-        lines.append("workloads (FP4 16x8192x8192, FP4 4096^3, E4M3 4096^3) and ends with one 512 MiB device")
+        lines.append('"python -m dense_tiled_gemm_02_amd.build"; bench.py --mx runs the five block-scaled')
+        lines.append("workloads (FP4 16x8192x8192; FP4, E4M3, FP6 E2M3 and E4M3 x FP4 at 4096^3) and ends with one")
+        lines.append("512 MiB device")
     else:
         lines.append('"python -m dense_tiled_gemm_02_amd.build"; bench.py runs the bf16 4096^3 and the')
         lines.append("skinny bf16 16x8192x8192 workloads back to back and ends with one 512 MiB device")
