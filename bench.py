@@ -8,7 +8,7 @@ A step is one launch of the whole hot path, D = A x B (+C), on the workload's
 synthetic inputs, which are resident in HBM before timing starts.  First the
 median and its spread: 12 (--batches, at least 10) batches of >= 1 ms, at
 least 10 launches each, every batch timed between two HIP events on the
-launch stream ("Tuning Triton", section 2: report the median with its
+launch stream ("Tuning Triton kernels", section 2: report the median with its
 spread).  Then, in the same warm regime, the timed region: W untimed launches,
 then exactly K launches on one stream between two HIP events, preceded and
 followed by a device synchronization; ms_per_step is elapsed / K.
@@ -27,7 +27,7 @@ One JSON line is printed (rank 0, N = 1):
 --sweep times interleaved variants (GROUP_M, instruction shape, tile sizes):
 every round visits the variants in a fresh seeded-random order and times a
 batch of launches per visit; the median and spread = (max - min) / median
-over the rounds are reported ("Tuning Triton", section 2: compare a delta with
+over the rounds are reported ("Tuning Triton kernels", section 2: compare a delta with
 the spread, not with zero).
 """
 import argparse
@@ -78,8 +78,9 @@ def plan_kernel_name(profiled):
 
 
 def measured_traffic(kernel_name, path=TRAFFIC_JSON):
-    """HBM bytes per launch of this kernel from the committed counter runs, or
-    None if there are none or the kernel sources changed since."""
+    """L2-to-fabric bytes per launch of this kernel (MALL hits included) from
+    the committed counter runs, or None if there are none or the kernel
+    sources changed since."""
     try:
         import json as _json
         from dense_tiled_gemm_02_amd import rocprof_summary

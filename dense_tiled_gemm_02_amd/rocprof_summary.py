@@ -63,9 +63,10 @@ def _largest_copy(d, name):
 
 
 def traffic(fetch_dir, write_dir, copy_bytes):
-    """HBM bytes per launch of every kernel: FETCH_SIZE and WRITE_SIZE (KiB per
-    dispatch), each scaled so that the copy kernel of copy_bytes reads and
-    writes exactly copy_bytes."""
+    """Bytes per launch between the L2s and the memory fabric (MALL hits
+    included) of every kernel: FETCH_SIZE and WRITE_SIZE (KiB per dispatch),
+    each scaled so that the copy kernel of copy_bytes reads and writes exactly
+    copy_bytes."""
     fetch = counter_means(fetch_dir, "FETCH_SIZE")
     write = counter_means(write_dir, "WRITE_SIZE")
     copy_f = _largest_copy(fetch_dir, "FETCH_SIZE")
@@ -203,7 +204,7 @@ def report(out, match, workload, work, copy_bytes, mx=False, bench=None, prefix=
                 if match in k:
                     lines.append("Calibration: the %d MiB copy kernel sets FETCH_SIZE x %.4f and WRITE_SIZE x %.4f,"
                                  % (copy_bytes >> 20, t["fetch_scale"], t["write_scale"]))
-                    lines.append("so HBM-side traffic per launch = %.1f KiB x %.4f + %.1f KiB x %.4f = %.1f MB" % (
+                    lines.append("so L2-to-fabric traffic per launch (MALL hits included) = %.1f KiB x %.4f + %.1f KiB x %.4f = %.1f MB" % (
                         v["fetch_kib"], t["fetch_scale"], v["write_kib"], t["write_scale"], v["bytes"] / 1e6))
     return "\n".join(lines) + "\n"
 

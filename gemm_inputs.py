@@ -14,9 +14,9 @@ distributions apply to every operand):
   square_f16_1024     fp16 1024^3, U[-1,1]  (the tile-size sweep shape of
                       "Hopper Support in Triton", slide 6: M=N=K=1024)
   square_bf16_4096    bf16 4096^3, N(0,1)/sqrt(K)  (the 4096^3 bf16 shape of
-                      "Tuning Triton", section 1)
+                      "Tuning Triton kernels", section 1)
   skinny_bf16_16x8192 bf16 M=16, N=K=8192, N(0,1)*0.02  (decode-like shape,
-                      "Tuning Triton", section 4 regime split)
+                      "Tuning Triton kernels", section 4 regime split)
   tail_f16_4000x3000x1000_c  fp16 4000x3000x1000 plus addend C, U[-1,1]
 
 Block-scaled (MX) workloads draw element codes and E8M0 scale codes directly

@@ -37,7 +37,7 @@
  * LDS ring (section "Software pipelining"), and masks M/N/K tails with zero
  * fill ("Hopper Support in Triton", slides 15-16, k_remaining masks with
  * other = 0).  The tile configuration is chosen per (M, N, K, dtype, layout,
- * has_c) key ("Tuning Triton", section 3: the key must name every dimension
+ * has_c) key ("Tuning Triton kernels", section 3: the key must name every dimension
  * the kernel tiles on), or forced by the caller.
  *
  * Ownership.  The caller owns A, B, C, D (device memory) and any plan.  The

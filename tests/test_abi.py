@@ -143,7 +143,7 @@ def test_few_tiles_and_deep_k_take_k_slices():
 
 
 def test_key_includes_m():
-    # "Tuning Triton", section 3: M=1 and M=4096 with equal N, K must not share a tile.
+    # "Tuning Triton kernels", section 3: M=1 and M=4096 with equal N, K must not share a tile.
     big = plan(4096, 4096, 4096).config
     small = plan(1, 4096, 4096).config
     assert (big.bm, big.bn, big.kernel) != (small.bm, small.bn, small.kernel)

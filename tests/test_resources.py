@@ -80,7 +80,7 @@ def _plan_name(demangled):
 
 
 def test_every_knob_reaches_the_compiled_kernel(report):
-    """"Tuning Triton", section 6: a knob the kernel accepts but never reads
+    """"Tuning Triton kernels", section 6: a knob the kernel accepts but never reads
     gives a fake win in a sweep.  Every tile knob here is a template argument:
     forcing a value selects a kernel whose name carries it, and that kernel is
     a distinct function in the compiler's report (its code is specialized on
