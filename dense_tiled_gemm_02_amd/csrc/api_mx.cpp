@@ -49,9 +49,10 @@ int elem_bits(int f) { return f == GEMM_MX_E2M1 ? 4 : (f == GEMM_MX_E2M3 || f ==
 // Bytes of k of one row of a format: K elements of 8, 6 or 4 bits.
 int64_t row_bytes(int64_t K, int fmt) { return K * elem_bits(fmt) / 8; }
 
-// The LDS-staged tile kernel takes pairs of one width, both 8-bit or both
-// E2M1; every other pair runs on the register-direct kernel.
-bool staged_pair(const gemm_mx_problem* p) {
+// Pairs of one width (8-bit with 8-bit, E2M1 with E2M1) have the tile
+// kernel's full variant table; the others (an FP6 operand, or 8-bit with
+// 4-bit) its 256 x 256, 128 x 128, 64 x 64 and 32 x 64 variants.
+bool one_width_pair(const gemm_mx_problem* p) {
     const int a = elem_bits(p->fmt_a), b = elem_bits(p->fmt_b);
     return a == b && a != 6;
 }
@@ -105,11 +106,12 @@ gemm_status validate(const gemm_mx_problem* p) {
 }
 
 const dtg::MxEntry* find_entry(const gemm_config& w, const gemm_mx_problem* p, const gemm_device_info& dev) {
-    int n = 0, nd = 0;
+    int n = 0, np = 0, nd = 0;
     const dtg::MxEntry* t = dtg::mx_kernel_table(&n);
+    const dtg::MxEntry* tp = dtg::mx_pair_kernel_table(&np);
     const dtg::MxEntry* td = dtg::mx_direct_kernel_table(&nd);
-    for (int i = 0; i < n + nd; ++i) {
-        const dtg::MxEntry* e = i < n ? &t[i] : &td[i - n];
+    for (int i = 0; i < n + np + nd; ++i) {
+        const dtg::MxEntry* e = i < n ? &t[i] : i < n + np ? &tp[i - n] : &td[i - n - np];
         if (e->fmt_a != p->fmt_a || e->fmt_b != p->fmt_b || e->lds_bytes > dev.lds_per_wg) continue;
         if (w.kernel && w.kernel != e->kind) continue;
         if ((w.bm && w.bm != e->bm) || (w.bn && w.bn != e->bn) || (w.stages && w.stages != e->stages) ||
@@ -132,7 +134,8 @@ gemm_status plan_impl(const gemm_mx_problem* prob, const gemm_device_info* dev, 
     gemm_config want;
     memset(&want, 0, sizeof want);
     int group_m = 8, xcd = 1;
-    const int64_t bke = prob->fmt_a == GEMM_MX_E2M1 ? 256 : 128;   // k per K step of the staged kernel
+    // k per K step of the tile kernel
+    const int64_t bke = (prob->fmt_a == GEMM_MX_E2M1 && prob->fmt_b == GEMM_MX_E2M1) ? 256 : 128;
     const int64_t nkt = cdiv(prob->K, bke);
     // K slices: enough workgroups for the CUs, at least 2 K steps per slice, at most 16
     auto slices = [&](int64_t tiles, int64_t min_steps) {
@@ -142,13 +145,7 @@ gemm_status plan_impl(const gemm_mx_problem* prob, const gemm_device_info* dev, 
         if (tiles > dtg::kMaxCounters) s = 1;
         return static_cast<int32_t>(s > 1 ? s : 1);
     };
-    if (!staged_pair(prob)) {
-        // FP6 elements or operands of different widths: the register-direct
-        // kernel, 128 x 128 tiles, no K slices
-        want.kernel = dtg::kMxKernelDirect;
-        want.bm = 128;
-        want.bn = 128;
-    } else if (prob->M <= 32) {
+    if (prob->M <= 32) {
         // decode regime: 32-row slabs of 64 columns, K sliced to fill the CUs
         // (more slices per tile cost more in the fp32 partial-tile reduction
         // than they gain in load parallelism)
@@ -172,7 +169,10 @@ gemm_status plan_impl(const gemm_mx_problem* prob, const gemm_device_info* dev, 
                                    {64, 64, 0.25},   {192, 256, 0.9}};
         const T* best = nullptr;
         double best_t = 0.0;
+        const bool full = one_width_pair(prob);
         for (const T& t : ladder) {
+            // pairs outside the one-width table have the square tiles only
+            if (!full && t.bm != t.bn) continue;
             const int64_t tiles = cdiv(prob->M, t.bm) * cdiv(prob->N, t.bn);
             const double est = static_cast<double>(cdiv(tiles, dev->cu_count)) * t.cost;
             if (!best || est < best_t) {

@@ -12,6 +12,7 @@ namespace dtg {
 namespace dev {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -176,6 +177,22 @@ __device__ __forceinline__ u32x4 lds_read16_any(uint32_t addr) {
         return lds_read16<OFF % 65536>(addr + static_cast<uint32_t>(OFF / 65536) * 65536u);
 }
 
+// 8-byte read at LDS byte address addr + OFF (addr + OFF a multiple of 8),
+// and the same for any non-negative offset.
+template <int OFF>
+__device__ __forceinline__ u32x2 lds_read8(uint32_t addr) {
+    u32x2 v;
+    asm volatile("ds_read_b64 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
+    return v;
+}
+template <int OFF>
+__device__ __forceinline__ u32x2 lds_read8_any(uint32_t addr) {
+    if constexpr (OFF < 65536)
+        return lds_read8<OFF>(addr);
+    else
+        return lds_read8<OFF % 65536>(addr + static_cast<uint32_t>(OFF / 65536) * 65536u);
+}
+
 // Transposing 64-bit read (ds_read_b64_tr_b16) at addr + OFF: within each
 // 16-lane group the 16 addressed 8-byte pieces, in lane order, form a 4 x 16
 // matrix of halfwords (lanes 4i..4i+3 give row i); lane t receives column t.
@@ -241,6 +258,7 @@ __device__ __forceinline__ void lds_wait_all() { asm volatile("s_waitcnt lgkmcnt
 // order), so no use of v is scheduled before the wait.
 __device__ __forceinline__ void tie(u32x4& v) { asm volatile("" : "+v"(v)); }
 __device__ __forceinline__ void tie(i16x4& v) { asm volatile("" : "+v"(v)); }
+__device__ __forceinline__ void tie(u32x2& v) { asm volatile("" : "+v"(v)); }
 __device__ __forceinline__ void tie(uint32_t& v) { asm volatile("" : "+v"(v)); }
 
 __device__ __forceinline__ uint32_t lds_addr(const uint16_t* p) {

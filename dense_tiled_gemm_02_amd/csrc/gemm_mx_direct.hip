@@ -40,7 +40,6 @@ namespace {
 using namespace dev;
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 template <int F>
 constexpr int elem_bits() { return F <= kMxE5M2 ? 8 : (F == kMxE2M1 ? 4 : 6); }

@@ -36,8 +36,9 @@ typedef hipError_t (*mx_launch_fn)(const MxArgs& args, int64_t grid, hipStream_t
 constexpr int kMxE4M3 = 0, kMxE5M2 = 1, kMxE2M3 = 2, kMxE3M2 = 3, kMxE2M1 = 4;
 
 // gemm_config.kernel values of the two block-scaled kernels: the LDS-staged
-// tile kernel (gemm_mx.hip; pairs of one width, 8-bit or E2M1) and the
-// register-direct kernel (gemm_mx_direct.hip; every pair of formats).
+// tile kernel (gemm_mx_kernel.h; every pair of formats, its variants in
+// gemm_mx.hip for pairs of one width and gemm_mx_pairs.hip for the others)
+// and the register-direct kernel (gemm_mx_direct.hip; every pair).
 constexpr int kMxKernelTile = 4, kMxKernelDirect = 5;
 
 // One compiled MX kernel variant.
@@ -55,6 +56,7 @@ struct MxEntry {
 };
 
 const MxEntry* mx_kernel_table(int* count);
+const MxEntry* mx_pair_kernel_table(int* count);
 const MxEntry* mx_direct_kernel_table(int* count);
 
 }  // namespace dtg

@@ -46,13 +46,16 @@
  * 4-byte groups of a row; scale bytes past ceil(K/32) are read but never
  * used).  M and N tails are masked: any M, N >= 0.
  *
- * Tiling.  Pairs of one width (both 8-bit, or both E2M1) run the
- * direct-to-LDS tile kernel of gemm.h with 128 bytes of k per K step (128 k of
- * an 8-bit format, 256 of E2M1), GROUP_M tile order, an LDS ring of stages,
- * and the scales of each K step staged beside the operands (kernel 4).  FP6
- * operands and operands of different widths run a register-direct kernel
- * (kernel 5): 128 x 128 tiles of 2 x 2 waves, each lane loading its operand
- * registers and scale bytes straight from memory, no K slices.
+ * Tiling.  Every pair runs the direct-to-LDS tile kernel of gemm.h (kernel
+ * 4): GROUP_M tile order, an LDS ring of stages, each operand staged in rows of
+ * one K step's k in its own width (256 k for E2M1 with E2M1, else 128 k: rows
+ * of 128, 96 or 64 bytes for 8-, 6- and 4-bit elements), and the scales of
+ * each K step staged beside the operands.  Pairs of one width (both 8-bit, or
+ * both E2M1) have the full tile ladder; the others (an FP6 operand, or 8-bit
+ * with 4-bit) its 256 x 256, 128 x 128 and 64 x 64 tiles and the decode slab.
+ * A register-direct kernel (kernel 5, forced only: 128 x 128 tiles of 2 x 2
+ * waves, each lane loading its operand registers and scale bytes straight
+ * from memory, no K slices) runs every pair as well.
  *
  * Ownership, errors and streams as in gemm.h: the caller owns every buffer,
  * the library allocates no device memory and never synchronizes; plans are
@@ -112,7 +115,8 @@ gemm_status gemm_mx_plan_create_for(const gemm_mx_problem* prob, const gemm_devi
 void gemm_mx_plan_destroy(gemm_mx_plan* plan);
 
 /* The configuration a plan runs: kernel = 4 (block-scaled tile kernel) or 5
- * (register-direct kernel), bk = k per K step in elements, mfma = 32 (32x32x64 scaled instruction),
+ * (register-direct kernel, when forced), bk = k per K step in elements,
+ * mfma = 32 (32x32x64 scaled instruction),
  * splitk = K slices across workgroups (their fp32 partial tiles summed in
  * slice order by the last workgroup of each tile: deterministic). */
 gemm_status gemm_mx_plan_config(const gemm_mx_plan* plan, gemm_config* out);

@@ -502,22 +502,35 @@ def test_static_scratch_entry_point_rejects_large_workspaces_before_any_device_c
     assert str(need.value) in msg and str(g.GEMM_STATIC_SCRATCH_BYTES) in msg, msg
 
 
-def test_mx_routes_fp6_and_mixed_widths_to_the_direct_kernel():
-    """Pairs of one width (8-bit, or E2M1) run the LDS-staged tile kernel
-    (kernel 4); FP6 operands and operands of different widths run the
-    register-direct kernel (kernel 5, 128 x 128 tiles, no K slices); either
-    may be forced where it applies."""
+def test_mx_routes_every_pair_to_the_tile_kernel():
+    """Every pair of formats runs the LDS-staged tile kernel (kernel 4): pairs
+    of one width (8-bit, or E2M1) over the whole ladder, the others (an FP6
+    operand, or 8-bit with 4-bit) over its square tiles and the decode slab,
+    with K slices where the planner takes them; the register-direct kernel
+    (kernel 5) only when forced, for any pair."""
     dev = fake_gfx950()
     for fa, fb in (("e4m3", "e4m3"), ("e5m2", "e4m3"), ("e2m1", "e2m1")):
         assert mx.gemm_mx_plan_create_for(mx.mx_problem(4096, 4096, 4096, fa, fb), dev).config.kernel == 4
     for fa, fb in (("e2m3", "e2m3"), ("e3m2", "e2m3"), ("e4m3", "e2m1"), ("e2m1", "e5m2"), ("e3m2", "e4m3")):
-        pl = mx.gemm_mx_plan_create_for(mx.mx_problem(4096, 4096, 4096, fa, fb), dev)
-        c = pl.config
-        assert (c.kernel, c.bm, c.bn, c.splitk) == (5, 128, 128, 1), (fa, fb, pl.describe())
-        assert "gemm_mx_direct_kernel<%d,%d>" % (mx.FORMATS[fa], mx.FORMATS[fb]) in pl.describe()
+        for (M, N, K), tile in (((4096, 4096, 4096), (256, 256)), ((1024, 1024, 4096), (64, 64)),
+                                ((2048, 2048, 4096), (128, 128)), ((16, 8192, 8192), (32, 64))):
+            pl = mx.gemm_mx_plan_create_for(mx.mx_problem(M, N, K, fa, fb), dev)
+            c = pl.config
+            assert (c.kernel, c.bm, c.bn) == (4, tile[0], tile[1]), (fa, fb, M, N, K, pl.describe())
+            assert "gemm_mx_kernel<%d,%d," % tile in pl.describe()
+            assert pl.describe().endswith("fmt=%d/%d out=1" % (mx.FORMATS[fa], mx.FORMATS[fb]))
+            assert c.bk == 128
+        # the decode slab slices K; deep K with few tiles slices 128 x 128 tiles
+        assert mx.gemm_mx_plan_create_for(mx.mx_problem(16, 8192, 8192, fa, fb), dev).config.splitk == 2
+        assert mx.gemm_mx_plan_create_for(mx.mx_problem(512, 512, 16384, fa, fb), dev).config.splitk >= 4
+        # tiles of the one-width ladder only
         with pytest.raises(g.GemmError) as e:
-            mx.gemm_mx_plan_create_for(mx.mx_problem(4096, 4096, 4096, fa, fb), dev, {"kernel": 4})
+            mx.gemm_mx_plan_create_for(mx.mx_problem(4096, 4096, 4096, fa, fb), dev, {"bm": 256, "bn": 128})
         assert e.value.status == g.GEMM_ERR_UNSUPPORTED
+        pl = mx.gemm_mx_plan_create_for(mx.mx_problem(4096, 4096, 4096, fa, fb), dev, {"kernel": 5})
+        assert (pl.config.kernel, pl.config.bm, pl.config.bn, pl.config.splitk) == (5, 128, 128, 1)
+        assert "gemm_mx_direct_kernel<%d,%d>" % (mx.FORMATS[fa], mx.FORMATS[fb]) in pl.describe()
+    assert mx.gemm_mx_plan_create_for(mx.mx_problem(4096, 4096, 4096, "e2m1", "e2m1"), dev).config.bk == 256
     forced = mx.gemm_mx_plan_create_for(mx.mx_problem(1024, 1024, 1024), dev, {"kernel": 5})
     assert forced.config.kernel == 5
     # FP6 rows: 3K/4 bytes, the default leading dimension

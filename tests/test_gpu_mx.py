@@ -316,24 +316,28 @@ def test_decode_slices_with_addend(out, splits):
 
 # ---------------------------------------------------------------- FP6 elements and mixed widths
 
-DIRECT_PAIRS = [("e2m3", "e2m3"), ("e3m2", "e3m2"), ("e2m3", "e3m2"), ("e4m3", "e2m1"), ("e2m1", "e4m3"),
-                ("e5m2", "e2m1"), ("e2m1", "e3m2"), ("e3m2", "e5m2"), ("e4m3", "e2m3")]
+MIXED_PAIRS = [("e2m3", "e2m3"), ("e3m2", "e3m2"), ("e2m3", "e3m2"), ("e4m3", "e2m1"), ("e2m1", "e4m3"),
+               ("e5m2", "e2m1"), ("e2m1", "e3m2"), ("e3m2", "e5m2"), ("e4m3", "e2m3")]
+# the tile kernel's variants for these pairs, and the register-direct kernel
+MIXED_TILES = [dict(kernel=4, bm=256, bn=256), dict(kernel=4, bm=128, bn=128), dict(kernel=4, bm=64, bn=64),
+               dict(kernel=4, bm=32, bn=64), dict(kernel=5)]
+# rows padded to a multiple of 16 bytes (an FP6 row is 3K/4 bytes) with 0xFF
+_pad16 = lambda x: np.concatenate([x, np.full((x.shape[0], -x.shape[1] % 16), 0xFF, np.uint8)], 1)
 
 
-@pytest.mark.parametrize("fa,fb", DIRECT_PAIRS)
+@pytest.mark.parametrize("fa,fb", MIXED_PAIRS)
 def test_fp6_and_mixed_widths_match_oracle(fa, fb):
-    """FP6 operands and operands of different widths (the register-direct
-    kernel): ragged M / N, a K that ends inside the instruction's 64 k, every
-    output type, with and without an addend."""
-    # rows padded to a multiple of 16 bytes (an FP6 row is 3K/4 bytes) with 0xFF
-    pad16 = lambda x: np.concatenate([x, np.full((x.shape[0], -x.shape[1] % 16), 0xFF, np.uint8)], 1)
-    for (M, N, K) in [(200, 136, 736), (129, 257, 160), (1, 1, 32), (64, 300, 4096)]:
+    """FP6 operands and operands of different widths through the planner (the
+    tile kernel, each operand staged in rows of its own width): ragged M / N,
+    a K that ends inside a K step and inside a 16-byte chunk of FP6 bytes,
+    every output type, with and without an addend."""
+    for (M, N, K) in [(200, 136, 736), (129, 257, 160), (1, 1, 32), (64, 300, 4096), (300, 520, 1056)]:
         A, SA, B, SB = _case(M, N, K, fa, fb, M + N + K)
-        A, B = pad16(A), pad16(B)
+        A, B = _pad16(A), _pad16(B)
         for out in ("bf16", "f16", "f32"):
             C = torch.from_numpy(np.random.default_rng(K).standard_normal((M, N)).astype(np.float32)).to(OUT[out])
             for c in (None, C):
-                print("mx direct", fa, fb, M, N, K, out, c is not None, flush=True)
+                print("mx pair", fa, fb, M, N, K, out, c is not None, flush=True)
                 D = mx.mx_matmul(_dev(A), _dev(SA), _dev(B), _dev(SB), K, fa, fb, out_dtype=OUT[out],
                                  C=c.cuda() if c is not None else None)
                 torch.cuda.synchronize()
@@ -341,6 +345,47 @@ def test_fp6_and_mixed_widths_match_oracle(fa, fb):
                 ref, S, S8 = oracle.mx_gemm_f64(A, SA, B, SB, K, fa, fb, cref, runs=True)
                 assert torch.isfinite(D.float()).all()
                 _check(D, ref, S, S8, out, "%s x %s %dx%dx%d out %s c=%d" % (fa, fb, M, N, K, out, c is not None))
+
+
+@pytest.mark.parametrize("fa,fb", MIXED_PAIRS)
+def test_fp6_and_mixed_widths_every_variant(fa, fb):
+    """Each compiled variant for these pairs, forced, on a ragged shape with
+    several K steps and a K tail inside an FP6 chunk, with an addend; the tile
+    variants of one K partition agree bit for bit."""
+    M, N, K = 300, 200, 1056
+    A, SA, B, SB = _case(M, N, K, fa, fb, 77)
+    A, B = _pad16(A), _pad16(B)
+    C = torch.from_numpy(np.random.default_rng(3).standard_normal((M, N)).astype(np.float32)).to(torch.bfloat16)
+    ref, S, S8 = oracle.mx_gemm_f64(A, SA, B, SB, K, fa, fb, C.to(torch.float64).numpy(), runs=True)
+    bits = {}
+    for cfg in MIXED_TILES:
+        print("mx pair variant", fa, fb, cfg, flush=True)
+        D = mx.mx_matmul(_dev(A), _dev(SA), _dev(B), _dev(SB), K, fa, fb, C=C.cuda(), out_dtype=torch.bfloat16,
+                         config=cfg)
+        torch.cuda.synchronize()
+        _check(D, ref, S, S8, "bf16", "%s x %s %s" % (fa, fb, cfg))
+        if cfg.get("kernel") == 4:
+            bits[str(cfg)] = gemm_inputs.bits(D.cpu())
+    vals = list(bits.values())
+    assert all(np.array_equal(vals[0], v) for v in vals[1:])
+
+
+@pytest.mark.parametrize("fa,fb", [("e2m3", "e2m3"), ("e4m3", "e2m1"), ("e3m2", "e2m1")])
+@pytest.mark.parametrize("splits", [2, 5])
+def test_fp6_and_mixed_widths_k_slices(fa, fb, splits):
+    """K slices across workgroups for these pairs: the decode slab and the
+    128 x 128 tile, with an addend, fp32 output."""
+    for (M, N, K), cfg in (((20, 520, 2560 + 32), dict(kernel=4, bm=32, bn=64, splitk=splits)),
+                           ((136, 264, 4096 + 96), dict(kernel=4, bm=128, bn=128, splitk=splits))):
+        A, SA, B, SB = _case(M, N, K, fa, fb, 31 + splits)
+        A, B = _pad16(A), _pad16(B)
+        C = torch.from_numpy(np.random.default_rng(5).standard_normal((M, N)).astype(np.float32))
+        ref, S, S8 = oracle.mx_gemm_f64(A, SA, B, SB, K, fa, fb, C.to(torch.float64).numpy(), runs=True)
+        print("mx pair slices", fa, fb, M, N, K, cfg, flush=True)
+        D = mx.mx_matmul(_dev(A), _dev(SA), _dev(B), _dev(SB), K, fa, fb, C=C.cuda(), out_dtype=torch.float32,
+                         config=cfg)
+        torch.cuda.synchronize()
+        _check(D, ref, S, S8, "f32", "%s x %s slices %s" % (fa, fb, cfg))
 
 
 @pytest.mark.parametrize("fa,fb", [("e4m3", "e4m3"), ("e2m1", "e2m1"), ("e5m2", "e4m3")])
@@ -356,11 +401,14 @@ def test_direct_kernel_forced_on_single_width_pairs(fa, fb):
     _check(D, ref, S, S8, "bf16", "forced direct %s x %s" % (fa, fb))
 
 
-@pytest.mark.parametrize("fa,fb", [("e2m3", "e3m2"), ("e4m3", "e2m1")])
-def test_direct_kernel_padding_never_enters_a_sum(fa, fb):
+@pytest.mark.parametrize("fa,fb", [("e2m3", "e3m2"), ("e4m3", "e2m1"), ("e2m3", "e2m3"), ("e3m2", "e4m3")])
+@pytest.mark.parametrize("force", [None, {"kernel": 5}, {"kernel": 4, "bm": 32, "bn": 64}])
+def test_padding_never_enters_a_sum(fa, fb, force):
     """Row bytes past K hold 0xFF (the most negative FP6 / FP4 magnitudes, a
     NaN in E4M3) and scale bytes past ceil(K/32) the NaN code: every output
-    stays finite and inside the bound with K ending mid-instruction."""
+    stays finite and inside the bound with K ending inside a K step and, for
+    FP6 rows, inside a 16-byte chunk (the tile kernel loads that chunk whole
+    and gives the block past K a zero scale)."""
     M, N, K = 136, 200, 736
     A0, SA0, B0, SB0 = _case(M, N, K, fa, fb, 9)
     pad = lambda x, extra, fill: np.concatenate([x, np.full((x.shape[0], extra), fill, np.uint8)], 1)
@@ -368,20 +416,22 @@ def test_direct_kernel_padding_never_enters_a_sum(fa, fb):
     SA, SB = pad(SA0, 8, 0xFF), pad(SB0, 4, 0xFF)
     p = mx.mx_problem(M, N, K, fa, fb, mx.GEMM_MX_OUT_BF16, lda=A.shape[1], ldb=B.shape[1], ldsa=SA.shape[1],
                       ldsb=SB.shape[1])
-    pl = mx.gemm_mx_plan_create(p, 0)
+    pl = mx.gemm_mx_plan_create(p, 0, force)
+    print("mx padded", fa, fb, pl.describe(), flush=True)
     D = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
     dA, dSA, dB, dSB = _dev(A), _dev(SA), _dev(B), _dev(SB)
+    ws, wsb = mx._workspace(pl, 0, torch.cuda.current_stream().cuda_stream)
     st = mx.mxlib().gemm_mx_run(pl.handle, dA.data_ptr(), dSA.data_ptr(), dB.data_ptr(), dSB.data_ptr(), None,
-                                D.data_ptr(), None, 0, torch.cuda.current_stream().cuda_stream)
+                                D.data_ptr(), ws, wsb, torch.cuda.current_stream().cuda_stream)
     assert st == 0, g.gemm_last_error()
     torch.cuda.synchronize()
     assert torch.isfinite(D.float()).all()
     ref, S, S8 = oracle.mx_gemm_f64(A0, SA0, B0, SB0, K, fa, fb, runs=True)
-    _check(D, ref, S, S8, "bf16", "padded direct %s x %s" % (fa, fb))
+    _check(D, ref, S, S8, "bf16", "padded %s x %s %s" % (fa, fb, force))
 
 
 @pytest.mark.parametrize("name", ["mx_e2m3_4096", "mx_e4m3xe2m1_4096"])
-def test_direct_workloads_sampled(name):
+def test_fp6_and_mixed_workloads_sampled(name):
     w = gemm_inputs.MX_WORKLOADS[name]
     A, SA, B, SB, _ = gemm_inputs.make_mx(w)
     D = mx.mx_matmul(_dev(A), _dev(SA), _dev(B), _dev(SB), w.K, w.fmt_a, w.fmt_b, out_dtype=torch.bfloat16)
