@@ -81,7 +81,8 @@ def test_random_problem_matches_oracle(case):
 
 def _mx_cases(n=max(8, N_CASES // 3), seed=77 + SEED):
     rng = np.random.default_rng(seed)
-    pairs = [("e4m3", "e4m3"), ("e5m2", "e5m2"), ("e4m3", "e5m2"), ("e5m2", "e4m3"), ("e2m1", "e2m1")]
+    fmts = ["e4m3", "e5m2", "e2m3", "e3m2", "e2m1"]
+    pairs = [(a, b) for a in fmts for b in fmts]       # every pair of element formats
     out = []
     for i in range(n):
         fa, fb = pairs[int(rng.integers(len(pairs)))]
@@ -100,6 +101,9 @@ def test_random_block_scaled_problem_matches_oracle(case):
     seed = (M * 31 + N * 131 + K) % (1 << 31)
     A, SA = gemm_inputs.draw_mx(M, K, fa, seed)
     B, SB = gemm_inputs.draw_mx(N, K, fb, seed + 1)
+    # rows to a multiple of 16 bytes (FP6 rows are 3K/4 bytes), padded with 0xFF
+    pad16 = lambda x: np.concatenate([x, np.full((x.shape[0], -x.shape[1] % 16), 0xFF, np.uint8)], 1)
+    A, B = pad16(A), pad16(B)
     dev = [torch.from_numpy(np.ascontiguousarray(x)).cuda() for x in (A, SA, B, SB)]
     print("fuzz mx", case, flush=True)
     D = mx.mx_matmul(dev[0], dev[1], dev[2], dev[3], K, fa, fb, out_dtype=torch.bfloat16)
