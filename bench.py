@@ -201,9 +201,21 @@ def time_region(launch, steps, warmup):
     return s.elapsed_time(e) / steps
 
 
-def batch_times(launch, batch, rounds):
-    """Per-launch ms of `rounds` batches of `batch` launches (for median/spread)."""
+def batch_times(launch, batch, rounds, back_to_back=False):
+    """Per-launch ms of `rounds` batches of `batch` launches (for median/spread).
+    back_to_back: the batches are enqueued one after another with an event
+    between each two and the host waits once at the end, so the GPU never
+    idles between them (the regime of a long timed region); otherwise the
+    host waits after every batch (interleaved comparisons of variants)."""
     import torch
+    if back_to_back:
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(rounds + 1)]
+        ev[0].record()
+        for r in range(rounds):
+            launch(batch)
+            ev[r + 1].record()
+        ev[-1].synchronize()
+        return [ev[r].elapsed_time(ev[r + 1]) / batch for r in range(rounds)]
     out = []
     for _ in range(rounds):
         s = torch.cuda.Event(enable_timing=True)
@@ -231,13 +243,18 @@ def batch_len(launch, target_ms=1.0, least=10):
 
 def headline_times(launch, steps, warmup, rounds):
     """The headline measurement of one kernel, in one warm regime:
-    `rounds` batches of >= 1 ms (>= 10 launches) each timed between two
-    events on the launch stream, for the median and its spread; then the
-    timed region proper, `warmup` untimed launches and exactly `steps`
-    launches between two events (ms_per_step).  Returns (ms_per_step,
-    stats of the batches with the batch length added)."""
+    `rounds` batches of >= 1 ms (>= 10 launches) enqueued back to back with
+    an event on the launch stream between each two, for the median and its
+    spread; then the timed region proper, `warmup` untimed launches and
+    exactly `steps` launches between two events (ms_per_step).  Before the
+    batches, ~100 ms of untimed launches let the clock settle (timed from a
+    cold start, the first batches ran ~10 % slower than the region).
+    Returns (ms_per_step, stats of the batches with the batch length
+    added)."""
     batch = batch_len(launch)
-    st = stats(batch_times(launch, batch, rounds))
+    # ~100 ms of untimed launches first: the clock settles before anything is timed
+    launch(max(warmup, batch * 100))
+    st = stats(batch_times(launch, batch, rounds, back_to_back=True))
     st["batch_launches"] = batch
     ms = time_region(launch, steps, warmup)
     return ms, st
