@@ -647,7 +647,11 @@ def mx_sweep(args):
         "mx_e2m1_16x8192x8192": [dict()] + [dict(bm=32, bn=64, splitk=k) for k in (1, 3, 4, 8)],
         "mx_e4m3_4096": [dict()] + [dict(bm=bm, bn=bn) for (bm, bn) in ((256, 128), (128, 256), (128, 128))],
         "mx_e2m1_4096": [dict()] + [dict(bm=bm, bn=bn) for (bm, bn) in ((256, 128), (128, 256), (128, 128))],
+        # FP6 and mixed widths: the planned tile kernel, its 128 x 128 tile and the register-direct kernel
+        "mx_e2m3_4096": [dict(), dict(kernel=4, bm=128, bn=128), dict(kernel=5)],
+        "mx_e4m3xe2m1_4096": [dict(), dict(kernel=4, bm=128, bn=128), dict(kernel=5)],
     }
+    rows = []
     for name, variants in cases.items():
         w = gemm_inputs.MX_WORKLOADS[name]
         A, SA, B, SB, _ = gemm_inputs.make_mx(w)
@@ -687,9 +691,14 @@ def mx_sweep(args):
             s = stats(times[i])
             ms = s["median_ms"]
             rec = {"workload": name, "variant": v, "plan": pl.describe(), "us": ms * 1e3, "spread": s["spread"],
+                   "p25_us": s["p25_ms"] * 1e3, "p75_us": s["p75_ms"] * 1e3,
                    "tflops": w.flops() / ms / 1e9, "gbs": w.bytes() / ms / 1e6}
+            rows.append(rec)
             print(json.dumps(rec), flush=True)
         del Bs
+    if args.save:
+        save_rows(args.save, rows, "block-scaled workloads: planned plan beside other tiles, K-slice counts and "
+                                   "kernels, %d interleaved rounds of 20-launch batches" % args.rounds)
 
 
 PEAK_I8_TOPS = 5000.0   # MI355X dense int8 matrix peak (2:1 sparsity excluded)
