@@ -101,30 +101,32 @@ __device__ __forceinline__ int mx_logical(int pc, int r) {
 //  - 8 bits: two 16-byte reads, bytes 0-15 and 16-31 of one instruction's operand;
 //  - 4 bits, two instructions per sub-step: one 16-byte read per instruction;
 //  - 4 bits, one instruction: one 16-byte read (register dwords 4-7 unused);
-//  - 6 bits: three 8-byte reads, the 24 bytes of one 32-k block (dwords 6-7 unused).
+//  - 6 bits: the 24 bytes of one 32-k block (dwords 6-7 unused) as a 16-byte
+//    and an 8-byte read: a block of even index starts a 16-byte chunk (a whole
+//    chunk, then the first half of the next), one of odd index starts in the
+//    middle of one (its second half, then the next chunk whole).  P is the
+//    block parity, that of the sub-step.
 // The operand tuple is assembled where the instruction uses it, after the
 // reads have been waited for (the reads are asm whose results the compiler
 // takes as ready at once, so no copy of them may come earlier).
 template <int BITS, int MPS>
 struct MxFrag {
-    static constexpr bool WIDE = BITS != 6;
-    static constexpr int NR = BITS == 6 ? 3 : (BITS == 4 && MPS == 1 ? 1 : 2);
-    u32x4 w[WIDE ? NR : 1];
-    u32x2 n[WIDE ? 1 : NR];
-    template <int R, int OFF>
+    static constexpr int NR = BITS == 4 && MPS == 1 ? 1 : 2;
+    u32x4 w[BITS == 6 ? 1 : NR];
+    u32x2 n;   // 6 bits: the 8-byte half
+    template <int R, int OFF, int P>
     __device__ __forceinline__ void read(uint32_t addr) {
-        if constexpr (WIDE) w[R] = lds_read16_any<OFF>(addr);
-        else n[R] = lds_read8_any<OFF>(addr);
+        if constexpr (BITS != 6) w[R] = lds_read16_any<OFF>(addr);
+        else if constexpr (R == 1 - P) n = lds_read8_any<OFF>(addr);
+        else w[0] = lds_read16_any<OFF>(addr);
     }
     __device__ __forceinline__ void tie_all() {
 #pragma unroll
-        for (int r = 0; r < NR; ++r) {
-            if constexpr (WIDE) tie(w[r]);
-            else tie(n[r]);
-        }
+        for (int r = 0; r < (BITS == 6 ? 1 : NR); ++r) tie(w[r]);
+        if constexpr (BITS == 6) tie(n);
     }
     // operand of instruction H of the sub-step
-    template <int H>
+    template <int H, int P>
     __device__ __forceinline__ i32x8 operand() const {
         if constexpr (BITS == 8) {
             return __builtin_shufflevector(__builtin_bit_cast(i32x4, w[0]), __builtin_bit_cast(i32x4, w[1]), 0, 1,
@@ -133,9 +135,10 @@ struct MxFrag {
             const i32x4 v = __builtin_bit_cast(i32x4, w[MPS == 2 ? H : 0]);
             return __builtin_shufflevector(v, v, 0, 1, 2, 3, -1, -1, -1, -1);
         } else {
-            const i32x4 lo = __builtin_bit_cast(i32x4, __builtin_shufflevector(n[0], n[1], 0, 1, 2, 3));
-            const i32x4 hi = __builtin_bit_cast(i32x4, __builtin_shufflevector(n[2], n[2], 0, 1, -1, -1));
-            return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            const i32x4 v = __builtin_bit_cast(i32x4, w[0]);
+            const i32x4 h = __builtin_bit_cast(i32x4, __builtin_shufflevector(n, n, 0, 1, -1, -1));
+            if constexpr (P == 0) return __builtin_shufflevector(v, h, 0, 1, 2, 3, 4, 5, -1, -1);
+            else return __builtin_shufflevector(h, v, 0, 1, 4, 5, 6, 7, -1, -1);
         }
     }
 };
@@ -459,9 +462,14 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mx_kernel(MxArgs p) {
         } else if constexpr (BITS == 4) {
             c = g * NKI + MPS * ks + r;
         } else {
-            const int o = 24 * (g * NKI + ks) + 8 * r;
-            c = o >> 4;
-            half = (o >> 3) & 1;
+            // block g NKI + ks (of parity ks & 1): read r of it (see MxFrag)
+            const int c0 = 3 * ((g * NKI + ks) >> 1);
+            if ((ks & 1) == 0) {
+                c = c0 + r;                 // chunk c0 whole, then the first half of c0 + 1
+            } else {
+                c = c0 + 1 + r;             // the second half of c0 + 1, then c0 + 2 whole
+                half = r == 0 ? 1 : 0;
+            }
         }
         return smem0 + base + fr * rowb + mx_phys<CH>(c, fr) * 16 + 8 * half;
     };
@@ -495,10 +503,10 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mx_kernel(MxArgs p) {
         constexpr int RR = decltype(r_tag)::value;
         if constexpr (RR < FN * RB) {
             constexpr int J = RR / RB, H = RR % RB;
-            fb[SL][J].template read<H, S * SB_B + J * 32 * ROWBB>(b_addr[KS][H]);
+            fb[SL][J].template read<H, S * SB_B + J * 32 * ROWBB, (KS & 1)>(b_addr[KS][H]);
         } else if constexpr (RR < NRF) {
             constexpr int I = (RR - FN * RB) / RA, H = (RR - FN * RB) % RA;
-            fa[SL][I].template read<H, S * SA_B + I * 32 * ROWA>(a_addr[KS][H]);
+            fa[SL][I].template read<H, S * SA_B + I * 32 * ROWA, (KS & 1)>(a_addr[KS][H]);
         } else if constexpr (RR - NRF < FN) {
             constexpr int J = RR - NRF;
             if constexpr (NKI == 2) ssb[TS][J] = lds_read_u16<S * SSB_B + J * 32 * NBLK>(sb_addr);
@@ -541,14 +549,15 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mx_kernel(MxArgs p) {
         constexpr int Q = decltype(q_tag)::value;
         if constexpr (MPS == 1) {
             constexpr int I = Q / FN, J = Q % FN;
-            acc[I][J] = mfma_mx<FB, FA, KS>(fb[SL][J].template operand<0>(), fa[SL][I].template operand<0>(),
+            acc[I][J] = mfma_mx<FB, FA, KS>(fb[SL][J].template operand<0, (KS & 1)>(),
+                                            fa[SL][I].template operand<0, (KS & 1)>(),
                                             static_cast<int>(ssb[TS][J]), static_cast<int>(ssa[TS][I]), acc[I][J]);
         } else {
             // all blocks of half 0, then of half 1: an accumulator's two
             // instructions are FM * FN instructions apart
             constexpr int H = Q / (FM * FN), I = (Q % (FM * FN)) / FN, J = Q % FN;
-            acc[I][J] = mfma_mx<FB, FA, MPS * KS + H>(fb[SL][J].template operand<H>(),
-                                                      fa[SL][I].template operand<H>(), static_cast<int>(ssb[TS][J]),
+            acc[I][J] = mfma_mx<FB, FA, MPS * KS + H>(fb[SL][J].template operand<H, 0>(),
+                                                      fa[SL][I].template operand<H, 0>(), static_cast<int>(ssb[TS][J]),
                                                       static_cast<int>(ssa[TS][I]), acc[I][J]);
         }
     };
