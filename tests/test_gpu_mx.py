@@ -319,8 +319,9 @@ def test_decode_slices_with_addend(out, splits):
 MIXED_PAIRS = [("e2m3", "e2m3"), ("e3m2", "e3m2"), ("e2m3", "e3m2"), ("e4m3", "e2m1"), ("e2m1", "e4m3"),
                ("e5m2", "e2m1"), ("e2m1", "e3m2"), ("e3m2", "e5m2"), ("e4m3", "e2m3")]
 # the tile kernel's variants for these pairs, and the register-direct kernel
-MIXED_TILES = [dict(kernel=4, bm=256, bn=256), dict(kernel=4, bm=128, bn=128), dict(kernel=4, bm=64, bn=64),
-               dict(kernel=4, bm=32, bn=64), dict(kernel=5)]
+MIXED_TILES = [dict(kernel=4, bm=256, bn=256), dict(kernel=4, bm=256, bn=256, stages=2),
+               dict(kernel=4, bm=128, bn=128), dict(kernel=4, bm=64, bn=64), dict(kernel=4, bm=32, bn=64),
+               dict(kernel=5)]
 # rows padded to a multiple of 16 bytes (an FP6 row is 3K/4 bytes) with 0xFF
 _pad16 = lambda x: np.concatenate([x, np.full((x.shape[0], -x.shape[1] % 16), 0xFF, np.uint8)], 1)
 
