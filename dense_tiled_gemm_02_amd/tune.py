@@ -297,11 +297,13 @@ def sweep(shapes, rounds, out_path):
 
 def table_lines(doc):
     """The initializers of the winning shapes of a (merged) sweep document."""
-    lines = []
+    lines, keys = [], set()
     for name, s in sorted(doc["shapes"].items()):
         w = s["winner"]
-        if not w:
+        key = (s["M"], s["N"], s["K"], s["dtype"], bool(s["has_c"]))
+        if not w or key in keys:       # one entry per key (a shape raced under two names)
             continue
+        keys.add(key)
         dt = 1 if s["dtype"] == "bf16" else 0
         lines.append("{%d, %d, %d, %d, %d, {%d, %d, %d, %d, %d, %d, %d, %d, %d, 0, %d}, %d, 1},   // %s: %.1f us "
                      "(heuristic %.1f us)" % (s["M"], s["N"], s["K"], dt, int(s["has_c"]), w["bm"], w["bn"], w["bk"],
