@@ -265,18 +265,37 @@ gemm_config heuristic(const gemm_problem* p, const gemm_device_info& dev, int* g
     *group_m = 8;
     if (M <= 32 && kernel_layout(p) == 0) {
         // Decode regime, bucketed by M: 16-row slabs for M <= 16, 32-row slabs
-        // (two MFMA row blocks) for M <= 32.  Stream B.  Each workgroup reads
-        // a 256-byte band of every row of its K slice (HBM needs >= 128-byte
-        // runs), and the K slices supply the
-        // workgroups: S = CUs / slabs (one workgroup per CU: these kernels
-        // hold most of the LDS), at most 8, each slice >= 512 k.
+        // (two MFMA row blocks) for M <= 32.  Stream B: each workgroup reads a
+        // band of every row of its K slice, and the slices supply the
+        // workgroups (one per CU: these kernels hold most of the LDS).  The
+        // slab is the widest of 128, 64 and 32 columns (256-, 128- and 64-byte
+        // bands) whose slabs fill the CUs with 4 K slices, then S = CUs /
+        // slabs, at most 8, each slice >= 512 k.  Four slices is where the
+        // per-slice exchange and the streaming balance: swept at M in {1, 4,
+        // 16, 32} x N = K in {2048, 4096, 8192} (bf16, every compiled decode
+        // variant, interleaved races), the winners at M <= 16 are 128-column
+        // slabs with 4 slices at 8192 (29.2 us), 64-column slabs of 4 waves with
+        // 4 slices at 4096 (11.4 us; 128 columns with 8 slices 12.2 us) and
+        // 32-column slabs with 4 slices at 2048 (6.8-7.0 us; 128 columns with
+        // 4 slices, i.e. a quarter of the CUs, 8.1-8.8 us).
         if (allow_ws && cdiv(N, 128) <= 4096) {
-            const int64_t slabs = cdiv(N, 128);
+            const int64_t s_max = K / 512 < 4 ? (K / 512 > 1 ? K / 512 : 1) : 4;
+            int bn = 32;
+            for (int w : {128, 64}) {
+                if (cdiv(N, w) * s_max >= dev.cu_count) {
+                    bn = w;
+                    break;
+                }
+            }
+            const int64_t slabs = cdiv(N, bn);
             int64_t s = dev.cu_count / (slabs > 0 ? slabs : 1);
             if (s > 8) s = 8;
             while (s > 1 && K / s < 512) --s;
             if (s < 1) s = 1;
-            gemm_config c = cfg_of(dtg::KF_SKINNY, M <= 16 ? 16 : 32, 128, 32, 2, 16, 1, 8);
+            const int bm = M <= 16 ? 16 : 32;
+            gemm_config c = bn == 128  ? cfg_of(dtg::KF_SKINNY, bm, 128, 32, 2, 16, 1, 8)
+                            : bn == 64 ? cfg_of(dtg::KF_SKINNY, bm, 64, bm == 16 ? 64 : 32, 3, 16, 1, bm == 16 ? 4 : 8)
+                                       : cfg_of(dtg::KF_SKINNY, bm, 32, bm == 16 ? 64 : 32, 3, 16, 1, 8);
             c.splitk = static_cast<int32_t>(s);
             return c;
         }
