@@ -375,6 +375,24 @@ gemm_config heuristic(const gemm_problem* p, const gemm_device_info& dev, int* g
         if (s > 16) s = 16;
         const double steps = static_cast<double>(nkt);
         if (s > 1 && split.cost * steps / static_cast<double>(s) + 3.3 < best_t * steps) {
+            // When K allows the 128 x 128 tiles only a few slices (<= 4) and
+            // the 4-wave 64 x 64 tiles can still take two or more, the
+            // smaller tile's slices win: swept (bf16, every compiled
+            // variant, interleaved races) 64 x 4096^2 11.1 us with 4 of them
+            // (128 x 128 with 4 slices 16.1), 64 x 8192^2 25.1 us with 2
+            // (30.3), 128 x 4096^2 13.9 us with 2 (16.5); with many slices
+            // the larger tile stays (512^2 x 32768: 128 x 128 with 16 slices
+            // 35.1 us, 64 x 64 with 4 41.3).
+            const C& small = ladder[5];
+            const int64_t tiles64 = cdiv(M, small.bm) * cdiv(N, small.bn);
+            int64_t s64 = dev.cu_count / tiles64;
+            if (s64 > nkt / 16) s64 = nkt / 16;
+            if (s64 > 16) s64 = 16;
+            if (s <= 4 && s64 > 1 && tiles64 <= dtg::kMaxCounters) {
+                gemm_config c = cfg_of(small.fam, small.bm, small.bn, small.bk, small.st, small.mf, small.wm, small.wn);
+                c.splitk = static_cast<int32_t>(s64);
+                return c;
+            }
             gemm_config c = cfg_of(split.fam, split.bm, split.bn, split.bk, split.st, split.mf, split.wm, split.wn);
             c.splitk = static_cast<int32_t>(s);
             return c;

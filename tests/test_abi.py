@@ -413,10 +413,12 @@ def test_tile_choice_by_rounds_of_workgroups():
     assert (c.bm, c.bn, c.splitk) == (128, 128, 16)
     assert c.stages == 4                               # slices run the 4-stage tile, one workgroup per CU
     for shape, s in (((1024, 1024, 16384), 4), ((1024, 1024, 4096), 4), ((256, 8192, 8192), 2),
-                     ((64, 8192, 8192), 4), ((128, 4096, 4096), 4), ((768, 768, 8192), 7),
-                     ((192, 8192, 8192), 2)):
+                     ((768, 768, 8192), 7), ((192, 8192, 8192), 2)):
         c = plan(*shape).config                        # wide or deep problems with few 128 x 128 tiles
         assert (c.bm, c.bn, c.stages, c.splitk) == (128, 128, 4, s), shape
+    for shape, s in (((64, 8192, 8192), 2), ((128, 4096, 4096), 2), ((64, 4096, 4096), 4)):
+        c = plan(*shape).config                        # few slices of 128 x 128: 64 x 64 tiles slice K
+        assert (c.bm, c.bn, c.stages, c.splitk, c.waves_m, c.waves_n) == (64, 64, 4, s, 2, 2), shape
     c = plan(768, 768, 2048).config                    # two slices would not pay for the reduce
     assert (c.bm, c.bn, c.splitk) == (64, 64, 1)
     for ta, tb in ((True, False), (False, True), (True, True)):   # every layout has the ladder's variants

@@ -131,7 +131,25 @@ def _variants(dt):
 
 DMA_SPLIT = [(128, 128, 64, 2, 16, 2, 4), (128, 128, 64, 4, 16, 2, 4), (128, 128, 64, 2, 16, 2, 2),
              (128, 128, 64, 2, 32, 2, 2),
-             (128, 128, 64, 4, 16, 2, 2), (256, 128, 64, 2, 16, 4, 2), (128, 256, 64, 2, 16, 2, 4)]
+             (128, 128, 64, 4, 16, 2, 2), (256, 128, 64, 2, 16, 4, 2), (128, 256, 64, 2, 16, 2, 4),
+             (64, 64, 64, 4, 16, 2, 2)]
+
+
+@pytest.mark.parametrize("mnk", [(64, 4096, 4096), (128, 4096, 4096), (64, 8192, 8192), (96, 2000, 4136)])
+def test_planned_k_slices_of_small_tiles(mnk):
+    """Short, wide problems whose planned K slices run on 64 x 64 tiles: the
+    planner's plan, full parity with the oracle, with an addend, and the same
+    bits on a second run."""
+    M, N, K = mnk
+    A, B, C = _inputs(M, N, K, "bf16", True, seed=M + N + K)
+    ref, S = oracle.gemm_f64(gemm_inputs.bits(A), gemm_inputs.bits(B), gemm_inputs.bits(C), "bf16")
+    desc = g.plan_for(A.cuda(), B.cuda(), C.cuda()).describe()
+    print("planned", mnk, desc, flush=True)
+    D1 = gpu_run(A, B, C)
+    D2 = gpu_run(A, B, C)
+    n, worst, first = oracle.tol_check(gemm_inputs.bits(D1), ref, S, "bf16")
+    assert n == 0, "%s %s: %d outside the bound (worst %.3g, first %d)" % (mnk, desc, n, worst, first)
+    assert torch.equal(D1.view(torch.int16), D2.view(torch.int16)), (mnk, desc)
 
 
 @pytest.mark.parametrize("mnk", [(300, 200, 1000), (130, 264, 2056), (128, 128, 4096), (520, 264, 200)])
