@@ -232,6 +232,23 @@ def test_in_place_addend_allowed_only_with_equal_strides():
     assert "overlaps C" in e.value.detail
 
 
+def test_decode_slab_rule():
+    """M <= 32: the widest slab (128, 64 or 32 columns) whose slabs fill the
+    CUs with 4 K slices; 128-column slabs instead when they fill the CUs with
+    up to 8 slices of at least 1024 k (shapes outside the tuned table)."""
+    def slab(M, N, K):
+        c = plan(M, N, K).config
+        return (c.kernel, c.bm, c.bn, c.splitk)
+    assert slab(1, 2048, 2048) == (2, 16, 32, 4)
+    assert slab(16, 4096, 4096) == (2, 16, 64, 4)
+    assert slab(4, 8192, 8192) == (2, 16, 128, 4)
+    assert slab(8, 6144, 4096) == (2, 16, 64, 2)
+    assert slab(4, 4096, 6144) == (2, 16, 64, 4)       # 8 slices would be 768 k each
+    assert slab(4, 4096, 11008) == (2, 16, 128, 8)
+    assert slab(1, 4096, 14336) == (2, 16, 128, 8)
+    assert slab(24, 4096, 14336) == (2, 32, 128, 8)
+
+
 def test_split_k_plans_need_and_check_a_workspace():
     p = plan(16, 8192, 8192)
     c = p.config

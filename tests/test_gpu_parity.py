@@ -274,6 +274,18 @@ def test_decode_buckets(m):
     check(A, B, C, D1.cpu(), "bf16", label="decode one-shot M=%d" % m)
 
 
+@pytest.mark.parametrize("mnk", [(1, 4096, 11008), (16, 4096, 14336), (1, 4096, 8192), (16, 14336, 4096),
+                                 (4, 6144, 4096)])
+def test_decode_planned_shapes(mnk):
+    """The planned decode plans of long-K and wide shapes (128-column slabs
+    with 8 K slices, the tuned entries, unsliced 64-column slabs), every
+    output against the oracle."""
+    M, N, K = mnk
+    A, B, C = _inputs(M, N, K, "bf16", M % 2 == 0, seed=M + N + K, dist="normal", scale=1 / 64)
+    D = gpu_run(A, B, C)
+    check(A, B, C, D, "bf16", label="decode %s" % (mnk,))
+
+
 def test_skinny_workspace_reuse():
     """Slab counters reset themselves: many launches (and two plans) on one
     workspace all give the same, correct result."""

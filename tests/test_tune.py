@@ -100,12 +100,10 @@ def test_table_switch_restores_the_heuristic():
         pytest.skip("no tuned entries committed")
     doc = json.load(open(os.path.join(ROOT, "profiles", "tuned_table.json")))
     code = ("import json,sys; from dense_tiled_gemm_02_amd import tune; "
-            "print(json.dumps([tune.heuristic_config(*tune.NAMED[n]) if n in tune.NAMED else None "
-            "for n in sys.argv[1:]]))")
+            "print(json.dumps([tune.heuristic_config(*tune.parse_shape(n)[1]) for n in sys.argv[1:]]))")
     names = sorted(doc["shapes"])
     env = dict(os.environ, GEMM_TUNED_TABLE="0")
     out = subprocess.run([sys.executable, "-c", code] + names, cwd=ROOT, env=env, check=True,
                          stdout=subprocess.PIPE, text=True).stdout
     for n, h in zip(names, json.loads(out.strip().splitlines()[-1])):
-        if h is not None:
-            assert h == doc["shapes"][n]["heuristic"], n
+        assert h == doc["shapes"][n]["heuristic"], n
