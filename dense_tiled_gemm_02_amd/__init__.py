@@ -28,6 +28,8 @@ GEMM_XCD_OFF = 2
 GEMM_STATIC_SCRATCH_BYTES = 24 << 20   # include/gemm.h: the workspace gemm_run_static provides
 KERNEL_TILE = 1
 KERNEL_SKINNY = 2
+KERNEL_DMA = 3
+KERNEL_DMA_SK = 6   # stream-K: config.splitk is the workgroup count
 
 _i64 = ctypes.c_int64
 _i32 = ctypes.c_int32
@@ -86,6 +88,8 @@ SIGNATURES = [
     ("gemm_lds_bytes", _i64, [_i32, _i32, _i32, _i32, ctypes.c_int]),
     ("gemm_tile_of_workgroup", ctypes.c_int,
      [_i64, _i64, _i64, _i32, _i32, ctypes.POINTER(_i64), ctypes.POINTER(_i64)]),
+    ("gemm_streamk_pieces", ctypes.c_int,
+     [_i32, _i32, _i32, _i32, ctypes.POINTER(_i32), _i32, ctypes.POINTER(_i32)]),
     ("gemm_status_string", ctypes.c_char_p, [ctypes.c_int]),
     ("gemm_last_error", ctypes.c_char_p, []),
 ]
@@ -243,6 +247,15 @@ def gemm_tile_of_workgroup(wg, num_pid_m, num_pid_n, group_m, xcd_count):
     _check(lib().gemm_tile_of_workgroup(wg, num_pid_m, num_pid_n, group_m, xcd_count,
                                         ctypes.byref(pm), ctypes.byref(pn)))
     return pm.value, pn.value
+
+
+def gemm_streamk_pieces(tiles, k_steps, workgroups, wg):
+    """The pieces of stream-K range `wg`: (tile, kt0, kt1, part, nparts, slot) each."""
+    n = _i32()
+    _check(lib().gemm_streamk_pieces(tiles, k_steps, workgroups, wg, None, 0, ctypes.byref(n)))
+    buf = (_i32 * (6 * max(n.value, 1)))()
+    _check(lib().gemm_streamk_pieces(tiles, k_steps, workgroups, wg, buf, n.value, ctypes.byref(n)))
+    return [tuple(buf[6 * i:6 * i + 6]) for i in range(n.value)]
 
 
 # ---------------------------------------------------------------- torch convenience

@@ -26,7 +26,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libgemm.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "api_mx.cpp", "gemm_tile.hip", "gemm_dma.hip", "gemm_dma_more.hip", "gemm_dma_layouts.hip",
+SOURCES = ["api.cpp", "api_mx.cpp", "gemm_tile.hip", "gemm_dma.hip", "gemm_dma_more.hip", "gemm_dma_layouts.hip", "gemm_dma_sk.hip",
            "gemm_mx.hip", "gemm_mx_pairs.hip",
            "gemm_skinny.hip", "gemm_static.hip", "gemm_i8.hip",
            "gemm_mx_direct.hip"]

@@ -215,7 +215,7 @@ const dtg::KernelEntry* find_entry(const gemm_config& want, int dtype, int vec,
         if (e->dtype != dtype || e->vec != vec) continue;
         if (e->layout != -1 && e->layout != lay) continue;
         if (e->lds_bytes > dev.lds_per_wg) continue;
-        if (e->family == dtg::KF_DMA && !dma_offsets_ok(p, e)) continue;
+        if ((e->family == dtg::KF_DMA || e->family == dtg::KF_DMA_SK) && !dma_offsets_ok(p, e)) continue;
         if (e->family == dtg::KF_SKINNY && !skinny_offsets_ok(p, e)) continue;
         if (matches(e, want)) return e;
     }
@@ -407,6 +407,11 @@ gemm_config heuristic(const gemm_problem* p, const gemm_device_info& dev, int* g
             return c;
         }
     }
+    // Stream-K (kernel 6) is not planned: measured against these tiles it
+    // loses at every shape tried (3072^2 x 4096 113.6 us against 68.6 for
+    // 192 x 256, 5120^2 x 4096 261 against 172 for 256 x 256): each cut tile
+    // moves 256 KiB fp32 parts through memory, and ranges at staggered K
+    // offsets lose the L2 reuse of A and B panels that tiles in lockstep get.
     return cfg_of(best->fam, best->bm, best->bn, best->bk, best->st, best->mf, best->wm, best->wn);
 }
 
@@ -488,6 +493,19 @@ gemm_status plan_impl(const gemm_problem* given, const gemm_device_info* dev, co
         return fail(GEMM_ERR_UNSUPPORTED, "this skinny kernel runs M <= %d only (M=%lld)", e->bm,
                     (long long)prob->M);
     int splits = 1;
+    int64_t sk_groups = 0;   // stream-K: workgroups the (tile, K step) iterations are dealt to
+    if (e->family == dtg::KF_DMA_SK) {
+        if (!allow_ws) return fail(GEMM_ERR_UNSUPPORTED, "stream-K needs a workspace");
+        const int64_t total = cdiv(prob->M, e->bm) * cdiv(prob->N, e->bn) * cdiv(prob->K, e->bk);
+        sk_groups = want.splitk >= 1 ? want.splitk : dev->cu_count;
+        if (want.splitk < 1 && sk_groups > total / 16) sk_groups = total / 16;
+        if (sk_groups < 1) sk_groups = 1;
+        if (sk_groups > total || sk_groups > dtg::kMaxCounters || total * sk_groups >= (int64_t(1) << 31))
+            return fail(GEMM_ERR_UNSUPPORTED,
+                        "stream-K takes 1 to min(%d, tiles x K steps = %lld) workgroups, with tiles x K steps x "
+                        "workgroups below 2^31 (splitk=%d)",
+                        dtg::kMaxCounters, (long long)total, want.splitk);
+    }
     if (e->family == dtg::KF_SKINNY || e->family == dtg::KF_DMA) {
         splits = want.splitk > 0 ? want.splitk : 1;
         if (splits > 64) return fail(GEMM_ERR_UNSUPPORTED, "at most 64 K slices (splitk=%d)", splits);
@@ -506,10 +524,12 @@ gemm_status plan_impl(const gemm_problem* given, const gemm_device_info* dev, co
     pl->fallback = fb;
     pl->num_pid_m = cdiv(prob->M, e->bm);
     pl->num_pid_n = cdiv(prob->N, e->bn);
-    pl->grid = pl->num_pid_m * pl->num_pid_n * splits;
+    pl->grid = e->family == dtg::KF_DMA_SK ? sk_groups : pl->num_pid_m * pl->num_pid_n * splits;
     pl->ws_bytes = e->family == dtg::KF_SKINNY ? dtg::skinny_workspace_bytes(pl->num_pid_n, e->bm, e->bn, splits)
                    : e->family == dtg::KF_DMA
                        ? dtg::dma_workspace_bytes(pl->num_pid_m * pl->num_pid_n, e->bm, e->bn, splits)
+                   : e->family == dtg::KF_DMA_SK
+                       ? dtg::dma_sk_workspace_bytes(pl->num_pid_m * pl->num_pid_n, e->bm, e->bn, sk_groups)
                        : 0;
     if (pl->ws_bytes < 0) {
         delete pl;
@@ -522,7 +542,7 @@ gemm_status plan_impl(const gemm_problem* given, const gemm_device_info* dev, co
     if (group_m > pl->num_pid_m) group_m = static_cast<int>(pl->num_pid_m);
     gemm_config& c = pl->cfg;
     c = cfg_of(e->family, e->bm, e->bn, e->bk, e->stages, e->mfma, e->waves_m, e->waves_n);
-    c.splitk = splits;
+    c.splitk = e->family == dtg::KF_DMA_SK ? static_cast<int32_t>(sk_groups) : splits;
     c.group_m = group_m;
     c.xcd_remap = (xcd && dev->xcd_count > 1) ? GEMM_XCD_ON : GEMM_XCD_OFF;
     if (log_enabled()) {
@@ -751,7 +771,7 @@ gemm_status gemm_run(const gemm_plan* plan, const void* A, const void* B, const 
                    ? plan->cfg.splitk
                    : 1;   // the element-wise fallback runs the whole K range per tile
     a.ws = workspace;
-    const int64_t grid = static_cast<int64_t>(a.num_pid_m) * a.num_pid_n * a.splits;
+    const int64_t grid = e == plan->entry ? plan->grid : static_cast<int64_t>(a.num_pid_m) * a.num_pid_n;
     hipError_t err = e->launch(a, grid, static_cast<hipStream_t>(stream));
     if (err != hipSuccess) return fail(GEMM_ERR_HIP, "launch of %s: %s", e->name, hipGetErrorString(err));
     return ok();
@@ -814,6 +834,35 @@ gemm_status gemm_tile_of_workgroup(int64_t wg, int64_t num_pid_m, int64_t num_pi
     if (wg < 0 || wg >= num_pid_m * num_pid_n) return fail(GEMM_ERR_INVALID_ARG, "workgroup outside the grid");
     const int64_t gm = group_m < num_pid_m ? group_m : num_pid_m;   // as the planners clamp it
     dtg::tile_of_workgroup<int64_t>(wg, num_pid_m, num_pid_n, gm, xcd_count, pid_m, pid_n);
+    return ok();
+}
+
+gemm_status gemm_streamk_pieces(int32_t tiles, int32_t k_steps, int32_t workgroups, int32_t wg, int32_t* out,
+                                int32_t max_pieces, int32_t* count) {
+    if (!count || (max_pieces > 0 && !out)) return fail(GEMM_ERR_INVALID_ARG, "output pointer is NULL");
+    const int64_t total = static_cast<int64_t>(tiles) * k_steps;
+    if (tiles <= 0 || k_steps <= 0 || workgroups <= 0 || wg < 0 || wg >= workgroups || workgroups > total ||
+        total * workgroups >= (int64_t(1) << 31))
+        return fail(GEMM_ERR_INVALID_ARG, "need 0 <= wg < workgroups <= tiles x k_steps < 2^31 / workgroups");
+    const uint32_t T = static_cast<uint32_t>(total), W = static_cast<uint32_t>(workgroups);
+    uint32_t it = dtg::sk_range_start(static_cast<uint32_t>(wg), T, W);
+    const uint32_t end = dtg::sk_range_start(static_cast<uint32_t>(wg) + 1, T, W);
+    int32_t n = 0;
+    while (it < end) {
+        const dtg::SkPiece q = dtg::sk_piece(it, end, T, static_cast<uint32_t>(k_steps), W);
+        if (n < max_pieces) {
+            int32_t* o = out + 6 * n;
+            o[0] = static_cast<int32_t>(q.tile);
+            o[1] = static_cast<int32_t>(q.kt0);
+            o[2] = static_cast<int32_t>(q.kt1);
+            o[3] = static_cast<int32_t>(q.part);
+            o[4] = static_cast<int32_t>(q.nparts);
+            o[5] = q.nparts == 1 ? -1 : static_cast<int32_t>(q.part == 0 ? q.slot0 : q.slot1 + q.part);
+        }
+        ++n;
+        it = q.next;
+    }
+    *count = n;
     return ok();
 }
 

@@ -28,11 +28,17 @@ const KernelEntry kTable[] = {
 
 const KernelEntry* dma_kernel_table_more(int* count);
 const KernelEntry* dma_kernel_table_layouts(int* count);
+const KernelEntry* dma_kernel_table_sk(int* count);
 
 int64_t dma_workspace_bytes(int64_t tiles, int bm, int bn, int splits) {
     if (splits <= 1) return 0;
     if (tiles > kMaxCounters) return -1;
     return kCounterBytes + tiles * splits * static_cast<int64_t>(bm) * bn * 4;
+}
+
+int64_t dma_sk_workspace_bytes(int64_t tiles, int bm, int bn, int64_t workgroups) {
+    if (tiles > kMaxCounters) return -1;
+    return kCounterBytes + 2 * workgroups * static_cast<int64_t>(bm) * bn * 4;
 }
 
 const KernelEntry* dma_kernel_table(int* count) {
@@ -42,6 +48,8 @@ const KernelEntry* dma_kernel_table(int* count) {
         const KernelEntry* t = dma_kernel_table_more(&n);
         v.insert(v.end(), t, t + n);
         t = dma_kernel_table_layouts(&n);
+        v.insert(v.end(), t, t + n);
+        t = dma_kernel_table_sk(&n);
         v.insert(v.end(), t, t + n);
         return v;
     }();

@@ -101,8 +101,43 @@ constexpr int mix_loads(int O, int NR, int NL) {
     return -(O - loads_before) - 1;
 }
 
-template <int BM, int BN, int BK, int WM, int WN, int MF, int ST, int EL, bool TA, bool TB>
-__device__ __forceinline__ void dma_tile(const KArgs& p) {
+// What one call of the tile body computes: output tile `tile` (grouped order)
+// over its K steps [kt0, kt1), as part `part` of `nparts` (1: the whole K
+// range, written out directly).  With several parts, part j's fp32 partial
+// tile goes to workspace slot base + slot0 when j == 0 and base + slot1 + j
+// otherwise; slots base .. base + nslots - 1 are this work's to address.
+struct Work {
+    int tile, kt0, kt1, part, nparts, base, slot0, slot1, nslots;
+};
+
+// The work of a data-parallel or K-sliced launch: one workgroup per (K slice,
+// output tile); the XCD permutation runs over the whole grid, consecutive
+// positions are consecutive tiles (grouped order) of one slice.  With one
+// slice this is tile_of_workgroup.
+template <int BK>
+__device__ __forceinline__ Work slice_work(const KArgs& p) {
+    const int ntiles = p.num_pid_m * p.num_pid_n;
+    const int NS = p.splits;
+    const int pos = xcd_permute<int>(blockIdx.x, ntiles * NS, p.xcds);
+    const int slice = pos / ntiles;
+    Work w;
+    w.tile = pos - slice * ntiles;
+    const int nkt_all = (p.K + BK - 1) / BK;
+    const int per_slice = (nkt_all + NS - 1) / NS;
+    w.kt0 = slice * per_slice;
+    w.kt1 = (w.kt0 + per_slice < nkt_all) ? w.kt0 + per_slice : nkt_all;
+    w.part = slice;
+    w.nparts = NS;
+    w.base = w.tile * NS;
+    w.slot0 = w.slot1 = 0;
+    w.nslots = NS;
+    return w;
+}
+
+// XCH: the K-slice exchange is compiled for tiles of more than 64
+// accumulators per lane too (the stream-K variants).
+template <int BM, int BN, int BK, int WM, int WN, int MF, int ST, int EL, bool TA, bool TB, bool XCH = false>
+__device__ __forceinline__ void dma_tile(const KArgs& p, const Work& wk) {
     constexpr bool BF16 = EL == kElBF16;
     constexpr bool I8 = EL == kElI8;
     constexpr int NW = WM * WN;
@@ -127,23 +162,19 @@ __device__ __forceinline__ void dma_tile(const KArgs& p) {
 
     __shared__ __attribute__((aligned(1024))) uint16_t smem[ST * (SA + SB)];
 
-    const int tid = threadIdx.x;
+    int tid = threadIdx.x;
+    // Stream-K runs this body in a loop: an opaque lane index keeps the
+    // compiler from hoisting lane-dependent addresses (the epilogue's among
+    // them) out of that loop, where they would stay live through the K loop.
+    if constexpr (XCH) asm volatile("" : "+v"(tid));
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / WN, wn = wave % WN;
 
-    // Workgroup -> (K slice, output tile): the XCD permutation runs over the
-    // whole grid, consecutive positions are consecutive tiles (grouped order)
-    // of one slice.  With one slice this is tile_of_workgroup.
-    const int ntiles = p.num_pid_m * p.num_pid_n;
-    const int NS = p.splits;
-    int pid_m, pid_n, tile_lin, slice;
-    {
-        const int pos = xcd_permute<int>(blockIdx.x, ntiles * NS, p.xcds);
-        slice = pos / ntiles;
-        tile_lin = pos - slice * ntiles;
-        grouped_tile<int>(tile_lin, p.num_pid_m, p.num_pid_n, p.group_m, &pid_m, &pid_n);
-    }
+    const int NS = wk.nparts;
+    const int tile_lin = wk.tile, slice = wk.part;
+    int pid_m, pid_n;
+    grouped_tile<int>(tile_lin, p.num_pid_m, p.num_pid_n, p.group_m, &pid_m, &pid_n);
     const int m0 = pid_m * BM, n0 = pid_n * BN;
     const int M = p.M, N = p.N, K = p.K;
 
@@ -197,11 +228,8 @@ __device__ __forceinline__ void dma_tile(const KArgs& p) {
         __amdgpu_buffer_rsrc_t ra, rb;
         int k0;
     };
-    // this slice's K steps: [kt0, kt1)
-    const int nkt_all = (K + BK - 1) / BK;
-    const int per_slice = (nkt_all + NS - 1) / NS;
-    const int kt0 = slice * per_slice;
-    const int kt1 = (kt0 + per_slice < nkt_all) ? kt0 + per_slice : nkt_all;
+    // this part's K steps: [kt0, kt1)
+    const int kt0 = wk.kt0, kt1 = wk.kt1;
     const uint64_t a_full = 2u * static_cast<uint64_t>(AKC ? static_cast<int64_t>(M - 1 - m0) * lda + K
                                                            : static_cast<int64_t>(K - 1) * lda + (M - m0));
     const uint64_t b_full = 2u * static_cast<uint64_t>(BKC ? static_cast<int64_t>(N - 1 - n0) * ldb + K
@@ -496,27 +524,29 @@ __device__ __forceinline__ void dma_tile(const KArgs& p) {
     }
     if constexpr (AGPR) agpr_settle();
 
-    // ---- K slices across workgroups: publish this slice's fp32 partial tile;
-    // the workgroup that arrives last at the tile's counter sums the slices
-    // in slice order (so the result does not depend on arrival order) into
+    // ---- K slices across workgroups: publish this part's fp32 partial tile;
+    // the workgroup that arrives last at the tile's counter sums the parts
+    // in part order (so the result does not depend on arrival order) into
     // acc and goes on to the epilogue below; the others are done.  Partials
-    // are kept in register order, [tile][slice][wave][block][lane][4 floats],
-    // so each lane writes and reads back only its own 16-byte runs, with
+    // are kept in register order, [slot][wave][block][lane][4 floats], so
+    // each lane writes and reads back only its own 16-byte runs, with
     // system-coherent accesses (they bypass the per-XCD L2 caches); see
     // arrive_last for the ordering.
     constexpr int NB = FM * FN * (AccT<MF>::regs / 4);   // 16-byte runs per lane
-    // (two slices of partials are held in registers: only tiles of at most
-    // 64 accumulators per lane take K slices; the planner keeps the others at 1)
+    // (two units of partials are held in registers: only tiles of at most
+    // 64 accumulators per lane take K slices, or 128 in the XCH variants;
+    // the planner keeps the others at 1)
     static_assert(NB > 16 || !AGPR, "K slices keep their partials in VGPRs");
-    if constexpr (NB <= 16 && !I8) if (NS > 1) {
-        constexpr int64_t WAVE_F = static_cast<int64_t>(NB) * 64 * 4;   // floats per wave per slice
+    if constexpr ((NB <= 16 || (XCH && NB <= 32)) && !I8 && !AGPR) if (NS > 1) {
+        constexpr int64_t WAVE_F = static_cast<int64_t>(NB) * 64 * 4;   // floats per wave per slot
         int* counters = static_cast<int*>(p.ws);
-        float* tile_part = reinterpret_cast<float*>(static_cast<char*>(p.ws) + kCounterBytes) +
-                           static_cast<int64_t>(tile_lin) * NS * NW * WAVE_F;
+        float* parts = reinterpret_cast<float*>(static_cast<char*>(p.ws) + kCounterBytes) +
+                       static_cast<int64_t>(wk.base) * NW * WAVE_F;
         const __amdgpu_buffer_rsrc_t pr = __builtin_amdgcn_make_buffer_rsrc(
-            tile_part, 0, clamp_records(static_cast<int64_t>(NS) * NW * WAVE_F * 4), kRsrcWord3);
-        auto run_off = [&](int sl, int b) {   // byte offset of lane's run b of slice sl
-            return static_cast<uint32_t>(((static_cast<int64_t>(sl) * NW + wave) * WAVE_F + (b * 64 + lane) * 4) * 4);
+            parts, 0, clamp_records(static_cast<int64_t>(wk.nslots) * NW * WAVE_F * 4), kRsrcWord3);
+        auto run_off = [&](int sl, int b) {   // byte offset of lane's run b of part sl
+            const int slot = sl == 0 ? wk.slot0 : wk.slot1 + sl;
+            return static_cast<uint32_t>(((static_cast<int64_t>(slot) * NW + wave) * WAVE_F + (b * 64 + lane) * 4) * 4);
         };
         // run b = (i * FN + j) * G + g holds registers 4g..4g+3 of acc[i][j]
         constexpr int G = AccT<MF>::regs / 4;
@@ -539,10 +569,10 @@ __device__ __forceinline__ void dma_tile(const KArgs& p) {
                                                    run_off(slice, decltype(b_tag)::value), 0, kSysScope);
         });
         if (!arrive_last(&counters[tile_lin], NS, reinterpret_cast<int*>(smem))) return;
-        // Sum the slices in order into acc (this slice's own runs are read back
+        // Sum the parts in order into acc (this part's own runs are read back
         // like the others: the same bits).  Loads go in units of HB runs, the
         // next unit in flight while one is added: two units of registers.
-        constexpr int HB = (NB <= 8) ? NB : NB / 2;
+        constexpr int HB = (NB <= 8) ? NB : 8;
         constexpr int UPS = NB / HB;                  // units per slice
         f32x4 buf[2][HB];
         auto fetch = [&](int u, int bb) {
@@ -818,14 +848,47 @@ __device__ __forceinline__ void dma_tile(const KArgs& p) {
 
 template <int BM, int BN, int BK, int WM, int WN, int MF, int ST, bool BF16, bool TA, bool TB>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(KArgs p) {
-    dma_tile<BM, BN, BK, WM, WN, MF, ST, BF16 ? kElBF16 : kElF16, TA, TB>(p);
+    dma_tile<BM, BN, BK, WM, WN, MF, ST, BF16 ? kElBF16 : kElF16, TA, TB>(p, slice_work<BK>(p));
+}
+
+// Stream-K: the (tile, K step) iterations dealt out to the grid's workgroups
+// as contiguous ranges (sk_piece, tile_order.h), positions after the XCD
+// permutation so one die's workgroups hold neighbouring tiles; each piece of
+// a range runs the tile body, and the tiles cut by range starts are summed
+// by the K-slice exchange in part order.
+template <int BM, int BN, int BK, int WM, int WN, int MF, int ST, bool BF16>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_dma_sk_kernel(KArgs p) {
+    const uint32_t W = gridDim.x;
+    const uint32_t nkt = static_cast<uint32_t>((p.K + BK - 1) / BK);
+    const uint32_t total = static_cast<uint32_t>(p.num_pid_m * p.num_pid_n) * nkt;
+    const uint32_t w = static_cast<uint32_t>(xcd_permute<int>(blockIdx.x, static_cast<int>(W), p.xcds));
+    uint32_t it = sk_range_start(w, total, W);
+    const uint32_t end = sk_range_start(w + 1, total, W);
+    while (it < end) {
+        const SkPiece q = sk_piece(it, end, total, nkt, W);
+        Work wk;
+        wk.tile = static_cast<int>(q.tile);
+        wk.kt0 = static_cast<int>(q.kt0);
+        wk.kt1 = static_cast<int>(q.kt1);
+        wk.part = static_cast<int>(q.part);
+        wk.nparts = static_cast<int>(q.nparts);
+        wk.base = 0;
+        wk.slot0 = static_cast<int>(q.slot0);
+        wk.slot1 = static_cast<int>(q.slot1);
+        wk.nslots = static_cast<int>(2 * W);
+        // the previous piece's epilogue, exchange flag and LDS reads are done
+        // before this piece's loads refill the LDS
+        __syncthreads();
+        dma_tile<BM, BN, BK, WM, WN, MF, ST, BF16 ? kElBF16 : kElF16, false, false, true>(p, wk);
+        it = q.next;
+    }
 }
 
 // int8 A (M x K, k contiguous) times int8 B stored N x K (k contiguous),
 // int32 C and D: the tile body with the integer instruction.
 template <int BM, int BN, int BK, int WM, int WN, int MF, int ST>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_i8_kernel(KArgs p) {
-    dma_tile<BM, BN, BK, WM, WN, MF, ST, kElI8, false, true>(p);
+    dma_tile<BM, BN, BK, WM, WN, MF, ST, kElI8, false, true>(p, slice_work<BK>(p));
 }
 
 constexpr int kMaxDmaSplits = 64;
@@ -834,6 +897,13 @@ template <int BM, int BN, int BK, int WM, int WN, int MF, int ST, bool BF16, boo
 hipError_t launch_dma(const KArgs& a, int64_t grid, hipStream_t stream) {
     hipLaunchKernelGGL((gemm_dma_kernel<BM, BN, BK, WM, WN, MF, ST, BF16, TA, TB>),
                        dim3(static_cast<unsigned>(grid)), dim3(64 * WM * WN), 0, stream, a);
+    return hipGetLastError();
+}
+
+template <int BM, int BN, int BK, int WM, int WN, int MF, int ST, bool BF16>
+hipError_t launch_dma_sk(const KArgs& a, int64_t grid, hipStream_t stream) {
+    hipLaunchKernelGGL((gemm_dma_sk_kernel<BM, BN, BK, WM, WN, MF, ST, BF16>), dim3(static_cast<unsigned>(grid)),
+                       dim3(64 * WM * WN), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -859,6 +929,15 @@ hipError_t launch_i8(const KArgs& a, int64_t grid, hipStream_t stream) {
     DMA_ENTRY(BM, BN, BK, WM, WN, MF, ST, 0, 1), DMA_ENTRY(BM, BN, BK, WM, WN, MF, ST, 1, 1),     \
     DMA_ENTRY(BM, BN, BK, WM, WN, MF, ST, 0, 2), DMA_ENTRY(BM, BN, BK, WM, WN, MF, ST, 1, 2),     \
     DMA_ENTRY(BM, BN, BK, WM, WN, MF, ST, 0, 3), DMA_ENTRY(BM, BN, BK, WM, WN, MF, ST, 1, 3)
+
+// Stream-K variants: row-major A and B; the grid is the plan's workgroup count.
+#define DMA_SK_ENTRY(BM, BN, BK, WM, WN, MF, ST, BF)                                           \
+    {KF_DMA_SK, BM, BN, BK, ST, MF, WM, WN, 0, BF, 1, 64 * WM * WN,                            \
+     static_cast<int64_t>(ST) * (BM + BN) * BK * 2, &launch_dma_sk<BM, BN, BK, WM, WN, MF, ST, (BF != 0)>, \
+     "gemm_dma_sk_kernel<" DTG_STR(BM) "," DTG_STR(BN) "," DTG_STR(BK) "," DTG_STR(WM) ","      \
+     DTG_STR(WN) "," DTG_STR(MF) "," DTG_STR(ST) "," DTG_STR(BF) ">", 0}
+#define DMA_SK_BOTH(BM, BN, BK, WM, WN, MF, ST) \
+    DMA_SK_ENTRY(BM, BN, BK, WM, WN, MF, ST, 0), DMA_SK_ENTRY(BM, BN, BK, WM, WN, MF, ST, 1)
 
 // int8 variants: dtype 2, B stored N x K; BK in 16-bit units (2 k each); no K slices.
 #define I8_ENTRY(BM, BN, BK, WM, WN, MF, ST)                                                     \

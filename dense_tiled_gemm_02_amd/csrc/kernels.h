@@ -35,7 +35,7 @@ constexpr int64_t kCounterBytes = kMaxCounters * 4;
 
 typedef hipError_t (*launch_fn)(const KArgs& args, int64_t grid, hipStream_t stream);
 
-enum KernelFamily { KF_TILE = 1, KF_SKINNY = 2, KF_DMA = 3 };
+enum KernelFamily { KF_TILE = 1, KF_SKINNY = 2, KF_DMA = 3, KF_DMA_SK = 6 };
 
 // One compiled kernel variant.  vec = 1: 16-byte vector loads (requires
 // K % 8 == 0, N % 8 == 0, lda % 8 == 0, ldb % 8 == 0 and 16-byte aligned A, B);
@@ -70,6 +70,10 @@ int64_t skinny_workspace_bytes(int64_t nslabs, int bm, int bn, int splits);
 // bm x bn split into `splits` K slices (0 when splits == 1, -1 when tiles is
 // above the counter region).
 int64_t dma_workspace_bytes(int64_t tiles, int bm, int bn, int splits);
+
+// Workspace bytes of a stream-K launch of `workgroups` workgroups over
+// `tiles` output tiles of bm x bn (-1 when tiles is above the counter region).
+int64_t dma_sk_workspace_bytes(int64_t tiles, int bm, int bn, int64_t workgroups);
 
 // Enqueue a kernel that writes zeros to nwords 32-bit words at p.
 hipError_t zero_words(void* p, int64_t nwords, hipStream_t stream);

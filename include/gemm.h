@@ -117,12 +117,19 @@ typedef struct gemm_problem {
  *                 last workgroup to finish each output slab or tile (skinny
  *                 family; direct-to-LDS family for tiles of at most 64 fp32
  *                 accumulators per lane); needs a workspace when > 1; 1 for
- *                 the register-staged family
+ *                 the register-staged family.  Stream-K family: the number
+ *                 of workgroups the (tile, K step) iterations are dealt to
+ *                 (0 when forced: one per CU, each range >= 16 K steps)
  *   xcd_remap     GEMM_XCD_ON: pre-permute workgroup ids so each XCD gets a
  *                 contiguous band of the tile order; GEMM_XCD_OFF: plain ids
  *                 (0 in a forced configuration: the planner's choice)
  *   kernel        kernel family: 1 = register-staged tile kernel (any shape),
- *                 2 = skinny split-K kernel, 3 = direct-to-LDS tile kernel */
+ *                 2 = skinny split-K kernel, 3 = direct-to-LDS tile kernel,
+ *                 6 = direct-to-LDS stream-K kernel (row-major A and B; the
+ *                 K steps of all tiles dealt out evenly to `splitk`
+ *                 workgroups, tiles cut between workgroups summed from fp32
+ *                 parts in a workspace, in part order, by the last to finish;
+ *                 "Hopper Support in Triton", the SplitK / stream-K slides) */
 #define GEMM_XCD_ON 1
 #define GEMM_XCD_OFF 2
 
@@ -252,6 +259,19 @@ int64_t gemm_lds_bytes(int32_t bm, int32_t bn, int32_t bk, int32_t stages, gemm_
 gemm_status gemm_tile_of_workgroup(int64_t wg, int64_t num_pid_m, int64_t num_pid_n,
                                    int32_t group_m, int32_t xcd_count,
                                    int64_t* pid_m, int64_t* pid_n);
+
+/* The stream-K schedule of a kernel-6 plan, as the kernel computes it: the
+ * pieces of workgroup range `wg` (after the XCD pre-permutation) when
+ * tiles x k_steps iterations are dealt to `workgroups` ranges, range w being
+ * [floor(w T / W), floor((w + 1) T / W)) of T = tiles x k_steps.  Piece p
+ * fills out[6p .. 6p + 5] with: tile (grouped order), first and end K step,
+ * part number, the tile's part count (1: whole tile, written directly),
+ * and the workspace slot of that part (-1 for a whole tile).  At most
+ * max_pieces are written; *count gets the range's piece count.
+ * GEMM_ERR_INVALID_ARG unless 0 <= wg < workgroups <= tiles x k_steps and
+ * tiles x k_steps x workgroups < 2^31. */
+gemm_status gemm_streamk_pieces(int32_t tiles, int32_t k_steps, int32_t workgroups, int32_t wg,
+                                int32_t* out, int32_t max_pieces, int32_t* count);
 
 const char* gemm_status_string(gemm_status status);
 
