@@ -500,10 +500,13 @@ gemm_status plan_impl(const gemm_problem* given, const gemm_device_info* dev, co
         sk_groups = want.splitk >= 1 ? want.splitk : dev->cu_count;
         if (want.splitk < 1 && sk_groups > total / 16) sk_groups = total / 16;
         if (sk_groups < 1) sk_groups = 1;
-        if (sk_groups > total || sk_groups > dtg::kMaxCounters || total * sk_groups >= (int64_t(1) << 31))
+        // 2 W fp32 tiles of parts, addressed with 32-bit offsets from one descriptor
+        const int64_t part_bytes = 2 * sk_groups * static_cast<int64_t>(e->bm) * e->bn * 4;
+        if (sk_groups > total || sk_groups > dtg::kMaxCounters || total * sk_groups >= (int64_t(1) << 31) ||
+            part_bytes >= (int64_t(1) << 31) - 4096)
             return fail(GEMM_ERR_UNSUPPORTED,
                         "stream-K takes 1 to min(%d, tiles x K steps = %lld) workgroups, with tiles x K steps x "
-                        "workgroups below 2^31 (splitk=%d)",
+                        "workgroups and the parts' bytes below 2^31 (splitk=%d)",
                         dtg::kMaxCounters, (long long)total, want.splitk);
     }
     if (e->family == dtg::KF_SKINNY || e->family == dtg::KF_DMA) {

@@ -74,6 +74,10 @@ def test_forced_stream_k_configurations():
     assert "gemm_dma_sk_kernel<256,256" in p.describe()
     p = plan(1000, 520, 1000, force={"kernel": g.KERNEL_DMA_SK, "bm": 256, "bn": 128})
     assert p.config.splitk == min(256, (4 * 5 * 16) // 16)
+    big = plan(8192, 8192, 8192, force={"kernel": g.KERNEL_DMA_SK, "bm": 256, "bn": 256, "splitk": 4000})
+    assert big.config.splitk == 4000
+    with pytest.raises(g.GemmError):                                        # 2 x 4096 parts of 256 KiB: 2 GiB
+        plan(8192, 8192, 8192, force={"kernel": g.KERNEL_DMA_SK, "bm": 256, "bn": 256, "splitk": 4096})
     for bad in ({"kernel": g.KERNEL_DMA_SK, "splitk": 16 * 16 + 1},):       # more workgroups than K steps
         with pytest.raises(g.GemmError) as e:
             plan(1024, 1024, 1024, force=dict(bad, bm=256, bn=256))
