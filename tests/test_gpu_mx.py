@@ -443,3 +443,53 @@ def test_fp6_and_mixed_workloads_sampled(name):
     got = gemm_inputs.bits(D.cpu())[ii, jj]
     n, worst, first = oracle.mx_tol_check(got, "bf16", ref, S, S8)
     assert n == 0, "%s: %d outside (worst %.3g)" % (name, n, worst)
+
+
+ALL_FORMATS = ("e4m3", "e5m2", "e2m3", "e3m2", "e2m1")
+_BITS = {"e4m3": 8, "e5m2": 8, "e2m3": 6, "e3m2": 6, "e2m1": 4}
+
+
+def _dyadic_rows(rows, K, fmt, rng):
+    """Rows of element codes (stored as the format packs them) whose values
+    are drawn from {0, +-1/2, +-1, +-2}, each code found by decoding every
+    code of the format with the oracle."""
+    n = 1 << _BITS[fmt]
+    vals = oracle.mx_decode(np.arange(n, dtype=np.uint8), fmt)
+    code = {}
+    for c in range(n):
+        v = float(vals[c])
+        if v not in code and not (v == 0 and c != 0):
+            code[v] = c
+    pick = np.array([code[v] for v in (0.0, 0.5, -0.5, 1.0, -1.0, 2.0, -2.0)], dtype=np.uint8)
+    c = pick[rng.integers(0, len(pick), (rows, K))]
+    if _BITS[fmt] == 8:
+        return np.ascontiguousarray(c)
+    if _BITS[fmt] == 6:
+        return gemm_inputs.pack_fp6(c)
+    return np.ascontiguousarray((c[:, 0::2] | (c[:, 1::2] << 4)).astype(np.uint8))
+
+
+@pytest.mark.parametrize("fa", ALL_FORMATS)
+@pytest.mark.parametrize("fb", ALL_FORMATS)
+def test_exact_dyadic_products_every_pair(fa, fb):
+    """A pin of the block-scaled path by exact arithmetic, independent of the
+    instruction's run rounding: with elements in {0, +-1/2, +-1, +-2} and
+    power-of-two scales spanning 2^8, every product, every run of 8 and
+    every fp32 partial sum is exact (K = 256: the sums need at most 20
+    significant bits), so a binary32 output must equal the exact result and
+    a bf16 output its round-to-nearest-even, bit for bit."""
+    M, N, K = 96, 136, 256
+    rng = np.random.default_rng(1000 + ALL_FORMATS.index(fa) * 5 + ALL_FORMATS.index(fb))
+    A, B = _dyadic_rows(M, K, fa, rng), _dyadic_rows(N, K, fb, rng)
+    nb = K // 32
+    SA = (127 + rng.integers(-2, 3, (M, nb))).astype(np.uint8)
+    SB = (127 + rng.integers(-2, 3, (N, nb))).astype(np.uint8)
+    ref, _ = oracle.mx_gemm_f64(A, SA, B, SB, K, fa, fb)
+    assert np.all(np.abs(ref) < 2.0 ** 16)
+    D32 = _run(A, SA, B, SB, K, fa, fb, "f32").cpu().numpy().astype(np.float64)
+    assert np.array_equal(D32, ref), "%s x %s: %d outputs differ from the exact sum" % (
+        fa, fb, int(np.sum(D32 != ref)))
+    D16 = gemm_inputs.bits(_run(A, SA, B, SB, K, fa, fb, "bf16").cpu())
+    want = oracle.encode_rne(ref, "bf16")
+    assert np.array_equal(D16, want), "%s x %s: %d bf16 outputs differ from RNE(exact)" % (
+        fa, fb, int(np.sum(D16 != want)))
