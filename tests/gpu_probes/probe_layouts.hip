@@ -17,6 +17,11 @@
 // transposing 64-bit LDS read at byte address 8 * lane; the 4 halfwords each
 // lane receives are written to out[4 * lane + 0..3].  It reports the lane
 // mapping of that instruction; every address is inside the 1024 bytes.
+//
+// probe_mfma_rate times back-to-back independent matrix instructions (no
+// memory access in the loop) over the whole chip: the throughput a kernel's
+// instruction stream can reach, against which the kernels' fractions of the
+// nominal peaks can be read.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -163,9 +168,95 @@ __global__ __launch_bounds__(64) void probe_lds_dma_kernel(const uint16_t* in, u
     for (int i = l; i < 1024; i += 64) out[i] = lds[i];
 }
 
+// Rate kernels: NACC independent accumulators per wave, `iters` rounds; each
+// thread writes one sum (so nothing is optimized away) to out[global id].
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+template <int FX, int FY, int NACC>
+__global__ __launch_bounds__(512) void rate_scaled_kernel(float* out, int iters) {
+    i32x8 x, y;
+    for (int i = 0; i < 8; ++i) {
+        x[i] = static_cast<int>((threadIdx.x * 7u + i) & 0x11111111u);
+        y[i] = static_cast<int>((threadIdx.x * 3u + i) & 0x22222222u);
+    }
+    f32x16 acc[NACC];
+    for (int a = 0; a < NACC; ++a)
+        for (int r = 0; r < 16; ++r) acc[a][r] = 0.0f;
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int a = 0; a < NACC; ++a)
+            acc[a] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(x, y, acc[a], FX, FY, 0, 127, 0, 127);
+    }
+    float sum = 0.0f;
+    for (int a = 0; a < NACC; ++a)
+        for (int r = 0; r < 16; ++r) sum += acc[a][r];
+    out[blockIdx.x * blockDim.x + threadIdx.x] = sum;
+}
+
+template <int NACC>
+__global__ __launch_bounds__(512) void rate_bf16_kernel(float* out, int iters) {
+    bf16x8 x, y;
+    for (int i = 0; i < 8; ++i) {
+        x[i] = static_cast<__bf16>(static_cast<float>((threadIdx.x + i) & 3));
+        y[i] = static_cast<__bf16>(static_cast<float>(i & 1));
+    }
+    f32x4 acc[NACC];
+    for (int a = 0; a < NACC; ++a)
+        for (int r = 0; r < 4; ++r) acc[a][r] = 0.0f;
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int a = 0; a < NACC; ++a) acc[a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x, y, acc[a], 0, 0, 0);
+    }
+    float sum = 0.0f;
+    for (int a = 0; a < NACC; ++a)
+        for (int r = 0; r < 4; ++r) sum += acc[a][r];
+    out[blockIdx.x * blockDim.x + threadIdx.x] = sum;
+}
+
 }  // namespace
 
 extern "C" {
+
+// kind: 0 bf16 16x16x32 (8 accumulators), 1 E4M3, 2 E2M1, 3 E2M3 (FP6),
+// 4 E4M3 x E2M1 (scaled 32x32x64, 4 accumulators).  grid workgroups of
+// 64 * waves threads (waves 4 or 8), `iters` rounds; out: device floats,
+// at least grid * 64 * waves.  *ms gets the timed launch's duration (one
+// untimed launch first); *flop the flops it performed.  Returns a hipError_t.
+int probe_mfma_rate(int kind, int grid, int waves, int iters, float* out, void* stream, float* ms, double* flop) {
+    if (grid < 1 || (waves != 4 && waves != 8) || iters < 1 || kind < 0 || kind > 4 || !out || !ms || !flop)
+        return static_cast<int>(hipErrorInvalidValue);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const dim3 g(static_cast<unsigned>(grid)), b(static_cast<unsigned>(64 * waves));
+    auto launch = [&](int n) {
+        switch (kind) {
+            case 0: hipLaunchKernelGGL(rate_bf16_kernel<8>, g, b, 0, s, out, n); break;
+            case 1: hipLaunchKernelGGL((rate_scaled_kernel<0, 0, 4>), g, b, 0, s, out, n); break;
+            case 2: hipLaunchKernelGGL((rate_scaled_kernel<4, 4, 4>), g, b, 0, s, out, n); break;
+            case 3: hipLaunchKernelGGL((rate_scaled_kernel<2, 2, 4>), g, b, 0, s, out, n); break;
+            default: hipLaunchKernelGGL((rate_scaled_kernel<0, 4, 4>), g, b, 0, s, out, n); break;
+        }
+    };
+    hipEvent_t e0, e1;
+    hipError_t err = hipEventCreate(&e0);
+    if (err != hipSuccess) return static_cast<int>(err);
+    err = hipEventCreate(&e1);
+    if (err != hipSuccess) {
+        hipEventDestroy(e0);
+        return static_cast<int>(err);
+    }
+    launch(iters);
+    hipEventRecord(e0, s);
+    launch(iters);
+    hipEventRecord(e1, s);
+    err = hipEventSynchronize(e1);
+    if (err == hipSuccess) err = hipEventElapsedTime(ms, e0, e1);
+    if (err == hipSuccess) err = hipGetLastError();
+    hipEventDestroy(e0);
+    hipEventDestroy(e1);
+    const double per = kind == 0 ? 8.0 * 2 * 16 * 16 * 32 : 4.0 * 2 * 32 * 32 * 64;
+    *flop = per * static_cast<double>(grid) * waves * iters;
+    return static_cast<int>(err);
+}
 
 // in: >= num_records + 128 bytes, out: 1024 halfwords (device pointers).
 int probe_lds_dma(const uint16_t* in, uint16_t* out, int num_records, void* stream) {

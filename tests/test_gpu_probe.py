@@ -246,3 +246,16 @@ def _run_scaled(L, mf, fa, fb, a, b, sa, sb):
                                out.data_ptr(), torch.cuda.current_stream().cuda_stream) == 0
     torch.cuda.synchronize()
     return out.cpu().numpy().reshape(64, regs)
+
+
+def test_matrix_instruction_rates():
+    """Back-to-back independent matrix instructions reach at least half of
+    their nominal dense peak (the ceiling a kernel's instruction stream is
+    read against; a mixed 8-bit x 4-bit pair runs at the 8-bit rate)."""
+    import os
+    import sys
+    sys.path.insert(0, os.path.join(os.path.dirname(os.path.abspath(__file__)), "gpu_probes"))
+    import rates
+    for name, per_simd, tf, peak in rates.rates(grid=1024, iters=500):
+        print("%s, %d wave(s) per SIMD: %.1f TFLOP/s (%.1f %% of %.1f)" % (name, per_simd, tf, 100 * tf / peak, peak))
+        assert tf >= 0.5 * peak, (name, per_simd, tf)
