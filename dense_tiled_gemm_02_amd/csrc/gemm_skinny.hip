@@ -158,13 +158,16 @@ __global__ __launch_bounds__(64 * NWV) void gemm_skinny_kernel(KArgs p) {
         a_voff[i] = static_cast<uint32_t>(static_cast<int64_t>(row) * p.lda * 2 + q * 16);
     }
 
-    // Each wave walks its chunks starting at a rotation that depends on the
-    // slab's 512-column run (1 KiB of a row), so that at any moment the runs
-    // read different rows rather than all the same ones: 16 x 8192 x 8192
-    // 29.3 -> 28.6 us (rotations 3 g mod nc; g mod nc, or per 256 columns,
-    // gained less).  A run's slabs share the rotation whatever their width,
-    // so equal K partitions still agree bit for bit.
-    const int rot = nc > 0 ? ((colx >> 9) * 3) % nc : 0;
+    // Slabs of 128 or more columns walk their chunks starting at a rotation
+    // set by the slab's 512-column run g (1 KiB of a row), chunk 3 g mod nc
+    // first, so that at any moment the runs read different rows of B rather
+    // than all the same ones: with B from HBM, 1 and 16 x 8192 x 8192
+    // 29.2-29.4 -> 28.2-28.6 us (g mod nc, or per 256 columns, gained less);
+    // the narrower slabs lose by it (64 columns at 4096 x 4096: 11.5 -> 12.3
+    // us) and keep the plain order.  A run's slabs share the rotation, so
+    // slabs of 128 and 256 columns with equal K partitions still agree bit
+    // for bit.
+    const int rot = (BN >= 128 && nc > 0) ? ((colx >> 9) * 3) % nc : 0;
     auto issue = [&](int c, int slot) {
         const int cr = c + rot;   // chunks in the order rot, rot + 1, ..., nc - 1, 0, ..., rot - 1
         const int k0 = (c_first + (cr >= nc ? cr - nc : cr)) * CK;

@@ -211,7 +211,8 @@ SKINNY = [(256, 4, 32, 2), (128, 4, 32, 3), (128, 4, 32, 4), (128, 2, 32, 8), (1
 def test_skinny_variants(mnk):
     """The skinny-M kernels on ragged shapes (N and K tails, M < 16, K split over
     waves and over 1-8 workgroup slices, some slices and waves left without
-    work); kernels with the same K partition (waves, chunk depth, slices) agree
+    work); kernels with the same K partition (waves, chunk depth, slices, and
+    chunk order: slabs of 128 columns or more walk their chunks rotated) agree
     bit for bit whatever their slab width."""
     M, N, K = mnk
     for dt, has_c in (("bf16", True), ("f16", False)):
@@ -222,7 +223,7 @@ def test_skinny_variants(mnk):
                 cfg = dict(kernel=2, bn=bn, waves_n=nw, bk=ck, stages=st, splitk=sk)
                 D = gpu_run(A, B, C, config=cfg)
                 check(A, B, C, D, dt, label="%s %s %s" % (dt, mnk, cfg))
-                key = (nw, ck, sk)
+                key = (nw, ck, sk, bn >= 128)
                 if key in by_part:
                     assert torch.equal(by_part[key].view(torch.int16), D.view(torch.int16)), cfg
                 else:
@@ -236,8 +237,9 @@ SKINNY32 = [(128, 8, 32, 2), (128, 4, 32, 3), (64, 8, 32, 3), (32, 8, 32, 3)]
                                  (20, 8, 1024)])
 def test_skinny32_variants(mnk):
     """The 32-row skinny kernels (two MFMA row blocks) for 16 < M <= 32, with
-    ragged N and K, over 1-8 workgroup slices; equal K partitions agree bit
-    for bit whatever the slab width."""
+    ragged N and K, over 1-8 workgroup slices; equal K partitions (with the
+    chunk order: rotated for slabs of 128 columns or more) agree bit for bit
+    whatever the slab width."""
     M, N, K = mnk
     for dt, has_c in (("bf16", True), ("f16", False)):
         A, B, C = _inputs(M, N, K, dt, has_c, seed=M + 11 * N + 3 * K)
@@ -247,7 +249,7 @@ def test_skinny32_variants(mnk):
                 cfg = dict(kernel=2, bm=32, bn=bn, waves_n=nw, bk=ck, stages=st, splitk=sk)
                 D = gpu_run(A, B, C, config=cfg)
                 check(A, B, C, D, dt, label="%s %s %s" % (dt, mnk, cfg))
-                key = (nw, ck, sk)
+                key = (nw, ck, sk, bn >= 128)
                 if key in by_part:
                     assert torch.equal(by_part[key].view(torch.int16), D.view(torch.int16)), cfg
                 else:
