@@ -69,7 +69,7 @@ NAMED = {
 
 CUS = 256
 # The axes of the space; `candidates` keeps the points the library compiled.
-KERNELS = (1, 2, 3)             # register-staged tile, skinny, direct-to-LDS tile
+KERNELS = (1, 2, 3, 6)          # register-staged tile, skinny, direct-to-LDS tile, its stream-K form
 BMS, BNS, BKS = (16, 32, 64, 128, 192, 256), (16, 32, 64, 128, 256), (32, 64, 128)
 STAGES, MFMAS = (2, 3, 4, 8), (16, 32)
 WAVES = ((1, 2), (1, 4), (1, 8), (2, 1), (2, 2), (2, 4), (4, 2), (4, 1))
@@ -107,19 +107,22 @@ def candidates(M, N, K, dt="bf16", has_c=False):
     for kern, bm, bn, bk, st, mf, (wm, wn) in itertools.product(KERNELS, BMS, BNS, BKS, STAGES, MFMAS, WAVES):
         if kern == 2 and bm > 32:
             continue
-        for sk in (SPLITS if kern in (2, 3) else (1,)):
+        # stream-K: splitk is the workgroup count; 0 lets the plan take one per CU
+        for sk in (SPLITS if kern in (2, 3) else (0,) if kern == 6 else (1,)):
             f = dict(kernel=kern, bm=bm, bn=bn, bk=bk, stages=st, mfma=mf, waves_m=wm, waves_n=wn, splitk=sk)
             try:
                 pl = g.gemm_plan_create_for(prob, dev, f)
             except g.GemmError:
                 continue
             c = pl.config.as_dict()
+            if kern == 6:
+                f["splitk"] = c["splitk"]
             key = tuple(c[k] for k in ("kernel", "bm", "bn", "bk", "stages", "mfma", "waves_m", "waves_n", "splitk"))
             if key in seen:
                 continue
             seen.add(key)
             tiles = -(-M // c["bm"]) * -(-N // c["bn"])
-            for gm in ((1, 4, 8) if kern != 2 and sk == 1 and tiles >= 2 * CUS else (c["group_m"],)):
+            for gm in ((1, 4, 8) if kern in (1, 3) and sk == 1 and tiles >= 2 * CUS else (c["group_m"],)):
                 out.append(dict(f, group_m=gm))
     return out
 
@@ -127,13 +130,18 @@ def candidates(M, N, K, dt="bf16", has_c=False):
 def prune(M, N, K, cands):
     """(kept, reasons): a tile may exceed a dimension by at most 2x (rounded
     to 16); K slices need >= 16 K steps each and at most one round of
-    workgroups; the skinny kernels only for M <= 32 (their slab height)."""
+    workgroups; the skinny kernels only for M <= 32 (their slab height);
+    stream-K only with >= 16 K steps per workgroup range."""
     kept, why = [], {}
     cdiv = lambda a, b: -(-a // b)
     for c in cands:
         r = None
         if c["kernel"] != 2 and (c["bm"] > 2 * max(16, M) or c["bn"] > 2 * max(16, N)):
             r = "tile more than twice the problem"
+        elif c["kernel"] == 6:
+            total = cdiv(M, c["bm"]) * cdiv(N, c["bn"]) * cdiv(K, c["bk"])
+            if total < 16 * c["splitk"]:
+                r = "stream-K ranges of fewer than 16 K steps"
         elif c["splitk"] > 1:
             steps = cdiv(K, c["bk"])
             wgs = cdiv(M, c["bm"]) * cdiv(N, c["bn"]) * c["splitk"]
