@@ -53,11 +53,12 @@ def _replays_equal(graph, D, ref, what):
 
 # (M, N, K, forced config or None): 256 x 256 tiles with ragged edges, K
 # slices of 128 x 128 tiles, the skinny kernel with K slices, a small ragged
-# problem (64 x 64 tiles)
+# problem (64 x 64 tiles), stream-K over 37 workgroups (cut tiles exchanged)
 CASES = [((1000, 1104, 520), dict(kernel=3, bm=256, bn=256, bk=64, stages=2, waves_m=2, waves_n=4)),
          ((512, 512, 8192), None),
          ((16, 8192, 2048), dict(kernel=2, bn=128, splitk=4)),
-         ((200, 328, 136), None)]
+         ((200, 328, 136), None),
+         ((1000, 1104, 1024), dict(kernel=6, bm=256, bn=256, splitk=37))]
 
 
 @pytest.mark.parametrize("mnk,force", CASES)
