@@ -240,7 +240,7 @@ def test_decode_slab_rule():
         c = plan(M, N, K).config
         return (c.kernel, c.bm, c.bn, c.splitk)
     assert slab(1, 2048, 2048) == (2, 16, 32, 4)
-    assert slab(16, 4096, 4096) == (2, 16, 64, 4)
+    assert slab(8, 4096, 4096) == (2, 16, 64, 4)
     assert slab(4, 8192, 8192) == (2, 16, 128, 4)
     assert slab(8, 6144, 4096) == (2, 16, 64, 2)
     assert slab(4, 4096, 6144) == (2, 16, 64, 4)       # 8 slices would be 768 k each
