@@ -138,6 +138,9 @@ constexpr uint32_t kOOB = 0x80000000u;         // offset past any descriptor ran
 // cache-policy bits of a buffer access at system scope (sc0 | sc1): the
 // access goes past the per-XCD L2 caches, like a system-scope atomic
 constexpr int kSysScope = 1 | 16;
+// cache-policy bit of a buffer load marking it non-temporal (nt): for data
+// read exactly once, such as a weight matrix streamed by the decode kernels
+constexpr int kNonTemporal = 2;
 constexpr int64_t kMaxRecords = 0x7ffffff0;
 
 template <int N, typename Fn>

@@ -421,7 +421,11 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mx_kernel(MxArgs p) {
             // (a non-const local: clang's host pass drops the kernel when the
             // builtin is handed a member of a const reference)
             __amdgpu_buffer_rsrc_t r = IS_A ? d.ra : d.rb;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(smem + dst), 16, v, 0, 0, 0);
+            // the decode slab (BM <= 32: one row of tiles) reads each byte of B
+            // exactly once: non-temporal loads; square tiles share B panels
+            // between rows of tiles through the L2 and keep the default policy
+            constexpr int AUX = (!IS_A && BM <= 32) ? kNonTemporal : 0;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(smem + dst), 16, v, 0, 0, AUX);
         } else {
             constexpr int S = X - IA_W - IB_W;
             __amdgpu_buffer_rsrc_t r = (S < NSA) ? d.rsa : d.rsb;
