@@ -212,7 +212,7 @@ const dtg::KernelEntry* find_entry(const gemm_config& want, int dtype, int vec,
                                    const gemm_device_info& dev, const gemm_problem* p) {
     const int lay = kernel_layout(p);
     for (const dtg::KernelEntry* e : all_entries()) {
-        if (e->dtype != dtype || e->vec != vec) continue;
+        if (e->dtype != dtype || e->vec != vec || e->stream_b) continue;   // streamed-B twins: stream_b_twin
         if (e->layout != -1 && e->layout != lay) continue;
         if (e->lds_bytes > dev.lds_per_wg) continue;
         if ((e->family == dtg::KF_DMA || e->family == dtg::KF_DMA_SK) && !dma_offsets_ok(p, e)) continue;
@@ -220,6 +220,22 @@ const dtg::KernelEntry* find_entry(const gemm_config& want, int dtype, int vec,
         if (matches(e, want)) return e;
     }
     return nullptr;
+}
+
+// The streamed-B twin of a direct-to-LDS variant (the same tile, ring, waves
+// and layout; B loaded non-temporal), or e itself when there is none.  Taken
+// when the grid has one row of tiles, so every byte of B is read once per K
+// slice and caching it gains nothing.
+const dtg::KernelEntry* stream_b_twin(const dtg::KernelEntry* e, const gemm_device_info& dev,
+                                      const gemm_problem* p) {
+    for (const dtg::KernelEntry* t : all_entries()) {
+        if (t->stream_b && t->family == e->family && t->bm == e->bm && t->bn == e->bn && t->bk == e->bk &&
+            t->stages == e->stages && t->mfma == e->mfma && t->waves_m == e->waves_m && t->waves_n == e->waves_n &&
+            t->dtype == e->dtype && t->vec == e->vec && t->layout == e->layout && t->lds_bytes <= dev.lds_per_wg &&
+            dma_offsets_ok(p, t))
+            return t;
+    }
+    return e;
 }
 
 gemm_config cfg_of(int fam, int bm, int bn, int bk, int st, int mf, int wm, int wn) {
@@ -489,6 +505,8 @@ gemm_status plan_impl(const gemm_problem* given, const gemm_device_info* dev, co
                         want.bm, want.bn, want.bk, want.stages, want.mfma, want.waves_m, want.waves_n,
                         want.kernel, (int)prob->dtype, (int)vec, (long long)dev->lds_per_wg);
     }
+    // one row of tiles: the streamed-B twin where one is compiled
+    if (e->family == dtg::KF_DMA && cdiv(prob->M, e->bm) == 1) e = stream_b_twin(e, *dev, prob);
     if (e->family == dtg::KF_SKINNY && prob->M > e->bm)
         return fail(GEMM_ERR_UNSUPPORTED, "this skinny kernel runs M <= %d only (M=%lld)", e->bm,
                     (long long)prob->M);

@@ -135,8 +135,11 @@ __device__ __forceinline__ Work slice_work(const KArgs& p) {
 }
 
 // XCH: the K-slice exchange is compiled for tiles of more than 64
-// accumulators per lane too (the stream-K variants).
-template <int BM, int BN, int BK, int WM, int WN, int MF, int ST, int EL, bool TA, bool TB, bool XCH = false>
+// accumulators per lane too (the stream-K variants).  NTB: B is loaded
+// non-temporal (the variants for a grid of one row of tiles, where each byte
+// of B is read by one workgroup per K slice).
+template <int BM, int BN, int BK, int WM, int WN, int MF, int ST, int EL, bool TA, bool TB, bool XCH = false,
+          bool NTB = false>
 __device__ __forceinline__ void dma_tile(const KArgs& p, const Work& wk) {
     constexpr bool BF16 = EL == kElBF16;
     constexpr bool I8 = EL == kElI8;
@@ -272,7 +275,8 @@ __device__ __forceinline__ void dma_tile(const KArgs& p, const Work& wk) {
             if constexpr (BKC) v |= (d.k0 + b_c8[V] < K) ? 0u : kOOB;
             __amdgpu_buffer_rsrc_t r = d.rb;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                r, (lds_void_t*)(smem + ST * SA + s * SB + (Y * NW + wave) * 512), 16, v, so, 0, 0);
+                r, (lds_void_t*)(smem + ST * SA + s * SB + (Y * NW + wave) * 512), 16, v, so, 0,
+                NTB ? kNonTemporal : 0);
         }
     };
     auto issue_tile = [&](int kt, int s) {
@@ -851,6 +855,13 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(KArgs p) {
     dma_tile<BM, BN, BK, WM, WN, MF, ST, BF16 ? kElBF16 : kElF16, TA, TB>(p, slice_work<BK>(p));
 }
 
+// One row of tiles (M <= BM: decode-like grids), row-major operands: the tile
+// body with B streamed non-temporal.  The same arithmetic as gemm_dma_kernel.
+template <int BM, int BN, int BK, int WM, int WN, int MF, int ST, bool BF16>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_dma_sb_kernel(KArgs p) {
+    dma_tile<BM, BN, BK, WM, WN, MF, ST, BF16 ? kElBF16 : kElF16, false, false, false, true>(p, slice_work<BK>(p));
+}
+
 // Stream-K: the (tile, K step) iterations dealt out to the grid's workgroups
 // as contiguous ranges (sk_piece, tile_order.h), positions after the XCD
 // permutation so one die's workgroups hold neighbouring tiles; each piece of
@@ -901,6 +912,13 @@ hipError_t launch_dma(const KArgs& a, int64_t grid, hipStream_t stream) {
 }
 
 template <int BM, int BN, int BK, int WM, int WN, int MF, int ST, bool BF16>
+hipError_t launch_dma_sb(const KArgs& a, int64_t grid, hipStream_t stream) {
+    hipLaunchKernelGGL((gemm_dma_sb_kernel<BM, BN, BK, WM, WN, MF, ST, BF16>), dim3(static_cast<unsigned>(grid)),
+                       dim3(64 * WM * WN), 0, stream, a);
+    return hipGetLastError();
+}
+
+template <int BM, int BN, int BK, int WM, int WN, int MF, int ST, bool BF16>
 hipError_t launch_dma_sk(const KArgs& a, int64_t grid, hipStream_t stream) {
     hipLaunchKernelGGL((gemm_dma_sk_kernel<BM, BN, BK, WM, WN, MF, ST, BF16>), dim3(static_cast<unsigned>(grid)),
                        dim3(64 * WM * WN), 0, stream, a);
@@ -929,6 +947,16 @@ hipError_t launch_i8(const KArgs& a, int64_t grid, hipStream_t stream) {
     DMA_ENTRY(BM, BN, BK, WM, WN, MF, ST, 0, 1), DMA_ENTRY(BM, BN, BK, WM, WN, MF, ST, 1, 1),     \
     DMA_ENTRY(BM, BN, BK, WM, WN, MF, ST, 0, 2), DMA_ENTRY(BM, BN, BK, WM, WN, MF, ST, 1, 2),     \
     DMA_ENTRY(BM, BN, BK, WM, WN, MF, ST, 0, 3), DMA_ENTRY(BM, BN, BK, WM, WN, MF, ST, 1, 3)
+
+// Streamed-B variants (stream_b = 1): row-major A and B, K slices as gemm_dma_kernel.
+#define DMA_SB_ENTRY(BM, BN, BK, WM, WN, MF, ST, BF)                                            \
+    {KF_DMA, BM, BN, BK, ST, MF, WM, WN, ((BM / WM) * (BN / WN) / 64 <= 64 ? kMaxDmaSplits : 1),  \
+     BF, 1, 64 * WM * WN, static_cast<int64_t>(ST) * (BM + BN) * BK * 2,                     \
+     &launch_dma_sb<BM, BN, BK, WM, WN, MF, ST, (BF != 0)>,                                   \
+     "gemm_dma_sb_kernel<" DTG_STR(BM) "," DTG_STR(BN) "," DTG_STR(BK) "," DTG_STR(WM) ","     \
+     DTG_STR(WN) "," DTG_STR(MF) "," DTG_STR(ST) "," DTG_STR(BF) ">", 0, 1}
+#define DMA_SB_BOTH(BM, BN, BK, WM, WN, MF, ST) \
+    DMA_SB_ENTRY(BM, BN, BK, WM, WN, MF, ST, 0), DMA_SB_ENTRY(BM, BN, BK, WM, WN, MF, ST, 1)
 
 // Stream-K variants: row-major A and B; the grid is the plan's workgroup count.
 #define DMA_SK_ENTRY(BM, BN, BK, WM, WN, MF, ST, BF)                                           \

@@ -50,6 +50,7 @@ struct KernelEntry {
     launch_fn launch;
     const char* name;
     int32_t layout;      // operands in memory: bit 0 A stored K x M, bit 1 B stored N x K; -1 any strides
+    int32_t stream_b;    // 1: B loaded non-temporal, for grids of one row of tiles (each byte of B read once)
 };
 
 // Layout code of a problem's A and B (see KernelEntry::layout).

@@ -249,6 +249,24 @@ def test_decode_slab_rule():
     assert slab(24, 4096, 14336) == (2, 32, 128, 8)
 
 
+def test_one_row_of_tiles_streams_b():
+    """A grid of one row of direct-to-LDS tiles reads each byte of B once per
+    K slice: the planner swaps in the streamed-B twin of the tile (non-temporal
+    B loads) where one is compiled (the 64 x 64 tile, row-major operands)."""
+    for shape in ((32, 4096, 4096), (64, 8192, 8192), (64, 4096, 4096)):
+        d = plan(*shape).describe()
+        assert "gemm_dma_sb_kernel<64,64,64,2,2,16,4,1>" in d, (shape, d)
+    d = plan(48, 2048, 8192).describe()                   # one row of K-sliced 128 x 128 tiles: no twin
+    assert "gemm_dma_kernel<128,128,64,2,4,16,4,1" in d and "splitk=8" in d, d
+    for shape, kw in (((128, 4096, 4096), {}), ((1024, 1024, 1024), {}), ((64, 4096, 4096), {"tb": True})):
+        d = plan(*shape, **kw).describe()
+        assert "gemm_dma_sb_kernel" not in d, (shape, d)
+    # a forced 64 x 64 configuration on one row of tiles takes the twin too
+    d = plan(64, 1024, 2048, force={"kernel": 3, "bm": 64, "bn": 64, "bk": 64, "stages": 4, "waves_m": 2,
+                                    "waves_n": 2, "splitk": 2}).describe()
+    assert "gemm_dma_sb_kernel" in d and "splitk=2" in d
+
+
 def test_split_k_plans_need_and_check_a_workspace():
     p = plan(16, 8192, 8192)
     c = p.config
