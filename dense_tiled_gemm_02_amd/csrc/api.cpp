@@ -293,11 +293,15 @@ gemm_config heuristic(const gemm_problem* p, const gemm_device_info& dev, int* g
         // slabs with 4 slices at 8192 (29.2 us), 64-column slabs of 4 waves with
         // 4 slices at 4096 (11.4 us; 128 columns with 8 slices 12.2 us) and
         // 32-column slabs with 4 slices at 2048 (6.8-7.0 us; 128 columns with
-        // 4 slices, i.e. a quarter of the CUs, 8.1-8.8 us).  A long K changes
-        // that: when 128-column slabs fill the CUs with up to 8 slices of at
-        // least 1024 k each, they beat the narrower slabs of the 4-slice rule
+        // 4 slices, i.e. a quarter of the CUs, 8.1-8.8 us).  When 128-column
+        // slabs fill the CUs with up to 8 slices of at least 512 k each, they
+        // beat the narrower slabs of the 4-slice rule: at first for a long K
         // (N = 4096, K = 11008: 20.4 against 22.5 us; K = 14336: 26.4 against
-        // 28.1 us, at M = 1 and 16).
+        // 28.1 us, at M = 1 and 16), and since the wide slabs walk their chunks
+        // rotated and stream B non-temporal, at N = K = 4096 too (M = 1, 4, 16:
+        // 11.0-11.2 against 11.2-11.5 us).  The 32-row slabs keep 1024 k: at
+        // M = 32, N = K = 4096, 128 columns with 8 slices take 14.6 us against
+        // 12.6 for the 4-slice rule's 64 columns.
         if (allow_ws && cdiv(N, 128) <= 4096) {
             const int64_t s_max = K / 512 < 4 ? (K / 512 > 1 ? K / 512 : 1) : 4;
             int bn = 32;
@@ -310,7 +314,7 @@ gemm_config heuristic(const gemm_problem* p, const gemm_device_info& dev, int* g
             if (bn < 128) {
                 int64_t s128 = dev.cu_count / cdiv(N, 128);
                 if (s128 > 8) s128 = 8;
-                if (cdiv(N, 128) * s128 >= dev.cu_count && K / s128 >= 1024) bn = 128;
+                if (cdiv(N, 128) * s128 >= dev.cu_count && K / s128 >= (M <= 16 ? 512 : 1024)) bn = 128;
             }
             const int64_t slabs = cdiv(N, bn);
             int64_t s = dev.cu_count / (slabs > 0 ? slabs : 1);

@@ -235,25 +235,28 @@ def test_in_place_addend_allowed_only_with_equal_strides():
 def test_decode_slab_rule():
     """M <= 32: the widest slab (128, 64 or 32 columns) whose slabs fill the
     CUs with 4 K slices; 128-column slabs instead when they fill the CUs with
-    up to 8 slices of at least 1024 k (shapes outside the tuned table)."""
+    up to 8 slices of at least 512 k (1024 k for the 32-row slabs of M > 16;
+    shapes outside the tuned table)."""
     def slab(M, N, K):
         c = plan(M, N, K).config
         return (c.kernel, c.bm, c.bn, c.splitk)
     assert slab(1, 2048, 2048) == (2, 16, 32, 4)
-    assert slab(8, 4096, 4096) == (2, 16, 64, 4)
+    assert slab(8, 4096, 4096) == (2, 16, 128, 8)
+    assert slab(8, 4096, 2048) == (2, 16, 64, 4)       # 8 slices would be 256 k each
     assert slab(4, 8192, 8192) == (2, 16, 128, 4)
     assert slab(8, 6144, 4096) == (2, 16, 64, 2)
-    assert slab(4, 4096, 6144) == (2, 16, 64, 4)       # 8 slices would be 768 k each
+    assert slab(4, 4096, 6144) == (2, 16, 128, 8)
     assert slab(4, 4096, 11008) == (2, 16, 128, 8)
     assert slab(1, 4096, 14336) == (2, 16, 128, 8)
     assert slab(24, 4096, 14336) == (2, 32, 128, 8)
+    assert slab(24, 4096, 4096) == (2, 32, 64, 4)       # 32-row slabs: slices of >= 1024 k
 
 
 def test_one_row_of_tiles_streams_b():
     """A grid of one row of direct-to-LDS tiles reads each byte of B once per
     K slice: the planner swaps in the streamed-B twin of the tile (non-temporal
     B loads) where one is compiled (the 64 x 64 tile, row-major operands)."""
-    for shape in ((32, 4096, 4096), (64, 8192, 8192), (64, 4096, 4096)):
+    for shape in ((32, 8192, 8192), (64, 8192, 8192), (64, 4096, 4096)):
         d = plan(*shape).describe()
         assert "gemm_dma_sb_kernel<64,64,64,2,2,16,4,1>" in d, (shape, d)
     d = plan(48, 2048, 8192).describe()                   # one row of K-sliced 128 x 128 tiles: no twin
