@@ -124,7 +124,9 @@ typedef struct gemm_problem {
  *                 contiguous band of the tile order; GEMM_XCD_OFF: plain ids
  *                 (0 in a forced configuration: the planner's choice)
  *   kernel        kernel family: 1 = register-staged tile kernel (any shape),
- *                 2 = skinny split-K kernel, 3 = direct-to-LDS tile kernel,
+ *                 2 = skinny split-K kernel, 3 = direct-to-LDS tile kernel
+ *                 (when M fits one row of its 64 x 64 tiles, the variant that
+ *                 loads B non-temporal: gemm_plan_describe names it),
  *                 6 = direct-to-LDS stream-K kernel (row-major A and B; the
  *                 K steps of all tiles dealt out evenly to `splitk`
  *                 workgroups, tiles cut between workgroups summed from fp32
